@@ -1,0 +1,424 @@
+"""Pins of the CPU oracle against facts other than itself.
+
+Every check here is CPU-only.  A plausible mistake in the oracle (a dropped
+term, a wrong sign or index, a transposed operand, a wrong scale decode)
+fails at least one of them:
+
+* golden bytes worked by hand from the format readings (codes, sites, scales,
+  sign planes, header fields);
+* byte totals printed on the WAL2-Ternary-27B card, which fix the 2-bit code
+  plus fp16-scale density exactly and the base-3 density approximately;
+* exact-rational brute force of the operator's definition on tiny matrices,
+  written directly from the logical arrays with Fraction arithmetic;
+* special cases that reduce to library routines (numpy matmul, scipy sparse);
+* invariants: the all-zero case, columns e_j, linearity, round trips,
+  exhaustive codec sweeps.
+"""
+import json
+import os
+import struct
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.sparse
+
+import synth
+from oracle import dense as D
+from oracle import format as F
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")))
+
+
+def tiny(out, inp, k, paths, rank, tf=0, sf=0, seed=0, zero_T=False):
+    m = synth.make_matrix(100 + seed, out * 1000 + inp + 7 * k + paths, out, inp, k=k,
+                          n_paths=paths, rank=rank, trit_fmt=tf, scale_fmt=sf, zero_T=zero_T)
+    return F.from_synth(m)
+
+
+def brute_y(L, x):
+    """y_n = sum_j W[n, j] x_j with W from the definition, in exact rationals.
+
+    W[n, j] = alpha[n, g] T[n, j] + beta[n, g] R[n, j]
+              + sum_p sum_r s_p[r] U_p[n, r] V_p[j, r],   g = j // 128,
+    R[n, j] = sign of the site of group g at position j - 128 g, else 0.
+    """
+    xs = [Fraction(float(v)) for v in x]
+    y = []
+    for n in range(L.out):
+        acc = Fraction(0)
+        R = {}
+        for g in range(L.inp // 128):
+            for i in range(L.k):
+                R[g * 128 + int(L.site_pos[n, g, i])] = int(L.site_sign[n, g, i])
+        for j in range(L.inp):
+            g = j // 128
+            w = Fraction(float(L.alpha[n, g])) * int(L.T[n, j])
+            if j in R:
+                w += Fraction(float(L.beta[n, g])) * R[j]
+            for p in range(L.U.shape[0]):
+                for r in range(L.U.shape[2]):
+                    w += Fraction(float(L.s[p, r])) * int(L.U[p, n, r]) * int(L.V[p, j, r])
+            acc += w * xs[j]
+        y.append(acc)
+    return y
+
+
+# --------------------------------------------------------------------------
+# Golden bytes worked from the format readings.
+
+def test_golden_2bit_codes():
+    # trits (+1, -1, 0, +1) -> codes 01, 11, 00, 01 at bits 0-1, 2-3, 4-5, 6-7
+    # -> 0b01_00_11_01 = 0x4D
+    T = np.array([[1, -1, 0, 1] * 32], dtype=np.int8)
+    assert F.encode_codes_2bit(T)[0, 0] == 0x4D
+    T = np.zeros((1, 128), np.int8)
+    T[0, 127] = -1                       # last trit of the row: byte 31, bits 6-7 = 11
+    assert F.encode_codes_2bit(T)[0, 31] == 0xC0
+    assert not F.encode_codes_2bit(T)[0, :31].any()
+
+
+def test_golden_base3_bytes():
+    # (+1, -1, 0, +1, 0) -> digits (2, 0, 1, 2, 1) -> 2 + 0*3 + 1*9 + 2*27 + 1*81 = 146 = 0x92
+    T = np.zeros((1, 128), np.int8)
+    T[0, :5] = [1, -1, 0, 1, 0]
+    row = F.encode_codes_base3(T)[0]
+    assert row[0] == 0x92
+    # five zero trits -> digits 1,1,1,1,1 -> 121 = 0x79; 128 trits -> 26 bytes, the
+    # 26th holds trits 125..127 and two zero-trit fillers; the row pads to 32 bytes
+    assert len(row) == 32 and row[1] == 0x79 and (row[26:] == 0x79).all()
+    T[0, 125:128] = [-1, -1, -1]         # digits 0,0,0,1,1 -> 27 + 81 = 108
+    assert F.encode_codes_base3(T)[0, 25] == 108
+    T = np.full((1, 5), 1, np.int8)
+    T = np.pad(T, ((0, 0), (0, 123)))
+    assert F.encode_codes_base3(T)[0, 0] == 242   # all digits 2 -> 3^5 - 1
+
+
+def test_golden_site_bytes():
+    pos = np.array([[[5, 127]]], np.uint8)
+    sign = np.array([[[-1, 1]]], np.int8)
+    assert list(F.encode_sites(pos, sign)[0, 0]) == [0x85, 0x7F]
+
+
+def test_golden_scales():
+    # 0.02 as fp32 = 0x3CA3D70A; fp24 keeps 0x3CA3D7 and stores it little-endian D7 A3 3C
+    v = np.array([np.float32(0.02)]).view(np.uint32) & np.uint32(0xFFFFFF00)
+    v = v.view(np.float32)
+    b = F._scale_bytes(v, F.SCALE_FP24)
+    assert list(b) == [0xD7, 0xA3, 0x3C]
+    assert float(F._scale_values(b, 1, F.SCALE_FP24)[0]) == 0.019999980926513672
+    # fp16 1.0 = 0x3C00 -> bytes 00 3C ; -2.0 = 0xC000
+    assert list(F._scale_bytes(np.array([1.0, -2.0], np.float32), F.SCALE_FP16)) == [0, 0x3C, 0, 0xC0]
+    with pytest.raises(F.FormatError):
+        F._scale_bytes(np.array([0.1], np.float32), F.SCALE_FP16)     # not an fp16 value
+    with pytest.raises(F.FormatError):
+        F._scale_bytes(np.array([np.float32(0.02)]), F.SCALE_FP24)    # low byte non-zero
+
+
+def test_golden_sign_planes_and_header():
+    L = tiny(2, 128, 2, 1, 9)
+    L.U[0] = 1
+    L.U[0, 1, 8] = -1                    # row 1, rank 8 -> byte 1 of row 1, bit 0
+    L.V[0] = 1
+    L.V[0, 9, 0] = -1                    # column 9 of rank 0 -> byte 1 of rank 0's row, bit 1
+    blob = F.pack(L)
+    h = F.parse_header(blob)
+    assert h["magic"] == 0x314C4157 and blob[:4] == b"WAL1"
+    U = np.frombuffer(blob, np.uint8)[h["U0"]: h["U0"] + 4].reshape(2, 2)
+    assert U.tolist() == [[0, 0], [0, 1]]
+    V = np.frombuffer(blob, np.uint8)[h["V0"]: h["V0"] + 16 * 9].reshape(9, 16)
+    assert V[0, 1] == 0x02 and V.sum() == 2
+    assert struct.unpack("<I", blob[8:12])[0] == 2 and struct.unpack("<I", blob[12:16])[0] == 128
+    assert h["codes"] == 256 and h["codes"] % 256 == 0 and h["total"] % 256 == 0
+
+
+# --------------------------------------------------------------------------
+# Byte totals printed on the pages.
+
+def test_pq2_total_matches_page_exactly():
+    """2-bit codes + one fp16 scale per 128 (our k = 0, no-path format) is
+    34 bytes per 128 weights; with F32 exceptions this reproduces the
+    WAL2-Ternary-27B card's PQ2_0 tensor bytes to the byte."""
+    g = GOLD["wal2_27b"]
+    for out, inp in [(5120, 17408), (17408, 5120), (1024, 5120), (256, 128)]:
+        sz = F.plane_sizes(out, inp, 0, 0, 0, F.TRIT_2BIT, F.SCALE_FP16)
+        assert sz["codes"] + sz["alpha"] == out * inp * 34 // 128
+    assert g["pq2_codes_bytes_per_128"] + g["pq2_scale_bytes_per_128"] == 34
+    total = g["ternary_params"] * 34 // 128 + g["exception_params"] * 4
+    assert total == g["pq2_tensor_bytes"]
+    assert abs(34 * 8 / 128 - g["pq2_bits_per_weight"]) < 1e-12
+    assert g["ternary_params"] + g["exception_params"] == g["text_params"]
+    assert g["text_params"] * 2 == g["bf16_ideal_bytes"]
+    # three of the four 2-bit codes are used by the oracle's encoder
+    T = np.array([[-1, 0, 1, 0] * 32], np.int8)
+    codes = set(((F.encode_codes_2bit(T)[0, :, None] >> np.array([0, 2, 4, 6])) & 3).ravel().tolist())
+    assert codes == {0, 1, 3} and len(codes) == g["pq2_codes_used_of_4"]
+
+
+def test_base3_total_matches_page_continuous_packing():
+    """Continuous five-trits-per-byte rows, bf16 scales per 128 and bf16
+    exceptions land within 0.01 % of the card's base-3 tensor bytes; packing
+    each 128-trit group into its own 26 bytes overshoots by more than 1 %."""
+    g = GOLD["wal2_27b"]
+    P = g["ternary_params"]
+    # our row width for the card's hidden size: 5120 trits -> exactly 1024 bytes
+    assert F.row_stride(5120, F.TRIT_BASE3) == 5120 // 5
+    continuous = P * 8 // 5 // 8 + P // 128 * 2 + g["exception_params"] * 2
+    per_group = P // 128 * 26 + P // 128 * 2 + g["exception_params"] * 2
+    printed = g["base3_tensor_bytes"]
+    assert abs(continuous - printed) / printed < 1e-4
+    assert (per_group - printed) / printed > 0.01
+    assert abs(printed * 8 / g["text_params"] - g["base3_bits_per_param"]) < 1e-5
+    assert abs(g["bf16_ideal_bytes"] / printed - g["ratio_bf16_to_base3"]) < 0.01
+    assert abs(g["bf16_ideal_bytes"] / g["pq2_tensor_bytes"] - g["ratio_bf16_to_pq2"]) < 0.01
+
+
+def test_sweep_counts_match_page():
+    g = GOLD["wal_ternary_8b"]
+    shapes = synth.sweep_shapes()
+    assert len(shapes) == g["body_matrices"] == g["layers"] * 7
+    mask = synth.sweep_lowrank_mask()
+    assert mask.sum() == g["walb2_matrices"] and (~mask).sum() == g["base_only_matrices"]
+    # the body's packed bytes in this format sit near the card's "about 2.3 GB"
+    # executable cache (2.39e9 bytes = 2.23 GiB)
+    tot = sum(F.algorithmic_bytes(o, i, 8, int(m), 16, 0, 0) for (o, i), m in zip(shapes, mask))
+    assert abs(tot / 2**30 - g["executable_cache_gb_approx"]) < 0.15
+
+
+# --------------------------------------------------------------------------
+# Exact-rational brute force.
+
+@pytest.mark.parametrize("out,inp,k,paths,rank,tf,sf", [
+    (1, 128, 0, 0, 0, 0, 0), (2, 128, 2, 0, 0, 0, 0), (3, 256, 8, 1, 8, 0, 0),
+    (2, 256, 4, 2, 3, 1, 1), (3, 128, 8, 1, 8, 1, 0), (1, 256, 0, 1, 8, 0, 1),
+])
+def test_bruteforce_integer_x_exact(out, inp, k, paths, rank, tf, sf):
+    L = tiny(out, inp, k, paths, rank, tf, sf)
+    x = np.random.default_rng(5).integers(-3, 4, size=inp).astype(np.float64)
+    y = D.gemv(F.pack(L), x)
+    exact = brute_y(L, x)
+    assert [Fraction(float(v)) for v in y] == exact
+
+
+@pytest.mark.parametrize("bf16", [True, False])
+def test_bruteforce_random_x_within_fp64_bound(bf16):
+    L = tiny(3, 256, 8, 2, 8, 0, 1)
+    x, _ = synth.make_x(9, 1, 256, bf16=bf16)
+    x = x[0]
+    y = D.gemv(F.pack(L), x)
+    exact = brute_y(L, x)
+    W = D.dense_W(L)
+    bound = 256 * 2.0 ** -52 * (np.abs(W) @ np.abs(x.astype(np.float64)))
+    for n in range(3):
+        assert abs(Fraction(float(y[n])) - exact[n]) <= Fraction(float(bound[n]))
+
+
+def test_columns_match_definition_exactly():
+    """x = e_j returns column j of W exactly (every W entry is a multiple of
+    2^-24 below 2^-2, so the column is exact in any precision >= fp32)."""
+    L = tiny(3, 256, 8, 2, 16, 1, 1)
+    blob = F.pack(L)
+    for j in [0, 1, 5, 127, 128, 200, 255]:
+        e = np.zeros(256)
+        e[j] = 1.0
+        y = D.gemv(blob, e)
+        col = brute_y(L, e)
+        assert [Fraction(float(v)) for v in y] == col
+        assert np.array_equal(y.astype(np.float32).astype(np.float64), y)
+
+
+# --------------------------------------------------------------------------
+# Special cases that reduce to library routines.
+
+def test_block_scaled_ternary_is_plain_matmul():
+    """k = 0 and no paths: a block-scaled ternary product (the PQ2_0 layout of
+    the WAL2-Ternary-27B card), (T * repeat(alpha, 128)) @ x."""
+    L = tiny(16, 512, 0, 0, 0)
+    x = np.random.default_rng(1).standard_normal(512)
+    ref = (L.T * np.repeat(L.alpha.astype(np.float64), 128, axis=1)) @ x
+    np.testing.assert_allclose(D.gemv(F.pack(L), x), ref, rtol=1e-13, atol=1e-13)
+
+
+def test_pure_sparse_matches_scipy_coo():
+    L = tiny(8, 384, 8, 0, 0, zero_T=True)
+    x = np.random.default_rng(2).standard_normal(384)
+    rows, cols, vals = [], [], []
+    for n in range(8):
+        for g in range(3):
+            for i in range(8):
+                rows.append(n)
+                cols.append(128 * g + int(L.site_pos[n, g, i]))
+                vals.append(float(L.beta[n, g]) * int(L.site_sign[n, g, i]))
+    S = scipy.sparse.coo_matrix((vals, (rows, cols)), shape=(8, 384)).tocsr()
+    np.testing.assert_allclose(D.gemv(F.pack(L), x), S @ x, rtol=1e-13, atol=1e-14)
+
+
+def test_pure_lowrank_matches_factored_product():
+    L = tiny(8, 256, 0, 2, 16, zero_T=True)
+    x = np.random.default_rng(3).standard_normal(256)
+    ref = sum(L.U[p].astype(np.float64) @ (L.s[p].astype(np.float64) * (L.V[p].astype(np.float64).T @ x))
+              for p in range(2))
+    np.testing.assert_allclose(D.gemv(F.pack(L), x), ref, rtol=1e-12, atol=1e-14)
+
+
+def test_all_zero_returns_zero():
+    L = tiny(4, 256, 0, 0, 0, zero_T=True)
+    x = np.random.default_rng(4).standard_normal(256)
+    assert not D.gemv(F.pack(L), x).any()
+    L = tiny(4, 256, 8, 1, 4, zero_T=True)
+    L.beta[:] = 0
+    L.s[:] = 0
+    assert not D.gemv(F.pack(L), x).any()
+
+
+def test_linearity():
+    L = tiny(8, 256, 4, 1, 8)
+    blob = F.pack(L)
+    rng = np.random.default_rng(6)
+    x1, x2 = rng.standard_normal(256), rng.standard_normal(256)
+    lhs = D.gemv(blob, 0.75 * x1 - 2.5 * x2)
+    rhs = 0.75 * D.gemv(blob, x1) - 2.5 * D.gemv(blob, x2)
+    np.testing.assert_allclose(lhs, rhs, rtol=1e-12, atol=1e-12)
+
+
+def test_gemm_rows_equal_gemv():
+    L = tiny(8, 256, 8, 1, 8)
+    blob = F.pack(L)
+    X = np.random.default_rng(7).standard_normal((5, 256))
+    Y = D.gemm(blob, X)
+    for b in range(5):
+        np.testing.assert_allclose(Y[b], D.gemv(blob, X[b]), rtol=1e-13, atol=1e-15)
+
+
+# --------------------------------------------------------------------------
+# Codecs: exhaustive sweeps and round trips.
+
+def test_base3_codec_is_a_bijection_on_243_bytes():
+    trits = np.array(np.meshgrid(*[[-1, 0, 1]] * 5, indexing="ij")).reshape(5, -1).T  # 243 x 5
+    T = np.zeros((243, 128), np.int8)
+    T[:, :5] = trits
+    b = F.encode_codes_base3(T)[:, 0]
+    assert sorted(b.tolist()) == list(range(243))
+    # digit i of the byte is trit i + 1 (least significant digit first)
+    for row, byte in zip(trits, b):
+        v = int(byte)
+        for i in range(5):
+            v, d = divmod(v, 3)
+            assert d == row[i] + 1
+    back = F.decode_codes_base3(F.encode_codes_base3(T), 128)
+    assert np.array_equal(back, T)
+
+
+@pytest.mark.parametrize("bad", [243, 250, 255])
+def test_base3_rejects_bytes_above_242(bad):
+    L = tiny(1, 128, 0, 0, 0, tf=1)
+    blob = bytearray(F.pack(L))
+    blob[256] = bad
+    blob[176:184] = struct.pack("<Q", F.checksum(bytes(blob)))
+    with pytest.raises(F.FormatError):
+        F.unpack(bytes(blob))
+
+
+def test_2bit_rejects_code_10():
+    L = tiny(1, 128, 0, 0, 0)
+    blob = bytearray(F.pack(L))
+    blob[256 + 3] = (blob[256 + 3] & ~(3 << 4)) | (2 << 4)
+    blob[176:184] = struct.pack("<Q", F.checksum(bytes(blob)))
+    with pytest.raises(F.FormatError):
+        F.unpack(bytes(blob))
+
+
+def test_every_2bit_code_at_a_probe_position():
+    """Each stored code at one position, read through the whole oracle with
+    x = e_j: 00 -> 0, 01 -> +alpha, 11 -> -alpha."""
+    L = tiny(1, 128, 0, 0, 0, zero_T=True)
+    L.alpha[:] = 0.5
+    for j in (0, 37, 127):
+        for code, want in ((0, 0.0), (1, 0.5), (3, -0.5)):
+            blob = bytearray(F.pack(L))
+            blob[256 + j // 4] |= code << (2 * (j % 4))
+            blob[176:184] = struct.pack("<Q", F.checksum(bytes(blob)))
+            e = np.zeros(128)
+            e[j] = 1
+            assert D.gemv(bytes(blob), e)[0] == want
+
+
+def test_every_site_byte():
+    """All 256 site bytes through the oracle (k = 2, T = 0, beta = 1): the
+    probe byte's site adds sign * x[pos] with pos = low 7 bits, sign = - iff bit 7."""
+    L = tiny(1, 128, 2, 0, 0, zero_T=True)
+    L.beta[:] = 1.0
+    x = np.arange(1, 129, dtype=np.float64)
+    for v in range(256):
+        pos, neg = v & 0x7F, v >> 7
+        other = 0 if pos else 1                        # a second, distinct site
+        lo, hi = sorted([(pos, v), (other, other)])
+        blob = bytearray(F.pack(L))
+        h = F.parse_header(blob)
+        blob[h["sites"]] = lo[1]
+        blob[h["sites"] + 1] = hi[1]
+        blob[176:184] = struct.pack("<Q", F.checksum(bytes(blob)))
+        y = D.gemv(bytes(blob), x)[0]
+        assert y == (-1 if neg else 1) * (pos + 1) + (other + 1)
+
+
+def test_each_lowrank_sign_bit():
+    """Flipping one stored U or V bit flips exactly that factor entry."""
+    L = tiny(2, 128, 0, 1, 8, zero_T=True)
+    base = F.unpack(F.pack(L))
+    blob = bytearray(F.pack(L))
+    h = F.parse_header(blob)
+    for plane, idx, check in (("U0", 1, lambda A, B: (A.U != B.U).sum() == 1 and A.U[0, 0, 1] == -B.U[0, 0, 1]),
+                              ("V0", 2, lambda A, B: (A.V != B.V).sum() == 1 and A.V[0, 2, 0] == -B.V[0, 2, 0])):
+        b2 = bytearray(blob)
+        b2[h[plane]] ^= 1 << (idx if plane == "U0" else 2)
+        b2[176:184] = struct.pack("<Q", F.checksum(bytes(b2)))
+        assert check(F.unpack(bytes(b2)), base)
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 4])
+def test_roundtrip_config_shapes(cfg):
+    if cfg == 4:
+        m = synth.make_matrix(4, 0, 64, 17408, k=4, n_paths=2, rank=16, trit_fmt=1, scale_fmt=1)
+    elif cfg == 1:
+        m = synth.make_matrix(1, 0, 96, 4096, k=8, n_paths=1, rank=16)
+    else:
+        m = synth.config_matrix(0)
+    L = F.from_synth(m)
+    back = F.unpack(F.pack(L))
+    for f in ["T", "site_pos", "site_sign", "alpha", "U", "V", "s"]:
+        assert np.array_equal(getattr(L, f), getattr(back, f)), f
+    if L.k:
+        assert np.array_equal(L.beta, back.beta)
+
+
+def test_rejections():
+    L = tiny(2, 256, 4, 1, 4)
+    good = F.pack(L)
+    F.unpack(good)
+    bad = bytearray(good)
+    bad[0] ^= 1
+    with pytest.raises(F.FormatError):
+        F.unpack(bytes(bad))                       # magic
+    bad = bytearray(good)
+    bad[4] = 2
+    with pytest.raises(F.FormatError):
+        F.unpack(bytes(bad))                       # version
+    bad = bytearray(good)
+    bad[-1] ^= 0xFF
+    with pytest.raises(F.FormatError):
+        F.unpack(bytes(bad))                       # checksum
+    with pytest.raises(F.FormatError):
+        F.unpack(good[:-256])                      # short
+    L2 = tiny(2, 256, 4, 1, 4)
+    L2.site_pos[0, 0, 1] = L2.site_pos[0, 0, 0]
+    with pytest.raises(F.FormatError):
+        F.pack(L2)                                 # duplicate site
+    L3 = tiny(2, 256, 4, 1, 4)
+    L3.k = 3
+    with pytest.raises(F.FormatError):
+        F.pack(L3)
+    L4 = tiny(2, 256, 4, 1, 4)
+    L4.T[0, 0] = 2
+    with pytest.raises(F.FormatError):
+        F.pack(L4)
