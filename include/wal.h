@@ -1,0 +1,223 @@
+/*
+ * wal.h - C ABI of libwal: matrix-vector products taken directly from the
+ * packed WAL ternary-hybrid weight format on AMD Instinct MI355X (gfx950).
+ *
+ * The operator is the one printed on the WAL-Ternary-8B model cards (Kazakh
+ * card, section "Модель пішімі"; English card, section "Representation"):
+ *
+ *     y = W(x) = (alpha * T + beta * R) x + sum_p sum_r s_p[r] U_p[:, r] (V_p[:, r]^T x)
+ *
+ *   T    ternary base, entries in {-1, 0, +1} ("T3", strict ternary);
+ *   R    exactly k signed residual sites per (row, group of 128 columns),
+ *        k in {0, 2, 4, 8} ("exactly 8 signed residual sites per group of
+ *        128 weights"; k0/k2/k4/k8 on the WAL-Ternary-27B-RC1 card,
+ *        "Representation");
+ *   alpha, beta  one scale per (row, group of 128 columns) (scale group 128:
+ *        WAL2-Ternary-27B card, "Архитектура"), stored as fp16 or as a 24-bit
+ *        float (the RC1 card's "24-bit float storage format decoded to FP32");
+ *   U_p, V_p  binary {+1, -1} low-rank factors of up to 4 paths ("WALB2",
+ *        two paths on the RC1 card), each path with fp16 per-rank scales s_p.
+ *
+ * No dense copy of W is ever formed: every kernel reads the packed planes.
+ *
+ * Blob layout (format version 1, little-endian), the byte-level reading of
+ * the pages used by this library:
+ *   header, 256 bytes:
+ *     0 u32 magic 0x314C4157 ("WAL1")  4 u32 version = 1
+ *     8 u32 out  12 u32 in  16 u32 k  20 u32 n_paths  24 u32 rank
+ *     28 u32 trit_fmt  32 u32 scale_fmt  36 u32 row_stride
+ *     40 u64 total_bytes  48 u64 off_codes  56 u64 off_sites  64 u64 off_alpha
+ *     72 u64 off_beta  80 u64 off_V[4]  112 u64 off_U[4]  144 u64 off_s[4]
+ *     176 u64 checksum = sum_i (i+1) * w_i mod 2^64 over the u32 words w_i
+ *         that follow the header;  184..255 zero.
+ *   planes, each at a multiple of 256 bytes, in the order
+ *     codes [out][row_stride]
+ *        2-bit:  row_stride = in/4; trit j of a row in bits 2(j%4)..2(j%4)+1
+ *                of byte j/4; 0 -> 00, +1 -> 01, -1 -> 11 (10 is invalid;
+ *                three of four codes used, WAL2-Ternary-27B card,
+ *                "Что означает битность").
+ *        base-3: five trits per byte (same section), packed continuously
+ *                along the row: byte m = sum_{i<5} (t[5m+i] + 1) * 3^i;
+ *                trits past `in` are zero; row_stride = ceil(in/5) rounded up
+ *                to 16, pad bytes 0x79 (five zero trits); bytes > 242 invalid.
+ *     sites [out][in/128][k]  (k > 0): bits 0-6 position in the group, bit 7
+ *                set = negative sign; ascending, distinct positions.
+ *     alpha [out][in/128], beta [out][in/128] (k > 0): fp16 (2 bytes) or fp24
+ *                (the upper 3 bytes of the fp32 pattern, little-endian).
+ *     per path p: V_p [rank][in/8] bits along `in`, U_p [out][ceil(rank/8)]
+ *                bits along rank, LSB first, set bit = -1, pad bits zero;
+ *                s_p [rank] fp16.
+ *
+ * Conventions for every call:
+ *   - The caller allocates and owns every buffer.  Host pointers are used by
+ *     the packing calls; device pointers (from hipMalloc or torch) by the
+ *     product calls.  The library allocates no memory, never synchronises a
+ *     stream and keeps no pointer after a call returns.
+ *   - Product calls enqueue work on `stream` (a hipStream_t; NULL = the
+ *     default stream) and return.  y / Y is overwritten, never accumulated.
+ *     x / X is read-only and must not overlap y / Y.
+ *   - Every argument, shape, alignment and format check happens before any
+ *     launch and returns a negative wal_status (fail-closed).  A failed
+ *     launch returns WAL_ERR_DEVICE.  A device fault surfaces at the
+ *     caller's next synchronisation of the stream.
+ *   - Calls are reentrant; the library holds no mutable global state.
+ */
+#ifndef WAL_H
+#define WAL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  WAL_OK = 0,
+  WAL_ERR_ARG = -1,         /* NULL pointer or value out of its domain      */
+  WAL_ERR_SHAPE = -2,       /* in % 128 != 0, zero size, rank/paths limits  */
+  WAL_ERR_CODE = -3,        /* invalid trit, site, sign or factor entry     */
+  WAL_ERR_INEXACT = -4,     /* scale not exactly representable when packing */
+  WAL_ERR_BUFFER = -5,      /* buffer too small                              */
+  WAL_ERR_ALIGN = -6,       /* device pointer misaligned                    */
+  WAL_ERR_FORMAT = -7,      /* bad magic, version, layout or checksum       */
+  WAL_ERR_DEVICE = -8,      /* a HIP call or kernel launch failed           */
+  WAL_ERR_UNSUPPORTED = -9  /* valid input that this build does not handle  */
+} wal_status;
+
+enum { WAL_TRIT_2BIT = 0, WAL_TRIT_BASE3 = 1 };
+enum { WAL_SCALE_FP16 = 0, WAL_SCALE_FP24 = 1 };
+enum { WAL_X_F32 = 0, WAL_X_BF16 = 1 };
+enum { WAL_GEMM_AUTO = 0, WAL_GEMM_VALU = 1, WAL_GEMM_MFMA = 2 };
+
+#define WAL_MAX_PATHS 4
+#define WAL_MAX_RANK 64
+#define WAL_HEADER_BYTES 256
+#define WAL_MAX_BATCH 32
+
+/* Shape and storage choice of one matrix. */
+typedef struct {
+  uint32_t out, in;        /* W is out x in; in must be a multiple of 128   */
+  uint32_t k;              /* sites per group: 0, 2, 4 or 8                 */
+  uint32_t n_paths, rank;  /* binary low-rank paths (0..4), rank (1..64)    */
+  uint32_t trit_fmt;       /* WAL_TRIT_2BIT or WAL_TRIT_BASE3               */
+  uint32_t scale_fmt;      /* WAL_SCALE_FP16 or WAL_SCALE_FP24 (alpha, beta) */
+} wal_desc;
+
+/* Host-side view of one blob: its descriptor and plane offsets. */
+typedef struct {
+  wal_desc d;
+  uint32_t row_stride;     /* bytes per row of the code plane               */
+  uint32_t groups;         /* in / 128                                      */
+  uint64_t total_bytes;    /* size of the blob                              */
+  uint64_t off_codes, off_sites, off_alpha, off_beta;
+  uint64_t off_V[WAL_MAX_PATHS], off_U[WAL_MAX_PATHS], off_s[WAL_MAX_PATHS];
+  uint64_t algorithmic_bytes; /* plane bytes a product reads (no header,
+                                 alignment or base-3 row padding)           */
+} wal_info;
+
+/* Launch summary of a grouped plan (filled by wal_grouped_plan). */
+typedef struct {
+  uint32_t n;              /* matrices                                      */
+  uint32_t n_tiles;        /* row tiles of the main kernel                  */
+  uint32_t n_zjobs;        /* (matrix, path, rank) reductions V^T x         */
+  uint32_t rows_per_wave;  /* rows one wavefront streams per tile           */
+  uint32_t x_dtype, trit_fmt;
+  uint32_t grid;           /* workgroups of the main kernel                 */
+  uint32_t reserved;
+  uint64_t plan_bytes;     /* bytes of the plan blob                        */
+  uint64_t algorithmic_bytes; /* sum of the matrices' algorithmic bytes     */
+} wal_grouped_info;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* wal_status_str(int status);
+
+/* Layout of a blob for `desc`: fills *info (offsets, total and algorithmic
+ * bytes).  Defined by the layout above.  Errors: ARG, SHAPE. */
+int wal_packed_size(const wal_desc* desc, wal_info* info);
+
+/* Pack logical arrays (host memory) into a blob at dst (host, dst_bytes >=
+ * info.total_bytes).  Arrays, all row-major:
+ *   T          int8   [out][in]        values in {-1, 0, +1}
+ *   site_pos   uint8  [out][in/128][k] ascending, distinct, < 128  (k > 0)
+ *   site_sign  int8   [out][in/128][k] values in {-1, +1}          (k > 0)
+ *   alpha      float  [out][in/128]
+ *   beta       float  [out][in/128]                                (k > 0)
+ *   U          int8   [n_paths][out][rank]   values in {-1, +1}
+ *   V          int8   [n_paths][in][rank]    values in {-1, +1}
+ *   s          float  [n_paths][rank]
+ * Pointers of absent parts (k == 0: sites, beta; n_paths == 0: U, V, s) may
+ * be NULL.  A scale that its storage format cannot hold exactly is rejected
+ * (WAL_ERR_INEXACT); nothing is rounded.  On success *info (if not NULL)
+ * describes the blob.  Errors: ARG, SHAPE, CODE, INEXACT, BUFFER. */
+int wal_pack(const wal_desc* desc, const int8_t* T, const uint8_t* site_pos,
+             const int8_t* site_sign, const float* alpha, const float* beta,
+             const int8_t* U, const int8_t* V, const float* s,
+             void* dst, size_t dst_bytes, wal_info* info);
+
+/* Parse and check a blob's header and layout (not its planes).
+ * Errors: ARG, BUFFER, FORMAT. */
+int wal_inspect(const void* blob, size_t bytes, wal_info* info);
+
+/* Full check of a host blob: header, layout, checksum and every stored code
+ * (2-bit 10, base-3 byte > 242 or bad padding, unsorted or repeated sites,
+ * non-zero pad bits).  Errors: ARG, BUFFER, FORMAT, CODE. */
+int wal_verify(const void* blob, size_t bytes);
+
+/* Unpack a verified host blob into logical arrays with the shapes of
+ * wal_pack (outputs of absent parts may be NULL).
+ * Errors: those of wal_verify. */
+int wal_unpack(const void* blob, size_t bytes, int8_t* T, uint8_t* site_pos,
+               int8_t* site_sign, float* alpha, float* beta, int8_t* U,
+               int8_t* V, float* s);
+
+/* Device workspace that wal_gemv / wal_gemm_small need for a blob and batch
+ * (the per-path reductions z_p = diag(s_p) V_p^T x).  Errors: ARG, SHAPE. */
+int wal_workspace_size(const wal_info* info, uint32_t batch, size_t* bytes);
+
+/* y = W(x) for one matrix, batch 1.
+ *   info   host view of the blob (from wal_inspect / wal_pack)
+ *   W_dev  the blob in device memory, 256-byte aligned
+ *   x_dev  [in] activations, fp32 or bf16 (x_dtype), 16-byte aligned
+ *   y_dev  [out] fp32 output, 4-byte aligned, overwritten
+ *   ws_dev workspace of wal_workspace_size(info, 1) bytes (may be NULL when
+ *          that size is 0), 16-byte aligned
+ * Errors: ARG, SHAPE, ALIGN, BUFFER, UNSUPPORTED, DEVICE. */
+int wal_gemv(const wal_info* info, const void* W_dev, const void* x_dev, int x_dtype,
+             float* y_dev, void* ws_dev, size_t ws_bytes, void* stream);
+
+/* Y = X W^T for a small batch (F.linear convention).
+ *   X_dev  [batch][ldx] activations (bf16 or fp32), ldx >= in, ldx*elem % 16 == 0
+ *   Y_dev  [batch][ldy] fp32 outputs, ldy >= out, overwritten
+ *   batch  1..WAL_MAX_BATCH
+ *   mode   WAL_GEMM_AUTO, WAL_GEMM_VALU (one decode feeds every batch
+ *          column on the vector ALUs) or WAL_GEMM_MFMA (trits decoded to bf16
+ *          tiles feeding matrix-core MFMA; bf16 X, 2-bit codes only)
+ * Errors: as wal_gemv. */
+int wal_gemm_small(const wal_info* info, const void* W_dev, const void* X_dev, int x_dtype,
+                   uint32_t batch, uint32_t ldx, float* Y_dev, uint32_t ldy, int mode,
+                   void* ws_dev, size_t ws_bytes, void* stream);
+
+/* Grouped products y_i = W_i(x_i), i < n, in one pass over all matrices
+ * (e.g. the 252 body matrices of a 36-layer model).  Two steps:
+ *   1. wal_grouped_plan writes a plan blob into plan_host (host memory of
+ *      plan_bytes, see wal_grouped_plan_size) describing every matrix (device
+ *      pointers of its planes, x_i, y_i, its workspace slot) and the tiling.
+ *   2. The caller copies the plan blob into device memory (plan_dev, 16-byte
+ *      aligned) and calls wal_gemv_grouped, as often as it likes while the
+ *      pointers stay valid.
+ * All matrices share x_dtype and trit_fmt.  ws_dev must hold
+ * wal_grouped_plan_size's ws_bytes.
+ * Errors: ARG, SHAPE, ALIGN, BUFFER, UNSUPPORTED, DEVICE. */
+int wal_grouped_plan_size(uint32_t n, const wal_info* infos, size_t* plan_bytes,
+                          size_t* ws_bytes);
+int wal_grouped_plan(uint32_t n, const wal_info* infos, const void* const* W_dev,
+                     const void* const* x_dev, int x_dtype, float* const* y_dev,
+                     void* ws_dev, size_t ws_bytes, void* plan_host, size_t plan_bytes,
+                     wal_grouped_info* ginfo);
+int wal_gemv_grouped(const wal_grouped_info* ginfo, const void* plan_dev, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* WAL_H */

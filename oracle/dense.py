@@ -64,3 +64,10 @@ def rel_l2(y, y_ref) -> float:
     if den == 0:
         return 0.0 if num == 0 else float("inf")
     return float(num / den)
+
+
+def gemv_rows(blob, x, rows) -> np.ndarray:
+    """y[rows] = W[rows, :] x, decoding only the selected rows."""
+    from .format import unpack_rows
+    W = dense_W(unpack_rows(blob, rows))
+    return W @ np.asarray(x, dtype=np.float64)

@@ -378,3 +378,44 @@ def from_synth(m) -> Logical:
     """Adopt a ``synth.Matrix`` (same fields) as oracle logical arrays."""
     return Logical(m.out, m.inp, m.k, m.trit_fmt, m.scale_fmt, m.T, m.site_pos, m.site_sign,
                    m.alpha, m.beta, m.U, m.V, m.s)
+
+
+def unpack_rows(blob, rows) -> Logical:
+    """Logical arrays of the selected rows only (out = len(rows)); V and s
+    are whole.  Each output y_n depends on row n alone, so the oracle can
+    check sampled outputs of matrices too large to decode in full."""
+    buf = np.frombuffer(bytes(blob) if not isinstance(blob, np.ndarray) else blob, dtype=np.uint8)
+    h = parse_header(buf)
+    if h["magic"] != MAGIC or h["version"] != VERSION:
+        raise FormatError("bad magic or version")
+    out, inp, k, P, r = h["out"], h["in"], h["k"], h["n_paths"], h["rank"]
+    tf, sf = h["trit_fmt"], h["scale_fmt"]
+    rows = np.asarray(rows, dtype=np.int64)
+    if rows.size == 0 or rows.min() < 0 or rows.max() >= out:
+        raise FormatError("row index out of range")
+    lay = layout(out, inp, k, P, r, tf, sf)
+    G = inp // GROUP
+    sb = 2 if sf == SCALE_FP16 else 3
+    stride = row_stride(inp, tf)
+    codes = buf[lay["codes"]: lay["codes"] + out * stride].reshape(out, stride)[rows]
+    T = decode_codes_2bit(codes, inp) if tf == TRIT_2BIT else decode_codes_base3(codes, inp)
+    araw = buf[lay["alpha"]: lay["alpha"] + out * G * sb].reshape(out, G * sb)[rows].reshape(-1)
+    alpha = _scale_values(araw, rows.size * G, sf).reshape(rows.size, G)
+    if k:
+        sraw = buf[lay["sites"]: lay["sites"] + out * G * k].reshape(out, G, k)[rows]
+        pos, sign = decode_sites(sraw)
+        braw = buf[lay["beta"]: lay["beta"] + out * G * sb].reshape(out, G * sb)[rows].reshape(-1)
+        beta = _scale_values(braw, rows.size * G, sf).reshape(rows.size, G)
+    else:
+        pos = np.zeros((rows.size, G, 0), np.uint8)
+        sign = np.zeros((rows.size, G, 0), np.int8)
+        beta = None
+    ub = (r + 7) // 8
+    U = np.zeros((P, rows.size, r), np.int8)
+    V = np.zeros((P, inp, r), np.int8)
+    s = np.zeros((P, r), np.float32)
+    for p in range(P):
+        V[p] = decode_signs(buf[lay[f"V{p}"]: lay[f"V{p}"] + r * (inp // 8)].reshape(r, inp // 8), inp).T
+        U[p] = decode_signs(buf[lay[f"U{p}"]: lay[f"U{p}"] + out * ub].reshape(out, ub)[rows], r)
+        s[p] = _scale_values(buf[lay[f"s{p}"]: lay[f"s{p}"] + 2 * r], r, SCALE_FP16)
+    return Logical(rows.size, inp, k, tf, sf, T, pos, sign, alpha, beta, U, V, s)

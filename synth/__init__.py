@@ -97,12 +97,11 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
 
 
 def _draw_trits(rng: np.random.Generator, shape) -> np.ndarray:
-    # uniform integers in [0, 100): [0, 30) -> 0, [30, 65) -> +1, [65, 100) -> -1
-    u = rng.integers(0, 100, size=shape, dtype=np.uint8)
-    table = np.zeros(100, dtype=np.int8)
-    table[30:65] = 1
-    table[65:] = -1
-    return table[u]
+    # u ~ U[0, 1) in float32: [0, 0.3) -> 0, [0.3, 0.65) -> +1, [0.65, 1) -> -1
+    u = rng.random(size=shape, dtype=np.float32)
+    t = (u >= np.float32(0.3)).astype(np.int8)
+    t -= 2 * (u >= np.float32(0.65)).astype(np.int8)
+    return t
 
 
 def _draw_sites(rng: np.random.Generator, rows: int, groups: int, k: int):

@@ -1,0 +1,238 @@
+"""Python binding of libwal (include/wal.h): argument marshalling only.
+
+Every step of a product runs in the HIP kernels of ``libwal.so``; this module
+converts numpy arrays and torch tensors to pointers and sizes, passes torch's
+current HIP stream, and raises ``WalError`` on a negative status.  torch is
+used for device memory and streams only.  If the library is missing the
+import fails: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libwal.so")
+
+WAL_TRIT_2BIT, WAL_TRIT_BASE3 = 0, 1
+WAL_SCALE_FP16, WAL_SCALE_FP24 = 0, 1
+WAL_X_F32, WAL_X_BF16 = 0, 1
+WAL_GEMM_AUTO, WAL_GEMM_VALU, WAL_GEMM_MFMA = 0, 1, 2
+WAL_MAX_PATHS = 4
+WAL_MAX_BATCH = 32
+
+STATUS = {0: "WAL_OK", -1: "WAL_ERR_ARG", -2: "WAL_ERR_SHAPE", -3: "WAL_ERR_CODE",
+          -4: "WAL_ERR_INEXACT", -5: "WAL_ERR_BUFFER", -6: "WAL_ERR_ALIGN", -7: "WAL_ERR_FORMAT",
+          -8: "WAL_ERR_DEVICE", -9: "WAL_ERR_UNSUPPORTED"}
+
+
+class WalError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)}")
+
+
+class wal_desc(ctypes.Structure):
+    _fields_ = [("out", ctypes.c_uint32), ("in_", ctypes.c_uint32), ("k", ctypes.c_uint32),
+                ("n_paths", ctypes.c_uint32), ("rank", ctypes.c_uint32),
+                ("trit_fmt", ctypes.c_uint32), ("scale_fmt", ctypes.c_uint32)]
+
+
+class wal_info(ctypes.Structure):
+    _fields_ = [("d", wal_desc), ("row_stride", ctypes.c_uint32), ("groups", ctypes.c_uint32),
+                ("total_bytes", ctypes.c_uint64), ("off_codes", ctypes.c_uint64),
+                ("off_sites", ctypes.c_uint64), ("off_alpha", ctypes.c_uint64),
+                ("off_beta", ctypes.c_uint64), ("off_V", ctypes.c_uint64 * 4),
+                ("off_U", ctypes.c_uint64 * 4), ("off_s", ctypes.c_uint64 * 4),
+                ("algorithmic_bytes", ctypes.c_uint64)]
+
+
+class wal_grouped_info(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_uint32), ("n_tiles", ctypes.c_uint32), ("n_zjobs", ctypes.c_uint32),
+                ("rows_per_wave", ctypes.c_uint32), ("x_dtype", ctypes.c_uint32),
+                ("trit_fmt", ctypes.c_uint32), ("grid", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+                ("plan_bytes", ctypes.c_uint64), ("algorithmic_bytes", ctypes.c_uint64)]
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libwal.so is not built ({LIB_PATH}); run python ternary_hybrid_bit_amd/build.py")
+_lib = ctypes.CDLL(LIB_PATH)
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_U32 = ctypes.c_uint32
+_SZ = ctypes.c_size_t
+_sig = {
+    "wal_status_str": (ctypes.c_char_p, [_I]),
+    "wal_packed_size": (_I, [ctypes.POINTER(wal_desc), ctypes.POINTER(wal_info)]),
+    "wal_pack": (_I, [ctypes.POINTER(wal_desc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
+                      ctypes.POINTER(wal_info)]),
+    "wal_inspect": (_I, [_P, _SZ, ctypes.POINTER(wal_info)]),
+    "wal_verify": (_I, [_P, _SZ]),
+    "wal_unpack": (_I, [_P, _SZ, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "wal_workspace_size": (_I, [ctypes.POINTER(wal_info), _U32, ctypes.POINTER(_SZ)]),
+    "wal_gemv": (_I, [ctypes.POINTER(wal_info), _P, _P, _I, _P, _P, _SZ, _P]),
+    "wal_gemm_small": (_I, [ctypes.POINTER(wal_info), _P, _P, _I, _U32, _U32, _P, _U32, _I, _P, _SZ, _P]),
+    "wal_grouped_plan_size": (_I, [_U32, _P, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)]),
+    "wal_grouped_plan": (_I, [_U32, _P, _P, _P, _I, _P, _P, _SZ, _P, _SZ, ctypes.POINTER(wal_grouped_info)]),
+    "wal_gemv_grouped": (_I, [ctypes.POINTER(wal_grouped_info), _P, _P]),
+}
+for _name, (_res, _args) in _sig.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+def _check(st: int, where: str):
+    if st != 0:
+        raise WalError(st, where)
+
+
+def _ptr(a) -> Optional[int]:
+    if a is None:
+        return None
+    if isinstance(a, np.ndarray):
+        return a.ctypes.data
+    return a.data_ptr()  # torch tensor
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def _stream(stream=None) -> Optional[int]:
+    if stream is not None:
+        return int(stream)
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def wal_status_str(status: int) -> str:
+    return _lib.wal_status_str(status).decode()
+
+
+def make_desc(out, inp, k=8, n_paths=0, rank=0, trit_fmt=WAL_TRIT_2BIT, scale_fmt=WAL_SCALE_FP16) -> wal_desc:
+    return wal_desc(out, inp, k, n_paths, rank if n_paths else 0, trit_fmt, scale_fmt)
+
+
+def wal_packed_size(desc: wal_desc) -> wal_info:
+    info = wal_info()
+    _check(_lib.wal_packed_size(ctypes.byref(desc), ctypes.byref(info)), "wal_packed_size")
+    return info
+
+
+def wal_pack(desc: wal_desc, T, site_pos=None, site_sign=None, alpha=None, beta=None,
+             U=None, V=None, s=None):
+    """Pack logical arrays (numpy) into a new uint8 blob; returns (blob, info)."""
+    info = wal_packed_size(desc)
+    dst = np.zeros(info.total_bytes, dtype=np.uint8)
+    arrays = [_c(T, np.int8), _c(site_pos, np.uint8), _c(site_sign, np.int8), _c(alpha, np.float32),
+              _c(beta, np.float32), _c(U, np.int8), _c(V, np.int8), _c(s, np.float32)]
+    out = wal_info()
+    st = _lib.wal_pack(ctypes.byref(desc), *[_ptr(a) for a in arrays], dst.ctypes.data, dst.size,
+                       ctypes.byref(out))
+    _check(st, "wal_pack")
+    return dst, out
+
+
+def pack_matrix(m) -> tuple:
+    """Pack a ``synth.Matrix``-like object (fields T, site_pos, ...)."""
+    desc = make_desc(m.out, m.inp, m.k, m.U.shape[0], m.U.shape[2] if m.U.shape[0] else 0,
+                     m.trit_fmt, m.scale_fmt)
+    k = m.k
+    return wal_pack(desc, m.T, m.site_pos if k else None, m.site_sign if k else None, m.alpha,
+                    m.beta if k else None, m.U if m.U.shape[0] else None,
+                    m.V if m.U.shape[0] else None, m.s if m.U.shape[0] else None)
+
+
+def wal_inspect(blob) -> wal_info:
+    b = np.ascontiguousarray(blob, dtype=np.uint8) if not isinstance(blob, np.ndarray) else blob
+    info = wal_info()
+    _check(_lib.wal_inspect(b.ctypes.data, b.size, ctypes.byref(info)), "wal_inspect")
+    return info
+
+
+def wal_verify(blob) -> int:
+    b = np.frombuffer(blob, dtype=np.uint8) if isinstance(blob, (bytes, bytearray)) else blob
+    return _lib.wal_verify(b.ctypes.data, b.size)
+
+
+def wal_unpack(blob) -> dict:
+    b = np.frombuffer(blob, dtype=np.uint8) if isinstance(blob, (bytes, bytearray)) else blob
+    info = wal_inspect(b)
+    d = info.d
+    G = d.in_ // 128
+    P, r = d.n_paths, d.rank
+    o = {"T": np.zeros((d.out, d.in_), np.int8), "site_pos": np.zeros((d.out, G, d.k), np.uint8),
+         "site_sign": np.zeros((d.out, G, d.k), np.int8), "alpha": np.zeros((d.out, G), np.float32),
+         "beta": np.zeros((d.out, G), np.float32) if d.k else None,
+         "U": np.zeros((P, d.out, r), np.int8), "V": np.zeros((P, d.in_, r), np.int8),
+         "s": np.zeros((P, r), np.float32)}
+    st = _lib.wal_unpack(b.ctypes.data, b.size, *[_ptr(o[k]) if o[k] is not None and o[k].size else None
+                                                   for k in ("T", "site_pos", "site_sign", "alpha", "beta",
+                                                             "U", "V", "s")])
+    _check(st, "wal_unpack")
+    return o
+
+
+def wal_workspace_size(info: wal_info, batch: int = 1) -> int:
+    n = _SZ()
+    _check(_lib.wal_workspace_size(ctypes.byref(info), batch, ctypes.byref(n)), "wal_workspace_size")
+    return n.value
+
+
+def wal_gemv(info: wal_info, W, x, y, ws=None, stream=None):
+    """y = W(x) on the GPU; W, x, y (and ws) are device tensors; y is fp32 [out]."""
+    import torch
+    xdt = WAL_X_BF16 if x.dtype == torch.bfloat16 else WAL_X_F32
+    wsb = ws.numel() * ws.element_size() if ws is not None else 0
+    st = _lib.wal_gemv(ctypes.byref(info), _ptr(W), _ptr(x), xdt, _ptr(y), _ptr(ws), wsb, _stream(stream))
+    _check(st, "wal_gemv")
+    return y
+
+
+def wal_gemm_small(info: wal_info, W, X, Y, mode=WAL_GEMM_AUTO, ws=None, stream=None):
+    """Y = X W^T on the GPU; X [batch][ldx], Y [batch][ldy] device tensors."""
+    import torch
+    xdt = WAL_X_BF16 if X.dtype == torch.bfloat16 else WAL_X_F32
+    wsb = ws.numel() * ws.element_size() if ws is not None else 0
+    st = _lib.wal_gemm_small(ctypes.byref(info), _ptr(W), _ptr(X), xdt, X.shape[0], X.stride(0), _ptr(Y),
+                             Y.stride(0), mode, _ptr(ws), wsb, _stream(stream))
+    _check(st, "wal_gemm_small")
+    return Y
+
+
+def wal_grouped_plan_size(infos: Sequence[wal_info]):
+    arr = (wal_info * len(infos))(*infos)
+    pb, wb = _SZ(), _SZ()
+    _check(_lib.wal_grouped_plan_size(len(infos), arr, ctypes.byref(pb), ctypes.byref(wb)),
+           "wal_grouped_plan_size")
+    return pb.value, wb.value
+
+
+def wal_grouped_plan(infos: Sequence[wal_info], Ws, xs, ys, ws, x_dtype: int):
+    """Build a grouped plan; returns (plan bytes as numpy uint8, wal_grouped_info)."""
+    n = len(infos)
+    arr = (wal_info * n)(*infos)
+    pb, _ = wal_grouped_plan_size(infos)
+    plan = np.zeros(pb, dtype=np.uint8)
+    Wp = (ctypes.c_void_p * n)(*[_ptr(w) for w in Ws])
+    xp = (ctypes.c_void_p * n)(*[_ptr(x) for x in xs])
+    yp = (ctypes.c_void_p * n)(*[_ptr(y) for y in ys])
+    g = wal_grouped_info()
+    wsb = ws.numel() * ws.element_size() if ws is not None else 0
+    st = _lib.wal_grouped_plan(n, arr, Wp, xp, x_dtype, yp, _ptr(ws), wsb, plan.ctypes.data, plan.size,
+                               ctypes.byref(g))
+    _check(st, "wal_grouped_plan")
+    return plan, g
+
+
+def wal_gemv_grouped(ginfo: wal_grouped_info, plan_dev, stream=None):
+    _check(_lib.wal_gemv_grouped(ctypes.byref(ginfo), _ptr(plan_dev), _stream(stream)), "wal_gemv_grouped")
+
+
+def exported_symbols() -> list:
+    return list(_sig)

@@ -1,0 +1,227 @@
+"""CPU tests of libwal's host side through its C ABI.
+
+* the library loads and exports every function include/wal.h declares;
+* the C++ packer writes the same bytes as the oracle's independent numpy
+  packer, on every workload configuration's shapes and formats;
+* wal_unpack inverts wal_pack; wal_packed_size matches the oracle's layout;
+* malformed inputs are rejected with their documented status before use.
+No GPU call is made here.
+"""
+import os
+import re
+import struct
+
+import numpy as np
+import pytest
+
+import synth
+import ternary_hybrid_bit_amd as wal
+from oracle import format as F
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "wal.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(wal_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    import ctypes
+    lib = ctypes.CDLL(wal.LIB_PATH)
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(wal.exported_symbols())
+
+
+def test_status_strings():
+    for code in range(0, -10, -1):
+        assert wal.wal_status_str(code).startswith(wal.STATUS[code])
+
+
+def _same_bytes(m):
+    cpp, info = wal.pack_matrix(m)
+    ref = np.frombuffer(F.pack(F.from_synth(m)), dtype=np.uint8)
+    assert cpp.size == ref.size == info.total_bytes
+    diff = np.nonzero(cpp != ref)[0]
+    assert diff.size == 0, f"first differing byte {diff[:8]}"
+    return cpp, info
+
+
+@pytest.mark.parametrize("cfg,mid", [(0, 0), (1, 0), (3, 0), (4, 0), (4, 1)])
+def test_cpp_pack_matches_oracle_full_configs(cfg, mid):
+    m = synth.config_matrix(cfg, mid)
+    cpp, info = _same_bytes(m)
+    lay = F.layout(m.out, m.inp, m.k, m.n_paths, m.rank, m.trit_fmt, m.scale_fmt)
+    assert info.off_codes == lay["codes"] and info.total_bytes == lay["total"]
+    assert info.algorithmic_bytes == F.algorithmic_bytes(m.out, m.inp, m.k, m.n_paths, m.rank,
+                                                         m.trit_fmt, m.scale_fmt)
+
+
+@pytest.mark.parametrize("mid", [0, 1, 2, 6, 8, 13])
+def test_cpp_pack_matches_oracle_sweep_matrices(mid):
+    """Sweep matrices of each shape (q, k, v, down with and without a path)."""
+    _same_bytes(synth.config_matrix(2, mid))
+
+
+@pytest.mark.parametrize("out,inp,k,P,r,tf,sf", [
+    (1, 128, 0, 0, 0, 0, 0), (3, 384, 2, 1, 3, 0, 1), (5, 640, 4, 3, 9, 1, 0),
+    (7, 1152, 8, 4, 64, 1, 1), (2, 17408, 8, 2, 16, 1, 1), (2, 128, 2, 1, 1, 1, 0),
+])
+def test_cpp_pack_matches_oracle_edge_shapes(out, inp, k, P, r, tf, sf):
+    m = synth.make_matrix(50, out * 7 + inp, out, inp, k=k, n_paths=P, rank=r, trit_fmt=tf, scale_fmt=sf)
+    cpp, _ = _same_bytes(m)
+    back = wal.wal_unpack(cpp)
+    assert np.array_equal(back["T"], m.T)
+    assert np.array_equal(back["alpha"], m.alpha)
+    if k:
+        assert np.array_equal(back["site_pos"], m.site_pos)
+        assert np.array_equal(back["site_sign"], m.site_sign)
+        assert np.array_equal(back["beta"], m.beta)
+    if P:
+        assert np.array_equal(back["U"], m.U) and np.array_equal(back["V"], m.V)
+        assert np.array_equal(back["s"], m.s)
+
+
+def test_packed_size_matches_oracle_layout():
+    for (o, i, k, P, r, tf, sf) in [(12288, 4096, 8, 1, 16, 0, 0), (5120, 17408, 4, 2, 16, 1, 1),
+                                    (256, 512, 8, 0, 0, 0, 0), (17408, 5120, 0, 2, 16, 1, 1)]:
+        info = wal.wal_packed_size(wal.make_desc(o, i, k, P, r, tf, sf))
+        lay = F.layout(o, i, k, P, r, tf, sf)
+        assert info.total_bytes == lay["total"]
+        assert info.off_alpha == lay["alpha"] and info.off_beta == lay["beta"]
+        for p in range(P):
+            assert info.off_V[p] == lay[f"V{p}"] and info.off_U[p] == lay[f"U{p}"]
+            assert info.off_s[p] == lay[f"s{p}"]
+        assert info.row_stride == F.row_stride(i, tf)
+
+
+def _status_of(fn):
+    with pytest.raises(wal.WalError) as e:
+        fn()
+    return e.value.status
+
+
+def test_pack_rejects_bad_logical_inputs():
+    m = synth.make_matrix(51, 0, 4, 256, k=4, n_paths=1, rank=4)
+    d = wal.make_desc(4, 256, 4, 1, 4)
+
+    def pack(**kw):
+        a = dict(T=m.T, site_pos=m.site_pos, site_sign=m.site_sign, alpha=m.alpha, beta=m.beta,
+                 U=m.U, V=m.V, s=m.s)
+        a.update(kw)
+        return wal.wal_pack(d, **a)
+
+    T = m.T.copy(); T[1, 3] = 2
+    assert _status_of(lambda: pack(T=T)) == -3
+    sp = m.site_pos.copy(); sp[0, 0, 1] = sp[0, 0, 0]
+    assert _status_of(lambda: pack(site_pos=sp)) == -3
+    sp = m.site_pos.copy(); sp[0, 0, 3] = 128
+    assert _status_of(lambda: pack(site_pos=sp)) == -3
+    sg = m.site_sign.copy(); sg[2, 1, 0] = 0
+    assert _status_of(lambda: pack(site_sign=sg)) == -3
+    U = m.U.copy(); U[0, 0, 0] = 0
+    assert _status_of(lambda: pack(U=U)) == -3
+    a = m.alpha.copy(); a[0, 0] = 0.1
+    assert _status_of(lambda: pack(alpha=a)) == -4
+    s = m.s.copy(); s[0, 0] = 1e-5 + 1e-9
+    assert _status_of(lambda: pack(s=s)) == -4
+    assert _status_of(lambda: wal.wal_pack(wal.make_desc(4, 200, 4, 1, 4), m.T)) == -2
+    assert _status_of(lambda: wal.wal_pack(wal.make_desc(4, 256, 3, 1, 4), m.T)) == -2
+    assert _status_of(lambda: wal.wal_pack(wal.make_desc(4, 256, 4, 5, 4), m.T)) == -2
+    assert _status_of(lambda: wal.wal_pack(wal.make_desc(4, 256, 4, 1, 65), m.T)) == -2
+    assert _status_of(lambda: wal.wal_pack(d, m.T, None, None, m.alpha, m.beta, m.U, m.V, m.s)) == -1
+
+
+def test_fp24_pack_rejects_low_bits():
+    m = synth.make_matrix(52, 0, 2, 128, k=2, n_paths=0, trit_fmt=1, scale_fmt=1)
+    a = m.alpha.copy()
+    a.view(np.uint32)[0, 0] |= 1
+    d = wal.make_desc(2, 128, 2, 0, 0, 1, 1)
+    assert _status_of(lambda: wal.wal_pack(d, m.T, m.site_pos, m.site_sign, a, m.beta)) == -4
+
+
+def _refresh(blob):
+    b = bytearray(blob)
+    b[176:184] = struct.pack("<Q", F.checksum(bytes(b)))
+    return np.frombuffer(bytes(b), dtype=np.uint8).copy()
+
+
+def test_verify_rejects_corruption():
+    m = synth.make_matrix(53, 0, 4, 256, k=8, n_paths=1, rank=9, trit_fmt=0)
+    blob, info = wal.pack_matrix(m)
+    assert wal.wal_verify(blob) == 0
+    bad = blob.copy(); bad[0] ^= 1
+    assert wal.wal_verify(bad) == -7                                   # magic
+    bad = blob.copy(); bad[4] = 9
+    assert wal.wal_verify(bad) == -7                                   # version
+    bad = blob.copy(); bad[info.off_codes + 5] ^= 0x10
+    assert wal.wal_verify(bad) == -7                                   # checksum
+    assert wal.wal_verify(blob[:-256].copy()) == -5                    # short
+    bad = blob.copy(); bad[info.off_codes] = (bad[info.off_codes] & 0xFC) | 2
+    assert wal.wal_verify(_refresh(bad)) == -3                         # code 10
+    bad = blob.copy(); bad[info.off_sites + 1] = bad[info.off_sites]
+    assert wal.wal_verify(_refresh(bad)) == -3                         # repeated site
+    bad = blob.copy(); bad[info.off_U[0] + 1] |= 0x80                  # pad bit of U (rank 9)
+    assert wal.wal_verify(_refresh(bad)) == -3
+    bad = blob.copy(); bad[40] ^= 1
+    assert wal.wal_verify(bad) == -7                                   # layout field
+    bad = blob.copy(); bad[200] = 1
+    assert wal.wal_verify(bad) == -7                                   # reserved bytes
+
+
+def test_verify_rejects_base3_corruption():
+    m = synth.make_matrix(54, 0, 2, 384, k=0, n_paths=0, trit_fmt=1)
+    blob, info = wal.pack_matrix(m)
+    assert wal.wal_verify(blob) == 0
+    bad = blob.copy(); bad[info.off_codes + 3] = 243
+    assert wal.wal_verify(_refresh(bad)) == -3
+    # 384 trits = 76.8 bytes: byte 76 holds 4 trits + 1 filler digit that must be 1
+    bad = blob.copy(); bad[info.off_codes + 76] = (bad[info.off_codes + 76] % 81)   # filler digit -> 0
+    assert wal.wal_verify(_refresh(bad)) == -3
+    bad = blob.copy(); bad[info.off_codes + 79] = 0                     # row padding
+    assert wal.wal_verify(_refresh(bad)) == -3
+
+
+def test_inspect_reads_header():
+    m = synth.make_matrix(55, 0, 6, 640, k=2, n_paths=2, rank=5, trit_fmt=1, scale_fmt=1)
+    blob, info = wal.pack_matrix(m)
+    got = wal.wal_inspect(blob)
+    assert (got.d.out, got.d.in_, got.d.k, got.d.n_paths, got.d.rank) == (6, 640, 2, 2, 5)
+    assert got.total_bytes == info.total_bytes and got.off_s[1] == info.off_s[1]
+
+
+def test_workspace_size():
+    info = wal.wal_packed_size(wal.make_desc(12288, 4096, 8, 1, 16))
+    assert wal.wal_workspace_size(info, 1) == 256
+    assert wal.wal_workspace_size(info, 32) == 4 * 16 * 32
+    assert wal.wal_workspace_size(wal.wal_packed_size(wal.make_desc(256, 512, 8)), 1) == 0
+    with pytest.raises(wal.WalError):
+        wal.wal_workspace_size(info, 33)
+
+
+def test_product_calls_check_arguments_before_any_launch():
+    """Host-side checks of the product entry points return their status
+    before touching the GPU (the pointers below are never dereferenced)."""
+    import ctypes
+    info = wal.wal_packed_size(wal.make_desc(64, 256, 8, 1, 16))
+    lib = wal._lib
+    W, x, y, ws = 0x10000, 0x20000, 0x30000, 0x40000
+    ok_args = (ctypes.byref(info), W, x, wal.WAL_X_BF16, y, ws, 256, None)
+    assert lib.wal_gemv(ctypes.byref(info), W + 16, x, 1, y, ws, 256, None) == -6     # W not 256-aligned
+    assert lib.wal_gemv(ctypes.byref(info), W, x + 2, 1, y, ws, 256, None) == -6      # x not 16-aligned
+    assert lib.wal_gemv(ctypes.byref(info), W, x, 1, y + 2, ws, 256, None) == -6      # y not 4-aligned
+    assert lib.wal_gemv(ctypes.byref(info), W, x, 1, y, ws, 8, None) == -5            # workspace too small
+    assert lib.wal_gemv(ctypes.byref(info), W, x, 1, y, None, 0, None) == -1          # workspace missing
+    assert lib.wal_gemv(ctypes.byref(info), W, x, 7, y, ws, 256, None) == -1          # dtype
+    assert lib.wal_gemv(ctypes.byref(info), None, x, 1, y, ws, 256, None) == -1
+    assert lib.wal_gemv(ctypes.byref(info), W, x, 1, x + 64, ws, 256, None) == -1     # y overlaps x
+    bad = wal.wal_info.from_buffer_copy(info)
+    bad.off_alpha += 256
+    assert lib.wal_gemv(ctypes.byref(bad), *ok_args[1:]) == -7                        # inconsistent info
+    assert lib.wal_gemm_small(ctypes.byref(info), W, x, 1, 0, 256, y, 64, 0, ws, 256, None) == -1
+    assert lib.wal_gemm_small(ctypes.byref(info), W, x, 1, 33, 256, y, 64, 0, ws, 256, None) == -1
+    assert lib.wal_gemv_grouped(None, 0x1000, None) == -1

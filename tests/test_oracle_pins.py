@@ -422,3 +422,19 @@ def test_rejections():
     L4.T[0, 0] = 2
     with pytest.raises(F.FormatError):
         F.pack(L4)
+
+
+def test_unpack_rows_equals_full_unpack():
+    for tf, sf, k, P in [(0, 0, 8, 1), (1, 1, 2, 2), (0, 1, 0, 0)]:
+        L = tiny(9, 384, k, P, 5, tf, sf)
+        blob = F.pack(L)
+        rows = [0, 3, 8, 3]
+        sub = F.unpack_rows(blob, rows)
+        full = F.unpack(blob)
+        for f in ["T", "site_pos", "site_sign", "alpha", "U"]:
+            a = getattr(full, f)
+            want = a[:, rows] if f == "U" else a[rows]
+            assert np.array_equal(getattr(sub, f), want), f
+        assert np.array_equal(sub.V, full.V) and np.array_equal(sub.s, full.s)
+        x = np.random.default_rng(8).standard_normal(384)
+        np.testing.assert_allclose(D.gemv_rows(blob, x, rows), D.gemv(blob, x)[rows], rtol=1e-13, atol=1e-15)
