@@ -1,0 +1,182 @@
+"""Benchmark: packed ternary-hybrid GEMV sweep over the 252 Qwen3-8B-shaped
+body matrices at batch 1 on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step = one grouped product y_i = W_i(x_i) over all 252 matrices (36
+layers x q, k, v, o, gate, up, down; sparse k = 8 on all, a rank-16 binary
+path on 213 of them; bf16 activations, fp32 outputs), launched through the C
+ABI on torch's current HIP stream.  The packed weights (about 2.39 GB) are
+resident in HBM before timing starts; the working set is far larger than the
+256 MB Infinity Cache, so every step streams the weights from HBM.
+
+Prints one JSON line with the contract's fields plus ``roofline`` (HIP-event
+timing of the steps on the launch stream, algorithmic packed bytes per step,
+against the 8 TB/s HBM peak) and ``cpu_baseline`` (the float64 CPU oracle
+timed on a bounded sample of the same workload, on this host).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "packed-weight GB/s & % of HBM peak, 252-matrix Qwen3-8B-shape GEMV sweep, batch 1"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sweep_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "ternary_hybrid_bit_amd", "csrc", f)
+                  for f in ("wal_gpu.hip", "wal_internal.h")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
+    when the kernel sources changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(items, budget_s: float):
+    """Time the oracle (unpack -> dense float64 W -> W @ x) on whole matrices
+    of the sweep, in order, until about ``budget_s`` seconds of CPU work."""
+    from oracle import dense as D
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    done_bytes, t_total, n = 0, 0.0, 0
+    for blob, info, xb in items:
+        x = synth.bf16_bits_to_f32(xb)
+        t0 = time.perf_counter()
+        D.gemv(blob, x)
+        t_total += time.perf_counter() - t0
+        done_bytes += info.algorithmic_bytes
+        n += 1
+        if t_total >= budget_s:
+            break
+    return {"value": done_bytes / t_total / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n} of 252 sweep matrices ({done_bytes / 1e9:.3f} GB packed), "
+                      f"{t_total:.1f} s: numpy unpack + dense float64 W + W@x per matrix"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after timing, run one fp32 elementwise copy of this many MiB (counter calibration)")
+    ap.add_argument("--layers", type=int, default=36, help=argparse.SUPPRESS)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the sweep's sharding across GPUs is described in DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import ternary_hybrid_bit_amd as wal
+    from ternary_hybrid_bit_amd import workloads
+
+    t0 = time.time()
+    items = workloads.sweep(layers=args.layers)
+    print(f"[bench] generated and packed {len(items)} matrices in {time.time() - t0:.1f} s", file=sys.stderr,
+          flush=True)
+    dev = torch.device("cuda:0")
+    Ws = [torch.from_numpy(b).to(dev) for b, _, _ in items]
+    xs = [torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16) for _, _, xb in items]
+    ys = [torch.empty(i.d.out, dtype=torch.float32, device=dev) for _, i, _ in items]
+    infos = [i for _, i, _ in items]
+    _, wsb = wal.wal_grouped_plan_size(infos)
+    ws = torch.zeros(max(wsb, 4) // 4, dtype=torch.float32, device=dev)
+    plan, g = wal.wal_grouped_plan(infos, Ws, xs, ys, ws, wal.WAL_X_BF16)
+    plan_dev = torch.from_numpy(plan).to(dev)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        wal.wal_gemv_grouped(g, plan_dev)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        wal.wal_gemv_grouped(g, plan_dev)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t_wall
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / args.steps
+    print(f"[bench] {args.steps} steps: {ms_step:.4f} ms/step (events), wall {wall_s * 1e3 / args.steps:.4f} ms",
+          file=sys.stderr, flush=True)
+
+    if args.copy_mib:
+        # a plain copy kernel of known size: reads and writes copy_mib MiB once
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+    alg_bytes = int(g.algorithmic_bytes)
+    weights = sum(int(i.d.out) * int(i.d.in_) for i in infos)
+    gbs = alg_bytes / (ms_step * 1e-3) / 1e9
+    traffic = stored_traffic()
+    out = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "qwen3-8b-body-sweep-252-gemv-batch1", "matrices": len(items),
+                   "layers": args.layers, "batch": 1, "x_dtype": "bf16", "y_dtype": "f32",
+                   "format": "2-bit T + sparse k8 + fp16 alpha/beta per 128 + rank-16 WALB2 on 213/252",
+                   "packed_bytes": alg_bytes, "weights": weights},
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "weights_per_s": round(weights / (ms_step * 1e-3), 1),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "k_gemv2_grouped (+ k_z_grouped pre-pass, inside the timed step)",
+                     "bytes_per_launch": alg_bytes},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(items, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
