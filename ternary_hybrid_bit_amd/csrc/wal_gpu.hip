@@ -4,30 +4,40 @@
 //     y = (alpha * T + beta * R) x + sum_p U_p diag(s_p) V_p^T x
 // computed straight from the packed planes described in include/wal.h.
 //
-// Kernel design (one 64-wide wavefront streams whole rows):
-//  * Codes.  Each lane owns 64 consecutive columns of a 4096-column pass and
-//    loads its 16 bytes of 2-bit codes per row with one 128-bit load, so a
-//    wavefront reads a 1 KB row segment fully coalesced.  A code keeps its
-//    magnitude bit below its sign bit, so shifting a code pair to bits 14-15
-//    and 30-31 and masking with 0xC000C000 yields a packed bf16 pair whose
-//    halves are +-2.0 or 0: the trits become sign-selected copies of x with
-//    no multiply and no table.  v_dot2c_f32_bf16 then adds both halves into
-//    an fp32 accumulator (products by +-2 and 0 are exact).  The lane's x
-//    stays in registers for the whole pass, pre-arranged in the same pairs.
-//  * Sites.  A per-workgroup LDS table holds +x and -x for every position of
-//    every group of the pass ([group][256] floats), so a site byte (7-bit
-//    position, sign in bit 7) indexes its signed value directly.
-//  * Scales.  alpha multiplies the lane's ternary partial and beta its site
-//    partial once per row and group, in fp32 (fp16 or fp24 decoded in
-//    registers).
-//  * Low rank.  A pre-pass computes z = diag(s) V^T x per path and rank; in
-//    the main pass lane t adds +-z[t] by the row's U bit before the row's
-//    wavefront reduction (DPP adds, no LDS).
-//  * Rows are reduced with DPP and their totals parked in lane (row - n0) of
-//    one register, so y is stored with one coalesced write per wavefront.
+// Two kernels per product:
+//  * k_z_*: the binary low-rank reductions z_p[r] = s_p[r] * sum_j (-1)^{V bit} x_j,
+//    kZTerms terms per workgroup, written to the caller's workspace.
+//  * k_stream_*: one streaming pass over the packed planes.  Every workgroup
+//    owns a contiguous range of rows of one or more matrices (for grouped
+//    products the host splits the total packed bytes evenly over a grid that
+//    fits the GPU at once, so no workgroup waits for another).  Inside a
+//    range, the 4 wavefronts take batches of RB rows in turn:
+//      - codes: each lane owns 64 consecutive columns of a 4096-column pass
+//        and reads its 16 bytes of 2-bit codes per row with one buffer load,
+//        so a wavefront reads a 1 KB row segment fully coalesced.  Row
+//        offsets live in scalar registers (buffer soffset), so stepping rows
+//        costs no vector instructions.  The loads of the next batch are in
+//        flight while the current batch is computed.
+//      - trits: a code keeps its magnitude bit below its sign bit, so shifting
+//        a dword to put a code pair at bits 14-15 and 30-31 and masking with
+//        0xC000C000 gives a bf16 pair whose halves are +-2.0 or 0: the trits
+//        become sign-selected copies of x with no multiply and no table, and
+//        v_dot2_f32_bf16 adds both into fp32 (products by +-2 and 0 are
+//        exact).  The lane's x stays in registers for the whole pass.
+//      - sites: an LDS table per workgroup holds +2x and -2x for every
+//        position of every group of the pass ([group][256] floats), so a site
+//        byte (7-bit position, sign in bit 7) indexes its signed value.
+//      - scales: alpha multiplies the lane's ternary partial and beta its site
+//        partial once per row in fp32 (fp16 scales feed v_fma_mix directly).
+//      - rows: the RB row partials of a lane are reduced across the
+//        wavefront with one transposed butterfly (permlane swaps and DPP), so
+//        each row's total lands in 64/RB lanes; those lanes add the low-rank
+//        term sum_t (-1)^{U bit} z_t (one term per lane) and one of them
+//        stores y.  Matrices wider than one pass accumulate y pass by pass.
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
+#include <atomic>
 #include <cstring>
 
 #include "wal_internal.h"
@@ -35,57 +45,112 @@
 using namespace wal;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 namespace {
 
-constexpr uint32_t kRowsMax = 64;   // rows one wavefront parks in a register
-
 // ---------------------------------------------------------------------------
-// Wavefront reduction: four DPP steps sum each row of 16 lanes, two row
-// broadcasts fold the rows into lane 63.
-template <int CTRL, int ROWMASK>
-__device__ __forceinline__ float dpp_term(float v) {
+// Cross-lane helpers.
+
+template <int CTRL, int ROWMASK = 0xF>
+__device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWMASK, 0xF, false));
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-  v += dpp_term<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
-  v += dpp_term<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
-  v += dpp_term<0x141, 0xF>(v);  // row_half_mirror
-  v += dpp_term<0x140, 0xF>(v);  // row_mirror
-  v += dpp_term<0x142, 0xA>(v);  // row_bcast:15 into rows 1, 3
-  v += dpp_term<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
+
+__device__ __forceinline__ void swap32_add(float& a, float& b) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  a = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap16_add(float& a, float& b) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  a = __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// One butterfly level on lane bit `BIT` (3, 2, 1 or 0) for R values: pairs
+// v[j] and v[j + H] (H = R >> (6 - BIT)), lanes with the bit set keep the
+// second of the pair.
+template <int BIT, int CTRL, int R>
+__device__ __forceinline__ void tlevel(float (&v)[R], int lane) {
+  constexpr int H = R >> (6 - BIT);
+  if constexpr (H >= 1) {
+    const bool hi = (lane >> BIT) & 1;
+#pragma unroll
+    for (int j = 0; j < H; ++j) {
+      const float a = hi ? v[j + H] : v[j];
+      const float b = hi ? v[j] : v[j + H];
+      v[j] = a + dpp<CTRL>(b);
+    }
+  } else {
+    v[0] += dpp<CTRL>(v[0]);
+  }
+}
+
+// Transposed reduction of R per-lane values (R a power of two <= 64): returns,
+// in lane l, the wavefront total of value (l >> (6 - log2 R)).
+template <int R>
+__device__ __forceinline__ float treduce(float (&v)[R], int lane) {
+  if constexpr (R >= 2) {
+#pragma unroll
+    for (int j = 0; j < R / 2; ++j) swap32_add(v[j], v[j + R / 2]);
+  } else {
+    float w = v[0];
+    swap32_add(v[0], w);
+  }
+  if constexpr (R >= 4) {
+#pragma unroll
+    for (int j = 0; j < R / 4; ++j) swap16_add(v[j], v[j + R / 4]);
+  } else {
+    float w = v[0];
+    swap16_add(v[0], w);
+  }
+  tlevel<3, 0x128>(v, lane);   // row_ror:8
+  tlevel<2, 0x141>(v, lane);   // row_half_mirror
+  tlevel<1, 0x4E>(v, lane);    // quad_perm [2,3,0,1]
+  tlevel<0, 0xB1>(v, lane);    // quad_perm [1,0,3,2]
+  return v[0];
+}
+
+// Sum over aligned groups of L lanes (L = 8, 16, 32 or 64); every lane of a
+// group receives the group total.
+template <int L>
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  v += dpp<0x141>(v);
+  if constexpr (L >= 16) v += dpp<0x140>(v);   // row_mirror
+  if constexpr (L >= 32) { float w = v; swap16_add(v, w); }
+  if constexpr (L >= 64) { float w = v; swap32_add(v, w); }
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 // ---------------------------------------------------------------------------
-// Scales: fp16, or fp24 = the upper 24 bits of an fp32 pattern.
-__device__ __forceinline__ uint32_t load_scale_raw(const uint8_t* p, uint32_t sfmt) {
-  if (sfmt == WAL_SCALE_FP16) return *reinterpret_cast<const uint16_t*>(p);
-  return (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16);
+// Buffer loads: a resource over one plane, a per-lane offset and a per-row
+// scalar offset.
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ float decode_scale(uint32_t raw, uint32_t sfmt) {
-  if (sfmt == WAL_SCALE_FP16) return __half2float(__ushort_as_half((unsigned short)raw));
-  return __uint_as_float(raw << 8);
-}
-__device__ __forceinline__ uint32_t scale_bytes(uint32_t sfmt) { return sfmt == WAL_SCALE_FP16 ? 2u : 3u; }
 
 // Activation element as fp32.
 template <int XT>
 __device__ __forceinline__ float xval(const void* x, uint32_t i) {
-  if (XT == WAL_X_F32) return reinterpret_cast<const float*>(x)[i];
+  if constexpr (XT == WAL_X_F32) return reinterpret_cast<const float*>(x)[i];
   return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(x)[i] << 16);
 }
 
 // ---------------------------------------------------------------------------
-// A lane's 64 activation columns for one pass, held in registers.
+// A lane's 64 activation columns of one pass, held in registers.
 template <int XT> struct XLane;
 
 template <> struct XLane<WAL_X_BF16> {
   // p[8d + i] = bf16 pair (x[c + 16d + i], x[c + 16d + 8 + i]): the pair of
   // columns whose codes sit at bits 2i and 2i + 16 of the lane's dword d.
   uint32_t p[32];
-  static constexpr float kScale = 0.5f;   // the decoded trits are +-2
+  static constexpr float kHalf = 0.5f;   // decoded trits and table entries are 2x
 
   __device__ __forceinline__ void load(const void* x, uint32_t c, bool active) {
     if (!active) {
@@ -97,7 +162,7 @@ template <> struct XLane<WAL_X_BF16> {
     uint32_t w[32];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      uint4 v = src[q];
+      const uint4 v = src[q];
       w[4 * q] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
     }
 #pragma unroll
@@ -112,24 +177,24 @@ template <> struct XLane<WAL_X_BF16> {
   }
 
   // 2 * sum_j T_j x_j over the lane's 64 columns of one row.
-  __device__ __forceinline__ float dot(const uint4& c) const {
-    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  __device__ __forceinline__ float dot(const u32x4_t& c) const {
+    float a0 = 0.f, a1 = 0.f;
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const uint32_t op = (w[d] << (14 - 2 * i)) & 0xC000C000u;
-        acc[d] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, op),
-                                                 __builtin_bit_cast(bf16x2_t, p[8 * d + i]), acc[d], false);
+        const uint32_t op = (c[d] << (14 - 2 * i)) & 0xC000C000u;
+        float& a = d < 2 ? a0 : a1;
+        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, op),
+                                            __builtin_bit_cast(bf16x2_t, p[8 * d + i]), a, false);
       }
-    return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    return a0 + a1;
   }
 };
 
 template <> struct XLane<WAL_X_F32> {
   float f[64];
-  static constexpr float kScale = 1.0f;
+  static constexpr float kHalf = 1.0f;
 
   __device__ __forceinline__ void load(const void* x, uint32_t c, bool active) {
     if (!active) {
@@ -140,219 +205,342 @@ template <> struct XLane<WAL_X_F32> {
     const float4* src = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + c);
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      float4 v = src[q];
+      const float4 v = src[q];
       f[4 * q] = v.x; f[4 * q + 1] = v.y; f[4 * q + 2] = v.z; f[4 * q + 3] = v.w;
     }
   }
 
   // sum_j T_j x_j: sign-extend each 2-bit code to {-1, 0, +1} and accumulate.
-  __device__ __forceinline__ float dot(const uint4& c) const {
-    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  __device__ __forceinline__ float dot(const u32x4_t& c) const {
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int t = (int)(w[d] << (30 - 2 * i)) >> 30;
+        const int t = (int)(c[d] << (30 - 2 * i)) >> 30;
         acc[d] = __builtin_fmaf((float)t, f[16 * d + i], acc[d]);
       }
     return (acc[0] + acc[1]) + (acc[2] + acc[3]);
   }
 };
 
-// ---------------------------------------------------------------------------
-// Per-lane low-rank terms: lane t (+64 j) owns term t = p * rank + r.
-struct LowRank {
-  float z[4];
-  const uint8_t* u[4];
-  uint32_t bit[4];
-  uint32_t ub;      // bytes per row of U
-};
-
-__device__ __forceinline__ void lowrank_setup(const MatDev& d, int lane, LowRank& lr) {
-  lr.ub = (d.rank + 7) / 8;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t t = lane + 64 * j;
-    lr.z[j] = 0.f;
-    lr.u[j] = nullptr;
-    lr.bit[j] = 0;
-    if (t < d.terms) {
-      const uint32_t p = t / d.rank, r = t % d.rank;
-      lr.z[j] = d.z[t];
-      lr.u[j] = d.U[p] + r / 8;
-      lr.bit[j] = r % 8;
-    }
-  }
+// p-th entry of a per-path pointer array, without dynamic indexing (which
+// would move the descriptor to scratch memory).
+__device__ __forceinline__ const uint8_t* path_ptr(const uint8_t* const (&a)[WAL_MAX_PATHS], uint32_t p) {
+  return p == 0 ? a[0] : p == 1 ? a[1] : p == 2 ? a[2] : a[3];
 }
 
 // ---------------------------------------------------------------------------
-// Row data of one row and one pass, loaded ahead of its use.
-struct RowData {
-  uint4 c;
-  uint32_t s;       // site bytes of this lane
-  uint32_t a, b;    // raw alpha, beta
-  uint32_t u;       // U bits of this lane's low-rank terms (bit j = term j)
+// Scales: fp16 (2 bytes) or fp24 (the upper 3 bytes of an fp32 pattern).
+
+template <int SF>
+__device__ __forceinline__ uint32_t load_scale(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  if constexpr (SF == WAL_SCALE_FP16) return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+  const uint32_t b0 = __builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
+  const uint32_t b1 = __builtin_amdgcn_raw_buffer_load_b8(r, voff + 1, soff, 0);
+  const uint32_t b2 = __builtin_amdgcn_raw_buffer_load_b8(r, voff + 2, soff, 0);
+  return b0 | (b1 << 8) | (b2 << 16);
+}
+
+// scale * v + acc in fp32.
+template <int SF>
+__device__ __forceinline__ float scale_fma(uint32_t raw, float v, float acc) {
+  if constexpr (SF == WAL_SCALE_FP16)
+    return __builtin_fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)raw), v, acc);
+  return __builtin_fmaf(__uint_as_float(raw << 8), v, acc);
+}
+
+__device__ __forceinline__ float f16_at(const uint8_t* p, uint32_t i) {
+  return (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(p)[i]);
+}
+
+// ---------------------------------------------------------------------------
+// Shared memory of the streaming kernels.
+struct StreamSmem {
+  float tbl[32 * 256];   // [group of the pass][site byte] -> +-2x (bf16) or +-x (fp32)
+  float z[kMaxTerms];    // low-rank reductions of the current matrix
 };
 
-template <int K>
-struct SiteMap {
-  static constexpr int SPL = K >= 4 ? 4 : K;   // sites per lane
-  static constexpr int LPG = K == 8 ? 2 : 1;   // lanes per group
-};
-
-template <int XT, int K>
-__device__ __forceinline__ void pass_rows_2bit(const MatDev& d, uint32_t n0, int nrows, uint32_t pass,
-                                               uint32_t Gp, bool last, const float* __restrict__ tbl,
-                                               const XLane<XT>& xl, const LowRank& lr, int lane,
-                                               float& rowacc) {
-  using SM = SiteMap<K>;
-  const uint32_t G = d.groups;
-  const uint32_t sb = scale_bytes(d.scale_fmt);
-  const uint32_t g0 = pass * (kPass2bit / 128);
-  const bool code_on = (uint32_t)lane < 2 * Gp;          // 64 columns per lane
-  const uint32_t tg = lane >> 1;                          // group of the lane's codes
-  const bool site_on = K > 0 && (uint32_t)lane < Gp * SM::LPG;
-  const uint32_t sg = K > 0 ? lane / SM::LPG : 0;         // group of the lane's sites
-  const uint32_t sofs = K > 0 ? sg * K + (lane % SM::LPG) * SM::SPL : 0;
-
-  auto load = [&](uint32_t n) {
-    RowData r;
-    r.c = make_uint4(0, 0, 0, 0);
-    r.s = 0; r.a = 0; r.b = 0; r.u = 0;
-    if (code_on) {
-      r.c = *reinterpret_cast<const uint4*>(d.codes + (size_t)n * d.row_stride + pass * (kPass2bit / 4) + 16 * lane);
-      r.a = load_scale_raw(d.alpha + ((size_t)n * G + g0 + tg) * sb, d.scale_fmt);
-    }
-    if (K > 0 && site_on) {
-      const uint8_t* sp = d.sites + ((size_t)n * G + g0) * K + sofs;
-      if (SM::SPL == 4) r.s = *reinterpret_cast<const uint32_t*>(sp);
-      else r.s = *reinterpret_cast<const uint16_t*>(sp);
-      r.b = load_scale_raw(d.beta + ((size_t)n * G + g0 + sg) * sb, d.scale_fmt);
-    }
-    if (last) {
+// Signed table of one 4096-column pass; groups past the pass width are zero.
+template <int XT>
+__device__ __forceinline__ void build_table(const void* x, uint32_t col0, uint32_t pw, float* tbl) {
+  constexpr float kT = XT == WAL_X_BF16 ? 2.0f : 1.0f;
+  for (uint32_t e = threadIdx.x; e < 32 * 16; e += kThreads) {
+    const uint32_t g = e >> 4, q = e & 15;   // 8 columns per item
+    float v[8];
+    if (g * 128 < pw) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (lr.u[j]) r.u |= (uint32_t)((lr.u[j][(size_t)n * lr.ub] >> lr.bit[j]) & 1u) << j;
+      for (int i = 0; i < 8; ++i) v[i] = kT * xval<XT>(x, col0 + g * 128 + q * 8 + i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = 0.f;
     }
-    return r;
+    float4* pos = reinterpret_cast<float4*>(tbl + g * 256 + q * 8);
+    float4* neg = reinterpret_cast<float4*>(tbl + g * 256 + 128 + q * 8);
+    pos[0] = make_float4(v[0], v[1], v[2], v[3]);
+    pos[1] = make_float4(v[4], v[5], v[6], v[7]);
+    neg[0] = make_float4(-v[0], -v[1], -v[2], -v[3]);
+    neg[1] = make_float4(-v[4], -v[5], -v[6], -v[7]);
+  }
+}
+
+// Packed data of one row for one lane.
+struct RowRaw {
+  u32x4_t c;        // 16 bytes of 2-bit codes (64 trits)
+  uint32_t s;       // site bytes (k / 2 of them)
+  uint32_t a, b;    // raw alpha, beta of the lane's group
+};
+
+template <int RB>
+struct Batch {
+  RowRaw r[RB];
+  float yprev;      // partial y of earlier passes (row of this lane)
+  uint32_t u;       // U byte holding this lane's low-rank sign bit
+};
+
+// Per-pass lane constants of the 2-bit stream.
+struct Lane2 {
+  __amdgpu_buffer_rsrc_t rc, rs, ra, rb;
+  uint32_t vc, vs, va;        // lane offsets within a row of each plane
+  uint32_t sc, ss, sa;        // row strides (bytes) of each plane
+  const float* tb;            // the lane's group in the site table
+  const uint8_t* up;          // U byte of the lane's first low-rank term (row 0)
+  uint32_t ub, ubit;          // bytes per U row, bit of the term in its byte
+  bool uon;                   // the lane owns a low-rank term
+};
+
+template <int XT, int SF, int K, int RB>
+__device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0, uint32_t row1, uint32_t pass,
+                                                 uint32_t npass, const XLane<XT>& xl, const StreamSmem& sm) {
+  constexpr int LOG = ilog2(RB);
+  constexpr int SH = 6 - LOG;        // lane >> SH = row of the batch after the reduction
+  constexpr int LPR = 64 >> LOG;     // lanes per row after the reduction
+  constexpr uint32_t SB = SF == WAL_SCALE_FP16 ? 2 : 3;
+  const int lane = threadIdx.x & 63;
+  const uint32_t wave = wave_id();
+  const uint32_t nb = (row1 - row0 + RB - 1) / RB;
+  uint32_t b = wave;
+  if (b >= nb) return;
+
+  const uint32_t pw = min(kPass2bit, d.in - pass * kPass2bit);
+  const uint32_t Gp = pw / 128, g0 = pass * (kPass2bit / 128), G = d.groups;
+  const bool on = (uint32_t)lane < 2 * Gp;
+  const uint32_t gl = on ? (uint32_t)lane >> 1 : 0;
+  const bool first = pass == 0, last = pass + 1 == npass;
+
+  Lane2 L;
+  L.rc = rsrc(d.codes, d.blob_bytes);
+  L.vc = pass * (kPass2bit / 4) + 16 * (on ? lane : 0);
+  L.sc = d.row_stride;
+  const uint32_t left_a = d.blob_bytes - (uint32_t)(d.alpha - d.codes);
+  L.ra = rsrc(d.alpha, left_a);
+  L.va = (g0 + gl) * SB;
+  L.sa = G * SB;
+  if constexpr (K > 0) {
+    L.rs = rsrc(d.sites, d.blob_bytes - (uint32_t)(d.sites - d.codes));
+    L.rb = rsrc(d.beta, d.blob_bytes - (uint32_t)(d.beta - d.codes));
+    L.vs = (g0 + gl) * K + (lane & 1) * (K / 2);
+    L.ss = G * K;
+  }
+  L.tb = sm.tbl + ((uint32_t)lane >> 1) * 256;
+  const uint32_t ti = lane & (LPR - 1);
+  L.uon = last && ti < d.terms;
+  L.ub = (d.rank + 7) / 8;
+  L.up = d.codes;    // any readable byte for lanes without a low-rank term
+  L.ubit = 0;
+  if (L.uon) {
+    const uint32_t p = ti / d.rank, r = ti % d.rank;
+    L.up = path_ptr(d.U, p) + r / 8;
+    L.ubit = r & 7;
+  }
+  // y and the U bytes go through buffer instructions too (a generic pointer
+  // would need flat instructions, whose completion the compiler tracks more
+  // conservatively): U offsets are taken from the codes plane's resource,
+  // which spans the rest of the blob.
+  const __amdgpu_buffer_rsrc_t ry_rs = rsrc(d.y, d.out * 4);
+  const uint32_t uoff = (uint32_t)(L.up - d.codes);
+  const uint32_t ustride = L.uon ? L.ub : 0;
+
+  // Every load is unconditional and in bounds (rows past the range repeat
+  // the last row of the range), so the compiler never has to merge loaded
+  // and unloaded values, which would make it wait for every load in flight.
+  auto load_batch = [&](uint32_t bb) {
+    Batch<RB> B;
+    const uint32_t base = row0 + bb * RB;
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      const uint32_t row = min(base + i, row1 - 1);
+      RowRaw& r = B.r[i];
+      r.c = __builtin_amdgcn_raw_buffer_load_b128(L.rc, L.vc, row * L.sc, 0);
+      r.a = load_scale<SF>(L.ra, L.va, row * L.sa);
+      if constexpr (K == 8) r.s = __builtin_amdgcn_raw_buffer_load_b32(L.rs, L.vs, row * L.ss, 0);
+      if constexpr (K == 4) r.s = __builtin_amdgcn_raw_buffer_load_b16(L.rs, L.vs, row * L.ss, 0);
+      if constexpr (K == 2) r.s = __builtin_amdgcn_raw_buffer_load_b8(L.rs, L.vs, row * L.ss, 0);
+      if constexpr (K > 0) r.b = load_scale<SF>(L.rb, L.va, row * L.sa);
+    }
+    const uint32_t ry = min(base + ((uint32_t)lane >> SH), row1 - 1);
+    B.yprev = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ry_rs, ry * 4, 0, 0));
+    B.u = __builtin_amdgcn_raw_buffer_load_b8(L.rc, uoff + ry * ustride, 0, 0);
+    // keep the scheduler from sinking these loads into the next computation
+    __builtin_amdgcn_sched_barrier(0);
+    return B;
   };
 
-  RowData cur = load(n0);
-  for (int i = 0; i < nrows; ++i) {
-    RowData nxt;
-    if (i + 1 < nrows) nxt = load(n0 + i + 1);
-    float part = 0.f;
-    if (code_on) part = XLane<XT>::kScale * decode_scale(cur.a, d.scale_fmt) * xl.dot(cur.c);
-    if (K > 0 && site_on) {
-      float accR = 0.f;
+  auto finish_batch = [&](const Batch<RB>& B, uint32_t bb) {
+    float acc[RB];
 #pragma unroll
-      for (int j = 0; j < SM::SPL; ++j) accR += tbl[sg * 256 + ((cur.s >> (8 * j)) & 0xFFu)];
-      part = __builtin_fmaf(decode_scale(cur.b, d.scale_fmt), accR, part);
-    }
-    if (last) {
+    for (int i = 0; i < RB; ++i) {
+      const RowRaw& r = B.r[i];
+      float v = scale_fma<SF>(r.a, xl.dot(r.c), 0.f);
+      if constexpr (K > 0) {
+        float sr = L.tb[r.s & 0xFFu];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (lr.u[j]) part += ((cur.u >> j) & 1u) ? -lr.z[j] : lr.z[j];
+        for (int j = 1; j < K / 2; ++j) sr += L.tb[(r.s >> (8 * j)) & 0xFFu];
+        v = scale_fma<SF>(r.b, sr, v);
+      }
+      acc[i] = v;
     }
-    const float total = wave_sum(part);
-    if (lane == i) rowacc += total;
-    cur = nxt;
+    float v = treduce<RB>(acc, lane) * XLane<XT>::kHalf;
+    if (!first) v = B.yprev + v;
+    const uint32_t base = row0 + bb * RB;
+    const uint32_t row = base + ((uint32_t)lane >> SH);
+    if (last && d.terms) {
+      float c = 0.f;
+      if (L.uon) {
+        const float zt = sm.z[ti];
+        c = ((B.u >> L.ubit) & 1u) ? -zt : zt;
+      }
+      // terms beyond one per lane (more than 64 / RB of them)
+      const uint32_t ry = min(row, row1 - 1);
+      for (uint32_t t = ti + LPR; t < d.terms; t += LPR) {
+        const uint32_t p = t / d.rank, r = t % d.rank;
+        const uint32_t byte = path_ptr(d.U, p)[(size_t)ry * L.ub + r / 8];
+        const float zt = sm.z[t];
+        c += ((byte >> (r & 7)) & 1u) ? -zt : zt;
+      }
+      v += group_sum<LPR>(c);
+    }
+    if ((lane & (LPR - 1)) == 0 && row < row1)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ry_rs, row * 4, 0, 0);
+  };
+
+  // Double-buffered batches: the next batch's loads are issued before the
+  // current batch is reduced.  Past the wave's last batch the prefetch
+  // repeats the current batch (an L2 hit), keeping every load unconditional.
+  auto next = [&](uint32_t bb) { return bb + kWaves < nb ? bb + kWaves : bb; };
+  Batch<RB> A = load_batch(b);
+  for (;;) {
+    const Batch<RB> Bn = load_batch(next(b));
+    finish_batch(A, b);
+    if (b + kWaves >= nb) break;
+    b += kWaves;
+    A = load_batch(next(b));
+    finish_batch(Bn, b);
+    if (b + kWaves >= nb) break;
+    b += kWaves;
   }
 }
 
-// One tile: kWavesPerBlock wavefronts, each owning RW consecutive rows.
-template <int XT>
-__device__ __forceinline__ void tile_2bit(const MatDev& d, uint32_t row0, uint32_t RW, float* tbl) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const uint32_t n0 = row0 + wave * RW;
-  const int nrows = n0 < d.out ? (int)min(RW, d.out - n0) : 0;
+template <int XT, int RB>
+__device__ __forceinline__ void run_segment_2bit(const MatDev& d, uint32_t row0, uint32_t row1, StreamSmem& sm) {
   const uint32_t npass = (d.in + kPass2bit - 1) / kPass2bit;
-  LowRank lr;
-  lowrank_setup(d, lane, lr);
-  float rowacc = 0.f;
+  const int lane = threadIdx.x & 63;
   for (uint32_t pass = 0; pass < npass; ++pass) {
     const uint32_t pw = min(kPass2bit, d.in - pass * kPass2bit);
-    const uint32_t Gp = pw / 128;
-    __syncthreads();                                   // previous readers of tbl are done
-    if (d.k) {
-      for (uint32_t e = threadIdx.x; e < Gp * 256; e += kBlockThreads) {
-        const uint32_t g = e >> 8, b = e & 255u;
-        const float v = xval<XT>(d.x, pass * kPass2bit + g * 128 + (b & 127u));
-        tbl[e] = (b & 128u) ? -v : v;
-      }
-    }
+    __syncthreads();   // readers of the previous table and z are done
+    if (pass == 0)
+      for (uint32_t t = threadIdx.x; t < d.terms; t += kThreads) sm.z[t] = d.z[t];
+    if (d.k) build_table<XT>(d.x, pass * kPass2bit, pw, sm.tbl);
     __syncthreads();
-    if (nrows > 0) {
-      XLane<XT> xl;
-      xl.load(d.x, pass * kPass2bit + 64 * lane, (uint32_t)(64 * lane) < pw);
-      const bool last = pass + 1 == npass;
-      switch (d.k) {
-        case 0: pass_rows_2bit<XT, 0>(d, n0, nrows, pass, Gp, last, tbl, xl, lr, lane, rowacc); break;
-        case 2: pass_rows_2bit<XT, 2>(d, n0, nrows, pass, Gp, last, tbl, xl, lr, lane, rowacc); break;
-        case 4: pass_rows_2bit<XT, 4>(d, n0, nrows, pass, Gp, last, tbl, xl, lr, lane, rowacc); break;
-        default: pass_rows_2bit<XT, 8>(d, n0, nrows, pass, Gp, last, tbl, xl, lr, lane, rowacc); break;
-      }
+    XLane<XT> xl;
+    xl.load(d.x, pass * kPass2bit + 64 * lane, (uint32_t)(64 * lane) < pw);
+    const uint32_t sel = d.scale_fmt * 4 + (d.k == 0 ? 0 : d.k == 2 ? 1 : d.k == 4 ? 2 : 3);
+    switch (sel) {
+      case 0: stream_rows_2bit<XT, WAL_SCALE_FP16, 0, RB>(d, row0, row1, pass, npass, xl, sm); break;
+      case 1: stream_rows_2bit<XT, WAL_SCALE_FP16, 2, RB>(d, row0, row1, pass, npass, xl, sm); break;
+      case 2: stream_rows_2bit<XT, WAL_SCALE_FP16, 4, RB>(d, row0, row1, pass, npass, xl, sm); break;
+      case 3: stream_rows_2bit<XT, WAL_SCALE_FP16, 8, RB>(d, row0, row1, pass, npass, xl, sm); break;
+      case 4: stream_rows_2bit<XT, WAL_SCALE_FP24, 0, RB>(d, row0, row1, pass, npass, xl, sm); break;
+      case 5: stream_rows_2bit<XT, WAL_SCALE_FP24, 2, RB>(d, row0, row1, pass, npass, xl, sm); break;
+      case 6: stream_rows_2bit<XT, WAL_SCALE_FP24, 4, RB>(d, row0, row1, pass, npass, xl, sm); break;
+      default: stream_rows_2bit<XT, WAL_SCALE_FP24, 8, RB>(d, row0, row1, pass, npass, xl, sm); break;
     }
   }
-  if (lane < nrows) d.y[n0 + lane] = rowacc;
 }
 
-template <int XT>
-__global__ __launch_bounds__(kBlockThreads) void k_gemv2_single(MatDev d, uint32_t RW) {
-  __shared__ float tbl[32 * 256];
-  tile_2bit<XT>(d, blockIdx.x * kWavesPerBlock * RW, RW, tbl);
-}
-
-template <int XT>
-__global__ __launch_bounds__(kBlockThreads) void k_gemv2_grouped(const MatDev* __restrict__ descs,
-                                                                 const uint2* __restrict__ tiles,
-                                                                 uint32_t n_tiles, uint32_t RW) {
-  __shared__ float tbl[32 * 256];
-  for (uint32_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
-    const uint2 tl = tiles[t];
-    tile_2bit<XT>(descs[tl.x], tl.y, RW, tbl);
+template <int XT, int RB>
+__global__ __launch_bounds__(kThreads) void k_stream_grouped(const MatDev* __restrict__ descs,
+                                                             const uint32_t* __restrict__ blockseg,
+                                                             const Seg* __restrict__ segs) {
+  __shared__ StreamSmem sm;
+  const uint32_t s0 = blockseg[blockIdx.x], s1 = blockseg[blockIdx.x + 1];
+  for (uint32_t s = s0; s < s1; ++s) {
+    const Seg sg = segs[s];
+    run_segment_2bit<XT, RB>(descs[sg.mat], sg.row0, sg.row1, sm);
   }
+}
+
+template <int XT, int RB>
+__global__ __launch_bounds__(kThreads) void k_stream_single(MatDev d, uint32_t rows_per_block) {
+  __shared__ StreamSmem sm;
+  const uint32_t r0 = blockIdx.x * rows_per_block;
+  const uint32_t r1 = min(d.out, r0 + rows_per_block);
+  if (r0 < r1) run_segment_2bit<XT, RB>(d, r0, r1, sm);
 }
 
 // ---------------------------------------------------------------------------
-// Low-rank pre-pass: z[t] = s_p[r] * sum_j (-1)^{V_p[r] bit j} x_j, one
-// wavefront per term t = p * rank + r.
+// Low-rank pre-pass: z[t] = s_p[r] * sum_j (-1)^{V_p[r] bit j} x_j for the
+// kZTerms terms t0 .. t0 + kZTerms - 1 of one matrix, one workgroup.
 template <int XT>
-__device__ __forceinline__ void zjob(const MatDev& d, uint32_t t, int lane) {
-  const uint32_t p = t / d.rank, r = t % d.rank;
-  const uint8_t* vrow = d.V[p] + (size_t)r * (d.in / 8);
-  float acc = 0.f;
-  for (uint32_t c = 64 * lane; c < d.in; c += 64 * 64) {
-    const uint2 bits = *reinterpret_cast<const uint2*>(vrow + c / 8);
+__device__ __forceinline__ void zjob(const MatDev& d, uint32_t t0) {
+  __shared__ float red[kWaves][kZTerms];
+  const uint32_t tid = threadIdx.x;
+  const int lane = tid & 63;
+  const uint32_t T = d.terms, vrow = d.in / 8;
+  float acc[kZTerms];
 #pragma unroll
-    for (int j = 0; j < 64; ++j) {
-      const float v = xval<XT>(d.x, c + j);
-      const uint32_t bit = j < 32 ? (bits.x >> j) & 1u : (bits.y >> (j - 32)) & 1u;
-      acc += bit ? -v : v;
+  for (int q = 0; q < (int)kZTerms; ++q) acc[q] = 0.f;
+  for (uint32_t c = tid * 16; c < d.in; c += kThreads * 16) {
+    float xv[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) xv[j] = xval<XT>(d.x, c + j);
+#pragma unroll
+    for (int q = 0; q < (int)kZTerms; ++q) {
+      const uint32_t t = t0 + q;
+      if (t < T) {
+        const uint32_t p = t / d.rank, r = t % d.rank;
+        const uint32_t bits = reinterpret_cast<const uint16_t*>(path_ptr(d.V, p) + (size_t)r * vrow)[c / 16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[q] += ((bits >> j) & 1u) ? -xv[j] : xv[j];
+      }
     }
   }
-  const float total = wave_sum(acc);
-  if (lane == 0) {
-    const float s = __half2float(__ushort_as_half(reinterpret_cast<const uint16_t*>(d.s[p])[r]));
-    d.z[t] = s * total;
+  const float tot = treduce<kZTerms>(acc, lane);
+  constexpr int SH = 6 - ilog2(kZTerms);
+  if ((lane & ((1 << SH) - 1)) == 0) red[tid >> 6][lane >> SH] = tot;
+  __syncthreads();
+  if (tid < kZTerms) {
+    const uint32_t t = t0 + tid;
+    if (t < T) {
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < (int)kWaves; ++w) sum += red[w][tid];
+      const uint32_t p = t / d.rank, r = t % d.rank;
+      d.z[t] = f16_at(path_ptr(d.s, p), r) * sum;
+    }
   }
 }
 
 template <int XT>
-__global__ __launch_bounds__(kBlockThreads) void k_z_single(MatDev d) {
-  const uint32_t t = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  if (t < d.terms) zjob<XT>(d, t, threadIdx.x & 63);
+__global__ __launch_bounds__(kThreads) void k_z_single(MatDev d) {
+  zjob<XT>(d, blockIdx.x * kZTerms);
 }
 
 template <int XT>
-__global__ __launch_bounds__(kBlockThreads) void k_z_grouped(const MatDev* __restrict__ descs,
-                                                             const uint32_t* __restrict__ jobs, uint32_t n) {
-  const uint32_t j = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  if (j < n) {
-    const uint32_t job = jobs[j];
-    zjob<XT>(descs[job >> 8], job & 255u, threadIdx.x & 63);
-  }
+__global__ __launch_bounds__(kThreads) void k_z_grouped(const MatDev* __restrict__ descs,
+                                                        const uint32_t* __restrict__ jobs) {
+  const uint32_t job = jobs[blockIdx.x];
+  zjob<XT>(descs[job >> 8], job & 255u);
 }
 
 // ---------------------------------------------------------------------------
@@ -367,14 +555,16 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 
 size_t xelem(int xdt) { return xdt == WAL_X_F32 ? 4 : 2; }
 
+uint64_t up64(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+
 MatDev make_dev(const wal_info* f, const void* W, const void* x, float* y, float* z, uint32_t ldx,
                 uint32_t ldy, uint32_t batch) {
   MatDev m{};
   const uint8_t* base = static_cast<const uint8_t*>(W);
   m.codes = base + f->off_codes;
-  m.sites = f->d.k ? base + f->off_sites : nullptr;
+  m.sites = f->d.k ? base + f->off_sites : m.codes;
   m.alpha = base + f->off_alpha;
-  m.beta = f->d.k ? base + f->off_beta : nullptr;
+  m.beta = f->d.k ? base + f->off_beta : m.alpha;
   for (uint32_t p = 0; p < WAL_MAX_PATHS; ++p) {
     const bool on = p < f->d.n_paths;
     m.V[p] = on ? base + f->off_V[p] : nullptr;
@@ -386,27 +576,69 @@ MatDev make_dev(const wal_info* f, const void* W, const void* x, float* y, float
   m.rank = f->d.rank; m.scale_fmt = f->d.scale_fmt; m.row_stride = f->row_stride;
   m.groups = f->groups; m.ldx = ldx; m.ldy = ldy; m.batch = batch;
   m.terms = f->d.n_paths * f->d.rank;
+  m.blob_bytes = (uint32_t)(f->total_bytes - f->off_codes);
+  m.trit_fmt = f->d.trit_fmt;
   return m;
 }
-
-// Rows per wavefront for a single matrix: enough tiles to cover the chip
-// about twice, at most kRowsMax.
-uint32_t rows_per_wave_single(uint32_t out) {
-  const uint32_t target_tiles = 512;
-  uint32_t rw = (out + target_tiles * kWavesPerBlock - 1) / (target_tiles * kWavesPerBlock);
-  if (rw < 1) rw = 1;
-  if (rw > 32) rw = 32;
-  return rw;
-}
-
-constexpr uint32_t kGroupedRW = 16;
 
 int launch_status() {
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? WAL_OK : WAL_ERR_DEVICE;
 }
 
-uint64_t up64(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+constexpr int kRB = 4;   // rows per batch of the streaming kernels
+
+// Workgroups of a streaming kernel that the current device holds at once.
+template <typename K>
+int resident_blocks(K kernel, uint32_t* out) {
+  int dev = 0, cus = 0, per = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return WAL_ERR_DEVICE;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return WAL_ERR_DEVICE;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, kThreads, 0) != hipSuccess) return WAL_ERR_DEVICE;
+  if (cus <= 0 || per <= 0) return WAL_ERR_DEVICE;
+  *out = (uint32_t)(cus * per);
+  return WAL_OK;
+}
+
+int resident_for(int x_dtype, uint32_t* out) {
+  if (x_dtype == WAL_X_BF16) return resident_blocks(k_stream_grouped<WAL_X_BF16, kRB>, out);
+  return resident_blocks(k_stream_grouped<WAL_X_F32, kRB>, out);
+}
+
+// Bytes one row of a matrix contributes to the stream (codes, sites, scales, U).
+uint64_t row_bytes(const wal_info& f) {
+  const uint64_t in = f.d.in, G = f.groups, sb = f.d.scale_fmt == WAL_SCALE_FP16 ? 2 : 3;
+  const uint64_t codes = f.d.trit_fmt == WAL_TRIT_2BIT ? in / 4 : (in + 4) / 5;
+  return codes + G * f.d.k + G * sb * (f.d.k ? 2 : 1) + (uint64_t)f.d.n_paths * ((f.d.rank + 7) / 8);
+}
+
+uint64_t count_zjobs(uint32_t n, const wal_info* infos) {
+  uint64_t j = 0;
+  for (uint32_t i = 0; i < n; ++i) {
+    const uint32_t T = infos[i].d.n_paths * infos[i].d.rank;
+    j += (T + kZTerms - 1) / kZTerms;
+  }
+  return j;
+}
+
+struct PlanLayout {
+  uint64_t off_descs, off_blockseg, off_segs, off_zjobs, bytes;
+};
+
+PlanLayout plan_layout(uint32_t n, uint32_t grid, uint64_t max_segs, uint64_t zjobs) {
+  PlanLayout L;
+  L.off_descs = up64(sizeof(PlanHeader), 64);
+  L.off_blockseg = L.off_descs + up64((uint64_t)n * sizeof(MatDev), 64);
+  L.off_segs = L.off_blockseg + up64(4ull * (grid + 1), 64);
+  L.off_zjobs = L.off_segs + up64(max_segs * sizeof(Seg), 64);
+  L.bytes = L.off_zjobs + up64(zjobs * 4, 64);
+  return L;
+}
+
+int check_blob_size(const wal_info* f) {
+  if (f->total_bytes - f->off_codes >= (1ull << 32)) return WAL_ERR_UNSUPPORTED;
+  return WAL_OK;
+}
 
 }  // namespace
 
@@ -425,18 +657,26 @@ int wal_gemv(const wal_info* info, const void* W_dev, const void* x_dev, int x_d
   if (need && !aligned(ws_dev, 16)) return WAL_ERR_ALIGN;
   if (overlap(x_dev, (size_t)info->d.in * xelem(x_dtype), y_dev, (size_t)info->d.out * 4)) return WAL_ERR_ARG;
   if (info->d.trit_fmt != WAL_TRIT_2BIT) return WAL_ERR_UNSUPPORTED;
+  if ((st = check_blob_size(info))) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   MatDev d = make_dev(info, W_dev, x_dev, y_dev, static_cast<float*>(ws_dev), info->d.in, info->d.out, 1);
   if (d.terms) {
-    const uint32_t g = (d.terms + kWavesPerBlock - 1) / kWavesPerBlock;
-    if (x_dtype == WAL_X_BF16) hipLaunchKernelGGL(k_z_single<WAL_X_BF16>, dim3(g), dim3(kBlockThreads), 0, s, d);
-    else hipLaunchKernelGGL(k_z_single<WAL_X_F32>, dim3(g), dim3(kBlockThreads), 0, s, d);
+    const uint32_t g = (d.terms + kZTerms - 1) / kZTerms;
+    if (x_dtype == WAL_X_BF16) hipLaunchKernelGGL(k_z_single<WAL_X_BF16>, dim3(g), dim3(kThreads), 0, s, d);
+    else hipLaunchKernelGGL(k_z_single<WAL_X_F32>, dim3(g), dim3(kThreads), 0, s, d);
     if ((st = launch_status())) return st;
   }
-  const uint32_t rw = rows_per_wave_single(d.out);
-  const uint32_t grid = (d.out + kWavesPerBlock * rw - 1) / (kWavesPerBlock * rw);
-  if (x_dtype == WAL_X_BF16) hipLaunchKernelGGL(k_gemv2_single<WAL_X_BF16>, dim3(grid), dim3(kBlockThreads), 0, s, d, rw);
-  else hipLaunchKernelGGL(k_gemv2_single<WAL_X_F32>, dim3(grid), dim3(kBlockThreads), 0, s, d, rw);
+  uint32_t resident = 0;
+  if ((st = resident_for(x_dtype, &resident))) return st;
+  uint32_t rpb = (d.out + resident - 1) / resident;
+  const uint32_t min_rows = kWaves * kRB * 2;
+  if (rpb < min_rows) rpb = min_rows;
+  rpb = (rpb + kRB - 1) / kRB * kRB;
+  const uint32_t grid = (d.out + rpb - 1) / rpb;
+  if (x_dtype == WAL_X_BF16)
+    hipLaunchKernelGGL((k_stream_single<WAL_X_BF16, kRB>), dim3(grid), dim3(kThreads), 0, s, d, rpb);
+  else
+    hipLaunchKernelGGL((k_stream_single<WAL_X_F32, kRB>), dim3(grid), dim3(kThreads), 0, s, d, rpb);
   return launch_status();
 }
 
@@ -453,34 +693,36 @@ int wal_gemm_small(const wal_info* info, const void* W_dev, const void* X_dev, i
   return WAL_ERR_UNSUPPORTED;
 }
 
-int wal_grouped_plan_size(uint32_t n, const wal_info* infos, size_t* plan_bytes, size_t* ws_bytes) {
+int wal_grouped_plan_size(uint32_t n, const wal_info* infos, uint32_t grid, int x_dtype, size_t* plan_bytes,
+                          size_t* ws_bytes, uint32_t* grid_out) {
   if (!n || !infos || !plan_bytes || !ws_bytes) return WAL_ERR_ARG;
-  uint64_t tiles = 0, jobs = 0, ws = 0;
+  if (x_dtype != WAL_X_F32 && x_dtype != WAL_X_BF16) return WAL_ERR_ARG;
+  uint64_t ws = 0;
   for (uint32_t i = 0; i < n; ++i) {
     int st = check_info(&infos[i]);
     if (st) return st;
-    const uint32_t rows_per_tile = kWavesPerBlock * kGroupedRW;
-    tiles += (infos[i].d.out + rows_per_tile - 1) / rows_per_tile;
-    jobs += infos[i].d.n_paths * infos[i].d.rank;
+    if ((st = check_blob_size(&infos[i]))) return st;
     ws += up64(4ull * infos[i].d.n_paths * infos[i].d.rank, 16);
   }
-  uint64_t b = up64(sizeof(PlanHeader), 64);
-  b += up64((uint64_t)n * sizeof(MatDev), 64);
-  b += up64(tiles * 8, 64);
-  b += up64(jobs * 4, 64);
-  *plan_bytes = (size_t)b;
+  if (n > (1u << 24)) return WAL_ERR_ARG;
+  if (grid == 0) {
+    int st = resident_for(x_dtype, &grid);
+    if (st) return st;
+  }
+  const PlanLayout L = plan_layout(n, grid, (uint64_t)n + grid, count_zjobs(n, infos));
+  *plan_bytes = (size_t)L.bytes;
   *ws_bytes = (size_t)up64(ws, 256);
+  if (grid_out) *grid_out = grid;
   return WAL_OK;
 }
 
 int wal_grouped_plan(uint32_t n, const wal_info* infos, const void* const* W_dev, const void* const* x_dev,
-                     int x_dtype, float* const* y_dev, void* ws_dev, size_t ws_bytes, void* plan_host,
-                     size_t plan_bytes, wal_grouped_info* ginfo) {
+                     int x_dtype, float* const* y_dev, void* ws_dev, size_t ws_bytes, uint32_t grid,
+                     void* plan_host, size_t plan_bytes, wal_grouped_info* ginfo) {
   size_t need_plan = 0, need_ws = 0;
-  int st = wal_grouped_plan_size(n, infos, &need_plan, &need_ws);
+  int st = wal_grouped_plan_size(n, infos, grid, x_dtype, &need_plan, &need_ws, &grid);
   if (st) return st;
   if (!W_dev || !x_dev || !y_dev || !plan_host || !ginfo) return WAL_ERR_ARG;
-  if (x_dtype != WAL_X_F32 && x_dtype != WAL_X_BF16) return WAL_ERR_ARG;
   if (plan_bytes < need_plan) return WAL_ERR_BUFFER;
   if (need_ws && (!ws_dev || ws_bytes < need_ws)) return ws_dev ? WAL_ERR_BUFFER : WAL_ERR_ARG;
   if (need_ws && !aligned(ws_dev, 16)) return WAL_ERR_ALIGN;
@@ -493,47 +735,85 @@ int wal_grouped_plan(uint32_t n, const wal_info* infos, const void* const* W_dev
       return WAL_ERR_ARG;
   }
   if (tf != WAL_TRIT_2BIT) return WAL_ERR_UNSUPPORTED;
+  const uint64_t zjobs = count_zjobs(n, infos);
+  const PlanLayout L = plan_layout(n, grid, (uint64_t)n + grid, zjobs);
   uint8_t* base = static_cast<uint8_t*>(plan_host);
-  std::memset(base, 0, need_plan);
+  std::memset(base, 0, L.bytes);
   PlanHeader* h = reinterpret_cast<PlanHeader*>(base);
+  MatDev* descs = reinterpret_cast<MatDev*>(base + L.off_descs);
+  uint32_t* blockseg = reinterpret_cast<uint32_t*>(base + L.off_blockseg);
+  Seg* segs = reinterpret_cast<Seg*>(base + L.off_segs);
+  uint32_t* jobs = reinterpret_cast<uint32_t*>(base + L.off_zjobs);
+
+  // descriptors and low-rank jobs
+  uint64_t zoff = 0, j = 0, total = 0;
+  for (uint32_t i = 0; i < n; ++i) {
+    const uint32_t T = infos[i].d.n_paths * infos[i].d.rank;
+    float* z = T ? static_cast<float*>(ws_dev) + zoff / 4 : nullptr;
+    descs[i] = make_dev(&infos[i], W_dev[i], x_dev[i], y_dev[i], z, infos[i].d.in, infos[i].d.out, 1);
+    zoff += up64(4ull * T, 16);
+    for (uint32_t t0 = 0; t0 < T; t0 += kZTerms) jobs[j++] = (i << 8) | t0;
+    total += row_bytes(infos[i]) * infos[i].d.out;
+  }
+
+  // Split the rows of all matrices, in order, into `grid` ranges of equal
+  // streamed bytes; block b owns the segments between boundaries b and b + 1.
+  auto boundary = [&](uint32_t b, uint32_t* mat, uint32_t* row) {
+    const unsigned __int128 pos128 = (unsigned __int128)total * b / grid;
+    uint64_t pos = (uint64_t)pos128, acc = 0;
+    for (uint32_t i = 0; i < n; ++i) {
+      const uint64_t rb = row_bytes(infos[i]), mb = rb * infos[i].d.out;
+      if (pos < acc + mb) {
+        uint64_t r = (pos - acc + rb / 2) / rb;
+        if (r >= infos[i].d.out) { *mat = i + 1; *row = 0; }
+        else { *mat = i; *row = (uint32_t)r; }
+        return;
+      }
+      acc += mb;
+    }
+    *mat = n; *row = 0;
+  };
+  uint32_t nseg = 0, m0 = 0, r0 = 0;
+  boundary(0, &m0, &r0);
+  for (uint32_t b = 0; b < grid; ++b) {
+    blockseg[b] = nseg;
+    uint32_t m1 = 0, r1 = 0;
+    boundary(b + 1, &m1, &r1);
+    uint32_t m = m0, r = r0;
+    while (m < m1 || (m == m1 && r < r1)) {
+      const uint32_t end = m < m1 ? infos[m].d.out : r1;
+      if (r < end) segs[nseg++] = Seg{m, r, end, 0};
+      ++m;
+      r = 0;
+      if (m > m1) break;
+    }
+    m0 = m1;
+    r0 = r1;
+  }
+  blockseg[grid] = nseg;
+
   h->magic = kPlanMagic;
   h->n = n;
-  h->rows_per_wave = kGroupedRW;
+  h->grid = grid;
+  h->n_segs = nseg;
+  h->n_zjobs = (uint32_t)zjobs;
   h->x_dtype = (uint32_t)x_dtype;
   h->trit_fmt = tf;
-  h->off_descs = up64(sizeof(PlanHeader), 64);
-  MatDev* descs = reinterpret_cast<MatDev*>(base + h->off_descs);
-  uint64_t zoff = 0, tiles = 0, jobs = 0;
-  const uint32_t rows_per_tile = kWavesPerBlock * kGroupedRW;
-  for (uint32_t i = 0; i < n; ++i) {
-    float* z = static_cast<float*>(ws_dev) + zoff / 4;
-    descs[i] = make_dev(&infos[i], W_dev[i], x_dev[i], y_dev[i], infos[i].d.n_paths ? z : nullptr,
-                        infos[i].d.in, infos[i].d.out, 1);
-    zoff += up64(4ull * infos[i].d.n_paths * infos[i].d.rank, 16);
-    tiles += (infos[i].d.out + rows_per_tile - 1) / rows_per_tile;
-    jobs += infos[i].d.n_paths * infos[i].d.rank;
-  }
-  h->n_tiles = (uint32_t)tiles;
-  h->n_zjobs = (uint32_t)jobs;
-  h->off_tiles = h->off_descs + up64((uint64_t)n * sizeof(MatDev), 64);
-  h->off_zjobs = h->off_tiles + up64(tiles * 8, 64);
-  h->bytes = need_plan;
-  uint32_t* tl = reinterpret_cast<uint32_t*>(base + h->off_tiles);
-  uint32_t* jb = reinterpret_cast<uint32_t*>(base + h->off_zjobs);
-  uint64_t t = 0, j = 0;
-  for (uint32_t i = 0; i < n; ++i) {
-    for (uint32_t r0 = 0; r0 < infos[i].d.out; r0 += rows_per_tile, ++t) { tl[2 * t] = i; tl[2 * t + 1] = r0; }
-    for (uint32_t q = 0; q < infos[i].d.n_paths * infos[i].d.rank; ++q, ++j) jb[j] = (i << 8) | q;
-  }
+  h->off_descs = L.off_descs;
+  h->off_blockseg = L.off_blockseg;
+  h->off_segs = L.off_segs;
+  h->off_zjobs = L.off_zjobs;
+  h->bytes = L.bytes;
+
   std::memset(ginfo, 0, sizeof(*ginfo));
   ginfo->n = n;
-  ginfo->n_tiles = h->n_tiles;
-  ginfo->n_zjobs = h->n_zjobs;
-  ginfo->rows_per_wave = kGroupedRW;
+  ginfo->grid = grid;
+  ginfo->n_segs = nseg;
+  ginfo->n_zjobs = (uint32_t)zjobs;
   ginfo->x_dtype = (uint32_t)x_dtype;
   ginfo->trit_fmt = tf;
-  ginfo->grid = h->n_tiles < 1024 ? h->n_tiles : 1024;
-  ginfo->plan_bytes = need_plan;
+  ginfo->rows_per_batch = kRB;
+  ginfo->plan_bytes = L.bytes;
   uint64_t alg = 0;
   for (uint32_t i = 0; i < n; ++i) alg += infos[i].algorithmic_bytes;
   ginfo->algorithmic_bytes = alg;
@@ -544,29 +824,29 @@ int wal_gemv_grouped(const wal_grouped_info* g, const void* plan_dev, void* stre
   if (!g || !plan_dev) return WAL_ERR_ARG;
   if (!aligned(plan_dev, 16)) return WAL_ERR_ALIGN;
   if (g->x_dtype > WAL_X_BF16 || g->trit_fmt != WAL_TRIT_2BIT || !g->n || !g->grid) return WAL_ERR_ARG;
+  if (g->rows_per_batch != (uint32_t)kRB) return WAL_ERR_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const PlanLayout L = plan_layout(g->n, g->grid, (uint64_t)g->n + g->grid, g->n_zjobs);
+  if (L.bytes != g->plan_bytes) return WAL_ERR_ARG;
   const uint8_t* base = static_cast<const uint8_t*>(plan_dev);
-  const uint64_t off_descs = up64(sizeof(PlanHeader), 64);
-  const uint64_t off_tiles = off_descs + up64((uint64_t)g->n * sizeof(MatDev), 64);
-  const uint64_t off_jobs = off_tiles + up64((uint64_t)g->n_tiles * 8, 64);
-  const MatDev* descs = reinterpret_cast<const MatDev*>(base + off_descs);
-  const uint2* tiles = reinterpret_cast<const uint2*>(base + off_tiles);
-  const uint32_t* jobs = reinterpret_cast<const uint32_t*>(base + off_jobs);
+  const MatDev* descs = reinterpret_cast<const MatDev*>(base + L.off_descs);
+  const uint32_t* blockseg = reinterpret_cast<const uint32_t*>(base + L.off_blockseg);
+  const Seg* segs = reinterpret_cast<const Seg*>(base + L.off_segs);
+  const uint32_t* jobs = reinterpret_cast<const uint32_t*>(base + L.off_zjobs);
   int st;
   if (g->n_zjobs) {
-    const uint32_t grid = (g->n_zjobs + kWavesPerBlock - 1) / kWavesPerBlock;
     if (g->x_dtype == WAL_X_BF16)
-      hipLaunchKernelGGL(k_z_grouped<WAL_X_BF16>, dim3(grid), dim3(kBlockThreads), 0, s, descs, jobs, g->n_zjobs);
+      hipLaunchKernelGGL(k_z_grouped<WAL_X_BF16>, dim3(g->n_zjobs), dim3(kThreads), 0, s, descs, jobs);
     else
-      hipLaunchKernelGGL(k_z_grouped<WAL_X_F32>, dim3(grid), dim3(kBlockThreads), 0, s, descs, jobs, g->n_zjobs);
+      hipLaunchKernelGGL(k_z_grouped<WAL_X_F32>, dim3(g->n_zjobs), dim3(kThreads), 0, s, descs, jobs);
     if ((st = launch_status())) return st;
   }
   if (g->x_dtype == WAL_X_BF16)
-    hipLaunchKernelGGL(k_gemv2_grouped<WAL_X_BF16>, dim3(g->grid), dim3(kBlockThreads), 0, s, descs, tiles,
-                       g->n_tiles, g->rows_per_wave);
+    hipLaunchKernelGGL((k_stream_grouped<WAL_X_BF16, kRB>), dim3(g->grid), dim3(kThreads), 0, s, descs, blockseg,
+                       segs);
   else
-    hipLaunchKernelGGL(k_gemv2_grouped<WAL_X_F32>, dim3(g->grid), dim3(kBlockThreads), 0, s, descs, tiles,
-                       g->n_tiles, g->rows_per_wave);
+    hipLaunchKernelGGL((k_stream_grouped<WAL_X_F32, kRB>), dim3(g->grid), dim3(kThreads), 0, s, descs, blockseg,
+                       segs);
   return launch_status();
 }
 

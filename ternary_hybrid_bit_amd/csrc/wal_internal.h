@@ -24,22 +24,33 @@ struct MatDev {
   float* z;            // [batch][n_paths * rank] workspace: diag(s_p) V_p^T x
   uint32_t out, in, k, n_paths, rank, scale_fmt, row_stride, groups;
   uint32_t ldx, ldy, batch, terms;  // terms = n_paths * rank
+  uint32_t blob_bytes;              // bytes of the blob from codes on (< 2^32)
+  uint32_t trit_fmt;
 };
 
-// Plan blob written by wal_grouped_plan (host) and read by the kernels.
+// Plan blob written by wal_grouped_plan (host) and read by the kernels:
+//   header | MatDev[n] | blockseg u32[grid + 1] | segs Seg[n_segs] | zjobs u32[n_zjobs]
+// Block b of the main kernel processes segs[blockseg[b] .. blockseg[b + 1]).
 struct PlanHeader {
-  uint32_t magic, n, n_tiles, n_zjobs, rows_per_wave, x_dtype, trit_fmt, reserved;
-  uint64_t off_descs, off_tiles, off_zjobs, bytes;
+  uint32_t magic, n, grid, n_segs, n_zjobs, x_dtype, trit_fmt, reserved;
+  uint64_t off_descs, off_blockseg, off_segs, off_zjobs, bytes;
 };
-constexpr uint32_t kPlanMagic = 0x4E4C5057u;  // "WPLN"
+struct Seg {
+  uint32_t mat, row0, row1, pad;
+};
+constexpr uint32_t kPlanMagic = 0x324E4C50u;  // "PLN2"
 
+// Streaming kernels: 4 wavefronts per workgroup.
+constexpr uint32_t kWaves = 4;
+constexpr uint32_t kThreads = 64 * kWaves;
 // Columns one wavefront covers per pass: 64 lanes x 16 bytes of codes.
 constexpr uint32_t kPass2bit = 4096;   // 2-bit: 64 trits per lane
 constexpr uint32_t kPassBase3 = 5120;  // base-3: 80 trits per lane
-constexpr uint32_t kWavesPerBlock = 8;
-constexpr uint32_t kBlockThreads = 64 * kWavesPerBlock;
+// Low-rank terms handled per workgroup of the V^T x pre-pass.
+constexpr uint32_t kZTerms = 4;
+constexpr uint32_t kMaxTerms = WAL_MAX_PATHS * WAL_MAX_RANK;
 
-// Host helpers implemented in wal_host.cpp / wal_gpu.hip.
+// Host helpers implemented in wal_host.cpp.
 int check_info(const wal_info* info);
 
 }  // namespace wal
