@@ -112,7 +112,7 @@ def main():
     xs = [torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16) for _, _, xb in items]
     ys = [torch.empty(i.d.out, dtype=torch.float32, device=dev) for _, i, _ in items]
     infos = [i for _, i, _ in items]
-    _, wsb, _ = wal.wal_grouped_plan_size(infos)
+    _, wsb = wal.wal_grouped_plan_size(infos)
     ws = torch.zeros(max(wsb, 4) // 4, dtype=torch.float32, device=dev)
     plan, g = wal.wal_grouped_plan(infos, Ws, xs, ys, ws, wal.WAL_X_BF16)
     plan_dev = torch.from_numpy(plan).to(dev)

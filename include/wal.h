@@ -116,17 +116,27 @@ typedef struct {
                                  alignment or base-3 row padding)           */
 } wal_info;
 
-/* Launch summary of a grouped plan (filled by wal_grouped_plan). */
+#define WAL_MAX_CLASSES 8
+
+/* Launch summary of a grouped plan (filled by wal_grouped_plan).  Matrices
+ * are grouped by (scale format, k) class, class id = 4 * scale_fmt + index
+ * of k in {0, 2, 4, 8}; each class present gets one streaming launch over
+ * its own split of rows into class_grid[c] workgroups. */
 typedef struct {
   uint32_t n;              /* matrices                                      */
-  uint32_t grid;           /* workgroups of the streaming kernel            */
-  uint32_t n_segs;         /* (matrix, row range) segments over all groups  */
+  uint32_t n_classes;      /* classes present (streaming launches)          */
+  uint32_t n_segs;         /* (matrix, row range) segments, all classes     */
   uint32_t n_zjobs;        /* workgroups of the low-rank V^T x pre-pass     */
   uint32_t x_dtype, trit_fmt;
   uint32_t rows_per_batch; /* rows a wavefront reduces at once              */
-  uint32_t reserved;
+  uint32_t grid;           /* largest class grid                           */
   uint64_t plan_bytes;     /* bytes of the plan blob                        */
   uint64_t algorithmic_bytes; /* sum of the matrices' algorithmic bytes     */
+  uint64_t off_descs, off_zjobs;              /* plan offsets               */
+  uint32_t class_id[WAL_MAX_CLASSES];
+  uint32_t class_grid[WAL_MAX_CLASSES];
+  uint64_t class_blockseg[WAL_MAX_CLASSES];   /* plan offsets per class     */
+  uint64_t class_segs[WAL_MAX_CLASSES];
 } wal_grouped_info;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -202,19 +212,20 @@ int wal_gemm_small(const wal_info* info, const void* W_dev, const void* X_dev, i
  * (e.g. the 252 body matrices of a 36-layer model).  Two steps:
  *   1. wal_grouped_plan writes a plan blob into plan_host (host memory of
  *      plan_bytes, see wal_grouped_plan_size) describing every matrix (device
- *      pointers of its planes, x_i, y_i, its workspace slot) and a split of
- *      all rows into `grid` contiguous ranges of equal packed bytes, one per
- *      workgroup of the streaming kernel.  grid = 0 asks for the number of
+ *      pointers of its planes, x_i, y_i, its workspace slot) and, for each
+ *      (scale format, k) class, a split of the class's rows into `grid`
+ *      contiguous ranges of equal packed bytes, one per workgroup of that
+ *      class's streaming launch.  grid = 0 asks for the number of
  *      workgroups the current device holds at once (a HIP query; the other
- *      steps of planning are host-only).
+ *      steps of planning are host-only), capped at one per 16 rows.
  *   2. The caller copies the plan blob into device memory (plan_dev, 16-byte
  *      aligned) and calls wal_gemv_grouped, as often as it likes while the
  *      pointers stay valid.
  * All matrices share x_dtype and trit_fmt.  ws_dev must hold
- * wal_grouped_plan_size's ws_bytes.  *grid_out (if not NULL) receives the
- * grid used.  Errors: ARG, SHAPE, ALIGN, BUFFER, UNSUPPORTED, DEVICE. */
+ * wal_grouped_plan_size's ws_bytes.
+ * Errors: ARG, SHAPE, ALIGN, BUFFER, UNSUPPORTED, DEVICE. */
 int wal_grouped_plan_size(uint32_t n, const wal_info* infos, uint32_t grid, int x_dtype,
-                          size_t* plan_bytes, size_t* ws_bytes, uint32_t* grid_out);
+                          size_t* plan_bytes, size_t* ws_bytes);
 int wal_grouped_plan(uint32_t n, const wal_info* infos, const void* const* W_dev,
                      const void* const* x_dev, int x_dtype, float* const* y_dev,
                      void* ws_dev, size_t ws_bytes, uint32_t grid, void* plan_host,

@@ -50,11 +50,18 @@ class wal_info(ctypes.Structure):
                 ("algorithmic_bytes", ctypes.c_uint64)]
 
 
+WAL_MAX_CLASSES = 8
+
+
 class wal_grouped_info(ctypes.Structure):
-    _fields_ = [("n", ctypes.c_uint32), ("grid", ctypes.c_uint32), ("n_segs", ctypes.c_uint32),
+    _fields_ = [("n", ctypes.c_uint32), ("n_classes", ctypes.c_uint32), ("n_segs", ctypes.c_uint32),
                 ("n_zjobs", ctypes.c_uint32), ("x_dtype", ctypes.c_uint32), ("trit_fmt", ctypes.c_uint32),
-                ("rows_per_batch", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
-                ("plan_bytes", ctypes.c_uint64), ("algorithmic_bytes", ctypes.c_uint64)]
+                ("rows_per_batch", ctypes.c_uint32), ("grid", ctypes.c_uint32),
+                ("plan_bytes", ctypes.c_uint64), ("algorithmic_bytes", ctypes.c_uint64),
+                ("off_descs", ctypes.c_uint64), ("off_zjobs", ctypes.c_uint64),
+                ("class_id", ctypes.c_uint32 * WAL_MAX_CLASSES), ("class_grid", ctypes.c_uint32 * WAL_MAX_CLASSES),
+                ("class_blockseg", ctypes.c_uint64 * WAL_MAX_CLASSES),
+                ("class_segs", ctypes.c_uint64 * WAL_MAX_CLASSES)]
 
 
 if not os.path.exists(LIB_PATH):
@@ -76,8 +83,7 @@ _sig = {
     "wal_workspace_size": (_I, [ctypes.POINTER(wal_info), _U32, ctypes.POINTER(_SZ)]),
     "wal_gemv": (_I, [ctypes.POINTER(wal_info), _P, _P, _I, _P, _P, _SZ, _P]),
     "wal_gemm_small": (_I, [ctypes.POINTER(wal_info), _P, _P, _I, _U32, _U32, _P, _U32, _I, _P, _SZ, _P]),
-    "wal_grouped_plan_size": (_I, [_U32, _P, _U32, _I, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ),
-                                   ctypes.POINTER(_U32)]),
+    "wal_grouped_plan_size": (_I, [_U32, _P, _U32, _I, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)]),
     "wal_grouped_plan": (_I, [_U32, _P, _P, _P, _I, _P, _P, _SZ, _U32, _P, _SZ,
                               ctypes.POINTER(wal_grouped_info)]),
     "wal_gemv_grouped": (_I, [ctypes.POINTER(wal_grouped_info), _P, _P]),
@@ -208,19 +214,19 @@ def wal_gemm_small(info: wal_info, W, X, Y, mode=WAL_GEMM_AUTO, ws=None, stream=
 
 
 def wal_grouped_plan_size(infos: Sequence[wal_info], grid: int = 0, x_dtype: int = WAL_X_BF16):
-    """(plan_bytes, ws_bytes, grid) of a grouped plan; grid 0 = what the current GPU holds at once."""
+    """(plan_bytes, ws_bytes) of a grouped plan; grid 0 = what the current GPU holds at once."""
     arr = (wal_info * len(infos))(*infos)
-    pb, wb, g = _SZ(), _SZ(), _U32()
-    _check(_lib.wal_grouped_plan_size(len(infos), arr, grid, x_dtype, ctypes.byref(pb), ctypes.byref(wb),
-                                      ctypes.byref(g)), "wal_grouped_plan_size")
-    return pb.value, wb.value, g.value
+    pb, wb = _SZ(), _SZ()
+    _check(_lib.wal_grouped_plan_size(len(infos), arr, grid, x_dtype, ctypes.byref(pb), ctypes.byref(wb)),
+           "wal_grouped_plan_size")
+    return pb.value, wb.value
 
 
 def wal_grouped_plan(infos: Sequence[wal_info], Ws, xs, ys, ws, x_dtype: int, grid: int = 0):
     """Build a grouped plan; returns (plan bytes as numpy uint8, wal_grouped_info)."""
     n = len(infos)
     arr = (wal_info * n)(*infos)
-    pb, _, grid = wal_grouped_plan_size(infos, grid, x_dtype)
+    pb, _ = wal_grouped_plan_size(infos, grid, x_dtype)
     plan = np.zeros(pb, dtype=np.uint8)
     Wp = (ctypes.c_void_p * n)(*[_ptr(w) for w in Ws])
     xp = (ctypes.c_void_p * n)(*[_ptr(x) for x in xs])

@@ -142,6 +142,20 @@ __device__ __forceinline__ float xval(const void* x, uint32_t i) {
   return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(x)[i] << 16);
 }
 
+// 64-bit left shift by a constant.  Written as an instruction so that the
+// compiler does not split it back into two 32-bit shifts (it would, seeing
+// that the bits crossing the halves are masked off afterwards).
+template <int S>
+__device__ __forceinline__ uint64_t shl64(uint64_t v) {
+  if constexpr (S == 0) {
+    return v;
+  } else {
+    uint64_t r;
+    asm("v_lshlrev_b64 %0, %1, %2" : "=v"(r) : "n"(S), "v"(v));
+    return r;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // A lane's 64 activation columns of one pass, held in registers.
 template <int XT> struct XLane;
@@ -176,18 +190,25 @@ template <> struct XLane<WAL_X_BF16> {
       }
   }
 
-  // 2 * sum_j T_j x_j over the lane's 64 columns of one row.
+  // 2 * sum_j T_j x_j over the lane's 64 columns of one row.  One 64-bit
+  // shift positions the code pairs of two dwords at once (a full-rate
+  // instruction on gfx950, as is a 32-bit shift); the mask and the dot
+  // product then work on each half.
+  template <int I>
+  __device__ __forceinline__ void dot_pairs(uint64_t q, int h, float& a0, float& a1) const {
+    const uint64_t t = shl64<14 - 2 * I>(q);
+    const uint32_t lo = (uint32_t)t & 0xC000C000u, hi = (uint32_t)(t >> 32) & 0xC000C000u;
+    a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lo),
+                                         __builtin_bit_cast(bf16x2_t, p[16 * h + I]), a0, false);
+    a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, hi),
+                                         __builtin_bit_cast(bf16x2_t, p[16 * h + 8 + I]), a1, false);
+    if constexpr (I < 7) dot_pairs<I + 1>(q, h, a0, a1);
+  }
+
   __device__ __forceinline__ float dot(const u32x4_t& c) const {
     float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t op = (c[d] << (14 - 2 * i)) & 0xC000C000u;
-        float& a = d < 2 ? a0 : a1;
-        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, op),
-                                            __builtin_bit_cast(bf16x2_t, p[8 * d + i]), a, false);
-      }
+    dot_pairs<0>(((uint64_t)c[1] << 32) | c[0], 0, a0, a1);
+    dot_pairs<0>(((uint64_t)c[3] << 32) | c[2], 1, a0, a1);
     return a0 + a1;
   }
 };
@@ -233,12 +254,17 @@ __device__ __forceinline__ const uint8_t* path_ptr(const uint8_t* const (&a)[WAL
 // ---------------------------------------------------------------------------
 // Scales: fp16 (2 bytes) or fp24 (the upper 3 bytes of an fp32 pattern).
 
+// Cache policy of the packed-weight loads: non-temporal.  Every packed byte
+// is read once per product, and marking the stream non-temporal lifts a
+// plain streaming read on MI355X from about 6.2 to 7.0 TB/s.
+constexpr int kStream = 2;
+
 template <int SF>
 __device__ __forceinline__ uint32_t load_scale(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  if constexpr (SF == WAL_SCALE_FP16) return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
-  const uint32_t b0 = __builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
-  const uint32_t b1 = __builtin_amdgcn_raw_buffer_load_b8(r, voff + 1, soff, 0);
-  const uint32_t b2 = __builtin_amdgcn_raw_buffer_load_b8(r, voff + 2, soff, 0);
+  if constexpr (SF == WAL_SCALE_FP16) return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, kStream);
+  const uint32_t b0 = __builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, kStream);
+  const uint32_t b1 = __builtin_amdgcn_raw_buffer_load_b8(r, voff + 1, soff, kStream);
+  const uint32_t b2 = __builtin_amdgcn_raw_buffer_load_b8(r, voff + 2, soff, kStream);
   return b0 | (b1 << 8) | (b2 << 16);
 }
 
@@ -371,16 +397,16 @@ __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0,
     for (int i = 0; i < RB; ++i) {
       const uint32_t row = min(base + i, row1 - 1);
       RowRaw& r = B.r[i];
-      r.c = __builtin_amdgcn_raw_buffer_load_b128(L.rc, L.vc, row * L.sc, 0);
+      r.c = __builtin_amdgcn_raw_buffer_load_b128(L.rc, L.vc, row * L.sc, kStream);
       r.a = load_scale<SF>(L.ra, L.va, row * L.sa);
-      if constexpr (K == 8) r.s = __builtin_amdgcn_raw_buffer_load_b32(L.rs, L.vs, row * L.ss, 0);
-      if constexpr (K == 4) r.s = __builtin_amdgcn_raw_buffer_load_b16(L.rs, L.vs, row * L.ss, 0);
-      if constexpr (K == 2) r.s = __builtin_amdgcn_raw_buffer_load_b8(L.rs, L.vs, row * L.ss, 0);
+      if constexpr (K == 8) r.s = __builtin_amdgcn_raw_buffer_load_b32(L.rs, L.vs, row * L.ss, kStream);
+      if constexpr (K == 4) r.s = __builtin_amdgcn_raw_buffer_load_b16(L.rs, L.vs, row * L.ss, kStream);
+      if constexpr (K == 2) r.s = __builtin_amdgcn_raw_buffer_load_b8(L.rs, L.vs, row * L.ss, kStream);
       if constexpr (K > 0) r.b = load_scale<SF>(L.rb, L.va, row * L.sa);
     }
     const uint32_t ry = min(base + ((uint32_t)lane >> SH), row1 - 1);
     B.yprev = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ry_rs, ry * 4, 0, 0));
-    B.u = __builtin_amdgcn_raw_buffer_load_b8(L.rc, uoff + ry * ustride, 0, 0);
+    B.u = __builtin_amdgcn_raw_buffer_load_b8(L.rc, uoff + ry * ustride, 0, kStream);
     // keep the scheduler from sinking these loads into the next computation
     __builtin_amdgcn_sched_barrier(0);
     return B;
@@ -424,24 +450,34 @@ __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0,
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ry_rs, row * 4, 0, 0);
   };
 
-  // Double-buffered batches: the next batch's loads are issued before the
-  // current batch is reduced.  Past the wave's last batch the prefetch
-  // repeats the current batch (an L2 hit), keeping every load unconditional.
-  auto next = [&](uint32_t bb) { return bb + kWaves < nb ? bb + kWaves : bb; };
-  Batch<RB> A = load_batch(b);
+  // Three batches in registers: while one is reduced, the next two are in
+  // flight.  Past the wave's last batch the prefetch repeats that batch (an
+  // L2 hit), keeping every load unconditional.
+  const uint32_t blast = wave + (nb - 1 - wave) / kWaves * kWaves;
+  auto ahead = [&](uint32_t bb) { return bb < nb ? bb : blast; };
+  Batch<RB> B0 = load_batch(b);
+  Batch<RB> B1 = load_batch(ahead(b + kWaves));
   for (;;) {
-    const Batch<RB> Bn = load_batch(next(b));
-    finish_batch(A, b);
+    const Batch<RB> B2 = load_batch(ahead(b + 2 * kWaves));
+    finish_batch(B0, b);
     if (b + kWaves >= nb) break;
     b += kWaves;
-    A = load_batch(next(b));
-    finish_batch(Bn, b);
+    B0 = load_batch(ahead(b + 2 * kWaves));
+    finish_batch(B1, b);
+    if (b + kWaves >= nb) break;
+    b += kWaves;
+    B1 = load_batch(ahead(b + 2 * kWaves));
+    finish_batch(B2, b);
     if (b + kWaves >= nb) break;
     b += kWaves;
   }
 }
 
-template <int XT, int RB>
+// One segment (rows row0..row1-1 of one matrix) of a workgroup, pass by pass.
+// SF and K are the matrix's scale format and sites per group: every
+// (scale format, k) class has kernels of its own, so the registers of the
+// hot fp16 / k = 8 loop are not set by the heavier fp24 loads.
+template <int XT, int SF, int K, int RB>
 __device__ __forceinline__ void run_segment_2bit(const MatDev& d, uint32_t row0, uint32_t row1, StreamSmem& sm) {
   const uint32_t npass = (d.in + kPass2bit - 1) / kPass2bit;
   const int lane = threadIdx.x & 63;
@@ -450,25 +486,15 @@ __device__ __forceinline__ void run_segment_2bit(const MatDev& d, uint32_t row0,
     __syncthreads();   // readers of the previous table and z are done
     if (pass == 0)
       for (uint32_t t = threadIdx.x; t < d.terms; t += kThreads) sm.z[t] = d.z[t];
-    if (d.k) build_table<XT>(d.x, pass * kPass2bit, pw, sm.tbl);
+    if constexpr (K > 0) build_table<XT>(d.x, pass * kPass2bit, pw, sm.tbl);
     __syncthreads();
     XLane<XT> xl;
     xl.load(d.x, pass * kPass2bit + 64 * lane, (uint32_t)(64 * lane) < pw);
-    const uint32_t sel = d.scale_fmt * 4 + (d.k == 0 ? 0 : d.k == 2 ? 1 : d.k == 4 ? 2 : 3);
-    switch (sel) {
-      case 0: stream_rows_2bit<XT, WAL_SCALE_FP16, 0, RB>(d, row0, row1, pass, npass, xl, sm); break;
-      case 1: stream_rows_2bit<XT, WAL_SCALE_FP16, 2, RB>(d, row0, row1, pass, npass, xl, sm); break;
-      case 2: stream_rows_2bit<XT, WAL_SCALE_FP16, 4, RB>(d, row0, row1, pass, npass, xl, sm); break;
-      case 3: stream_rows_2bit<XT, WAL_SCALE_FP16, 8, RB>(d, row0, row1, pass, npass, xl, sm); break;
-      case 4: stream_rows_2bit<XT, WAL_SCALE_FP24, 0, RB>(d, row0, row1, pass, npass, xl, sm); break;
-      case 5: stream_rows_2bit<XT, WAL_SCALE_FP24, 2, RB>(d, row0, row1, pass, npass, xl, sm); break;
-      case 6: stream_rows_2bit<XT, WAL_SCALE_FP24, 4, RB>(d, row0, row1, pass, npass, xl, sm); break;
-      default: stream_rows_2bit<XT, WAL_SCALE_FP24, 8, RB>(d, row0, row1, pass, npass, xl, sm); break;
-    }
+    stream_rows_2bit<XT, SF, K, RB>(d, row0, row1, pass, npass, xl, sm);
   }
 }
 
-template <int XT, int RB>
+template <int XT, int SF, int K, int RB>
 __global__ __launch_bounds__(kThreads) void k_stream_grouped(const MatDev* __restrict__ descs,
                                                              const uint32_t* __restrict__ blockseg,
                                                              const Seg* __restrict__ segs) {
@@ -476,16 +502,16 @@ __global__ __launch_bounds__(kThreads) void k_stream_grouped(const MatDev* __res
   const uint32_t s0 = blockseg[blockIdx.x], s1 = blockseg[blockIdx.x + 1];
   for (uint32_t s = s0; s < s1; ++s) {
     const Seg sg = segs[s];
-    run_segment_2bit<XT, RB>(descs[sg.mat], sg.row0, sg.row1, sm);
+    run_segment_2bit<XT, SF, K, RB>(descs[sg.mat], sg.row0, sg.row1, sm);
   }
 }
 
-template <int XT, int RB>
+template <int XT, int SF, int K, int RB>
 __global__ __launch_bounds__(kThreads) void k_stream_single(MatDev d, uint32_t rows_per_block) {
   __shared__ StreamSmem sm;
   const uint32_t r0 = blockIdx.x * rows_per_block;
   const uint32_t r1 = min(d.out, r0 + rows_per_block);
-  if (r0 < r1) run_segment_2bit<XT, RB>(d, r0, r1, sm);
+  if (r0 < r1) run_segment_2bit<XT, SF, K, RB>(d, r0, r1, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -588,9 +614,49 @@ int launch_status() {
 
 constexpr int kRB = 4;   // rows per batch of the streaming kernels
 
+// (scale format, k) class of a matrix: 4 * scale_fmt + index of k in {0, 2, 4, 8}.
+uint32_t class_of(const wal_desc& d) {
+  return d.scale_fmt * 4 + (d.k == 0 ? 0 : d.k == 2 ? 1 : d.k == 4 ? 2 : 3);
+}
+
+using GroupedFn = void (*)(const MatDev*, const uint32_t*, const Seg*);
+using SingleFn = void (*)(MatDev, uint32_t);
+
+template <int XT>
+GroupedFn grouped_kernel(uint32_t cls) {
+  switch (cls) {
+    case 0: return k_stream_grouped<XT, WAL_SCALE_FP16, 0, kRB>;
+    case 1: return k_stream_grouped<XT, WAL_SCALE_FP16, 2, kRB>;
+    case 2: return k_stream_grouped<XT, WAL_SCALE_FP16, 4, kRB>;
+    case 3: return k_stream_grouped<XT, WAL_SCALE_FP16, 8, kRB>;
+    case 4: return k_stream_grouped<XT, WAL_SCALE_FP24, 0, kRB>;
+    case 5: return k_stream_grouped<XT, WAL_SCALE_FP24, 2, kRB>;
+    case 6: return k_stream_grouped<XT, WAL_SCALE_FP24, 4, kRB>;
+    default: return k_stream_grouped<XT, WAL_SCALE_FP24, 8, kRB>;
+  }
+}
+template <int XT>
+SingleFn single_kernel(uint32_t cls) {
+  switch (cls) {
+    case 0: return k_stream_single<XT, WAL_SCALE_FP16, 0, kRB>;
+    case 1: return k_stream_single<XT, WAL_SCALE_FP16, 2, kRB>;
+    case 2: return k_stream_single<XT, WAL_SCALE_FP16, 4, kRB>;
+    case 3: return k_stream_single<XT, WAL_SCALE_FP16, 8, kRB>;
+    case 4: return k_stream_single<XT, WAL_SCALE_FP24, 0, kRB>;
+    case 5: return k_stream_single<XT, WAL_SCALE_FP24, 2, kRB>;
+    case 6: return k_stream_single<XT, WAL_SCALE_FP24, 4, kRB>;
+    default: return k_stream_single<XT, WAL_SCALE_FP24, 8, kRB>;
+  }
+}
+GroupedFn grouped_for(int x_dtype, uint32_t cls) {
+  return x_dtype == WAL_X_BF16 ? grouped_kernel<WAL_X_BF16>(cls) : grouped_kernel<WAL_X_F32>(cls);
+}
+SingleFn single_for(int x_dtype, uint32_t cls) {
+  return x_dtype == WAL_X_BF16 ? single_kernel<WAL_X_BF16>(cls) : single_kernel<WAL_X_F32>(cls);
+}
+
 // Workgroups of a streaming kernel that the current device holds at once.
-template <typename K>
-int resident_blocks(K kernel, uint32_t* out) {
+int resident_blocks(const void* kernel, uint32_t* out) {
   int dev = 0, cus = 0, per = 0;
   if (hipGetDevice(&dev) != hipSuccess) return WAL_ERR_DEVICE;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return WAL_ERR_DEVICE;
@@ -598,11 +664,6 @@ int resident_blocks(K kernel, uint32_t* out) {
   if (cus <= 0 || per <= 0) return WAL_ERR_DEVICE;
   *out = (uint32_t)(cus * per);
   return WAL_OK;
-}
-
-int resident_for(int x_dtype, uint32_t* out) {
-  if (x_dtype == WAL_X_BF16) return resident_blocks(k_stream_grouped<WAL_X_BF16, kRB>, out);
-  return resident_blocks(k_stream_grouped<WAL_X_F32, kRB>, out);
 }
 
 // Bytes one row of a matrix contributes to the stream (codes, sites, scales, U).
@@ -621,22 +682,56 @@ uint64_t count_zjobs(uint32_t n, const wal_info* infos) {
   return j;
 }
 
-struct PlanLayout {
-  uint64_t off_descs, off_blockseg, off_segs, off_zjobs, bytes;
-};
-
-PlanLayout plan_layout(uint32_t n, uint32_t grid, uint64_t max_segs, uint64_t zjobs) {
-  PlanLayout L;
-  L.off_descs = up64(sizeof(PlanHeader), 64);
-  L.off_blockseg = L.off_descs + up64((uint64_t)n * sizeof(MatDev), 64);
-  L.off_segs = L.off_blockseg + up64(4ull * (grid + 1), 64);
-  L.off_zjobs = L.off_segs + up64(max_segs * sizeof(Seg), 64);
-  L.bytes = L.off_zjobs + up64(zjobs * 4, 64);
-  return L;
-}
-
 int check_blob_size(const wal_info* f) {
   if (f->total_bytes - f->off_codes >= (1ull << 32)) return WAL_ERR_UNSUPPORTED;
+  return WAL_OK;
+}
+
+// Layout of a grouped plan: header | MatDev[n] | zjobs | per class:
+// blockseg[grid + 1] | segs[matrices of the class + grid].
+struct PlanShape {
+  uint32_t n_classes;
+  uint32_t cls[WAL_MAX_CLASSES], grid[WAL_MAX_CLASSES], mats[WAL_MAX_CLASSES];
+  uint64_t off_descs, off_zjobs, off_blockseg[WAL_MAX_CLASSES], off_segs[WAL_MAX_CLASSES], bytes;
+};
+
+int plan_shape(uint32_t n, const wal_info* infos, uint32_t grid, int x_dtype, PlanShape* P) {
+  std::memset(P, 0, sizeof(*P));
+  uint64_t rows[WAL_MAX_CLASSES] = {0};
+  uint32_t mats[WAL_MAX_CLASSES] = {0};
+  for (uint32_t i = 0; i < n; ++i) {
+    const uint32_t c = class_of(infos[i].d);
+    rows[c] += infos[i].d.out;
+    ++mats[c];
+  }
+  for (uint32_t c = 0; c < WAL_MAX_CLASSES; ++c) {
+    if (!mats[c]) continue;
+    uint32_t g = grid;
+    if (!g) {
+      uint32_t res = 0;
+      int st = resident_blocks(reinterpret_cast<const void*>(grouped_for(x_dtype, c)), &res);
+      if (st) return st;
+      const uint64_t by_rows = (rows[c] + 15) / 16;
+      g = (uint32_t)(by_rows < res ? by_rows : res);
+      if (!g) g = 1;
+    }
+    const uint32_t k = P->n_classes++;
+    P->cls[k] = c;
+    P->grid[k] = g;
+    P->mats[k] = mats[c];
+  }
+  uint64_t off = up64(sizeof(PlanHeader), 64);
+  P->off_descs = off;
+  off += up64((uint64_t)n * sizeof(MatDev), 64);
+  P->off_zjobs = off;
+  off += up64(count_zjobs(n, infos) * 4, 64);
+  for (uint32_t k = 0; k < P->n_classes; ++k) {
+    P->off_blockseg[k] = off;
+    off += up64(4ull * (P->grid[k] + 1), 64);
+    P->off_segs[k] = off;
+    off += up64((uint64_t)(P->mats[k] + P->grid[k]) * sizeof(Seg), 64);
+  }
+  P->bytes = off;
   return WAL_OK;
 }
 
@@ -666,17 +761,15 @@ int wal_gemv(const wal_info* info, const void* W_dev, const void* x_dev, int x_d
     else hipLaunchKernelGGL(k_z_single<WAL_X_F32>, dim3(g), dim3(kThreads), 0, s, d);
     if ((st = launch_status())) return st;
   }
+  const uint32_t cls = class_of(info->d);
   uint32_t resident = 0;
-  if ((st = resident_for(x_dtype, &resident))) return st;
+  if ((st = resident_blocks(reinterpret_cast<const void*>(grouped_for(x_dtype, cls)), &resident))) return st;
   uint32_t rpb = (d.out + resident - 1) / resident;
   const uint32_t min_rows = kWaves * kRB * 2;
   if (rpb < min_rows) rpb = min_rows;
   rpb = (rpb + kRB - 1) / kRB * kRB;
   const uint32_t grid = (d.out + rpb - 1) / rpb;
-  if (x_dtype == WAL_X_BF16)
-    hipLaunchKernelGGL((k_stream_single<WAL_X_BF16, kRB>), dim3(grid), dim3(kThreads), 0, s, d, rpb);
-  else
-    hipLaunchKernelGGL((k_stream_single<WAL_X_F32, kRB>), dim3(grid), dim3(kThreads), 0, s, d, rpb);
+  hipLaunchKernelGGL(single_for(x_dtype, cls), dim3(grid), dim3(kThreads), 0, s, d, rpb);
   return launch_status();
 }
 
@@ -694,9 +787,10 @@ int wal_gemm_small(const wal_info* info, const void* W_dev, const void* X_dev, i
 }
 
 int wal_grouped_plan_size(uint32_t n, const wal_info* infos, uint32_t grid, int x_dtype, size_t* plan_bytes,
-                          size_t* ws_bytes, uint32_t* grid_out) {
+                          size_t* ws_bytes) {
   if (!n || !infos || !plan_bytes || !ws_bytes) return WAL_ERR_ARG;
   if (x_dtype != WAL_X_F32 && x_dtype != WAL_X_BF16) return WAL_ERR_ARG;
+  if (n > (1u << 24)) return WAL_ERR_ARG;
   uint64_t ws = 0;
   for (uint32_t i = 0; i < n; ++i) {
     int st = check_info(&infos[i]);
@@ -704,15 +798,11 @@ int wal_grouped_plan_size(uint32_t n, const wal_info* infos, uint32_t grid, int 
     if ((st = check_blob_size(&infos[i]))) return st;
     ws += up64(4ull * infos[i].d.n_paths * infos[i].d.rank, 16);
   }
-  if (n > (1u << 24)) return WAL_ERR_ARG;
-  if (grid == 0) {
-    int st = resident_for(x_dtype, &grid);
-    if (st) return st;
-  }
-  const PlanLayout L = plan_layout(n, grid, (uint64_t)n + grid, count_zjobs(n, infos));
-  *plan_bytes = (size_t)L.bytes;
+  PlanShape P;
+  int st = plan_shape(n, infos, grid, x_dtype, &P);
+  if (st) return st;
+  *plan_bytes = (size_t)P.bytes;
   *ws_bytes = (size_t)up64(ws, 256);
-  if (grid_out) *grid_out = grid;
   return WAL_OK;
 }
 
@@ -720,7 +810,7 @@ int wal_grouped_plan(uint32_t n, const wal_info* infos, const void* const* W_dev
                      int x_dtype, float* const* y_dev, void* ws_dev, size_t ws_bytes, uint32_t grid,
                      void* plan_host, size_t plan_bytes, wal_grouped_info* ginfo) {
   size_t need_plan = 0, need_ws = 0;
-  int st = wal_grouped_plan_size(n, infos, grid, x_dtype, &need_plan, &need_ws, &grid);
+  int st = wal_grouped_plan_size(n, infos, grid, x_dtype, &need_plan, &need_ws);
   if (st) return st;
   if (!W_dev || !x_dev || !y_dev || !plan_host || !ginfo) return WAL_ERR_ARG;
   if (plan_bytes < need_plan) return WAL_ERR_BUFFER;
@@ -735,85 +825,106 @@ int wal_grouped_plan(uint32_t n, const wal_info* infos, const void* const* W_dev
       return WAL_ERR_ARG;
   }
   if (tf != WAL_TRIT_2BIT) return WAL_ERR_UNSUPPORTED;
-  const uint64_t zjobs = count_zjobs(n, infos);
-  const PlanLayout L = plan_layout(n, grid, (uint64_t)n + grid, zjobs);
+  PlanShape P;
+  if ((st = plan_shape(n, infos, grid, x_dtype, &P))) return st;
   uint8_t* base = static_cast<uint8_t*>(plan_host);
-  std::memset(base, 0, L.bytes);
+  std::memset(base, 0, P.bytes);
   PlanHeader* h = reinterpret_cast<PlanHeader*>(base);
-  MatDev* descs = reinterpret_cast<MatDev*>(base + L.off_descs);
-  uint32_t* blockseg = reinterpret_cast<uint32_t*>(base + L.off_blockseg);
-  Seg* segs = reinterpret_cast<Seg*>(base + L.off_segs);
-  uint32_t* jobs = reinterpret_cast<uint32_t*>(base + L.off_zjobs);
+  MatDev* descs = reinterpret_cast<MatDev*>(base + P.off_descs);
+  uint32_t* jobs = reinterpret_cast<uint32_t*>(base + P.off_zjobs);
 
   // descriptors and low-rank jobs
-  uint64_t zoff = 0, j = 0, total = 0;
+  uint64_t zoff = 0, j = 0;
   for (uint32_t i = 0; i < n; ++i) {
     const uint32_t T = infos[i].d.n_paths * infos[i].d.rank;
     float* z = T ? static_cast<float*>(ws_dev) + zoff / 4 : nullptr;
     descs[i] = make_dev(&infos[i], W_dev[i], x_dev[i], y_dev[i], z, infos[i].d.in, infos[i].d.out, 1);
     zoff += up64(4ull * T, 16);
     for (uint32_t t0 = 0; t0 < T; t0 += kZTerms) jobs[j++] = (i << 8) | t0;
-    total += row_bytes(infos[i]) * infos[i].d.out;
   }
 
-  // Split the rows of all matrices, in order, into `grid` ranges of equal
-  // streamed bytes; block b owns the segments between boundaries b and b + 1.
-  auto boundary = [&](uint32_t b, uint32_t* mat, uint32_t* row) {
-    const unsigned __int128 pos128 = (unsigned __int128)total * b / grid;
-    uint64_t pos = (uint64_t)pos128, acc = 0;
-    for (uint32_t i = 0; i < n; ++i) {
-      const uint64_t rb = row_bytes(infos[i]), mb = rb * infos[i].d.out;
-      if (pos < acc + mb) {
-        uint64_t r = (pos - acc + rb / 2) / rb;
-        if (r >= infos[i].d.out) { *mat = i + 1; *row = 0; }
-        else { *mat = i; *row = (uint32_t)r; }
-        return;
+  std::memset(ginfo, 0, sizeof(*ginfo));
+  uint32_t nseg_total = 0, gmax = 0;
+  for (uint32_t k = 0; k < P.n_classes; ++k) {
+    // The class's matrices in order; their rows are split into grid ranges
+    // of equal streamed bytes, one per workgroup.
+    const uint32_t c = P.cls[k], G = P.grid[k];
+    uint32_t* blockseg = reinterpret_cast<uint32_t*>(base + P.off_blockseg[k]);
+    Seg* segs = reinterpret_cast<Seg*>(base + P.off_segs[k]);
+    uint64_t total = 0;
+    for (uint32_t i = 0; i < n; ++i)
+      if (class_of(infos[i].d) == c) total += row_bytes(infos[i]) * infos[i].d.out;
+    // boundary b: (matrix, row) where the b-th range starts; mat == n past the end
+    auto boundary = [&](uint32_t b, uint32_t* mat, uint32_t* row) {
+      const uint64_t pos = (uint64_t)((unsigned __int128)total * b / G);
+      uint64_t acc = 0;
+      for (uint32_t i = 0; i < n; ++i) {
+        if (class_of(infos[i].d) != c) continue;
+        const uint64_t rb = row_bytes(infos[i]), mb = rb * infos[i].d.out;
+        if (pos < acc + mb) {
+          const uint64_t r = (pos - acc + rb / 2) / rb;
+          *mat = i;
+          *row = (uint32_t)r;
+          if (r >= infos[i].d.out) {   // rounds to the next matrix of the class
+            uint32_t nx = i + 1;
+            while (nx < n && class_of(infos[nx].d) != c) ++nx;
+            *mat = nx;
+            *row = 0;
+          }
+          return;
+        }
+        acc += mb;
       }
-      acc += mb;
+      *mat = n;
+      *row = 0;
+    };
+    uint32_t nseg = 0, m0 = 0, r0 = 0;
+    boundary(0, &m0, &r0);
+    for (uint32_t b = 0; b < G; ++b) {
+      blockseg[b] = nseg;
+      uint32_t m1 = 0, r1 = 0;
+      boundary(b + 1, &m1, &r1);
+      for (uint32_t m = m0; m < n && m <= m1; ++m) {
+        if (class_of(infos[m].d) != c) continue;
+        const uint32_t rs = m == m0 ? r0 : 0;
+        const uint32_t re = m == m1 ? r1 : infos[m].d.out;
+        if (rs < re) segs[nseg++] = Seg{m, rs, re, 0};
+      }
+      m0 = m1;
+      r0 = r1;
     }
-    *mat = n; *row = 0;
-  };
-  uint32_t nseg = 0, m0 = 0, r0 = 0;
-  boundary(0, &m0, &r0);
-  for (uint32_t b = 0; b < grid; ++b) {
-    blockseg[b] = nseg;
-    uint32_t m1 = 0, r1 = 0;
-    boundary(b + 1, &m1, &r1);
-    uint32_t m = m0, r = r0;
-    while (m < m1 || (m == m1 && r < r1)) {
-      const uint32_t end = m < m1 ? infos[m].d.out : r1;
-      if (r < end) segs[nseg++] = Seg{m, r, end, 0};
-      ++m;
-      r = 0;
-      if (m > m1) break;
-    }
-    m0 = m1;
-    r0 = r1;
+    blockseg[G] = nseg;
+    ginfo->class_id[k] = c;
+    ginfo->class_grid[k] = G;
+    ginfo->class_blockseg[k] = P.off_blockseg[k];
+    ginfo->class_segs[k] = P.off_segs[k];
+    nseg_total += nseg;
+    if (G > gmax) gmax = G;
   }
-  blockseg[grid] = nseg;
 
   h->magic = kPlanMagic;
   h->n = n;
-  h->grid = grid;
-  h->n_segs = nseg;
-  h->n_zjobs = (uint32_t)zjobs;
+  h->grid = gmax;
+  h->n_segs = nseg_total;
+  h->n_zjobs = (uint32_t)j;
   h->x_dtype = (uint32_t)x_dtype;
   h->trit_fmt = tf;
-  h->off_descs = L.off_descs;
-  h->off_blockseg = L.off_blockseg;
-  h->off_segs = L.off_segs;
-  h->off_zjobs = L.off_zjobs;
-  h->bytes = L.bytes;
+  h->reserved = P.n_classes;
+  h->off_descs = P.off_descs;
+  h->off_zjobs = P.off_zjobs;
+  h->bytes = P.bytes;
 
-  std::memset(ginfo, 0, sizeof(*ginfo));
   ginfo->n = n;
-  ginfo->grid = grid;
-  ginfo->n_segs = nseg;
-  ginfo->n_zjobs = (uint32_t)zjobs;
+  ginfo->n_classes = P.n_classes;
+  ginfo->n_segs = nseg_total;
+  ginfo->n_zjobs = (uint32_t)j;
   ginfo->x_dtype = (uint32_t)x_dtype;
   ginfo->trit_fmt = tf;
   ginfo->rows_per_batch = kRB;
-  ginfo->plan_bytes = L.bytes;
+  ginfo->grid = gmax;
+  ginfo->plan_bytes = P.bytes;
+  ginfo->off_descs = P.off_descs;
+  ginfo->off_zjobs = P.off_zjobs;
   uint64_t alg = 0;
   for (uint32_t i = 0; i < n; ++i) alg += infos[i].algorithmic_bytes;
   ginfo->algorithmic_bytes = alg;
@@ -823,16 +934,17 @@ int wal_grouped_plan(uint32_t n, const wal_info* infos, const void* const* W_dev
 int wal_gemv_grouped(const wal_grouped_info* g, const void* plan_dev, void* stream) {
   if (!g || !plan_dev) return WAL_ERR_ARG;
   if (!aligned(plan_dev, 16)) return WAL_ERR_ALIGN;
-  if (g->x_dtype > WAL_X_BF16 || g->trit_fmt != WAL_TRIT_2BIT || !g->n || !g->grid) return WAL_ERR_ARG;
-  if (g->rows_per_batch != (uint32_t)kRB) return WAL_ERR_ARG;
+  if (g->x_dtype > WAL_X_BF16 || g->trit_fmt != WAL_TRIT_2BIT || !g->n) return WAL_ERR_ARG;
+  if (g->rows_per_batch != (uint32_t)kRB || !g->n_classes || g->n_classes > WAL_MAX_CLASSES) return WAL_ERR_ARG;
+  for (uint32_t k = 0; k < g->n_classes; ++k) {
+    if (g->class_id[k] >= WAL_MAX_CLASSES || !g->class_grid[k]) return WAL_ERR_ARG;
+    if (g->class_blockseg[k] >= g->plan_bytes || g->class_segs[k] >= g->plan_bytes) return WAL_ERR_ARG;
+  }
+  if (g->off_descs >= g->plan_bytes || (g->n_zjobs && g->off_zjobs >= g->plan_bytes)) return WAL_ERR_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const PlanLayout L = plan_layout(g->n, g->grid, (uint64_t)g->n + g->grid, g->n_zjobs);
-  if (L.bytes != g->plan_bytes) return WAL_ERR_ARG;
   const uint8_t* base = static_cast<const uint8_t*>(plan_dev);
-  const MatDev* descs = reinterpret_cast<const MatDev*>(base + L.off_descs);
-  const uint32_t* blockseg = reinterpret_cast<const uint32_t*>(base + L.off_blockseg);
-  const Seg* segs = reinterpret_cast<const Seg*>(base + L.off_segs);
-  const uint32_t* jobs = reinterpret_cast<const uint32_t*>(base + L.off_zjobs);
+  const MatDev* descs = reinterpret_cast<const MatDev*>(base + g->off_descs);
+  const uint32_t* jobs = reinterpret_cast<const uint32_t*>(base + g->off_zjobs);
   int st;
   if (g->n_zjobs) {
     if (g->x_dtype == WAL_X_BF16)
@@ -841,13 +953,14 @@ int wal_gemv_grouped(const wal_grouped_info* g, const void* plan_dev, void* stre
       hipLaunchKernelGGL(k_z_grouped<WAL_X_F32>, dim3(g->n_zjobs), dim3(kThreads), 0, s, descs, jobs);
     if ((st = launch_status())) return st;
   }
-  if (g->x_dtype == WAL_X_BF16)
-    hipLaunchKernelGGL((k_stream_grouped<WAL_X_BF16, kRB>), dim3(g->grid), dim3(kThreads), 0, s, descs, blockseg,
-                       segs);
-  else
-    hipLaunchKernelGGL((k_stream_grouped<WAL_X_F32, kRB>), dim3(g->grid), dim3(kThreads), 0, s, descs, blockseg,
-                       segs);
-  return launch_status();
+  for (uint32_t k = 0; k < g->n_classes; ++k) {
+    const uint32_t* blockseg = reinterpret_cast<const uint32_t*>(base + g->class_blockseg[k]);
+    const Seg* segs = reinterpret_cast<const Seg*>(base + g->class_segs[k]);
+    hipLaunchKernelGGL(grouped_for((int)g->x_dtype, g->class_id[k]), dim3(g->class_grid[k]), dim3(kThreads), 0, s,
+                       descs, blockseg, segs);
+    if ((st = launch_status())) return st;
+  }
+  return WAL_OK;
 }
 
 }  // extern "C"

@@ -29,11 +29,14 @@ struct MatDev {
 };
 
 // Plan blob written by wal_grouped_plan (host) and read by the kernels:
-//   header | MatDev[n] | blockseg u32[grid + 1] | segs Seg[n_segs] | zjobs u32[n_zjobs]
-// Block b of the main kernel processes segs[blockseg[b] .. blockseg[b + 1]).
+//   header | MatDev[n] | zjobs u32[n_zjobs] | per (scale format, k) class:
+//   blockseg u32[grid + 1] | segs Seg[...]
+// Workgroup b of a class's streaming launch processes its
+// segs[blockseg[b] .. blockseg[b + 1]).  The header is informative only
+// (reserved = number of classes); launches take offsets from wal_grouped_info.
 struct PlanHeader {
   uint32_t magic, n, grid, n_segs, n_zjobs, x_dtype, trit_fmt, reserved;
-  uint64_t off_descs, off_blockseg, off_segs, off_zjobs, bytes;
+  uint64_t off_descs, off_zjobs, bytes;
 };
 struct Seg {
   uint32_t mat, row0, row1, pad;

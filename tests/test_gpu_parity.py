@@ -141,7 +141,7 @@ def grouped(wal, items, x_bf16=True):
     xs = [to_dev(xb.view(np.int16)).view(torch.bfloat16) if x_bf16 else to_dev(xb) for _, _, xb in items]
     ys = [torch.full((i.d.out,), float("nan"), dtype=torch.float32, device=dev()) for _, i, _ in items]
     infos = [i for _, i, _ in items]
-    _, wsb, _ = wal.wal_grouped_plan_size(infos, 0, wal.WAL_X_BF16 if x_bf16 else wal.WAL_X_F32)
+    _, wsb = wal.wal_grouped_plan_size(infos, 0, wal.WAL_X_BF16 if x_bf16 else wal.WAL_X_F32)
     ws = torch.zeros(max(wsb, 4) // 4, dtype=torch.float32, device=dev())
     plan, g = wal.wal_grouped_plan(infos, Ws, xs, ys, ws, wal.WAL_X_BF16 if x_bf16 else wal.WAL_X_F32)
     plan_dev = to_dev(plan)

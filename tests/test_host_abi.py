@@ -233,8 +233,7 @@ def _plan_on_host(infos, grid, x_dtype=wal.WAL_X_BF16):
     import ctypes
     n = len(infos)
     arr = (wal.wal_info * n)(*infos)
-    pb, wsb, g = wal.wal_grouped_plan_size(infos, grid, x_dtype)
-    assert g == grid
+    pb, wsb = wal.wal_grouped_plan_size(infos, grid, x_dtype)
     plan = np.zeros(pb, np.uint8)
     base = 1 << 40
     Wp = (ctypes.c_void_p * n)(*[base + i * (1 << 28) for i in range(n)])
@@ -247,62 +246,78 @@ def _plan_on_host(infos, grid, x_dtype=wal.WAL_X_BF16):
     return plan, ginfo
 
 
-def _plan_segments(plan):
-    magic, n, grid, n_segs, n_zjobs = struct.unpack_from("<5I", plan, 0)
-    off_descs, off_blockseg, off_segs, off_zjobs, nbytes = struct.unpack_from("<5Q", plan, 32)
-    assert nbytes <= plan.size
-    blockseg = np.frombuffer(plan, np.uint32, grid + 1, off_blockseg)
-    segs = np.frombuffer(plan, np.uint32, 4 * n_segs, off_segs).reshape(n_segs, 4)
-    jobs = np.frombuffer(plan, np.uint32, n_zjobs, off_zjobs)
-    return grid, blockseg, segs, jobs
+def _class_of(info):
+    return 4 * info.d.scale_fmt + {0: 0, 2: 1, 4: 2, 8: 3}[info.d.k]
+
+
+def _plan_classes(plan, g):
+    """[(class id, blockseg, segs)] and the low-rank jobs of a plan."""
+    out = []
+    for c in range(g.n_classes):
+        G = g.class_grid[c]
+        blockseg = np.frombuffer(plan, np.uint32, G + 1, g.class_blockseg[c])
+        segs = np.frombuffer(plan, np.uint32, 4 * int(blockseg[-1]), g.class_segs[c]).reshape(-1, 4)
+        out.append((g.class_id[c], blockseg, segs))
+    jobs = np.frombuffer(plan, np.uint32, g.n_zjobs, g.off_zjobs)
+    return out, jobs
 
 
 @pytest.mark.parametrize("grid", [1, 7, 768, 1024, 3000])
 def test_grouped_plan_covers_every_row_once(grid):
-    """The grouped plan splits the rows of all matrices into `grid` contiguous
-    ranges of near-equal packed bytes; every row of every matrix belongs to
-    exactly one workgroup."""
-    shapes = [(4096, 4096, 8, 1, 16), (1024, 4096, 8, 0, 0), (1024, 4096, 8, 1, 16), (4096, 4096, 8, 1, 16),
-              (12288, 4096, 8, 1, 16), (12288, 4096, 8, 0, 0), (4096, 12288, 8, 1, 16), (1, 128, 2, 0, 0),
-              (7, 384, 4, 4, 64)]
-    infos = [wal.wal_packed_size(wal.make_desc(o, i, k, P, r)) for o, i, k, P, r in shapes]
+    """Per (scale format, k) class, the grouped plan splits the rows of the
+    class's matrices into `grid` contiguous ranges of near-equal packed
+    bytes; every row of every matrix belongs to exactly one workgroup of the
+    launch of its class."""
+    shapes = [(4096, 4096, 8, 1, 16, 0), (1024, 4096, 8, 0, 0, 0), (1024, 4096, 8, 1, 16, 0),
+              (4096, 4096, 8, 1, 16, 0), (12288, 4096, 8, 1, 16, 0), (300, 4096, 2, 0, 0, 1),
+              (12288, 4096, 8, 0, 0, 0), (4096, 12288, 8, 1, 16, 0), (1, 128, 2, 0, 0, 0),
+              (7, 384, 4, 4, 64, 0), (129, 512, 2, 1, 8, 1)]
+    infos = [wal.wal_packed_size(wal.make_desc(o, i, k, P, r, scale_fmt=sf)) for o, i, k, P, r, sf in shapes]
     plan, g = _plan_on_host(infos, grid)
-    G, blockseg, segs, jobs = _plan_segments(plan)
-    assert G == grid == g.grid and blockseg[0] == 0 and blockseg[-1] == len(segs) == g.n_segs
-    assert np.all(np.diff(blockseg.astype(np.int64)) >= 0)
+    classes, jobs = _plan_classes(plan, g)
+    assert sorted(c for c, _, _ in classes) == sorted(set(_class_of(i) for i in infos))
+    assert sum(len(sg) for _, _, sg in classes) == g.n_segs
+    rb = [i.d.in_ // 4 + (i.d.in_ // 128) * (i.d.k + (2 if i.d.scale_fmt == 0 else 3) * (2 if i.d.k else 1))
+          + i.d.n_paths * ((i.d.rank + 7) // 8) for i in infos]
     covered = [np.zeros(o, np.int32) for o, *_ in shapes]
-    for m, r0, r1, _ in segs:
-        assert r0 < r1 <= shapes[m][0]
-        covered[m][r0:r1] += 1
+    for c, blockseg, segs in classes:
+        assert len(blockseg) == grid + 1 and blockseg[0] == 0
+        assert np.all(np.diff(blockseg.astype(np.int64)) >= 0)
+        per_block = np.zeros(grid)
+        for b in range(grid):
+            for m, r0, r1, _ in segs[blockseg[b]:blockseg[b + 1]]:
+                assert _class_of(infos[m]) == c
+                assert r0 < r1 <= shapes[m][0]
+                covered[m][r0:r1] += 1
+                per_block[b] += (r1 - r0) * rb[m]
+        # streamed bytes per workgroup are balanced to within a row of the
+        # class's widest matrix
+        members = [m for m in range(len(infos)) if _class_of(infos[m]) == c]
+        ideal = sum(rb[m] * infos[m].d.out for m in members) / grid
+        assert per_block.max() <= ideal + max(rb[m] for m in members) + 1
     for c in covered:
         assert np.all(c == 1)
-    # streamed bytes per workgroup (codes, sites, scales and U bits of its
-    # rows) are balanced to within a row of the widest matrix
-    rb = [i.d.in_ // 4 + (i.d.in_ // 128) * (i.d.k + 2 * (2 if i.d.k else 1)) + i.d.n_paths * ((i.d.rank + 7) // 8)
-          for i in infos]
-    per_block = np.zeros(grid)
-    for b in range(grid):
-        for m, r0, r1, _ in segs[blockseg[b]:blockseg[b + 1]]:
-            per_block[b] += (r1 - r0) * rb[m]
-    ideal = sum(r * i.d.out for r, i in zip(rb, infos)) / grid
-    assert per_block.max() <= ideal + max(rb) + 1
     # one low-rank job per 4 terms of every matrix that has paths
-    want = [(m << 8) | t0 for m, (o, i, k, P, r) in enumerate(shapes) for t0 in range(0, P * r, 4)]
+    want = [(m << 8) | t0 for m, (o, i, k, P, r, sf) in enumerate(shapes) for t0 in range(0, P * r, 4)]
     assert sorted(jobs.tolist()) == sorted(want)
 
 
 def test_grouped_plan_rejects_bad_arguments():
+    import ctypes
     infos = [wal.wal_packed_size(wal.make_desc(64, 256, 8, 1, 16))]
     with pytest.raises(wal.WalError):
-        wal.wal_grouped_plan_size(infos, 16, 7)
-    base3 = [wal.wal_packed_size(wal.make_desc(64, 256, 8, 0, 0, wal.WAL_TRIT_BASE3, wal.WAL_SCALE_FP24))]
-    plan, g = None, None
-    import ctypes
-    arr = (wal.wal_info * 1)(*base3)
-    pb, wsb, _ = wal.wal_grouped_plan_size(base3, 4)
+        wal.wal_grouped_plan_size(infos, 16, 7)                  # x dtype
+    one = (ctypes.c_void_p * 1)(1 << 40)
+    arr = (wal.wal_info * 1)(*infos)
+    pb, wsb = wal.wal_grouped_plan_size(infos, 4)
     buf = np.zeros(pb, np.uint8)
     ginfo = wal.wal_grouped_info()
-    one = (ctypes.c_void_p * 1)(1 << 40)
-    st = wal._lib.wal_grouped_plan(1, arr, one, one, 1, (ctypes.c_void_p * 1)(1 << 41), None, 0, 4,
-                                   buf.ctypes.data, buf.size, ctypes.byref(ginfo))
-    assert st in (0, -9)
+    y = (ctypes.c_void_p * 1)(1 << 41)
+    # workspace missing, plan buffer too small, misaligned x
+    assert wal._lib.wal_grouped_plan(1, arr, one, one, 1, y, None, 0, 4, buf.ctypes.data, buf.size,
+                                     ctypes.byref(ginfo)) == -1
+    assert wal._lib.wal_grouped_plan(1, arr, one, one, 1, y, 1 << 42, wsb, 4, buf.ctypes.data, buf.size - 64,
+                                     ctypes.byref(ginfo)) == -5
+    assert wal._lib.wal_grouped_plan(1, arr, one, (ctypes.c_void_p * 1)((1 << 40) + 2), 1, y, 1 << 42, wsb, 4,
+                                     buf.ctypes.data, buf.size, ctypes.byref(ginfo)) == -6
+    assert wal._lib.wal_gemv_grouped(ctypes.byref(wal.wal_grouped_info()), 1 << 40, None) == -1
