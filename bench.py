@@ -108,10 +108,35 @@ def main():
     print(f"[bench] generated and packed {len(items)} matrices in {time.time() - t0:.1f} s", file=sys.stderr,
           flush=True)
     dev = torch.device("cuda:0")
-    Ws = [torch.from_numpy(b).to(dev) for b, _, _ in items]
-    xs = [torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16) for _, _, xb in items]
-    ys = [torch.empty(i.d.out, dtype=torch.float32, device=dev) for _, i, _ in items]
+    # One device arena for all packed blobs (each 256-byte aligned), one for
+    # the activations and one for the outputs, as a runtime keeps resident
+    # weights; every matrix is a view into them.
     infos = [i for _, i, _ in items]
+    offs, cur = [], 0
+    for b, _, _ in items:
+        offs.append(cur)
+        cur += (b.size + 255) // 256 * 256
+    arena_host = np.zeros(cur, dtype=np.uint8)
+    for (b, _, _), o in zip(items, offs):
+        arena_host[o:o + b.size] = b
+    arena = torch.from_numpy(arena_host).to(dev)
+    del arena_host
+    Ws = [arena[o:o + b.size] for (b, _, _), o in zip(items, offs)]
+    xoffs, xcur = [], 0
+    for _, i, _ in items:
+        xoffs.append(xcur)
+        xcur += (i.d.in_ + 127) // 128 * 128
+    x_host = np.zeros(xcur, dtype=np.uint16)
+    for (_, i, xb), o in zip(items, xoffs):
+        x_host[o:o + i.d.in_] = xb
+    x_all = torch.from_numpy(x_host.view(np.int16)).to(dev).view(torch.bfloat16)
+    xs = [x_all[o:o + i.d.in_] for (_, i, _), o in zip(items, xoffs)]
+    yoffs, ycur = [], 0
+    for _, i, _ in items:
+        yoffs.append(ycur)
+        ycur += (i.d.out + 63) // 64 * 64
+    y_all = torch.empty(ycur, dtype=torch.float32, device=dev)
+    ys = [y_all[o:o + i.d.out] for (_, i, _), o in zip(items, yoffs)]
     _, wsb = wal.wal_grouped_plan_size(infos)
     ws = torch.zeros(max(wsb, 4) // 4, dtype=torch.float32, device=dev)
     plan, g = wal.wal_grouped_plan(infos, Ws, xs, ys, ws, wal.WAL_X_BF16)

@@ -283,8 +283,10 @@ __device__ __forceinline__ float f16_at(const uint8_t* p, uint32_t i) {
 // ---------------------------------------------------------------------------
 // Shared memory of the streaming kernels.
 struct StreamSmem {
-  float tbl[32 * 256];   // [group of the pass][site byte] -> +-2x (bf16) or +-x (fp32)
-  float z[kMaxTerms];    // low-rank reductions of the current matrix
+  float tbl[32 * 256];      // [group of the pass][site byte] -> +-2x (bf16) or +-x (fp32)
+  float z[kMaxTerms];       // low-rank reductions of the current matrix
+  float ybuf[kSegRows + 64];   // y of the segment's rows, accumulated over passes
+                               // (padded: lanes of a last, partial batch index past it)
 };
 
 // Signed table of one 4096-column pass; groups past the pass width are zero.
@@ -320,7 +322,6 @@ struct RowRaw {
 template <int RB>
 struct Batch {
   RowRaw r[RB];
-  float yprev;      // partial y of earlier passes (row of this lane)
   uint32_t u;       // U byte holding this lane's low-rank sign bit
 };
 
@@ -335,9 +336,13 @@ struct Lane2 {
   bool uon;                   // the lane owns a low-rank term
 };
 
+// One pass of one segment.  The workgroup-wide set-up of the pass (site table,
+// low-rank terms, behind barriers) runs after each wave has issued the loads
+// of its first two batches and of its x columns, so the set-up overlaps the
+// memory latency instead of adding to it.  Every wave reaches both barriers.
 template <int XT, int SF, int K, int RB>
 __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0, uint32_t row1, uint32_t pass,
-                                                 uint32_t npass, const XLane<XT>& xl, const StreamSmem& sm) {
+                                                 uint32_t npass, StreamSmem& sm) {
   constexpr int LOG = ilog2(RB);
   constexpr int SH = 6 - LOG;        // lane >> SH = row of the batch after the reduction
   constexpr int LPR = 64 >> LOG;     // lanes per row after the reduction
@@ -345,8 +350,8 @@ __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0,
   const int lane = threadIdx.x & 63;
   const uint32_t wave = wave_id();
   const uint32_t nb = (row1 - row0 + RB - 1) / RB;
-  uint32_t b = wave;
-  if (b >= nb) return;
+  const bool has_rows = wave < nb;
+  uint32_t b = has_rows ? wave : nb - 1;   // waves without rows prefetch nothing new
 
   const uint32_t pw = min(kPass2bit, d.in - pass * kPass2bit);
   const uint32_t Gp = pw / 128, g0 = pass * (kPass2bit / 128), G = d.groups;
@@ -383,9 +388,14 @@ __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0,
   // would need flat instructions, whose completion the compiler tracks more
   // conservatively): U offsets are taken from the codes plane's resource,
   // which spans the rest of the blob.
-  const __amdgpu_buffer_rsrc_t ry_rs = rsrc(d.y, d.out * 4);
   const uint32_t uoff = (uint32_t)(L.up - d.codes);
   const uint32_t ustride = L.uon ? L.ub : 0;
+  // Passes that need no U bits (all but the last) read them through an
+  // empty resource: out-of-range buffer loads return 0 without a memory
+  // access, and the instruction stream stays the same.
+  const __amdgpu_buffer_rsrc_t u_rs = rsrc(d.codes, last && d.terms ? d.blob_bytes : 0u);
+
+  XLane<XT> xl;
 
   // Every load is unconditional and in bounds (rows past the range repeat
   // the last row of the range), so the compiler never has to merge loaded
@@ -405,8 +415,7 @@ __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0,
       if constexpr (K > 0) r.b = load_scale<SF>(L.rb, L.va, row * L.sa);
     }
     const uint32_t ry = min(base + ((uint32_t)lane >> SH), row1 - 1);
-    B.yprev = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ry_rs, ry * 4, 0, 0));
-    B.u = __builtin_amdgcn_raw_buffer_load_b8(L.rc, uoff + ry * ustride, 0, kStream);
+    B.u = __builtin_amdgcn_raw_buffer_load_b8(u_rs, uoff + ry * ustride, 0, kStream);
     // keep the scheduler from sinking these loads into the next computation
     __builtin_amdgcn_sched_barrier(0);
     return B;
@@ -427,7 +436,8 @@ __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0,
       acc[i] = v;
     }
     float v = treduce<RB>(acc, lane) * XLane<XT>::kHalf;
-    if (!first) v = B.yprev + v;
+    const uint32_t yi = bb * RB + ((uint32_t)lane >> SH);   // row within the segment
+    if (!first) v = sm.ybuf[yi] + v;   // written by this lane in the previous pass
     const uint32_t base = row0 + bb * RB;
     const uint32_t row = base + ((uint32_t)lane >> SH);
     if (last && d.terms) {
@@ -447,16 +457,25 @@ __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0,
       v += group_sum<LPR>(c);
     }
     if ((lane & (LPR - 1)) == 0 && row < row1)
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ry_rs, row * 4, 0, 0);
+      sm.ybuf[yi] = v;
   };
 
   // Three batches in registers: while one is reduced, the next two are in
   // flight.  Past the wave's last batch the prefetch repeats that batch (an
   // L2 hit), keeping every load unconditional.
-  const uint32_t blast = wave + (nb - 1 - wave) / kWaves * kWaves;
+  const uint32_t blast = has_rows ? wave + (nb - 1 - wave) / kWaves * kWaves : b;
   auto ahead = [&](uint32_t bb) { return bb < nb ? bb : blast; };
   Batch<RB> B0 = load_batch(b);
   Batch<RB> B1 = load_batch(ahead(b + kWaves));
+  xl.load(d.x, pass * kPass2bit + 64 * lane, (uint32_t)(64 * lane) < pw);
+
+  __syncthreads();   // readers of the previous table and z are done
+  if (pass == 0)
+    for (uint32_t t = threadIdx.x; t < d.terms; t += kThreads) sm.z[t] = d.z[t];
+  if constexpr (K > 0) build_table<XT>(d.x, pass * kPass2bit, pw, sm.tbl);
+  __syncthreads();
+  if (!has_rows) return;
+
   for (;;) {
     const Batch<RB> B2 = load_batch(ahead(b + 2 * kWaves));
     finish_batch(B0, b);
@@ -480,18 +499,12 @@ __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0,
 template <int XT, int SF, int K, int RB>
 __device__ __forceinline__ void run_segment_2bit(const MatDev& d, uint32_t row0, uint32_t row1, StreamSmem& sm) {
   const uint32_t npass = (d.in + kPass2bit - 1) / kPass2bit;
-  const int lane = threadIdx.x & 63;
-  for (uint32_t pass = 0; pass < npass; ++pass) {
-    const uint32_t pw = min(kPass2bit, d.in - pass * kPass2bit);
-    __syncthreads();   // readers of the previous table and z are done
-    if (pass == 0)
-      for (uint32_t t = threadIdx.x; t < d.terms; t += kThreads) sm.z[t] = d.z[t];
-    if constexpr (K > 0) build_table<XT>(d.x, pass * kPass2bit, pw, sm.tbl);
-    __syncthreads();
-    XLane<XT> xl;
-    xl.load(d.x, pass * kPass2bit + 64 * lane, (uint32_t)(64 * lane) < pw);
-    stream_rows_2bit<XT, SF, K, RB>(d, row0, row1, pass, npass, xl, sm);
-  }
+  for (uint32_t pass = 0; pass < npass; ++pass) stream_rows_2bit<XT, SF, K, RB>(d, row0, row1, pass, npass, sm);
+  // y leaves through LDS: one coalesced write of the segment's rows instead
+  // of a few scattered bytes per batch of rows.
+  __syncthreads();
+  const uint32_t nrows = row1 - row0;
+  for (uint32_t i = threadIdx.x; i < nrows; i += kThreads) d.y[row0 + i] = sm.ybuf[i];
 }
 
 template <int XT, int SF, int K, int RB>
@@ -692,6 +705,7 @@ int check_blob_size(const wal_info* f) {
 struct PlanShape {
   uint32_t n_classes;
   uint32_t cls[WAL_MAX_CLASSES], grid[WAL_MAX_CLASSES], mats[WAL_MAX_CLASSES];
+  uint64_t rows[WAL_MAX_CLASSES];
   uint64_t off_descs, off_zjobs, off_blockseg[WAL_MAX_CLASSES], off_segs[WAL_MAX_CLASSES], bytes;
 };
 
@@ -719,6 +733,7 @@ int plan_shape(uint32_t n, const wal_info* infos, uint32_t grid, int x_dtype, Pl
     P->cls[k] = c;
     P->grid[k] = g;
     P->mats[k] = mats[c];
+    P->rows[k] = rows[c];
   }
   uint64_t off = up64(sizeof(PlanHeader), 64);
   P->off_descs = off;
@@ -729,7 +744,7 @@ int plan_shape(uint32_t n, const wal_info* infos, uint32_t grid, int x_dtype, Pl
     P->off_blockseg[k] = off;
     off += up64(4ull * (P->grid[k] + 1), 64);
     P->off_segs[k] = off;
-    off += up64((uint64_t)(P->mats[k] + P->grid[k]) * sizeof(Seg), 64);
+    off += up64(((uint64_t)P->mats[k] + P->grid[k] + P->rows[k] / kSegRows + 1) * sizeof(Seg), 64);
   }
   P->bytes = off;
   return WAL_OK;
@@ -768,6 +783,7 @@ int wal_gemv(const wal_info* info, const void* W_dev, const void* x_dev, int x_d
   const uint32_t min_rows = kWaves * kRB * 2;
   if (rpb < min_rows) rpb = min_rows;
   rpb = (rpb + kRB - 1) / kRB * kRB;
+  if (rpb > kSegRows) rpb = kSegRows;
   const uint32_t grid = (d.out + rpb - 1) / rpb;
   hipLaunchKernelGGL(single_for(x_dtype, cls), dim3(grid), dim3(kThreads), 0, s, d, rpb);
   return launch_status();
@@ -888,7 +904,7 @@ int wal_grouped_plan(uint32_t n, const wal_info* infos, const void* const* W_dev
         if (class_of(infos[m].d) != c) continue;
         const uint32_t rs = m == m0 ? r0 : 0;
         const uint32_t re = m == m1 ? r1 : infos[m].d.out;
-        if (rs < re) segs[nseg++] = Seg{m, rs, re, 0};
+        for (uint32_t r = rs; r < re; r += kSegRows) segs[nseg++] = Seg{m, r, re - r > kSegRows ? r + kSegRows : re, 0};
       }
       m0 = m1;
       r0 = r1;
