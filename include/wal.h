@@ -116,12 +116,13 @@ typedef struct {
                                  alignment or base-3 row padding)           */
 } wal_info;
 
-#define WAL_MAX_CLASSES 8
+#define WAL_MAX_CLASSES 16
 
 /* Launch summary of a grouped plan (filled by wal_grouped_plan).  Matrices
- * are grouped by (scale format, k) class, class id = 4 * scale_fmt + index
- * of k in {0, 2, 4, 8}; each class present gets one streaming launch over
- * its own split of rows into class_grid[c] workgroups. */
+ * are grouped by kernel class, class id = 8 * trit_fmt + 4 * scale_fmt +
+ * index of k in {0, 2, 4, 8}; each class present gets one streaming launch
+ * over its own split of rows into class_grid[c] workgroups.  trit_fmt is 0
+ * (classes carry the format). */
 typedef struct {
   uint32_t n;              /* matrices                                      */
   uint32_t n_classes;      /* classes present (streaming launches)          */
@@ -221,7 +222,8 @@ int wal_gemm_small(const wal_info* info, const void* W_dev, const void* X_dev, i
  *   2. The caller copies the plan blob into device memory (plan_dev, 16-byte
  *      aligned) and calls wal_gemv_grouped, as often as it likes while the
  *      pointers stay valid.
- * All matrices share x_dtype and trit_fmt.  ws_dev must hold
+ * All matrices share x_dtype; base-3 matrices need bf16 activations
+ * (WAL_ERR_UNSUPPORTED otherwise).  ws_dev must hold
  * wal_grouped_plan_size's ws_bytes.
  * Errors: ARG, SHAPE, ALIGN, BUFFER, UNSUPPORTED, DEVICE. */
 int wal_grouped_plan_size(uint32_t n, const wal_info* infos, uint32_t grid, int x_dtype,

@@ -50,7 +50,7 @@ class wal_info(ctypes.Structure):
                 ("algorithmic_bytes", ctypes.c_uint64)]
 
 
-WAL_MAX_CLASSES = 8
+WAL_MAX_CLASSES = 16
 
 
 class wal_grouped_info(ctypes.Structure):

@@ -20,6 +20,7 @@ LIB = os.path.join(PKG, "libwal.so")
 ARCH = os.environ.get("WAL_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
+HIP_SOURCES = ["wal_gpu.hip", "wal_base3.hip"]
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wno-unused-command-line-argument"]
@@ -38,12 +39,15 @@ def _run(cmd, verbose):
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     host_o = os.path.join(BUILD, "wal_host.o")
-    gpu_o = os.path.join(BUILD, "wal_gpu.o")
     _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-c", os.path.join(CSRC, "wal_host.cpp"),
           "-o", host_o], verbose)
-    _run([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "wal_gpu.hip"), "-o", gpu_o], verbose)
+    objs = [host_o]
+    for src in HIP_SOURCES:
+        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        _run([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
     tmp = LIB + ".tmp"
-    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", host_o, gpu_o, "-o", tmp], verbose)
+    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -1,0 +1,161 @@
+// Device helpers shared by the HIP kernels of libwal (gfx950, wave64):
+// cross-lane reductions, buffer resources, scale decoding.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "wal_internal.h"
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x3_t __attribute__((ext_vector_type(3)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+namespace {
+
+using namespace wal;
+
+// ---------------------------------------------------------------------------
+// Cross-lane helpers.
+
+template <int CTRL, int ROWMASK = 0xF>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWMASK, 0xF, false));
+}
+
+constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
+
+__device__ __forceinline__ void swap32_add(float& a, float& b) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  a = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap16_add(float& a, float& b) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  a = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// One butterfly level on lane bit `BIT` (3, 2, 1 or 0) for R values: pairs
+// v[j] and v[j + H] (H = R >> (6 - BIT)), lanes with the bit set keep the
+// second of the pair.
+template <int BIT, int CTRL, int R>
+__device__ __forceinline__ void tlevel(float (&v)[R], int lane) {
+  constexpr int H = R >> (6 - BIT);
+  if constexpr (H >= 1) {
+    const bool hi = (lane >> BIT) & 1;
+#pragma unroll
+    for (int j = 0; j < H; ++j) {
+      const float a = hi ? v[j + H] : v[j];
+      const float b = hi ? v[j] : v[j + H];
+      v[j] = a + dpp<CTRL>(b);
+    }
+  } else {
+    v[0] += dpp<CTRL>(v[0]);
+  }
+}
+
+// Transposed reduction of R per-lane values (R a power of two <= 64): returns,
+// in lane l, the wavefront total of value (l >> (6 - log2 R)).
+template <int R>
+__device__ __forceinline__ float treduce(float (&v)[R], int lane) {
+  if constexpr (R >= 2) {
+#pragma unroll
+    for (int j = 0; j < R / 2; ++j) swap32_add(v[j], v[j + R / 2]);
+  } else {
+    float w = v[0];
+    swap32_add(v[0], w);
+  }
+  if constexpr (R >= 4) {
+#pragma unroll
+    for (int j = 0; j < R / 4; ++j) swap16_add(v[j], v[j + R / 4]);
+  } else {
+    float w = v[0];
+    swap16_add(v[0], w);
+  }
+  tlevel<3, 0x128>(v, lane);   // row_ror:8
+  tlevel<2, 0x141>(v, lane);   // row_half_mirror
+  tlevel<1, 0x4E>(v, lane);    // quad_perm [2,3,0,1]
+  tlevel<0, 0xB1>(v, lane);    // quad_perm [1,0,3,2]
+  return v[0];
+}
+
+// Sum over aligned groups of L lanes (L = 8, 16, 32 or 64); every lane of a
+// group receives the group total.
+template <int L>
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  v += dpp<0x141>(v);
+  if constexpr (L >= 16) v += dpp<0x140>(v);   // row_mirror
+  if constexpr (L >= 32) { float w = v; swap16_add(v, w); }
+  if constexpr (L >= 64) { float w = v; swap32_add(v, w); }
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// ---------------------------------------------------------------------------
+// Buffer loads: a resource over one plane, a per-lane offset and a per-row
+// scalar offset.
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+// Activation element as fp32.
+template <int XT>
+__device__ __forceinline__ float xval(const void* x, uint32_t i) {
+  if constexpr (XT == WAL_X_F32) return reinterpret_cast<const float*>(x)[i];
+  return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(x)[i] << 16);
+}
+
+// 64-bit left shift by a constant.  Written as an instruction so that the
+// compiler does not split it back into two 32-bit shifts (it would, seeing
+// that the bits crossing the halves are masked off afterwards).
+template <int S>
+__device__ __forceinline__ uint64_t shl64(uint64_t v) {
+  if constexpr (S == 0) {
+    return v;
+  } else {
+    uint64_t r;
+    asm("v_lshlrev_b64 %0, %1, %2" : "=v"(r) : "n"(S), "v"(v));
+    return r;
+  }
+}
+
+// p-th entry of a per-path pointer array, without dynamic indexing (which
+// would move the descriptor to scratch memory).
+__device__ __forceinline__ const uint8_t* path_ptr(const uint8_t* const (&a)[WAL_MAX_PATHS], uint32_t p) {
+  return p == 0 ? a[0] : p == 1 ? a[1] : p == 2 ? a[2] : a[3];
+}
+
+// ---------------------------------------------------------------------------
+// Scales: fp16 (2 bytes) or fp24 (the upper 3 bytes of an fp32 pattern).
+
+// Cache policy of the packed-weight loads: non-temporal.  Every packed byte
+// is read once per product, and marking the stream non-temporal lifts a
+// plain streaming read on MI355X from about 6.2 to 7.0 TB/s.
+constexpr int kStream = 2;
+
+template <int SF>
+__device__ __forceinline__ uint32_t load_scale(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  if constexpr (SF == WAL_SCALE_FP16) return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, kStream);
+  const uint32_t b0 = __builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, kStream);
+  const uint32_t b1 = __builtin_amdgcn_raw_buffer_load_b8(r, voff + 1, soff, kStream);
+  const uint32_t b2 = __builtin_amdgcn_raw_buffer_load_b8(r, voff + 2, soff, kStream);
+  return b0 | (b1 << 8) | (b2 << 16);
+}
+
+// scale * v + acc in fp32.
+template <int SF>
+__device__ __forceinline__ float scale_fma(uint32_t raw, float v, float acc) {
+  if constexpr (SF == WAL_SCALE_FP16)
+    return __builtin_fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)raw), v, acc);
+  return __builtin_fmaf(__uint_as_float(raw << 8), v, acc);
+}
+
+__device__ __forceinline__ float f16_at(const uint8_t* p, uint32_t i) {
+  return (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(p)[i]);
+}
+
+
+}  // namespace

@@ -40,121 +40,12 @@
 #include <atomic>
 #include <cstring>
 
+#include "wal_device.h"
 #include "wal_internal.h"
 
 using namespace wal;
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-
 namespace {
-
-// ---------------------------------------------------------------------------
-// Cross-lane helpers.
-
-template <int CTRL, int ROWMASK = 0xF>
-__device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWMASK, 0xF, false));
-}
-
-constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
-
-__device__ __forceinline__ void swap32_add(float& a, float& b) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-  a = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ void swap16_add(float& a, float& b) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-  a = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// One butterfly level on lane bit `BIT` (3, 2, 1 or 0) for R values: pairs
-// v[j] and v[j + H] (H = R >> (6 - BIT)), lanes with the bit set keep the
-// second of the pair.
-template <int BIT, int CTRL, int R>
-__device__ __forceinline__ void tlevel(float (&v)[R], int lane) {
-  constexpr int H = R >> (6 - BIT);
-  if constexpr (H >= 1) {
-    const bool hi = (lane >> BIT) & 1;
-#pragma unroll
-    for (int j = 0; j < H; ++j) {
-      const float a = hi ? v[j + H] : v[j];
-      const float b = hi ? v[j] : v[j + H];
-      v[j] = a + dpp<CTRL>(b);
-    }
-  } else {
-    v[0] += dpp<CTRL>(v[0]);
-  }
-}
-
-// Transposed reduction of R per-lane values (R a power of two <= 64): returns,
-// in lane l, the wavefront total of value (l >> (6 - log2 R)).
-template <int R>
-__device__ __forceinline__ float treduce(float (&v)[R], int lane) {
-  if constexpr (R >= 2) {
-#pragma unroll
-    for (int j = 0; j < R / 2; ++j) swap32_add(v[j], v[j + R / 2]);
-  } else {
-    float w = v[0];
-    swap32_add(v[0], w);
-  }
-  if constexpr (R >= 4) {
-#pragma unroll
-    for (int j = 0; j < R / 4; ++j) swap16_add(v[j], v[j + R / 4]);
-  } else {
-    float w = v[0];
-    swap16_add(v[0], w);
-  }
-  tlevel<3, 0x128>(v, lane);   // row_ror:8
-  tlevel<2, 0x141>(v, lane);   // row_half_mirror
-  tlevel<1, 0x4E>(v, lane);    // quad_perm [2,3,0,1]
-  tlevel<0, 0xB1>(v, lane);    // quad_perm [1,0,3,2]
-  return v[0];
-}
-
-// Sum over aligned groups of L lanes (L = 8, 16, 32 or 64); every lane of a
-// group receives the group total.
-template <int L>
-__device__ __forceinline__ float group_sum(float v) {
-  v += dpp<0xB1>(v);
-  v += dpp<0x4E>(v);
-  v += dpp<0x141>(v);
-  if constexpr (L >= 16) v += dpp<0x140>(v);   // row_mirror
-  if constexpr (L >= 32) { float w = v; swap16_add(v, w); }
-  if constexpr (L >= 64) { float w = v; swap32_add(v, w); }
-  return v;
-}
-
-__device__ __forceinline__ uint32_t wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
-
-// ---------------------------------------------------------------------------
-// Buffer loads: a resource over one plane, a per-lane offset and a per-row
-// scalar offset.
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
-}
-
-// Activation element as fp32.
-template <int XT>
-__device__ __forceinline__ float xval(const void* x, uint32_t i) {
-  if constexpr (XT == WAL_X_F32) return reinterpret_cast<const float*>(x)[i];
-  return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(x)[i] << 16);
-}
-
-// 64-bit left shift by a constant.  Written as an instruction so that the
-// compiler does not split it back into two 32-bit shifts (it would, seeing
-// that the bits crossing the halves are masked off afterwards).
-template <int S>
-__device__ __forceinline__ uint64_t shl64(uint64_t v) {
-  if constexpr (S == 0) {
-    return v;
-  } else {
-    uint64_t r;
-    asm("v_lshlrev_b64 %0, %1, %2" : "=v"(r) : "n"(S), "v"(v));
-    return r;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // A lane's 64 activation columns of one pass, held in registers.
@@ -244,41 +135,6 @@ template <> struct XLane<WAL_X_F32> {
     return (acc[0] + acc[1]) + (acc[2] + acc[3]);
   }
 };
-
-// p-th entry of a per-path pointer array, without dynamic indexing (which
-// would move the descriptor to scratch memory).
-__device__ __forceinline__ const uint8_t* path_ptr(const uint8_t* const (&a)[WAL_MAX_PATHS], uint32_t p) {
-  return p == 0 ? a[0] : p == 1 ? a[1] : p == 2 ? a[2] : a[3];
-}
-
-// ---------------------------------------------------------------------------
-// Scales: fp16 (2 bytes) or fp24 (the upper 3 bytes of an fp32 pattern).
-
-// Cache policy of the packed-weight loads: non-temporal.  Every packed byte
-// is read once per product, and marking the stream non-temporal lifts a
-// plain streaming read on MI355X from about 6.2 to 7.0 TB/s.
-constexpr int kStream = 2;
-
-template <int SF>
-__device__ __forceinline__ uint32_t load_scale(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  if constexpr (SF == WAL_SCALE_FP16) return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, kStream);
-  const uint32_t b0 = __builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, kStream);
-  const uint32_t b1 = __builtin_amdgcn_raw_buffer_load_b8(r, voff + 1, soff, kStream);
-  const uint32_t b2 = __builtin_amdgcn_raw_buffer_load_b8(r, voff + 2, soff, kStream);
-  return b0 | (b1 << 8) | (b2 << 16);
-}
-
-// scale * v + acc in fp32.
-template <int SF>
-__device__ __forceinline__ float scale_fma(uint32_t raw, float v, float acc) {
-  if constexpr (SF == WAL_SCALE_FP16)
-    return __builtin_fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)raw), v, acc);
-  return __builtin_fmaf(__uint_as_float(raw << 8), v, acc);
-}
-
-__device__ __forceinline__ float f16_at(const uint8_t* p, uint32_t i) {
-  return (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(p)[i]);
-}
 
 // ---------------------------------------------------------------------------
 // Shared memory of the streaming kernels.
@@ -625,15 +481,16 @@ int launch_status() {
   return e == hipSuccess ? WAL_OK : WAL_ERR_DEVICE;
 }
 
-constexpr int kRB = 4;   // rows per batch of the streaming kernels
+constexpr int kRB = 4;   // rows per batch of the 2-bit streaming kernels
+constexpr uint32_t kClasses = 16;   // kernel classes (see class_of)
 
-// (scale format, k) class of a matrix: 4 * scale_fmt + index of k in {0, 2, 4, 8}.
+// Kernel class of a matrix: 8 * trit_fmt + 4 * scale_fmt + index of k in {0, 2, 4, 8}.
 uint32_t class_of(const wal_desc& d) {
-  return d.scale_fmt * 4 + (d.k == 0 ? 0 : d.k == 2 ? 1 : d.k == 4 ? 2 : 3);
+  return d.trit_fmt * 8 + d.scale_fmt * 4 + (d.k == 0 ? 0 : d.k == 2 ? 1 : d.k == 4 ? 2 : 3);
 }
 
-using GroupedFn = void (*)(const MatDev*, const uint32_t*, const Seg*);
-using SingleFn = void (*)(MatDev, uint32_t);
+// Longest row range one workgroup of a class takes (its y is staged in LDS).
+uint32_t seg_rows(uint32_t cls) { return cls >= 8 ? base3_seg_rows() : kSegRows; }
 
 template <int XT>
 GroupedFn grouped_kernel(uint32_t cls) {
@@ -661,10 +518,14 @@ SingleFn single_kernel(uint32_t cls) {
     default: return k_stream_single<XT, WAL_SCALE_FP24, 8, kRB>;
   }
 }
+// Streaming kernel of a class; NULL when the combination is not built
+// (base-3 codes take bf16 activations only).
 GroupedFn grouped_for(int x_dtype, uint32_t cls) {
+  if (cls >= 8) return x_dtype == WAL_X_BF16 ? base3_grouped_kernel(cls) : nullptr;
   return x_dtype == WAL_X_BF16 ? grouped_kernel<WAL_X_BF16>(cls) : grouped_kernel<WAL_X_F32>(cls);
 }
 SingleFn single_for(int x_dtype, uint32_t cls) {
+  if (cls >= 8) return x_dtype == WAL_X_BF16 ? base3_single_kernel(cls) : nullptr;
   return x_dtype == WAL_X_BF16 ? single_kernel<WAL_X_BF16>(cls) : single_kernel<WAL_X_F32>(cls);
 }
 
@@ -711,15 +572,16 @@ struct PlanShape {
 
 int plan_shape(uint32_t n, const wal_info* infos, uint32_t grid, int x_dtype, PlanShape* P) {
   std::memset(P, 0, sizeof(*P));
-  uint64_t rows[WAL_MAX_CLASSES] = {0};
-  uint32_t mats[WAL_MAX_CLASSES] = {0};
+  uint64_t rows[kClasses] = {0};
+  uint32_t mats[kClasses] = {0};
   for (uint32_t i = 0; i < n; ++i) {
     const uint32_t c = class_of(infos[i].d);
     rows[c] += infos[i].d.out;
     ++mats[c];
   }
-  for (uint32_t c = 0; c < WAL_MAX_CLASSES; ++c) {
+  for (uint32_t c = 0; c < kClasses; ++c) {
     if (!mats[c]) continue;
+    if (!grouped_for(x_dtype, c)) return WAL_ERR_UNSUPPORTED;
     uint32_t g = grid;
     if (!g) {
       uint32_t res = 0;
@@ -744,7 +606,7 @@ int plan_shape(uint32_t n, const wal_info* infos, uint32_t grid, int x_dtype, Pl
     P->off_blockseg[k] = off;
     off += up64(4ull * (P->grid[k] + 1), 64);
     P->off_segs[k] = off;
-    off += up64(((uint64_t)P->mats[k] + P->grid[k] + P->rows[k] / kSegRows + 1) * sizeof(Seg), 64);
+    off += up64(((uint64_t)P->mats[k] + P->grid[k] + P->rows[k] / seg_rows(P->cls[k]) + 1) * sizeof(Seg), 64);
   }
   P->bytes = off;
   return WAL_OK;
@@ -766,8 +628,9 @@ int wal_gemv(const wal_info* info, const void* W_dev, const void* x_dev, int x_d
   if (need && (!ws_dev || ws_bytes < need)) return ws_dev ? WAL_ERR_BUFFER : WAL_ERR_ARG;
   if (need && !aligned(ws_dev, 16)) return WAL_ERR_ALIGN;
   if (overlap(x_dev, (size_t)info->d.in * xelem(x_dtype), y_dev, (size_t)info->d.out * 4)) return WAL_ERR_ARG;
-  if (info->d.trit_fmt != WAL_TRIT_2BIT) return WAL_ERR_UNSUPPORTED;
   if ((st = check_blob_size(info))) return st;
+  const uint32_t cls = class_of(info->d);
+  if (!single_for(x_dtype, cls)) return WAL_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   MatDev d = make_dev(info, W_dev, x_dev, y_dev, static_cast<float*>(ws_dev), info->d.in, info->d.out, 1);
   if (d.terms) {
@@ -776,14 +639,13 @@ int wal_gemv(const wal_info* info, const void* W_dev, const void* x_dev, int x_d
     else hipLaunchKernelGGL(k_z_single<WAL_X_F32>, dim3(g), dim3(kThreads), 0, s, d);
     if ((st = launch_status())) return st;
   }
-  const uint32_t cls = class_of(info->d);
   uint32_t resident = 0;
   if ((st = resident_blocks(reinterpret_cast<const void*>(grouped_for(x_dtype, cls)), &resident))) return st;
   uint32_t rpb = (d.out + resident - 1) / resident;
   const uint32_t min_rows = kWaves * kRB * 2;
   if (rpb < min_rows) rpb = min_rows;
   rpb = (rpb + kRB - 1) / kRB * kRB;
-  if (rpb > kSegRows) rpb = kSegRows;
+  if (rpb > seg_rows(cls)) rpb = seg_rows(cls);
   const uint32_t grid = (d.out + rpb - 1) / rpb;
   hipLaunchKernelGGL(single_for(x_dtype, cls), dim3(grid), dim3(kThreads), 0, s, d, rpb);
   return launch_status();
@@ -832,15 +694,12 @@ int wal_grouped_plan(uint32_t n, const wal_info* infos, const void* const* W_dev
   if (plan_bytes < need_plan) return WAL_ERR_BUFFER;
   if (need_ws && (!ws_dev || ws_bytes < need_ws)) return ws_dev ? WAL_ERR_BUFFER : WAL_ERR_ARG;
   if (need_ws && !aligned(ws_dev, 16)) return WAL_ERR_ALIGN;
-  const uint32_t tf = infos[0].d.trit_fmt;
   for (uint32_t i = 0; i < n; ++i) {
     if (!W_dev[i] || !x_dev[i] || !y_dev[i]) return WAL_ERR_ARG;
     if (!aligned(W_dev[i], 256) || !aligned(x_dev[i], 16) || !aligned(y_dev[i], 4)) return WAL_ERR_ALIGN;
-    if (infos[i].d.trit_fmt != tf) return WAL_ERR_ARG;
     if (overlap(x_dev[i], (size_t)infos[i].d.in * xelem(x_dtype), y_dev[i], (size_t)infos[i].d.out * 4))
       return WAL_ERR_ARG;
   }
-  if (tf != WAL_TRIT_2BIT) return WAL_ERR_UNSUPPORTED;
   PlanShape P;
   if ((st = plan_shape(n, infos, grid, x_dtype, &P))) return st;
   uint8_t* base = static_cast<uint8_t*>(plan_host);
@@ -904,7 +763,8 @@ int wal_grouped_plan(uint32_t n, const wal_info* infos, const void* const* W_dev
         if (class_of(infos[m].d) != c) continue;
         const uint32_t rs = m == m0 ? r0 : 0;
         const uint32_t re = m == m1 ? r1 : infos[m].d.out;
-        for (uint32_t r = rs; r < re; r += kSegRows) segs[nseg++] = Seg{m, r, re - r > kSegRows ? r + kSegRows : re, 0};
+        const uint32_t sr = seg_rows(c);
+        for (uint32_t r = rs; r < re; r += sr) segs[nseg++] = Seg{m, r, re - r > sr ? r + sr : re, 0};
       }
       m0 = m1;
       r0 = r1;
@@ -924,7 +784,7 @@ int wal_grouped_plan(uint32_t n, const wal_info* infos, const void* const* W_dev
   h->n_segs = nseg_total;
   h->n_zjobs = (uint32_t)j;
   h->x_dtype = (uint32_t)x_dtype;
-  h->trit_fmt = tf;
+  h->trit_fmt = 0;
   h->reserved = P.n_classes;
   h->off_descs = P.off_descs;
   h->off_zjobs = P.off_zjobs;
@@ -935,7 +795,7 @@ int wal_grouped_plan(uint32_t n, const wal_info* infos, const void* const* W_dev
   ginfo->n_segs = nseg_total;
   ginfo->n_zjobs = (uint32_t)j;
   ginfo->x_dtype = (uint32_t)x_dtype;
-  ginfo->trit_fmt = tf;
+  ginfo->trit_fmt = 0;
   ginfo->rows_per_batch = kRB;
   ginfo->grid = gmax;
   ginfo->plan_bytes = P.bytes;
@@ -950,10 +810,11 @@ int wal_grouped_plan(uint32_t n, const wal_info* infos, const void* const* W_dev
 int wal_gemv_grouped(const wal_grouped_info* g, const void* plan_dev, void* stream) {
   if (!g || !plan_dev) return WAL_ERR_ARG;
   if (!aligned(plan_dev, 16)) return WAL_ERR_ALIGN;
-  if (g->x_dtype > WAL_X_BF16 || g->trit_fmt != WAL_TRIT_2BIT || !g->n) return WAL_ERR_ARG;
+  if (g->x_dtype > WAL_X_BF16 || !g->n) return WAL_ERR_ARG;
   if (g->rows_per_batch != (uint32_t)kRB || !g->n_classes || g->n_classes > WAL_MAX_CLASSES) return WAL_ERR_ARG;
   for (uint32_t k = 0; k < g->n_classes; ++k) {
-    if (g->class_id[k] >= WAL_MAX_CLASSES || !g->class_grid[k]) return WAL_ERR_ARG;
+    if (g->class_id[k] >= kClasses || !g->class_grid[k]) return WAL_ERR_ARG;
+    if (!grouped_for((int)g->x_dtype, g->class_id[k])) return WAL_ERR_UNSUPPORTED;
     if (g->class_blockseg[k] >= g->plan_bytes || g->class_segs[k] >= g->plan_bytes) return WAL_ERR_ARG;
   }
   if (g->off_descs >= g->plan_bytes || (g->n_zjobs && g->off_zjobs >= g->plan_bytes)) return WAL_ERR_ARG;

@@ -56,7 +56,19 @@ constexpr uint32_t kSegRows = 8192;
 constexpr uint32_t kZTerms = 4;
 constexpr uint32_t kMaxTerms = WAL_MAX_PATHS * WAL_MAX_RANK;
 
+// Streaming kernels as host-side launch targets.
+struct Seg;
+using GroupedFn = void (*)(const MatDev*, const uint32_t*, const Seg*);
+using SingleFn = void (*)(MatDev, uint32_t);
+
 // Host helpers implemented in wal_host.cpp.
 int check_info(const wal_info* info);
+
+// Base-3 streaming kernels (wal_base3.hip), bf16 activations, by
+// (scale format, k) class (4 * scale_fmt + index of k in {0, 2, 4, 8}), and
+// the longest row range one of their workgroups takes.
+GroupedFn base3_grouped_kernel(uint32_t cls);
+SingleFn base3_single_kernel(uint32_t cls);
+uint32_t base3_seg_rows();
 
 }  // namespace wal

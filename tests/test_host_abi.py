@@ -247,7 +247,7 @@ def _plan_on_host(infos, grid, x_dtype=wal.WAL_X_BF16):
 
 
 def _class_of(info):
-    return 4 * info.d.scale_fmt + {0: 0, 2: 1, 4: 2, 8: 3}[info.d.k]
+    return 8 * info.d.trit_fmt + 4 * info.d.scale_fmt + {0: 0, 2: 1, 4: 2, 8: 3}[info.d.k]
 
 
 def _plan_classes(plan, g):
@@ -268,16 +268,19 @@ def test_grouped_plan_covers_every_row_once(grid):
     class's matrices into `grid` contiguous ranges of near-equal packed
     bytes; every row of every matrix belongs to exactly one workgroup of the
     launch of its class."""
-    shapes = [(4096, 4096, 8, 1, 16, 0), (1024, 4096, 8, 0, 0, 0), (1024, 4096, 8, 1, 16, 0),
-              (4096, 4096, 8, 1, 16, 0), (12288, 4096, 8, 1, 16, 0), (300, 4096, 2, 0, 0, 1),
-              (12288, 4096, 8, 0, 0, 0), (4096, 12288, 8, 1, 16, 0), (1, 128, 2, 0, 0, 0),
-              (7, 384, 4, 4, 64, 0), (129, 512, 2, 1, 8, 1)]
-    infos = [wal.wal_packed_size(wal.make_desc(o, i, k, P, r, scale_fmt=sf)) for o, i, k, P, r, sf in shapes]
+    shapes = [(4096, 4096, 8, 1, 16, 0, 0), (1024, 4096, 8, 0, 0, 0, 0), (1024, 4096, 8, 1, 16, 0, 0),
+              (4096, 4096, 8, 1, 16, 0, 0), (12288, 4096, 8, 1, 16, 0, 0), (300, 4096, 2, 0, 0, 1, 0),
+              (12288, 4096, 8, 0, 0, 0, 0), (4096, 12288, 8, 1, 16, 0, 0), (1, 128, 2, 0, 0, 0, 0),
+              (7, 384, 4, 4, 64, 0, 0), (129, 512, 2, 1, 8, 1, 0), (17408, 5120, 2, 2, 16, 1, 1),
+              (5120, 17408, 4, 2, 16, 1, 1), (3000, 640, 8, 0, 0, 0, 1)]
+    infos = [wal.wal_packed_size(wal.make_desc(o, i, k, P, r, trit_fmt=tf, scale_fmt=sf))
+             for o, i, k, P, r, sf, tf in shapes]
     plan, g = _plan_on_host(infos, grid)
     classes, jobs = _plan_classes(plan, g)
     assert sorted(c for c, _, _ in classes) == sorted(set(_class_of(i) for i in infos))
     assert sum(len(sg) for _, _, sg in classes) == g.n_segs
-    rb = [i.d.in_ // 4 + (i.d.in_ // 128) * (i.d.k + (2 if i.d.scale_fmt == 0 else 3) * (2 if i.d.k else 1))
+    rb = [(i.d.in_ // 4 if i.d.trit_fmt == 0 else (i.d.in_ + 4) // 5)
+          + (i.d.in_ // 128) * (i.d.k + (2 if i.d.scale_fmt == 0 else 3) * (2 if i.d.k else 1))
           + i.d.n_paths * ((i.d.rank + 7) // 8) for i in infos]
     covered = [np.zeros(o, np.int32) for o, *_ in shapes]
     for c, blockseg, segs in classes:
@@ -288,6 +291,7 @@ def test_grouped_plan_covers_every_row_once(grid):
             for m, r0, r1, _ in segs[blockseg[b]:blockseg[b + 1]]:
                 assert _class_of(infos[m]) == c
                 assert r0 < r1 <= shapes[m][0]
+                assert r1 - r0 <= (1024 if c >= 8 else 8192)   # rows whose y one workgroup stages
                 covered[m][r0:r1] += 1
                 per_block[b] += (r1 - r0) * rb[m]
         # streamed bytes per workgroup are balanced to within a row of the
@@ -298,7 +302,7 @@ def test_grouped_plan_covers_every_row_once(grid):
     for c in covered:
         assert np.all(c == 1)
     # one low-rank job per 4 terms of every matrix that has paths
-    want = [(m << 8) | t0 for m, (o, i, k, P, r, sf) in enumerate(shapes) for t0 in range(0, P * r, 4)]
+    want = [(m << 8) | t0 for m, (o, i, k, P, r, sf, tf) in enumerate(shapes) for t0 in range(0, P * r, 4)]
     assert sorted(jobs.tolist()) == sorted(want)
 
 
