@@ -157,5 +157,46 @@ __device__ __forceinline__ float f16_at(const uint8_t* p, uint32_t i) {
   return (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(p)[i]);
 }
 
-
+// ---------------------------------------------------------------------------
+// Low-rank pre-pass: z[t] = s_p[r] * sum_j (-1)^{V_p[r] bit j} x_j for the
+// kZTerms terms t0 .. t0 + kZTerms - 1 of one matrix, one workgroup.
+template <int XT>
+__device__ __forceinline__ void zjob(const MatDev& d, uint32_t t0) {
+  __shared__ float red[kWaves][kZTerms];
+  const uint32_t tid = threadIdx.x;
+  const int lane = tid & 63;
+  const uint32_t T = d.terms, vrow = d.in / 8;
+  float acc[kZTerms];
+#pragma unroll
+  for (int q = 0; q < (int)kZTerms; ++q) acc[q] = 0.f;
+  for (uint32_t c = tid * 16; c < d.in; c += kThreads * 16) {
+    float xv[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) xv[j] = xval<XT>(d.x, c + j);
+#pragma unroll
+    for (int q = 0; q < (int)kZTerms; ++q) {
+      const uint32_t t = t0 + q;
+      if (t < T) {
+        const uint32_t p = t / d.rank, r = t % d.rank;
+        const uint32_t bits = reinterpret_cast<const uint16_t*>(path_ptr(d.V, p) + (size_t)r * vrow)[c / 16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[q] += ((bits >> j) & 1u) ? -xv[j] : xv[j];
+      }
+    }
+  }
+  const float tot = treduce<kZTerms>(acc, lane);
+  constexpr int SH = 6 - ilog2(kZTerms);
+  if ((lane & ((1 << SH) - 1)) == 0) red[tid >> 6][lane >> SH] = tot;
+  __syncthreads();
+  if (tid < kZTerms) {
+    const uint32_t t = t0 + tid;
+    if (t < T) {
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < (int)kWaves; ++w) sum += red[w][tid];
+      const uint32_t p = t / d.rank, r = t % d.rank;
+      d.z[t] = f16_at(path_ptr(d.s, p), r) * sum;
+    }
+  }
+}
 }  // namespace

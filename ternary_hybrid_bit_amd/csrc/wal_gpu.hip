@@ -383,49 +383,6 @@ __global__ __launch_bounds__(kThreads) void k_stream_single(MatDev d, uint32_t r
   if (r0 < r1) run_segment_2bit<XT, SF, K, RB>(d, r0, r1, sm);
 }
 
-// ---------------------------------------------------------------------------
-// Low-rank pre-pass: z[t] = s_p[r] * sum_j (-1)^{V_p[r] bit j} x_j for the
-// kZTerms terms t0 .. t0 + kZTerms - 1 of one matrix, one workgroup.
-template <int XT>
-__device__ __forceinline__ void zjob(const MatDev& d, uint32_t t0) {
-  __shared__ float red[kWaves][kZTerms];
-  const uint32_t tid = threadIdx.x;
-  const int lane = tid & 63;
-  const uint32_t T = d.terms, vrow = d.in / 8;
-  float acc[kZTerms];
-#pragma unroll
-  for (int q = 0; q < (int)kZTerms; ++q) acc[q] = 0.f;
-  for (uint32_t c = tid * 16; c < d.in; c += kThreads * 16) {
-    float xv[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) xv[j] = xval<XT>(d.x, c + j);
-#pragma unroll
-    for (int q = 0; q < (int)kZTerms; ++q) {
-      const uint32_t t = t0 + q;
-      if (t < T) {
-        const uint32_t p = t / d.rank, r = t % d.rank;
-        const uint32_t bits = reinterpret_cast<const uint16_t*>(path_ptr(d.V, p) + (size_t)r * vrow)[c / 16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) acc[q] += ((bits >> j) & 1u) ? -xv[j] : xv[j];
-      }
-    }
-  }
-  const float tot = treduce<kZTerms>(acc, lane);
-  constexpr int SH = 6 - ilog2(kZTerms);
-  if ((lane & ((1 << SH) - 1)) == 0) red[tid >> 6][lane >> SH] = tot;
-  __syncthreads();
-  if (tid < kZTerms) {
-    const uint32_t t = t0 + tid;
-    if (t < T) {
-      float sum = 0.f;
-#pragma unroll
-      for (int w = 0; w < (int)kWaves; ++w) sum += red[w][tid];
-      const uint32_t p = t / d.rank, r = t % d.rank;
-      d.z[t] = f16_at(path_ptr(d.s, p), r) * sum;
-    }
-  }
-}
-
 template <int XT>
 __global__ __launch_bounds__(kThreads) void k_z_single(MatDev d) {
   zjob<XT>(d, blockIdx.x * kZTerms);
@@ -482,6 +439,9 @@ int launch_status() {
 }
 
 constexpr int kRB = 4;   // rows per batch of the 2-bit streaming kernels
+// Batch from which WAL_GEMM_AUTO takes the MFMA kernel (measured on MI355X
+// on the 4096 x 12288 shape).
+constexpr uint32_t kGemmCrossover = 8;
 constexpr uint32_t kClasses = 16;   // kernel classes (see class_of)
 
 // Kernel class of a matrix: 8 * trit_fmt + 4 * scale_fmt + index of k in {0, 2, 4, 8}.
@@ -623,8 +583,7 @@ int wal_gemv(const wal_info* info, const void* W_dev, const void* x_dev, int x_d
   if (!W_dev || !x_dev || !y_dev) return WAL_ERR_ARG;
   if (x_dtype != WAL_X_F32 && x_dtype != WAL_X_BF16) return WAL_ERR_ARG;
   if (!aligned(W_dev, 256) || !aligned(x_dev, 16) || !aligned(y_dev, 4)) return WAL_ERR_ALIGN;
-  size_t need = 0;
-  if ((st = wal_workspace_size(info, 1, &need))) return st;
+  const size_t need = (size_t)gemm_shape(*info, 1).off_xp;   // z only
   if (need && (!ws_dev || ws_bytes < need)) return ws_dev ? WAL_ERR_BUFFER : WAL_ERR_ARG;
   if (need && !aligned(ws_dev, 16)) return WAL_ERR_ALIGN;
   if (overlap(x_dev, (size_t)info->d.in * xelem(x_dtype), y_dev, (size_t)info->d.out * 4)) return WAL_ERR_ARG;
@@ -658,10 +617,36 @@ int wal_gemm_small(const wal_info* info, const void* W_dev, const void* X_dev, i
   if (st) return st;
   if (batch == 0 || batch > WAL_MAX_BATCH) return WAL_ERR_ARG;
   if (mode < WAL_GEMM_AUTO || mode > WAL_GEMM_MFMA) return WAL_ERR_ARG;
-  if (batch == 1 && mode != WAL_GEMM_MFMA)
-    return wal_gemv(info, W_dev, X_dev, x_dtype, Y_dev, ws_dev, ws_bytes, stream);
-  (void)ldx; (void)ldy;
-  return WAL_ERR_UNSUPPORTED;
+  if (!W_dev || !X_dev || !Y_dev) return WAL_ERR_ARG;
+  if (x_dtype != WAL_X_F32 && x_dtype != WAL_X_BF16) return WAL_ERR_ARG;
+  if (ldx < info->d.in || ldy < info->d.out) return WAL_ERR_ARG;
+  const size_t xe = xelem(x_dtype);
+  if (!aligned(W_dev, 256) || !aligned(X_dev, 16) || !aligned(Y_dev, 4) || (ldx * xe) % 16) return WAL_ERR_ALIGN;
+  size_t need = 0;
+  if ((st = wal_workspace_size(info, batch, &need))) return st;
+  if (!ws_dev || ws_bytes < need) return ws_dev ? WAL_ERR_BUFFER : WAL_ERR_ARG;
+  if (!aligned(ws_dev, 16)) return WAL_ERR_ALIGN;
+  const size_t xbytes = ((size_t)(batch - 1) * ldx + info->d.in) * xe;
+  const size_t ybytes = ((size_t)(batch - 1) * ldy + info->d.out) * 4;
+  if (overlap(X_dev, xbytes, Y_dev, ybytes) || overlap(ws_dev, need, Y_dev, ybytes) ||
+      overlap(ws_dev, need, X_dev, xbytes))
+    return WAL_ERR_ARG;
+  if ((st = check_blob_size(info))) return st;
+  // The batched kernels take bf16 activations and 2-bit codes; other inputs
+  // run one batch-1 product per column.
+  const bool batched = x_dtype == WAL_X_BF16 && info->d.trit_fmt == WAL_TRIT_2BIT;
+  if (mode == WAL_GEMM_AUTO) mode = batched && batch >= kGemmCrossover ? WAL_GEMM_MFMA : WAL_GEMM_VALU;
+  MatDev d = make_dev(info, W_dev, X_dev, Y_dev, static_cast<float*>(ws_dev), ldx, ldy, batch);
+  if (mode == WAL_GEMM_MFMA) {
+    if (!batched) return WAL_ERR_UNSUPPORTED;
+    return launch_gemm_mfma(*info, d, batch, ws_dev, stream);
+  }
+  if (batched && batch > 1) return launch_gemm_valu(*info, d, batch, ws_dev, stream);
+  for (uint32_t n = 0; n < batch; ++n) {
+    const void* xn = static_cast<const uint8_t*>(X_dev) + (size_t)n * ldx * xe;
+    if ((st = wal_gemv(info, W_dev, xn, x_dtype, Y_dev + (size_t)n * ldy, ws_dev, ws_bytes, stream))) return st;
+  }
+  return WAL_OK;
 }
 
 int wal_grouped_plan_size(uint32_t n, const wal_info* infos, uint32_t grid, int x_dtype, size_t* plan_bytes,

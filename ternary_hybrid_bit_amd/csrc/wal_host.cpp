@@ -432,11 +432,33 @@ int wal_unpack(const void* blob, size_t bytes, int8_t* T, uint8_t* site_pos, int
 int wal_workspace_size(const wal_info* info, uint32_t batch, size_t* bytes) {
   if (!info || !bytes) return WAL_ERR_ARG;
   if (batch == 0 || batch > WAL_MAX_BATCH) return WAL_ERR_ARG;
-  int st = check_desc(&info->d);
+  const int st = wal::check_info(info);
   if (st) return st;
-  // z_p[r] for every path, rank and batch column, padded to 256 bytes
-  *bytes = info->d.n_paths ? (size_t)up(4ull * info->d.n_paths * info->d.rank * batch, 256) : 0;
+  // z_p[r] for every path, rank and batch column, the operand-order copy of X
+  // and the partial sums of the small-batch kernels (wal_gemv uses the first
+  // part only)
+  *bytes = (size_t)wal::gemm_shape(*info, batch).bytes;
   return WAL_OK;
 }
 
 }  // extern "C"
+
+namespace wal {
+
+GemmShape gemm_shape(const wal_info& f, uint32_t batch) {
+  GemmShape S;
+  const uint64_t terms = (uint64_t)f.d.n_paths * f.d.rank;
+  S.nt = (batch + 15) / 16;
+  S.row_blocks = (f.d.out + kMfmaRows - 1) / kMfmaRows;
+  uint32_t ks = (kMfmaWaves + S.row_blocks - 1) / S.row_blocks;
+  S.ks = ks > f.groups ? f.groups : ks < 1 ? 1 : ks;
+  S.passes = (f.d.in + kPass2bit - 1) / kPass2bit;
+  S.slices = S.ks > S.passes ? S.ks : S.passes;
+  S.off_z = 0;
+  S.off_xp = up(4 * terms * batch, 256);
+  S.off_p = S.off_xp + up((uint64_t)f.groups * S.nt * 4 * 64 * 16, 256);
+  S.bytes = S.off_p + up(4ull * S.slices * batch * f.d.out, 256);
+  return S;
+}
+
+}  // namespace wal

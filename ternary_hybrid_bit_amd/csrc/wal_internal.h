@@ -61,6 +61,30 @@ struct Seg;
 using GroupedFn = void (*)(const MatDev*, const uint32_t*, const Seg*);
 using SingleFn = void (*)(MatDev, uint32_t);
 
+// Small-batch products (wal_gemm.hip).  Both kernels write per-K-slice
+// partial sums P[slice][n][row] to the workspace; a last kernel adds the
+// slices in order and the low-rank term.
+//  * batched GEMV (vector ALUs): a wavefront takes kGemvRows rows of one
+//    4096-column pass and up to kGemvCols activation columns, every decoded
+//    trit feeding all of them; slices = passes.
+//  * MFMA: a wavefront takes kMfmaTiles row tiles of 16 rows over a range of
+//    groups; slices = K splits.
+constexpr uint32_t kGemvRows = 8;
+constexpr uint32_t kGemvCols = 4;
+constexpr uint32_t kMfmaTiles = 4;
+constexpr uint32_t kMfmaRows = 16 * kMfmaTiles;
+constexpr uint32_t kMfmaWaves = 1024;   // K splits are chosen to reach about this many wavefronts
+// Workspace of a small-batch product: z[batch][terms] | X in operand order
+// (MFMA) | partial sums P[slices][batch][out].
+struct GemmShape {
+  uint32_t nt, row_blocks, ks, passes, slices;
+  uint64_t off_z, off_xp, off_p, bytes;
+};
+GemmShape gemm_shape(const wal_info& f, uint32_t batch);
+// Launchers (stream as hipStream_t); WAL_OK or WAL_ERR_DEVICE.
+int launch_gemm_valu(const wal_info& f, const MatDev& d, uint32_t batch, void* ws, void* stream);
+int launch_gemm_mfma(const wal_info& f, const MatDev& d, uint32_t batch, void* ws, void* stream);
+
 // Host helpers implemented in wal_host.cpp.
 int check_info(const wal_info* info);
 
