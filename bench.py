@@ -6,14 +6,22 @@ body matrices at batch 1 on one MI355X.
 One step = one grouped product y_i = W_i(x_i) over all 252 matrices (36
 layers x q, k, v, o, gate, up, down; sparse k = 8 on all, a rank-16 binary
 path on 213 of them; bf16 activations, fp32 outputs), launched through the C
-ABI on torch's current HIP stream.  The packed weights (about 2.39 GB) are
-resident in HBM before timing starts; the working set is far larger than the
-256 MB Infinity Cache, so every step streams the weights from HBM.
+ABI on torch's current HIP stream: the low-rank pre-pass, then the streaming
+kernel.  The packed weights (about 2.39 GB) are resident in HBM before timing
+starts; the working set is far larger than the 256 MB Infinity Cache, so
+every step streams the weights from HBM.
 
-Prints one JSON line with the contract's fields plus ``roofline`` (HIP-event
-timing of the steps on the launch stream, algorithmic packed bytes per step,
-against the 8 TB/s HBM peak) and ``cpu_baseline`` (the float64 CPU oracle
-timed on a bounded sample of the same workload, on this host).
+After idle the GPU runs the first ~100 steps up to 30 % slower while its
+power management raises the clocks, so before the W warmup steps the step is
+repeated, untimed, for --settle-s seconds (default 1 s).
+
+Prints one JSON line with the contract's fields plus ``roofline`` (the
+streaming kernel's average duration from HIP events recorded around it on
+its stream in every timed step, algorithmic packed bytes per launch, against
+the 8 TB/s HBM peak; HBM traffic from the committed rocprofv3 counter runs
+when the kernel sources are unchanged since) and ``cpu_baseline`` (the
+float64 CPU oracle timed on a bounded sample of the same workload, on this
+host).
 """
 from __future__ import annotations
 
@@ -32,9 +40,10 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "packed-weight GB/s & % of HBM peak, 252-matrix Qwen3-8B-shape GEMV sweep, batch 1"
+KERNEL = "k_stream_grouped<bf16 x, fp16 scales, k=8, 4 rows/batch>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sweep_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "ternary_hybrid_bit_amd", "csrc", f)
-                  for f in ("wal_gpu.hip", "wal_internal.h")]
+                  for f in ("wal_gpu.hip", "wal_device.h", "wal_internal.h")]
 
 
 def kernel_source_hash() -> str:
@@ -46,8 +55,8 @@ def kernel_source_hash() -> str:
 
 
 def stored_traffic():
-    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
-    when the kernel sources changed since they were taken."""
+    """HBM bytes per streaming launch from the committed rocprofv3 counter
+    runs, or None when the kernel sources changed since they were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -78,7 +87,8 @@ def cpu_baseline(items, budget_s: float):
         n += 1
         if t_total >= budget_s:
             break
-    return {"value": done_bytes / t_total / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+    return {"value": round(done_bytes / t_total / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
             "sample": f"first {n} of 252 sweep matrices ({done_bytes / 1e9:.3f} GB packed), "
                       f"{t_total:.1f} s: numpy unpack + dense float64 W + W@x per matrix"}
 
@@ -86,17 +96,18 @@ def cpu_baseline(items, budget_s: float):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--settle-s", type=float, default=1.0,
+                    help="seconds of untimed steps before the warmup (clock ramp after idle)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after timing, run one fp32 elementwise copy of this many MiB (counter calibration)")
-    ap.add_argument("--layers", type=int, default=36, help=argparse.SUPPRESS)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the sweep's sharding across GPUs is described in DESIGN.md).", file=sys.stderr)
+              "(the sweep is timed on a single MI355X).", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -104,7 +115,7 @@ def main():
     from ternary_hybrid_bit_amd import workloads
 
     t0 = time.time()
-    items = workloads.sweep(layers=args.layers)
+    items = workloads.sweep()
     print(f"[bench] generated and packed {len(items)} matrices in {time.time() - t0:.1f} s", file=sys.stderr,
           flush=True)
     dev = torch.device("cuda:0")
@@ -144,21 +155,41 @@ def main():
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
 
+    t_settle, n_settle = time.perf_counter(), 0
+    while True:
+        for _ in range(20):
+            wal.wal_gemv_grouped(g, plan_dev)
+        torch.cuda.synchronize()
+        n_settle += 20
+        if time.perf_counter() - t_settle >= args.settle_s:
+            break
     for _ in range(args.warmup):
         wal.wal_gemv_grouped(g, plan_dev)
     torch.cuda.synchronize()
+
+    # Timed region: every step is the low-rank pre-pass and the streaming
+    # launch; events around the streaming launch, on its stream, give the
+    # dominant kernel's own average duration.
+    K = args.steps
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_wall = time.perf_counter()
     ev0.record(stream)
-    for _ in range(args.steps):
-        wal.wal_gemv_grouped(g, plan_dev)
+    for i in range(K):
+        wal.wal_gemv_grouped_phases(g, plan_dev, wal.WAL_PHASE_LOWRANK)
+        ev_a[i].record(stream)
+        wal.wal_gemv_grouped_phases(g, plan_dev, wal.WAL_PHASE_STREAM)
+        ev_b[i].record(stream)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - t_wall
-    ms_total = ev0.elapsed_time(ev1)
-    ms_step = ms_total / args.steps
-    print(f"[bench] {args.steps} steps: {ms_step:.4f} ms/step (events), wall {wall_s * 1e3 / args.steps:.4f} ms",
-          file=sys.stderr, flush=True)
+    ms_step = ev0.elapsed_time(ev1) / K
+    k_ms = np.array([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)])
+    ms_kernel = float(k_ms.mean())
+    print(f"[bench] settle {n_settle} steps, warmup {args.warmup}; {K} steps: {ms_step:.4f} ms/step (events), "
+          f"wall {wall_s * 1e3 / K:.4f} ms; streaming kernel mean {ms_kernel:.4f} ms "
+          f"(median {np.median(k_ms):.4f}, min {k_ms.min():.4f}, max {k_ms.max():.4f})", file=sys.stderr, flush=True)
 
     if args.copy_mib:
         # a plain copy kernel of known size: reads and writes copy_mib MiB once
@@ -173,13 +204,13 @@ def main():
     alg_bytes = int(g.algorithmic_bytes)
     weights = sum(int(i.d.out) * int(i.d.in_) for i in infos)
     gbs = alg_bytes / (ms_step * 1e-3) / 1e9
-    traffic = stored_traffic()
+    k_gbs = alg_bytes / (ms_kernel * 1e-3) / 1e9
     out = {
         "metric": METRIC,
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
@@ -188,15 +219,14 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "qwen3-8b-body-sweep-252-gemv-batch1", "matrices": len(items),
-                   "layers": args.layers, "batch": 1, "x_dtype": "bf16", "y_dtype": "f32",
+                   "layers": 36, "batch": 1, "x_dtype": "bf16", "y_dtype": "f32",
                    "format": "2-bit T + sparse k8 + fp16 alpha/beta per 128 + rank-16 WALB2 on 213/252",
-                   "packed_bytes": alg_bytes, "weights": weights},
+                   "packed_bytes": alg_bytes, "weights": weights, "settle_s": args.settle_s},
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "weights_per_s": round(weights / (ms_step * 1e-3), 1),
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "k_gemv2_grouped (+ k_z_grouped pre-pass, inside the timed step)",
-                     "bytes_per_launch": alg_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(k_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": stored_traffic(),
+                     "kernel": KERNEL, "ms_per_launch": round(ms_kernel, 5), "bytes_per_launch": alg_bytes},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(items, args.cpu_budget)

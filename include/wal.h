@@ -182,29 +182,39 @@ int wal_unpack(const void* blob, size_t bytes, int8_t* T, uint8_t* site_pos,
                int8_t* site_sign, float* alpha, float* beta, int8_t* U,
                int8_t* V, float* s);
 
-/* Device workspace that wal_gemv / wal_gemm_small need for a blob and batch
- * (the per-path reductions z_p = diag(s_p) V_p^T x).  Errors: ARG, SHAPE. */
+/* Device workspace that wal_gemm_small needs for a blob and batch: the
+ * per-path reductions z_p = diag(s_p) V_p^T X [batch][n_paths * rank], X in
+ * MFMA operand order and the per-K-slice partial sums [slices][batch][out]
+ * (fp32), each part padded to 256 bytes.  Errors: ARG, SHAPE, FORMAT. */
 int wal_workspace_size(const wal_info* info, uint32_t batch, size_t* bytes);
 
-/* y = W(x) for one matrix, batch 1.
+/* y = W(x) for one matrix, batch 1 (WAL-Ternary-8B cards, "Representation":
+ * the ternary-hybrid product with its binary low-rank paths).  One kernel
+ * launch; no workspace (each workgroup computes the low-rank reductions).
  *   info   host view of the blob (from wal_inspect / wal_pack)
  *   W_dev  the blob in device memory, 256-byte aligned
  *   x_dev  [in] activations, fp32 or bf16 (x_dtype), 16-byte aligned
  *   y_dev  [out] fp32 output, 4-byte aligned, overwritten
- *   ws_dev workspace of wal_workspace_size(info, 1) bytes (may be NULL when
- *          that size is 0), 16-byte aligned
- * Errors: ARG, SHAPE, ALIGN, BUFFER, UNSUPPORTED, DEVICE. */
+ * Errors: ARG, SHAPE, ALIGN, UNSUPPORTED, DEVICE. */
 int wal_gemv(const wal_info* info, const void* W_dev, const void* x_dev, int x_dtype,
-             float* y_dev, void* ws_dev, size_t ws_bytes, void* stream);
+             float* y_dev, void* stream);
 
-/* Y = X W^T for a small batch (F.linear convention).
+/* Y = X W^T for a small batch (F.linear convention): row n of Y is W(x_n)
+ * with x_n row n of X (WAL-Ternary-8B cards, "Representation").
  *   X_dev  [batch][ldx] activations (bf16 or fp32), ldx >= in, ldx*elem % 16 == 0
- *   Y_dev  [batch][ldy] fp32 outputs, ldy >= out, overwritten
+ *   Y_dev  [batch][ldy] fp32 outputs, ldy >= out; columns past out untouched
  *   batch  1..WAL_MAX_BATCH
- *   mode   WAL_GEMM_AUTO, WAL_GEMM_VALU (one decode feeds every batch
- *          column on the vector ALUs) or WAL_GEMM_MFMA (trits decoded to bf16
- *          tiles feeding matrix-core MFMA; bf16 X, 2-bit codes only)
- * Errors: as wal_gemv. */
+ *   mode   WAL_GEMM_VALU (batched GEMV: one decode of a row feeds every batch
+ *          column on the vector ALUs), WAL_GEMM_MFMA (trits decoded to bf16
+ *          operands of matrix-core MFMA, alpha / beta applied per group in
+ *          fp32) or WAL_GEMM_AUTO (MFMA from a measured crossover batch on).
+ *          Both batched kernels take bf16 X and 2-bit codes; fp32 X or
+ *          base-3 codes run one wal_gemv per row with WAL_GEMM_VALU / AUTO,
+ *          and WAL_GEMM_MFMA returns WAL_ERR_UNSUPPORTED for them.
+ *   ws_dev wal_workspace_size(info, batch) bytes, 16-byte aligned, disjoint
+ *          from X and Y; its contents on entry do not matter
+ * Calls that share a workspace must be ordered (one stream).
+ * Errors: ARG, SHAPE, ALIGN, BUFFER, UNSUPPORTED, DEVICE. */
 int wal_gemm_small(const wal_info* info, const void* W_dev, const void* X_dev, int x_dtype,
                    uint32_t batch, uint32_t ldx, float* Y_dev, uint32_t ldy, int mode,
                    void* ws_dev, size_t ws_bytes, void* stream);
@@ -233,6 +243,17 @@ int wal_grouped_plan(uint32_t n, const wal_info* infos, const void* const* W_dev
                      void* ws_dev, size_t ws_bytes, uint32_t grid, void* plan_host,
                      size_t plan_bytes, wal_grouped_info* ginfo);
 int wal_gemv_grouped(const wal_grouped_info* ginfo, const void* plan_dev, void* stream);
+
+/* The two phases of wal_gemv_grouped, for callers that schedule or time them
+ * apart: WAL_PHASE_LOWRANK launches the low-rank pre-pass (z_p of every
+ * matrix into the workspace given to wal_grouped_plan), WAL_PHASE_STREAM the
+ * streaming launches (one per class), which read those z_p; phases is a mask
+ * of the two, and
+ * the pre-pass of a call must precede its streaming phase on the stream.
+ * Errors: those of wal_gemv_grouped; ARG for an empty or unknown mask. */
+enum { WAL_PHASE_LOWRANK = 1, WAL_PHASE_STREAM = 2, WAL_PHASE_ALL = 3 };
+int wal_gemv_grouped_phases(const wal_grouped_info* ginfo, const void* plan_dev, int phases,
+                            void* stream);
 
 #ifdef __cplusplus
 }

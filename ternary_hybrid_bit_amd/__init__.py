@@ -21,6 +21,7 @@ WAL_TRIT_2BIT, WAL_TRIT_BASE3 = 0, 1
 WAL_SCALE_FP16, WAL_SCALE_FP24 = 0, 1
 WAL_X_F32, WAL_X_BF16 = 0, 1
 WAL_GEMM_AUTO, WAL_GEMM_VALU, WAL_GEMM_MFMA = 0, 1, 2
+WAL_PHASE_LOWRANK, WAL_PHASE_STREAM, WAL_PHASE_ALL = 1, 2, 3
 WAL_MAX_PATHS = 4
 WAL_MAX_BATCH = 32
 
@@ -81,12 +82,13 @@ _sig = {
     "wal_verify": (_I, [_P, _SZ]),
     "wal_unpack": (_I, [_P, _SZ, _P, _P, _P, _P, _P, _P, _P, _P]),
     "wal_workspace_size": (_I, [ctypes.POINTER(wal_info), _U32, ctypes.POINTER(_SZ)]),
-    "wal_gemv": (_I, [ctypes.POINTER(wal_info), _P, _P, _I, _P, _P, _SZ, _P]),
+    "wal_gemv": (_I, [ctypes.POINTER(wal_info), _P, _P, _I, _P, _P]),
     "wal_gemm_small": (_I, [ctypes.POINTER(wal_info), _P, _P, _I, _U32, _U32, _P, _U32, _I, _P, _SZ, _P]),
     "wal_grouped_plan_size": (_I, [_U32, _P, _U32, _I, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)]),
     "wal_grouped_plan": (_I, [_U32, _P, _P, _P, _I, _P, _P, _SZ, _U32, _P, _SZ,
                               ctypes.POINTER(wal_grouped_info)]),
     "wal_gemv_grouped": (_I, [ctypes.POINTER(wal_grouped_info), _P, _P]),
+    "wal_gemv_grouped_phases": (_I, [ctypes.POINTER(wal_grouped_info), _P, _I, _P]),
 }
 for _name, (_res, _args) in _sig.items():
     _fn = getattr(_lib, _name)
@@ -192,13 +194,11 @@ def wal_workspace_size(info: wal_info, batch: int = 1) -> int:
     return n.value
 
 
-def wal_gemv(info: wal_info, W, x, y, ws=None, stream=None):
-    """y = W(x) on the GPU; W, x, y (and ws) are device tensors; y is fp32 [out]."""
+def wal_gemv(info: wal_info, W, x, y, stream=None):
+    """y = W(x) on the GPU; W, x, y are device tensors; y is fp32 [out]."""
     import torch
     xdt = WAL_X_BF16 if x.dtype == torch.bfloat16 else WAL_X_F32
-    wsb = ws.numel() * ws.element_size() if ws is not None else 0
-    st = _lib.wal_gemv(ctypes.byref(info), _ptr(W), _ptr(x), xdt, _ptr(y), _ptr(ws), wsb, _stream(stream))
-    _check(st, "wal_gemv")
+    _check(_lib.wal_gemv(ctypes.byref(info), _ptr(W), _ptr(x), xdt, _ptr(y), _stream(stream)), "wal_gemv")
     return y
 
 
@@ -241,6 +241,11 @@ def wal_grouped_plan(infos: Sequence[wal_info], Ws, xs, ys, ws, x_dtype: int, gr
 
 def wal_gemv_grouped(ginfo: wal_grouped_info, plan_dev, stream=None):
     _check(_lib.wal_gemv_grouped(ctypes.byref(ginfo), _ptr(plan_dev), _stream(stream)), "wal_gemv_grouped")
+
+
+def wal_gemv_grouped_phases(ginfo: wal_grouped_info, plan_dev, phases: int, stream=None):
+    _check(_lib.wal_gemv_grouped_phases(ctypes.byref(ginfo), _ptr(plan_dev), phases, _stream(stream)),
+           "wal_gemv_grouped_phases")
 
 
 def exported_symbols() -> list:

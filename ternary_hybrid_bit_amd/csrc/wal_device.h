@@ -158,45 +158,80 @@ __device__ __forceinline__ float f16_at(const uint8_t* p, uint32_t i) {
 }
 
 // ---------------------------------------------------------------------------
-// Low-rank pre-pass: z[t] = s_p[r] * sum_j (-1)^{V_p[r] bit j} x_j for the
-// kZTerms terms t0 .. t0 + kZTerms - 1 of one matrix, one workgroup.
-template <int XT>
-__device__ __forceinline__ void zjob(const MatDev& d, uint32_t t0) {
-  __shared__ float red[kWaves][kZTerms];
+// Low-rank reductions of one matrix by a whole workgroup:
+// z[t] = s_p[r] * sum_j (-1)^{V_p[r] bit j} x_j for the C terms t0 .. t0 + C - 1
+// (those below d.terms), written to out[t] by threads t - t0.  Every thread
+// of the workgroup calls it (it holds a barrier).
+template <int XT, int C>
+__device__ __forceinline__ void z_chunk(const MatDev& d, const void* x, uint32_t t0, float* out) {
+  __shared__ float red[kWaves][C];
   const uint32_t tid = threadIdx.x;
   const int lane = tid & 63;
   const uint32_t T = d.terms, vrow = d.in / 8;
-  float acc[kZTerms];
+  float acc[C];
 #pragma unroll
-  for (int q = 0; q < (int)kZTerms; ++q) acc[q] = 0.f;
+  for (int q = 0; q < C; ++q) acc[q] = 0.f;
   for (uint32_t c = tid * 16; c < d.in; c += kThreads * 16) {
-    float xv[16];
+    uint32_t xb[16];   // fp32 bit patterns of x[c .. c + 15]
+    if constexpr (XT == WAL_X_BF16) {
+      const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + c);
+      const uint4 a = src[0], b = src[1];
+      const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
-    for (int j = 0; j < 16; ++j) xv[j] = xval<XT>(d.x, c + j);
+      for (int k = 0; k < 8; ++k) {
+        xb[2 * k] = w[k] << 16;
+        xb[2 * k + 1] = w[k] & 0xFFFF0000u;
+      }
+    } else {
+      const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(x) + c);
 #pragma unroll
-    for (int q = 0; q < (int)kZTerms; ++q) {
+      for (int k = 0; k < 4; ++k) {
+        const uint4 v = src[k];
+        xb[4 * k] = v.x; xb[4 * k + 1] = v.y; xb[4 * k + 2] = v.z; xb[4 * k + 3] = v.w;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < C; ++q) {
       const uint32_t t = t0 + q;
       if (t < T) {
         const uint32_t p = t / d.rank, r = t % d.rank;
         const uint32_t bits = reinterpret_cast<const uint16_t*>(path_ptr(d.V, p) + (size_t)r * vrow)[c / 16];
+        // a set bit flips the sign of x_j
 #pragma unroll
-        for (int j = 0; j < 16; ++j) acc[q] += ((bits >> j) & 1u) ? -xv[j] : xv[j];
+        for (int j = 0; j < 16; ++j) acc[q] += __uint_as_float(xb[j] ^ ((bits << (31 - j)) & 0x80000000u));
       }
     }
   }
-  const float tot = treduce<kZTerms>(acc, lane);
-  constexpr int SH = 6 - ilog2(kZTerms);
+  const float tot = treduce<C>(acc, lane);
+  constexpr int SH = 6 - ilog2(C);
   if ((lane & ((1 << SH) - 1)) == 0) red[tid >> 6][lane >> SH] = tot;
   __syncthreads();
-  if (tid < kZTerms) {
+  if (tid < (uint32_t)C) {
     const uint32_t t = t0 + tid;
     if (t < T) {
       float sum = 0.f;
 #pragma unroll
       for (int w = 0; w < (int)kWaves; ++w) sum += red[w][tid];
       const uint32_t p = t / d.rank, r = t % d.rank;
-      d.z[t] = f16_at(path_ptr(d.s, p), r) * sum;
+      out[t] = f16_at(path_ptr(d.s, p), r) * sum;
     }
+  }
+}
+
+// One pre-pass workgroup: terms t0 .. t0 + kZTerms - 1 of one matrix into d.z.
+template <int XT>
+__device__ __forceinline__ void zjob(const MatDev& d, uint32_t t0) {
+  z_chunk<XT, (int)kZTerms>(d, d.x, t0, d.z);
+}
+
+// Every low-rank term of one matrix into out (LDS), visible to the whole
+// workgroup on return.  Every thread calls it.
+constexpr int kZChunk = 16;
+template <int XT>
+__device__ __forceinline__ void z_all(const MatDev& d, float* out) {
+  for (uint32_t t0 = 0; t0 < d.terms; t0 += kZChunk) {
+    z_chunk<XT, kZChunk>(d, d.x, t0, out);
+    __syncthreads();   // out is complete and red free for the next chunk
   }
 }
 }  // namespace

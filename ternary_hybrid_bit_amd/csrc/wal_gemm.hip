@@ -55,7 +55,7 @@ __global__ __launch_bounds__(kThreads) void k_z_batch(MatDev d) {
   MatDev e = d;
   e.x = reinterpret_cast<const uint16_t*>(d.x) + (size_t)blockIdx.y * d.ldx;
   e.z = d.z + (size_t)blockIdx.y * d.terms;
-  zjob<WAL_X_BF16>(e, blockIdx.x * kZTerms);
+  z_chunk<WAL_X_BF16, kZTerms>(e, e.x, blockIdx.x * kZTerms, e.z);
 }
 
 // Y[n][row] = sum over K slices of the partials (in slice order) + the

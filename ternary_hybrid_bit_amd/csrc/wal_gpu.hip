@@ -4,9 +4,12 @@
 //     y = (alpha * T + beta * R) x + sum_p U_p diag(s_p) V_p^T x
 // computed straight from the packed planes described in include/wal.h.
 //
-// Two kernels per product:
-//  * k_z_*: the binary low-rank reductions z_p[r] = s_p[r] * sum_j (-1)^{V bit} x_j,
-//    kZTerms terms per workgroup, written to the caller's workspace.
+// Kernels:
+//  * the binary low-rank reductions z_p[r] = s_p[r] * sum_j (-1)^{V bit} x_j:
+//    for grouped products a pre-pass (k_z_grouped, kZTerms terms per
+//    workgroup) writes them to the caller's workspace; a single product
+//    (wal_gemv) computes them inside each streaming workgroup at the start of
+//    its rows, so it is one launch and needs no workspace.
 //  * k_stream_*: one streaming pass over the packed planes.  Every workgroup
 //    owns a contiguous range of rows of one or more matrices (for grouped
 //    products the host splits the total packed bytes evenly over a grid that
@@ -194,9 +197,9 @@ struct Lane2 {
 
 // One pass of one segment.  The workgroup-wide set-up of the pass (site table,
 // low-rank terms, behind barriers) runs after each wave has issued the loads
-// of its first two batches and of its x columns, so the set-up overlaps the
+// of its first batch and of its x columns, so the set-up overlaps the
 // memory latency instead of adding to it.  Every wave reaches both barriers.
-template <int XT, int SF, int K, int RB>
+template <int XT, int SF, int K, int RB, bool ZIN>
 __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0, uint32_t row1, uint32_t pass,
                                                  uint32_t npass, StreamSmem& sm) {
   constexpr int LOG = ilog2(RB);
@@ -316,33 +319,29 @@ __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0,
       sm.ybuf[yi] = v;
   };
 
-  // Three batches in registers: while one is reduced, the next two are in
-  // flight.  Past the wave's last batch the prefetch repeats that batch (an
-  // L2 hit), keeping every load unconditional.
+  // Two batches in registers: while one is reduced, the next is in flight
+  // (three resident workgroups per CU keep three wavefronts per SIMD, six
+  // batches, in flight).  Past the wave's last batch the prefetch repeats
+  // that batch (an L2 hit), keeping every load unconditional.
   const uint32_t blast = has_rows ? wave + (nb - 1 - wave) / kWaves * kWaves : b;
   auto ahead = [&](uint32_t bb) { return bb < nb ? bb : blast; };
   Batch<RB> B0 = load_batch(b);
-  Batch<RB> B1 = load_batch(ahead(b + kWaves));
   xl.load(d.x, pass * kPass2bit + 64 * lane, (uint32_t)(64 * lane) < pw);
 
   __syncthreads();   // readers of the previous table and z are done
-  if (pass == 0)
+  if (!ZIN && pass == 0)
     for (uint32_t t = threadIdx.x; t < d.terms; t += kThreads) sm.z[t] = d.z[t];
   if constexpr (K > 0) build_table<XT>(d.x, pass * kPass2bit, pw, sm.tbl);
   __syncthreads();
   if (!has_rows) return;
 
   for (;;) {
-    const Batch<RB> B2 = load_batch(ahead(b + 2 * kWaves));
+    const Batch<RB> B1 = load_batch(ahead(b + kWaves));
     finish_batch(B0, b);
     if (b + kWaves >= nb) break;
     b += kWaves;
-    B0 = load_batch(ahead(b + 2 * kWaves));
+    B0 = load_batch(ahead(b + kWaves));
     finish_batch(B1, b);
-    if (b + kWaves >= nb) break;
-    b += kWaves;
-    B1 = load_batch(ahead(b + 2 * kWaves));
-    finish_batch(B2, b);
     if (b + kWaves >= nb) break;
     b += kWaves;
   }
@@ -352,10 +351,15 @@ __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0,
 // SF and K are the matrix's scale format and sites per group: every
 // (scale format, k) class has kernels of its own, so the registers of the
 // hot fp16 / k = 8 loop are not set by the heavier fp24 loads.
-template <int XT, int SF, int K, int RB>
+// ZIN: the workgroup computes the matrix's low-rank reductions itself (at the
+// start, before any row load, which keeps their registers apart from the
+// streaming loop's); otherwise a pre-pass left them in d.z.
+template <int XT, int SF, int K, int RB, bool ZIN>
 __device__ __forceinline__ void run_segment_2bit(const MatDev& d, uint32_t row0, uint32_t row1, StreamSmem& sm) {
   const uint32_t npass = (d.in + kPass2bit - 1) / kPass2bit;
-  for (uint32_t pass = 0; pass < npass; ++pass) stream_rows_2bit<XT, SF, K, RB>(d, row0, row1, pass, npass, sm);
+  if (ZIN && d.terms) z_all<XT>(d, sm.z);
+  for (uint32_t pass = 0; pass < npass; ++pass)
+    stream_rows_2bit<XT, SF, K, RB, ZIN>(d, row0, row1, pass, npass, sm);
   // y leaves through LDS: one coalesced write of the segment's rows instead
   // of a few scattered bytes per batch of rows.
   __syncthreads();
@@ -363,29 +367,32 @@ __device__ __forceinline__ void run_segment_2bit(const MatDev& d, uint32_t row0,
   for (uint32_t i = threadIdx.x; i < nrows; i += kThreads) d.y[row0 + i] = sm.ybuf[i];
 }
 
+// Three workgroups per CU (the LDS of a workgroup allows it) when the class's
+// registers fit three wavefronts per SIMD without spilling; the fp32 and the
+// fp24 / k = 8 loops need more registers and run two.
+constexpr int stream_waves_per_simd(int XT, int SF, int K) {
+  return XT == WAL_X_BF16 && !(SF == WAL_SCALE_FP24 && K == 8) ? 3 : 1;
+}
+
 template <int XT, int SF, int K, int RB>
-__global__ __launch_bounds__(kThreads) void k_stream_grouped(const MatDev* __restrict__ descs,
-                                                             const uint32_t* __restrict__ blockseg,
-                                                             const Seg* __restrict__ segs) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(stream_waves_per_simd(XT, SF, K))))
+void k_stream_grouped(const MatDev* __restrict__ descs, const uint32_t* __restrict__ blockseg,
+                      const Seg* __restrict__ segs) {
   __shared__ StreamSmem sm;
   const uint32_t s0 = blockseg[blockIdx.x], s1 = blockseg[blockIdx.x + 1];
   for (uint32_t s = s0; s < s1; ++s) {
     const Seg sg = segs[s];
-    run_segment_2bit<XT, SF, K, RB>(descs[sg.mat], sg.row0, sg.row1, sm);
+    run_segment_2bit<XT, SF, K, RB, false>(descs[sg.mat], sg.row0, sg.row1, sm);
   }
 }
 
 template <int XT, int SF, int K, int RB>
-__global__ __launch_bounds__(kThreads) void k_stream_single(MatDev d, uint32_t rows_per_block) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(stream_waves_per_simd(XT, SF, K))))
+void k_stream_single(MatDev d, uint32_t rows_per_block) {
   __shared__ StreamSmem sm;
   const uint32_t r0 = blockIdx.x * rows_per_block;
   const uint32_t r1 = min(d.out, r0 + rows_per_block);
-  if (r0 < r1) run_segment_2bit<XT, SF, K, RB>(d, r0, r1, sm);
-}
-
-template <int XT>
-__global__ __launch_bounds__(kThreads) void k_z_single(MatDev d) {
-  zjob<XT>(d, blockIdx.x * kZTerms);
+  if (r0 < r1) run_segment_2bit<XT, SF, K, RB, true>(d, r0, r1, sm);
 }
 
 template <int XT>
@@ -576,28 +583,19 @@ int plan_shape(uint32_t n, const wal_info* infos, uint32_t grid, int x_dtype, Pl
 
 extern "C" {
 
-int wal_gemv(const wal_info* info, const void* W_dev, const void* x_dev, int x_dtype, float* y_dev,
-             void* ws_dev, size_t ws_bytes, void* stream) {
+int wal_gemv(const wal_info* info, const void* W_dev, const void* x_dev, int x_dtype, float* y_dev, void* stream) {
   int st = check_info(info);
   if (st) return st;
   if (!W_dev || !x_dev || !y_dev) return WAL_ERR_ARG;
   if (x_dtype != WAL_X_F32 && x_dtype != WAL_X_BF16) return WAL_ERR_ARG;
   if (!aligned(W_dev, 256) || !aligned(x_dev, 16) || !aligned(y_dev, 4)) return WAL_ERR_ALIGN;
-  const size_t need = (size_t)gemm_shape(*info, 1).off_xp;   // z only
-  if (need && (!ws_dev || ws_bytes < need)) return ws_dev ? WAL_ERR_BUFFER : WAL_ERR_ARG;
-  if (need && !aligned(ws_dev, 16)) return WAL_ERR_ALIGN;
   if (overlap(x_dev, (size_t)info->d.in * xelem(x_dtype), y_dev, (size_t)info->d.out * 4)) return WAL_ERR_ARG;
   if ((st = check_blob_size(info))) return st;
   const uint32_t cls = class_of(info->d);
   if (!single_for(x_dtype, cls)) return WAL_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  MatDev d = make_dev(info, W_dev, x_dev, y_dev, static_cast<float*>(ws_dev), info->d.in, info->d.out, 1);
-  if (d.terms) {
-    const uint32_t g = (d.terms + kZTerms - 1) / kZTerms;
-    if (x_dtype == WAL_X_BF16) hipLaunchKernelGGL(k_z_single<WAL_X_BF16>, dim3(g), dim3(kThreads), 0, s, d);
-    else hipLaunchKernelGGL(k_z_single<WAL_X_F32>, dim3(g), dim3(kThreads), 0, s, d);
-    if ((st = launch_status())) return st;
-  }
+  // one launch: every workgroup computes the low-rank reductions itself
+  const MatDev d = make_dev(info, W_dev, x_dev, y_dev, nullptr, info->d.in, info->d.out, 1);
   uint32_t resident = 0;
   if ((st = resident_blocks(reinterpret_cast<const void*>(grouped_for(x_dtype, cls)), &resident))) return st;
   uint32_t rpb = (d.out + resident - 1) / resident;
@@ -644,7 +642,7 @@ int wal_gemm_small(const wal_info* info, const void* W_dev, const void* X_dev, i
   if (batched && batch > 1) return launch_gemm_valu(*info, d, batch, ws_dev, stream);
   for (uint32_t n = 0; n < batch; ++n) {
     const void* xn = static_cast<const uint8_t*>(X_dev) + (size_t)n * ldx * xe;
-    if ((st = wal_gemv(info, W_dev, xn, x_dtype, Y_dev + (size_t)n * ldy, ws_dev, ws_bytes, stream))) return st;
+    if ((st = wal_gemv(info, W_dev, xn, x_dtype, Y_dev + (size_t)n * ldy, stream))) return st;
   }
   return WAL_OK;
 }
@@ -792,8 +790,9 @@ int wal_grouped_plan(uint32_t n, const wal_info* infos, const void* const* W_dev
   return WAL_OK;
 }
 
-int wal_gemv_grouped(const wal_grouped_info* g, const void* plan_dev, void* stream) {
+int wal_gemv_grouped_phases(const wal_grouped_info* g, const void* plan_dev, int phases, void* stream) {
   if (!g || !plan_dev) return WAL_ERR_ARG;
+  if (phases < 1 || phases > WAL_PHASE_ALL) return WAL_ERR_ARG;
   if (!aligned(plan_dev, 16)) return WAL_ERR_ALIGN;
   if (g->x_dtype > WAL_X_BF16 || !g->n) return WAL_ERR_ARG;
   if (g->rows_per_batch != (uint32_t)kRB || !g->n_classes || g->n_classes > WAL_MAX_CLASSES) return WAL_ERR_ARG;
@@ -808,14 +807,14 @@ int wal_gemv_grouped(const wal_grouped_info* g, const void* plan_dev, void* stre
   const MatDev* descs = reinterpret_cast<const MatDev*>(base + g->off_descs);
   const uint32_t* jobs = reinterpret_cast<const uint32_t*>(base + g->off_zjobs);
   int st;
-  if (g->n_zjobs) {
+  if ((phases & WAL_PHASE_LOWRANK) && g->n_zjobs) {
     if (g->x_dtype == WAL_X_BF16)
       hipLaunchKernelGGL(k_z_grouped<WAL_X_BF16>, dim3(g->n_zjobs), dim3(kThreads), 0, s, descs, jobs);
     else
       hipLaunchKernelGGL(k_z_grouped<WAL_X_F32>, dim3(g->n_zjobs), dim3(kThreads), 0, s, descs, jobs);
     if ((st = launch_status())) return st;
   }
-  for (uint32_t k = 0; k < g->n_classes; ++k) {
+  for (uint32_t k = 0; (phases & WAL_PHASE_STREAM) && k < g->n_classes; ++k) {
     const uint32_t* blockseg = reinterpret_cast<const uint32_t*>(base + g->class_blockseg[k]);
     const Seg* segs = reinterpret_cast<const Seg*>(base + g->class_segs[k]);
     hipLaunchKernelGGL(grouped_for((int)g->x_dtype, g->class_id[k]), dim3(g->class_grid[k]), dim3(kThreads), 0, s,
@@ -823,6 +822,10 @@ int wal_gemv_grouped(const wal_grouped_info* g, const void* plan_dev, void* stre
     if ((st = launch_status())) return st;
   }
   return WAL_OK;
+}
+
+int wal_gemv_grouped(const wal_grouped_info* g, const void* plan_dev, void* stream) {
+  return wal_gemv_grouped_phases(g, plan_dev, WAL_PHASE_ALL, stream);
 }
 
 }  // extern "C"

@@ -50,9 +50,10 @@ constexpr uint32_t kThreads = 64 * kWaves;
 constexpr uint32_t kPass2bit = 4096;   // 2-bit: 64 trits per lane
 constexpr uint32_t kPassBase3 = 5120;  // base-3: 80 trits per lane
 // Rows of one segment of a streaming workgroup (its y values are staged in
-// LDS): the plans split longer row ranges.
-constexpr uint32_t kSegRows = 8192;
-// Low-rank terms handled per workgroup of the V^T x pre-pass.
+// LDS): the plans split longer row ranges.  Sized so that three workgroups
+// fit in a CU's LDS.
+constexpr uint32_t kSegRows = 4096;
+// Low-rank terms handled per workgroup of the V^T x pre-passes.
 constexpr uint32_t kZTerms = 4;
 constexpr uint32_t kMaxTerms = WAL_MAX_PATHS * WAL_MAX_RANK;
 

@@ -27,6 +27,12 @@ def _pack_one(args) -> Tuple[bytes, bytes]:
 
 
 def default_workers() -> int:
+    """Packing processes: WAL_PACK_WORKERS if set (1 packs in-process, e.g.
+    under a profiler that would follow every child), else the usable CPUs up
+    to 16."""
+    env = os.environ.get("WAL_PACK_WORKERS")
+    if env:
+        return max(1, int(env))
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:

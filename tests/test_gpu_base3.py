@@ -39,8 +39,7 @@ def run_gemv(wal, blob, info, x_bits):
     W = to_dev(blob)
     xt = to_dev(x_bits.view(np.int16)).view(torch.bfloat16)
     y = torch.full((info.d.out,), float("nan"), dtype=torch.float32, device=dev())
-    ws = torch.zeros(max(wal.wal_workspace_size(info, 1), 4) // 4, dtype=torch.float32, device=dev())
-    wal.wal_gemv(info, W, xt, y, ws)
+    wal.wal_gemv(info, W, xt, y)
     torch.cuda.synchronize()
     return y.cpu().numpy().astype(np.float64)
 
@@ -111,7 +110,7 @@ def test_base3_rejects_fp32_activations(wal):
     x = torch.zeros(128, dtype=torch.float32, device=dev())
     y = torch.zeros(8, dtype=torch.float32, device=dev())
     with pytest.raises(wal.WalError) as ei:
-        wal.wal_gemv(info, W, x, y, None)
+        wal.wal_gemv(info, W, x, y)
     assert ei.value.status == -9
 
 

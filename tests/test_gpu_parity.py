@@ -46,9 +46,7 @@ def run_gemv(wal, blob, info, x_f32, x_bits):
     W = to_dev(blob)
     xt = x_tensor(x_f32, x_bits)
     y = torch.full((info.d.out,), float("nan"), dtype=torch.float32, device=dev())
-    nws = wal.wal_workspace_size(info, 1)
-    ws = torch.zeros(max(nws, 4) // 4, dtype=torch.float32, device=dev())
-    wal.wal_gemv(info, W, xt, y, ws)
+    wal.wal_gemv(info, W, xt, y)
     torch.cuda.synchronize()
     return y.cpu().numpy().astype(np.float64)
 

@@ -228,20 +228,27 @@ def test_product_calls_check_arguments_before_any_launch():
     info = wal.wal_packed_size(wal.make_desc(64, 256, 8, 1, 16))
     lib = wal._lib
     W, x, y, ws = 0x10000, 0x20000, 0x30000, 0x40000
-    ok_args = (ctypes.byref(info), W, x, wal.WAL_X_BF16, y, ws, 256, None)
-    assert lib.wal_gemv(ctypes.byref(info), W + 16, x, 1, y, ws, 256, None) == -6     # W not 256-aligned
-    assert lib.wal_gemv(ctypes.byref(info), W, x + 2, 1, y, ws, 256, None) == -6      # x not 16-aligned
-    assert lib.wal_gemv(ctypes.byref(info), W, x, 1, y + 2, ws, 256, None) == -6      # y not 4-aligned
-    assert lib.wal_gemv(ctypes.byref(info), W, x, 1, y, ws, 8, None) == -5            # workspace too small
-    assert lib.wal_gemv(ctypes.byref(info), W, x, 1, y, None, 0, None) == -1          # workspace missing
-    assert lib.wal_gemv(ctypes.byref(info), W, x, 7, y, ws, 256, None) == -1          # dtype
-    assert lib.wal_gemv(ctypes.byref(info), None, x, 1, y, ws, 256, None) == -1
-    assert lib.wal_gemv(ctypes.byref(info), W, x, 1, x + 64, ws, 256, None) == -1     # y overlaps x
+    ok_args = (ctypes.byref(info), W, x, wal.WAL_X_BF16, y, None)
+    assert lib.wal_gemv(ctypes.byref(info), W + 16, x, 1, y, None) == -6     # W not 256-aligned
+    assert lib.wal_gemv(ctypes.byref(info), W, x + 2, 1, y, None) == -6      # x not 16-aligned
+    assert lib.wal_gemv(ctypes.byref(info), W, x, 1, y + 2, None) == -6      # y not 4-aligned
+    assert lib.wal_gemv(ctypes.byref(info), W, x, 7, y, None) == -1          # dtype
+    assert lib.wal_gemv(ctypes.byref(info), None, x, 1, y, None) == -1
+    assert lib.wal_gemv(ctypes.byref(info), W, x, 1, x + 64, None) == -1     # y overlaps x
     bad = wal.wal_info.from_buffer_copy(info)
     bad.off_alpha += 256
-    assert lib.wal_gemv(ctypes.byref(bad), *ok_args[1:]) == -7                        # inconsistent info
-    assert lib.wal_gemm_small(ctypes.byref(info), W, x, 1, 0, 256, y, 64, 0, ws, 256, None) == -1
-    assert lib.wal_gemm_small(ctypes.byref(info), W, x, 1, 33, 256, y, 64, 0, ws, 256, None) == -1
+    assert lib.wal_gemv(ctypes.byref(bad), *ok_args[1:]) == -7               # inconsistent info
+    need = wal.wal_workspace_size(info, 2)
+    gs = lambda *a: lib.wal_gemm_small(ctypes.byref(info), *a)  # noqa: E731
+    assert gs(W, x, 1, 0, 256, y, 64, 0, ws, need, None) == -1               # batch 0
+    assert gs(W, x, 1, 33, 256, y, 64, 0, ws, need, None) == -1              # batch > 32
+    assert gs(W, x, 1, 2, 256, y, 64, 3, ws, need, None) == -1               # mode
+    assert gs(W, x, 1, 2, 255, y, 64, 0, ws, need, None) == -1               # ldx < in
+    assert gs(W, x, 1, 2, 256, y, 63, 0, ws, need, None) == -1               # ldy < out
+    assert gs(W, x, 1, 2, 260, y, 64, 0, ws, need, None) == -6               # row pitch
+    assert gs(W, x, 1, 2, 256, y, 64, 0, ws, need - 4, None) == -5           # workspace too small
+    assert gs(W, x, 1, 2, 256, y, 64, 0, None, 0, None) == -1                # workspace missing
+    assert gs(W, x, 1, 2, 256, y, 64, 0, x + 256, need, None) == -1          # workspace overlaps X
     assert lib.wal_gemv_grouped(None, 0x1000, None) == -1
 
 
@@ -309,7 +316,7 @@ def test_grouped_plan_covers_every_row_once(grid):
             for m, r0, r1, _ in segs[blockseg[b]:blockseg[b + 1]]:
                 assert _class_of(infos[m]) == c
                 assert r0 < r1 <= shapes[m][0]
-                assert r1 - r0 <= (1024 if c >= 8 else 8192)   # rows whose y one workgroup stages
+                assert r1 - r0 <= (1024 if c >= 8 else 4096)   # rows whose y one workgroup stages
                 covered[m][r0:r1] += 1
                 per_block[b] += (r1 - r0) * rb[m]
         # streamed bytes per workgroup are balanced to within a row of the
