@@ -182,10 +182,11 @@ int wal_unpack(const void* blob, size_t bytes, int8_t* T, uint8_t* site_pos,
                int8_t* site_sign, float* alpha, float* beta, int8_t* U,
                int8_t* V, float* s);
 
-/* Device workspace that wal_gemm_small needs for a blob and batch: the
- * per-path reductions z_p = diag(s_p) V_p^T X [batch][n_paths * rank], X in
- * MFMA operand order and the per-K-slice partial sums [slices][batch][out]
- * (fp32), each part padded to 256 bytes.  Errors: ARG, SHAPE, FORMAT. */
+/* Device workspace that wal_gemm_small needs for a blob and batch (the
+ * batched-GEMV kernel's): the per-path reductions z_p = diag(s_p) V_p^T X per
+ * 4096-column chunk [chunks][batch][n_paths * rank] and the per-pass partial
+ * sums [passes][batch][out] (fp32), each part padded to 256 bytes.
+ * Errors: ARG, SHAPE, FORMAT. */
 int wal_workspace_size(const wal_info* info, uint32_t batch, size_t* bytes);
 
 /* y = W(x) for one matrix, batch 1 (WAL-Ternary-8B cards, "Representation":

@@ -159,19 +159,21 @@ __device__ __forceinline__ float f16_at(const uint8_t* p, uint32_t i) {
 
 // ---------------------------------------------------------------------------
 // Low-rank reductions of one matrix by a whole workgroup:
-// z[t] = s_p[r] * sum_j (-1)^{V_p[r] bit j} x_j for the C terms t0 .. t0 + C - 1
-// (those below d.terms), written to out[t] by threads t - t0.  Every thread
-// of the workgroup calls it (it holds a barrier).
+// z[t] = s_p[r] * sum_j (-1)^{V_p[r] bit j} x_j over the columns j in
+// [c0, c1) (multiples of 16) for the C terms t0 .. t0 + C - 1 (those below
+// d.terms), written to out[t] by threads t - t0.  Every thread of the
+// workgroup (up to 1024) calls it (it holds a barrier).
 template <int XT, int C>
-__device__ __forceinline__ void z_chunk(const MatDev& d, const void* x, uint32_t t0, float* out) {
-  __shared__ float red[kWaves][C];
-  const uint32_t tid = threadIdx.x;
+__device__ __forceinline__ void z_chunk(const MatDev& d, const void* x, uint32_t t0, float* out, uint32_t c0,
+                                        uint32_t c1) {
+  __shared__ float red[16][C];
+  const uint32_t tid = threadIdx.x, nthr = blockDim.x;
   const int lane = tid & 63;
   const uint32_t T = d.terms, vrow = d.in / 8;
   float acc[C];
 #pragma unroll
   for (int q = 0; q < C; ++q) acc[q] = 0.f;
-  for (uint32_t c = tid * 16; c < d.in; c += kThreads * 16) {
+  for (uint32_t c = c0 + tid * 16; c < c1; c += nthr * 16) {
     uint32_t xb[16];   // fp32 bit patterns of x[c .. c + 15]
     if constexpr (XT == WAL_X_BF16) {
       const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + c);
@@ -210,8 +212,7 @@ __device__ __forceinline__ void z_chunk(const MatDev& d, const void* x, uint32_t
     const uint32_t t = t0 + tid;
     if (t < T) {
       float sum = 0.f;
-#pragma unroll
-      for (int w = 0; w < (int)kWaves; ++w) sum += red[w][tid];
+      for (uint32_t w = 0; w < (nthr >> 6); ++w) sum += red[w][tid];
       const uint32_t p = t / d.rank, r = t % d.rank;
       out[t] = f16_at(path_ptr(d.s, p), r) * sum;
     }
@@ -221,7 +222,7 @@ __device__ __forceinline__ void z_chunk(const MatDev& d, const void* x, uint32_t
 // One pre-pass workgroup: terms t0 .. t0 + kZTerms - 1 of one matrix into d.z.
 template <int XT>
 __device__ __forceinline__ void zjob(const MatDev& d, uint32_t t0) {
-  z_chunk<XT, (int)kZTerms>(d, d.x, t0, d.z);
+  z_chunk<XT, (int)kZTerms>(d, d.x, t0, d.z, 0, d.in);
 }
 
 // Every low-rank term of one matrix into out (LDS), visible to the whole
@@ -230,7 +231,7 @@ constexpr int kZChunk = 16;
 template <int XT>
 __device__ __forceinline__ void z_all(const MatDev& d, float* out) {
   for (uint32_t t0 = 0; t0 < d.terms; t0 += kZChunk) {
-    z_chunk<XT, kZChunk>(d, d.x, t0, out);
+    z_chunk<XT, kZChunk>(d, d.x, t0, out, 0, d.in);
     __syncthreads();   // out is complete and red free for the next chunk
   }
 }

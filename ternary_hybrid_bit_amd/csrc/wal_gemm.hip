@@ -4,25 +4,34 @@
 //     Y[n][row] = sum_g ( alpha[row][g] * sum_{k in g} T[row][k] X[n][k]
 //                       +  beta[row][g] * sum_{k in g} R[row][k] X[n][k] )
 //               + sum_t (-1)^{U bit} z[n][t]
-// (WAL pages, "Format": the ternary-hybrid product and its binary low-rank
-// paths; the per-(row, group) scales are applied in fp32 in both kernels).
+// (WAL-Ternary-8B cards, "Representation": the ternary-hybrid product and its
+// binary low-rank paths; the per-(row, group) scales are applied in fp32).
 //
-// Two kernels, both writing per-K-slice partial sums to the workspace, which
-// a last kernel adds in a fixed order together with the low-rank term:
-//  * k_gemv_batch (vector ALUs): a wavefront takes kGemvRows rows of one
-//    4096-column pass for up to kGemvCols columns.  Each lane decodes its 64
-//    trits of a row once (shift and mask to bf16 +-2 / 0, as the batch-1
-//    kernels do) and feeds them to one v_dot2_f32_bf16 per trit pair and
-//    column; the sites gather 2x from a per-pass LDS copy of X.
-//  * k_mfma (matrix cores): v_mfma_f32_16x16x32_bf16 over 16 rows x 16 batch
-//    columns x 32 columns of a group.  A lane (row i = lane & 15, K block
-//    kb = lane >> 4) decodes its 8 code bytes straight into A operands; the
-//    group's sites are scattered as +-2 into a per-wavefront LDS tile in
-//    operand order, read back as a second A operand and cleared; X comes in
-//    operand order from a pre-pass (k_xperm).  The two group sums land in
-//    separate accumulators that alpha and beta scale in fp32.
-// Decoded values are exact in bf16, the products and sums are fp32, so
-// x = e_j still gives column j of W exactly.
+// Batched GEMV (k_gemv_batch, vector ALUs), two launches:
+//  1. a wavefront takes kGemvRows rows of one 4096-column pass for up to
+//     kGemvCols columns and writes its partial sums P[pass][n][row].  Each
+//     lane decodes its 64 trits of a row once (shift and mask to bf16 +-2 / 0,
+//     as the batch-1 kernels do) and feeds them to one v_dot2_f32_bf16 per
+//     trit pair and column; the sites gather 2x from a per-pass LDS copy of X.
+//     Extra workgroups at the end of the grid write the low-rank reductions
+//     of every batch column per 4096-column chunk, zpart[chunk][n][t];
+//  2. k_reduce adds the passes and the chunks in a fixed order, adds the
+//     low-rank term and stores Y.
+// MFMA (k_mfma, matrix cores), one launch: one workgroup per 16-row tile; its
+// wavefronts split the tile's 128-column groups, and each group is a few
+// v_mfma_f32_16x16x32_bf16 over 16 rows x 16 batch columns x 32 columns.  A
+// lane (row i = lane & 15, K block kb = lane >> 4) decodes its 8 code bytes
+// straight into A operands; the group's sites are scattered as +-2 into a
+// per-wavefront LDS tile in operand order, read back as a second A operand
+// and cleared; the lane builds its B operands from 64 bytes of X row 16t + i
+// with byte permutes.  The two group sums land in separate accumulators that
+// alpha and beta scale in fp32.  V enters as a third, +-1 A operand on the
+// same B operands, which gives the low-rank reductions z of the tile's
+// columns; the wavefronts' sums meet in LDS, where the workgroup finishes Y.
+// Every weight load of a wavefront is issued before it touches X, so the HBM
+// latency is paid once.  Decoded values are exact in bf16 and every product
+// and sum is fp32, so x = e_j still gives column j of W exactly, and every
+// sum runs in a fixed order: results do not depend on timing.
 #include <hip/hip_runtime.h>
 
 #include "wal_device.h"
@@ -50,28 +59,44 @@ __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v 
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 
 // ---------------------------------------------------------------------------
-// Low-rank reductions for every batch column: z[n][t], blockIdx.y = n.
-__global__ __launch_bounds__(kThreads) void k_z_batch(MatDev d) {
-  MatDev e = d;
-  e.x = reinterpret_cast<const uint16_t*>(d.x) + (size_t)blockIdx.y * d.ldx;
-  e.z = d.z + (size_t)blockIdx.y * d.terms;
-  z_chunk<WAL_X_BF16, kZTerms>(e, e.x, blockIdx.x * kZTerms, e.z);
+// Low-rank partials: block b of the z part of a grid computes, for batch
+// column n, terms 16 tc .. 16 tc + 15 over columns [4096 cc, 4096 cc + 4096).
+__device__ __forceinline__ void z_block(const MatDev& d, float* __restrict__ zpart, uint32_t b) {
+  const uint32_t tcs = (d.terms + kZTermsPerBlock - 1) / kZTermsPerBlock;
+  const uint32_t tc = b % tcs, rest = b / tcs, n = rest % d.batch, cc = rest / d.batch;
+  const void* x = reinterpret_cast<const uint16_t*>(d.x) + (size_t)n * d.ldx;
+  float* out = zpart + ((size_t)cc * d.batch + n) * d.terms;
+  const uint32_t c0 = cc * kZChunkCols, c1 = min(d.in, c0 + kZChunkCols);
+  z_chunk<WAL_X_BF16, (int)kZTermsPerBlock>(d, x, tc * kZTermsPerBlock, out, c0, c1);
+}
+
+uint32_t z_blocks(const MatDev& d, const GemmShape& S) {
+  return d.terms ? S.zc * d.batch * ((d.terms + kZTermsPerBlock - 1) / kZTermsPerBlock) : 0;
 }
 
 // Y[n][row] = sum over K slices of the partials (in slice order) + the
-// low-rank term.
-__global__ __launch_bounds__(256) void k_partial_reduce(MatDev d, const float* __restrict__ P, uint32_t slices) {
-  const uint32_t row = blockIdx.x * 256 + threadIdx.x, n = blockIdx.y;
+// low-rank term with z[n][t] = sum over chunks of zpart (in chunk order).
+__global__ __launch_bounds__(256) void k_reduce(MatDev d, const float* __restrict__ zpart,
+                                                const float* __restrict__ P, uint32_t slices, uint32_t zc) {
+  __shared__ float zs[kMaxTerms];
+  const uint32_t n = blockIdx.y, row = blockIdx.x * 256 + threadIdx.x;
+  for (uint32_t t = threadIdx.x; t < d.terms; t += 256) {
+    float z = 0.f;
+    for (uint32_t cc = 0; cc < zc; ++cc) z += zpart[((size_t)cc * d.batch + n) * d.terms + t];
+    zs[t] = z;
+  }
+  __syncthreads();
   if (row >= d.out) return;
   const size_t plane = (size_t)d.batch * d.out;
   float v = 0.f;
   for (uint32_t s = 0; s < slices; ++s) v += P[s * plane + (size_t)n * d.out + row];
   const uint32_t ub = (d.rank + 7) / 8;
-  for (uint32_t t = 0; t < d.terms; ++t) {
-    const uint32_t p = t / d.rank, r = t % d.rank;
-    const uint32_t bit = (path_ptr(d.U, p)[(size_t)row * ub + r / 8] >> (r & 7)) & 1u;
-    const float zt = d.z[(size_t)n * d.terms + t];
-    v += bit ? -zt : zt;
+  for (uint32_t p = 0; p < d.n_paths; ++p) {
+    const uint8_t* u = path_ptr(d.U, p) + (size_t)row * ub;
+    for (uint32_t r = 0; r < d.rank; ++r) {
+      const float zt = zs[p * d.rank + r];
+      v += ((u[r >> 3] >> (r & 7)) & 1u) ? -zt : zt;
+    }
   }
   d.y[(size_t)n * d.ldy + row] = v;
 }
@@ -95,26 +120,55 @@ __device__ __forceinline__ void dot_batch(uint64_t q, int h, const uint32_t (&p)
   if constexpr (I < 7) dot_batch<NB, I + 1>(q, h, p, a);
 }
 
+// Block b < nmain: pass b % passes, rows of block (b / passes) % nrb, batch
+// columns NB * (b / (passes * nrb)) ..; blocks past nmain: low-rank partials.
 template <int SF, int K, int NB>
-__global__ __launch_bounds__(kThreads) void k_gemv_batch(MatDev d, float* __restrict__ P) {
+__global__ __launch_bounds__(kThreads) void k_gemv_batch(MatDev d, float* __restrict__ P, float* __restrict__ zpart,
+                                                         uint32_t nmain, uint32_t passes, uint32_t nrb) {
+  if (blockIdx.x >= nmain) {
+    z_block(d, zpart, blockIdx.x - nmain);
+    return;
+  }
   // X of the pass, doubled, as [column][NB] bf16: the site gathers
   __shared__ uint16_t tbl[kPass2bit * NB];
   constexpr uint32_t R = kGemvRows * NB;
   constexpr uint32_t SB = SF == WAL_SCALE_FP16 ? 2 : 3;
-  const uint32_t pass = blockIdx.x, c0 = blockIdx.z * NB;
+  const uint32_t pass = blockIdx.x % passes, rest = blockIdx.x / passes;
+  const uint32_t c0 = (rest / nrb) * NB;
+  const uint32_t row_base = (rest % nrb) * (kWaves * kGemvRows) + wave_id() * kGemvRows;
   const uint32_t col0 = pass * kPass2bit, pw = min(kPass2bit, d.in - col0);
   const int lane = threadIdx.x & 63;
+  const bool active = (uint32_t)lane * 64 < pw;
   const uint16_t* X = reinterpret_cast<const uint16_t*>(d.x);
 
-  for (uint32_t e = threadIdx.x; e < kPass2bit; e += kThreads)
+  // Weights first: every row of the wavefront (rows past the matrix repeat
+  // its last row; lanes past the pass width read their row's last group, in
+  // bounds, with zero x and scales).
+  const uint32_t G = d.groups;
+  const uint32_t g = min(pass * (kPass2bit / 128) + (lane >> 1), G - 1), h = lane & 1;
+  const uint32_t cvoff = min(col0 / 4 + lane * 16, d.row_stride - 16);
+  const __amdgpu_buffer_rsrc_t rc = rsrc(d.codes, d.blob_bytes);
+  const __amdgpu_buffer_rsrc_t ra = rsrc(d.alpha, d.blob_bytes - (uint32_t)(d.alpha - d.codes));
+  __amdgpu_buffer_rsrc_t rs = rsrc(d.codes, 0u), rb = rsrc(d.codes, 0u);
+  if constexpr (K > 0) {
+    rs = rsrc(d.sites, d.blob_bytes - (uint32_t)(d.sites - d.codes));
+    rb = rsrc(d.beta, d.blob_bytes - (uint32_t)(d.beta - d.codes));
+  }
+  u32x4_t c[kGemvRows];
+  uint32_t sa[kGemvRows], sbeta[kGemvRows], st[kGemvRows];
 #pragma unroll
-    for (int n = 0; n < NB; ++n) {
-      uint32_t v = 0;
-      if (e < pw && c0 + n < d.batch) v = X[(size_t)(c0 + n) * d.ldx + col0 + e];
-      tbl[e * NB + n] = (uint16_t)(__float_as_uint(2.0f * __uint_as_float(v << 16)) >> 16);
+  for (uint32_t j = 0; j < kGemvRows; ++j) {
+    const uint32_t row = min(row_base + j, d.out - 1);
+    c[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rc, cvoff, row * d.row_stride,
+                                                                             kStream));
+    sa[j] = load_scale<SF>(ra, g * SB, row * G * SB);
+    if constexpr (K > 0) {
+      sbeta[j] = load_scale<SF>(rb, g * SB, row * G * SB);
+      st[j] = load_sites<K>(rs, g * K + h * (K / 2), row * G * K);
     }
+  }
 
-  const bool active = (uint32_t)lane * 64 < pw;
+  // x pairs of the lane's 64 columns, every batch column of the block
   uint32_t p[NB][32];
 #pragma unroll
   for (int n = 0; n < NB; ++n) {
@@ -139,36 +193,22 @@ __global__ __launch_bounds__(kThreads) void k_gemv_batch(MatDev d, float* __rest
       for (int q = 0; q < 32; ++q) p[n][q] = 0;
     }
   }
-  __syncthreads();
-
-  const uint32_t row_base = blockIdx.y * (kWaves * kGemvRows) + wave_id() * kGemvRows;
-  if (row_base >= d.out) return;   // no barrier follows
-  // Lanes past the pass width read their row's last group (in bounds; their
-  // x pairs and scales are zero).
-  const uint32_t G = d.groups;
-  const uint32_t g = min(pass * (kPass2bit / 128) + (lane >> 1), G - 1), h = lane & 1;
-  const uint32_t cvoff = min(col0 / 4 + lane * 16, d.row_stride - 16);
-  const __amdgpu_buffer_rsrc_t rc = rsrc(d.codes, d.blob_bytes);
-  const __amdgpu_buffer_rsrc_t ra = rsrc(d.alpha, d.blob_bytes - (uint32_t)(d.alpha - d.codes));
-  __amdgpu_buffer_rsrc_t rs = rsrc(d.codes, 0u), rb = rsrc(d.codes, 0u);
-  if constexpr (K > 0) {
-    rs = rsrc(d.sites, d.blob_bytes - (uint32_t)(d.sites - d.codes));
-    rb = rsrc(d.beta, d.blob_bytes - (uint32_t)(d.beta - d.codes));
-  }
-
-  u32x4_t c[kGemvRows];
-  uint32_t sa[kGemvRows], sbeta[kGemvRows], st[kGemvRows];
+  // site table: 8 columns of one batch column per thread and step (a fixed
+  // trip count, so every load is issued before the first store)
 #pragma unroll
-  for (uint32_t j = 0; j < kGemvRows; ++j) {
-    const uint32_t row = min(row_base + j, d.out - 1);
-    c[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rc, cvoff, row * d.row_stride,
-                                                                             kStream));
-    sa[j] = load_scale<SF>(ra, g * SB, row * G * SB);
-    if constexpr (K > 0) {
-      sbeta[j] = load_scale<SF>(rb, g * SB, row * G * SB);
-      st[j] = load_sites<K>(rs, g * K + h * (K / 2), row * G * K);
+  for (uint32_t it = 0; it < kPass2bit / 8 * NB / kThreads; ++it) {
+    const uint32_t e = threadIdx.x + it * kThreads;
+    const uint32_t n = e % NB, c8 = (e / NB) * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (c8 < pw && c0 + n < d.batch) v = *reinterpret_cast<const uint4*>(X + (size_t)(c0 + n) * d.ldx + col0 + c8);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t b = (w[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
+      tbl[(c8 + k) * NB + n] = (uint16_t)(__float_as_uint(2.0f * __uint_as_float(b << 16)) >> 16);
     }
   }
+  __syncthreads();
 
   float acc[R];
 #pragma unroll
@@ -217,98 +257,155 @@ __global__ __launch_bounds__(kThreads) void k_gemv_batch(MatDev d, float* __rest
 // ---------------------------------------------------------------------------
 // MFMA path.
 
-// X in operand order: Xp[g][t][m][lane][q] (bf16 pairs).  For n-tile t,
-// MFMA m of group g and lane (n, kb), pair q holds X[16t + n][K_lo],
-// X[16t + n][K_lo + 8] with o = 4m + q, K_lo = 128g + 32kb + 16(o >> 3) + (o & 7):
-// the trit pair the A-operand decode puts in the same slot.
-__global__ __launch_bounds__(256) void k_xperm(MatDev d, uint32_t nt, uint32_t* __restrict__ Xp) {
-  const uint32_t id = blockIdx.x * 256 + threadIdx.x;   // (g, t, m, lane)
-  if (id >= d.groups * nt * 4 * 64) return;
-  const uint32_t lane = id & 63, m = (id >> 6) & 3, rest = id >> 8;
-  const uint32_t t = rest % nt, g = rest / nt;
-  const uint32_t n = 16 * t + (lane & 15), kb = lane >> 4;
-  const uint16_t* X = reinterpret_cast<const uint16_t*>(d.x) + (size_t)n * d.ldx;
-  uint32_t v[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t o = 4 * m + q;
-    const uint32_t klo = 128 * g + 32 * kb + 16 * (o >> 3) + (o & 7);
-    v[q] = n < d.batch ? (uint32_t)X[klo] | ((uint32_t)X[klo + 8] << 16) : 0u;
-  }
-  reinterpret_cast<uint4*>(Xp)[id] = make_uint4(v[0], v[1], v[2], v[3]);
-}
-
 __device__ __forceinline__ f32x4_t mfma(const uint4& a, const uint4& b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
                                                  0, 0, 0);
 }
 
-// One wavefront: kMfmaTiles row tiles x NT n-tiles over groups [g0, g1) of
-// K slice ks; writes 0.5 x its partial (decoded values are 2x).
+// B operands of one group for one n-tile: lane (n, kb) holds X[n][128 g + 32 kb
+// + c], c < 32, as w[16] (bf16 pairs in memory order); operand m, pair q is
+// (X[.][K_lo], X[.][K_lo + 8]) with o = 4m + q, K_lo = 16 (o >> 3) + (o & 7):
+// the trit pair the A-operand decode puts in the same slot.
+__device__ __forceinline__ void x_operands(const uint4 (&raw)[4], uint4 (&b)[4]) {
+  const uint32_t w[16] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w, raw[1].x, raw[1].y, raw[1].z, raw[1].w,
+                          raw[2].x, raw[2].y, raw[2].z, raw[2].w, raw[3].x, raw[3].y, raw[3].z, raw[3].w};
+  uint32_t o4[16];
+#pragma unroll
+  for (int o = 0; o < 16; ++o) {
+    const int lo = 16 * (o >> 3) + (o & 7);   // hi = lo + 8: same half of w[lo / 2 + 4]
+    // one v_perm_b32: low or high halves of the two dwords
+    o4[o] = __builtin_amdgcn_perm(w[(lo >> 1) + 4], w[lo >> 1], (lo & 1) ? 0x07060302u : 0x05040100u);
+  }
+#pragma unroll
+  for (int m = 0; m < 4; ++m) b[m] = make_uint4(o4[4 * m], o4[4 * m + 1], o4[4 * m + 2], o4[4 * m + 3]);
+}
+
+// T operands of one group from the lane's 8 code bytes (q: dword 1 : dword
+// 0): operand m, pair k holds the trits of columns 16 (o >> 3) + (o & 7) and
+// + 8, o = 4m + k, as bf16 +-2 / 0.  A 64-bit shift positions the pairs of
+// both dwords at once (pairs o and o + 8 share a shift).
+template <int I>
+__device__ __forceinline__ void a_operands(uint64_t q, uint4 (&a)[4]) {
+  const uint64_t s = shl64<14 - 2 * I>(q);
+  const uint32_t lo = (uint32_t)s & 0xC000C000u, hi = (uint32_t)(s >> 32) & 0xC000C000u;
+  // o = I (dword 0) and o = 8 + I (dword 1)
+  reinterpret_cast<uint32_t*>(&a[I >> 2])[I & 3] = lo;
+  reinterpret_cast<uint32_t*>(&a[2 + (I >> 2)])[I & 3] = hi;
+  if constexpr (I < 7) a_operands<I + 1>(q, a);
+}
+
+// Wavefronts per workgroup of k_mfma (at most) and group slots per sweep.
+template <int NT>
+constexpr uint32_t mfma_max_waves() { return NT == 1 ? 12 : 8; }
+constexpr uint32_t kSlots = 4;
+
+// Block b < tiles: one 16-row tile over all columns; its wavefronts take gpw
+// consecutive groups each (kSlots per sweep) and are summed in LDS into
+// P[0][n][row] = 0.5 sum_waves (alpha sT + beta sR) (decoded values are 2x).
+// Blocks past the tiles: low-rank partials (z_block).
 template <int SF, int K, int NT>
-__global__ __launch_bounds__(kThreads) void k_mfma(MatDev d, const uint32_t* __restrict__ Xp,
-                                                   float* __restrict__ P, uint32_t ks_count) {
-  __shared__ uint4 rtile[kWaves][64][4];   // per-wavefront R operands, operand order
+__global__ __launch_bounds__(mfma_max_waves<NT>() * 64) void k_mfma(MatDev d, float* __restrict__ P,
+                                                                      float* __restrict__ zpart, uint32_t tiles,
+                                                                      uint32_t gpw) {
+  if (blockIdx.x >= tiles) {
+    z_block(d, zpart, blockIdx.x - tiles);
+    return;
+  }
+  constexpr uint32_t MW = mfma_max_waves<NT>();
+  // per-wavefront R tiles during the sweeps, then the wavefront partials
+  __shared__ __align__(16) uint8_t lds[MW * 4096 > MW * NT * 1024 ? MW * 4096 : MW * NT * 1024];
+  const uint32_t nw = blockDim.x >> 6;
   const int lane = threadIdx.x & 63;
   const uint32_t wave = wave_id();
-  const uint32_t w = blockIdx.x * kWaves + wave;
-  const uint32_t rb = w / ks_count, ks = w % ks_count;
-  const uint32_t row_base = rb * kMfmaRows;
-  if (row_base >= d.out) return;   // whole wavefront; no barrier follows
+  const uint32_t row_base = blockIdx.x * 16;
   const uint32_t G = d.groups;
-  const uint32_t g0 = (uint32_t)((uint64_t)ks * G / ks_count);
-  const uint32_t g1 = (uint32_t)((uint64_t)(ks + 1) * G / ks_count);
+  const uint32_t gw0 = min(G, wave * gpw), gw1 = min(G, gw0 + gpw);
   constexpr uint32_t SB = SF == WAL_SCALE_FP16 ? 2 : 3;
   const uint32_t i = lane & 15, kb = lane >> 4;
-  uint4* rt = rtile[wave][0];
-  uint16_t* rt16 = reinterpret_cast<uint16_t*>(rtile[wave][0]);
+  const uint32_t row = min(row_base + i, d.out - 1);
+  uint4* rt4 = reinterpret_cast<uint4*>(lds + wave * 4096);
+  uint16_t* rt16 = reinterpret_cast<uint16_t*>(lds + wave * 4096);
+  f32x4_t* red = reinterpret_cast<f32x4_t*>(lds);
+
+  const __amdgpu_buffer_rsrc_t rc = rsrc(d.codes, d.blob_bytes);
+  // one resource over the alpha and beta planes: lanes 0-15 fetch alpha of
+  // tile row (lane & 15), lanes 16-31 its beta (a per-lane offset, so the
+  // resource stays uniform)
+  const __amdgpu_buffer_rsrc_t ra = rsrc(d.alpha, d.blob_bytes - (uint32_t)(d.alpha - d.codes));
+  const uint32_t sbase = (K > 0 && lane >= 16) ? (uint32_t)(d.beta - d.alpha) : 0u;
+  __amdgpu_buffer_rsrc_t rs = rsrc(d.codes, 0u);
+  if constexpr (K > 0) rs = rsrc(d.sites, d.blob_bytes - (uint32_t)(d.sites - d.codes));
+  // The weight loads read 8 to 32 bytes per row and instruction; the rest of
+  // each cache line is read moments later by the next slots or wavefronts,
+  // so they keep the default cache policy (the lines stay in L2).
+  constexpr int kCached = 0;
+
+  // X rows of the lane's batch columns (columns past the batch read row 0:
+  // a B-operand column only feeds its own output column, never stored)
+  const uint16_t* xr[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const uint32_t n = 16 * t + i;
+    xr[t] = reinterpret_cast<const uint16_t*>(d.x) + (size_t)(n < d.batch ? n : 0) * d.ldx + 32 * kb;
+  }
+  auto load_x = [&](uint32_t g, uint4 (&raw)[NT][4]) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const uint4* src = reinterpret_cast<const uint4*>(xr[t] + 128 * g);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) raw[t][k] = src[k];
+    }
+  };
+
+  f32x4_t C[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) C[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   if constexpr (K > 0) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) rt[lane * 4 + m] = make_uint4(0, 0, 0, 0);
+    for (int m = 0; m < 4; ++m) rt4[m * 64 + lane] = make_uint4(0, 0, 0, 0);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   }
 
-  const __amdgpu_buffer_rsrc_t rc = rsrc(d.codes, d.blob_bytes);
-  const __amdgpu_buffer_rsrc_t ra = rsrc(d.alpha, d.blob_bytes - (uint32_t)(d.alpha - d.codes));
-  __amdgpu_buffer_rsrc_t rs = rsrc(d.codes, 0u), rbe = rsrc(d.codes, 0u);
-  if constexpr (K > 0) {
-    rs = rsrc(d.sites, d.blob_bytes - (uint32_t)(d.sites - d.codes));
-    rbe = rsrc(d.beta, d.blob_bytes - (uint32_t)(d.beta - d.codes));
-  }
-  // lanes 0-15 fetch alpha of tile row (lane & 15), lanes 16-31 its beta
-  const bool fetch_beta = K > 0 && lane >= 16;
-
-  f32x4_t C[kMfmaTiles][NT];
+  for (uint32_t c0 = gw0; c0 < gw1; c0 += kSlots) {   // wave-uniform
+    const uint32_t ns = min(kSlots, gw1 - c0);
+    // every weight load of the sweep first (slots past the range repeat the
+    // last group of the matrix: in bounds, dropped by a zero scale); rows
+    // differ across the lanes, so the row offsets go in the voffset
+    u32x4_t cw[kSlots / 2];   // codes of slots 2h, 2h + 1 (8 bytes each)
+    uint32_t sraw[kSlots], sbytes[kSlots];
 #pragma unroll
-  for (uint32_t r = 0; r < kMfmaTiles; ++r)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) C[r][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  for (uint32_t g = g0; g < g1; ++g) {
-    uint4 xb[NT][4];
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-        xb[t][m] = reinterpret_cast<const uint4*>(Xp)[(((size_t)g * NT + t) * 4 + m) * 64 + lane];
-#pragma unroll
-    for (uint32_t r = 0; r < kMfmaTiles; ++r) {
-      const uint32_t row = min(row_base + 16 * r + i, d.out - 1);
-      const u32x2_t c = __builtin_bit_cast(
-          u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rc, g * 32 + 8 * kb, row * d.row_stride, kStream));
-      const uint32_t sraw = fetch_beta ? load_scale<SF>(rbe, g * SB, row * G * SB)
-                                       : load_scale<SF>(ra, g * SB, row * G * SB);
-      uint4 a[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        uint32_t op[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int o = 4 * m + q;
-          op[q] = (c[o >> 3] << (14 - 2 * (o & 7))) & 0xC000C000u;
-        }
-        a[m] = make_uint4(op[0], op[1], op[2], op[3]);
+    for (uint32_t q = 0; q < kSlots; ++q) {
+      const uint32_t g = min(c0 + q, G - 1);
+      const u32x2_t c2 = __builtin_bit_cast(
+          u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rc, row * d.row_stride + g * 32 + 8 * kb, 0, kCached));
+      cw[q / 2][2 * (q & 1)] = c2[0];
+      cw[q / 2][2 * (q & 1) + 1] = c2[1];
+      const uint32_t so = sbase + (row * G + g) * SB;
+      if constexpr (SF == WAL_SCALE_FP16) {
+        sraw[q] = __builtin_amdgcn_raw_buffer_load_b16(ra, so, 0, kCached);
+      } else {
+        sraw[q] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(ra, so, 0, kCached) |
+                  ((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(ra, so + 1, 0, kCached) << 8) |
+                  ((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(ra, so + 2, 0, kCached) << 16);
       }
+      if constexpr (K == 8) sbytes[q] = __builtin_amdgcn_raw_buffer_load_b16(rs, (row * G + g) * 8 + 2 * kb, 0, kCached);
+      if constexpr (K == 4) sbytes[q] = __builtin_amdgcn_raw_buffer_load_b8(rs, (row * G + g) * 4 + kb, 0, kCached);
+      if constexpr (K == 2)
+        sbytes[q] = __builtin_amdgcn_raw_buffer_load_b8(rs, (row * G + g) * 2 + (kb & 1), 0, kCached);
+    }
+    uint4 xnext[NT][4];
+    load_x(min(c0, G - 1), xnext);
+#pragma unroll
+    for (uint32_t q = 0; q < kSlots; ++q) {
+      const bool valid = q < ns;   // wave-uniform
+      uint4 xb[NT][4];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) x_operands(xnext[t], xb[t]);
+      if (q + 1 < kSlots) load_x(min(c0 + q + 1, G - 1), xnext);
+      // T operands: one 64-bit shift positions the code pairs of both dwords
+      uint4 a[4];
+      const uint64_t cq = ((uint64_t)cw[q / 2][2 * (q & 1) + 1] << 32) | cw[q / 2][2 * (q & 1)];
+      a_operands<0>(cq, a);
       f32x4_t sT[NT], sR[NT];
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
@@ -318,27 +415,24 @@ __global__ __launch_bounds__(kThreads) void k_mfma(MatDev d, const uint32_t* __r
       }
       if constexpr (K > 0) {
         // lane (i, kb) scatters sites kb * K / 4 .. of row i (K = 2: the
-        // lanes with kb < 2, one site each)
-        uint32_t sbytes;
-        if constexpr (K == 8) sbytes = __builtin_amdgcn_raw_buffer_load_b16(rs, g * 8 + 2 * kb, row * G * 8, kStream);
-        else if constexpr (K == 4) sbytes = __builtin_amdgcn_raw_buffer_load_b8(rs, g * 4 + kb, row * G * 4, kStream);
-        else sbytes = __builtin_amdgcn_raw_buffer_load_b8(rs, g * 2 + (kb & 1), row * G * 2, kStream);
+        // lanes with kb < 2, one site each) into the R tile, operand m of
+        // lane L at [m][L]
         constexpr int PER = K == 8 ? 2 : 1;
         const bool writer = K != 2 || kb < 2;
         uint32_t addr[PER];
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
-          const uint32_t sb = (sbytes >> (8 * j)) & 0xFFu;
+          const uint32_t sb = (sbytes[q] >> (8 * j)) & 0xFFu;
           const uint32_t pos = sb & 127u, local = pos & 31u, rr = local & 15u;
           const uint32_t o = 8 * (local >> 4) + (rr & 7u);
           const uint32_t lt = (pos >> 5) * 16 + i;   // lane whose operand holds column pos of row i
-          addr[j] = lt * 32 + (o >> 2) * 8 + (o & 3) * 2 + (rr >> 3);
+          addr[j] = ((o >> 2) * 64 + lt) * 8 + (o & 3) * 2 + (rr >> 3);
           if (writer) rt16[addr[j]] = (sb & 128u) ? 0xC000u : 0x4000u;
         }
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
         uint4 ro[4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) ro[m] = rt[lane * 4 + m];
+        for (int m = 0; m < 4; ++m) ro[m] = rt4[m * 64 + lane];
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 #pragma unroll
         for (int j = 0; j < PER; ++j)
@@ -351,31 +445,35 @@ __global__ __launch_bounds__(kThreads) void k_mfma(MatDev d, const uint32_t* __r
         }
       }
       // C layout: lane holds rows 4 kb + j of the tile, batch column i
+      const uint32_t sq = valid ? sraw[q] : 0u;   // a zero scale drops a slot past the range
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int src = 4 * kb + j;
-        const float al = scale_value<SF>((uint32_t)__builtin_amdgcn_ds_bpermute(4 * src, (int)sraw));
+        const float al = scale_value<SF>((uint32_t)__builtin_amdgcn_ds_bpermute(4 * src, (int)sq));
 #pragma unroll
-        for (int t = 0; t < NT; ++t) C[r][t][j] = __builtin_fmaf(al, sT[t][j], C[r][t][j]);
+        for (int t = 0; t < NT; ++t) C[t][j] = __builtin_fmaf(al, sT[t][j], C[t][j]);
         if constexpr (K > 0) {
-          const float be = scale_value<SF>((uint32_t)__builtin_amdgcn_ds_bpermute(4 * (16 + src), (int)sraw));
+          const float be = scale_value<SF>((uint32_t)__builtin_amdgcn_ds_bpermute(4 * (16 + src), (int)sq));
 #pragma unroll
-          for (int t = 0; t < NT; ++t) C[r][t][j] = __builtin_fmaf(be, sR[t][j], C[r][t][j]);
+          for (int t = 0; t < NT; ++t) C[t][j] = __builtin_fmaf(be, sR[t][j], C[t][j]);
         }
       }
     }
   }
+
+  // the tile's sum over its wavefronts, in wavefront order
+  __syncthreads();   // the R tiles are free
 #pragma unroll
-  for (uint32_t r = 0; r < kMfmaTiles; ++r)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const uint32_t n = 16 * t + i;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t row = row_base + 16 * r + 4 * kb + j;
-        if (n < d.batch && row < d.out) P[((size_t)ks * d.batch + n) * d.out + row] = 0.5f * C[r][t][j];
-      }
-    }
+  for (int t = 0; t < NT; ++t) red[(wave * NT + t) * 64 + lane] = C[t];
+  __syncthreads();
+  for (uint32_t e = threadIdx.x; e < 16 * 32; e += blockDim.x) {
+    const uint32_t r = e >> 5, n = e & 31, yr = row_base + r;
+    if (n >= d.batch || n >= 16 * NT || yr >= d.out) continue;
+    const uint32_t L = (r >> 2) * 16 + (n & 15);
+    float v = 0.f;
+    for (uint32_t w = 0; w < nw; ++w) v += red[(w * NT + (n >> 4)) * 64 + L][r & 3];
+    P[(size_t)n * d.out + yr] = 0.5f * v;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -386,80 +484,81 @@ uint32_t class_index(const MatDev& d) {
 }
 
 template <int SF, int K>
-void launch_gemv_nb(uint32_t nb, dim3 grid, hipStream_t s, const MatDev& d, float* P) {
-  if (nb == 1) hipLaunchKernelGGL((k_gemv_batch<SF, K, 1>), grid, dim3(kThreads), 0, s, d, P);
-  else if (nb == 2) hipLaunchKernelGGL((k_gemv_batch<SF, K, 2>), grid, dim3(kThreads), 0, s, d, P);
-  else hipLaunchKernelGGL((k_gemv_batch<SF, K, 4>), grid, dim3(kThreads), 0, s, d, P);
+void launch_gemv_nb(uint32_t nb, dim3 grid, hipStream_t s, const MatDev& d, float* P, float* zp, uint32_t nmain,
+                    uint32_t passes, uint32_t nrb) {
+  if (nb == 1) hipLaunchKernelGGL((k_gemv_batch<SF, K, 1>), grid, dim3(kThreads), 0, s, d, P, zp, nmain, passes, nrb);
+  else if (nb == 2)
+    hipLaunchKernelGGL((k_gemv_batch<SF, K, 2>), grid, dim3(kThreads), 0, s, d, P, zp, nmain, passes, nrb);
+  else hipLaunchKernelGGL((k_gemv_batch<SF, K, 4>), grid, dim3(kThreads), 0, s, d, P, zp, nmain, passes, nrb);
 }
 
 template <int SF, int K>
-void launch_mfma_nt(uint32_t nt, dim3 grid, hipStream_t s, const MatDev& d, const uint32_t* Xp, float* P,
-                    uint32_t ks) {
-  if (nt == 1) hipLaunchKernelGGL((k_mfma<SF, K, 1>), grid, dim3(kThreads), 0, s, d, Xp, P, ks);
-  else hipLaunchKernelGGL((k_mfma<SF, K, 2>), grid, dim3(kThreads), 0, s, d, Xp, P, ks);
+void launch_mfma_nt(uint32_t nt, dim3 grid, uint32_t nw, hipStream_t s, const MatDev& d, float* P, float* zp,
+                    uint32_t tiles, uint32_t gpw) {
+  if (nt == 1) hipLaunchKernelGGL((k_mfma<SF, K, 1>), grid, dim3(64 * nw), 0, s, d, P, zp, tiles, gpw);
+  else hipLaunchKernelGGL((k_mfma<SF, K, 2>), grid, dim3(64 * nw), 0, s, d, P, zp, tiles, gpw);
 }
 
-// z pre-pass into the workspace; points the descriptor at it.
-bool launch_z(MatDev& d, const GemmShape& S, uint8_t* ws, uint32_t batch, hipStream_t s) {
-  d.z = reinterpret_cast<float*>(ws + S.off_z);
-  if (!d.terms) return true;
-  hipLaunchKernelGGL(k_z_batch, dim3((d.terms + kZTerms - 1) / kZTerms, batch), dim3(kThreads), 0, s, d);
-  return hipGetLastError() == hipSuccess;
+int launch_reduce(const MatDev& d, const GemmShape& S, const float* zp, const float* P, uint32_t slices,
+                  hipStream_t s) {
+  if (hipGetLastError() != hipSuccess) return WAL_ERR_DEVICE;
+  hipLaunchKernelGGL(k_reduce, dim3((d.out + 255) / 256, d.batch), dim3(256), 0, s, d, zp, P, slices, S.zc);
+  return hipGetLastError() == hipSuccess ? WAL_OK : WAL_ERR_DEVICE;
 }
 
 }  // namespace
 
 namespace wal {
 
-int launch_gemm_valu(const wal_info& f, const MatDev& d0, uint32_t batch, void* ws, void* stream) {
+int launch_gemm_valu(const wal_info& f, const MatDev& d, uint32_t batch, void* ws, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const GemmShape S = gemm_shape(f, batch);
   uint8_t* w = static_cast<uint8_t*>(ws);
-  MatDev d = d0;
-  if (!launch_z(d, S, w, batch, s)) return WAL_ERR_DEVICE;
+  float* zp = reinterpret_cast<float*>(w + S.off_z);
   float* P = reinterpret_cast<float*>(w + S.off_p);
   const uint32_t nb = batch >= 3 ? kGemvCols : batch;
-  const dim3 grid(S.passes, (f.d.out + kWaves * kGemvRows - 1) / (kWaves * kGemvRows), (batch + nb - 1) / nb);
+  const uint32_t nrb = (f.d.out + kWaves * kGemvRows - 1) / (kWaves * kGemvRows);
+  const uint32_t nmain = S.passes * nrb * ((batch + nb - 1) / nb);
+  const dim3 grid(nmain + z_blocks(d, S));
   switch (class_index(d)) {
-    case 0: launch_gemv_nb<WAL_SCALE_FP16, 0>(nb, grid, s, d, P); break;
-    case 1: launch_gemv_nb<WAL_SCALE_FP16, 2>(nb, grid, s, d, P); break;
-    case 2: launch_gemv_nb<WAL_SCALE_FP16, 4>(nb, grid, s, d, P); break;
-    case 3: launch_gemv_nb<WAL_SCALE_FP16, 8>(nb, grid, s, d, P); break;
-    case 4: launch_gemv_nb<WAL_SCALE_FP24, 0>(nb, grid, s, d, P); break;
-    case 5: launch_gemv_nb<WAL_SCALE_FP24, 2>(nb, grid, s, d, P); break;
-    case 6: launch_gemv_nb<WAL_SCALE_FP24, 4>(nb, grid, s, d, P); break;
-    default: launch_gemv_nb<WAL_SCALE_FP24, 8>(nb, grid, s, d, P); break;
+    case 0: launch_gemv_nb<WAL_SCALE_FP16, 0>(nb, grid, s, d, P, zp, nmain, S.passes, nrb); break;
+    case 1: launch_gemv_nb<WAL_SCALE_FP16, 2>(nb, grid, s, d, P, zp, nmain, S.passes, nrb); break;
+    case 2: launch_gemv_nb<WAL_SCALE_FP16, 4>(nb, grid, s, d, P, zp, nmain, S.passes, nrb); break;
+    case 3: launch_gemv_nb<WAL_SCALE_FP16, 8>(nb, grid, s, d, P, zp, nmain, S.passes, nrb); break;
+    case 4: launch_gemv_nb<WAL_SCALE_FP24, 0>(nb, grid, s, d, P, zp, nmain, S.passes, nrb); break;
+    case 5: launch_gemv_nb<WAL_SCALE_FP24, 2>(nb, grid, s, d, P, zp, nmain, S.passes, nrb); break;
+    case 6: launch_gemv_nb<WAL_SCALE_FP24, 4>(nb, grid, s, d, P, zp, nmain, S.passes, nrb); break;
+    default: launch_gemv_nb<WAL_SCALE_FP24, 8>(nb, grid, s, d, P, zp, nmain, S.passes, nrb); break;
   }
-  if (hipGetLastError() != hipSuccess) return WAL_ERR_DEVICE;
-  hipLaunchKernelGGL(k_partial_reduce, dim3((f.d.out + 255) / 256, batch), dim3(256), 0, s, d, P, S.passes);
-  return hipGetLastError() == hipSuccess ? WAL_OK : WAL_ERR_DEVICE;
+  return launch_reduce(d, S, zp, P, S.passes, s);
 }
 
-int launch_gemm_mfma(const wal_info& f, const MatDev& d0, uint32_t batch, void* ws, void* stream) {
+int launch_gemm_mfma(const wal_info& f, const MatDev& d, uint32_t batch, void* ws, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const GemmShape S = gemm_shape(f, batch);
   uint8_t* w = static_cast<uint8_t*>(ws);
-  MatDev d = d0;
-  if (!launch_z(d, S, w, batch, s)) return WAL_ERR_DEVICE;
-  uint32_t* Xp = reinterpret_cast<uint32_t*>(w + S.off_xp);
+  float* zp = reinterpret_cast<float*>(w + S.off_z);
   float* P = reinterpret_cast<float*>(w + S.off_p);
-  const uint32_t nx = f.groups * S.nt * 4 * 64;
-  hipLaunchKernelGGL(k_xperm, dim3((nx + 255) / 256), dim3(256), 0, s, d, S.nt, Xp);
-  if (hipGetLastError() != hipSuccess) return WAL_ERR_DEVICE;
-  const dim3 grid((S.row_blocks * S.ks + kWaves - 1) / kWaves);
+  const uint32_t nt = (batch + 15) / 16;
+  const uint32_t maxw = nt == 1 ? mfma_max_waves<1>() : mfma_max_waves<2>();
+  // groups per wavefront: a multiple of the sweep's slots, as few
+  // wavefronts as that allows
+  uint32_t gpw = (f.groups + maxw - 1) / maxw;
+  gpw = (gpw + kSlots - 1) / kSlots * kSlots;
+  const uint32_t nw = (f.groups + gpw - 1) / gpw;
+  const uint32_t tiles = (f.d.out + 15) / 16;
+  const dim3 grid(tiles + z_blocks(d, S));
   switch (class_index(d)) {
-    case 0: launch_mfma_nt<WAL_SCALE_FP16, 0>(S.nt, grid, s, d, Xp, P, S.ks); break;
-    case 1: launch_mfma_nt<WAL_SCALE_FP16, 2>(S.nt, grid, s, d, Xp, P, S.ks); break;
-    case 2: launch_mfma_nt<WAL_SCALE_FP16, 4>(S.nt, grid, s, d, Xp, P, S.ks); break;
-    case 3: launch_mfma_nt<WAL_SCALE_FP16, 8>(S.nt, grid, s, d, Xp, P, S.ks); break;
-    case 4: launch_mfma_nt<WAL_SCALE_FP24, 0>(S.nt, grid, s, d, Xp, P, S.ks); break;
-    case 5: launch_mfma_nt<WAL_SCALE_FP24, 2>(S.nt, grid, s, d, Xp, P, S.ks); break;
-    case 6: launch_mfma_nt<WAL_SCALE_FP24, 4>(S.nt, grid, s, d, Xp, P, S.ks); break;
-    default: launch_mfma_nt<WAL_SCALE_FP24, 8>(S.nt, grid, s, d, Xp, P, S.ks); break;
+    case 0: launch_mfma_nt<WAL_SCALE_FP16, 0>(nt, grid, nw, s, d, P, zp, tiles, gpw); break;
+    case 1: launch_mfma_nt<WAL_SCALE_FP16, 2>(nt, grid, nw, s, d, P, zp, tiles, gpw); break;
+    case 2: launch_mfma_nt<WAL_SCALE_FP16, 4>(nt, grid, nw, s, d, P, zp, tiles, gpw); break;
+    case 3: launch_mfma_nt<WAL_SCALE_FP16, 8>(nt, grid, nw, s, d, P, zp, tiles, gpw); break;
+    case 4: launch_mfma_nt<WAL_SCALE_FP24, 0>(nt, grid, nw, s, d, P, zp, tiles, gpw); break;
+    case 5: launch_mfma_nt<WAL_SCALE_FP24, 2>(nt, grid, nw, s, d, P, zp, tiles, gpw); break;
+    case 6: launch_mfma_nt<WAL_SCALE_FP24, 4>(nt, grid, nw, s, d, P, zp, tiles, gpw); break;
+    default: launch_mfma_nt<WAL_SCALE_FP24, 8>(nt, grid, nw, s, d, P, zp, tiles, gpw); break;
   }
-  if (hipGetLastError() != hipSuccess) return WAL_ERR_DEVICE;
-  hipLaunchKernelGGL(k_partial_reduce, dim3((f.d.out + 255) / 256, batch), dim3(256), 0, s, d, P, S.ks);
-  return hipGetLastError() == hipSuccess ? WAL_OK : WAL_ERR_DEVICE;
+  return launch_reduce(d, S, zp, P, 1, s);
 }
 
 }  // namespace wal

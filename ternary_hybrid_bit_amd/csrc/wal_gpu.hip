@@ -448,7 +448,7 @@ int launch_status() {
 constexpr int kRB = 4;   // rows per batch of the 2-bit streaming kernels
 // Batch from which WAL_GEMM_AUTO takes the MFMA kernel (measured on MI355X
 // on the 4096 x 12288 shape).
-constexpr uint32_t kGemmCrossover = 8;
+constexpr uint32_t kGemmCrossover = 5;
 constexpr uint32_t kClasses = 16;   // kernel classes (see class_of)
 
 // Kernel class of a matrix: 8 * trit_fmt + 4 * scale_fmt + index of k in {0, 2, 4, 8}.
@@ -639,7 +639,7 @@ int wal_gemm_small(const wal_info* info, const void* W_dev, const void* X_dev, i
     if (!batched) return WAL_ERR_UNSUPPORTED;
     return launch_gemm_mfma(*info, d, batch, ws_dev, stream);
   }
-  if (batched && batch > 1) return launch_gemm_valu(*info, d, batch, ws_dev, stream);
+  if (batched) return launch_gemm_valu(*info, d, batch, ws_dev, stream);
   for (uint32_t n = 0; n < batch; ++n) {
     const void* xn = static_cast<const uint8_t*>(X_dev) + (size_t)n * ldx * xe;
     if ((st = wal_gemv(info, W_dev, xn, x_dtype, Y_dev + (size_t)n * ldy, stream))) return st;

@@ -449,15 +449,11 @@ GemmShape gemm_shape(const wal_info& f, uint32_t batch) {
   GemmShape S;
   const uint64_t terms = (uint64_t)f.d.n_paths * f.d.rank;
   S.nt = (batch + 15) / 16;
-  S.row_blocks = (f.d.out + kMfmaRows - 1) / kMfmaRows;
-  uint32_t ks = (kMfmaWaves + S.row_blocks - 1) / S.row_blocks;
-  S.ks = ks > f.groups ? f.groups : ks < 1 ? 1 : ks;
   S.passes = (f.d.in + kPass2bit - 1) / kPass2bit;
-  S.slices = S.ks > S.passes ? S.ks : S.passes;
+  S.zc = (f.d.in + kZChunkCols - 1) / kZChunkCols;
   S.off_z = 0;
-  S.off_xp = up(4 * terms * batch, 256);
-  S.off_p = S.off_xp + up((uint64_t)f.groups * S.nt * 4 * 64 * 16, 256);
-  S.bytes = S.off_p + up(4ull * S.slices * batch * f.d.out, 256);
+  S.off_p = up(4 * terms * batch * S.zc, 256);
+  S.bytes = S.off_p + up(4ull * S.passes * batch * f.d.out, 256);
   return S;
 }
 

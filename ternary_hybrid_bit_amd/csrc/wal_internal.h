@@ -62,24 +62,23 @@ struct Seg;
 using GroupedFn = void (*)(const MatDev*, const uint32_t*, const Seg*);
 using SingleFn = void (*)(MatDev, uint32_t);
 
-// Small-batch products (wal_gemm.hip).  Both kernels write per-K-slice
-// partial sums P[slice][n][row] to the workspace; a last kernel adds the
-// slices in order and the low-rank term.
-//  * batched GEMV (vector ALUs): a wavefront takes kGemvRows rows of one
-//    4096-column pass and up to kGemvCols activation columns, every decoded
-//    trit feeding all of them; slices = passes.
-//  * MFMA: a wavefront takes kMfmaTiles row tiles of 16 rows over a range of
-//    groups; slices = K splits.
+// Small-batch products (wal_gemm.hip).
+//  * batched GEMV (vector ALUs), two launches: the first writes per-pass
+//    partial sums P[pass][n][row] to the workspace (a wavefront takes
+//    kGemvRows rows of one 4096-column pass for up to kGemvCols activation
+//    columns, every decoded trit feeding all of them), and extra workgroups
+//    of the same launch the low-rank reductions of every batch column per
+//    4096-column chunk, zpart[chunk][n][term]; the second adds the passes and
+//    the chunks in a fixed order, adds the low-rank term and stores Y.
+//  * MFMA, one launch: a workgroup takes a 16-row tile over all columns and
+//    finishes its Y in LDS (no workspace).
 constexpr uint32_t kGemvRows = 8;
 constexpr uint32_t kGemvCols = 4;
-constexpr uint32_t kMfmaTiles = 4;
-constexpr uint32_t kMfmaRows = 16 * kMfmaTiles;
-constexpr uint32_t kMfmaWaves = 1024;   // K splits are chosen to reach about this many wavefronts
-// Workspace of a small-batch product: z[batch][terms] | X in operand order
-// (MFMA) | partial sums P[slices][batch][out].
+constexpr uint32_t kZChunkCols = 4096;   // columns per low-rank partial
+constexpr uint32_t kZTermsPerBlock = 16;
 struct GemmShape {
-  uint32_t nt, row_blocks, ks, passes, slices;
-  uint64_t off_z, off_xp, off_p, bytes;
+  uint32_t nt, passes, zc;   // n-tiles, GEMV passes (= P planes), z chunks
+  uint64_t off_z, off_p, bytes;
 };
 GemmShape gemm_shape(const wal_info& f, uint32_t batch);
 // Launchers (stream as hipStream_t); WAL_OK or WAL_ERR_DEVICE.

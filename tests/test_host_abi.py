@@ -195,23 +195,18 @@ def test_inspect_reads_header():
 
 
 def test_workspace_size():
-    """z [batch][terms] | X in MFMA operand order | partial sums
-    [slices][batch][out], each padded to 256 bytes; slices = the larger of the
-    MFMA K splits (enough for about 1024 wavefronts of 64 rows) and the
-    4096-column passes."""
+    """Low-rank partials z [chunk][batch][terms] (one chunk per 4096 columns)
+    | per-pass partial sums [passes][batch][out] of the batched GEMV, each
+    padded to 256 bytes."""
     def up(v):
         return (v + 255) // 256 * 256
 
     def expect(out, inp, terms, B):
-        groups = inp // 128
-        nt = (B + 15) // 16
-        row_blocks = (out + 63) // 64
-        ks = max(1, min(groups, (1024 + row_blocks - 1) // row_blocks))
-        slices = max(ks, (inp + 4095) // 4096)
-        return up(4 * terms * B) + up(groups * nt * 4 * 64 * 16) + up(4 * slices * B * out)
+        passes = (inp + 4095) // 4096
+        return up(4 * terms * B * passes) + up(4 * passes * B * out)
 
     info = wal.wal_packed_size(wal.make_desc(12288, 4096, 8, 1, 16))
-    assert wal.wal_workspace_size(info, 1) == expect(12288, 4096, 16, 1) == 256 + 131072 + 294912
+    assert wal.wal_workspace_size(info, 1) == expect(12288, 4096, 16, 1) == 256 + 49152
     assert wal.wal_workspace_size(info, 32) == expect(12288, 4096, 16, 32)
     info = wal.wal_packed_size(wal.make_desc(4096, 12288, 8, 1, 16))
     for B in (1, 4, 16, 17, 32):
