@@ -15,6 +15,16 @@ After idle the GPU runs the first ~100 steps up to 30 % slower while its
 power management raises the clocks, so before the W warmup steps the step is
 repeated, untimed, for --settle-s seconds (default 1 s).
 
+``--workload config1|config3|config4`` instead measures the single-matrix
+configurations (one JSON line each, no contract fields): config 1 is the
+12288x4096 gate shape through wal_gemv, config 3 the 4096x12288 down shape
+through wal_gemm_small with both kernels at batch 1, 2, 4, 5, 8, 16 and 32
+(and the batch from which the matrix-core kernel is faster), config 4 the two
+base-3 / fp24 27B shapes through wal_gemv.  Each call reads one of about
+1 GB of distinct packed copies in turn, so the 256 MB Infinity Cache cannot
+serve the weights; x stays fixed.  The line also carries a measured
+read-only streaming rate (torch.sum over 2 GiB) as the achievable bandwidth.
+
 Prints one JSON line with the contract's fields plus ``roofline`` (the
 streaming kernel's average duration from HIP events recorded around it on
 its stream in every timed step, algorithmic packed bytes per launch, against
@@ -93,6 +103,157 @@ def cpu_baseline(items, budget_s: float):
                       f"{t_total:.1f} s: numpy unpack + dense float64 W + W@x per matrix"}
 
 
+def achievable_read_gbs(torch, dev) -> float:
+    """Read-only streaming rate of this GPU: torch.sum over 2 GiB of fp32."""
+    a = torch.ones(1 << 29, dtype=torch.float32, device=dev)
+    for _ in range(5):
+        a.sum()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(20):
+        a.sum()
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 20 * a.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a
+    return round(gbs, 1)
+
+
+def rotating_copies(torch, dev, blob, total_bytes=1 << 30):
+    """About total_bytes of distinct device copies of one packed blob (each
+    256-byte aligned): views into one arena."""
+    stride = (blob.size + 255) // 256 * 256
+    n = max(2, -(-total_bytes // stride))
+    arena = torch.empty(n * stride, dtype=torch.uint8, device=dev)
+    first = torch.from_numpy(blob).to(dev)
+    for i in range(n):
+        arena[i * stride:i * stride + blob.size].copy_(first)
+    torch.cuda.synchronize()
+    return [arena[i * stride:i * stride + blob.size] for i in range(n)], arena
+
+
+def time_calls(torch, fn, calls: int, settle_s: float = 0.3) -> float:
+    """Microseconds per call of fn(i) (i = call index), after settle_s seconds
+    of untimed calls; HIP events around the timed calls on the current stream."""
+    t0, i = time.perf_counter(), 0
+    while time.perf_counter() - t0 < settle_s:
+        for _ in range(50):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for k in range(calls):
+        fn(i + k)
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / calls
+
+
+def oracle_time(blob, X):
+    """Seconds of the oracle for one matrix: unpack + dense float64 W + X W^T,
+    and of the product alone with W built."""
+    from oracle import dense as D
+    from oracle import format as F
+    t0 = time.perf_counter()
+    W = D.dense_W(F.unpack(blob))
+    Xd = np.asarray(X, dtype=np.float64)
+    t1 = time.perf_counter()
+    Xd @ W.T
+    t2 = time.perf_counter()
+    return t2 - t0, t2 - t1
+
+
+def host_info():
+    try:
+        from threadpoolctl import threadpool_info
+        pools = [{"api": p.get("internal_api"), "threads": p.get("num_threads")} for p in threadpool_info()]
+    except Exception:  # noqa: BLE001
+        pools = []
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:
+        aff = None
+    return {"cpu_count": os.cpu_count(), "affinity": aff, "blas": pools}
+
+
+def run_single(args):
+    """Single-matrix configurations (see the module docstring)."""
+    import torch
+    import synth
+    import ternary_hybrid_bit_amd as wal
+    dev = torch.device("cuda:0")
+    read_gbs = achievable_read_gbs(torch, dev)
+    calls = max(args.steps, 50)
+
+    def to_x(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    if args.workload in ("config1", "config4"):
+        cfg = 1 if args.workload == "config1" else 4
+        mids = [0] if cfg == 1 else [0, 1]
+        res = []
+        for mid in mids:
+            m = synth.config_matrix(cfg, mid)
+            blob, info = wal.pack_matrix(m)
+            x, bits = synth.config_x(cfg, mid)
+            Ws, keep = rotating_copies(torch, dev, blob)
+            xt = to_x(bits[0])
+            y = torch.empty(info.d.out, dtype=torch.float32, device=dev)
+            ws = torch.empty(max(wal.wal_workspace_size(info, 1), 4) // 4, dtype=torch.float32, device=dev)
+            us = time_calls(torch, lambda i: wal.wal_gemv(info, Ws[i % len(Ws)], xt, y, ws), calls)
+            gbs = info.algorithmic_bytes / (us * 1e-6) / 1e9
+            t_all, t_mm = oracle_time(blob, x[:1])
+            res.append({"shape": [int(info.d.out), int(info.d.in_)], "k": int(info.d.k),
+                        "format": "base-3 / fp24" if info.d.trit_fmt else "2-bit / fp16",
+                        "packed_bytes": int(info.algorithmic_bytes), "copies": len(Ws), "us_per_call": round(us, 3),
+                        "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                        "achievable_frac": round(gbs / read_gbs, 4),
+                        "weights_per_s": round(info.d.out * info.d.in_ / (us * 1e-6), 1),
+                        "oracle_s": round(t_all, 3), "oracle_matmul_s": round(t_mm, 4)})
+            del Ws, keep
+        out = {"workload": args.workload, "entry": "wal_gemv", "x_dtype": "bf16", "data": "synthetic",
+               "calls": calls, "achievable_read_gbs": read_gbs, "results": res, "host": host_info()}
+        print(json.dumps(out), flush=True)
+        return
+
+    # config 3: both kernels at every batch
+    m = synth.config_matrix(3)
+    blob, info = wal.pack_matrix(m)
+    x, bits = synth.config_x(3, batch=32)
+    Ws, keep = rotating_copies(torch, dev, blob)
+    X = to_x(bits)
+    Y = torch.empty((32, info.d.out), dtype=torch.float32, device=dev)
+    ws = torch.empty(wal.wal_workspace_size(info, 32) // 4 + 64, dtype=torch.float32, device=dev)
+    rows = []
+    for B in (1, 2, 4, 5, 8, 16, 32):
+        row = {"batch": B}
+        for name, mode in (("valu", wal.WAL_GEMM_VALU), ("mfma", wal.WAL_GEMM_MFMA)):
+            us = time_calls(torch, lambda i: wal.wal_gemm_small(info, Ws[i % len(Ws)], X[:B], Y[:B], mode, ws),
+                            calls)
+            gbs = info.algorithmic_bytes / (us * 1e-6) / 1e9
+            row[name] = {"us_per_call": round(us, 3), "GB/s": round(gbs, 1),
+                         "weight_macs_per_s": round(info.d.out * info.d.in_ * B / (us * 1e-6), 1)}
+        # dense-equivalent matrix-core use: 2 out in B flops of one bf16 GEMM
+        row["mfma"]["dense_equiv_frac_of_2.5PF"] = round(
+            2 * info.d.out * info.d.in_ * B / (row["mfma"]["us_per_call"] * 1e-6) / 2.5e15, 5)
+        row["faster"] = "mfma" if row["mfma"]["us_per_call"] < row["valu"]["us_per_call"] else "valu"
+        rows.append(row)
+        print(f"[bench] config 3 B={B}: valu {row['valu']['us_per_call']} us, mfma {row['mfma']['us_per_call']} us",
+              file=sys.stderr, flush=True)
+    cross = next((r["batch"] for r in rows if r["faster"] == "mfma" and
+                  all(q["faster"] == "mfma" for q in rows if q["batch"] >= r["batch"])), None)
+    t_all, t_mm = oracle_time(blob, x)
+    out = {"workload": "config3", "entry": "wal_gemm_small", "shape": [int(info.d.out), int(info.d.in_)],
+           "x_dtype": "bf16", "data": "synthetic", "packed_bytes": int(info.algorithmic_bytes),
+           "copies": len(Ws), "calls": calls, "achievable_read_gbs": read_gbs, "results": rows,
+           "crossover_batch": cross, "oracle_batch32_s": round(t_all, 3), "oracle_matmul_batch32_s": round(t_mm, 4),
+           "host": host_info()}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -104,11 +265,15 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after timing, run one fp32 elementwise copy of this many MiB (counter calibration)")
+    ap.add_argument("--workload", default="sweep", choices=("sweep", "config1", "config3", "config4"))
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the sweep is timed on a single MI355X).", file=sys.stderr)
         sys.exit(2)
+    if args.workload != "sweep":
+        run_single(args)
+        return
 
     import torch
     import ternary_hybrid_bit_amd as wal

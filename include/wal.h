@@ -182,23 +182,25 @@ int wal_unpack(const void* blob, size_t bytes, int8_t* T, uint8_t* site_pos,
                int8_t* site_sign, float* alpha, float* beta, int8_t* U,
                int8_t* V, float* s);
 
-/* Device workspace that wal_gemm_small needs for a blob and batch (the
- * batched-GEMV kernel's): the per-path reductions z_p = diag(s_p) V_p^T X per
- * 4096-column chunk [chunks][batch][n_paths * rank] and the per-pass partial
- * sums [passes][batch][out] (fp32), each part padded to 256 bytes.
- * Errors: ARG, SHAPE, FORMAT. */
+/* Device workspace that wal_gemv and wal_gemm_small need for a blob and
+ * batch: the per-path reductions z_p = diag(s_p) V_p^T X per 4096-column
+ * chunk [chunks][batch][n_paths * rank] and the batched GEMV's per-pass
+ * partial sums [passes][batch][out] (fp32), each part padded to 256 bytes.
+ * wal_gemv uses the first part only.  Errors: ARG, SHAPE, FORMAT. */
 int wal_workspace_size(const wal_info* info, uint32_t batch, size_t* bytes);
 
 /* y = W(x) for one matrix, batch 1 (WAL-Ternary-8B cards, "Representation":
- * the ternary-hybrid product with its binary low-rank paths).  One kernel
- * launch; no workspace (each workgroup computes the low-rank reductions).
+ * the ternary-hybrid product with its binary low-rank paths): a low-rank
+ * pre-pass (when the blob has paths) and one streaming launch.
  *   info   host view of the blob (from wal_inspect / wal_pack)
  *   W_dev  the blob in device memory, 256-byte aligned
  *   x_dev  [in] activations, fp32 or bf16 (x_dtype), 16-byte aligned
  *   y_dev  [out] fp32 output, 4-byte aligned, overwritten
- * Errors: ARG, SHAPE, ALIGN, UNSUPPORTED, DEVICE. */
+ *   ws_dev workspace of wal_workspace_size(info, 1) bytes, 16-byte aligned,
+ *          disjoint from x and y (may be NULL for a blob without paths)
+ * Errors: ARG, SHAPE, ALIGN, BUFFER, UNSUPPORTED, DEVICE. */
 int wal_gemv(const wal_info* info, const void* W_dev, const void* x_dev, int x_dtype,
-             float* y_dev, void* stream);
+             float* y_dev, void* ws_dev, size_t ws_bytes, void* stream);
 
 /* Y = X W^T for a small batch (F.linear convention): row n of Y is W(x_n)
  * with x_n row n of X (WAL-Ternary-8B cards, "Representation").

@@ -82,7 +82,7 @@ _sig = {
     "wal_verify": (_I, [_P, _SZ]),
     "wal_unpack": (_I, [_P, _SZ, _P, _P, _P, _P, _P, _P, _P, _P]),
     "wal_workspace_size": (_I, [ctypes.POINTER(wal_info), _U32, ctypes.POINTER(_SZ)]),
-    "wal_gemv": (_I, [ctypes.POINTER(wal_info), _P, _P, _I, _P, _P]),
+    "wal_gemv": (_I, [ctypes.POINTER(wal_info), _P, _P, _I, _P, _P, _SZ, _P]),
     "wal_gemm_small": (_I, [ctypes.POINTER(wal_info), _P, _P, _I, _U32, _U32, _P, _U32, _I, _P, _SZ, _P]),
     "wal_grouped_plan_size": (_I, [_U32, _P, _U32, _I, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)]),
     "wal_grouped_plan": (_I, [_U32, _P, _P, _P, _I, _P, _P, _SZ, _U32, _P, _SZ,
@@ -194,11 +194,14 @@ def wal_workspace_size(info: wal_info, batch: int = 1) -> int:
     return n.value
 
 
-def wal_gemv(info: wal_info, W, x, y, stream=None):
-    """y = W(x) on the GPU; W, x, y are device tensors; y is fp32 [out]."""
+def wal_gemv(info: wal_info, W, x, y, ws=None, stream=None):
+    """y = W(x) on the GPU; W, x, y (and ws, see wal_workspace_size) are device
+    tensors; y is fp32 [out]."""
     import torch
     xdt = WAL_X_BF16 if x.dtype == torch.bfloat16 else WAL_X_F32
-    _check(_lib.wal_gemv(ctypes.byref(info), _ptr(W), _ptr(x), xdt, _ptr(y), _stream(stream)), "wal_gemv")
+    wsb = ws.numel() * ws.element_size() if ws is not None else 0
+    st = _lib.wal_gemv(ctypes.byref(info), _ptr(W), _ptr(x), xdt, _ptr(y), _ptr(ws), wsb, _stream(stream))
+    _check(st, "wal_gemv")
     return y
 
 

@@ -187,7 +187,7 @@ __device__ __forceinline__ void build_table3(const void* x, uint32_t col0, uint3
 
 template <int SF, int K>
 __device__ __forceinline__ void stream_rows_base3(const MatDev& d, uint32_t row0, uint32_t row1, uint32_t pass,
-                                                  uint32_t npass, bool zin, Smem3& sm) {
+                                                  uint32_t npass, Smem3& sm) {
   constexpr int RB = kRB3;
   constexpr int LOG = ilog2(RB);
   constexpr int SH = 6 - LOG;
@@ -339,8 +339,12 @@ __device__ __forceinline__ void stream_rows_base3(const MatDev& d, uint32_t row0
   xl.load(d.x, pass * kPassBase3 + 80 * lane, ncols);
 
   __syncthreads();   // readers of the previous table and z are done
-  if (!zin && pass == 0)
-    for (uint32_t t = threadIdx.x; t < d.terms; t += kThreads) sm.z[t] = d.z[t];
+  if (pass == 0)
+    for (uint32_t t = threadIdx.x; t < d.terms; t += kThreads) {
+      float z = 0.f;
+      for (uint32_t cc = 0; cc < d.zc; ++cc) z += d.z[cc * d.terms + t];
+      sm.z[t] = z;
+    }
   if constexpr (K > 0) build_table3(d.x, pass * kPassBase3, pw, sm.tbl);
   __syncthreads();
   if (!has_rows) return;
@@ -365,13 +369,10 @@ __device__ __forceinline__ void build_lut(uint32_t* lut) {
   for (uint32_t i = threadIdx.x; i < 256 * kLutCopies; i += kThreads) lut[i] = base3_entry(i / kLutCopies);
 }
 
-// ZIN: the workgroup computes the low-rank reductions itself (single
-// products); otherwise a pre-pass left them in d.z.
-template <int SF, int K, bool ZIN>
+template <int SF, int K>
 __device__ __forceinline__ void run_segment_base3(const MatDev& d, uint32_t row0, uint32_t row1, Smem3& sm) {
   const uint32_t npass = (d.in + kPassBase3 - 1) / kPassBase3;
-  if (ZIN && d.terms) z_all<WAL_X_BF16>(d, sm.z);
-  for (uint32_t pass = 0; pass < npass; ++pass) stream_rows_base3<SF, K>(d, row0, row1, pass, npass, ZIN, sm);
+  for (uint32_t pass = 0; pass < npass; ++pass) stream_rows_base3<SF, K>(d, row0, row1, pass, npass, sm);
   __syncthreads();
   const uint32_t nrows = row1 - row0;
   for (uint32_t i = threadIdx.x; i < nrows; i += kThreads) d.y[row0 + i] = sm.ybuf[i];
@@ -386,7 +387,7 @@ __global__ __launch_bounds__(kThreads) void k_stream3_grouped(const MatDev* __re
   const uint32_t s0 = blockseg[blockIdx.x], s1 = blockseg[blockIdx.x + 1];
   for (uint32_t s = s0; s < s1; ++s) {
     const Seg sg = segs[s];
-    run_segment_base3<SF, K, false>(descs[sg.mat], sg.row0, sg.row1, sm);
+    run_segment_base3<SF, K>(descs[sg.mat], sg.row0, sg.row1, sm);
   }
 }
 
@@ -396,7 +397,7 @@ __global__ __launch_bounds__(kThreads) void k_stream3_single(MatDev d, uint32_t 
   build_lut(sm.lut);
   const uint32_t r0 = blockIdx.x * rows_per_block;
   const uint32_t r1 = min(d.out, r0 + rows_per_block);
-  if (r0 < r1) run_segment_base3<SF, K, true>(d, r0, r1, sm);
+  if (r0 < r1) run_segment_base3<SF, K>(d, r0, r1, sm);
 }
 
 }  // namespace

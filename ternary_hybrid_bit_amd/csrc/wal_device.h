@@ -225,14 +225,4 @@ __device__ __forceinline__ void zjob(const MatDev& d, uint32_t t0) {
   z_chunk<XT, (int)kZTerms>(d, d.x, t0, d.z, 0, d.in);
 }
 
-// Every low-rank term of one matrix into out (LDS), visible to the whole
-// workgroup on return.  Every thread calls it.
-constexpr int kZChunk = 16;
-template <int XT>
-__device__ __forceinline__ void z_all(const MatDev& d, float* out) {
-  for (uint32_t t0 = 0; t0 < d.terms; t0 += kZChunk) {
-    z_chunk<XT, kZChunk>(d, d.x, t0, out, 0, d.in);
-    __syncthreads();   // out is complete and red free for the next chunk
-  }
-}
 }  // namespace

@@ -5,11 +5,11 @@
 // computed straight from the packed planes described in include/wal.h.
 //
 // Kernels:
-//  * the binary low-rank reductions z_p[r] = s_p[r] * sum_j (-1)^{V bit} x_j:
-//    for grouped products a pre-pass (k_z_grouped, kZTerms terms per
-//    workgroup) writes them to the caller's workspace; a single product
-//    (wal_gemv) computes them inside each streaming workgroup at the start of
-//    its rows, so it is one launch and needs no workspace.
+//  * the binary low-rank reductions z_p[r] = s_p[r] * sum_j (-1)^{V bit} x_j,
+//    a pre-pass into the caller's workspace: kZTerms terms per workgroup for
+//    grouped products (k_z_grouped), 16 terms x 4096 columns per workgroup
+//    for a single product (k_z_chunks, partial sums that the streaming
+//    kernel adds), so that wide matrices get enough workgroups.
 //  * k_stream_*: one streaming pass over the packed planes.  Every workgroup
 //    owns a contiguous range of rows of one or more matrices (for grouped
 //    products the host splits the total packed bytes evenly over a grid that
@@ -199,7 +199,7 @@ struct Lane2 {
 // low-rank terms, behind barriers) runs after each wave has issued the loads
 // of its first batch and of its x columns, so the set-up overlaps the
 // memory latency instead of adding to it.  Every wave reaches both barriers.
-template <int XT, int SF, int K, int RB, bool ZIN>
+template <int XT, int SF, int K, int RB>
 __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0, uint32_t row1, uint32_t pass,
                                                  uint32_t npass, StreamSmem& sm) {
   constexpr int LOG = ilog2(RB);
@@ -329,8 +329,12 @@ __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0,
   xl.load(d.x, pass * kPass2bit + 64 * lane, (uint32_t)(64 * lane) < pw);
 
   __syncthreads();   // readers of the previous table and z are done
-  if (!ZIN && pass == 0)
-    for (uint32_t t = threadIdx.x; t < d.terms; t += kThreads) sm.z[t] = d.z[t];
+  if (pass == 0)
+    for (uint32_t t = threadIdx.x; t < d.terms; t += kThreads) {
+      float z = 0.f;
+      for (uint32_t cc = 0; cc < d.zc; ++cc) z += d.z[cc * d.terms + t];
+      sm.z[t] = z;
+    }
   if constexpr (K > 0) build_table<XT>(d.x, pass * kPass2bit, pw, sm.tbl);
   __syncthreads();
   if (!has_rows) return;
@@ -351,15 +355,10 @@ __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0,
 // SF and K are the matrix's scale format and sites per group: every
 // (scale format, k) class has kernels of its own, so the registers of the
 // hot fp16 / k = 8 loop are not set by the heavier fp24 loads.
-// ZIN: the workgroup computes the matrix's low-rank reductions itself (at the
-// start, before any row load, which keeps their registers apart from the
-// streaming loop's); otherwise a pre-pass left them in d.z.
-template <int XT, int SF, int K, int RB, bool ZIN>
+template <int XT, int SF, int K, int RB>
 __device__ __forceinline__ void run_segment_2bit(const MatDev& d, uint32_t row0, uint32_t row1, StreamSmem& sm) {
   const uint32_t npass = (d.in + kPass2bit - 1) / kPass2bit;
-  if (ZIN && d.terms) z_all<XT>(d, sm.z);
-  for (uint32_t pass = 0; pass < npass; ++pass)
-    stream_rows_2bit<XT, SF, K, RB, ZIN>(d, row0, row1, pass, npass, sm);
+  for (uint32_t pass = 0; pass < npass; ++pass) stream_rows_2bit<XT, SF, K, RB>(d, row0, row1, pass, npass, sm);
   // y leaves through LDS: one coalesced write of the segment's rows instead
   // of a few scattered bytes per batch of rows.
   __syncthreads();
@@ -382,7 +381,7 @@ void k_stream_grouped(const MatDev* __restrict__ descs, const uint32_t* __restri
   const uint32_t s0 = blockseg[blockIdx.x], s1 = blockseg[blockIdx.x + 1];
   for (uint32_t s = s0; s < s1; ++s) {
     const Seg sg = segs[s];
-    run_segment_2bit<XT, SF, K, RB, false>(descs[sg.mat], sg.row0, sg.row1, sm);
+    run_segment_2bit<XT, SF, K, RB>(descs[sg.mat], sg.row0, sg.row1, sm);
   }
 }
 
@@ -392,7 +391,18 @@ void k_stream_single(MatDev d, uint32_t rows_per_block) {
   __shared__ StreamSmem sm;
   const uint32_t r0 = blockIdx.x * rows_per_block;
   const uint32_t r1 = min(d.out, r0 + rows_per_block);
-  if (r0 < r1) run_segment_2bit<XT, SF, K, RB, true>(d, r0, r1, sm);
+  if (r0 < r1) run_segment_2bit<XT, SF, K, RB>(d, r0, r1, sm);
+}
+
+// Low-rank partials of a single product: block (tc, cc) computes terms
+// 16 tc .. 16 tc + 15 over columns [4096 cc, 4096 cc + 4096) into
+// d.z[cc][t].
+template <int XT>
+__global__ __launch_bounds__(kThreads) void k_z_chunks(MatDev d) {
+  const uint32_t tcs = (d.terms + 15) / 16;
+  const uint32_t tc = blockIdx.x % tcs, cc = blockIdx.x / tcs;
+  const uint32_t c0 = cc * kZChunkCols, c1 = min(d.in, c0 + kZChunkCols);
+  z_chunk<XT, 16>(d, d.x, tc * 16, d.z + (size_t)cc * d.terms, c0, c1);
 }
 
 template <int XT>
@@ -437,6 +447,7 @@ MatDev make_dev(const wal_info* f, const void* W, const void* x, float* y, float
   m.terms = f->d.n_paths * f->d.rank;
   m.blob_bytes = (uint32_t)(f->total_bytes - f->off_codes);
   m.trit_fmt = f->d.trit_fmt;
+  m.zc = 1;
   return m;
 }
 
@@ -583,23 +594,37 @@ int plan_shape(uint32_t n, const wal_info* infos, uint32_t grid, int x_dtype, Pl
 
 extern "C" {
 
-int wal_gemv(const wal_info* info, const void* W_dev, const void* x_dev, int x_dtype, float* y_dev, void* stream) {
+int wal_gemv(const wal_info* info, const void* W_dev, const void* x_dev, int x_dtype, float* y_dev,
+             void* ws_dev, size_t ws_bytes, void* stream) {
   int st = check_info(info);
   if (st) return st;
   if (!W_dev || !x_dev || !y_dev) return WAL_ERR_ARG;
   if (x_dtype != WAL_X_F32 && x_dtype != WAL_X_BF16) return WAL_ERR_ARG;
   if (!aligned(W_dev, 256) || !aligned(x_dev, 16) || !aligned(y_dev, 4)) return WAL_ERR_ALIGN;
+  const GemmShape S = gemm_shape(*info, 1);
+  const size_t need = info->d.n_paths ? (size_t)S.off_p : 0;   // z partials [chunks][terms]
+  if (need && (!ws_dev || ws_bytes < need)) return ws_dev ? WAL_ERR_BUFFER : WAL_ERR_ARG;
+  if (need && !aligned(ws_dev, 16)) return WAL_ERR_ALIGN;
   if (overlap(x_dev, (size_t)info->d.in * xelem(x_dtype), y_dev, (size_t)info->d.out * 4)) return WAL_ERR_ARG;
+  if (need && (overlap(ws_dev, need, y_dev, (size_t)info->d.out * 4) ||
+               overlap(ws_dev, need, x_dev, (size_t)info->d.in * xelem(x_dtype))))
+    return WAL_ERR_ARG;
   if ((st = check_blob_size(info))) return st;
   const uint32_t cls = class_of(info->d);
   if (!single_for(x_dtype, cls)) return WAL_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // one launch: every workgroup computes the low-rank reductions itself
-  const MatDev d = make_dev(info, W_dev, x_dev, y_dev, nullptr, info->d.in, info->d.out, 1);
+  MatDev d = make_dev(info, W_dev, x_dev, y_dev, static_cast<float*>(ws_dev), info->d.in, info->d.out, 1);
+  d.zc = S.zc;
+  if (d.terms) {
+    const uint32_t g = (d.terms + 15) / 16 * S.zc;
+    if (x_dtype == WAL_X_BF16) hipLaunchKernelGGL(k_z_chunks<WAL_X_BF16>, dim3(g), dim3(kThreads), 0, s, d);
+    else hipLaunchKernelGGL(k_z_chunks<WAL_X_F32>, dim3(g), dim3(kThreads), 0, s, d);
+    if ((st = launch_status())) return st;
+  }
   uint32_t resident = 0;
   if ((st = resident_blocks(reinterpret_cast<const void*>(grouped_for(x_dtype, cls)), &resident))) return st;
   uint32_t rpb = (d.out + resident - 1) / resident;
-  const uint32_t min_rows = kWaves * kRB * 2;
+  const uint32_t min_rows = kWaves * kRB;   // one batch per wavefront
   if (rpb < min_rows) rpb = min_rows;
   rpb = (rpb + kRB - 1) / kRB * kRB;
   if (rpb > seg_rows(cls)) rpb = seg_rows(cls);
@@ -642,7 +667,7 @@ int wal_gemm_small(const wal_info* info, const void* W_dev, const void* X_dev, i
   if (batched) return launch_gemm_valu(*info, d, batch, ws_dev, stream);
   for (uint32_t n = 0; n < batch; ++n) {
     const void* xn = static_cast<const uint8_t*>(X_dev) + (size_t)n * ldx * xe;
-    if ((st = wal_gemv(info, W_dev, xn, x_dtype, Y_dev + (size_t)n * ldy, stream))) return st;
+    if ((st = wal_gemv(info, W_dev, xn, x_dtype, Y_dev + (size_t)n * ldy, ws_dev, ws_bytes, stream))) return st;
   }
   return WAL_OK;
 }

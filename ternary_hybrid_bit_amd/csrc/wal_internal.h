@@ -21,11 +21,13 @@ struct MatDev {
   const uint8_t* s[WAL_MAX_PATHS];
   const void* x;       // [batch][ldx] activations
   float* y;            // [batch][ldy] outputs
-  float* z;            // [batch][n_paths * rank] workspace: diag(s_p) V_p^T x
+  float* z;            // workspace: diag(s_p) V_p^T x, zc partial sums over
+                       // 4096-column chunks [zc][n_paths * rank] (streaming kernels)
   uint32_t out, in, k, n_paths, rank, scale_fmt, row_stride, groups;
   uint32_t ldx, ldy, batch, terms;  // terms = n_paths * rank
   uint32_t blob_bytes;              // bytes of the blob from codes on (< 2^32)
   uint32_t trit_fmt;
+  uint32_t zc;                      // chunks of z to add (1 for grouped plans)
 };
 
 // Plan blob written by wal_grouped_plan (host) and read by the kernels:

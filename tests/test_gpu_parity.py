@@ -46,7 +46,9 @@ def run_gemv(wal, blob, info, x_f32, x_bits):
     W = to_dev(blob)
     xt = x_tensor(x_f32, x_bits)
     y = torch.full((info.d.out,), float("nan"), dtype=torch.float32, device=dev())
-    wal.wal_gemv(info, W, xt, y)
+    nws = wal.wal_workspace_size(info, 1)
+    ws = torch.empty(max(nws, 4) // 4, dtype=torch.float32, device=dev())
+    wal.wal_gemv(info, W, xt, y, ws)
     torch.cuda.synchronize()
     return y.cpu().numpy().astype(np.float64)
 

@@ -223,16 +223,21 @@ def test_product_calls_check_arguments_before_any_launch():
     info = wal.wal_packed_size(wal.make_desc(64, 256, 8, 1, 16))
     lib = wal._lib
     W, x, y, ws = 0x10000, 0x20000, 0x30000, 0x40000
-    ok_args = (ctypes.byref(info), W, x, wal.WAL_X_BF16, y, None)
-    assert lib.wal_gemv(ctypes.byref(info), W + 16, x, 1, y, None) == -6     # W not 256-aligned
-    assert lib.wal_gemv(ctypes.byref(info), W, x + 2, 1, y, None) == -6      # x not 16-aligned
-    assert lib.wal_gemv(ctypes.byref(info), W, x, 1, y + 2, None) == -6      # y not 4-aligned
-    assert lib.wal_gemv(ctypes.byref(info), W, x, 7, y, None) == -1          # dtype
-    assert lib.wal_gemv(ctypes.byref(info), None, x, 1, y, None) == -1
-    assert lib.wal_gemv(ctypes.byref(info), W, x, 1, x + 64, None) == -1     # y overlaps x
+    n1 = wal.wal_workspace_size(info, 1)
+    ok_args = (ctypes.byref(info), W, x, wal.WAL_X_BF16, y, ws, n1, None)
+    assert lib.wal_gemv(ctypes.byref(info), W + 16, x, 1, y, ws, n1, None) == -6     # W not 256-aligned
+    assert lib.wal_gemv(ctypes.byref(info), W, x + 2, 1, y, ws, n1, None) == -6      # x not 16-aligned
+    assert lib.wal_gemv(ctypes.byref(info), W, x, 1, y + 2, ws, n1, None) == -6      # y not 4-aligned
+    assert lib.wal_gemv(ctypes.byref(info), W, x, 1, y, ws, 8, None) == -5           # workspace too small
+    assert lib.wal_gemv(ctypes.byref(info), W, x, 1, y, None, 0, None) == -1         # workspace missing
+    assert lib.wal_gemv(ctypes.byref(info), W, x, 1, y, ws + 8, n1, None) == -6      # workspace misaligned
+    assert lib.wal_gemv(ctypes.byref(info), W, x, 7, y, ws, n1, None) == -1          # dtype
+    assert lib.wal_gemv(ctypes.byref(info), None, x, 1, y, ws, n1, None) == -1
+    assert lib.wal_gemv(ctypes.byref(info), W, x, 1, x + 64, ws, n1, None) == -1     # y overlaps x
+    assert lib.wal_gemv(ctypes.byref(info), W, x, 1, y, x, n1, None) == -1           # workspace overlaps x
     bad = wal.wal_info.from_buffer_copy(info)
     bad.off_alpha += 256
-    assert lib.wal_gemv(ctypes.byref(bad), *ok_args[1:]) == -7               # inconsistent info
+    assert lib.wal_gemv(ctypes.byref(bad), *ok_args[1:]) == -7                       # inconsistent info
     need = wal.wal_workspace_size(info, 2)
     gs = lambda *a: lib.wal_gemm_small(ctypes.byref(info), *a)  # noqa: E731
     assert gs(W, x, 1, 0, 256, y, 64, 0, ws, need, None) == -1               # batch 0
