@@ -67,15 +67,23 @@ struct XLane3 {
   uint32_t P[48];
   uint32_t Q15, Q47;
 
-  __device__ __forceinline__ void load(const void* x, uint32_t c0, uint32_t ncols) {
+  // The lane's 80 columns as loaded: bf16 pairs in column order.
+  struct Raw {
     uint32_t w[40];
-    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + c0);
+  };
+
+  // Columns c0 .. c0 + 79 through a resource over x: columns past the row's
+  // end (the last pass's tail) read zeros.
+  static __device__ __forceinline__ void load_raw(__amdgpu_buffer_rsrc_t rx, uint32_t c0, Raw& r) {
 #pragma unroll
     for (int q = 0; q < 10; ++q) {
-      const uint4 v = (uint32_t)(8 * q) < ncols ? src[q] : make_uint4(0, 0, 0, 0);
-      w[4 * q] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rx, 2 * c0 + 16 * q, 0, 0);
+      r.w[4 * q] = v[0]; r.w[4 * q + 1] = v[1]; r.w[4 * q + 2] = v[2]; r.w[4 * q + 3] = v[3];
     }
-    auto xv = [&](int j) { return (w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu; };
+  }
+
+  __device__ __forceinline__ void set(const Raw& r) {
+    auto xv = [&](int j) { return (r.w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu; };
 #pragma unroll
     for (int m = 0; m < 16; ++m) {
       P[3 * m] = xv(5 * m) | (xv(5 * m + 1) << 16);
@@ -167,27 +175,60 @@ struct Batch3 {
   uint32_t u;
 };
 
-// Signed site table of one pass (2x scaled bf16 activations); groups past the
-// pass and slot kGroups3 are zero.
-__device__ __forceinline__ void build_table3(const void* x, uint32_t col0, uint32_t pw, float* tbl) {
-  for (uint32_t e = threadIdx.x; e < (kGroups3 + 1) * 16; e += kThreads) {
-    const uint32_t g = e >> 4, q = e & 15;
-    float v[8];
+// The activations of a thread's share of one pass's signed site table
+// (2x scaled bf16): items e = threadIdx.x + 256 i < (kGroups3 + 1) * 16, each
+// 8 columns of group e >> 4, loaded before the set-up barrier and stored
+// after it.  Groups past the row's end read as zero; slot kGroups3 is zero.
+struct TableX3 {
+  static constexpr int kItems = ((kGroups3 + 1) * 16 + kThreads - 1) / kThreads;
+  u32x4_t w[kItems];
+
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rx, uint32_t col0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      v[i] = g * 128 < pw ? 2.0f * xval<WAL_X_BF16>(x, col0 + g * 128 + q * 8 + i) : 0.f;
-    float4* pos = reinterpret_cast<float4*>(tbl + g * 256 + q * 8);
-    float4* neg = reinterpret_cast<float4*>(tbl + g * 256 + 128 + q * 8);
-    pos[0] = make_float4(v[0], v[1], v[2], v[3]);
-    pos[1] = make_float4(v[4], v[5], v[6], v[7]);
-    neg[0] = make_float4(-v[0], -v[1], -v[2], -v[3]);
-    neg[1] = make_float4(-v[4], -v[5], -v[6], -v[7]);
+    for (int i = 0; i < kItems; ++i) {
+      const uint32_t e = threadIdx.x + kThreads * i, g = e >> 4;
+      const uint32_t col = col0 + g * 128 + (e & 15) * 8;
+      // the zero slot (and items past it) load from far out of range: zeros
+      w[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, g < kGroups3 ? 2 * col : 0x7FFFFFF0u, 0, 0);
+    }
   }
+
+  __device__ __forceinline__ void store(float* tbl) const {
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+      const uint32_t e = threadIdx.x + kThreads * i;
+      if (e >= (kGroups3 + 1) * 16) break;
+      const uint32_t g = e >> 4, q = e & 15;
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        v[j] = 2.0f * __uint_as_float((j & 1) ? (w[i][j >> 1] & 0xFFFF0000u) : (w[i][j >> 1] << 16));
+      float4* pos = reinterpret_cast<float4*>(tbl + g * 256 + q * 8);
+      float4* neg = reinterpret_cast<float4*>(tbl + g * 256 + 128 + q * 8);
+      pos[0] = make_float4(v[0], v[1], v[2], v[3]);
+      pos[1] = make_float4(v[4], v[5], v[6], v[7]);
+      neg[0] = make_float4(-v[0], -v[1], -v[2], -v[3]);
+      neg[1] = make_float4(-v[4], -v[5], -v[6], -v[7]);
+    }
+  }
+};
+
+// The byte table: thread t computes byte t's entry once and writes its
+// kLutCopies copies (128 contiguous bytes), starting at a thread-dependent
+// 16-byte slot so that a wavefront's writes spread over the LDS banks.
+__device__ __forceinline__ void build_lut(uint32_t* lut) {
+  static_assert(kThreads == 256 && kLutCopies == 32, "one byte value per thread, 8 x 16 bytes of copies");
+  const uint32_t e = base3_entry(threadIdx.x);
+  uint4* dst = reinterpret_cast<uint4*>(lut + threadIdx.x * kLutCopies);
+#pragma unroll
+  for (uint32_t k = 0; k < 8; ++k) dst[(k + threadIdx.x) & 7] = make_uint4(e, e, e, e);
 }
 
-template <int SF, int K>
+// ZP: low-rank partials prefetched per term; lut: the workgroup's first pass,
+// which also fills the byte table.
+template <int SF, int K, int ZP>
 __device__ __forceinline__ void stream_rows_base3(const MatDev& d, uint32_t row0, uint32_t row1, uint32_t pass,
-                                                  uint32_t npass, Smem3& sm) {
+                                                  uint32_t npass, bool lut_first, Smem3& sm) {
   constexpr int RB = kRB3;
   constexpr int LOG = ilog2(RB);
   constexpr int SH = 6 - LOG;
@@ -197,7 +238,7 @@ __device__ __forceinline__ void stream_rows_base3(const MatDev& d, uint32_t row0
   const uint32_t wave = wave_id();
   const uint32_t nb = (row1 - row0 + RB - 1) / RB;
   const bool has_rows = wave < nb;
-  uint32_t b = has_rows ? wave : nb - 1;
+  uint32_t b = wave;   // the wave's batches: wave, wave + kWaves, ...
 
   const uint32_t pw = min(kPassBase3, d.in - pass * kPassBase3);   // trits of this pass
   const uint32_t Gp = (pw + 127) / 128, g0 = pass * kGroups3, G = d.groups;
@@ -205,7 +246,8 @@ __device__ __forceinline__ void stream_rows_base3(const MatDev& d, uint32_t row0
   const uint32_t ncols = 80 * (uint32_t)lane < pw ? min(80u, pw - 80 * lane) : 0u;
 
   // codes
-  const __amdgpu_buffer_rsrc_t rc = rsrc(d.codes, d.blob_bytes);
+  // one resource over the blob; plane offsets go into the vector offsets
+  const __amdgpu_buffer_rsrc_t rw_ = rsrc(d.codes, d.blob_bytes);
   const uint32_t vc = pass * (kPassBase3 / 5) + 16 * (ncols ? lane : 0);
   // groups of the lane's trits: A, and A + 1 when a boundary falls inside
   const uint32_t cls = lane & 7;
@@ -214,20 +256,18 @@ __device__ __forceinline__ void stream_rows_base3(const MatDev& d, uint32_t row0
   const uint32_t gAc = gA < G ? gA : G - 1;
   const uint32_t gB = split && gA + 1 < G ? gA + 1 : gAc;
   // alpha window: SB-byte scales of gA and gB
-  const __amdgpu_buffer_rsrc_t ra = rsrc(d.alpha, d.blob_bytes - (uint32_t)(d.alpha - d.codes));
   const uint32_t aoff = gAc * SB, abase = aoff & ~3u, oA = aoff - abase;
+  const uint32_t aplane = (uint32_t)(d.alpha - d.codes);
   const uint32_t boff = gB * SB - abase;   // byte of gB's scale within the window (0..7)
   // beta / sites: lane l < 40 owns group g0 + l of the pass
   const bool site_lane = K > 0 && (uint32_t)lane < Gp;
   const uint32_t gs = site_lane ? g0 + lane : g0;
-  __amdgpu_buffer_rsrc_t rs = rsrc(d.codes, 0u), rb = rsrc(d.codes, 0u);
   uint32_t vs = 0, bbase = 0, oB = 0;
   if constexpr (K > 0) {
-    rs = rsrc(d.sites, d.blob_bytes - (uint32_t)(d.sites - d.codes));
-    rb = rsrc(d.beta, d.blob_bytes - (uint32_t)(d.beta - d.codes));
-    vs = gs * K;
+    vs = (uint32_t)(d.sites - d.codes) + gs * K;
     bbase = (gs * SB) & ~3u;
     oB = gs * SB - bbase;
+    bbase += (uint32_t)(d.beta - d.codes);
   }
   const uint32_t tslot = site_lane ? (uint32_t)lane : kGroups3;   // zero slot for other lanes
   // prefix-sum weights: which of total / p16 / p32 / p48 / p64 is S_A
@@ -242,47 +282,53 @@ __device__ __forceinline__ void stream_rows_base3(const MatDev& d, uint32_t row0
   uint32_t ubit = 0;
   if (uon) {
     const uint32_t p = ti / d.rank, r = ti % d.rank;
-    up = path_ptr(d.U, p) + r / 8;
+    up = path_plane(d.U, d, p) + r / 8;
     ubit = r & 7;
   }
-  const __amdgpu_buffer_rsrc_t u_rs = rsrc(d.codes, last && d.terms ? d.blob_bytes : 0u);
+  const bool ulive = last && d.terms;
   const uint32_t uoff = (uint32_t)(up - d.codes), ustride = uon ? ub : 0;
   const uint32_t* lut = sm.lut + (lane & (kLutCopies - 1));
 
   XLane3 xl;
 
+  // Batches past the wave's last one read through empty resources (zeros,
+  // no memory access), keeping every load unconditional.
+  const __amdgpu_buffer_rsrc_t r_none = rsrc(d.codes, 0u);
   auto load_batch = [&](uint32_t bb) {
     Batch3<RB> B;
-    const uint32_t base = row0 + bb * RB;
+    const bool live = bb < nb;
+    const __amdgpu_buffer_rsrc_t rw = live ? rw_ : r_none;
+    const __amdgpu_buffer_rsrc_t ru = live && ulive ? rw_ : r_none;
+    const uint32_t base = row0 + (live ? bb : nb - 1) * RB;
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       const uint32_t row = min(base + i, row1 - 1);
       Raw3& r = B.r[i];
-      r.c = __builtin_amdgcn_raw_buffer_load_b128(rc, vc, row * d.row_stride, kStream);
+      r.c = __builtin_amdgcn_raw_buffer_load_b128(rw, vc, row * d.row_stride, kStream);
       // The scale windows may reach a few bytes past the row's scales: their
       // row offset goes in the range-checked vector offset, so bytes past
       // the blob read as zero instead of touching memory.
-      const Win<SF> wa = load_win<SF>(ra, abase + row * G * SB, 0);
+      const Win<SF> wa = load_win<SF>(rw, aplane + abase + row * G * SB, 0);
       r.sa[0] = wa.w[0]; r.sa[1] = wa.w[1];
       if constexpr (SF == WAL_SCALE_FP24) r.sa[2] = wa.w[2]; else r.sa[2] = 0;
       if constexpr (K > 0) {
         if constexpr (SF == WAL_SCALE_FP24) {
-          const u32x2_t wb = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rb, bbase + row * G * SB, 0, kStream));
+          const u32x2_t wb = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rw, bbase + row * G * SB, 0, kStream));
           r.sb[0] = wb[0]; r.sb[1] = wb[1];
         } else {
-          r.sb[0] = __builtin_amdgcn_raw_buffer_load_b32(rb, bbase + row * G * SB, 0, kStream);
+          r.sb[0] = __builtin_amdgcn_raw_buffer_load_b32(rw, bbase + row * G * SB, 0, kStream);
           r.sb[1] = 0;
         }
         if constexpr (K == 8) {
-          const u32x2_t sv = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, vs, row * G * K, kStream));
+          const u32x2_t sv = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rw, vs, row * G * K, kStream));
           r.s[0] = sv[0]; r.s[1] = sv[1];
         }
-        if constexpr (K == 4) { r.s[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, vs, row * G * K, kStream); r.s[1] = 0; }
-        if constexpr (K == 2) { r.s[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, vs, row * G * K, kStream); r.s[1] = 0; }
+        if constexpr (K == 4) { r.s[0] = __builtin_amdgcn_raw_buffer_load_b32(rw, vs, row * G * K, kStream); r.s[1] = 0; }
+        if constexpr (K == 2) { r.s[0] = __builtin_amdgcn_raw_buffer_load_b16(rw, vs, row * G * K, kStream); r.s[1] = 0; }
       }
     }
     const uint32_t ry = min(base + ((uint32_t)lane >> SH), row1 - 1);
-    B.u = __builtin_amdgcn_raw_buffer_load_b8(u_rs, uoff + ry * ustride, 0, kStream);
+    B.u = __builtin_amdgcn_raw_buffer_load_b8(ru, uoff + ry * ustride, 0, kStream);
     __builtin_amdgcn_sched_barrier(0);
     return B;
   };
@@ -323,7 +369,7 @@ __device__ __forceinline__ void stream_rows_base3(const MatDev& d, uint32_t row0
       const uint32_t ry = min(row, row1 - 1);
       for (uint32_t t = ti + LPR; t < d.terms; t += LPR) {
         const uint32_t p = t / d.rank, r = t % d.rank;
-        const uint32_t byte = path_ptr(d.U, p)[(size_t)ry * ub + r / 8];
+        const uint32_t byte = path_plane(d.U, d, p)[(size_t)ry * ub + r / 8];
         const float zt = sm.z[t];
         c += ((byte >> (r & 7)) & 1u) ? -zt : zt;
       }
@@ -332,47 +378,50 @@ __device__ __forceinline__ void stream_rows_base3(const MatDev& d, uint32_t row0
     if ((lane & (LPR - 1)) == 0 && row < row1) sm.ybuf[yi] = v;
   };
 
-  const uint32_t blast = has_rows ? wave + (nb - 1 - wave) / kWaves * kWaves : b;
-  auto ahead = [&](uint32_t bb) { return bb < nb ? bb : blast; };
+  // Set-up loads first (L2 hits: x, the table's x, the low-rank partials),
+  // then the first two batches (HBM): loads complete in order, so waiting
+  // for the set-up data does not wait for the batches.
+  const __amdgpu_buffer_rsrc_t rx = x_rsrc<WAL_X_BF16>(d.x, d.in);
+  XLane3::Raw xr;
+  XLane3::load_raw(rx, pass * kPassBase3 + 80 * lane, xr);
+  TableX3 tx;
+  if constexpr (K > 0) tx.load(rx, pass * kPassBase3);
+  const bool zpass = pass == 0 && d.terms;
+  ZPart<ZP> zp;
+  if (zpass) z_prefetch<ZP>(d, threadIdx.x, zp);
   Batch3<RB> B0 = load_batch(b);
-  Batch3<RB> B1 = load_batch(ahead(b + kWaves));
-  xl.load(d.x, pass * kPassBase3 + 80 * lane, ncols);
+  Batch3<RB> B1 = load_batch(b + kWaves);
 
   __syncthreads();   // readers of the previous table and z are done
-  if (pass == 0)
-    for (uint32_t t = threadIdx.x; t < d.terms; t += kThreads) {
-      float z = 0.f;
-      for (uint32_t cc = 0; cc < d.zc; ++cc) z += d.z[cc * d.terms + t];
-      sm.z[t] = z;
-    }
-  if constexpr (K > 0) build_table3(d.x, pass * kPassBase3, pw, sm.tbl);
+  if (lut_first) build_lut(sm.lut);
+  if (zpass && threadIdx.x < d.terms) sm.z[threadIdx.x] = z_total<ZP>(d, threadIdx.x, zp);
+  if constexpr (K > 0) tx.store(sm.tbl);
   __syncthreads();
   if (!has_rows) return;
+  xl.set(xr);
 
   for (;;) {
-    const Batch3<RB> B2 = load_batch(ahead(b + 2 * kWaves));
+    const Batch3<RB> B2 = load_batch(b + 2 * kWaves);
     finish_batch(B0, b);
     if (b + kWaves >= nb) break;
     b += kWaves;
-    B0 = load_batch(ahead(b + 2 * kWaves));
+    B0 = load_batch(b + 2 * kWaves);
     finish_batch(B1, b);
     if (b + kWaves >= nb) break;
     b += kWaves;
-    B1 = load_batch(ahead(b + 2 * kWaves));
+    B1 = load_batch(b + 2 * kWaves);
     finish_batch(B2, b);
     if (b + kWaves >= nb) break;
     b += kWaves;
   }
 }
 
-__device__ __forceinline__ void build_lut(uint32_t* lut) {
-  for (uint32_t i = threadIdx.x; i < 256 * kLutCopies; i += kThreads) lut[i] = base3_entry(i / kLutCopies);
-}
-
-template <int SF, int K>
-__device__ __forceinline__ void run_segment_base3(const MatDev& d, uint32_t row0, uint32_t row1, Smem3& sm) {
+template <int SF, int K, int ZP>
+__device__ __forceinline__ void run_segment_base3(const MatDev& d, uint32_t row0, uint32_t row1, bool lut_first,
+                                                  Smem3& sm) {
   const uint32_t npass = (d.in + kPassBase3 - 1) / kPassBase3;
-  for (uint32_t pass = 0; pass < npass; ++pass) stream_rows_base3<SF, K>(d, row0, row1, pass, npass, sm);
+  for (uint32_t pass = 0; pass < npass; ++pass)
+    stream_rows_base3<SF, K, ZP>(d, row0, row1, pass, npass, lut_first && pass == 0, sm);
   __syncthreads();
   const uint32_t nrows = row1 - row0;
   for (uint32_t i = threadIdx.x; i < nrows; i += kThreads) d.y[row0 + i] = sm.ybuf[i];
@@ -383,21 +432,19 @@ __global__ __launch_bounds__(kThreads) void k_stream3_grouped(const MatDev* __re
                                                               const uint32_t* __restrict__ blockseg,
                                                               const Seg* __restrict__ segs) {
   __shared__ Smem3 sm;
-  build_lut(sm.lut);   // read only after the first pass's barriers
   const uint32_t s0 = blockseg[blockIdx.x], s1 = blockseg[blockIdx.x + 1];
   for (uint32_t s = s0; s < s1; ++s) {
     const Seg sg = segs[s];
-    run_segment_base3<SF, K>(descs[sg.mat], sg.row0, sg.row1, sm);
+    run_segment_base3<SF, K, 1>(descs[sg.mat], sg.row0, sg.row1, s == s0, sm);
   }
 }
 
 template <int SF, int K>
 __global__ __launch_bounds__(kThreads) void k_stream3_single(MatDev d, uint32_t rows_per_block) {
   __shared__ Smem3 sm;
-  build_lut(sm.lut);
   const uint32_t r0 = blockIdx.x * rows_per_block;
   const uint32_t r1 = min(d.out, r0 + rows_per_block);
-  if (r0 < r1) run_segment_base3<SF, K>(d, r0, r1, sm);
+  if (r0 < r1) run_segment_base3<SF, K, kZSinglePrefetch>(d, r0, r1, true, sm);
 }
 
 }  // namespace

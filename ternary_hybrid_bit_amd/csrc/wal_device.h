@@ -101,6 +101,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
 
+// A resource over the activations of one product: loads past the row's end
+// (lanes beyond the last pass's width) read zeros without touching memory.
+template <int XT>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t x_rsrc(const void* x, uint32_t n) {
+  return rsrc(x, n * (XT == WAL_X_F32 ? 4u : 2u));
+}
+
 // Activation element as fp32.
 template <int XT>
 __device__ __forceinline__ float xval(const void* x, uint32_t i) {
@@ -122,10 +129,9 @@ __device__ __forceinline__ uint64_t shl64(uint64_t v) {
   }
 }
 
-// p-th entry of a per-path pointer array, without dynamic indexing (which
-// would move the descriptor to scratch memory).
-__device__ __forceinline__ const uint8_t* path_ptr(const uint8_t* const (&a)[WAL_MAX_PATHS], uint32_t p) {
-  return p == 0 ? a[0] : p == 1 ? a[1] : p == 2 ? a[2] : a[3];
+// Plane of low-rank path p, from path 0's plane of the same kind.
+__device__ __forceinline__ const uint8_t* path_plane(const uint8_t* p0, const MatDev& d, uint32_t p) {
+  return p0 + (size_t)p * d.pstride;
 }
 
 // ---------------------------------------------------------------------------
@@ -170,6 +176,13 @@ __device__ __forceinline__ void z_chunk(const MatDev& d, const void* x, uint32_t
   const uint32_t tid = threadIdx.x, nthr = blockDim.x;
   const int lane = tid & 63;
   const uint32_t T = d.terms, vrow = d.in / 8;
+  // the per-rank scale of the thread's term, loaded before the sweep so its
+  // latency is not paid after the barrier
+  float scale = 0.f;
+  if (tid < (uint32_t)C && t0 + tid < T) {
+    const uint32_t p = (t0 + tid) / d.rank, r = (t0 + tid) % d.rank;
+    scale = f16_at(path_plane(d.s, d, p), r);
+  }
   float acc[C];
 #pragma unroll
   for (int q = 0; q < C; ++q) acc[q] = 0.f;
@@ -197,7 +210,7 @@ __device__ __forceinline__ void z_chunk(const MatDev& d, const void* x, uint32_t
       const uint32_t t = t0 + q;
       if (t < T) {
         const uint32_t p = t / d.rank, r = t % d.rank;
-        const uint32_t bits = reinterpret_cast<const uint16_t*>(path_ptr(d.V, p) + (size_t)r * vrow)[c / 16];
+        const uint32_t bits = reinterpret_cast<const uint16_t*>(path_plane(d.V, d, p) + (size_t)r * vrow)[c / 16];
         // a set bit flips the sign of x_j
 #pragma unroll
         for (int j = 0; j < 16; ++j) acc[q] += __uint_as_float(xb[j] ^ ((bits << (31 - j)) & 0x80000000u));
@@ -213,10 +226,40 @@ __device__ __forceinline__ void z_chunk(const MatDev& d, const void* x, uint32_t
     if (t < T) {
       float sum = 0.f;
       for (uint32_t w = 0; w < (nthr >> 6); ++w) sum += red[w][tid];
-      const uint32_t p = t / d.rank, r = t % d.rank;
-      out[t] = f16_at(path_ptr(d.s, p), r) * sum;
+      out[t] = scale * sum;
     }
   }
+}
+
+// The low-rank reductions a streaming workgroup needs, z[t] for t < d.terms,
+// are the sums of d.zc partials (one per column chunk).  A thread first issues
+// the loads of up to ZP partials of its term (prefetch) and adds them later
+// (total), so the loads overlap other memory latency.
+template <int ZP>
+struct ZPart {
+  float v[ZP];
+};
+
+// Only when d.terms > 0.  Threads past the last term load the last term's
+// partials (unused) rather than branch.
+template <int ZP>
+__device__ __forceinline__ void z_prefetch(const MatDev& d, uint32_t t, ZPart<ZP>& zp) {
+  const uint32_t tt = t < d.terms ? t : d.terms - 1;
+  const __amdgpu_buffer_rsrc_t rz = rsrc(d.z, 4 * d.zc * d.terms);
+#pragma unroll
+  for (int cc = 0; cc < ZP; ++cc)
+    zp.v[cc] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rz, 4 * (cc * d.terms + tt), 0, 0));
+}
+
+// Partials in chunk order (a fixed order: results do not depend on timing).
+// Chunks past d.zc read as zero (out of the resource's range).
+template <int ZP>
+__device__ __forceinline__ float z_total(const MatDev& d, uint32_t t, const ZPart<ZP>& zp) {
+  float z = zp.v[0];
+#pragma unroll
+  for (int cc = 1; cc < ZP; ++cc) z += zp.v[cc];
+  for (uint32_t cc = ZP; cc < d.zc; ++cc) z += d.z[cc * d.terms + t];
+  return z;
 }
 
 // One pre-pass workgroup: terms t0 .. t0 + kZTerms - 1 of one matrix into d.z.

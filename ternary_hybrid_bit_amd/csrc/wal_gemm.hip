@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void k_reduce(MatDev d, const float* __restric
   for (uint32_t s = 0; s < slices; ++s) v += P[s * plane + (size_t)n * d.out + row];
   const uint32_t ub = (d.rank + 7) / 8;
   for (uint32_t p = 0; p < d.n_paths; ++p) {
-    const uint8_t* u = path_ptr(d.U, p) + (size_t)row * ub;
+    const uint8_t* u = path_plane(d.U, d, p) + (size_t)row * ub;
     for (uint32_t r = 0; r < d.rank; ++r) {
       const float zt = zs[p * d.rank + r];
       v += ((u[r >> 3] >> (r & 7)) & 1u) ? -zt : zt;

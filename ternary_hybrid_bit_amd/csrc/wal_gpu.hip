@@ -7,9 +7,9 @@
 // Kernels:
 //  * the binary low-rank reductions z_p[r] = s_p[r] * sum_j (-1)^{V bit} x_j,
 //    a pre-pass into the caller's workspace: kZTerms terms per workgroup for
-//    grouped products (k_z_grouped), 16 terms x 4096 columns per workgroup
-//    for a single product (k_z_chunks, partial sums that the streaming
-//    kernel adds), so that wide matrices get enough workgroups.
+//    grouped products (k_z_grouped), kZTerms terms x 4096 columns per
+//    workgroup for a single product (k_z_chunks, partial sums that the
+//    streaming kernel adds), so that wide matrices get enough workgroups.
 //  * k_stream_*: one streaming pass over the packed planes.  Every workgroup
 //    owns a contiguous range of rows of one or more matrices (for grouped
 //    products the host splits the total packed bytes evenly over a grid that
@@ -60,26 +60,29 @@ template <> struct XLane<WAL_X_BF16> {
   uint32_t p[32];
   static constexpr float kHalf = 0.5f;   // decoded trits and table entries are 2x
 
-  __device__ __forceinline__ void load(const void* x, uint32_t c, bool active) {
-    if (!active) {
-#pragma unroll
-      for (int q = 0; q < 32; ++q) p[q] = 0;
-      return;
-    }
-    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + c);
+  // The lane's 64 columns as loaded: bf16 pairs in column order.
+  struct Raw {
     uint32_t w[32];
+  };
+
+  // Columns c .. c + 63 through a resource over x (lanes past the pass width
+  // read zeros).
+  static __device__ __forceinline__ void load_raw(__amdgpu_buffer_rsrc_t rx, uint32_t c, Raw& r) {
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const uint4 v = src[q];
-      w[4 * q] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rx, 2 * c + 16 * q, 0, 0);
+      r.w[4 * q] = v[0]; r.w[4 * q + 1] = v[1]; r.w[4 * q + 2] = v[2]; r.w[4 * q + 3] = v[3];
     }
+  }
+
+  __device__ __forceinline__ void set(const Raw& r) {
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int lo = 16 * d + i, hi = 16 * d + 8 + i;
-        const uint32_t xl = (w[lo >> 1] >> (16 * (lo & 1))) & 0xFFFFu;
-        const uint32_t xh = (w[hi >> 1] >> (16 * (hi & 1))) & 0xFFFFu;
+        const uint32_t xl = (r.w[lo >> 1] >> (16 * (lo & 1))) & 0xFFFFu;
+        const uint32_t xh = (r.w[hi >> 1] >> (16 * (hi & 1))) & 0xFFFFu;
         p[8 * d + i] = xl | (xh << 16);
       }
   }
@@ -111,18 +114,22 @@ template <> struct XLane<WAL_X_F32> {
   float f[64];
   static constexpr float kHalf = 1.0f;
 
-  __device__ __forceinline__ void load(const void* x, uint32_t c, bool active) {
-    if (!active) {
-#pragma unroll
-      for (int q = 0; q < 64; ++q) f[q] = 0.f;
-      return;
-    }
-    const float4* src = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + c);
+  struct Raw {
+    float f[64];
+  };
+
+  static __device__ __forceinline__ void load_raw(__amdgpu_buffer_rsrc_t rx, uint32_t c, Raw& r) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      const float4 v = src[q];
-      f[4 * q] = v.x; f[4 * q + 1] = v.y; f[4 * q + 2] = v.z; f[4 * q + 3] = v.w;
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rx, 4 * c + 16 * q, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r.f[4 * q + j] = __uint_as_float(v[j]);
     }
+  }
+
+  __device__ __forceinline__ void set(const Raw& r) {
+#pragma unroll
+    for (int q = 0; q < 64; ++q) f[q] = r.f[q];
   }
 
   // sum_j T_j x_j: sign-extend each 2-bit code to {-1, 0, +1} and accumulate.
@@ -148,28 +155,53 @@ struct StreamSmem {
                                // (padded: lanes of a last, partial batch index past it)
 };
 
-// Signed table of one 4096-column pass; groups past the pass width are zero.
+// The activations of a thread's share of one 4096-column pass's signed table:
+// items e = threadIdx.x and threadIdx.x + 256, each 8 columns of group e >> 4.
+// They are loaded before the set-up barrier and stored after it; columns past
+// the row's end (groups past the pass width) read as zero.
 template <int XT>
-__device__ __forceinline__ void build_table(const void* x, uint32_t col0, uint32_t pw, float* tbl) {
-  constexpr float kT = XT == WAL_X_BF16 ? 2.0f : 1.0f;
-  for (uint32_t e = threadIdx.x; e < 32 * 16; e += kThreads) {
-    const uint32_t g = e >> 4, q = e & 15;   // 8 columns per item
-    float v[8];
-    if (g * 128 < pw) {
+struct TableX {
+  static constexpr int kW = XT == WAL_X_BF16 ? 4 : 8;   // dwords per item
+  uint32_t w[2][kW];
+
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rx, uint32_t col0) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = kT * xval<XT>(x, col0 + g * 128 + q * 8 + i);
-    } else {
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t e = threadIdx.x + kThreads * i;
+      const uint32_t col = col0 + (e >> 4) * 128 + (e & 15) * 8;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = 0.f;
+      for (int h = 0; h < kW / 4; ++h) {
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rx, col * (XT == WAL_X_BF16 ? 2 : 4) + 16 * h, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[i][4 * h + j] = v[j];
+      }
     }
-    float4* pos = reinterpret_cast<float4*>(tbl + g * 256 + q * 8);
-    float4* neg = reinterpret_cast<float4*>(tbl + g * 256 + 128 + q * 8);
-    pos[0] = make_float4(v[0], v[1], v[2], v[3]);
-    pos[1] = make_float4(v[4], v[5], v[6], v[7]);
-    neg[0] = make_float4(-v[0], -v[1], -v[2], -v[3]);
-    neg[1] = make_float4(-v[4], -v[5], -v[6], -v[7]);
   }
-}
+
+  // +-2x (bf16 x) or +-x (fp32 x) for every position of every group:
+  // tbl[group][site byte].
+  __device__ __forceinline__ void store(float* tbl) const {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t e = threadIdx.x + kThreads * i;
+      const uint32_t g = e >> 4, q = e & 15;
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if constexpr (XT == WAL_X_BF16)
+          v[j] = 2.0f * __uint_as_float((j & 1) ? (w[i][j >> 1] & 0xFFFF0000u) : (w[i][j >> 1] << 16));
+        else
+          v[j] = __uint_as_float(w[i][j]);
+      }
+      float4* pos = reinterpret_cast<float4*>(tbl + g * 256 + q * 8);
+      float4* neg = reinterpret_cast<float4*>(tbl + g * 256 + 128 + q * 8);
+      pos[0] = make_float4(v[0], v[1], v[2], v[3]);
+      pos[1] = make_float4(v[4], v[5], v[6], v[7]);
+      neg[0] = make_float4(-v[0], -v[1], -v[2], -v[3]);
+      neg[1] = make_float4(-v[4], -v[5], -v[6], -v[7]);
+    }
+  }
+};
 
 // Packed data of one row for one lane.
 struct RowRaw {
@@ -186,8 +218,8 @@ struct Batch {
 
 // Per-pass lane constants of the 2-bit stream.
 struct Lane2 {
-  __amdgpu_buffer_rsrc_t rc, rs, ra, rb;
-  uint32_t vc, vs, va;        // lane offsets within a row of each plane
+  __amdgpu_buffer_rsrc_t rw;  // the blob from the codes plane on
+  uint32_t vc, vs, va, vb;    // lane offsets (from the codes plane) in row 0 of each plane
   uint32_t sc, ss, sa;        // row strides (bytes) of each plane
   const float* tb;            // the lane's group in the site table
   const uint8_t* up;          // U byte of the lane's first low-rank term (row 0)
@@ -199,7 +231,8 @@ struct Lane2 {
 // low-rank terms, behind barriers) runs after each wave has issued the loads
 // of its first batch and of its x columns, so the set-up overlaps the
 // memory latency instead of adding to it.  Every wave reaches both barriers.
-template <int XT, int SF, int K, int RB>
+// ZP: low-rank partials (column chunks) prefetched per term.
+template <int XT, int SF, int K, int RB, int ZP>
 __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0, uint32_t row1, uint32_t pass,
                                                  uint32_t npass, StreamSmem& sm) {
   constexpr int LOG = ilog2(RB);
@@ -210,7 +243,7 @@ __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0,
   const uint32_t wave = wave_id();
   const uint32_t nb = (row1 - row0 + RB - 1) / RB;
   const bool has_rows = wave < nb;
-  uint32_t b = has_rows ? wave : nb - 1;   // waves without rows prefetch nothing new
+  uint32_t b = wave;   // the wave's batches: wave, wave + kWaves, ...
 
   const uint32_t pw = min(kPass2bit, d.in - pass * kPass2bit);
   const uint32_t Gp = pw / 128, g0 = pass * (kPass2bit / 128), G = d.groups;
@@ -218,18 +251,17 @@ __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0,
   const uint32_t gl = on ? (uint32_t)lane >> 1 : 0;
   const bool first = pass == 0, last = pass + 1 == npass;
 
+  // One resource over the blob; the plane offsets go into the per-lane
+  // offsets (the planes are 256-byte aligned, so alignments carry over).
   Lane2 L;
-  L.rc = rsrc(d.codes, d.blob_bytes);
+  L.rw = rsrc(d.codes, d.blob_bytes);
   L.vc = pass * (kPass2bit / 4) + 16 * (on ? lane : 0);
   L.sc = d.row_stride;
-  const uint32_t left_a = d.blob_bytes - (uint32_t)(d.alpha - d.codes);
-  L.ra = rsrc(d.alpha, left_a);
-  L.va = (g0 + gl) * SB;
+  L.va = (uint32_t)(d.alpha - d.codes) + (g0 + gl) * SB;
   L.sa = G * SB;
   if constexpr (K > 0) {
-    L.rs = rsrc(d.sites, d.blob_bytes - (uint32_t)(d.sites - d.codes));
-    L.rb = rsrc(d.beta, d.blob_bytes - (uint32_t)(d.beta - d.codes));
-    L.vs = (g0 + gl) * K + (lane & 1) * (K / 2);
+    L.vb = (uint32_t)(d.beta - d.codes) + (g0 + gl) * SB;
+    L.vs = (uint32_t)(d.sites - d.codes) + (g0 + gl) * K + (lane & 1) * (K / 2);
     L.ss = G * K;
   }
   L.tb = sm.tbl + ((uint32_t)lane >> 1) * 256;
@@ -240,41 +272,46 @@ __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0,
   L.ubit = 0;
   if (L.uon) {
     const uint32_t p = ti / d.rank, r = ti % d.rank;
-    L.up = path_ptr(d.U, p) + r / 8;
+    L.up = path_plane(d.U, d, p) + r / 8;
     L.ubit = r & 7;
   }
-  // y and the U bytes go through buffer instructions too (a generic pointer
-  // would need flat instructions, whose completion the compiler tracks more
-  // conservatively): U offsets are taken from the codes plane's resource,
-  // which spans the rest of the blob.
+  // The U bytes go through buffer instructions too (a generic pointer would
+  // need flat instructions, whose completion the compiler tracks more
+  // conservatively).  Passes that need no U bits (all but the last) read
+  // them through an empty resource.
   const uint32_t uoff = (uint32_t)(L.up - d.codes);
   const uint32_t ustride = L.uon ? L.ub : 0;
-  // Passes that need no U bits (all but the last) read them through an
-  // empty resource: out-of-range buffer loads return 0 without a memory
-  // access, and the instruction stream stays the same.
-  const __amdgpu_buffer_rsrc_t u_rs = rsrc(d.codes, last && d.terms ? d.blob_bytes : 0u);
+  const bool ulive = last && d.terms;
 
   XLane<XT> xl;
 
-  // Every load is unconditional and in bounds (rows past the range repeat
-  // the last row of the range), so the compiler never has to merge loaded
-  // and unloaded values, which would make it wait for every load in flight.
+  // Every load is unconditional (rows past the range repeat the last row of
+  // the range), so the compiler never has to merge loaded and unloaded
+  // values, which would make it wait for every load in flight.  Batches past
+  // the wave's last one (the prefetch at the end of the loop) read through
+  // empty resources: out-of-range buffer loads return 0 without a memory
+  // access, and the instruction stream stays the same.
+  // (Out-of-range buffer loads return 0 without a memory access.)
+  const __amdgpu_buffer_rsrc_t r_none = rsrc(d.codes, 0u);
   auto load_batch = [&](uint32_t bb) {
     Batch<RB> B;
-    const uint32_t base = row0 + bb * RB;
+    const bool live = bb < nb;
+    const __amdgpu_buffer_rsrc_t rw = live ? L.rw : r_none;
+    const __amdgpu_buffer_rsrc_t ru = live && ulive ? L.rw : r_none;
+    const uint32_t base = row0 + (live ? bb : nb - 1) * RB;
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       const uint32_t row = min(base + i, row1 - 1);
       RowRaw& r = B.r[i];
-      r.c = __builtin_amdgcn_raw_buffer_load_b128(L.rc, L.vc, row * L.sc, kStream);
-      r.a = load_scale<SF>(L.ra, L.va, row * L.sa);
-      if constexpr (K == 8) r.s = __builtin_amdgcn_raw_buffer_load_b32(L.rs, L.vs, row * L.ss, kStream);
-      if constexpr (K == 4) r.s = __builtin_amdgcn_raw_buffer_load_b16(L.rs, L.vs, row * L.ss, kStream);
-      if constexpr (K == 2) r.s = __builtin_amdgcn_raw_buffer_load_b8(L.rs, L.vs, row * L.ss, kStream);
-      if constexpr (K > 0) r.b = load_scale<SF>(L.rb, L.va, row * L.sa);
+      r.c = __builtin_amdgcn_raw_buffer_load_b128(rw, L.vc, row * L.sc, kStream);
+      r.a = load_scale<SF>(rw, L.va, row * L.sa);
+      if constexpr (K == 8) r.s = __builtin_amdgcn_raw_buffer_load_b32(rw, L.vs, row * L.ss, kStream);
+      if constexpr (K == 4) r.s = __builtin_amdgcn_raw_buffer_load_b16(rw, L.vs, row * L.ss, kStream);
+      if constexpr (K == 2) r.s = __builtin_amdgcn_raw_buffer_load_b8(rw, L.vs, row * L.ss, kStream);
+      if constexpr (K > 0) r.b = load_scale<SF>(rw, L.vb, row * L.sa);
     }
     const uint32_t ry = min(base + ((uint32_t)lane >> SH), row1 - 1);
-    B.u = __builtin_amdgcn_raw_buffer_load_b8(u_rs, uoff + ry * ustride, 0, kStream);
+    B.u = __builtin_amdgcn_raw_buffer_load_b8(ru, uoff + ry * ustride, 0, kStream);
     // keep the scheduler from sinking these loads into the next computation
     __builtin_amdgcn_sched_barrier(0);
     return B;
@@ -309,7 +346,7 @@ __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0,
       const uint32_t ry = min(row, row1 - 1);
       for (uint32_t t = ti + LPR; t < d.terms; t += LPR) {
         const uint32_t p = t / d.rank, r = t % d.rank;
-        const uint32_t byte = path_ptr(d.U, p)[(size_t)ry * L.ub + r / 8];
+        const uint32_t byte = path_plane(d.U, d, p)[(size_t)ry * L.ub + r / 8];
         const float zt = sm.z[t];
         c += ((byte >> (r & 7)) & 1u) ? -zt : zt;
       }
@@ -319,32 +356,37 @@ __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0,
       sm.ybuf[yi] = v;
   };
 
+  // Set-up loads first: the lane's x, the x of its share of the site table
+  // and the low-rank partials (L2 hits).  Vector memory loads complete in
+  // order, so waiting for these after the first batch's loads (HBM) are
+  // issued does not wait for the batch.
+  const __amdgpu_buffer_rsrc_t rx = x_rsrc<XT>(d.x, d.in);
+  typename XLane<XT>::Raw xr;
+  XLane<XT>::load_raw(rx, pass * kPass2bit + 64 * lane, xr);
+  TableX<XT> tx;
+  if constexpr (K > 0) tx.load(rx, pass * kPass2bit);
+  const bool zpass = pass == 0 && d.terms;
+  ZPart<ZP> zp;
+  if (zpass) z_prefetch<ZP>(d, threadIdx.x, zp);
+
   // Two batches in registers: while one is reduced, the next is in flight
   // (three resident workgroups per CU keep three wavefronts per SIMD, six
-  // batches, in flight).  Past the wave's last batch the prefetch repeats
-  // that batch (an L2 hit), keeping every load unconditional.
-  const uint32_t blast = has_rows ? wave + (nb - 1 - wave) / kWaves * kWaves : b;
-  auto ahead = [&](uint32_t bb) { return bb < nb ? bb : blast; };
+  // batches, in flight).
   Batch<RB> B0 = load_batch(b);
-  xl.load(d.x, pass * kPass2bit + 64 * lane, (uint32_t)(64 * lane) < pw);
 
   __syncthreads();   // readers of the previous table and z are done
-  if (pass == 0)
-    for (uint32_t t = threadIdx.x; t < d.terms; t += kThreads) {
-      float z = 0.f;
-      for (uint32_t cc = 0; cc < d.zc; ++cc) z += d.z[cc * d.terms + t];
-      sm.z[t] = z;
-    }
-  if constexpr (K > 0) build_table<XT>(d.x, pass * kPass2bit, pw, sm.tbl);
+  if (zpass && threadIdx.x < d.terms) sm.z[threadIdx.x] = z_total<ZP>(d, threadIdx.x, zp);
+  if constexpr (K > 0) tx.store(sm.tbl);
   __syncthreads();
   if (!has_rows) return;
+  xl.set(xr);
 
   for (;;) {
-    const Batch<RB> B1 = load_batch(ahead(b + kWaves));
+    const Batch<RB> B1 = load_batch(b + kWaves);
     finish_batch(B0, b);
     if (b + kWaves >= nb) break;
     b += kWaves;
-    B0 = load_batch(ahead(b + kWaves));
+    B0 = load_batch(b + kWaves);
     finish_batch(B1, b);
     if (b + kWaves >= nb) break;
     b += kWaves;
@@ -355,10 +397,11 @@ __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0,
 // SF and K are the matrix's scale format and sites per group: every
 // (scale format, k) class has kernels of its own, so the registers of the
 // hot fp16 / k = 8 loop are not set by the heavier fp24 loads.
-template <int XT, int SF, int K, int RB>
+template <int XT, int SF, int K, int RB, int ZP>
 __device__ __forceinline__ void run_segment_2bit(const MatDev& d, uint32_t row0, uint32_t row1, StreamSmem& sm) {
   const uint32_t npass = (d.in + kPass2bit - 1) / kPass2bit;
-  for (uint32_t pass = 0; pass < npass; ++pass) stream_rows_2bit<XT, SF, K, RB>(d, row0, row1, pass, npass, sm);
+  for (uint32_t pass = 0; pass < npass; ++pass)
+    stream_rows_2bit<XT, SF, K, RB, ZP>(d, row0, row1, pass, npass, sm);
   // y leaves through LDS: one coalesced write of the segment's rows instead
   // of a few scattered bytes per batch of rows.
   __syncthreads();
@@ -381,7 +424,7 @@ void k_stream_grouped(const MatDev* __restrict__ descs, const uint32_t* __restri
   const uint32_t s0 = blockseg[blockIdx.x], s1 = blockseg[blockIdx.x + 1];
   for (uint32_t s = s0; s < s1; ++s) {
     const Seg sg = segs[s];
-    run_segment_2bit<XT, SF, K, RB>(descs[sg.mat], sg.row0, sg.row1, sm);
+    run_segment_2bit<XT, SF, K, RB, 1>(descs[sg.mat], sg.row0, sg.row1, sm);
   }
 }
 
@@ -391,18 +434,19 @@ void k_stream_single(MatDev d, uint32_t rows_per_block) {
   __shared__ StreamSmem sm;
   const uint32_t r0 = blockIdx.x * rows_per_block;
   const uint32_t r1 = min(d.out, r0 + rows_per_block);
-  if (r0 < r1) run_segment_2bit<XT, SF, K, RB>(d, r0, r1, sm);
+  if (r0 < r1) run_segment_2bit<XT, SF, K, RB, kZSinglePrefetch>(d, r0, r1, sm);
 }
 
 // Low-rank partials of a single product: block (tc, cc) computes terms
-// 16 tc .. 16 tc + 15 over columns [4096 cc, 4096 cc + 4096) into
-// d.z[cc][t].
+// kZTerms tc .. kZTerms tc + kZTerms - 1 over columns [8192 cc, 8192 cc + 8192)
+// into d.z[cc][t].  Few terms per block keep each thread's share short: the
+// streaming kernel waits for this launch.
 template <int XT>
 __global__ __launch_bounds__(kThreads) void k_z_chunks(MatDev d) {
-  const uint32_t tcs = (d.terms + 15) / 16;
+  const uint32_t tcs = (d.terms + kZTerms - 1) / kZTerms;
   const uint32_t tc = blockIdx.x % tcs, cc = blockIdx.x / tcs;
-  const uint32_t c0 = cc * kZChunkCols, c1 = min(d.in, c0 + kZChunkCols);
-  z_chunk<XT, 16>(d, d.x, tc * 16, d.z + (size_t)cc * d.terms, c0, c1);
+  const uint32_t c0 = cc * kZSingleCols, c1 = min(d.in, c0 + kZSingleCols);
+  z_chunk<XT, (int)kZTerms>(d, d.x, tc * kZTerms, d.z + (size_t)cc * d.terms, c0, c1);
 }
 
 template <int XT>
@@ -434,12 +478,12 @@ MatDev make_dev(const wal_info* f, const void* W, const void* x, float* y, float
   m.sites = f->d.k ? base + f->off_sites : m.codes;
   m.alpha = base + f->off_alpha;
   m.beta = f->d.k ? base + f->off_beta : m.alpha;
-  for (uint32_t p = 0; p < WAL_MAX_PATHS; ++p) {
-    const bool on = p < f->d.n_paths;
-    m.V[p] = on ? base + f->off_V[p] : nullptr;
-    m.U[p] = on ? base + f->off_U[p] : nullptr;
-    m.s[p] = on ? base + f->off_s[p] : nullptr;
-  }
+  // check_info has verified the canonical layout: path planes at a fixed stride
+  const bool paths = f->d.n_paths > 0;
+  m.V = paths ? base + f->off_V[0] : m.codes;
+  m.U = paths ? base + f->off_U[0] : m.codes;
+  m.s = paths ? base + f->off_s[0] : m.codes;
+  m.pstride = f->d.n_paths > 1 ? (uint32_t)(f->off_V[1] - f->off_V[0]) : 0;
   m.x = x; m.y = y; m.z = z;
   m.out = f->d.out; m.in = f->d.in; m.k = f->d.k; m.n_paths = f->d.n_paths;
   m.rank = f->d.rank; m.scale_fmt = f->d.scale_fmt; m.row_stride = f->row_stride;
@@ -614,9 +658,9 @@ int wal_gemv(const wal_info* info, const void* W_dev, const void* x_dev, int x_d
   if (!single_for(x_dtype, cls)) return WAL_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   MatDev d = make_dev(info, W_dev, x_dev, y_dev, static_cast<float*>(ws_dev), info->d.in, info->d.out, 1);
-  d.zc = S.zc;
+  d.zc = (info->d.in + kZSingleCols - 1) / kZSingleCols;   // at most S.zc partials
   if (d.terms) {
-    const uint32_t g = (d.terms + 15) / 16 * S.zc;
+    const uint32_t g = (d.terms + kZTerms - 1) / kZTerms * d.zc;
     if (x_dtype == WAL_X_BF16) hipLaunchKernelGGL(k_z_chunks<WAL_X_BF16>, dim3(g), dim3(kThreads), 0, s, d);
     else hipLaunchKernelGGL(k_z_chunks<WAL_X_F32>, dim3(g), dim3(kThreads), 0, s, d);
     if ((st = launch_status())) return st;

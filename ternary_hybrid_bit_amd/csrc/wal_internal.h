@@ -16,9 +16,13 @@ struct MatDev {
   const uint8_t* sites;
   const uint8_t* alpha;
   const uint8_t* beta;
-  const uint8_t* V[WAL_MAX_PATHS];
-  const uint8_t* U[WAL_MAX_PATHS];
-  const uint8_t* s[WAL_MAX_PATHS];
+  // Low-rank path 0's planes; path p's are pstride bytes further per path
+  // (every path's V, U and s planes have the same sizes, and the blob layout
+  // places them one path after another).
+  const uint8_t* V;
+  const uint8_t* U;
+  const uint8_t* s;
+  uint32_t pstride;
   const void* x;       // [batch][ldx] activations
   float* y;            // [batch][ldy] outputs
   float* z;            // workspace: diag(s_p) V_p^T x, zc partial sums over
@@ -58,6 +62,7 @@ constexpr uint32_t kSegRows = 4096;
 // Low-rank terms handled per workgroup of the V^T x pre-passes.
 constexpr uint32_t kZTerms = 4;
 constexpr uint32_t kMaxTerms = WAL_MAX_PATHS * WAL_MAX_RANK;
+static_assert(kMaxTerms <= kThreads, "one low-rank term per thread of a streaming workgroup");
 
 // Streaming kernels as host-side launch targets.
 struct Seg;
@@ -76,7 +81,11 @@ using SingleFn = void (*)(MatDev, uint32_t);
 //    finishes its Y in LDS (no workspace).
 constexpr uint32_t kGemvRows = 8;
 constexpr uint32_t kGemvCols = 4;
-constexpr uint32_t kZChunkCols = 4096;   // columns per low-rank partial
+constexpr uint32_t kZChunkCols = 4096;   // columns per low-rank partial (small batch)
+// Single products: columns per low-rank partial, and the partials a streaming
+// workgroup prefetches (more are added after the set-up barrier).
+constexpr uint32_t kZSingleCols = 8192;
+constexpr int kZSinglePrefetch = 4;
 constexpr uint32_t kZTermsPerBlock = 16;
 struct GemmShape {
   uint32_t nt, passes, zc;   // n-tiles, GEMV passes (= P planes), z chunks
