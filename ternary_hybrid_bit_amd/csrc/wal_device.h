@@ -178,15 +178,19 @@ __device__ __forceinline__ void z_chunk(const MatDev& d, const void* x, uint32_t
   const uint32_t T = d.terms, vrow = d.in / 8;
   // the per-rank scale of the thread's term, loaded before the sweep so its
   // latency is not paid after the barrier
-  float scale = 0.f;
-  if (tid < (uint32_t)C && t0 + tid < T) {
-    const uint32_t p = (t0 + tid) / d.rank, r = (t0 + tid) % d.rank;
-    scale = f16_at(path_plane(d.s, d, p), r);
+  // (every thread loads a valid scale, without a branch, so that nothing
+  // waits for it before the end)
+  uint32_t scale_bits;
+  {
+    const uint32_t t = min(t0 + (tid < (uint32_t)C ? tid : 0u), T - 1);
+    const uint32_t p = t / d.rank, r = t % d.rank;
+    scale_bits = reinterpret_cast<const uint16_t*>(path_plane(d.s, d, p))[r];
   }
   float acc[C];
 #pragma unroll
   for (int q = 0; q < C; ++q) acc[q] = 0.f;
-  for (uint32_t c = c0 + tid * 16; c < c1; c += nthr * 16) {
+  // columns c .. c + 15 of the C terms
+  auto step = [&](uint32_t c) {
     uint32_t xb[16];   // fp32 bit patterns of x[c .. c + 15]
     if constexpr (XT == WAL_X_BF16) {
       const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + c);
@@ -205,18 +209,29 @@ __device__ __forceinline__ void z_chunk(const MatDev& d, const void* x, uint32_t
         xb[4 * k] = v.x; xb[4 * k + 1] = v.y; xb[4 * k + 2] = v.z; xb[4 * k + 3] = v.w;
       }
     }
+    // the sign words of all C terms first (terms past the last one read the
+    // last term's word, unused), so their latencies overlap
+    uint32_t bits[C];
 #pragma unroll
     for (int q = 0; q < C; ++q) {
-      const uint32_t t = t0 + q;
-      if (t < T) {
-        const uint32_t p = t / d.rank, r = t % d.rank;
-        const uint32_t bits = reinterpret_cast<const uint16_t*>(path_plane(d.V, d, p) + (size_t)r * vrow)[c / 16];
+      const uint32_t t = min(t0 + q, T - 1);
+      const uint32_t p = t / d.rank, r = t % d.rank;
+      bits[q] = reinterpret_cast<const uint16_t*>(path_plane(d.V, d, p) + (size_t)r * vrow)[c / 16];
+    }
+#pragma unroll
+    for (int q = 0; q < C; ++q) {
+      if (t0 + q < T) {
         // a set bit flips the sign of x_j
 #pragma unroll
-        for (int j = 0; j < 16; ++j) acc[q] += __uint_as_float(xb[j] ^ ((bits << (31 - j)) & 0x80000000u));
+        for (int j = 0; j < 16; ++j) acc[q] += __uint_as_float(xb[j] ^ ((bits[q] << (31 - j)) & 0x80000000u));
       }
     }
-  }
+  };
+  // The first step is written out before the loop: its loads then follow
+  // the scale's at once (a loop head would wait for every load in flight).
+  uint32_t c = c0 + tid * 16;
+  if (c < c1) step(c);
+  for (c += nthr * 16; c < c1; c += nthr * 16) step(c);
   const float tot = treduce<C>(acc, lane);
   constexpr int SH = 6 - ilog2(C);
   if ((lane & ((1 << SH) - 1)) == 0) red[tid >> 6][lane >> SH] = tot;
@@ -226,7 +241,7 @@ __device__ __forceinline__ void z_chunk(const MatDev& d, const void* x, uint32_t
     if (t < T) {
       float sum = 0.f;
       for (uint32_t w = 0; w < (nthr >> 6); ++w) sum += red[w][tid];
-      out[t] = scale * sum;
+      out[t] = (float)__builtin_bit_cast(_Float16, (uint16_t)scale_bits) * sum;
     }
   }
 }

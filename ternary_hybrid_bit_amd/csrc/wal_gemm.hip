@@ -17,9 +17,10 @@
 //     of every batch column per 4096-column chunk, zpart[chunk][n][t];
 //  2. k_reduce adds the passes and the chunks in a fixed order, adds the
 //     low-rank term and stores Y.
-// MFMA (k_mfma, matrix cores), one launch: one workgroup per 16-row tile; its
-// wavefronts split the tile's 128-column groups, and each group is a few
-// v_mfma_f32_16x16x32_bf16 over 16 rows x 16 batch columns x 32 columns.  A
+// MFMA (k_mfma, matrix cores), then k_reduce: one workgroup per 16-row tile
+// and 4096-column slice; its wavefronts take four 128-column groups each, and
+// each group is a few v_mfma_f32_16x16x32_bf16 over 16 rows x 16 batch
+// columns x 32 columns.  A
 // lane (row i = lane & 15, K block kb = lane >> 4) decodes its 8 code bytes
 // straight into A operands; the group's sites are scattered as +-2 into a
 // per-wavefront LDS tile in operand order, read back as a second A operand
@@ -27,11 +28,12 @@
 // with byte permutes.  The two group sums land in separate accumulators that
 // alpha and beta scale in fp32.  V enters as a third, +-1 A operand on the
 // same B operands, which gives the low-rank reductions z of the tile's
-// columns; the wavefronts' sums meet in LDS, where the workgroup finishes Y.
-// Every weight load of a wavefront is issued before it touches X, so the HBM
-// latency is paid once.  Decoded values are exact in bf16 and every product
-// and sum is fp32, so x = e_j still gives column j of W exactly, and every
-// sum runs in a fixed order: results do not depend on timing.
+// columns; the wavefronts' sums meet in LDS, and the workgroup writes its
+// slice's partial sums, which k_reduce adds.  Every weight load of a wavefront
+// is issued before it touches X, so the HBM latency is paid once.  Decoded
+// values are exact in bf16 and every product and sum is fp32, so x = e_j
+// still gives column j of W exactly, and every sum runs in a fixed order:
+// results do not depend on timing.
 #include <hip/hip_runtime.h>
 
 #include "wal_device.h"
@@ -76,26 +78,58 @@ uint32_t z_blocks(const MatDev& d, const GemmShape& S) {
 
 // Y[n][row] = sum over K slices of the partials (in slice order) + the
 // low-rank term with z[n][t] = sum over chunks of zpart (in chunk order).
+// Every load is issued before the first sum, so the kernel pays one memory
+// latency, not one per slice, chunk or U byte.
+constexpr uint32_t kReduceSlices = 4;   // partial slices loaded ahead (more: a loop)
+constexpr uint32_t kReduceChunks = 8;   // z chunks loaded ahead
+
 __global__ __launch_bounds__(256) void k_reduce(MatDev d, const float* __restrict__ zpart,
                                                 const float* __restrict__ P, uint32_t slices, uint32_t zc) {
   __shared__ float zs[kMaxTerms];
   const uint32_t n = blockIdx.y, row = blockIdx.x * 256 + threadIdx.x;
-  for (uint32_t t = threadIdx.x; t < d.terms; t += 256) {
-    float z = 0.f;
-    for (uint32_t cc = 0; cc < zc; ++cc) z += zpart[((size_t)cc * d.batch + n) * d.terms + t];
+  const uint32_t rr = min(row, d.out - 1);
+  const size_t plane = (size_t)d.batch * d.out, at = (size_t)n * d.out + rr;
+  float pv[kReduceSlices];
+#pragma unroll
+  for (uint32_t s = 0; s < kReduceSlices; ++s) pv[s] = s < slices ? P[s * plane + at] : 0.f;
+  const uint32_t ub = (d.rank + 7) / 8;   // at most 8
+  uint32_t ubyte[WAL_MAX_PATHS][8];
+#pragma unroll
+  for (uint32_t p = 0; p < WAL_MAX_PATHS; ++p)
+#pragma unroll
+    for (uint32_t j = 0; j < 8; ++j)
+      ubyte[p][j] = p < d.n_paths && j < ub ? path_plane(d.U, d, p)[(size_t)rr * ub + j] : 0u;
+  uint64_t ubits[WAL_MAX_PATHS];   // the row's U bits of path p, rank r at bit r
+#pragma unroll
+  for (uint32_t p = 0; p < WAL_MAX_PATHS; ++p) {
+    ubits[p] = 0;
+#pragma unroll
+    for (uint32_t j = 0; j < 8; ++j) ubits[p] |= (uint64_t)ubyte[p][j] << (8 * j);
+  }
+  const uint32_t t = threadIdx.x;
+  float zv[kReduceChunks];
+#pragma unroll
+  for (uint32_t cc = 0; cc < kReduceChunks; ++cc)
+    zv[cc] = t < d.terms && cc < zc ? zpart[((size_t)cc * d.batch + n) * d.terms + t] : 0.f;
+  if (t < d.terms) {
+    float z = zv[0];
+#pragma unroll
+    for (uint32_t cc = 1; cc < kReduceChunks; ++cc) z += zv[cc];
+    for (uint32_t cc = kReduceChunks; cc < zc; ++cc) z += zpart[((size_t)cc * d.batch + n) * d.terms + t];
     zs[t] = z;
   }
   __syncthreads();
   if (row >= d.out) return;
-  const size_t plane = (size_t)d.batch * d.out;
-  float v = 0.f;
-  for (uint32_t s = 0; s < slices; ++s) v += P[s * plane + (size_t)n * d.out + row];
-  const uint32_t ub = (d.rank + 7) / 8;
-  for (uint32_t p = 0; p < d.n_paths; ++p) {
-    const uint8_t* u = path_plane(d.U, d, p) + (size_t)row * ub;
+  float v = pv[0];
+#pragma unroll
+  for (uint32_t s = 1; s < kReduceSlices; ++s) v += pv[s];
+  for (uint32_t s = kReduceSlices; s < slices; ++s) v += P[s * plane + at];
+#pragma unroll
+  for (uint32_t p = 0; p < WAL_MAX_PATHS; ++p) {
+    if (p >= d.n_paths) break;
     for (uint32_t r = 0; r < d.rank; ++r) {
       const float zt = zs[p * d.rank + r];
-      v += ((u[r >> 3] >> (r & 7)) & 1u) ? -zt : zt;
+      v += ((ubits[p] >> r) & 1u) ? -zt : zt;
     }
   }
   d.y[(size_t)n * d.ldy + row] = v;
@@ -294,32 +328,35 @@ __device__ __forceinline__ void a_operands(uint64_t q, uint4 (&a)[4]) {
   if constexpr (I < 7) a_operands<I + 1>(q, a);
 }
 
-// Wavefronts per workgroup of k_mfma (at most) and group slots per sweep.
-template <int NT>
-constexpr uint32_t mfma_max_waves() { return NT == 1 ? 12 : 8; }
+// Group slots per sweep, and wavefronts per workgroup of k_mfma: one sweep
+// each over a 4096-column slice (32 groups).
 constexpr uint32_t kSlots = 4;
+constexpr uint32_t kMfmaWaves = (kPass2bit / 128) / kSlots;
 
-// Block b < tiles: one 16-row tile over all columns; its wavefronts take gpw
-// consecutive groups each (kSlots per sweep) and are summed in LDS into
-// P[0][n][row] = 0.5 sum_waves (alpha sT + beta sR) (decoded values are 2x).
-// Blocks past the tiles: low-rank partials (z_block).
+// Block b < tiles * slices: 16-row tile b / slices over the 4096-column slice
+// b % slices; wavefront w takes groups 4 w .. 4 w + 3 of the slice, and the
+// wavefronts are summed in LDS into P[slice][n][row] = 0.5 sum_waves (alpha
+// sT + beta sR) (decoded values are 2x).  Splitting the columns over
+// workgroups keeps each wavefront's chain of dependent steps to one sweep.
+// Blocks past them: low-rank partials (z_block).
 template <int SF, int K, int NT>
-__global__ __launch_bounds__(mfma_max_waves<NT>() * 64) void k_mfma(MatDev d, float* __restrict__ P,
-                                                                      float* __restrict__ zpart, uint32_t tiles,
-                                                                      uint32_t gpw) {
-  if (blockIdx.x >= tiles) {
-    z_block(d, zpart, blockIdx.x - tiles);
+__global__ __launch_bounds__(kMfmaWaves * 64) void k_mfma(MatDev d, float* __restrict__ P, float* __restrict__ zpart,
+                                                           uint32_t tiles, uint32_t slices) {
+  if (blockIdx.x >= tiles * slices) {
+    z_block(d, zpart, blockIdx.x - tiles * slices);
     return;
   }
-  constexpr uint32_t MW = mfma_max_waves<NT>();
-  // per-wavefront R tiles during the sweeps, then the wavefront partials
+  constexpr uint32_t MW = kMfmaWaves;
+  // per-wavefront R tiles during the sweep, then the wavefront partials
   __shared__ __align__(16) uint8_t lds[MW * 4096 > MW * NT * 1024 ? MW * 4096 : MW * NT * 1024];
   const uint32_t nw = blockDim.x >> 6;
   const int lane = threadIdx.x & 63;
   const uint32_t wave = wave_id();
-  const uint32_t row_base = blockIdx.x * 16;
+  const uint32_t tile = blockIdx.x / slices, slice = blockIdx.x % slices;
+  const uint32_t row_base = tile * 16;
   const uint32_t G = d.groups;
-  const uint32_t gw0 = min(G, wave * gpw), gw1 = min(G, gw0 + gpw);
+  const uint32_t gs0 = slice * (kPass2bit / 128);
+  const uint32_t gw0 = min(G, gs0 + wave * kSlots), gw1 = min(G, gw0 + kSlots);
   constexpr uint32_t SB = SF == WAL_SCALE_FP16 ? 2 : 3;
   const uint32_t i = lane & 15, kb = lane >> 4;
   const uint32_t row = min(row_base + i, d.out - 1);
@@ -393,15 +430,19 @@ __global__ __launch_bounds__(mfma_max_waves<NT>() * 64) void k_mfma(MatDev d, fl
       if constexpr (K == 2)
         sbytes[q] = __builtin_amdgcn_raw_buffer_load_b8(rs, (row * G + g) * 2 + (kb & 1), 0, kCached);
     }
-    uint4 xnext[NT][4];
-    load_x(min(c0, G - 1), xnext);
+    // X of the sweep's groups: all four slots at once for one n-tile, one
+    // slot ahead for two (registers)
+    constexpr uint32_t XA = NT == 1 ? kSlots : 1;
+    uint4 xpre[XA][NT][4];
+#pragma unroll
+    for (uint32_t q = 0; q < XA; ++q) load_x(min(c0 + q, G - 1), xpre[q]);
 #pragma unroll
     for (uint32_t q = 0; q < kSlots; ++q) {
       const bool valid = q < ns;   // wave-uniform
       uint4 xb[NT][4];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) x_operands(xnext[t], xb[t]);
-      if (q + 1 < kSlots) load_x(min(c0 + q + 1, G - 1), xnext);
+      for (int t = 0; t < NT; ++t) x_operands(xpre[NT == 1 ? q : 0][t], xb[t]);
+      if (NT != 1 && q + 1 < kSlots) load_x(min(c0 + q + 1, G - 1), xpre[0]);
       // T operands: one 64-bit shift positions the code pairs of both dwords
       uint4 a[4];
       const uint64_t cq = ((uint64_t)cw[q / 2][2 * (q & 1) + 1] << 32) | cw[q / 2][2 * (q & 1)];
@@ -472,7 +513,7 @@ __global__ __launch_bounds__(mfma_max_waves<NT>() * 64) void k_mfma(MatDev d, fl
     const uint32_t L = (r >> 2) * 16 + (n & 15);
     float v = 0.f;
     for (uint32_t w = 0; w < nw; ++w) v += red[(w * NT + (n >> 4)) * 64 + L][r & 3];
-    P[(size_t)n * d.out + yr] = 0.5f * v;
+    P[((size_t)slice * d.batch + n) * d.out + yr] = 0.5f * v;
   }
 }
 
@@ -493,10 +534,11 @@ void launch_gemv_nb(uint32_t nb, dim3 grid, hipStream_t s, const MatDev& d, floa
 }
 
 template <int SF, int K>
-void launch_mfma_nt(uint32_t nt, dim3 grid, uint32_t nw, hipStream_t s, const MatDev& d, float* P, float* zp,
-                    uint32_t tiles, uint32_t gpw) {
-  if (nt == 1) hipLaunchKernelGGL((k_mfma<SF, K, 1>), grid, dim3(64 * nw), 0, s, d, P, zp, tiles, gpw);
-  else hipLaunchKernelGGL((k_mfma<SF, K, 2>), grid, dim3(64 * nw), 0, s, d, P, zp, tiles, gpw);
+void launch_mfma_nt(uint32_t nt, dim3 grid, hipStream_t s, const MatDev& d, float* P, float* zp, uint32_t tiles,
+                    uint32_t slices) {
+  const dim3 block(64 * kMfmaWaves);
+  if (nt == 1) hipLaunchKernelGGL((k_mfma<SF, K, 1>), grid, block, 0, s, d, P, zp, tiles, slices);
+  else hipLaunchKernelGGL((k_mfma<SF, K, 2>), grid, block, 0, s, d, P, zp, tiles, slices);
 }
 
 int launch_reduce(const MatDev& d, const GemmShape& S, const float* zp, const float* P, uint32_t slices,
@@ -540,25 +582,21 @@ int launch_gemm_mfma(const wal_info& f, const MatDev& d, uint32_t batch, void* w
   float* zp = reinterpret_cast<float*>(w + S.off_z);
   float* P = reinterpret_cast<float*>(w + S.off_p);
   const uint32_t nt = (batch + 15) / 16;
-  const uint32_t maxw = nt == 1 ? mfma_max_waves<1>() : mfma_max_waves<2>();
-  // groups per wavefront: a multiple of the sweep's slots, as few
-  // wavefronts as that allows
-  uint32_t gpw = (f.groups + maxw - 1) / maxw;
-  gpw = (gpw + kSlots - 1) / kSlots * kSlots;
-  const uint32_t nw = (f.groups + gpw - 1) / gpw;
-  const uint32_t tiles = (f.d.out + 15) / 16;
-  const dim3 grid(tiles + z_blocks(d, S));
+  // one workgroup per (16-row tile, 4096-column slice): the slices are the
+  // workspace's per-pass partial planes
+  const uint32_t tiles = (f.d.out + 15) / 16, slices = S.passes;
+  const dim3 grid(tiles * slices + z_blocks(d, S));
   switch (class_index(d)) {
-    case 0: launch_mfma_nt<WAL_SCALE_FP16, 0>(nt, grid, nw, s, d, P, zp, tiles, gpw); break;
-    case 1: launch_mfma_nt<WAL_SCALE_FP16, 2>(nt, grid, nw, s, d, P, zp, tiles, gpw); break;
-    case 2: launch_mfma_nt<WAL_SCALE_FP16, 4>(nt, grid, nw, s, d, P, zp, tiles, gpw); break;
-    case 3: launch_mfma_nt<WAL_SCALE_FP16, 8>(nt, grid, nw, s, d, P, zp, tiles, gpw); break;
-    case 4: launch_mfma_nt<WAL_SCALE_FP24, 0>(nt, grid, nw, s, d, P, zp, tiles, gpw); break;
-    case 5: launch_mfma_nt<WAL_SCALE_FP24, 2>(nt, grid, nw, s, d, P, zp, tiles, gpw); break;
-    case 6: launch_mfma_nt<WAL_SCALE_FP24, 4>(nt, grid, nw, s, d, P, zp, tiles, gpw); break;
-    default: launch_mfma_nt<WAL_SCALE_FP24, 8>(nt, grid, nw, s, d, P, zp, tiles, gpw); break;
+    case 0: launch_mfma_nt<WAL_SCALE_FP16, 0>(nt, grid, s, d, P, zp, tiles, slices); break;
+    case 1: launch_mfma_nt<WAL_SCALE_FP16, 2>(nt, grid, s, d, P, zp, tiles, slices); break;
+    case 2: launch_mfma_nt<WAL_SCALE_FP16, 4>(nt, grid, s, d, P, zp, tiles, slices); break;
+    case 3: launch_mfma_nt<WAL_SCALE_FP16, 8>(nt, grid, s, d, P, zp, tiles, slices); break;
+    case 4: launch_mfma_nt<WAL_SCALE_FP24, 0>(nt, grid, s, d, P, zp, tiles, slices); break;
+    case 5: launch_mfma_nt<WAL_SCALE_FP24, 2>(nt, grid, s, d, P, zp, tiles, slices); break;
+    case 6: launch_mfma_nt<WAL_SCALE_FP24, 4>(nt, grid, s, d, P, zp, tiles, slices); break;
+    default: launch_mfma_nt<WAL_SCALE_FP24, 8>(nt, grid, s, d, P, zp, tiles, slices); break;
   }
-  return launch_reduce(d, S, zp, P, 1, s);
+  return launch_reduce(d, S, zp, P, slices, s);
 }
 
 }  // namespace wal
