@@ -18,7 +18,7 @@ repeated, untimed, for --settle-s seconds (default 1 s).
 ``--workload config1|config3|config4`` instead measures the single-matrix
 configurations (one JSON line each, no contract fields): config 1 is the
 12288x4096 gate shape through wal_gemv, config 3 the 4096x12288 down shape
-through wal_gemm_small with both kernels at batch 1, 2, 4, 5, 8, 16 and 32
+through wal_gemm_small with both kernels at batch 1, 2, 3, 4, 5, 8, 16 and 32
 (and the batch from which the matrix-core kernel is faster), config 4 the two
 base-3 / fp24 27B shapes through wal_gemv.  Each call reads one of about
 1 GB of distinct packed copies in turn, so the 256 MB Infinity Cache cannot
@@ -229,7 +229,7 @@ def run_single(args):
     Y = torch.empty((32, info.d.out), dtype=torch.float32, device=dev)
     ws = torch.empty(wal.wal_workspace_size(info, 32) // 4 + 64, dtype=torch.float32, device=dev)
     rows = []
-    for B in (1, 2, 4, 5, 8, 16, 32):
+    for B in (1, 2, 3, 4, 5, 8, 16, 32):
         row = {"batch": B}
         for name, mode in (("valu", wal.WAL_GEMM_VALU), ("mfma", wal.WAL_GEMM_MFMA)):
             us = time_calls(torch, lambda i: wal.wal_gemm_small(info, Ws[i % len(Ws)], X[:B], Y[:B], mode, ws),

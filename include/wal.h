@@ -184,9 +184,10 @@ int wal_unpack(const void* blob, size_t bytes, int8_t* T, uint8_t* site_pos,
 
 /* Device workspace that wal_gemv and wal_gemm_small need for a blob and
  * batch: the per-path reductions z_p = diag(s_p) V_p^T X per 4096-column
- * chunk [chunks][batch][n_paths * rank] and the batched GEMV's per-pass
- * partial sums [passes][batch][out] (fp32), each part padded to 256 bytes.
- * wal_gemv uses the first part only.  Errors: ARG, SHAPE, FORMAT. */
+ * chunk [chunks][batch][n_paths * rank] and the small-batch kernels' partial
+ * sums per 1024-column slice [ceil(in / 1024)][batch][out] (fp32), each part
+ * padded to 256 bytes.  wal_gemv uses the first part only.
+ * Errors: ARG, SHAPE, FORMAT. */
 int wal_workspace_size(const wal_info* info, uint32_t batch, size_t* bytes);
 
 /* y = W(x) for one matrix, batch 1 (WAL-Ternary-8B cards, "Representation":
@@ -210,7 +211,8 @@ int wal_gemv(const wal_info* info, const void* W_dev, const void* x_dev, int x_d
  *   mode   WAL_GEMM_VALU (batched GEMV: one decode of a row feeds every batch
  *          column on the vector ALUs), WAL_GEMM_MFMA (trits decoded to bf16
  *          operands of matrix-core MFMA, alpha / beta applied per group in
- *          fp32) or WAL_GEMM_AUTO (MFMA from a measured crossover batch on).
+ *          fp32) or WAL_GEMM_AUTO (MFMA from a measured crossover batch on,
+ *          the batched GEMV below it, the single-product path at batch 1).
  *          Both batched kernels take bf16 X and 2-bit codes; fp32 X or
  *          base-3 codes run one wal_gemv per row with WAL_GEMM_VALU / AUTO,
  *          and WAL_GEMM_MFMA returns WAL_ERR_UNSUPPORTED for them.

@@ -57,6 +57,26 @@ __device__ __forceinline__ uint32_t load_sites(__amdgpu_buffer_rsrc_t r, uint32_
   return __builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, kStream);
 }
 
+// Raw scale bits at byte offset `off` of a resource (fp16: 2 bytes, fp24: 3);
+// out of range: 0.
+template <int SF>
+__device__ __forceinline__ uint32_t load_scale_raw(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (SF == WAL_SCALE_FP16) return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0) |
+         ((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, off + 1, 0, 0) << 8) |
+         ((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, off + 2, 0, 0) << 16);
+}
+
+// Lane n of each row of 16 lanes, to the whole row (DPP row_newbcast).
+__device__ __forceinline__ uint32_t row_bcast(uint32_t v, uint32_t n) {
+  switch (n) {
+#define WAL_BC(N) case N: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x150 + N, 0xF, 0xF, false);
+    WAL_BC(0) WAL_BC(1) WAL_BC(2) WAL_BC(3) WAL_BC(4) WAL_BC(5) WAL_BC(6) WAL_BC(7)
+    WAL_BC(8) WAL_BC(9) WAL_BC(10) WAL_BC(11) WAL_BC(12) WAL_BC(13) WAL_BC(14) default: WAL_BC(15)
+#undef WAL_BC
+  }
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 
@@ -80,7 +100,7 @@ uint32_t z_blocks(const MatDev& d, const GemmShape& S) {
 // low-rank term with z[n][t] = sum over chunks of zpart (in chunk order).
 // Every load is issued before the first sum, so the kernel pays one memory
 // latency, not one per slice, chunk or U byte.
-constexpr uint32_t kReduceSlices = 4;   // partial slices loaded ahead (more: a loop)
+constexpr uint32_t kReduceSlices = 16;  // partial slices loaded ahead (more: a loop)
 constexpr uint32_t kReduceChunks = 8;   // z chunks loaded ahead
 
 __global__ __launch_bounds__(256) void k_reduce(MatDev d, const float* __restrict__ zpart,
@@ -328,71 +348,89 @@ __device__ __forceinline__ void a_operands(uint64_t q, uint4 (&a)[4]) {
   if constexpr (I < 7) a_operands<I + 1>(q, a);
 }
 
-// Group slots per sweep, and wavefronts per workgroup of k_mfma: one sweep
-// each over a 4096-column slice (32 groups).
+// k_mfma's work split: a workgroup of kMfmaTiles wavefronts takes kMfmaTiles
+// 16-row tiles (one per wavefront) and one slice of kSliceCols columns; the
+// slice is swept kSlots 128-column groups at a time (kSweeps sweeps).  Every wavefront needs
+// the same X for a sweep, so the workgroup stages it once in LDS and each
+// wavefront reads its B operands from there: X crosses from L2 once per
+// kMfmaTiles tiles instead of once per tile.
 constexpr uint32_t kSlots = 4;
-constexpr uint32_t kMfmaWaves = (kPass2bit / 128) / kSlots;
+constexpr uint32_t kSweeps = kSliceCols / 128 / kSlots;
+constexpr uint32_t kMfmaTiles = 8;
+constexpr uint32_t kMfmaWaves = kMfmaTiles;
 
-// Block b < tiles * slices: 16-row tile b / slices over the 4096-column slice
-// b % slices; wavefront w takes groups 4 w .. 4 w + 3 of the slice, and the
-// wavefronts are summed in LDS into P[slice][n][row] = 0.5 sum_waves (alpha
-// sT + beta sR) (decoded values are 2x).  Splitting the columns over
-// workgroups keeps each wavefront's chain of dependent steps to one sweep.
-// Blocks past them: low-rank partials (z_block).
+// X rows 16 t .. 16 t + 15 of one sweep in LDS: [t][n][kSlots * 128 columns]
+// bf16 (rows padded by 16 bytes, so that the 16 rows a B-operand read touches
+// start in different banks), about 16 KB per n-tile.  Thread j loads 32 bytes
+// of row (j >> 5) per n-tile.
+template <int NT>
+struct XStage {
+  static constexpr uint32_t kRowBytes = kSlots * 128 * 2 + 16;
+  u32x4_t v[NT][2];
+
+  // X[n][128 c0 + 16 (j & 31) .. + 16], zero past the row's end; rows past
+  // the batch read row 0 (such B-operand columns only feed unused outputs).
+  __device__ __forceinline__ void load(const MatDev& d, __amdgpu_buffer_rsrc_t rx, uint32_t c0) {
+    const uint32_t j = threadIdx.x, r = j >> 5, col = 128 * c0 + 16 * (j & 31);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const uint32_t n = 16 * t + r;
+      const uint32_t off = col < d.in ? 2 * ((n < d.batch ? n : 0) * d.ldx + col) : 0x7FFFFFF0u;
+      v[t][0] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+      v[t][1] = __builtin_amdgcn_raw_buffer_load_b128(rx, off + 16, 0, 0);
+    }
+  }
+
+  __device__ __forceinline__ void store(uint8_t* xs) const {
+    const uint32_t j = threadIdx.x;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      u32x4_t* dst = reinterpret_cast<u32x4_t*>(xs + (t * 16 + (j >> 5)) * kRowBytes + 32 * (j & 31));
+      dst[0] = v[t][0];
+      dst[1] = v[t][1];
+    }
+  }
+};
+
+// The first nz blocks compute the low-rank partials (z_block), so that they
+// run alongside the rest.  Block nz + b: row block b / slices (kMfmaTiles
+// tiles, tile w to wavefront w) over column slice b % slices.  Wavefront w
+// writes P[slice][n][row] = 0.5 sum over the slice's groups (alpha sT + beta
+// sR) for its tile (decoded values are 2x).
 template <int SF, int K, int NT>
 __global__ __launch_bounds__(kMfmaWaves * 64) void k_mfma(MatDev d, float* __restrict__ P, float* __restrict__ zpart,
-                                                           uint32_t tiles, uint32_t slices) {
-  if (blockIdx.x >= tiles * slices) {
-    z_block(d, zpart, blockIdx.x - tiles * slices);
+                                                           uint32_t nz, uint32_t slices) {
+  if (blockIdx.x < nz) {
+    z_block(d, zpart, blockIdx.x);
     return;
   }
-  constexpr uint32_t MW = kMfmaWaves;
-  // per-wavefront R tiles during the sweep, then the wavefront partials
-  __shared__ __align__(16) uint8_t lds[MW * 4096 > MW * NT * 1024 ? MW * 4096 : MW * NT * 1024];
-  const uint32_t nw = blockDim.x >> 6;
+  static_assert(kMfmaWaves * 64 == 512 && kSlots * 128 * 2 == 32 * 32, "XStage: 32 threads of 32 bytes per X row");
+  __shared__ __align__(16) uint8_t xs[NT * 16 * XStage<NT>::kRowBytes];
+  __shared__ __align__(16) uint8_t rts[kMfmaWaves * 4096];   // per-wavefront R tiles
   const int lane = threadIdx.x & 63;
   const uint32_t wave = wave_id();
-  const uint32_t tile = blockIdx.x / slices, slice = blockIdx.x % slices;
-  const uint32_t row_base = tile * 16;
+  const uint32_t rb = (blockIdx.x - nz) / slices, slice = (blockIdx.x - nz) % slices;
+  const uint32_t row_base = (rb * kMfmaTiles + wave) * 16;
   const uint32_t G = d.groups;
-  const uint32_t gs0 = slice * (kPass2bit / 128);
-  const uint32_t gw0 = min(G, gs0 + wave * kSlots), gw1 = min(G, gw0 + kSlots);
+  const uint32_t gs0 = slice * (kSliceCols / 128), gs1 = min(G, gs0 + kSliceCols / 128);
   constexpr uint32_t SB = SF == WAL_SCALE_FP16 ? 2 : 3;
   const uint32_t i = lane & 15, kb = lane >> 4;
   const uint32_t row = min(row_base + i, d.out - 1);
-  uint4* rt4 = reinterpret_cast<uint4*>(lds + wave * 4096);
-  uint16_t* rt16 = reinterpret_cast<uint16_t*>(lds + wave * 4096);
-  f32x4_t* red = reinterpret_cast<f32x4_t*>(lds);
+  uint4* rt4 = reinterpret_cast<uint4*>(rts + wave * 4096);
+  uint16_t* rt16 = reinterpret_cast<uint16_t*>(rts + wave * 4096);
 
   const __amdgpu_buffer_rsrc_t rc = rsrc(d.codes, d.blob_bytes);
-  // one resource over the alpha and beta planes: lanes 0-15 fetch alpha of
-  // tile row (lane & 15), lanes 16-31 its beta (a per-lane offset, so the
-  // resource stays uniform)
+  // one resource over the alpha and beta planes (beta at a fixed offset)
   const __amdgpu_buffer_rsrc_t ra = rsrc(d.alpha, d.blob_bytes - (uint32_t)(d.alpha - d.codes));
-  const uint32_t sbase = (K > 0 && lane >= 16) ? (uint32_t)(d.beta - d.alpha) : 0u;
+  const uint32_t boff = K > 0 ? (uint32_t)(d.beta - d.alpha) : 0u;
   __amdgpu_buffer_rsrc_t rs = rsrc(d.codes, 0u);
   if constexpr (K > 0) rs = rsrc(d.sites, d.blob_bytes - (uint32_t)(d.sites - d.codes));
+  const __amdgpu_buffer_rsrc_t rx =
+      rsrc(d.x, 2 * ((d.batch - 1) * d.ldx + d.in));
   // The weight loads read 8 to 32 bytes per row and instruction; the rest of
-  // each cache line is read moments later by the next slots or wavefronts,
-  // so they keep the default cache policy (the lines stay in L2).
+  // each cache line is read moments later by the next slots, so they keep the
+  // default cache policy (the lines stay in L2).
   constexpr int kCached = 0;
-
-  // X rows of the lane's batch columns (columns past the batch read row 0:
-  // a B-operand column only feeds its own output column, never stored)
-  const uint16_t* xr[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const uint32_t n = 16 * t + i;
-    xr[t] = reinterpret_cast<const uint16_t*>(d.x) + (size_t)(n < d.batch ? n : 0) * d.ldx + 32 * kb;
-  }
-  auto load_x = [&](uint32_t g, uint4 (&raw)[NT][4]) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const uint4* src = reinterpret_cast<const uint4*>(xr[t] + 128 * g);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) raw[t][k] = src[k];
-    }
-  };
 
   f32x4_t C[NT];
 #pragma unroll
@@ -403,46 +441,69 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void k_mfma(MatDev d, float* __res
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   }
 
-  for (uint32_t c0 = gw0; c0 < gw1; c0 += kSlots) {   // wave-uniform
-    const uint32_t ns = min(kSlots, gw1 - c0);
-    // every weight load of the sweep first (slots past the range repeat the
-    // last group of the matrix: in bounds, dropped by a zero scale); rows
-    // differ across the lanes, so the row offsets go in the voffset
-    u32x4_t cw[kSlots / 2];   // codes of slots 2h, 2h + 1 (8 bytes each)
-    uint32_t sraw[kSlots], sbytes[kSlots];
+  // Every load of the slice first: X of both sweeps (L2), then the weights
+  // of both sweeps (HBM; slots past the range repeat the last group of the
+  // matrix: in bounds, dropped by a zero scale).  Rows differ across the
+  // lanes, so the row offsets go in the voffset.
+  XStage<NT> xg[kSweeps];
+#pragma unroll
+  for (uint32_t sw = 0; sw < kSweeps; ++sw) xg[sw].load(d, rx, gs0 + sw * kSlots);
+  u32x4_t cws[kSweeps][kSlots / 2];   // codes of slots 2h, 2h + 1 (8 bytes each)
+  uint32_t sbyteses[kSweeps][kSlots];
+  // Scales: lane (i, kb) fetches alpha and beta of tile row 4 kb + (i & 3) and
+  // slot i >> 2, so that each row of 16 lanes holds the 4 x 4 scales its C
+  // entries need (C holds rows 4 kb .. 4 kb + 3); a DPP row broadcast hands
+  // them out.  Slots past the range read zero scales (out of range).
+  uint32_t araws[kSweeps], braws[kSweeps];
+  {
+    const uint32_t ra_row = min(row_base + 4 * kb + (i & 3), d.out - 1);
+#pragma unroll
+    for (uint32_t sw = 0; sw < kSweeps; ++sw) {
+      const uint32_t g = gs0 + sw * kSlots + (i >> 2);
+      const uint32_t so = g < gs1 ? (ra_row * G + g) * SB : 0x7FFFFFF0u;
+      araws[sw] = load_scale_raw<SF>(ra, so);
+      braws[sw] = K > 0 ? load_scale_raw<SF>(ra, so + boff) : 0u;
+    }
+  }
+#pragma unroll
+  for (uint32_t sw = 0; sw < kSweeps; ++sw)
 #pragma unroll
     for (uint32_t q = 0; q < kSlots; ++q) {
-      const uint32_t g = min(c0 + q, G - 1);
+      const uint32_t g = min(gs0 + sw * kSlots + q, G - 1);
       const u32x2_t c2 = __builtin_bit_cast(
           u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rc, row * d.row_stride + g * 32 + 8 * kb, 0, kCached));
-      cw[q / 2][2 * (q & 1)] = c2[0];
-      cw[q / 2][2 * (q & 1) + 1] = c2[1];
-      const uint32_t so = sbase + (row * G + g) * SB;
-      if constexpr (SF == WAL_SCALE_FP16) {
-        sraw[q] = __builtin_amdgcn_raw_buffer_load_b16(ra, so, 0, kCached);
-      } else {
-        sraw[q] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(ra, so, 0, kCached) |
-                  ((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(ra, so + 1, 0, kCached) << 8) |
-                  ((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(ra, so + 2, 0, kCached) << 16);
-      }
-      if constexpr (K == 8) sbytes[q] = __builtin_amdgcn_raw_buffer_load_b16(rs, (row * G + g) * 8 + 2 * kb, 0, kCached);
-      if constexpr (K == 4) sbytes[q] = __builtin_amdgcn_raw_buffer_load_b8(rs, (row * G + g) * 4 + kb, 0, kCached);
-      if constexpr (K == 2)
-        sbytes[q] = __builtin_amdgcn_raw_buffer_load_b8(rs, (row * G + g) * 2 + (kb & 1), 0, kCached);
+      cws[sw][q / 2][2 * (q & 1)] = c2[0];
+      cws[sw][q / 2][2 * (q & 1) + 1] = c2[1];
+      uint32_t sb = 0;
+      if constexpr (K == 8) sb = __builtin_amdgcn_raw_buffer_load_b16(rs, (row * G + g) * 8 + 2 * kb, 0, kCached);
+      if constexpr (K == 4) sb = __builtin_amdgcn_raw_buffer_load_b8(rs, (row * G + g) * 4 + kb, 0, kCached);
+      if constexpr (K == 2) sb = __builtin_amdgcn_raw_buffer_load_b8(rs, (row * G + g) * 2 + (kb & 1), 0, kCached);
+      sbyteses[sw][q] = sb;
     }
-    // X of the sweep's groups: all four slots at once for one n-tile, one
-    // slot ahead for two (registers)
-    constexpr uint32_t XA = NT == 1 ? kSlots : 1;
-    uint4 xpre[XA][NT][4];
 #pragma unroll
-    for (uint32_t q = 0; q < XA; ++q) load_x(min(c0 + q, G - 1), xpre[q]);
+  for (uint32_t sw = 0; sw < kSweeps; ++sw) {
+    const uint32_t c0 = gs0 + sw * kSlots;
+    if (c0 >= gs1) break;   // block-uniform
+    const uint32_t ns = min(kSlots, gs1 - c0);
+    const u32x4_t (&cw)[kSlots / 2] = cws[sw];
+    const uint32_t (&sbytes)[kSlots] = sbyteses[sw];
+    // X of this sweep into LDS
+    __syncthreads();   // the previous sweep's readers are done
+    xg[sw].store(xs);
+    __syncthreads();
 #pragma unroll
     for (uint32_t q = 0; q < kSlots; ++q) {
-      const bool valid = q < ns;   // wave-uniform
+      const bool valid = q < ns;   // block-uniform
+      // B operands: lane (n, kb) reads 64 bytes of X row 16 t + n
       uint4 xb[NT][4];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) x_operands(xpre[NT == 1 ? q : 0][t], xb[t]);
-      if (NT != 1 && q + 1 < kSlots) load_x(min(c0 + q + 1, G - 1), xpre[0]);
+      for (int t = 0; t < NT; ++t) {
+        const uint4* src = reinterpret_cast<const uint4*>(xs + (t * 16 + i) * XStage<NT>::kRowBytes + q * 256 + 64 * kb);
+        uint4 raw[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) raw[k] = src[k];
+        x_operands(raw, xb[t]);
+      }
       // T operands: one 64-bit shift positions the code pairs of both dwords
       uint4 a[4];
       const uint64_t cq = ((uint64_t)cw[q / 2][2 * (q & 1) + 1] << 32) | cw[q / 2][2 * (q & 1)];
@@ -486,15 +547,14 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void k_mfma(MatDev d, float* __res
         }
       }
       // C layout: lane holds rows 4 kb + j of the tile, batch column i
-      const uint32_t sq = valid ? sraw[q] : 0u;   // a zero scale drops a slot past the range
+      (void)valid;   // slots past the range have zero scales
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int src = 4 * kb + j;
-        const float al = scale_value<SF>((uint32_t)__builtin_amdgcn_ds_bpermute(4 * src, (int)sq));
+        const float al = scale_value<SF>(row_bcast(araws[sw], 4 * q + j));
 #pragma unroll
         for (int t = 0; t < NT; ++t) C[t][j] = __builtin_fmaf(al, sT[t][j], C[t][j]);
         if constexpr (K > 0) {
-          const float be = scale_value<SF>((uint32_t)__builtin_amdgcn_ds_bpermute(4 * (16 + src), (int)sq));
+          const float be = scale_value<SF>(row_bcast(braws[sw], 4 * q + j));
 #pragma unroll
           for (int t = 0; t < NT; ++t) C[t][j] = __builtin_fmaf(be, sR[t][j], C[t][j]);
         }
@@ -502,19 +562,14 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void k_mfma(MatDev d, float* __res
     }
   }
 
-  // the tile's sum over its wavefronts, in wavefront order
-  __syncthreads();   // the R tiles are free
+  // the wavefront's tile: rows 4 kb + j, batch columns 16 t + i
 #pragma unroll
-  for (int t = 0; t < NT; ++t) red[(wave * NT + t) * 64 + lane] = C[t];
-  __syncthreads();
-  for (uint32_t e = threadIdx.x; e < 16 * 32; e += blockDim.x) {
-    const uint32_t r = e >> 5, n = e & 31, yr = row_base + r;
-    if (n >= d.batch || n >= 16 * NT || yr >= d.out) continue;
-    const uint32_t L = (r >> 2) * 16 + (n & 15);
-    float v = 0.f;
-    for (uint32_t w = 0; w < nw; ++w) v += red[(w * NT + (n >> 4)) * 64 + L][r & 3];
-    P[((size_t)slice * d.batch + n) * d.out + yr] = 0.5f * v;
-  }
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t yr = row_base + 4 * kb + j, n = 16 * t + i;
+      if (yr < d.out && n < d.batch) P[((size_t)slice * d.batch + n) * d.out + yr] = 0.5f * C[t][j];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -534,11 +589,11 @@ void launch_gemv_nb(uint32_t nb, dim3 grid, hipStream_t s, const MatDev& d, floa
 }
 
 template <int SF, int K>
-void launch_mfma_nt(uint32_t nt, dim3 grid, hipStream_t s, const MatDev& d, float* P, float* zp, uint32_t tiles,
+void launch_mfma_nt(uint32_t nt, dim3 grid, hipStream_t s, const MatDev& d, float* P, float* zp, uint32_t nz,
                     uint32_t slices) {
   const dim3 block(64 * kMfmaWaves);
-  if (nt == 1) hipLaunchKernelGGL((k_mfma<SF, K, 1>), grid, block, 0, s, d, P, zp, tiles, slices);
-  else hipLaunchKernelGGL((k_mfma<SF, K, 2>), grid, block, 0, s, d, P, zp, tiles, slices);
+  if (nt == 1) hipLaunchKernelGGL((k_mfma<SF, K, 1>), grid, block, 0, s, d, P, zp, nz, slices);
+  else hipLaunchKernelGGL((k_mfma<SF, K, 2>), grid, block, 0, s, d, P, zp, nz, slices);
 }
 
 int launch_reduce(const MatDev& d, const GemmShape& S, const float* zp, const float* P, uint32_t slices,
@@ -582,19 +637,19 @@ int launch_gemm_mfma(const wal_info& f, const MatDev& d, uint32_t batch, void* w
   float* zp = reinterpret_cast<float*>(w + S.off_z);
   float* P = reinterpret_cast<float*>(w + S.off_p);
   const uint32_t nt = (batch + 15) / 16;
-  // one workgroup per (16-row tile, 4096-column slice): the slices are the
-  // workspace's per-pass partial planes
-  const uint32_t tiles = (f.d.out + 15) / 16, slices = S.passes;
-  const dim3 grid(tiles * slices + z_blocks(d, S));
+  // one workgroup per (kMfmaTiles row tiles, kSliceCols-column slice)
+  const uint32_t rblocks = (f.d.out + 16 * kMfmaTiles - 1) / (16 * kMfmaTiles), slices = S.slices;
+  const uint32_t nz = z_blocks(d, S);
+  const dim3 grid(nz + rblocks * slices);
   switch (class_index(d)) {
-    case 0: launch_mfma_nt<WAL_SCALE_FP16, 0>(nt, grid, s, d, P, zp, tiles, slices); break;
-    case 1: launch_mfma_nt<WAL_SCALE_FP16, 2>(nt, grid, s, d, P, zp, tiles, slices); break;
-    case 2: launch_mfma_nt<WAL_SCALE_FP16, 4>(nt, grid, s, d, P, zp, tiles, slices); break;
-    case 3: launch_mfma_nt<WAL_SCALE_FP16, 8>(nt, grid, s, d, P, zp, tiles, slices); break;
-    case 4: launch_mfma_nt<WAL_SCALE_FP24, 0>(nt, grid, s, d, P, zp, tiles, slices); break;
-    case 5: launch_mfma_nt<WAL_SCALE_FP24, 2>(nt, grid, s, d, P, zp, tiles, slices); break;
-    case 6: launch_mfma_nt<WAL_SCALE_FP24, 4>(nt, grid, s, d, P, zp, tiles, slices); break;
-    default: launch_mfma_nt<WAL_SCALE_FP24, 8>(nt, grid, s, d, P, zp, tiles, slices); break;
+    case 0: launch_mfma_nt<WAL_SCALE_FP16, 0>(nt, grid, s, d, P, zp, nz, slices); break;
+    case 1: launch_mfma_nt<WAL_SCALE_FP16, 2>(nt, grid, s, d, P, zp, nz, slices); break;
+    case 2: launch_mfma_nt<WAL_SCALE_FP16, 4>(nt, grid, s, d, P, zp, nz, slices); break;
+    case 3: launch_mfma_nt<WAL_SCALE_FP16, 8>(nt, grid, s, d, P, zp, nz, slices); break;
+    case 4: launch_mfma_nt<WAL_SCALE_FP24, 0>(nt, grid, s, d, P, zp, nz, slices); break;
+    case 5: launch_mfma_nt<WAL_SCALE_FP24, 2>(nt, grid, s, d, P, zp, nz, slices); break;
+    case 6: launch_mfma_nt<WAL_SCALE_FP24, 4>(nt, grid, s, d, P, zp, nz, slices); break;
+    default: launch_mfma_nt<WAL_SCALE_FP24, 8>(nt, grid, s, d, P, zp, nz, slices); break;
   }
   return launch_reduce(d, S, zp, P, slices, s);
 }

@@ -502,8 +502,9 @@ int launch_status() {
 
 constexpr int kRB = 4;   // rows per batch of the 2-bit streaming kernels
 // Batch from which WAL_GEMM_AUTO takes the MFMA kernel (measured on MI355X
-// on the 4096 x 12288 shape).
-constexpr uint32_t kGemmCrossover = 5;
+// on the 4096 x 12288 shape); below it the batched GEMV, and at batch 1 the
+// single-product path, which is faster still.
+constexpr uint32_t kGemmCrossover = 3;
 constexpr uint32_t kClasses = 16;   // kernel classes (see class_of)
 
 // Kernel class of a matrix: 8 * trit_fmt + 4 * scale_fmt + index of k in {0, 2, 4, 8}.
@@ -702,13 +703,17 @@ int wal_gemm_small(const wal_info* info, const void* W_dev, const void* X_dev, i
   // The batched kernels take bf16 activations and 2-bit codes; other inputs
   // run one batch-1 product per column.
   const bool batched = x_dtype == WAL_X_BF16 && info->d.trit_fmt == WAL_TRIT_2BIT;
-  if (mode == WAL_GEMM_AUTO) mode = batched && batch >= kGemmCrossover ? WAL_GEMM_MFMA : WAL_GEMM_VALU;
+  bool per_row = !batched;
+  if (mode == WAL_GEMM_AUTO) {
+    mode = batched && batch >= kGemmCrossover ? WAL_GEMM_MFMA : WAL_GEMM_VALU;
+    per_row = per_row || batch == 1;
+  }
   MatDev d = make_dev(info, W_dev, X_dev, Y_dev, static_cast<float*>(ws_dev), ldx, ldy, batch);
   if (mode == WAL_GEMM_MFMA) {
     if (!batched) return WAL_ERR_UNSUPPORTED;
     return launch_gemm_mfma(*info, d, batch, ws_dev, stream);
   }
-  if (batched) return launch_gemm_valu(*info, d, batch, ws_dev, stream);
+  if (!per_row) return launch_gemm_valu(*info, d, batch, ws_dev, stream);
   for (uint32_t n = 0; n < batch; ++n) {
     const void* xn = static_cast<const uint8_t*>(X_dev) + (size_t)n * ldx * xe;
     if ((st = wal_gemv(info, W_dev, xn, x_dtype, Y_dev + (size_t)n * ldy, ws_dev, ws_bytes, stream))) return st;

@@ -451,9 +451,10 @@ GemmShape gemm_shape(const wal_info& f, uint32_t batch) {
   S.nt = (batch + 15) / 16;
   S.passes = (f.d.in + kPass2bit - 1) / kPass2bit;
   S.zc = (f.d.in + kZChunkCols - 1) / kZChunkCols;
+  S.slices = (f.d.in + kSliceCols - 1) / kSliceCols;
   S.off_z = 0;
   S.off_p = up(4 * terms * batch * S.zc, 256);
-  S.bytes = S.off_p + up(4ull * S.passes * batch * f.d.out, 256);
+  S.bytes = S.off_p + up(4ull * S.slices * batch * f.d.out, 256);
   return S;
 }
 

@@ -87,8 +87,12 @@ constexpr uint32_t kZChunkCols = 4096;   // columns per low-rank partial (small 
 constexpr uint32_t kZSingleCols = 8192;
 constexpr int kZSinglePrefetch = 4;
 constexpr uint32_t kZTermsPerBlock = 16;
+// Columns of one partial-sum slice of the MFMA small-batch kernel.
+constexpr uint32_t kSliceCols = 1024;
+
 struct GemmShape {
-  uint32_t nt, passes, zc;   // n-tiles, GEMV passes (= P planes), z chunks
+  uint32_t nt, passes, zc;   // n-tiles, batched GEMV passes, z chunks
+  uint32_t slices;           // partial-sum planes of P: ceil(in / kSliceCols) >= passes
   uint64_t off_z, off_p, bytes;
 };
 GemmShape gemm_shape(const wal_info& f, uint32_t batch);

@@ -77,7 +77,7 @@ def config3(wal):
     return blob, info, x, bits, ref
 
 
-@pytest.mark.parametrize("B", [1, 4, 16, 32])
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 16, 32])
 @pytest.mark.parametrize("mode", ["valu", "mfma", "auto"])
 def test_config3(wal, config3, B, mode):
     blob, info, x, bits, ref = config3

@@ -196,17 +196,17 @@ def test_inspect_reads_header():
 
 def test_workspace_size():
     """Low-rank partials z [chunk][batch][terms] (one chunk per 4096 columns)
-    | per-pass partial sums [passes][batch][out] of the batched GEMV, each
-    padded to 256 bytes."""
+    | partial sums [slices][batch][out] of the small-batch kernels (one slice
+    per 1024 columns), each padded to 256 bytes."""
     def up(v):
         return (v + 255) // 256 * 256
 
     def expect(out, inp, terms, B):
-        passes = (inp + 4095) // 4096
-        return up(4 * terms * B * passes) + up(4 * passes * B * out)
+        chunks, slices = (inp + 4095) // 4096, (inp + 1023) // 1024
+        return up(4 * terms * B * chunks) + up(4 * slices * B * out)
 
     info = wal.wal_packed_size(wal.make_desc(12288, 4096, 8, 1, 16))
-    assert wal.wal_workspace_size(info, 1) == expect(12288, 4096, 16, 1) == 256 + 49152
+    assert wal.wal_workspace_size(info, 1) == expect(12288, 4096, 16, 1) == 256 + 4 * 49152
     assert wal.wal_workspace_size(info, 32) == expect(12288, 4096, 16, 32)
     info = wal.wal_packed_size(wal.make_desc(4096, 12288, 8, 1, 16))
     for B in (1, 4, 16, 17, 32):
