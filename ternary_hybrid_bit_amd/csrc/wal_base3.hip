@@ -228,7 +228,7 @@ __device__ __forceinline__ void build_lut(uint32_t* lut) {
 // which also fills the byte table.
 template <int SF, int K, int ZP>
 __device__ __forceinline__ void stream_rows_base3(const MatDev& d, uint32_t row0, uint32_t row1, uint32_t pass,
-                                                  uint32_t npass, bool lut_first, Smem3& sm) {
+                                                  uint32_t npass, bool lut_first, bool partial, Smem3& sm) {
   constexpr int RB = kRB3;
   constexpr int LOG = ilog2(RB);
   constexpr int SH = 6 - LOG;
@@ -242,7 +242,9 @@ __device__ __forceinline__ void stream_rows_base3(const MatDev& d, uint32_t row0
 
   const uint32_t pw = min(kPassBase3, d.in - pass * kPassBase3);   // trits of this pass
   const uint32_t Gp = (pw + 127) / 128, g0 = pass * kGroups3, G = d.groups;
-  const bool first = pass == 0, last = pass + 1 == npass;
+  // first: y starts here; last: the low-rank term is added here (a partial
+  // pass, one pass written on its own: first, without the low-rank term)
+  const bool first = partial || pass == 0, last = !partial && pass + 1 == npass;
   const uint32_t ncols = 80 * (uint32_t)lane < pw ? min(80u, pw - 80 * lane) : 0u;
 
   // codes
@@ -386,7 +388,7 @@ __device__ __forceinline__ void stream_rows_base3(const MatDev& d, uint32_t row0
   XLane3::load_raw(rx, pass * kPassBase3 + 80 * lane, xr);
   TableX3 tx;
   if constexpr (K > 0) tx.load(rx, pass * kPassBase3);
-  const bool zpass = pass == 0 && d.terms;
+  const bool zpass = !partial && pass == 0 && d.terms;
   ZPart<ZP> zp;
   if (zpass) z_prefetch<ZP>(d, threadIdx.x, zp);
   Batch3<RB> B0 = load_batch(b);
@@ -416,15 +418,20 @@ __device__ __forceinline__ void stream_rows_base3(const MatDev& d, uint32_t row0
   }
 }
 
+// With P, only pass `split_pass`, written to P[split_pass][row] without the
+// low-rank term (a reduce adds the passes and that term).
 template <int SF, int K, int ZP>
 __device__ __forceinline__ void run_segment_base3(const MatDev& d, uint32_t row0, uint32_t row1, bool lut_first,
-                                                  Smem3& sm) {
+                                                  Smem3& sm, float* P = nullptr, uint32_t split_pass = 0) {
   const uint32_t npass = (d.in + kPassBase3 - 1) / kPassBase3;
-  for (uint32_t pass = 0; pass < npass; ++pass)
-    stream_rows_base3<SF, K, ZP>(d, row0, row1, pass, npass, lut_first && pass == 0, sm);
+  const bool partial = P != nullptr;
+  const uint32_t p0 = partial ? split_pass : 0, p1 = partial ? split_pass + 1 : npass;
+  for (uint32_t pass = p0; pass < p1; ++pass)
+    stream_rows_base3<SF, K, ZP>(d, row0, row1, pass, npass, lut_first && pass == p0, partial, sm);
   __syncthreads();
   const uint32_t nrows = row1 - row0;
-  for (uint32_t i = threadIdx.x; i < nrows; i += kThreads) d.y[row0 + i] = sm.ybuf[i];
+  float* dst = partial ? P + (size_t)split_pass * d.out : d.y;
+  for (uint32_t i = threadIdx.x; i < nrows; i += kThreads) dst[row0 + i] = sm.ybuf[i];
 }
 
 template <int SF, int K>
@@ -440,11 +447,15 @@ __global__ __launch_bounds__(kThreads) void k_stream3_grouped(const MatDev* __re
 }
 
 template <int SF, int K>
-__global__ __launch_bounds__(kThreads) void k_stream3_single(MatDev d, uint32_t rows_per_block) {
+__global__ __launch_bounds__(kThreads) void k_stream3_single(MatDev d, uint32_t rows_per_block, uint32_t nrb,
+                                                             float* P) {
+  // without P: block b takes rows [b rpb, b rpb + rpb) over every pass; with
+  // P: block b takes pass b / nrb of row block b % nrb
   __shared__ Smem3 sm;
-  const uint32_t r0 = blockIdx.x * rows_per_block;
+  const uint32_t rb = P ? blockIdx.x % nrb : blockIdx.x;
+  const uint32_t r0 = rb * rows_per_block;
   const uint32_t r1 = min(d.out, r0 + rows_per_block);
-  if (r0 < r1) run_segment_base3<SF, K, kZSinglePrefetch>(d, r0, r1, true, sm);
+  if (r0 < r1) run_segment_base3<SF, K, kZSinglePrefetch>(d, r0, r1, true, sm, P, P ? blockIdx.x / nrb : 0u);
 }
 
 }  // namespace

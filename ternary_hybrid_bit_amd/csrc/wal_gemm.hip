@@ -607,6 +607,13 @@ int launch_reduce(const MatDev& d, const GemmShape& S, const float* zp, const fl
 
 namespace wal {
 
+int launch_reduce_single(const MatDev& d, const float* zpart, uint32_t zc, const float* P, uint32_t slices,
+                         void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(k_reduce, dim3((d.out + 255) / 256, 1), dim3(256), 0, s, d, zpart, P, slices, zc);
+  return hipGetLastError() == hipSuccess ? WAL_OK : WAL_ERR_DEVICE;
+}
+
 int launch_gemm_valu(const wal_info& f, const MatDev& d, uint32_t batch, void* ws, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const GemmShape S = gemm_shape(f, batch);

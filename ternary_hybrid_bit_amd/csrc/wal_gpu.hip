@@ -234,7 +234,7 @@ struct Lane2 {
 // ZP: low-rank partials (column chunks) prefetched per term.
 template <int XT, int SF, int K, int RB, int ZP>
 __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0, uint32_t row1, uint32_t pass,
-                                                 uint32_t npass, StreamSmem& sm) {
+                                                 uint32_t npass, bool split, StreamSmem& sm) {
   constexpr int LOG = ilog2(RB);
   constexpr int SH = 6 - LOG;        // lane >> SH = row of the batch after the reduction
   constexpr int LPR = 64 >> LOG;     // lanes per row after the reduction
@@ -249,7 +249,10 @@ __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0,
   const uint32_t Gp = pw / 128, g0 = pass * (kPass2bit / 128), G = d.groups;
   const bool on = (uint32_t)lane < 2 * Gp;
   const uint32_t gl = on ? (uint32_t)lane >> 1 : 0;
-  const bool first = pass == 0, last = pass + 1 == npass;
+  // first: y starts here (no earlier pass in LDS); last: the low-rank term is
+  // added here.  A split pass (one pass of a row range, written as a partial
+  // sum) is both first and without the low-rank term.
+  const bool first = split || pass == 0, last = !split && pass + 1 == npass;
 
   // One resource over the blob; the plane offsets go into the per-lane
   // offsets (the planes are 256-byte aligned, so alignments carry over).
@@ -365,7 +368,7 @@ __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0,
   XLane<XT>::load_raw(rx, pass * kPass2bit + 64 * lane, xr);
   TableX<XT> tx;
   if constexpr (K > 0) tx.load(rx, pass * kPass2bit);
-  const bool zpass = pass == 0 && d.terms;
+  const bool zpass = !split && pass == 0 && d.terms;
   ZPart<ZP> zp;
   if (zpass) z_prefetch<ZP>(d, threadIdx.x, zp);
 
@@ -397,16 +400,22 @@ __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0,
 // SF and K are the matrix's scale format and sites per group: every
 // (scale format, k) class has kernels of its own, so the registers of the
 // hot fp16 / k = 8 loop are not set by the heavier fp24 loads.
+// With P, only pass `split_pass`, written to P[split_pass][row] without the
+// low-rank term (a reduce adds the passes and that term).
 template <int XT, int SF, int K, int RB, int ZP>
-__device__ __forceinline__ void run_segment_2bit(const MatDev& d, uint32_t row0, uint32_t row1, StreamSmem& sm) {
+__device__ __forceinline__ void run_segment_2bit(const MatDev& d, uint32_t row0, uint32_t row1, StreamSmem& sm,
+                                                 float* P = nullptr, uint32_t split_pass = 0) {
   const uint32_t npass = (d.in + kPass2bit - 1) / kPass2bit;
-  for (uint32_t pass = 0; pass < npass; ++pass)
-    stream_rows_2bit<XT, SF, K, RB, ZP>(d, row0, row1, pass, npass, sm);
+  const bool split = P != nullptr;
+  const uint32_t p0 = split ? split_pass : 0, p1 = split ? split_pass + 1 : npass;
+  for (uint32_t pass = p0; pass < p1; ++pass)
+    stream_rows_2bit<XT, SF, K, RB, ZP>(d, row0, row1, pass, npass, split, sm);
   // y leaves through LDS: one coalesced write of the segment's rows instead
   // of a few scattered bytes per batch of rows.
   __syncthreads();
   const uint32_t nrows = row1 - row0;
-  for (uint32_t i = threadIdx.x; i < nrows; i += kThreads) d.y[row0 + i] = sm.ybuf[i];
+  float* dst = split ? P + (size_t)split_pass * d.out : d.y;
+  for (uint32_t i = threadIdx.x; i < nrows; i += kThreads) dst[row0 + i] = sm.ybuf[i];
 }
 
 // Three workgroups per CU (the LDS of a workgroup allows it) when the class's
@@ -430,11 +439,14 @@ void k_stream_grouped(const MatDev* __restrict__ descs, const uint32_t* __restri
 
 template <int XT, int SF, int K, int RB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(stream_waves_per_simd(XT, SF, K))))
-void k_stream_single(MatDev d, uint32_t rows_per_block) {
+void k_stream_single(MatDev d, uint32_t rows_per_block, uint32_t nrb, float* P) {
+  // without P: block b takes rows [b rpb, b rpb + rpb) over every pass; with
+  // P: block b takes pass b / nrb of row block b % nrb
   __shared__ StreamSmem sm;
-  const uint32_t r0 = blockIdx.x * rows_per_block;
+  const uint32_t rb = P ? blockIdx.x % nrb : blockIdx.x;
+  const uint32_t r0 = rb * rows_per_block;
   const uint32_t r1 = min(d.out, r0 + rows_per_block);
-  if (r0 < r1) run_segment_2bit<XT, SF, K, RB, kZSinglePrefetch>(d, r0, r1, sm);
+  if (r0 < r1) run_segment_2bit<XT, SF, K, RB, kZSinglePrefetch>(d, r0, r1, sm, P, P ? blockIdx.x / nrb : 0u);
 }
 
 // Low-rank partials of a single product: block (tc, cc) computes terms
@@ -647,7 +659,13 @@ int wal_gemv(const wal_info* info, const void* W_dev, const void* x_dev, int x_d
   if (x_dtype != WAL_X_F32 && x_dtype != WAL_X_BF16) return WAL_ERR_ARG;
   if (!aligned(W_dev, 256) || !aligned(x_dev, 16) || !aligned(y_dev, 4)) return WAL_ERR_ALIGN;
   const GemmShape S = gemm_shape(*info, 1);
-  const size_t need = info->d.n_paths ? (size_t)S.off_p : 0;   // z partials [chunks][terms]
+  const uint32_t cls = class_of(info->d);
+  const uint32_t npass = cls >= 8 ? (info->d.in + kPassBase3 - 1) / kPassBase3 : (info->d.in + kPass2bit - 1) / kPass2bit;
+  // Matrices wider than one pass run their passes in separate workgroups
+  // when the workspace holds the per-pass partial sums (it does at
+  // wal_workspace_size(info, 1) bytes); a reduce adds them.
+  const bool split = npass > 1 && ws_dev && ws_bytes >= S.bytes;
+  const size_t need = split ? (size_t)S.bytes : info->d.n_paths ? (size_t)S.off_p : 0;   // z partials [chunks][terms]
   if (need && (!ws_dev || ws_bytes < need)) return ws_dev ? WAL_ERR_BUFFER : WAL_ERR_ARG;
   if (need && !aligned(ws_dev, 16)) return WAL_ERR_ALIGN;
   if (overlap(x_dev, (size_t)info->d.in * xelem(x_dtype), y_dev, (size_t)info->d.out * 4)) return WAL_ERR_ARG;
@@ -655,7 +673,6 @@ int wal_gemv(const wal_info* info, const void* W_dev, const void* x_dev, int x_d
                overlap(ws_dev, need, x_dev, (size_t)info->d.in * xelem(x_dtype))))
     return WAL_ERR_ARG;
   if ((st = check_blob_size(info))) return st;
-  const uint32_t cls = class_of(info->d);
   if (!single_for(x_dtype, cls)) return WAL_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   MatDev d = make_dev(info, W_dev, x_dev, y_dev, static_cast<float*>(ws_dev), info->d.in, info->d.out, 1);
@@ -668,14 +685,19 @@ int wal_gemv(const wal_info* info, const void* W_dev, const void* x_dev, int x_d
   }
   uint32_t resident = 0;
   if ((st = resident_blocks(reinterpret_cast<const void*>(grouped_for(x_dtype, cls)), &resident))) return st;
-  uint32_t rpb = (d.out + resident - 1) / resident;
+  // rows per block: the (row, pass) work spread evenly over the blocks the
+  // GPU holds at once
+  const uint64_t units = (uint64_t)d.out * (split ? npass : 1);
+  uint32_t rpb = (uint32_t)((units + resident - 1) / resident);
   const uint32_t min_rows = kWaves * kRB;   // one batch per wavefront
   if (rpb < min_rows) rpb = min_rows;
   rpb = (rpb + kRB - 1) / kRB * kRB;
   if (rpb > seg_rows(cls)) rpb = seg_rows(cls);
-  const uint32_t grid = (d.out + rpb - 1) / rpb;
-  hipLaunchKernelGGL(single_for(x_dtype, cls), dim3(grid), dim3(kThreads), 0, s, d, rpb);
-  return launch_status();
+  const uint32_t nrb = (d.out + rpb - 1) / rpb;
+  float* P = split ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws_dev) + S.off_p) : nullptr;
+  hipLaunchKernelGGL(single_for(x_dtype, cls), dim3(nrb * (split ? npass : 1)), dim3(kThreads), 0, s, d, rpb, nrb, P);
+  if ((st = launch_status()) || !split) return st;
+  return launch_reduce_single(d, d.z, d.zc, P, npass, stream);
 }
 
 int wal_gemm_small(const wal_info* info, const void* W_dev, const void* X_dev, int x_dtype, uint32_t batch,

@@ -67,7 +67,9 @@ static_assert(kMaxTerms <= kThreads, "one low-rank term per thread of a streamin
 // Streaming kernels as host-side launch targets.
 struct Seg;
 using GroupedFn = void (*)(const MatDev*, const uint32_t*, const Seg*);
-using SingleFn = void (*)(MatDev, uint32_t);
+// Single-product streaming kernel: (descriptor, rows per block, row blocks,
+// per-pass partial sums or null; see k_stream_single).
+using SingleFn = void (*)(MatDev, uint32_t, uint32_t, float*);
 
 // Small-batch products (wal_gemm.hip).
 //  * batched GEMV (vector ALUs), two launches: the first writes per-pass
@@ -98,6 +100,10 @@ struct GemmShape {
 GemmShape gemm_shape(const wal_info& f, uint32_t batch);
 // Launchers (stream as hipStream_t); WAL_OK or WAL_ERR_DEVICE.
 int launch_gemm_valu(const wal_info& f, const MatDev& d, uint32_t batch, void* ws, void* stream);
+// y = sum over `slices` per-pass partial planes P[slice][row] + the low-rank
+// term with z = the sum of zc partials (d.batch == 1).
+int launch_reduce_single(const MatDev& d, const float* zpart, uint32_t zc, const float* P, uint32_t slices,
+                         void* stream);
 int launch_gemm_mfma(const wal_info& f, const MatDev& d, uint32_t batch, void* ws, void* stream);
 
 // Host helpers implemented in wal_host.cpp.

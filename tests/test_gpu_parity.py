@@ -115,6 +115,33 @@ def test_columns_bit_exact(wal, sf, P):
         assert np.array_equal(y, W[:, j].astype(np.float32).astype(np.float64)), j
 
 
+@pytest.mark.parametrize("out,inp,k,P,r,sf,b3", [
+    (1000, 4224, 8, 1, 16, 0, False),    # two passes, the second of one group
+    (300, 12288, 2, 0, 0, 1, False),     # three passes, no low-rank path
+    (129, 8320, 4, 2, 7, 0, False),
+    (200, 17408, 4, 2, 16, 1, True),     # base-3, four passes, ragged last pass
+])
+def test_wide_single_split_and_whole(wal, out, inp, k, P, r, sf, b3):
+    """A matrix wider than one pass runs its passes in separate workgroups
+    when the workspace holds the per-pass partial sums, else every workgroup
+    takes all passes of its rows: both agree with the oracle."""
+    m = synth.make_matrix(305, out + inp + k, out, inp, k=k, n_paths=P, rank=r, scale_fmt=sf,
+                          trit_fmt=synth.TRIT_BASE3 if b3 else synth.TRIT_2BIT)
+    blob, info = wal.pack_matrix(m)
+    x, bits = synth.make_x(305, out, inp)
+    ref = D.gemv(F.pack(F.from_synth(m)), x[0])
+    W, xt = to_dev(blob), x_tensor(x[0], bits[0])
+    full = wal.wal_workspace_size(info, 1)
+    zonly = (4 * P * r * ((inp + 4095) // 4096) + 255) // 256 * 256   # the low-rank part alone
+    for nbytes in (full, zonly):
+        print(f"wide {out}x{inp} k={k} P={P} base3={b3} workspace {nbytes} B", flush=True)
+        y = torch.full((out,), float("nan"), dtype=torch.float32, device=dev())
+        ws = torch.empty(nbytes // 4, dtype=torch.float32, device=dev()) if nbytes else None
+        wal.wal_gemv(info, W, xt, y, ws)
+        torch.cuda.synchronize()
+        assert D.rel_l2(y.cpu().numpy().astype(np.float64), ref) <= BF16_TOL, nbytes
+
+
 def test_zero_case_returns_exact_zero(wal):
     m = synth.make_matrix(302, 0, 300, 4096, k=0, n_paths=0, zero_T=True)
     y, _ = case(wal, m)
