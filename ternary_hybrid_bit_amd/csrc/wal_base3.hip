@@ -442,7 +442,7 @@ __global__ __launch_bounds__(kThreads) void k_stream3_grouped(const MatDev* __re
   const uint32_t s0 = blockseg[blockIdx.x], s1 = blockseg[blockIdx.x + 1];
   for (uint32_t s = s0; s < s1; ++s) {
     const Seg sg = segs[s];
-    run_segment_base3<SF, K, 1>(descs[sg.mat], sg.row0, sg.row1, s == s0, sm);
+    run_segment_base3<SF, K, kZSinglePrefetch>(descs[sg.mat], sg.row0, sg.row1, s == s0, sm);
   }
 }
 

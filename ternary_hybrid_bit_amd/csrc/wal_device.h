@@ -277,10 +277,5 @@ __device__ __forceinline__ float z_total(const MatDev& d, uint32_t t, const ZPar
   return z;
 }
 
-// One pre-pass workgroup: terms t0 .. t0 + kZTerms - 1 of one matrix into d.z.
-template <int XT>
-__device__ __forceinline__ void zjob(const MatDev& d, uint32_t t0) {
-  z_chunk<XT, (int)kZTerms>(d, d.x, t0, d.z, 0, d.in);
-}
 
 }  // namespace

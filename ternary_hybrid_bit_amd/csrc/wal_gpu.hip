@@ -433,7 +433,7 @@ void k_stream_grouped(const MatDev* __restrict__ descs, const uint32_t* __restri
   const uint32_t s0 = blockseg[blockIdx.x], s1 = blockseg[blockIdx.x + 1];
   for (uint32_t s = s0; s < s1; ++s) {
     const Seg sg = segs[s];
-    run_segment_2bit<XT, SF, K, RB, 1>(descs[sg.mat], sg.row0, sg.row1, sm);
+    run_segment_2bit<XT, SF, K, RB, kZSinglePrefetch>(descs[sg.mat], sg.row0, sg.row1, sm);
   }
 }
 
@@ -464,8 +464,11 @@ __global__ __launch_bounds__(kThreads) void k_z_chunks(MatDev d) {
 template <int XT>
 __global__ __launch_bounds__(kThreads) void k_z_grouped(const MatDev* __restrict__ descs,
                                                         const uint32_t* __restrict__ jobs) {
-  const uint32_t job = jobs[blockIdx.x];
-  zjob<XT>(descs[job >> 8], job & 255u);
+  const uint32_t m = jobs[2 * blockIdx.x], tc = jobs[2 * blockIdx.x + 1];
+  const MatDev& d = descs[m];
+  const uint32_t t0 = tc >> 16, cc = tc & 0xFFFFu;
+  const uint32_t c0 = cc * kZChunkCols, c1 = min(d.in, c0 + kZChunkCols);
+  z_chunk<XT, (int)kZTerms>(d, d.x, t0, d.z + (size_t)cc * d.terms, c0, c1);
 }
 
 // ---------------------------------------------------------------------------
@@ -582,11 +585,15 @@ uint64_t row_bytes(const wal_info& f) {
   return codes + G * f.d.k + G * sb * (f.d.k ? 2 : 1) + (uint64_t)f.d.n_paths * ((f.d.rank + 7) / 8);
 }
 
+// Low-rank column chunks of a matrix in a grouped product (one partial sum of
+// z per chunk: jobs stay short however wide the matrix).
+uint32_t grouped_zc(const wal_info& f) { return (f.d.in + kZChunkCols - 1) / kZChunkCols; }
+
 uint64_t count_zjobs(uint32_t n, const wal_info* infos) {
   uint64_t j = 0;
   for (uint32_t i = 0; i < n; ++i) {
     const uint32_t T = infos[i].d.n_paths * infos[i].d.rank;
-    j += (T + kZTerms - 1) / kZTerms;
+    j += (uint64_t)(T + kZTerms - 1) / kZTerms * (T ? grouped_zc(infos[i]) : 0);
   }
   return j;
 }
@@ -636,7 +643,7 @@ int plan_shape(uint32_t n, const wal_info* infos, uint32_t grid, int x_dtype, Pl
   P->off_descs = off;
   off += up64((uint64_t)n * sizeof(MatDev), 64);
   P->off_zjobs = off;
-  off += up64(count_zjobs(n, infos) * 4, 64);
+  off += up64(count_zjobs(n, infos) * 8, 64);   // (matrix, t0 << 16 | chunk) pairs
   for (uint32_t k = 0; k < P->n_classes; ++k) {
     P->off_blockseg[k] = off;
     off += up64(4ull * (P->grid[k] + 1), 64);
@@ -753,7 +760,8 @@ int wal_grouped_plan_size(uint32_t n, const wal_info* infos, uint32_t grid, int 
     int st = check_info(&infos[i]);
     if (st) return st;
     if ((st = check_blob_size(&infos[i]))) return st;
-    ws += up64(4ull * infos[i].d.n_paths * infos[i].d.rank, 16);
+    const uint64_t T = (uint64_t)infos[i].d.n_paths * infos[i].d.rank;
+    ws += T ? up64(4 * T * grouped_zc(infos[i]), 16) : 0;
   }
   PlanShape P;
   int st = plan_shape(n, infos, grid, x_dtype, &P);
@@ -790,11 +798,17 @@ int wal_grouped_plan(uint32_t n, const wal_info* infos, const void* const* W_dev
   // descriptors and low-rank jobs
   uint64_t zoff = 0, j = 0;
   for (uint32_t i = 0; i < n; ++i) {
-    const uint32_t T = infos[i].d.n_paths * infos[i].d.rank;
+    const uint32_t T = infos[i].d.n_paths * infos[i].d.rank, zc = grouped_zc(infos[i]);
     float* z = T ? static_cast<float*>(ws_dev) + zoff / 4 : nullptr;
     descs[i] = make_dev(&infos[i], W_dev[i], x_dev[i], y_dev[i], z, infos[i].d.in, infos[i].d.out, 1);
-    zoff += up64(4ull * T, 16);
-    for (uint32_t t0 = 0; t0 < T; t0 += kZTerms) jobs[j++] = (i << 8) | t0;
+    descs[i].zc = zc;   // z partials [zc][T]
+    zoff += T ? up64(4ull * T * zc, 16) : 0;
+    for (uint32_t cc = 0; T && cc < zc; ++cc)
+      for (uint32_t t0 = 0; t0 < T; t0 += kZTerms) {
+        jobs[2 * j] = i;
+        jobs[2 * j + 1] = (t0 << 16) | cc;
+        ++j;
+      }
   }
 
   std::memset(ginfo, 0, sizeof(*ginfo));

@@ -26,16 +26,17 @@ struct MatDev {
   const void* x;       // [batch][ldx] activations
   float* y;            // [batch][ldy] outputs
   float* z;            // workspace: diag(s_p) V_p^T x, zc partial sums over
-                       // 4096-column chunks [zc][n_paths * rank] (streaming kernels)
+                       // column chunks [zc][n_paths * rank] (streaming kernels)
   uint32_t out, in, k, n_paths, rank, scale_fmt, row_stride, groups;
   uint32_t ldx, ldy, batch, terms;  // terms = n_paths * rank
   uint32_t blob_bytes;              // bytes of the blob from codes on (< 2^32)
   uint32_t trit_fmt;
-  uint32_t zc;                      // chunks of z to add (1 for grouped plans)
+  uint32_t zc;                      // chunks of z to add
 };
 
 // Plan blob written by wal_grouped_plan (host) and read by the kernels:
-//   header | MatDev[n] | zjobs u32[n_zjobs] | per (scale format, k) class:
+//   header | MatDev[n] | zjobs u32[2 n_zjobs] (matrix, t0 << 16 | chunk) |
+//   per (scale format, k) class:
 //   blockseg u32[grid + 1] | segs Seg[...]
 // Workgroup b of a class's streaming launch processes its
 // segs[blockseg[b] .. blockseg[b + 1]).  The header is informative only

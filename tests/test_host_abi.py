@@ -283,7 +283,7 @@ def _plan_classes(plan, g):
         blockseg = np.frombuffer(plan, np.uint32, G + 1, g.class_blockseg[c])
         segs = np.frombuffer(plan, np.uint32, 4 * int(blockseg[-1]), g.class_segs[c]).reshape(-1, 4)
         out.append((g.class_id[c], blockseg, segs))
-    jobs = np.frombuffer(plan, np.uint32, g.n_zjobs, g.off_zjobs)
+    jobs = np.frombuffer(plan, np.uint32, 2 * g.n_zjobs, g.off_zjobs).reshape(-1, 2)
     return out, jobs
 
 
@@ -326,9 +326,11 @@ def test_grouped_plan_covers_every_row_once(grid):
         assert per_block.max() <= ideal + max(rb[m] for m in members) + 1
     for c in covered:
         assert np.all(c == 1)
-    # one low-rank job per 4 terms of every matrix that has paths
-    want = [(m << 8) | t0 for m, (o, i, k, P, r, sf, tf) in enumerate(shapes) for t0 in range(0, P * r, 4)]
-    assert sorted(jobs.tolist()) == sorted(want)
+    # one low-rank job per 4 terms and 4096-column chunk of every matrix
+    # that has paths: (matrix, t0 << 16 | chunk)
+    want = [(m, (t0 << 16) | cc) for m, (o, i, k, P, r, sf, tf) in enumerate(shapes)
+            for cc in range((i + 4095) // 4096) for t0 in range(0, P * r, 4)]
+    assert sorted(map(tuple, jobs.tolist())) == sorted(want)
 
 
 def test_grouped_plan_rejects_bad_arguments():
