@@ -20,7 +20,9 @@ configurations (one JSON line each, no contract fields): config 1 is the
 12288x4096 gate shape through wal_gemv, config 3 the 4096x12288 down shape
 through wal_gemm_small with both kernels at batch 1, 2, 3, 4, 5, 8, 16 and 32
 (and the batch from which the matrix-core kernel is faster), config 4 the two
-base-3 / fp24 27B shapes through wal_gemv.  Each call reads one of about
+base-3 / fp24 27B shapes through wal_gemv; ``--workload prefill`` runs the
+down shape through wal_gemm_prefill at batch 64 to 2048 beside torch's dense
+bf16 matmul of that shape.  Each call reads one of about
 1 GB of distinct packed copies in turn, so the 256 MB Infinity Cache cannot
 serve the weights; x stays fixed.  For context the line also carries the
 rate of torch's own reduction (torch.sum over 2 GiB) on the same GPU; it is
@@ -220,6 +222,10 @@ def run_single(args):
         print(json.dumps(out), flush=True)
         return
 
+    if args.workload == "prefill":
+        run_prefill(args, torch, wal, synth, dev, read_gbs, to_x)
+        return
+
     # config 3: both kernels at every batch
     m = synth.config_matrix(3)
     blob, info = wal.pack_matrix(m)
@@ -255,6 +261,47 @@ def run_single(args):
     print(json.dumps(out), flush=True)
 
 
+def run_prefill(args, torch, wal, synth, dev, read_gbs, to_x):
+    """The 4096 x 12288 down_proj matrix through wal_gemm_prefill at batch 64
+    to 2048; beside it, for context, torch's dense bf16 matmul of the same
+    shape (random bf16 weights: timing only)."""
+    m = synth.config_matrix(3)
+    blob, info = wal.pack_matrix(m)
+    out_, in_ = int(info.d.out), int(info.d.in_)
+    batches = (64, 128, 256, 512, 1024, 2048)
+    Bmax = max(batches)
+    _, bits = synth.make_x(3, 0, in_, Bmax)
+    X = to_x(bits)
+    Ws, keep = rotating_copies(torch, dev, blob, total_bytes=1 << 29)
+    Y = torch.empty((Bmax, out_), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(wal.wal_prefill_workspace_size(info, B) for B in batches) // 4 + 64,
+                     dtype=torch.float32, device=dev)
+    Wd = torch.randn((out_, in_), dtype=torch.bfloat16, device=dev)
+    calls = max(args.steps // 4, 20)
+    rows = []
+    for B in batches:
+        us = time_calls(torch, lambda i: wal.wal_gemm_prefill(info, Ws[i % len(Ws)], X[:B], Y[:B], ws), calls)
+        us_d = time_calls(torch, lambda i: torch.matmul(X[:B], Wd.t()), calls)
+        flops = 2.0 * out_ * in_ * B
+        # the kernel issues one MFMA chain for T and one for R per group (k > 0)
+        issued = flops * (2 if info.d.k else 1)
+        row = {"batch": B, "us_per_call": round(us, 2),
+               "dense_equiv_TFLOPs": round(flops / (us * 1e-6) / 1e12, 1),
+               "dense_equiv_frac_of_2.5PF": round(flops / (us * 1e-6) / 2.5e15, 4),
+               "mfma_issued_frac_of_2.5PF": round(issued / (us * 1e-6) / 2.5e15, 4),
+               "packed_GB/s": round(info.algorithmic_bytes / (us * 1e-6) / 1e9, 1),
+               "torch_bf16_dense_us": round(us_d, 2),
+               "speedup_vs_dense_bf16": round(us_d / us, 3)}
+        rows.append(row)
+        print(f"[bench] prefill B={B}: {row['us_per_call']} us, dense bf16 {row['torch_bf16_dense_us']} us",
+              file=sys.stderr, flush=True)
+    out = {"workload": "prefill", "entry": "wal_gemm_prefill", "shape": [out_, in_], "k": int(info.d.k),
+           "x_dtype": "bf16", "data": "synthetic", "packed_bytes": int(info.algorithmic_bytes),
+           "copies": len(Ws), "calls": calls, "results": rows, "torch_sum_2gib_gbs": read_gbs}
+    print(json.dumps(out), flush=True)
+    del keep
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -266,7 +313,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after timing, run one fp32 elementwise copy of this many MiB (counter calibration)")
-    ap.add_argument("--workload", default="sweep", choices=("sweep", "config1", "config3", "config4"))
+    ap.add_argument("--workload", default="sweep", choices=("sweep", "config1", "config3", "config4", "prefill"))
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "

@@ -94,6 +94,7 @@ enum { WAL_GEMM_AUTO = 0, WAL_GEMM_VALU = 1, WAL_GEMM_MFMA = 2 };
 #define WAL_MAX_RANK 64
 #define WAL_HEADER_BYTES 256
 #define WAL_MAX_BATCH 32
+#define WAL_MAX_PREFILL_BATCH 16384
 
 /* Shape and storage choice of one matrix. */
 typedef struct {
@@ -223,6 +224,34 @@ int wal_gemv(const wal_info* info, const void* W_dev, const void* x_dev, int x_d
 int wal_gemm_small(const wal_info* info, const void* W_dev, const void* X_dev, int x_dtype,
                    uint32_t batch, uint32_t ldx, float* Y_dev, uint32_t ldy, int mode,
                    void* ws_dev, size_t ws_bytes, void* stream);
+
+/* Device workspace that wal_gemm_prefill needs for a blob and batch
+ * (1..WAL_MAX_PREFILL_BATCH): the low-rank partials [ceil(in / 4096)][batch]
+ * [n_paths * rank] and, when the product is split along K (few output tiles),
+ * the per-split partial sums [splits][batch][out] (fp32), each part padded to
+ * 256 bytes.  0 for a blob without paths that is not split.
+ * Errors: ARG, SHAPE, FORMAT. */
+int wal_prefill_workspace_size(const wal_info* info, uint32_t batch, size_t* bytes);
+
+/* Y = X W^T for a prefill-size batch (F.linear convention; WAL-Ternary-8B
+ * cards, "Representation", and the pages' note that batched packed products
+ * were left unoptimised): trits decoded to bf16 operands of matrix-core MFMA
+ * tiles of 128 rows x 32 activation rows, alpha / beta applied per group in
+ * fp32, the low-rank term added from a pre-pass.
+ *   X_dev  [batch][ldx] bf16 activations, ldx >= in, ldx * 2 % 16 == 0,
+ *          (batch - 1) * ldx + in < 2^30 elements
+ *   Y_dev  [batch][ldy] fp32 outputs, ldy >= out; columns past out untouched
+ *   batch  1..WAL_MAX_PREFILL_BATCH (any batch works; from a few hundred rows
+ *          on, the tiles alone fill the GPU and nothing is split)
+ *   ws_dev wal_prefill_workspace_size(info, batch) bytes, 16-byte aligned,
+ *          disjoint from X and Y (may be NULL when that size is 0)
+ * fp32 X and base-3 codes return WAL_ERR_UNSUPPORTED.  Every sum runs in a
+ * fixed order: results do not depend on timing.  Calls that share a
+ * workspace must be ordered (one stream).
+ * Errors: ARG, SHAPE, ALIGN, BUFFER, UNSUPPORTED, DEVICE. */
+int wal_gemm_prefill(const wal_info* info, const void* W_dev, const void* X_dev, int x_dtype,
+                     uint32_t batch, uint32_t ldx, float* Y_dev, uint32_t ldy,
+                     void* ws_dev, size_t ws_bytes, void* stream);
 
 /* Grouped products y_i = W_i(x_i), i < n, in one pass over all matrices
  * (e.g. the 252 body matrices of a 36-layer model).  Two steps:

@@ -24,6 +24,7 @@ WAL_GEMM_AUTO, WAL_GEMM_VALU, WAL_GEMM_MFMA = 0, 1, 2
 WAL_PHASE_LOWRANK, WAL_PHASE_STREAM, WAL_PHASE_ALL = 1, 2, 3
 WAL_MAX_PATHS = 4
 WAL_MAX_BATCH = 32
+WAL_MAX_PREFILL_BATCH = 16384
 
 STATUS = {0: "WAL_OK", -1: "WAL_ERR_ARG", -2: "WAL_ERR_SHAPE", -3: "WAL_ERR_CODE",
           -4: "WAL_ERR_INEXACT", -5: "WAL_ERR_BUFFER", -6: "WAL_ERR_ALIGN", -7: "WAL_ERR_FORMAT",
@@ -84,6 +85,8 @@ _sig = {
     "wal_workspace_size": (_I, [ctypes.POINTER(wal_info), _U32, ctypes.POINTER(_SZ)]),
     "wal_gemv": (_I, [ctypes.POINTER(wal_info), _P, _P, _I, _P, _P, _SZ, _P]),
     "wal_gemm_small": (_I, [ctypes.POINTER(wal_info), _P, _P, _I, _U32, _U32, _P, _U32, _I, _P, _SZ, _P]),
+    "wal_prefill_workspace_size": (_I, [ctypes.POINTER(wal_info), _U32, ctypes.POINTER(_SZ)]),
+    "wal_gemm_prefill": (_I, [ctypes.POINTER(wal_info), _P, _P, _I, _U32, _U32, _P, _U32, _P, _SZ, _P]),
     "wal_grouped_plan_size": (_I, [_U32, _P, _U32, _I, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)]),
     "wal_grouped_plan": (_I, [_U32, _P, _P, _P, _I, _P, _P, _SZ, _U32, _P, _SZ,
                               ctypes.POINTER(wal_grouped_info)]),
@@ -194,6 +197,12 @@ def wal_workspace_size(info: wal_info, batch: int = 1) -> int:
     return n.value
 
 
+def wal_prefill_workspace_size(info: wal_info, batch: int) -> int:
+    n = _SZ()
+    _check(_lib.wal_prefill_workspace_size(ctypes.byref(info), batch, ctypes.byref(n)), "wal_prefill_workspace_size")
+    return n.value
+
+
 def wal_gemv(info: wal_info, W, x, y, ws=None, stream=None):
     """y = W(x) on the GPU; W, x, y (and ws, see wal_workspace_size) are device
     tensors; y is fp32 [out]."""
@@ -213,6 +222,18 @@ def wal_gemm_small(info: wal_info, W, X, Y, mode=WAL_GEMM_AUTO, ws=None, stream=
     st = _lib.wal_gemm_small(ctypes.byref(info), _ptr(W), _ptr(X), xdt, X.shape[0], X.stride(0), _ptr(Y),
                              Y.stride(0), mode, _ptr(ws), wsb, _stream(stream))
     _check(st, "wal_gemm_small")
+    return Y
+
+
+def wal_gemm_prefill(info: wal_info, W, X, Y, ws=None, stream=None):
+    """Y = X W^T for a prefill-size batch; X [batch][ldx] bf16, Y [batch][ldy]
+    fp32 device tensors, ws of wal_prefill_workspace_size bytes (or None when 0)."""
+    import torch
+    xdt = WAL_X_BF16 if X.dtype == torch.bfloat16 else WAL_X_F32
+    wsb = ws.numel() * ws.element_size() if ws is not None else 0
+    st = _lib.wal_gemm_prefill(ctypes.byref(info), _ptr(W), _ptr(X), xdt, X.shape[0], X.stride(0), _ptr(Y),
+                               Y.stride(0), _ptr(ws), wsb, _stream(stream))
+    _check(st, "wal_gemm_prefill")
     return Y
 
 

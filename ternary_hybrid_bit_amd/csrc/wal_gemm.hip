@@ -348,21 +348,23 @@ __device__ __forceinline__ void a_operands(uint64_t q, uint4 (&a)[4]) {
   if constexpr (I < 7) a_operands<I + 1>(q, a);
 }
 
-// k_mfma's work split: a workgroup of kMfmaTiles wavefronts takes kMfmaTiles
-// 16-row tiles (one per wavefront) and one slice of kSliceCols columns; the
-// slice is swept kSlots 128-column groups at a time (kSweeps sweeps).  Every wavefront needs
-// the same X for a sweep, so the workgroup stages it once in LDS and each
-// wavefront reads its B operands from there: X crosses from L2 once per
-// kMfmaTiles tiles instead of once per tile.
+// MFMA kernels' work split: a workgroup of kMfmaTiles wavefronts takes
+// kMfmaTiles 16-row tiles (one per wavefront) and sweeps its columns kSlots
+// 128-column groups at a time.  Every wavefront needs the same X for a sweep,
+// so the workgroup stages it once in LDS and each wavefront reads its B
+// operands from there: X crosses from L2 once per kMfmaTiles tiles instead of
+// once per tile.  k_mfma (small batch) gives a workgroup one kSliceCols-column
+// slice (kSweeps sweeps) and writes partial sums; k_prefill (large batch)
+// gives it every column of a 32-row batch chunk and writes Y.
 constexpr uint32_t kSlots = 4;
 constexpr uint32_t kSweeps = kSliceCols / 128 / kSlots;
 constexpr uint32_t kMfmaTiles = 8;
 constexpr uint32_t kMfmaWaves = kMfmaTiles;
 
-// X rows 16 t .. 16 t + 15 of one sweep in LDS: [t][n][kSlots * 128 columns]
-// bf16 (rows padded by 16 bytes, so that the 16 rows a B-operand read touches
-// start in different banks), about 16 KB per n-tile.  Thread j loads 32 bytes
-// of row (j >> 5) per n-tile.
+// X rows nbase + 16 t .. + 15 of one sweep in LDS: [t][n][kSlots * 128
+// columns] bf16 (rows padded by 16 bytes, so that the 16 rows a B-operand
+// read touches start in different banks), about 16 KB per n-tile.  Thread j
+// loads 32 bytes of row (j >> 5) per n-tile.
 template <int NT>
 struct XStage {
   static constexpr uint32_t kRowBytes = kSlots * 128 * 2 + 16;
@@ -370,11 +372,11 @@ struct XStage {
 
   // X[n][128 c0 + 16 (j & 31) .. + 16], zero past the row's end; rows past
   // the batch read row 0 (such B-operand columns only feed unused outputs).
-  __device__ __forceinline__ void load(const MatDev& d, __amdgpu_buffer_rsrc_t rx, uint32_t c0) {
+  __device__ __forceinline__ void load(const MatDev& d, __amdgpu_buffer_rsrc_t rx, uint32_t c0, uint32_t nbase) {
     const uint32_t j = threadIdx.x, r = j >> 5, col = 128 * c0 + 16 * (j & 31);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const uint32_t n = 16 * t + r;
+      const uint32_t n = nbase + 16 * t + r;
       const uint32_t off = col < d.in ? 2 * ((n < d.batch ? n : 0) * d.ldx + col) : 0x7FFFFFF0u;
       v[t][0] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
       v[t][1] = __builtin_amdgcn_raw_buffer_load_b128(rx, off + 16, 0, 0);
@@ -391,6 +393,147 @@ struct XStage {
     }
   }
 };
+
+// One wavefront's weights for one sweep: lane (i, kb) holds the codes of row
+// i of its tile (8 bytes per slot), its site bytes, and the scales of tile
+// row 4 kb + (i & 3) for slot i >> 2 (so that each row of 16 lanes holds the
+// 4 x 4 scales its C entries need, C holding rows 4 kb .. 4 kb + 3; a DPP row
+// broadcast hands them out).
+struct SweepW {
+  u32x4_t cw[kSlots / 2];   // codes of slots 2h, 2h + 1 (8 bytes each)
+  uint32_t sbytes[kSlots];
+  uint32_t araw, braw;
+};
+
+// Resources and fixed offsets of the weight loads.
+struct WRes {
+  __amdgpu_buffer_rsrc_t rc, ra, rs;
+  uint32_t boff;   // beta plane from the alpha plane
+};
+
+template <int K>
+__device__ __forceinline__ WRes make_wres(const MatDev& d) {
+  WRes w;
+  w.rc = rsrc(d.codes, d.blob_bytes);
+  // one resource over the alpha and beta planes (beta at a fixed offset)
+  w.ra = rsrc(d.alpha, d.blob_bytes - (uint32_t)(d.alpha - d.codes));
+  w.boff = K > 0 ? (uint32_t)(d.beta - d.alpha) : 0u;
+  w.rs = rsrc(d.codes, 0u);
+  if constexpr (K > 0) w.rs = rsrc(d.sites, d.blob_bytes - (uint32_t)(d.sites - d.codes));
+  return w;
+}
+
+// Groups c0 .. c0 + kSlots - 1 of the tile rows row_base .. + 15; groups at
+// or past gend get zero scales (their codes and sites repeat the matrix's
+// last group: in bounds, dropped by the zero scale).  The loads read 8 to
+// 32 bytes per row and instruction; the rest of each cache line is read
+// moments later by the next slots, so they keep the default cache policy.
+template <int SF, int K>
+__device__ __forceinline__ SweepW load_sweep(const MatDev& d, const WRes& w, uint32_t row_base, uint32_t c0,
+                                             uint32_t gend, int lane) {
+  constexpr uint32_t SB = SF == WAL_SCALE_FP16 ? 2 : 3;
+  const uint32_t i = lane & 15, kb = lane >> 4, G = d.groups;
+  const uint32_t row = min(row_base + i, d.out - 1);
+  SweepW s;
+  {
+    const uint32_t ra_row = min(row_base + 4 * kb + (i & 3), d.out - 1);
+    const uint32_t g = c0 + (i >> 2);
+    const uint32_t so = g < gend ? (ra_row * G + g) * SB : 0x7FFFFFF0u;
+    s.araw = load_scale_raw<SF>(w.ra, so);
+    s.braw = K > 0 ? load_scale_raw<SF>(w.ra, so + w.boff) : 0u;
+  }
+#pragma unroll
+  for (uint32_t q = 0; q < kSlots; ++q) {
+    const uint32_t g = min(c0 + q, G - 1);
+    const u32x2_t c2 =
+        __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(w.rc, row * d.row_stride + g * 32 + 8 * kb, 0, 0));
+    s.cw[q / 2][2 * (q & 1)] = c2[0];
+    s.cw[q / 2][2 * (q & 1) + 1] = c2[1];
+    uint32_t sb = 0;
+    if constexpr (K == 8) sb = __builtin_amdgcn_raw_buffer_load_b16(w.rs, (row * G + g) * 8 + 2 * kb, 0, 0);
+    if constexpr (K == 4) sb = __builtin_amdgcn_raw_buffer_load_b8(w.rs, (row * G + g) * 4 + kb, 0, 0);
+    if constexpr (K == 2) sb = __builtin_amdgcn_raw_buffer_load_b8(w.rs, (row * G + g) * 2 + (kb & 1), 0, 0);
+    s.sbytes[q] = sb;
+  }
+  return s;
+}
+
+// The four slots of a sweep for one wavefront: C[t][j] += alpha sT + beta sR
+// for tile row 4 kb + j and batch column 16 t + i (decoded values are 2x).
+// xs: the sweep's X in LDS; rt4 / rt16: the wavefront's R tile (zero on
+// entry and on exit).
+template <int SF, int K, int NT>
+__device__ __forceinline__ void sweep_mfma(const uint8_t* xs, const SweepW& w, int lane, uint4* rt4, uint16_t* rt16,
+                                           f32x4_t (&C)[NT]) {
+  const uint32_t i = lane & 15, kb = lane >> 4;
+#pragma unroll
+  for (uint32_t q = 0; q < kSlots; ++q) {
+    // B operands: lane (n, kb) reads 64 bytes of X row 16 t + n
+    uint4 xb[NT][4];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const uint4* src = reinterpret_cast<const uint4*>(xs + (t * 16 + i) * XStage<NT>::kRowBytes + q * 256 + 64 * kb);
+      uint4 raw[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) raw[k] = src[k];
+      x_operands(raw, xb[t]);
+    }
+    // T operands: one 64-bit shift positions the code pairs of both dwords
+    uint4 a[4];
+    const uint64_t cq = ((uint64_t)w.cw[q / 2][2 * (q & 1) + 1] << 32) | w.cw[q / 2][2 * (q & 1)];
+    a_operands<0>(cq, a);
+    f32x4_t sT[NT], sR[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      sT[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) sT[t] = mfma(a[m], xb[t][m], sT[t]);
+    }
+    if constexpr (K > 0) {
+      // lane (i, kb) scatters sites kb * K / 4 .. of row i (K = 2: the lanes
+      // with kb < 2, one site each) into the R tile, operand m of lane L at
+      // [m][L]
+      constexpr int PER = K == 8 ? 2 : 1;
+      const bool writer = K != 2 || kb < 2;
+      uint32_t addr[PER];
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const uint32_t sb = (w.sbytes[q] >> (8 * j)) & 0xFFu;
+        const uint32_t pos = sb & 127u, local = pos & 31u, rr = local & 15u;
+        const uint32_t o = 8 * (local >> 4) + (rr & 7u);
+        const uint32_t lt = (pos >> 5) * 16 + i;   // lane whose operand holds column pos of row i
+        addr[j] = ((o >> 2) * 64 + lt) * 8 + (o & 3) * 2 + (rr >> 3);
+        if (writer) rt16[addr[j]] = (sb & 128u) ? 0xC000u : 0x4000u;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      uint4 ro[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) ro[m] = rt4[m * 64 + lane];
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+      for (int j = 0; j < PER; ++j)
+        if (writer) rt16[addr[j]] = 0;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        sR[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) sR[t] = mfma(ro[m], xb[t][m], sR[t]);
+      }
+    }
+    // C layout: lane holds rows 4 kb + j of the tile, batch column i
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float al = scale_value<SF>(row_bcast(w.araw, 4 * q + j));
+#pragma unroll
+      for (int t = 0; t < NT; ++t) C[t][j] = __builtin_fmaf(al, sT[t][j], C[t][j]);
+      if constexpr (K > 0) {
+        const float be = scale_value<SF>(row_bcast(w.braw, 4 * q + j));
+#pragma unroll
+        for (int t = 0; t < NT; ++t) C[t][j] = __builtin_fmaf(be, sR[t][j], C[t][j]);
+      }
+    }
+  }
+}
 
 // The first nz blocks compute the low-rank partials (z_block), so that they
 // run alongside the rest.  Block nz + b: row block b / slices (kMfmaTiles
@@ -411,26 +554,11 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void k_mfma(MatDev d, float* __res
   const uint32_t wave = wave_id();
   const uint32_t rb = (blockIdx.x - nz) / slices, slice = (blockIdx.x - nz) % slices;
   const uint32_t row_base = (rb * kMfmaTiles + wave) * 16;
-  const uint32_t G = d.groups;
-  const uint32_t gs0 = slice * (kSliceCols / 128), gs1 = min(G, gs0 + kSliceCols / 128);
-  constexpr uint32_t SB = SF == WAL_SCALE_FP16 ? 2 : 3;
-  const uint32_t i = lane & 15, kb = lane >> 4;
-  const uint32_t row = min(row_base + i, d.out - 1);
+  const uint32_t gs0 = slice * (kSliceCols / 128), gs1 = min(d.groups, gs0 + kSliceCols / 128);
   uint4* rt4 = reinterpret_cast<uint4*>(rts + wave * 4096);
   uint16_t* rt16 = reinterpret_cast<uint16_t*>(rts + wave * 4096);
-
-  const __amdgpu_buffer_rsrc_t rc = rsrc(d.codes, d.blob_bytes);
-  // one resource over the alpha and beta planes (beta at a fixed offset)
-  const __amdgpu_buffer_rsrc_t ra = rsrc(d.alpha, d.blob_bytes - (uint32_t)(d.alpha - d.codes));
-  const uint32_t boff = K > 0 ? (uint32_t)(d.beta - d.alpha) : 0u;
-  __amdgpu_buffer_rsrc_t rs = rsrc(d.codes, 0u);
-  if constexpr (K > 0) rs = rsrc(d.sites, d.blob_bytes - (uint32_t)(d.sites - d.codes));
-  const __amdgpu_buffer_rsrc_t rx =
-      rsrc(d.x, 2 * ((d.batch - 1) * d.ldx + d.in));
-  // The weight loads read 8 to 32 bytes per row and instruction; the rest of
-  // each cache line is read moments later by the next slots, so they keep the
-  // default cache policy (the lines stay in L2).
-  constexpr int kCached = 0;
+  const WRes wr = make_wres<K>(d);
+  const __amdgpu_buffer_rsrc_t rx = rsrc(d.x, 2 * ((d.batch - 1) * d.ldx + d.in));
 
   f32x4_t C[NT];
 #pragma unroll
@@ -442,127 +570,25 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void k_mfma(MatDev d, float* __res
   }
 
   // Every load of the slice first: X of both sweeps (L2), then the weights
-  // of both sweeps (HBM; slots past the range repeat the last group of the
-  // matrix: in bounds, dropped by a zero scale).  Rows differ across the
-  // lanes, so the row offsets go in the voffset.
+  // of both sweeps (HBM).  Rows differ across the lanes, so the row offsets
+  // go in the voffset.
   XStage<NT> xg[kSweeps];
 #pragma unroll
-  for (uint32_t sw = 0; sw < kSweeps; ++sw) xg[sw].load(d, rx, gs0 + sw * kSlots);
-  u32x4_t cws[kSweeps][kSlots / 2];   // codes of slots 2h, 2h + 1 (8 bytes each)
-  uint32_t sbyteses[kSweeps][kSlots];
-  // Scales: lane (i, kb) fetches alpha and beta of tile row 4 kb + (i & 3) and
-  // slot i >> 2, so that each row of 16 lanes holds the 4 x 4 scales its C
-  // entries need (C holds rows 4 kb .. 4 kb + 3); a DPP row broadcast hands
-  // them out.  Slots past the range read zero scales (out of range).
-  uint32_t araws[kSweeps], braws[kSweeps];
-  {
-    const uint32_t ra_row = min(row_base + 4 * kb + (i & 3), d.out - 1);
+  for (uint32_t sw = 0; sw < kSweeps; ++sw) xg[sw].load(d, rx, gs0 + sw * kSlots, 0);
+  SweepW ws[kSweeps];
 #pragma unroll
-    for (uint32_t sw = 0; sw < kSweeps; ++sw) {
-      const uint32_t g = gs0 + sw * kSlots + (i >> 2);
-      const uint32_t so = g < gs1 ? (ra_row * G + g) * SB : 0x7FFFFFF0u;
-      araws[sw] = load_scale_raw<SF>(ra, so);
-      braws[sw] = K > 0 ? load_scale_raw<SF>(ra, so + boff) : 0u;
-    }
-  }
-#pragma unroll
-  for (uint32_t sw = 0; sw < kSweeps; ++sw)
-#pragma unroll
-    for (uint32_t q = 0; q < kSlots; ++q) {
-      const uint32_t g = min(gs0 + sw * kSlots + q, G - 1);
-      const u32x2_t c2 = __builtin_bit_cast(
-          u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rc, row * d.row_stride + g * 32 + 8 * kb, 0, kCached));
-      cws[sw][q / 2][2 * (q & 1)] = c2[0];
-      cws[sw][q / 2][2 * (q & 1) + 1] = c2[1];
-      uint32_t sb = 0;
-      if constexpr (K == 8) sb = __builtin_amdgcn_raw_buffer_load_b16(rs, (row * G + g) * 8 + 2 * kb, 0, kCached);
-      if constexpr (K == 4) sb = __builtin_amdgcn_raw_buffer_load_b8(rs, (row * G + g) * 4 + kb, 0, kCached);
-      if constexpr (K == 2) sb = __builtin_amdgcn_raw_buffer_load_b8(rs, (row * G + g) * 2 + (kb & 1), 0, kCached);
-      sbyteses[sw][q] = sb;
-    }
+  for (uint32_t sw = 0; sw < kSweeps; ++sw) ws[sw] = load_sweep<SF, K>(d, wr, row_base, gs0 + sw * kSlots, gs1, lane);
 #pragma unroll
   for (uint32_t sw = 0; sw < kSweeps; ++sw) {
-    const uint32_t c0 = gs0 + sw * kSlots;
-    if (c0 >= gs1) break;   // block-uniform
-    const uint32_t ns = min(kSlots, gs1 - c0);
-    const u32x4_t (&cw)[kSlots / 2] = cws[sw];
-    const uint32_t (&sbytes)[kSlots] = sbyteses[sw];
-    // X of this sweep into LDS
+    if (gs0 + sw * kSlots >= gs1) break;   // block-uniform
     __syncthreads();   // the previous sweep's readers are done
     xg[sw].store(xs);
     __syncthreads();
-#pragma unroll
-    for (uint32_t q = 0; q < kSlots; ++q) {
-      const bool valid = q < ns;   // block-uniform
-      // B operands: lane (n, kb) reads 64 bytes of X row 16 t + n
-      uint4 xb[NT][4];
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const uint4* src = reinterpret_cast<const uint4*>(xs + (t * 16 + i) * XStage<NT>::kRowBytes + q * 256 + 64 * kb);
-        uint4 raw[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) raw[k] = src[k];
-        x_operands(raw, xb[t]);
-      }
-      // T operands: one 64-bit shift positions the code pairs of both dwords
-      uint4 a[4];
-      const uint64_t cq = ((uint64_t)cw[q / 2][2 * (q & 1) + 1] << 32) | cw[q / 2][2 * (q & 1)];
-      a_operands<0>(cq, a);
-      f32x4_t sT[NT], sR[NT];
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        sT[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m = 0; m < 4; ++m) sT[t] = mfma(a[m], xb[t][m], sT[t]);
-      }
-      if constexpr (K > 0) {
-        // lane (i, kb) scatters sites kb * K / 4 .. of row i (K = 2: the
-        // lanes with kb < 2, one site each) into the R tile, operand m of
-        // lane L at [m][L]
-        constexpr int PER = K == 8 ? 2 : 1;
-        const bool writer = K != 2 || kb < 2;
-        uint32_t addr[PER];
-#pragma unroll
-        for (int j = 0; j < PER; ++j) {
-          const uint32_t sb = (sbytes[q] >> (8 * j)) & 0xFFu;
-          const uint32_t pos = sb & 127u, local = pos & 31u, rr = local & 15u;
-          const uint32_t o = 8 * (local >> 4) + (rr & 7u);
-          const uint32_t lt = (pos >> 5) * 16 + i;   // lane whose operand holds column pos of row i
-          addr[j] = ((o >> 2) * 64 + lt) * 8 + (o & 3) * 2 + (rr >> 3);
-          if (writer) rt16[addr[j]] = (sb & 128u) ? 0xC000u : 0x4000u;
-        }
-        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-        uint4 ro[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) ro[m] = rt4[m * 64 + lane];
-        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-#pragma unroll
-        for (int j = 0; j < PER; ++j)
-          if (writer) rt16[addr[j]] = 0;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          sR[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int m = 0; m < 4; ++m) sR[t] = mfma(ro[m], xb[t][m], sR[t]);
-        }
-      }
-      // C layout: lane holds rows 4 kb + j of the tile, batch column i
-      (void)valid;   // slots past the range have zero scales
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float al = scale_value<SF>(row_bcast(araws[sw], 4 * q + j));
-#pragma unroll
-        for (int t = 0; t < NT; ++t) C[t][j] = __builtin_fmaf(al, sT[t][j], C[t][j]);
-        if constexpr (K > 0) {
-          const float be = scale_value<SF>(row_bcast(braws[sw], 4 * q + j));
-#pragma unroll
-          for (int t = 0; t < NT; ++t) C[t][j] = __builtin_fmaf(be, sR[t][j], C[t][j]);
-        }
-      }
-    }
+    sweep_mfma<SF, K, NT>(xs, ws[sw], lane, rt4, rt16, C);
   }
 
   // the wavefront's tile: rows 4 kb + j, batch columns 16 t + i
+  const uint32_t i = lane & 15, kb = lane >> 4;
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -571,6 +597,124 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void k_mfma(MatDev d, float* __res
       if (yr < d.out && n < d.batch) P[((size_t)slice * d.batch + n) * d.out + yr] = 0.5f * C[t][j];
     }
 }
+
+// Large batches (k_prefill): a workgroup takes kMfmaTiles row tiles (128
+// rows) by one 32-row batch chunk over one range of sweeps.  A tile id t
+// names (row block, chunk, K split); the ids run chunk group by chunk group
+// (cgw chunks each), row block by row block within a group, so that tiles
+// that run at the same time share their X chunks and weight rows.  The
+// hardware hands consecutive workgroups to the 8 XCDs in turn, so block b
+// takes id (b % 8) * per_xcd + b / 8: each XCD walks its own contiguous run
+// of ids, and its L2 serves the reuse.
+// One tile: if nsplit == 1 the workgroup writes Y (with the low-rank term
+// from the z partials [zc][batch][terms]), else its split's partial sums
+// P[split][n][row] for k_reduce.
+template <int SF, int K>
+__global__ __launch_bounds__(kMfmaWaves * 64) void k_prefill(MatDev d, PrefillShape pg, const float* __restrict__ zpart,
+                                                              uint32_t zc, float* __restrict__ P) {
+  constexpr int NT = kPrefillCols / 16;
+  __shared__ __align__(16) uint8_t xs[NT * 16 * XStage<NT>::kRowBytes];
+  __shared__ __align__(16) uint8_t rts[kMfmaWaves * 4096];   // R tiles; z in the epilogue
+  static_assert(kMfmaWaves * 4096 >= NT * 16 * kMaxTerms * 4, "z of a chunk fits the R tiles' space");
+  const int lane = threadIdx.x & 63;
+  const uint32_t wave = wave_id();
+  static_assert(kMfmaTiles * 16 == 128, "a row block is 128 rows");
+  const uint32_t t = (blockIdx.x % 8) * pg.per_xcd + blockIdx.x / 8;
+  if (t >= pg.tiles) return;   // block-uniform
+  const uint32_t per_group = pg.rblocks * pg.nsplit * pg.cgw;
+  const uint32_t cg = t / per_group, r = t % per_group;
+  const uint32_t rb = r / (pg.nsplit * pg.cgw), r2 = r % (pg.nsplit * pg.cgw);
+  const uint32_t split = r2 / pg.cgw, chunk = cg * pg.cgw + r2 % pg.cgw;
+  if (chunk >= pg.chunks) return;   // block-uniform: the last group may be narrower
+  const uint32_t row_base = (rb * kMfmaTiles + wave) * 16, nbase = chunk * 16 * NT;
+  // sweeps of this split: an even share, the first ones one longer
+  const uint32_t q0 = pg.sweeps / pg.nsplit, rem = pg.sweeps % pg.nsplit;
+  const uint32_t sw0 = split * q0 + min(split, rem), sw1 = sw0 + q0 + (split < rem ? 1u : 0u);
+  const uint32_t G = d.groups, g1 = min(G, sw1 * kSlots);
+  uint4* rt4 = reinterpret_cast<uint4*>(rts + wave * 4096);
+  uint16_t* rt16 = reinterpret_cast<uint16_t*>(rts + wave * 4096);
+  const WRes wr = make_wres<K>(d);
+  const __amdgpu_buffer_rsrc_t rx = rsrc(d.x, 2 * ((d.batch - 1) * d.ldx + d.in));
+
+  f32x4_t C[NT];
+#pragma unroll
+  for (int u = 0; u < NT; ++u) C[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if constexpr (K > 0) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) rt4[m * 64 + lane] = make_uint4(0, 0, 0, 0);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  }
+
+  // each sweep's X and weights are loaded during the previous sweep
+  XStage<NT> xg;
+  xg.load(d, rx, sw0 * kSlots, nbase);
+  SweepW w = load_sweep<SF, K>(d, wr, row_base, sw0 * kSlots, g1, lane);
+  for (uint32_t c0 = sw0 * kSlots; c0 < g1; c0 += kSlots) {   // block-uniform
+    __syncthreads();   // the previous sweep's readers are done
+    xg.store(xs);
+    __syncthreads();
+    const SweepW cur = w;
+    if (c0 + kSlots < g1) {
+      xg.load(d, rx, c0 + kSlots, nbase);
+      w = load_sweep<SF, K>(d, wr, row_base, c0 + kSlots, g1, lane);
+    }
+    sweep_mfma<SF, K, NT>(xs, cur, lane, rt4, rt16, C);
+  }
+
+  const uint32_t i = lane & 15, kb = lane >> 4;
+  if (pg.nsplit > 1) {   // block-uniform
+#pragma unroll
+    for (int u = 0; u < NT; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t yr = row_base + 4 * kb + j, n = nbase + 16 * u + i;
+        if (yr < d.out && n < d.batch) P[((size_t)split * d.batch + n) * d.out + yr] = 0.5f * C[u][j];
+      }
+    return;
+  }
+
+  // z of the chunk's batch rows, summed over the column chunks in order,
+  // into the R tiles' space
+  float* zs = reinterpret_cast<float*>(rts);   // [NT * 16][terms]
+  __syncthreads();   // every wavefront is done with its R tile
+  for (uint32_t e = threadIdx.x; e < NT * 16 * d.terms; e += blockDim.x) {
+    const uint32_t n = nbase + e / d.terms, tt = e % d.terms;
+    float z = 0.f;
+    if (n < d.batch)
+      for (uint32_t cc = 0; cc < zc; ++cc) z += zpart[((size_t)cc * d.batch + n) * d.terms + tt];
+    zs[e] = z;
+  }
+  __syncthreads();
+  // the wavefront's tile: rows 4 kb + j, batch columns nbase + 16 u + i,
+  // plus sum_t (-1)^{U bit} z[n][t]
+  const uint32_t ub = (d.rank + 7) / 8;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t yr = row_base + 4 * kb + j;
+    if (yr >= d.out) continue;
+    float lr[NT] = {};
+    for (uint32_t p = 0; p < d.n_paths; ++p) {
+      const uint8_t* u8 = path_plane(d.U, d, p) + (size_t)yr * ub;
+      for (uint32_t rr = 0; rr < d.rank; ++rr) {
+        const bool neg = (u8[rr >> 3] >> (rr & 7)) & 1u;
+#pragma unroll
+        for (int u = 0; u < NT; ++u) {
+          const float zt = zs[(16 * u + i) * d.terms + p * d.rank + rr];
+          lr[u] += neg ? -zt : zt;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+      const uint32_t n = nbase + 16 * u + i;
+      if (n < d.batch) d.y[(size_t)n * d.ldy + yr] = 0.5f * C[u][j] + lr[u];
+    }
+  }
+}
+
+// Low-rank partials for k_prefill: block b computes terms 16 tc .. 16 tc + 15
+// of batch row n over a 4096-column chunk (z_block).
+__global__ __launch_bounds__(256) void k_zpre(MatDev d, float* __restrict__ zpart) { z_block(d, zpart, blockIdx.x); }
 
 // ---------------------------------------------------------------------------
 // Host side.
@@ -594,6 +738,11 @@ void launch_mfma_nt(uint32_t nt, dim3 grid, hipStream_t s, const MatDev& d, floa
   const dim3 block(64 * kMfmaWaves);
   if (nt == 1) hipLaunchKernelGGL((k_mfma<SF, K, 1>), grid, block, 0, s, d, P, zp, nz, slices);
   else hipLaunchKernelGGL((k_mfma<SF, K, 2>), grid, block, 0, s, d, P, zp, nz, slices);
+}
+
+template <int SF, int K>
+void launch_prefill_k(dim3 grid, hipStream_t s, const MatDev& d, const PrefillShape& S, const float* zp, float* P) {
+  hipLaunchKernelGGL((k_prefill<SF, K>), grid, dim3(64 * kMfmaWaves), 0, s, d, S, zp, S.zc, P);
 }
 
 int launch_reduce(const MatDev& d, const GemmShape& S, const float* zp, const float* P, uint32_t slices,
@@ -659,6 +808,34 @@ int launch_gemm_mfma(const wal_info& f, const MatDev& d, uint32_t batch, void* w
     default: launch_mfma_nt<WAL_SCALE_FP24, 8>(nt, grid, s, d, P, zp, nz, slices); break;
   }
   return launch_reduce(d, S, zp, P, slices, s);
+}
+
+int launch_gemm_prefill(const wal_info& f, const MatDev& d, uint32_t batch, void* ws, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const PrefillShape S = prefill_shape(f, batch);
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  float* zp = reinterpret_cast<float*>(w);
+  float* P = S.nsplit > 1 ? reinterpret_cast<float*>(w + S.off_p) : nullptr;
+  if (d.terms) {
+    const uint32_t nz = S.zc * batch * ((d.terms + kZTermsPerBlock - 1) / kZTermsPerBlock);
+    hipLaunchKernelGGL(k_zpre, dim3(nz), dim3(256), 0, s, d, zp);
+    if (hipGetLastError() != hipSuccess) return WAL_ERR_DEVICE;
+  }
+  const dim3 grid(8 * S.per_xcd);
+  switch (class_index(d)) {
+    case 0: launch_prefill_k<WAL_SCALE_FP16, 0>(grid, s, d, S, zp, P); break;
+    case 1: launch_prefill_k<WAL_SCALE_FP16, 2>(grid, s, d, S, zp, P); break;
+    case 2: launch_prefill_k<WAL_SCALE_FP16, 4>(grid, s, d, S, zp, P); break;
+    case 3: launch_prefill_k<WAL_SCALE_FP16, 8>(grid, s, d, S, zp, P); break;
+    case 4: launch_prefill_k<WAL_SCALE_FP24, 0>(grid, s, d, S, zp, P); break;
+    case 5: launch_prefill_k<WAL_SCALE_FP24, 2>(grid, s, d, S, zp, P); break;
+    case 6: launch_prefill_k<WAL_SCALE_FP24, 4>(grid, s, d, S, zp, P); break;
+    default: launch_prefill_k<WAL_SCALE_FP24, 8>(grid, s, d, S, zp, P); break;
+  }
+  if (hipGetLastError() != hipSuccess) return WAL_ERR_DEVICE;
+  if (S.nsplit == 1) return WAL_OK;
+  hipLaunchKernelGGL(k_reduce, dim3((d.out + 255) / 256, batch), dim3(256), 0, s, d, zp, P, S.nsplit, S.zc);
+  return hipGetLastError() == hipSuccess ? WAL_OK : WAL_ERR_DEVICE;
 }
 
 }  // namespace wal

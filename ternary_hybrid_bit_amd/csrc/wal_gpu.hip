@@ -750,6 +750,31 @@ int wal_gemm_small(const wal_info* info, const void* W_dev, const void* X_dev, i
   return WAL_OK;
 }
 
+int wal_gemm_prefill(const wal_info* info, const void* W_dev, const void* X_dev, int x_dtype, uint32_t batch,
+                     uint32_t ldx, float* Y_dev, uint32_t ldy, void* ws_dev, size_t ws_bytes, void* stream) {
+  int st = check_info(info);
+  if (st) return st;
+  if (batch == 0 || batch > WAL_MAX_PREFILL_BATCH) return WAL_ERR_ARG;
+  if (!W_dev || !X_dev || !Y_dev) return WAL_ERR_ARG;
+  if (x_dtype != WAL_X_F32 && x_dtype != WAL_X_BF16) return WAL_ERR_ARG;
+  if (ldx < info->d.in || ldy < info->d.out) return WAL_ERR_ARG;
+  if (x_dtype != WAL_X_BF16 || info->d.trit_fmt != WAL_TRIT_2BIT) return WAL_ERR_UNSUPPORTED;
+  if (!aligned(W_dev, 256) || !aligned(X_dev, 16) || !aligned(Y_dev, 4) || (ldx * 2u) % 16) return WAL_ERR_ALIGN;
+  const size_t xbytes = ((size_t)(batch - 1) * ldx + info->d.in) * 2;
+  const size_t ybytes = ((size_t)(batch - 1) * ldy + info->d.out) * 4;
+  if (xbytes >= (1ull << 31)) return WAL_ERR_SHAPE;   // X is addressed with 32-bit byte offsets
+  size_t need = 0;
+  if ((st = wal_prefill_workspace_size(info, batch, &need))) return st;
+  if (need && (!ws_dev || ws_bytes < need)) return ws_dev ? WAL_ERR_BUFFER : WAL_ERR_ARG;
+  if (ws_dev && !aligned(ws_dev, 16)) return WAL_ERR_ALIGN;
+  if (overlap(X_dev, xbytes, Y_dev, ybytes) || (need && (overlap(ws_dev, need, Y_dev, ybytes) ||
+                                                         overlap(ws_dev, need, X_dev, xbytes))))
+    return WAL_ERR_ARG;
+  if ((st = check_blob_size(info))) return st;
+  MatDev d = make_dev(info, W_dev, X_dev, Y_dev, static_cast<float*>(ws_dev), ldx, ldy, batch);
+  return launch_gemm_prefill(*info, d, batch, ws_dev, stream);
+}
+
 int wal_grouped_plan_size(uint32_t n, const wal_info* infos, uint32_t grid, int x_dtype, size_t* plan_bytes,
                           size_t* ws_bytes) {
   if (!n || !infos || !plan_bytes || !ws_bytes) return WAL_ERR_ARG;

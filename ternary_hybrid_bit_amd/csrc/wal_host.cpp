@@ -11,6 +11,7 @@
 // describe for their caches: anything malformed is rejected before use.
 #include "wal_internal.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 
@@ -434,16 +435,44 @@ int wal_workspace_size(const wal_info* info, uint32_t batch, size_t* bytes) {
   if (batch == 0 || batch > WAL_MAX_BATCH) return WAL_ERR_ARG;
   const int st = wal::check_info(info);
   if (st) return st;
-  // z_p[r] for every path, rank and batch column, the operand-order copy of X
-  // and the partial sums of the small-batch kernels (wal_gemv uses the first
-  // part only)
+  // z_p[r] for every path, rank and batch column and the partial sums of the
+  // small-batch kernels (wal_gemv uses the first part only)
   *bytes = (size_t)wal::gemm_shape(*info, batch).bytes;
+  return WAL_OK;
+}
+
+int wal_prefill_workspace_size(const wal_info* info, uint32_t batch, size_t* bytes) {
+  if (!info || !bytes) return WAL_ERR_ARG;
+  if (batch == 0 || batch > WAL_MAX_PREFILL_BATCH) return WAL_ERR_ARG;
+  const int st = wal::check_info(info);
+  if (st) return st;
+  *bytes = (size_t)wal::prefill_shape(*info, batch).bytes;
   return WAL_OK;
 }
 
 }  // extern "C"
 
 namespace wal {
+
+PrefillShape prefill_shape(const wal_info& f, uint32_t batch) {
+  PrefillShape S;
+  S.rblocks = (f.d.out + 127) / 128;
+  S.chunks = (batch + kPrefillCols - 1) / kPrefillCols;
+  S.sweeps = (f.groups + 3) / 4;
+  const uint64_t base = (uint64_t)S.rblocks * S.chunks;
+  S.nsplit = 1;
+  if (base < kPrefillTiles) S.nsplit = (uint32_t)std::min<uint64_t>(S.sweeps, (kPrefillTiles + base - 1) / base);
+  S.cgw = std::min<uint32_t>(8, S.chunks);
+  const uint64_t ngroups = (S.chunks + S.cgw - 1) / S.cgw;
+  const uint64_t ids = ngroups * S.rblocks * S.nsplit * S.cgw;
+  S.per_xcd = (uint32_t)((ids + 7) / 8);
+  S.tiles = (uint32_t)ids;
+  S.zc = (f.d.in + kZChunkCols - 1) / kZChunkCols;
+  const uint64_t terms = (uint64_t)f.d.n_paths * f.d.rank;
+  S.off_p = up(4 * terms * batch * S.zc, 256);
+  S.bytes = S.off_p + (S.nsplit > 1 ? up(4ull * S.nsplit * batch * f.d.out, 256) : 0);
+  return S;
+}
 
 GemmShape gemm_shape(const wal_info& f, uint32_t batch) {
   GemmShape S;

@@ -80,8 +80,13 @@ using SingleFn = void (*)(MatDev, uint32_t, uint32_t, float*);
 //    of the same launch the low-rank reductions of every batch column per
 //    4096-column chunk, zpart[chunk][n][term]; the second adds the passes and
 //    the chunks in a fixed order, adds the low-rank term and stores Y.
-//  * MFMA, one launch: a workgroup takes a 16-row tile over all columns and
-//    finishes its Y in LDS (no workspace).
+//  * MFMA: the first blocks of the launch write the low-rank partials; every
+//    other workgroup takes 128 rows by one kSliceCols-column slice for up to
+//    32 activation columns on the matrix cores and writes its slice's partial
+//    sums P[slice][n][row]; the same reduce kernel finishes Y.
+// Large batches (prefill) run MFMA workgroups of 128 rows by 32 activation
+// columns over all columns (or an even share of them, split when the tiles
+// alone would not fill the GPU) after a low-rank pre-pass; see PrefillShape.
 constexpr uint32_t kGemvRows = 8;
 constexpr uint32_t kGemvCols = 4;
 constexpr uint32_t kZChunkCols = 4096;   // columns per low-rank partial (small batch)
@@ -106,6 +111,23 @@ int launch_gemm_valu(const wal_info& f, const MatDev& d, uint32_t batch, void* w
 int launch_reduce_single(const MatDev& d, const float* zpart, uint32_t zc, const float* P, uint32_t slices,
                          void* stream);
 int launch_gemm_mfma(const wal_info& f, const MatDev& d, uint32_t batch, void* ws, void* stream);
+
+// Prefill products: tiles of 128 rows x kPrefillCols activation columns.  A
+// tile id names (row block, column chunk, K split); see k_prefill for the
+// order of the ids and their mapping to workgroups.  K splits are made only
+// while rblocks * chunks * nsplit < kPrefillTiles; their partial sums
+// P[split][n][row] go to the workspace after the low-rank partials
+// [zc][batch][terms].
+constexpr uint32_t kPrefillCols = 32;
+constexpr uint32_t kPrefillTiles = 512;   // workgroups the GPU holds at once (2 per CU)
+struct PrefillShape {
+  uint32_t rblocks, chunks, nsplit, sweeps;   // sweeps of 4 groups over the whole K
+  uint32_t cgw, per_xcd, tiles;               // chunks per id group, ids per XCD, padded ids
+  uint32_t zc;                                // low-rank partials per batch row
+  uint64_t off_p, bytes;                      // workspace layout
+};
+PrefillShape prefill_shape(const wal_info& f, uint32_t batch);
+int launch_gemm_prefill(const wal_info& f, const MatDev& d, uint32_t batch, void* ws, void* stream);
 
 // Host helpers implemented in wal_host.cpp.
 int check_info(const wal_info* info);

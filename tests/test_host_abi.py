@@ -216,6 +216,38 @@ def test_workspace_size():
         wal.wal_workspace_size(info, 33)
 
 
+def test_prefill_workspace_size():
+    """Low-rank partials z [chunk][batch][terms] | per-split partial sums
+    [splits][batch][out] when the K dimension is split: splits are made only
+    while the (128-row, 32-batch-row) tiles number fewer than 512, at most
+    one per 4-group sweep."""
+    def up(v):
+        return (v + 255) // 256 * 256
+
+    def expect(out, inp, terms, B):
+        tiles = ((out + 127) // 128) * ((B + 31) // 32)
+        sweeps = (inp // 128 + 3) // 4
+        nsplit = 1 if tiles >= 512 else min(sweeps, -(-512 // tiles))
+        z = up(4 * terms * B * ((inp + 4095) // 4096))
+        return z + (up(4 * nsplit * B * out) if nsplit > 1 else 0), nsplit
+
+    info = wal.wal_packed_size(wal.make_desc(4096, 12288, 8, 1, 16))
+    for B in (1, 64, 96, 200, 256, 512, 2048):
+        n, nsplit = expect(4096, 12288, 16, B)
+        assert wal.wal_prefill_workspace_size(info, B) == n, B
+    assert expect(4096, 12288, 16, 64)[1] == 8 and expect(4096, 12288, 16, 512)[1] == 1
+    info = wal.wal_packed_size(wal.make_desc(64, 1024, 0))
+    assert wal.wal_prefill_workspace_size(info, 1) == up(4 * 2 * 1 * 64)   # two splits of one sweep each
+    info = wal.wal_packed_size(wal.make_desc(64, 256, 0))
+    assert wal.wal_prefill_workspace_size(info, 1) == 0                     # one sweep: nothing to split
+    info = wal.wal_packed_size(wal.make_desc(16384, 512, 0))
+    assert wal.wal_prefill_workspace_size(info, 1024) == 0                 # no paths, no split
+    with pytest.raises(wal.WalError):
+        wal.wal_prefill_workspace_size(info, 0)
+    with pytest.raises(wal.WalError):
+        wal.wal_prefill_workspace_size(info, wal.WAL_MAX_PREFILL_BATCH + 1)
+
+
 def test_product_calls_check_arguments_before_any_launch():
     """Host-side checks of the product entry points return their status
     before touching the GPU (the pointers below are never dereferenced)."""
@@ -249,6 +281,17 @@ def test_product_calls_check_arguments_before_any_launch():
     assert gs(W, x, 1, 2, 256, y, 64, 0, ws, need - 4, None) == -5           # workspace too small
     assert gs(W, x, 1, 2, 256, y, 64, 0, None, 0, None) == -1                # workspace missing
     assert gs(W, x, 1, 2, 256, y, 64, 0, x + 256, need, None) == -1          # workspace overlaps X
+    need = wal.wal_prefill_workspace_size(info, 64)
+    gp = lambda *a: lib.wal_gemm_prefill(ctypes.byref(info), *a)  # noqa: E731
+    assert gp(W, x, 1, 0, 256, y, 64, ws, need, None) == -1                  # batch 0
+    assert gp(W, x, 1, 16385, 256, y, 64, ws, need, None) == -1              # batch too large
+    assert gp(W, x, 0, 64, 256, y, 64, ws, need, None) == -9                 # fp32 activations
+    assert gp(W, x, 1, 64, 255, y, 64, ws, need, None) == -1                 # ldx < in
+    assert gp(W, x, 1, 64, 260, y, 64, ws, need, None) == -6                 # row pitch
+    assert gp(W, x, 1, 64, 256, y, 64, ws, need - 4, None) == -5             # workspace too small
+    assert gp(W, x, 1, 64, 256, y, 64, None, 0, None) == -1                  # workspace missing
+    assert gp(W, x, 1, 64, 256, x + 256, 64, ws, need, None) == -1           # Y overlaps X
+    assert gp(W, x, 1, 16384, 1 << 17, y, 64, ws, need, None) == -2          # X beyond 2 GiB
     assert lib.wal_gemv_grouped(None, 0x1000, None) == -1
 
 
