@@ -206,7 +206,8 @@ int wal_gemv(const wal_info* info, const void* W_dev, const void* x_dev, int x_d
 
 /* Y = X W^T for a small batch (F.linear convention): row n of Y is W(x_n)
  * with x_n row n of X (WAL-Ternary-8B cards, "Representation").
- *   X_dev  [batch][ldx] activations (bf16 or fp32), ldx >= in, ldx*elem % 16 == 0
+ *   X_dev  [batch][ldx] activations (bf16 or fp32), ldx >= in, ldx*elem % 16 == 0,
+ *          ((batch - 1) * ldx + in) * elem < 2^31 bytes (else WAL_ERR_SHAPE)
  *   Y_dev  [batch][ldy] fp32 outputs, ldy >= out; columns past out untouched
  *   batch  1..WAL_MAX_BATCH
  *   mode   WAL_GEMM_VALU (batched GEMV: one decode of a row feeds every batch

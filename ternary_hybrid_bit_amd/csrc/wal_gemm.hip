@@ -57,20 +57,10 @@ __device__ __forceinline__ uint32_t load_sites(__amdgpu_buffer_rsrc_t r, uint32_
   return __builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, kStream);
 }
 
-// Raw scale bits at byte offset `off` of a resource (fp16: 2 bytes, fp24: 3);
-// out of range: 0.
-template <int SF>
-__device__ __forceinline__ uint32_t load_scale_raw(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  if constexpr (SF == WAL_SCALE_FP16) return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
-  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0) |
-         ((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, off + 1, 0, 0) << 8) |
-         ((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, off + 2, 0, 0) << 16);
-}
-
 // Lane n of each row of 16 lanes, to the whole row (DPP row_newbcast).
 __device__ __forceinline__ uint32_t row_bcast(uint32_t v, uint32_t n) {
   switch (n) {
-#define WAL_BC(N) case N: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x150 + N, 0xF, 0xF, false);
+#define WAL_BC(N) case N: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x150 + N, 0xF, 0xF, true);
     WAL_BC(0) WAL_BC(1) WAL_BC(2) WAL_BC(3) WAL_BC(4) WAL_BC(5) WAL_BC(6) WAL_BC(7)
     WAL_BC(8) WAL_BC(9) WAL_BC(10) WAL_BC(11) WAL_BC(12) WAL_BC(13) WAL_BC(14) default: WAL_BC(15)
 #undef WAL_BC
@@ -361,48 +351,81 @@ constexpr uint32_t kSweeps = kSliceCols / 128 / kSlots;
 constexpr uint32_t kMfmaTiles = 8;
 constexpr uint32_t kMfmaWaves = kMfmaTiles;
 
-// X rows nbase + 16 t .. + 15 of one sweep in LDS: [t][n][kSlots * 128
-// columns] bf16 (rows padded by 16 bytes, so that the 16 rows a B-operand
-// read touches start in different banks), about 16 KB per n-tile.  Thread j
-// loads 32 bytes of row (j >> 5) per n-tile.
-template <int NT>
-struct XStage {
-  static constexpr uint32_t kRowBytes = kSlots * 128 * 2 + 16;
-  u32x4_t v[NT][2];
+// X rows nbase .. nbase + 16 NT - 1 of one sweep of SL groups in LDS, in
+// MFMA operand order: one 1 KB block per (n-tile t, slot q, operand m) in
+// which lane L = (n, kb) finds its B operand at 16 L, so that every
+// B-operand read of a wavefront is one contiguous 1 KB (the only ds_read_b128
+// pattern free of bank conflicts on gfx950; row-padded layouts are not).
+// Operand m of lane (n, kb) holds the pairs (column k, column k + 8), k =
+// 4 (m & 1) .. + 3, of the 16-column half m >> 1 of the lane's 32-column block
+// kb: the trit pairs that the A-operand decode puts in the same slots.
+// Staging job j (one wavefront instruction pair) covers (t, q, half h): lane L
+// loads the 32 bytes of its row and half, permutes them into pair order and
+// writes both 16-byte operand chunks at 16 L of blocks m = 2h and 2h + 1.
+// The W wavefronts take the 2 NT SL jobs in turn.
+template <int NT, int SL>
+__device__ __forceinline__ uint32_t x_block(int t, uint32_t q, int m) { return ((t * SL + q) * 4 + m) * 1024; }
 
-  // X[n][128 c0 + 16 (j & 31) .. + 16], zero past the row's end; rows past
-  // the batch read row 0 (such B-operand columns only feed unused outputs).
+template <int NT, int W, int SL>
+struct XStage {
+  static constexpr uint32_t kBytes = NT * SL * 4 * 1024;
+  static constexpr int kPer = 2 * NT * SL / W;  // jobs per wavefront
+  static_assert(kPer * W == 2 * NT * SL, "whole jobs per wavefront");
+  u32x4_t v[kPer][2];
+
+  // X[n][128 (c0 + q) + 32 kb + 16 h .. + 16] of job j = wave + W u, zero
+  // past the row's end (bit 31 set: X is smaller than 2 GiB, so the buffer
+  // load returns zeros; an OR rather than a select keeps the address
+  // arithmetic unconditional, so no branch splits the loop); rows past the
+  // batch read row 0 (such B-operand columns only feed unused outputs).
   __device__ __forceinline__ void load(const MatDev& d, __amdgpu_buffer_rsrc_t rx, uint32_t c0, uint32_t nbase) {
-    const uint32_t j = threadIdx.x, r = j >> 5, col = 128 * c0 + 16 * (j & 31);
+    const uint32_t lane = threadIdx.x & 63, wave = wave_id();
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const uint32_t n = nbase + 16 * t + r;
-      const uint32_t off = col < d.in ? 2 * ((n < d.batch ? n : 0) * d.ldx + col) : 0x7FFFFFF0u;
-      v[t][0] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
-      v[t][1] = __builtin_amdgcn_raw_buffer_load_b128(rx, off + 16, 0, 0);
+    for (int u = 0; u < kPer; ++u) {
+      const uint32_t j = wave + W * u, t = j / (2 * SL), q = (j / 2) % SL, h = j & 1;
+      const uint32_t n = nbase + 16 * t + (lane & 15);
+      const uint32_t col = 128 * (c0 + q) + 32 * (lane >> 4) + 16 * h;
+      const uint32_t off = (2 * ((n < d.batch ? n : 0u) * d.ldx + col)) | (col < d.in ? 0u : 0x80000000u);
+      v[u][0] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+      v[u][1] = __builtin_amdgcn_raw_buffer_load_b128(rx, off + 16, 0, 0);
     }
   }
 
+  // Pair dword k = (column k, column k + 8): low halves of dwords k / 2 and
+  // k / 2 + 4 for even k, high halves for odd k (one v_perm_b32 each).
   __device__ __forceinline__ void store(uint8_t* xs) const {
-    const uint32_t j = threadIdx.x;
+    const uint32_t lane = threadIdx.x & 63, wave = wave_id();
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      u32x4_t* dst = reinterpret_cast<u32x4_t*>(xs + (t * 16 + (j >> 5)) * kRowBytes + 32 * (j & 31));
-      dst[0] = v[t][0];
-      dst[1] = v[t][1];
+    for (int u = 0; u < kPer; ++u) {
+      const uint32_t j = wave + W * u, t = j / (2 * SL), q = (j / 2) % SL, h = j & 1;
+      const uint32_t w[8] = {v[u][0][0], v[u][0][1], v[u][0][2], v[u][0][3],
+                             v[u][1][0], v[u][1][1], v[u][1][2], v[u][1][3]};
+      u32x4_t o[2];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        o[k >> 2][k & 3] = __builtin_amdgcn_perm(w[(k >> 1) + 4], w[k >> 1], (k & 1) ? 0x07060302u : 0x05040100u);
+      *reinterpret_cast<u32x4_t*>(xs + x_block<NT, SL>(t, q, 2 * h) + 16 * lane) = o[0];
+      *reinterpret_cast<u32x4_t*>(xs + x_block<NT, SL>(t, q, 2 * h + 1) + 16 * lane) = o[1];
     }
   }
 };
 
-// One wavefront's weights for one sweep: lane (i, kb) holds the codes of row
-// i of its tile (8 bytes per slot), its site bytes, and the scales of tile
-// row 4 kb + (i & 3) for slot i >> 2 (so that each row of 16 lanes holds the
-// 4 x 4 scales its C entries need, C holding rows 4 kb .. 4 kb + 3; a DPP row
-// broadcast hands them out).
+// One wavefront's weights for one sweep of SL groups: lane (i, kb) holds the
+// codes of row i of its tile (8 bytes per slot), its site bytes, and the
+// scales of tile row 4 kb + (i & 3) for slot i >> 2 (so that each row of 16
+// lanes holds the 4 x SL scales its C entries need, C holding rows 4 kb ..
+// 4 kb + 3; a DPP row broadcast hands them out).
+// Every field holds a load's result as loaded (16-bit or byte loads keep
+// their own type): conversions happen where the values are used, so that no
+// instruction needs a load before its sweep (a zero-extension hoisted to the
+// loop head would wait for the next sweep's loads).
+template <int SL>
 struct SweepW {
-  u32x4_t cw[kSlots / 2];   // codes of slots 2h, 2h + 1 (8 bytes each)
-  uint32_t sbytes[kSlots];
-  uint32_t araw, braw;
+  static_assert(SL == 2 || SL == 4, "sweeps of 2 or 4 groups");
+  u32x4_t cw[SL / 2];      // codes of slots 2h, 2h + 1 (8 bytes each)
+  uint16_t sites[SL];      // site byte(s) of the lane (K = 8: two, else one)
+  uint16_t a16, b16;       // fp16 scales
+  uint8_t a24[3], b24[3];  // fp24 scales, byte by byte
 };
 
 // Resources and fixed offsets of the weight loads.
@@ -423,114 +446,170 @@ __device__ __forceinline__ WRes make_wres(const MatDev& d) {
   return w;
 }
 
-// Groups c0 .. c0 + kSlots - 1 of the tile rows row_base .. + 15; groups at
-// or past gend get zero scales (their codes and sites repeat the matrix's
-// last group: in bounds, dropped by the zero scale).  The loads read 8 to
-// 32 bytes per row and instruction; the rest of each cache line is read
+// Groups c0 .. c0 + SL - 1 of the tile rows row_base .. + 15; groups at or
+// past gend get zero scales (their codes and sites repeat the matrix's last
+// group: in bounds, dropped by the zero scale).  The loads read 8 to 32
+// bytes per row and instruction; the rest of each cache line is read
 // moments later by the next slots, so they keep the default cache policy.
-template <int SF, int K>
-__device__ __forceinline__ SweepW load_sweep(const MatDev& d, const WRes& w, uint32_t row_base, uint32_t c0,
-                                             uint32_t gend, int lane) {
+// K = 2: lanes kb and kb + 2 read the same site (their writes coincide).
+template <int SF, int K, int SL>
+__device__ __forceinline__ SweepW<SL> load_sweep(const MatDev& d, const WRes& w, uint32_t row_base, uint32_t c0,
+                                                 uint32_t gend, int lane) {
   constexpr uint32_t SB = SF == WAL_SCALE_FP16 ? 2 : 3;
   const uint32_t i = lane & 15, kb = lane >> 4, G = d.groups;
   const uint32_t row = min(row_base + i, d.out - 1);
-  SweepW s;
+  SweepW<SL> s;
   {
     const uint32_t ra_row = min(row_base + 4 * kb + (i & 3), d.out - 1);
     const uint32_t g = c0 + (i >> 2);
-    const uint32_t so = g < gend ? (ra_row * G + g) * SB : 0x7FFFFFF0u;
-    s.araw = load_scale_raw<SF>(w.ra, so);
-    s.braw = K > 0 ? load_scale_raw<SF>(w.ra, so + w.boff) : 0u;
+    const uint32_t so = g < gend && (i >> 2) < (uint32_t)SL ? (ra_row * G + g) * SB : 0x7FFFFFF0u;
+    if constexpr (SF == WAL_SCALE_FP16) {
+      s.a16 = __builtin_amdgcn_raw_buffer_load_b16(w.ra, so, 0, 0);
+      s.b16 = K > 0 ? __builtin_amdgcn_raw_buffer_load_b16(w.ra, so + w.boff, 0, 0) : (uint16_t)0;
+    } else {
+#pragma unroll
+      for (int b = 0; b < 3; ++b) {
+        s.a24[b] = __builtin_amdgcn_raw_buffer_load_b8(w.ra, so + b, 0, 0);
+        s.b24[b] = K > 0 ? __builtin_amdgcn_raw_buffer_load_b8(w.ra, so + w.boff + b, 0, 0) : (uint8_t)0;
+      }
+    }
   }
 #pragma unroll
-  for (uint32_t q = 0; q < kSlots; ++q) {
+  for (uint32_t q = 0; q < (uint32_t)SL; ++q) {
     const uint32_t g = min(c0 + q, G - 1);
     const u32x2_t c2 =
         __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(w.rc, row * d.row_stride + g * 32 + 8 * kb, 0, 0));
     s.cw[q / 2][2 * (q & 1)] = c2[0];
     s.cw[q / 2][2 * (q & 1) + 1] = c2[1];
-    uint32_t sb = 0;
-    if constexpr (K == 8) sb = __builtin_amdgcn_raw_buffer_load_b16(w.rs, (row * G + g) * 8 + 2 * kb, 0, 0);
-    if constexpr (K == 4) sb = __builtin_amdgcn_raw_buffer_load_b8(w.rs, (row * G + g) * 4 + kb, 0, 0);
-    if constexpr (K == 2) sb = __builtin_amdgcn_raw_buffer_load_b8(w.rs, (row * G + g) * 2 + (kb & 1), 0, 0);
-    s.sbytes[q] = sb;
+    s.sites[q] = 0;
+    if constexpr (K == 8) s.sites[q] = __builtin_amdgcn_raw_buffer_load_b16(w.rs, (row * G + g) * 8 + 2 * kb, 0, 0);
+    if constexpr (K == 4) s.sites[q] = __builtin_amdgcn_raw_buffer_load_b8(w.rs, (row * G + g) * 4 + kb, 0, 0);
+    if constexpr (K == 2) s.sites[q] = __builtin_amdgcn_raw_buffer_load_b8(w.rs, (row * G + g) * 2 + (kb & 1), 0, 0);
   }
   return s;
 }
 
-// The four slots of a sweep for one wavefront: C[t][j] += alpha sT + beta sR
-// for tile row 4 kb + j and batch column 16 t + i (decoded values are 2x).
-// xs: the sweep's X in LDS; rt4 / rt16: the wavefront's R tile (zero on
-// entry and on exit).
-template <int SF, int K, int NT>
-__device__ __forceinline__ void sweep_mfma(const uint8_t* xs, const SweepW& w, int lane, uint4* rt4, uint16_t* rt16,
-                                           f32x4_t (&C)[NT]) {
+// The lane's raw alpha and beta bits (32-bit) of a loaded sweep.  The empty
+// asm statements pin the conversion to the point of use: without them the
+// compiler merges the fp24 bytes (and zero-extends fp16) where the loop-carried
+// values meet, at the loop head, which then waits for loads still in flight.
+__device__ __forceinline__ uint32_t pin(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+template <int SF, int SL>
+__device__ __forceinline__ uint32_t alpha_raw(const SweepW<SL>& w) {
+  if constexpr (SF == WAL_SCALE_FP16) return pin(w.a16);
+  return pin(w.a24[0]) | (pin(w.a24[1]) << 8) | (pin(w.a24[2]) << 16);
+}
+template <int SF, int SL>
+__device__ __forceinline__ uint32_t beta_raw(const SweepW<SL>& w) {
+  if constexpr (SF == WAL_SCALE_FP16) return pin(w.b16);
+  return pin(w.b24[0]) | (pin(w.b24[1]) << 8) | (pin(w.b24[2]) << 16);
+}
+
+// The SL slots of a sweep for one wavefront and RT row tiles:
+// C[r][t][j] += alpha sT + beta sR for row 4 kb + j of tile r and batch
+// column 16 t + i (decoded values are 2x).  xs: the sweep's X in LDS
+// (operand order); rtile: the wavefront's RT R tiles of 4 KB (zero on entry
+// and on exit).  Each B operand read from LDS feeds the T and R products of
+// all RT tiles: LDS bandwidth (about 128 bytes per clock and CU) is what
+// bounds these kernels, and a 1 KB operand read per two MFMAs would use all
+// of it.
+template <int SF, int K, int NT, int RT, int SL>
+__device__ __forceinline__ void sweep_mfma(const uint8_t* xs, const SweepW<SL> (&w)[RT], int lane, uint8_t* rtile,
+                                           f32x4_t (&C)[RT][NT]) {
   const uint32_t i = lane & 15, kb = lane >> 4;
 #pragma unroll
-  for (uint32_t q = 0; q < kSlots; ++q) {
-    // B operands: lane (n, kb) reads 64 bytes of X row 16 t + n
-    uint4 xb[NT][4];
+  for (uint32_t q = 0; q < (uint32_t)SL; ++q) {
+    constexpr int PER = K == 8 ? 2 : 1;
+    uint32_t addr[RT][PER];
+    uint4 ro[RT][4];
+    if constexpr (K > 0) {
+      // lane (i, kb) scatters sites kb * K / 4 .. of row i (K = 2: site kb & 1,
+      // lanes kb and kb + 2 writing the same value) into its R tiles, operand
+      // m of lane L at [m][L]
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const uint4* src = reinterpret_cast<const uint4*>(xs + (t * 16 + i) * XStage<NT>::kRowBytes + q * 256 + 64 * kb);
-      uint4 raw[4];
+      for (int r = 0; r < RT; ++r) {
+        uint16_t* rt16 = reinterpret_cast<uint16_t*>(rtile + 4096 * r);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) raw[k] = src[k];
-      x_operands(raw, xb[t]);
+        for (int j = 0; j < PER; ++j) {
+          const uint32_t sb = ((uint32_t)w[r].sites[q] >> (8 * j)) & 0xFFu;
+          const uint32_t pos = sb & 127u, local = pos & 31u, rr = local & 15u;
+          const uint32_t o = 8 * (local >> 4) + (rr & 7u);
+          const uint32_t lt = (pos >> 5) * 16 + i;   // lane whose operand holds column pos of row i
+          addr[r][j] = ((o >> 2) * 64 + lt) * 8 + (o & 3) * 2 + (rr >> 3);
+          rt16[addr[r][j]] = (sb & 128u) ? 0xC000u : 0x4000u;
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+      for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) ro[r][m] = reinterpret_cast<const uint4*>(rtile + 4096 * r)[m * 64 + lane];
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        uint16_t* rt16 = reinterpret_cast<uint16_t*>(rtile + 4096 * r);
+#pragma unroll
+        for (int j = 0; j < PER; ++j) rt16[addr[r][j]] = 0;
+      }
     }
     // T operands: one 64-bit shift positions the code pairs of both dwords
-    uint4 a[4];
-    const uint64_t cq = ((uint64_t)w.cw[q / 2][2 * (q & 1) + 1] << 32) | w.cw[q / 2][2 * (q & 1)];
-    a_operands<0>(cq, a);
-    f32x4_t sT[NT], sR[NT];
+    uint4 a[RT][4];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const uint64_t cq = ((uint64_t)w[r].cw[q / 2][2 * (q & 1) + 1] << 32) | w[r].cw[q / 2][2 * (q & 1)];
+      a_operands<0>(cq, a[r]);
+    }
+    // scales of the lane's C rows 4 kb + j (a DPP row broadcast)
+    float al[RT][4], be[RT][4];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const uint32_t araw = alpha_raw<SF>(w[r]), braw = K > 0 ? beta_raw<SF>(w[r]) : 0u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        al[r][j] = scale_value<SF>(row_bcast(araw, 4 * q + j));
+        be[r][j] = K > 0 ? scale_value<SF>(row_bcast(braw, 4 * q + j)) : 0.f;
+      }
+    }
+    // B operands of lane (n, kb) for X row 16 t + n: contiguous 1 KB reads,
+    // those of n-tile t + 1 issued before the products of n-tile t (the
+    // scheduling barriers keep the compiler from hoisting more of them)
+    uint4 xn[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) xn[m] = *reinterpret_cast<const uint4*>(xs + x_block<NT, SL>(0, q, m) + 16 * lane);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      sT[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      uint4 xb[4];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) sT[t] = mfma(a[m], xb[t][m], sT[t]);
-    }
-    if constexpr (K > 0) {
-      // lane (i, kb) scatters sites kb * K / 4 .. of row i (K = 2: the lanes
-      // with kb < 2, one site each) into the R tile, operand m of lane L at
-      // [m][L]
-      constexpr int PER = K == 8 ? 2 : 1;
-      const bool writer = K != 2 || kb < 2;
-      uint32_t addr[PER];
+      for (int m = 0; m < 4; ++m) xb[m] = xn[m];
+      if (t + 1 < NT) {
 #pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const uint32_t sb = (w.sbytes[q] >> (8 * j)) & 0xFFu;
-        const uint32_t pos = sb & 127u, local = pos & 31u, rr = local & 15u;
-        const uint32_t o = 8 * (local >> 4) + (rr & 7u);
-        const uint32_t lt = (pos >> 5) * 16 + i;   // lane whose operand holds column pos of row i
-        addr[j] = ((o >> 2) * 64 + lt) * 8 + (o & 3) * 2 + (rr >> 3);
-        if (writer) rt16[addr[j]] = (sb & 128u) ? 0xC000u : 0x4000u;
+        for (int m = 0; m < 4; ++m)
+          xn[m] = *reinterpret_cast<const uint4*>(xs + x_block<NT, SL>(t + 1, q, m) + 16 * lane);
       }
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-      uint4 ro[4];
+      f32x4_t sT[RT], sR[RT];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) ro[m] = rt4[m * 64 + lane];
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-#pragma unroll
-      for (int j = 0; j < PER; ++j)
-        if (writer) rt16[addr[j]] = 0;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        sR[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m = 0; m < 4; ++m) sR[t] = mfma(ro[m], xb[t][m], sR[t]);
+      for (int r = 0; r < RT; ++r) {
+        sT[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        sR[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
-    }
-    // C layout: lane holds rows 4 kb + j of the tile, batch column i
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float al = scale_value<SF>(row_bcast(w.araw, 4 * q + j));
+      for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int t = 0; t < NT; ++t) C[t][j] = __builtin_fmaf(al, sT[t][j], C[t][j]);
-      if constexpr (K > 0) {
-        const float be = scale_value<SF>(row_bcast(w.braw, 4 * q + j));
+        for (int r = 0; r < RT; ++r) {
+          sT[r] = mfma(a[r][m], xb[m], sT[r]);
+          if constexpr (K > 0) sR[r] = mfma(ro[r][m], xb[m], sR[r]);
+        }
 #pragma unroll
-        for (int t = 0; t < NT; ++t) C[t][j] = __builtin_fmaf(be, sR[t][j], C[t][j]);
-      }
+      for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          C[r][t][j] = __builtin_fmaf(al[r][j], sT[r][j], C[r][t][j]);
+          if constexpr (K > 0) C[r][t][j] = __builtin_fmaf(be[r][j], sR[r][j], C[r][t][j]);
+        }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
@@ -547,44 +626,42 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void k_mfma(MatDev d, float* __res
     z_block(d, zpart, blockIdx.x);
     return;
   }
-  static_assert(kMfmaWaves * 64 == 512 && kSlots * 128 * 2 == 32 * 32, "XStage: 32 threads of 32 bytes per X row");
-  __shared__ __align__(16) uint8_t xs[NT * 16 * XStage<NT>::kRowBytes];
+  __shared__ __align__(16) uint8_t xs[XStage<NT, kMfmaWaves, kSlots>::kBytes];
   __shared__ __align__(16) uint8_t rts[kMfmaWaves * 4096];   // per-wavefront R tiles
   const int lane = threadIdx.x & 63;
   const uint32_t wave = wave_id();
   const uint32_t rb = (blockIdx.x - nz) / slices, slice = (blockIdx.x - nz) % slices;
   const uint32_t row_base = (rb * kMfmaTiles + wave) * 16;
   const uint32_t gs0 = slice * (kSliceCols / 128), gs1 = min(d.groups, gs0 + kSliceCols / 128);
-  uint4* rt4 = reinterpret_cast<uint4*>(rts + wave * 4096);
-  uint16_t* rt16 = reinterpret_cast<uint16_t*>(rts + wave * 4096);
+  uint8_t* rtile = rts + wave * 4096;
   const WRes wr = make_wres<K>(d);
   const __amdgpu_buffer_rsrc_t rx = rsrc(d.x, 2 * ((d.batch - 1) * d.ldx + d.in));
 
-  f32x4_t C[NT];
+  f32x4_t C[1][NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) C[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < NT; ++t) C[0][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   if constexpr (K > 0) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) rt4[m * 64 + lane] = make_uint4(0, 0, 0, 0);
+    for (int m = 0; m < 4; ++m) reinterpret_cast<uint4*>(rtile)[m * 64 + lane] = make_uint4(0, 0, 0, 0);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   }
 
   // Every load of the slice first: X of both sweeps (L2), then the weights
   // of both sweeps (HBM).  Rows differ across the lanes, so the row offsets
   // go in the voffset.
-  XStage<NT> xg[kSweeps];
+  XStage<NT, kMfmaWaves, kSlots> xg[kSweeps];
 #pragma unroll
   for (uint32_t sw = 0; sw < kSweeps; ++sw) xg[sw].load(d, rx, gs0 + sw * kSlots, 0);
-  SweepW ws[kSweeps];
+  SweepW<kSlots> ws[kSweeps][1];
 #pragma unroll
-  for (uint32_t sw = 0; sw < kSweeps; ++sw) ws[sw] = load_sweep<SF, K>(d, wr, row_base, gs0 + sw * kSlots, gs1, lane);
+  for (uint32_t sw = 0; sw < kSweeps; ++sw) ws[sw][0] = load_sweep<SF, K, kSlots>(d, wr, row_base, gs0 + sw * kSlots, gs1, lane);
 #pragma unroll
   for (uint32_t sw = 0; sw < kSweeps; ++sw) {
     if (gs0 + sw * kSlots >= gs1) break;   // block-uniform
     __syncthreads();   // the previous sweep's readers are done
     xg[sw].store(xs);
     __syncthreads();
-    sweep_mfma<SF, K, NT>(xs, ws[sw], lane, rt4, rt16, C);
+    sweep_mfma<SF, K, NT, 1, kSlots>(xs, ws[sw], lane, rtile, C);
   }
 
   // the wavefront's tile: rows 4 kb + j, batch columns 16 t + i
@@ -594,90 +671,134 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void k_mfma(MatDev d, float* __res
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t yr = row_base + 4 * kb + j, n = 16 * t + i;
-      if (yr < d.out && n < d.batch) P[((size_t)slice * d.batch + n) * d.out + yr] = 0.5f * C[t][j];
+      if (yr < d.out && n < d.batch) P[((size_t)slice * d.batch + n) * d.out + yr] = 0.5f * C[0][t][j];
     }
 }
 
-// Large batches (k_prefill): a workgroup takes kMfmaTiles row tiles (128
-// rows) by one 32-row batch chunk over one range of sweeps.  A tile id t
-// names (row block, chunk, K split); the ids run chunk group by chunk group
-// (cgw chunks each), row block by row block within a group, so that tiles
-// that run at the same time share their X chunks and weight rows.  The
-// hardware hands consecutive workgroups to the 8 XCDs in turn, so block b
-// takes id (b % 8) * per_xcd + b / 8: each XCD walks its own contiguous run
-// of ids, and its L2 serves the reuse.
-// One tile: if nsplit == 1 the workgroup writes Y (with the low-rank term
-// from the z partials [zc][batch][terms]), else its split's partial sums
+// Large batches (k_prefill): a workgroup of kPrefillWaves wavefronts takes
+// prefill_rows(SF) rows (RT 16-row tiles per wavefront) by one
+// kPrefillCols-row batch chunk (four n-tiles) over one range of sweeps: each
+// decoded A operand feeds four n-tiles, and each B operand read from LDS the
+// T and R products of the wavefront's row tiles.  A tile id t names (row block, chunk,
+// K split); the ids run chunk group by chunk group (cgw chunks each), row
+// block by row block within a group, so that tiles that run at the same time
+// share their X chunks and weight rows.  The hardware hands consecutive
+// workgroups to the 8 XCDs in turn, so block b takes id (b % 8) * per_xcd +
+// b / 8: each XCD walks its own contiguous run of ids, and its L2 serves the
+// reuse.  If nsplit == 1 the workgroup writes Y (with the low-rank term from
+// the z partials [zc][batch][terms]), else its split's partial sums
 // P[split][n][row] for k_reduce.
+constexpr int kPrefillSL = (int)kPrefillSweepGroups;
+
 template <int SF, int K>
-__global__ __launch_bounds__(kMfmaWaves * 64) void k_prefill(MatDev d, PrefillShape pg, const float* __restrict__ zpart,
-                                                              uint32_t zc, float* __restrict__ P) {
-  constexpr int NT = kPrefillCols / 16;
-  __shared__ __align__(16) uint8_t xs[NT * 16 * XStage<NT>::kRowBytes];
-  __shared__ __align__(16) uint8_t rts[kMfmaWaves * 4096];   // R tiles; z in the epilogue
-  static_assert(kMfmaWaves * 4096 >= NT * 16 * kMaxTerms * 4, "z of a chunk fits the R tiles' space");
+__global__ __launch_bounds__(kPrefillWaves * 64) void k_prefill(MatDev d, PrefillShape pg,
+                                                                 const float* __restrict__ zpart, uint32_t zc,
+                                                                 float* __restrict__ P) {
+  constexpr int NT = kPrefillCols / 16, W = kPrefillWaves, SL = kPrefillSL;
+  constexpr int RT = SF == WAL_SCALE_FP16 ? 2 : 1;   // row tiles per wavefront
+  static_assert(W * RT * 16 == prefill_rows(SF), "rows of a prefill workgroup");
+  using XS = XStage<NT, W, SL>;
+  __shared__ __align__(16) uint8_t xs[2][XS::kBytes];   // double-buffered sweeps; z in the epilogue
+  __shared__ __align__(16) uint8_t rts[W * RT * 4096];   // R tiles
+  static_assert(2 * XS::kBytes >= NT * 16 * kMaxTerms * 4, "z of a chunk fits the X buffers' space");
   const int lane = threadIdx.x & 63;
   const uint32_t wave = wave_id();
-  static_assert(kMfmaTiles * 16 == 128, "a row block is 128 rows");
   const uint32_t t = (blockIdx.x % 8) * pg.per_xcd + blockIdx.x / 8;
   if (t >= pg.tiles) return;   // block-uniform
   const uint32_t per_group = pg.rblocks * pg.nsplit * pg.cgw;
-  const uint32_t cg = t / per_group, r = t % per_group;
-  const uint32_t rb = r / (pg.nsplit * pg.cgw), r2 = r % (pg.nsplit * pg.cgw);
+  const uint32_t cg = t / per_group, rem0 = t % per_group;
+  const uint32_t rb = rem0 / (pg.nsplit * pg.cgw), r2 = rem0 % (pg.nsplit * pg.cgw);
   const uint32_t split = r2 / pg.cgw, chunk = cg * pg.cgw + r2 % pg.cgw;
   if (chunk >= pg.chunks) return;   // block-uniform: the last group may be narrower
-  const uint32_t row_base = (rb * kMfmaTiles + wave) * 16, nbase = chunk * 16 * NT;
+  const uint32_t row_base = rb * prefill_rows(SF) + wave * 16 * RT, nbase = chunk * kPrefillCols;
   // sweeps of this split: an even share, the first ones one longer
   const uint32_t q0 = pg.sweeps / pg.nsplit, rem = pg.sweeps % pg.nsplit;
   const uint32_t sw0 = split * q0 + min(split, rem), sw1 = sw0 + q0 + (split < rem ? 1u : 0u);
-  const uint32_t G = d.groups, g1 = min(G, sw1 * kSlots);
-  uint4* rt4 = reinterpret_cast<uint4*>(rts + wave * 4096);
-  uint16_t* rt16 = reinterpret_cast<uint16_t*>(rts + wave * 4096);
+  const uint32_t G = d.groups, g0 = sw0 * SL, g1 = min(G, sw1 * SL);
+  const uint32_t nsw = (g1 - g0 + SL - 1) / SL;   // >= 1
+  uint8_t* rtile = rts + wave * RT * 4096;
   const WRes wr = make_wres<K>(d);
   const __amdgpu_buffer_rsrc_t rx = rsrc(d.x, 2 * ((d.batch - 1) * d.ldx + d.in));
 
-  f32x4_t C[NT];
+  f32x4_t C[RT][NT];
 #pragma unroll
-  for (int u = 0; u < NT; ++u) C[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int u = 0; u < NT; ++u) C[r][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   if constexpr (K > 0) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) rt4[m * 64 + lane] = make_uint4(0, 0, 0, 0);
+    for (int m = 0; m < 4 * RT; ++m) reinterpret_cast<uint4*>(rtile)[m * 64 + lane] = make_uint4(0, 0, 0, 0);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   }
 
-  // each sweep's X and weights are loaded during the previous sweep
-  XStage<NT> xg;
-  xg.load(d, rx, sw0 * kSlots, nbase);
-  SweepW w = load_sweep<SF, K>(d, wr, row_base, sw0 * kSlots, g1, lane);
-  for (uint32_t c0 = sw0 * kSlots; c0 < g1; c0 += kSlots) {   // block-uniform
-    __syncthreads();   // the previous sweep's readers are done
-    xg.store(xs);
-    __syncthreads();
-    const SweepW cur = w;
-    if (c0 + kSlots < g1) {
-      xg.load(d, rx, c0 + kSlots, nbase);
-      w = load_sweep<SF, K>(d, wr, row_base, c0 + kSlots, g1, lane);
+  // Sweep s computes from xs[s & 1] while the X of sweep s + 1 (loaded during
+  // sweep s - 1) goes to the other buffer and the loads of sweep s + 2 are
+  // issued; one barrier per sweep.  The loop runs two sweeps per trip, so
+  // that the weights of even and odd sweeps keep registers of their own (no
+  // copy waits for loads in flight), and always both: an odd count ends
+  // with one sweep past the split, whose scales load as zero (it adds
+  // exactly 0).  With no exit in the middle of a trip the loop entry and the
+  // back edge leave the same loads in flight, so each sweep waits only for
+  // its own data.  Loads past the split's last group read zero scales and X
+  // (or in-bounds codes, sites and X that the zero scales drop).
+  // (The scheduling barriers keep the prologue's loads in this order, the
+  // order of the loop's back edge.)
+  XS xg;
+  SweepW<SL> wa[RT], wb[RT];
+  xg.load(d, rx, g0, nbase);
+#pragma unroll
+  for (int r = 0; r < RT; ++r) wa[r] = load_sweep<SF, K, SL>(d, wr, row_base + 16 * r, g0, g1, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  xg.store(xs[0]);
+  __builtin_amdgcn_sched_barrier(0);
+  xg.load(d, rx, g0 + SL, nbase);
+#pragma unroll
+  for (int r = 0; r < RT; ++r) wb[r] = load_sweep<SF, K, SL>(d, wr, row_base + 16 * r, g0 + SL, g1, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  for (uint32_t sw = 0; sw < nsw; sw += 2) {   // block-uniform
+    // (scheduling barriers: no work of one sweep moves into the other, where
+    // it would wait for loads still in flight)
+    __builtin_amdgcn_sched_barrier(0);
+    sweep_mfma<SF, K, NT, RT, SL>(xs[0], wa, lane, rtile, C);
+    xg.store(xs[1]);   // its last readers finished before the previous barrier
+    {
+      const uint32_t c2 = g0 + (sw + 2) * SL;
+      xg.load(d, rx, c2, nbase);
+#pragma unroll
+      for (int r = 0; r < RT; ++r) wa[r] = load_sweep<SF, K, SL>(d, wr, row_base + 16 * r, c2, g1, lane);
     }
-    sweep_mfma<SF, K, NT>(xs, cur, lane, rt4, rt16, C);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    sweep_mfma<SF, K, NT, RT, SL>(xs[1], wb, lane, rtile, C);
+    xg.store(xs[0]);
+    {
+      const uint32_t c3 = g0 + (sw + 3) * SL;
+      xg.load(d, rx, c3, nbase);
+#pragma unroll
+      for (int r = 0; r < RT; ++r) wb[r] = load_sweep<SF, K, SL>(d, wr, row_base + 16 * r, c3, g1, lane);
+    }
+    __syncthreads();
   }
 
   const uint32_t i = lane & 15, kb = lane >> 4;
   if (pg.nsplit > 1) {   // block-uniform
 #pragma unroll
-    for (int u = 0; u < NT; ++u)
+    for (int r = 0; r < RT; ++r)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t yr = row_base + 4 * kb + j, n = nbase + 16 * u + i;
-        if (yr < d.out && n < d.batch) P[((size_t)split * d.batch + n) * d.out + yr] = 0.5f * C[u][j];
-      }
+      for (int u = 0; u < NT; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t yr = row_base + 16 * r + 4 * kb + j, n = nbase + 16 * u + i;
+          if (yr < d.out && n < d.batch) P[((size_t)split * d.batch + n) * d.out + yr] = 0.5f * C[r][u][j];
+        }
     return;
   }
 
   // z of the chunk's batch rows, summed over the column chunks in order,
-  // into the R tiles' space
-  float* zs = reinterpret_cast<float*>(rts);   // [NT * 16][terms]
-  __syncthreads();   // every wavefront is done with its R tile
-  for (uint32_t e = threadIdx.x; e < NT * 16 * d.terms; e += blockDim.x) {
+  // into the X buffers' space (the loop ended with a barrier: no reader left)
+  float* zs = reinterpret_cast<float*>(&xs[0][0]);   // [kPrefillCols][terms]
+  for (uint32_t e = threadIdx.x; e < kPrefillCols * d.terms; e += blockDim.x) {
     const uint32_t n = nbase + e / d.terms, tt = e % d.terms;
     float z = 0.f;
     if (n < d.batch)
@@ -685,31 +806,33 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void k_prefill(MatDev d, PrefillSh
     zs[e] = z;
   }
   __syncthreads();
-  // the wavefront's tile: rows 4 kb + j, batch columns nbase + 16 u + i,
-  // plus sum_t (-1)^{U bit} z[n][t]
+  // the wavefront's tiles: rows 16 r + 4 kb + j, batch columns nbase + 16 u
+  // + i, plus sum_t (-1)^{U bit} z[n][t]
   const uint32_t ub = (d.rank + 7) / 8;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t yr = row_base + 4 * kb + j;
-    if (yr >= d.out) continue;
-    float lr[NT] = {};
-    for (uint32_t p = 0; p < d.n_paths; ++p) {
-      const uint8_t* u8 = path_plane(d.U, d, p) + (size_t)yr * ub;
-      for (uint32_t rr = 0; rr < d.rank; ++rr) {
-        const bool neg = (u8[rr >> 3] >> (rr & 7)) & 1u;
+  for (int r = 0; r < RT; ++r)
 #pragma unroll
-        for (int u = 0; u < NT; ++u) {
-          const float zt = zs[(16 * u + i) * d.terms + p * d.rank + rr];
-          lr[u] += neg ? -zt : zt;
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t yr = row_base + 16 * r + 4 * kb + j;
+      if (yr >= d.out) continue;
+      float lr[NT] = {};
+      for (uint32_t p = 0; p < d.n_paths; ++p) {
+        const uint8_t* u8 = path_plane(d.U, d, p) + (size_t)yr * ub;
+        for (uint32_t rr = 0; rr < d.rank; ++rr) {
+          const bool neg = (u8[rr >> 3] >> (rr & 7)) & 1u;
+#pragma unroll
+          for (int u = 0; u < NT; ++u) {
+            const float zt = zs[(16 * u + i) * d.terms + p * d.rank + rr];
+            lr[u] += neg ? -zt : zt;
+          }
         }
       }
-    }
 #pragma unroll
-    for (int u = 0; u < NT; ++u) {
-      const uint32_t n = nbase + 16 * u + i;
-      if (n < d.batch) d.y[(size_t)n * d.ldy + yr] = 0.5f * C[u][j] + lr[u];
+      for (int u = 0; u < NT; ++u) {
+        const uint32_t n = nbase + 16 * u + i;
+        if (n < d.batch) d.y[(size_t)n * d.ldy + yr] = 0.5f * C[r][u][j] + lr[u];
+      }
     }
-  }
 }
 
 // Low-rank partials for k_prefill: block b computes terms 16 tc .. 16 tc + 15
@@ -742,7 +865,7 @@ void launch_mfma_nt(uint32_t nt, dim3 grid, hipStream_t s, const MatDev& d, floa
 
 template <int SF, int K>
 void launch_prefill_k(dim3 grid, hipStream_t s, const MatDev& d, const PrefillShape& S, const float* zp, float* P) {
-  hipLaunchKernelGGL((k_prefill<SF, K>), grid, dim3(64 * kMfmaWaves), 0, s, d, S, zp, S.zc, P);
+  hipLaunchKernelGGL((k_prefill<SF, K>), grid, dim3(64 * kPrefillWaves), 0, s, d, S, zp, S.zc, P);
 }
 
 int launch_reduce(const MatDev& d, const GemmShape& S, const float* zp, const float* P, uint32_t slices,

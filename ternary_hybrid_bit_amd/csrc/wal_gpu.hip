@@ -725,6 +725,7 @@ int wal_gemm_small(const wal_info* info, const void* W_dev, const void* X_dev, i
   if (!aligned(ws_dev, 16)) return WAL_ERR_ALIGN;
   const size_t xbytes = ((size_t)(batch - 1) * ldx + info->d.in) * xe;
   const size_t ybytes = ((size_t)(batch - 1) * ldy + info->d.out) * 4;
+  if (xbytes >= (1ull << 31)) return WAL_ERR_SHAPE;   // X is addressed with 32-bit byte offsets
   if (overlap(X_dev, xbytes, Y_dev, ybytes) || overlap(ws_dev, need, Y_dev, ybytes) ||
       overlap(ws_dev, need, X_dev, xbytes))
     return WAL_ERR_ARG;

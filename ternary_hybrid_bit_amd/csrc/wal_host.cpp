@@ -456,9 +456,10 @@ namespace wal {
 
 PrefillShape prefill_shape(const wal_info& f, uint32_t batch) {
   PrefillShape S;
-  S.rblocks = (f.d.out + 127) / 128;
+  const uint32_t rows = prefill_rows(f.d.scale_fmt);
+  S.rblocks = (f.d.out + rows - 1) / rows;
   S.chunks = (batch + kPrefillCols - 1) / kPrefillCols;
-  S.sweeps = (f.groups + 3) / 4;
+  S.sweeps = (f.groups + kPrefillSweepGroups - 1) / kPrefillSweepGroups;
   const uint64_t base = (uint64_t)S.rblocks * S.chunks;
   S.nsplit = 1;
   if (base < kPrefillTiles) S.nsplit = (uint32_t)std::min<uint64_t>(S.sweeps, (kPrefillTiles + base - 1) / base);

@@ -84,8 +84,8 @@ using SingleFn = void (*)(MatDev, uint32_t, uint32_t, float*);
 //    other workgroup takes 128 rows by one kSliceCols-column slice for up to
 //    32 activation columns on the matrix cores and writes its slice's partial
 //    sums P[slice][n][row]; the same reduce kernel finishes Y.
-// Large batches (prefill) run MFMA workgroups of 128 rows by 32 activation
-// columns over all columns (or an even share of them, split when the tiles
+// Large batches (prefill) run MFMA workgroups of 256 (fp16 scales) or 128
+// rows by 64 activation columns over all columns (or an even share of them, split when the tiles
 // alone would not fill the GPU) after a low-rank pre-pass; see PrefillShape.
 constexpr uint32_t kGemvRows = 8;
 constexpr uint32_t kGemvCols = 4;
@@ -112,16 +112,21 @@ int launch_reduce_single(const MatDev& d, const float* zpart, uint32_t zc, const
                          void* stream);
 int launch_gemm_mfma(const wal_info& f, const MatDev& d, uint32_t batch, void* ws, void* stream);
 
-// Prefill products: tiles of 128 rows x kPrefillCols activation columns.  A
-// tile id names (row block, column chunk, K split); see k_prefill for the
-// order of the ids and their mapping to workgroups.  K splits are made only
-// while rblocks * chunks * nsplit < kPrefillTiles; their partial sums
+// Prefill products: tiles of prefill_rows(scale format) rows x kPrefillCols
+// activation rows (two 16-row tiles per wavefront with fp16 scales, one with
+// fp24 scales, whose byte-wise loads need more registers).  A tile id names
+// (row block, column chunk, K split); see k_prefill for the order of the ids
+// and their mapping to workgroups.  K splits are made only while
+// rblocks * chunks * nsplit < kPrefillTiles; their partial sums
 // P[split][n][row] go to the workspace after the low-rank partials
 // [zc][batch][terms].
-constexpr uint32_t kPrefillCols = 32;
-constexpr uint32_t kPrefillTiles = 512;   // workgroups the GPU holds at once (2 per CU)
+constexpr uint32_t kPrefillWaves = 8;
+constexpr uint32_t prefill_rows(uint32_t scale_fmt) { return kPrefillWaves * 16 * (scale_fmt == WAL_SCALE_FP16 ? 2 : 1); }
+constexpr uint32_t kPrefillCols = 64;
+constexpr uint32_t kPrefillTiles = 256;   // workgroups the GPU holds at once (1 per CU)
+constexpr uint32_t kPrefillSweepGroups = 2;   // 128-column groups per sweep (a K split holds whole sweeps)
 struct PrefillShape {
-  uint32_t rblocks, chunks, nsplit, sweeps;   // sweeps of 4 groups over the whole K
+  uint32_t rblocks, chunks, nsplit, sweeps;   // sweeps of kPrefillSweepGroups groups over the whole K
   uint32_t cgw, per_xcd, tiles;               // chunks per id group, ids per XCD, padded ids
   uint32_t zc;                                // low-rank partials per batch row
   uint64_t off_p, bytes;                      // workspace layout

@@ -1,7 +1,7 @@
 """GPU parity of the prefill-size product Y = X W^T (wal_gemm_prefill) against
 the CPU oracle.
 
-The kernel tiles Y into 128 rows x 32 batch rows; with few tiles it splits
+The kernel tiles Y into 256 (fp16 scales) or 128 (fp24) rows x 64 batch rows; with few tiles it splits
 the K dimension and a reduce adds the splits, so the cases below cover both
 launches (split and whole), ragged row blocks and batch chunks, every site
 count, both scale formats and up to 256 low-rank terms.
@@ -40,11 +40,13 @@ def to_dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev())
 
 
-def split_count(out, inp, B):
+def split_count(out, inp, B, sf=0):
     """K splits of the launch (the library's rule, restated for the test
-    names): while the tiles number fewer than 512, up to one per sweep."""
-    tiles = ((out + 127) // 128) * ((B + 31) // 32)
-    return 1 if tiles >= 512 else min((inp // 128 + 3) // 4, -(-512 // tiles))
+    names): while the tiles (256 x 64 with fp16 scales, 128 x 64 with fp24)
+    number fewer than 256, up to one per 2-group sweep."""
+    rows = 256 if sf == 0 else 128
+    tiles = ((out + rows - 1) // rows) * ((B + 63) // 64)
+    return 1 if tiles >= 256 else min((inp // 128 + 1) // 2, -(-256 // tiles))
 
 
 def run_prefill(wal, W, info, bits, ldx=None, ldy=None):
@@ -68,19 +70,19 @@ def run_prefill(wal, W, info, bits, ldx=None, ldy=None):
 
 
 @pytest.mark.parametrize("out,inp,k,P,r,sf,B", [
-    (300, 1024, 8, 1, 16, 0, 64),       # two splits of one sweep each
-    (129, 4224, 4, 2, 7, 1, 96),        # ragged rows, fp24, nine splits, last sweep of one group
+    (300, 1024, 8, 1, 16, 0, 64),       # four splits of one sweep each
+    (129, 4224, 4, 2, 7, 1, 96),        # ragged rows, fp24, 17 splits, last sweep of one group
     (1000, 4096, 0, 4, 64, 0, 200),     # 256 low-rank terms, ragged batch chunk
-    (2050, 1024, 2, 2, 16, 1, 1000),    # 17 x 32 tiles: whole K, ragged rows and chunk
+    (8200, 1024, 2, 2, 16, 1, 1000),    # fp24: 65 x 16 tiles, whole K, ragged rows and chunk
     (4099, 12288, 8, 1, 16, 0, 70),     # down_proj width, ragged rows
-    (2048, 4224, 8, 0, 0, 0, 1024),     # whole K, no low-rank path
+    (8192, 1152, 8, 0, 0, 0, 1024),     # whole K, no low-rank path, odd sweep count, last sweep of one group
     (16, 128, 2, 1, 1, 0, 33),          # one row tile, one group, rank 1
 ])
 def test_shapes(wal, out, inp, k, P, r, sf, B):
     m = synth.make_matrix(320, out * 3 + inp + k, out, inp, k=k, n_paths=P, rank=r, scale_fmt=sf)
     blob, info = wal.pack_matrix(m)
     x, bits = synth.make_x(320, out + inp, inp, B)
-    print(f"prefill {out}x{inp} k={k} P={P} r={r} sf={sf} B={B} splits={split_count(out, inp, B)}", flush=True)
+    print(f"prefill {out}x{inp} k={k} P={P} r={r} sf={sf} B={B} splits={split_count(out, inp, B, sf)}", flush=True)
     Y = run_prefill(wal, to_dev(blob), info, bits, ldx=inp + 64, ldy=out + 3)
     ref = D.gemm(F.pack(F.from_synth(m)), x)
     errs = [D.rel_l2(Y[n], ref[n]) for n in range(B)]
@@ -115,7 +117,8 @@ def test_down_proj_full_size(wal, config3, B):
     print(f"  sampled worst rel_l2 = {worst:.3e}", flush=True)
 
 
-@pytest.mark.parametrize("sf,P,k,out,B", [(0, 1, 8, 200, 18), (1, 2, 2, 4096, 512), (0, 0, 4, 300, 40)])
+@pytest.mark.parametrize("sf,P,k,out,B", [(0, 1, 8, 200, 18), (1, 2, 2, 2048, 256), (0, 0, 4, 300, 40),
+                                          (1, 1, 8, 8192, 1024)])
 def test_columns_bit_exact(wal, sf, P, k, out, B):
     inp = 4224
     m = synth.make_matrix(321, sf * 8 + k, out, inp, k=k, n_paths=P, rank=16, scale_fmt=sf)
@@ -126,7 +129,7 @@ def test_columns_bit_exact(wal, sf, P, k, out, B):
     E = np.zeros((B, inp), np.float32)
     E[np.arange(B), cols] = 1.0
     bits = synth.round_bf16_bits(E)
-    print(f"prefill columns {out}x{inp} sf={sf} P={P} k={k} B={B} splits={split_count(out, inp, B)}", flush=True)
+    print(f"prefill columns {out}x{inp} sf={sf} P={P} k={k} B={B} splits={split_count(out, inp, B, sf)}", flush=True)
     Y = run_prefill(wal, to_dev(blob), info, bits)
     for n, j in enumerate(cols):
         assert np.array_equal(Y[n], W[:, j].astype(np.float32).astype(np.float64)), (n, j)
@@ -140,7 +143,7 @@ def test_zero_case_and_determinism(wal):
     x, bits = synth.make_x(322, 0, 4096, 100)
     print("prefill zero blob B=100", flush=True)
     assert not run_prefill(wal, to_dev(blob), info, bits).any()
-    m = synth.make_matrix(322, 1, 2048, 4096, k=8, n_paths=1, rank=16)
+    m = synth.make_matrix(322, 1, 8192, 4096, k=8, n_paths=1, rank=16)
     blob, info = wal.pack_matrix(m)
     W = to_dev(blob)
     for B in (100, 1024):   # split and whole

@@ -219,29 +219,33 @@ def test_workspace_size():
 def test_prefill_workspace_size():
     """Low-rank partials z [chunk][batch][terms] | per-split partial sums
     [splits][batch][out] when the K dimension is split: splits are made only
-    while the (128-row, 32-batch-row) tiles number fewer than 512, at most
-    one per 4-group sweep."""
+    while the tiles (256 rows with fp16 scales, 128 with fp24, by 64 batch
+    rows) number fewer than 256, at most one per 2-group sweep."""
     def up(v):
         return (v + 255) // 256 * 256
 
     def expect(out, inp, terms, B):
-        tiles = ((out + 127) // 128) * ((B + 31) // 32)
-        sweeps = (inp // 128 + 3) // 4
-        nsplit = 1 if tiles >= 512 else min(sweeps, -(-512 // tiles))
+        tiles = ((out + 255) // 256) * ((B + 63) // 64)
+        sweeps = (inp // 128 + 1) // 2
+        nsplit = 1 if tiles >= 256 else min(sweeps, -(-256 // tiles))
         z = up(4 * terms * B * ((inp + 4095) // 4096))
         return z + (up(4 * nsplit * B * out) if nsplit > 1 else 0), nsplit
 
     info = wal.wal_packed_size(wal.make_desc(4096, 12288, 8, 1, 16))
-    for B in (1, 64, 96, 200, 256, 512, 2048):
+    for B in (1, 64, 96, 200, 256, 512, 1024, 2048):
         n, nsplit = expect(4096, 12288, 16, B)
         assert wal.wal_prefill_workspace_size(info, B) == n, B
-    assert expect(4096, 12288, 16, 64)[1] == 8 and expect(4096, 12288, 16, 512)[1] == 1
-    info = wal.wal_packed_size(wal.make_desc(64, 1024, 0))
+    assert expect(4096, 12288, 16, 64)[1] == 16 and expect(4096, 12288, 16, 1024)[1] == 1
+    info = wal.wal_packed_size(wal.make_desc(64, 512, 0))
     assert wal.wal_prefill_workspace_size(info, 1) == up(4 * 2 * 1 * 64)   # two splits of one sweep each
     info = wal.wal_packed_size(wal.make_desc(64, 256, 0))
     assert wal.wal_prefill_workspace_size(info, 1) == 0                     # one sweep: nothing to split
     info = wal.wal_packed_size(wal.make_desc(16384, 512, 0))
     assert wal.wal_prefill_workspace_size(info, 1024) == 0                 # no paths, no split
+    fp24 = wal.wal_packed_size(wal.make_desc(4096, 12288, 8, 1, 16, scale_fmt=1))
+    n = wal.wal_prefill_workspace_size(fp24, 512)   # 32 x 8 tiles: whole K
+    assert n == up(4 * 16 * 512 * 3)
+    assert wal.wal_prefill_workspace_size(fp24, 256) == up(4 * 16 * 256 * 3) + up(4 * 2 * 256 * 4096)
     with pytest.raises(wal.WalError):
         wal.wal_prefill_workspace_size(info, 0)
     with pytest.raises(wal.WalError):
