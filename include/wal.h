@@ -227,8 +227,11 @@ int wal_gemm_small(const wal_info* info, const void* W_dev, const void* X_dev, i
                    void* ws_dev, size_t ws_bytes, void* stream);
 
 /* Device workspace that wal_gemm_prefill needs for a blob and batch
- * (1..WAL_MAX_PREFILL_BATCH): the low-rank partials [ceil(in / 4096)][batch]
- * [n_paths * rank] and, when the product is split along K (few output tiles),
+ * (1..WAL_MAX_PREFILL_BATCH): the low-rank partials [zc][batch][n_paths *
+ * rank], one per column split of the pre-pass (zc splits of whole 128-column
+ * groups, as many as bring the pre-pass to about 1024 wavefronts of 16 batch
+ * rows x 16 terms, at most 8) and, when the product is split along K (few
+ * output tiles),
  * the per-split partial sums [splits][batch][out] (fp32), each part padded to
  * 256 bytes.  0 for a blob without paths that is not split.
  * Errors: ARG, SHAPE, FORMAT. */

@@ -835,10 +835,52 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void k_prefill(MatDev d, Prefil
     }
 }
 
-// Low-rank partials for k_prefill: block b computes terms 16 tc .. 16 tc + 15
-// of batch row n over a 4096-column chunk (z_block).
-__global__ __launch_bounds__(256) void k_zpre(MatDev d, float* __restrict__ zpart) { z_block(d, zpart, blockIdx.x); }
-
+// Low-rank reductions for k_prefill on the matrix cores:
+//     zpart[ks][n][t] = s_t * sum over split ks's columns of (-1)^{V bit} X[n][c]
+// (WAL-Ternary-8B cards, "Representation": the binary paths' V^T x).  One
+// wavefront per (16 batch rows, 16 terms, column split): X is the A operand
+// as stored (lane (n, kb) takes 8 consecutive columns, 16 bytes), and the
+// lane (t, kb) of the B operand expands the matching 8 V bits of term t into
+// +-1 bf16 (one V dword serves the four MFMAs of a 128-column group).  Rows
+// past the batch read its last row and terms past the last term the last
+// term's plane; neither is stored.
+__global__ __launch_bounds__(64) void k_zmma(MatDev d, float* __restrict__ zpart, uint32_t groups_per_split) {
+  const uint32_t lane = threadIdx.x, i = lane & 15, kb = lane >> 4;
+  const uint32_t T = d.terms, ks = blockIdx.z;
+  const uint32_t n = min(blockIdx.x * 16 + i, d.batch - 1);
+  const uint32_t t = min(blockIdx.y * 16 + i, T - 1), p = t / d.rank, q = t % d.rank;
+  const uint32_t g0 = ks * groups_per_split, g1 = min(d.groups, g0 + groups_per_split);
+  const __amdgpu_buffer_rsrc_t rx = rsrc(d.x, 2 * ((d.batch - 1) * d.ldx + d.in));
+  const __amdgpu_buffer_rsrc_t rv = rsrc(d.V, d.blob_bytes - (uint32_t)(d.V - d.codes));
+  const uint32_t xoff = 2 * (n * d.ldx + 32 * kb), voff = p * d.pstride + q * (d.in / 8) + 4 * kb;
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (uint32_t g = g0; g < g1; ++g) {
+    uint4 xa[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      xa[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff + 256 * g + 16 * m, 0, 0));
+    const uint32_t vw = __builtin_amdgcn_raw_buffer_load_b32(rv, voff + 16 * g, 0, 0);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t b = vw >> (8 * m);
+      uint4 vb;
+      uint32_t* e = reinterpret_cast<uint32_t*>(&vb);
+#pragma unroll
+      for (int k = 0; k < 4; ++k)   // elements 2k, 2k + 1: +1 (0x3F80), the bit sets the sign
+        e[k] = 0x3F803F80u | ((b << (15 - 2 * k)) & 0x8000u) | ((b << (30 - 2 * k)) & 0x80000000u);
+      acc = mfma(xa[m], vb, acc);
+    }
+  }
+  // C layout: lane (t = i, kb) holds batch rows 4 kb + j of the tile
+  const uint32_t tt = blockIdx.y * 16 + i;
+  if (tt >= T) return;
+  const float sc = (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(path_plane(d.s, d, p))[q]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t nn = blockIdx.x * 16 + 4 * kb + j;
+    if (nn < d.batch) zpart[((size_t)ks * d.batch + nn) * T + tt] = sc * acc[j];
+  }
+}
 // ---------------------------------------------------------------------------
 // Host side.
 
@@ -940,8 +982,8 @@ int launch_gemm_prefill(const wal_info& f, const MatDev& d, uint32_t batch, void
   float* zp = reinterpret_cast<float*>(w);
   float* P = S.nsplit > 1 ? reinterpret_cast<float*>(w + S.off_p) : nullptr;
   if (d.terms) {
-    const uint32_t nz = S.zc * batch * ((d.terms + kZTermsPerBlock - 1) / kZTermsPerBlock);
-    hipLaunchKernelGGL(k_zpre, dim3(nz), dim3(256), 0, s, d, zp);
+    const dim3 zg((batch + 15) / 16, (d.terms + 15) / 16, S.zc);
+    hipLaunchKernelGGL(k_zmma, zg, dim3(64), 0, s, d, zp, S.zgroups);
     if (hipGetLastError() != hipSuccess) return WAL_ERR_DEVICE;
   }
   const dim3 grid(8 * S.per_xcd);

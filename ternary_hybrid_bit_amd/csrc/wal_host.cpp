@@ -468,7 +468,13 @@ PrefillShape prefill_shape(const wal_info& f, uint32_t batch) {
   const uint64_t ids = ngroups * S.rblocks * S.nsplit * S.cgw;
   S.per_xcd = (uint32_t)((ids + 7) / 8);
   S.tiles = (uint32_t)ids;
-  S.zc = (f.d.in + kZChunkCols - 1) / kZChunkCols;
+  {
+    const uint64_t tiles = std::max<uint64_t>(1, (uint64_t)((batch + 15) / 16) * ((f.d.n_paths * f.d.rank + 15) / 16));
+    uint64_t splits = std::max<uint64_t>(1, (kZmmaWaves + tiles - 1) / tiles);
+    splits = std::min<uint64_t>(std::min<uint64_t>(splits, kZmmaMaxSplits), f.groups);
+    S.zgroups = (uint32_t)((f.groups + splits - 1) / splits);
+    S.zc = (f.groups + S.zgroups - 1) / S.zgroups;
+  }
   const uint64_t terms = (uint64_t)f.d.n_paths * f.d.rank;
   S.off_p = up(4 * terms * batch * S.zc, 256);
   S.bytes = S.off_p + (S.nsplit > 1 ? up(4ull * S.nsplit * batch * f.d.out, 256) : 0);

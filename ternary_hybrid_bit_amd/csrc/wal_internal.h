@@ -119,16 +119,20 @@ int launch_gemm_mfma(const wal_info& f, const MatDev& d, uint32_t batch, void* w
 // and their mapping to workgroups.  K splits are made only while
 // rblocks * chunks * nsplit < kPrefillTiles; their partial sums
 // P[split][n][row] go to the workspace after the low-rank partials
-// [zc][batch][terms].
+// [zc][batch][terms] (zc column splits of zgroups groups, chosen so that the
+// pre-pass runs about kZmmaWaves wavefronts, at most kZmmaMaxSplits: every
+// consumer adds the zc partials).
 constexpr uint32_t kPrefillWaves = 8;
 constexpr uint32_t prefill_rows(uint32_t scale_fmt) { return kPrefillWaves * 16 * (scale_fmt == WAL_SCALE_FP16 ? 2 : 1); }
 constexpr uint32_t kPrefillCols = 64;
 constexpr uint32_t kPrefillTiles = 256;   // workgroups the GPU holds at once (1 per CU)
 constexpr uint32_t kPrefillSweepGroups = 2;   // 128-column groups per sweep (a K split holds whole sweeps)
+constexpr uint32_t kZmmaWaves = 1024;
+constexpr uint32_t kZmmaMaxSplits = 8;
 struct PrefillShape {
   uint32_t rblocks, chunks, nsplit, sweeps;   // sweeps of kPrefillSweepGroups groups over the whole K
   uint32_t cgw, per_xcd, tiles;               // chunks per id group, ids per XCD, padded ids
-  uint32_t zc;                                // low-rank partials per batch row
+  uint32_t zc, zgroups;                       // low-rank partials per batch row, groups per partial
   uint64_t off_p, bytes;                      // workspace layout
 };
 PrefillShape prefill_shape(const wal_info& f, uint32_t batch);

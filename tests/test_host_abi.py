@@ -201,6 +201,13 @@ def test_workspace_size():
     def up(v):
         return (v + 255) // 256 * 256
 
+    def zsplits(inp, terms, B):   # column splits of the low-rank pre-pass
+        G = inp // 128
+        tiles = -(-B // 16) * -(-terms // 16)
+        s = min(max(1, -(-1024 // tiles)), 8, G)
+        per = -(-G // s)
+        return -(-G // per)
+
     def expect(out, inp, terms, B):
         chunks, slices = (inp + 4095) // 4096, (inp + 1023) // 1024
         return up(4 * terms * B * chunks) + up(4 * slices * B * out)
@@ -217,18 +224,26 @@ def test_workspace_size():
 
 
 def test_prefill_workspace_size():
-    """Low-rank partials z [chunk][batch][terms] | per-split partial sums
+    """Low-rank partials z [zc][batch][terms] (zc column splits that bring the
+    pre-pass to about 1024 wavefronts, at most 8) | per-split partial sums
     [splits][batch][out] when the K dimension is split: splits are made only
     while the tiles (256 rows with fp16 scales, 128 with fp24, by 64 batch
     rows) number fewer than 256, at most one per 2-group sweep."""
     def up(v):
         return (v + 255) // 256 * 256
 
+    def zsplits(inp, terms, B):   # column splits of the low-rank pre-pass
+        G = inp // 128
+        tiles = -(-B // 16) * -(-terms // 16)
+        s = min(max(1, -(-1024 // tiles)), 8, G)
+        per = -(-G // s)
+        return -(-G // per)
+
     def expect(out, inp, terms, B):
         tiles = ((out + 255) // 256) * ((B + 63) // 64)
         sweeps = (inp // 128 + 1) // 2
         nsplit = 1 if tiles >= 256 else min(sweeps, -(-256 // tiles))
-        z = up(4 * terms * B * ((inp + 4095) // 4096))
+        z = up(4 * terms * B * zsplits(inp, terms, B)) if terms else 0
         return z + (up(4 * nsplit * B * out) if nsplit > 1 else 0), nsplit
 
     info = wal.wal_packed_size(wal.make_desc(4096, 12288, 8, 1, 16))
@@ -244,8 +259,8 @@ def test_prefill_workspace_size():
     assert wal.wal_prefill_workspace_size(info, 1024) == 0                 # no paths, no split
     fp24 = wal.wal_packed_size(wal.make_desc(4096, 12288, 8, 1, 16, scale_fmt=1))
     n = wal.wal_prefill_workspace_size(fp24, 512)   # 32 x 8 tiles: whole K
-    assert n == up(4 * 16 * 512 * 3)
-    assert wal.wal_prefill_workspace_size(fp24, 256) == up(4 * 16 * 256 * 3) + up(4 * 2 * 256 * 4096)
+    assert n == up(4 * 16 * 512 * zsplits(12288, 16, 512))
+    assert wal.wal_prefill_workspace_size(fp24, 256) == up(4 * 16 * 256 * zsplits(12288, 16, 256)) + up(4 * 2 * 256 * 4096)
     with pytest.raises(wal.WalError):
         wal.wal_prefill_workspace_size(info, 0)
     with pytest.raises(wal.WalError):
