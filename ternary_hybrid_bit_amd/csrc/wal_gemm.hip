@@ -1,13 +1,13 @@
-// Small-batch kernels of libwal for gfx950: Y = X W^T for a batch of up to 32
-// bf16 activation rows (multi-sequence decode, short prefill) on the 2-bit
-// planes.  With B activation columns every decoded trit feeds B products:
+// Batched kernels of libwal for gfx950: Y = X W^T for bf16 activation rows on
+// the 2-bit planes, from a few rows (multi-sequence decode) to prefill sizes.
+// With B activation rows every decoded trit feeds B products:
 //     Y[n][row] = sum_g ( alpha[row][g] * sum_{k in g} T[row][k] X[n][k]
 //                       +  beta[row][g] * sum_{k in g} R[row][k] X[n][k] )
 //               + sum_t (-1)^{U bit} z[n][t]
 // (WAL-Ternary-8B cards, "Representation": the ternary-hybrid product and its
 // binary low-rank paths; the per-(row, group) scales are applied in fp32).
 //
-// Batched GEMV (k_gemv_batch, vector ALUs), two launches:
+// Batched GEMV (k_gemv_batch, vector ALUs, B <= 32), two launches:
 //  1. a wavefront takes kGemvRows rows of one 4096-column pass for up to
 //     kGemvCols columns and writes its partial sums P[pass][n][row].  Each
 //     lane decodes its 64 trits of a row once (shift and mask to bf16 +-2 / 0,
@@ -17,23 +17,20 @@
 //     of every batch column per 4096-column chunk, zpart[chunk][n][t];
 //  2. k_reduce adds the passes and the chunks in a fixed order, adds the
 //     low-rank term and stores Y.
-// MFMA (k_mfma, matrix cores), then k_reduce: one workgroup per 16-row tile
-// and 4096-column slice; its wavefronts take four 128-column groups each, and
-// each group is a few v_mfma_f32_16x16x32_bf16 over 16 rows x 16 batch
-// columns x 32 columns.  A
-// lane (row i = lane & 15, K block kb = lane >> 4) decodes its 8 code bytes
-// straight into A operands; the group's sites are scattered as +-2 into a
-// per-wavefront LDS tile in operand order, read back as a second A operand
-// and cleared; the lane builds its B operands from 64 bytes of X row 16t + i
-// with byte permutes.  The two group sums land in separate accumulators that
-// alpha and beta scale in fp32.  V enters as a third, +-1 A operand on the
-// same B operands, which gives the low-rank reductions z of the tile's
-// columns; the wavefronts' sums meet in LDS, and the workgroup writes its
-// slice's partial sums, which k_reduce adds.  Every weight load of a wavefront
-// is issued before it touches X, so the HBM latency is paid once.  Decoded
-// values are exact in bf16 and every product and sum is fp32, so x = e_j
-// still gives column j of W exactly, and every sum runs in a fixed order:
-// results do not depend on timing.
+// Matrix cores (k_mfma for B <= 32, k_prefill beyond): the trits of a 16-row
+// tile become bf16 A operands of v_mfma_f32_16x16x32_bf16 (lane (row i =
+// lane & 15, K block kb = lane >> 4) decodes its 8 code bytes with one 64-bit
+// shift and a mask per operand pair); the group's sites are scattered as +-2
+// into a per-wavefront LDS tile in operand order, read back as a second A
+// operand and cleared; X is staged once per workgroup in LDS in operand order
+// and read as the B operand.  The T and R group sums land in separate
+// accumulators that alpha and beta scale in fp32.  k_mfma writes partial sums
+// per 1024-column slice for k_reduce; k_prefill sweeps all columns (split
+// along K only when its tiles would not fill the GPU) and writes Y with the
+// low-rank term of k_zmma's partials.  Decoded values are exact in bf16 and
+// every product and sum is fp32, so x = e_j still gives column j of W
+// exactly, and every sum runs in a fixed order: results do not depend on
+// timing.
 #include <hip/hip_runtime.h>
 
 #include "wal_device.h"
