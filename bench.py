@@ -22,7 +22,9 @@ through wal_gemm_small with both kernels at batch 1, 2, 3, 4, 5, 8, 16 and 32
 (and the batch from which the matrix-core kernel is faster), config 4 the two
 base-3 / fp24 27B shapes through wal_gemv; ``--workload prefill`` runs the
 down shape through wal_gemm_prefill at batch 64 to 2048 beside torch's dense
-bf16 matmul of that shape.  Each call reads one of about
+bf16 matmul of that shape; ``--workload decode-step`` runs the 36-layer step
+with its dependencies (q|k|v, o, gate|up, down per layer, one grouped product
+each, in order), eagerly and as a HIP graph replay.  Each call reads one of about
 1 GB of distinct packed copies in turn, so the 256 MB Infinity Cache cannot
 serve the weights; x stays fixed.  For context the line also carries the
 rate of torch's own reduction (torch.sum over 2 GiB) on the same GPU; it is
@@ -302,39 +304,10 @@ def run_prefill(args, torch, wal, synth, dev, read_gbs, to_x):
     del keep
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--settle-s", type=float, default=1.0,
-                    help="seconds of untimed steps before the warmup (clock ramp after idle)")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-mib", type=int, default=0,
-                    help="after timing, run one fp32 elementwise copy of this many MiB (counter calibration)")
-    ap.add_argument("--workload", default="sweep", choices=("sweep", "config1", "config3", "config4", "prefill"))
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the sweep is timed on a single MI355X).", file=sys.stderr)
-        sys.exit(2)
-    if args.workload != "sweep":
-        run_single(args)
-        return
-
-    import torch
-    import ternary_hybrid_bit_amd as wal
-    from ternary_hybrid_bit_amd import workloads
-
-    t0 = time.time()
-    items = workloads.sweep()
-    print(f"[bench] generated and packed {len(items)} matrices in {time.time() - t0:.1f} s", file=sys.stderr,
-          flush=True)
-    dev = torch.device("cuda:0")
-    # One device arena for all packed blobs (each 256-byte aligned), one for
-    # the activations and one for the outputs, as a runtime keeps resident
-    # weights; every matrix is a view into them.
+def resident(torch, items, dev):
+    """Device copies of the packed blobs (one arena, each 256-byte aligned),
+    the bf16 activations and the fp32 outputs, as a runtime keeps resident
+    weights: (infos, Ws, xs, ys, keep) with every matrix a view into them."""
     infos = [i for _, i, _ in items]
     offs, cur = [], 0
     for b, _, _ in items:
@@ -361,6 +334,94 @@ def main():
         ycur += (i.d.out + 63) // 64 * 64
     y_all = torch.empty(ycur, dtype=torch.float32, device=dev)
     ys = [y_all[o:o + i.d.out] for (_, i, _), o in zip(items, yoffs)]
+    return infos, Ws, xs, ys, (arena, x_all, y_all)
+
+
+def run_decode_step(args):
+    """The 36-layer decode step with its dependencies: per layer q|k|v (one
+    grouped product, shared x), o, gate|up (shared x), down, each product
+    launched after the one before (144 grouped products, 288 kernels), over
+    the same 252 matrices as the sweep; once as one wal_gemv_grouped_seq call
+    per step and once as a replay of the chain captured in a HIP graph.  For
+    context the same process times the sweep as one grouped product of
+    independent matrices.  The products read synthetic bf16 activations (the
+    layers' nonlinear steps are not part of this path), so a product waits
+    for the one before it only through stream order, as it would for data."""
+    import torch
+    import ternary_hybrid_bit_amd as wal
+    from ternary_hybrid_bit_amd import workloads
+    dev = torch.device("cuda:0")
+    items = workloads.sweep()
+    infos, Ws, xs, ys, keep = resident(torch, items, dev)
+    groups = []
+    for layer in range(36):
+        b = 7 * layer
+        for ids in ((b, b + 1, b + 2), (b + 3,), (b + 4, b + 5), (b + 6,)):
+            groups.append(ids)
+    wsb = max(wal.wal_grouped_plan_size([infos[i] for i in ids])[1] for ids in groups)
+    ws = torch.zeros(max(wsb, 4) // 4, dtype=torch.float32, device=dev)
+    chain = []
+    for ids in groups:   # matrices of a group read the first one's x
+        plan, g = wal.wal_grouped_plan([infos[i] for i in ids], [Ws[i] for i in ids], [xs[ids[0]]] * len(ids),
+                                       [ys[i] for i in ids], ws, wal.WAL_X_BF16)
+        chain.append((g, torch.from_numpy(plan).to(dev)))
+    _, wsb_all = wal.wal_grouped_plan_size(infos)
+    ws_all = torch.zeros(max(wsb_all, 4) // 4, dtype=torch.float32, device=dev)
+    plan_all, g_all = wal.wal_grouped_plan(infos, Ws, xs, ys, ws_all, wal.WAL_X_BF16)
+    plan_all = torch.from_numpy(plan_all).to(dev)
+    graph = wal.WalGraph(chain)
+    torch.cuda.synchronize()
+    steps = max(args.steps, 50)
+    eager_ms = time_calls(torch, lambda i: wal.wal_gemv_grouped_seq(chain), steps, args.settle_s) / 1e3
+    graph_ms = time_calls(torch, lambda i: graph.launch(), steps, 0.3) / 1e3
+    sweep_ms = time_calls(torch, lambda i: wal.wal_gemv_grouped(g_all, plan_all), steps, 0.3) / 1e3
+    nbytes = sum(i.algorithmic_bytes for i in infos)
+    res = {"workload": "decode-step", "entry": "wal_gemv_grouped_seq / wal_graph_launch",
+           "layers": 36, "grouped_products": len(chain),
+           "kernels_per_step": sum(1 + g.n_classes if g.n_zjobs else g.n_classes for g, _ in chain),
+           "packed_bytes": int(nbytes), "x_dtype": "bf16", "data": "synthetic", "steps": steps,
+           "eager_ms_per_step": round(eager_ms, 4), "graph_ms_per_step": round(graph_ms, 4),
+           "graph_tokens_per_s": round(1e3 / graph_ms, 1), "graph_GB/s": round(nbytes / (graph_ms * 1e-3) / 1e9, 1),
+           "independent_sweep_ms": round(sweep_ms, 4), "host": host_info()}
+    graph.close()
+    print(json.dumps(res), flush=True)
+    del keep
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--settle-s", type=float, default=1.0,
+                    help="seconds of untimed steps before the warmup (clock ramp after idle)")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after timing, run one fp32 elementwise copy of this many MiB (counter calibration)")
+    ap.add_argument("--workload", default="sweep", choices=("sweep", "config1", "config3", "config4", "prefill", "decode-step"))
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the sweep is timed on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+    if args.workload == "decode-step":
+        run_decode_step(args)
+        return
+    if args.workload != "sweep":
+        run_single(args)
+        return
+
+    import torch
+    import ternary_hybrid_bit_amd as wal
+    from ternary_hybrid_bit_amd import workloads
+
+    t0 = time.time()
+    items = workloads.sweep()
+    print(f"[bench] generated and packed {len(items)} matrices in {time.time() - t0:.1f} s", file=sys.stderr,
+          flush=True)
+    dev = torch.device("cuda:0")
+    infos, Ws, xs, ys, keep = resident(torch, items, dev)
     _, wsb = wal.wal_grouped_plan_size(infos)
     ws = torch.zeros(max(wsb, 4) // 4, dtype=torch.float32, device=dev)
     plan, g = wal.wal_grouped_plan(infos, Ws, xs, ys, ws, wal.WAL_X_BF16)

@@ -293,6 +293,37 @@ enum { WAL_PHASE_LOWRANK = 1, WAL_PHASE_STREAM = 2, WAL_PHASE_ALL = 3 };
 int wal_gemv_grouped_phases(const wal_grouped_info* ginfo, const void* plan_dev, int phases,
                             void* stream);
 
+/* A decode step as a chain of grouped products that depend on each other
+ * (SURVEY-ranked next step after the grouped sweep; the 8B card's runtime
+ * captures its decode step in a CUDA graph, "Runtime"/"Performance"): product
+ * i + 1 starts only after product i has finished, as when matrices that
+ * share an input (q|k|v, gate|up) form one grouped product and the next
+ * product reads the previous one's output.
+ *
+ * wal_gemv_grouped_seq launches the n grouped products in order on `stream`
+ * (plans_dev[i] as for wal_gemv_grouped with ginfos[i]).
+ * Errors: those of wal_gemv_grouped, for the first product that fails (the
+ * products before it are already enqueued). */
+int wal_gemv_grouped_seq(uint32_t n, const wal_grouped_info* ginfos, const void* const* plans_dev,
+                         void* stream);
+
+/* The same chain captured once into a HIP graph and replayed with one call.
+ * wal_graph_create captures the n grouped products (on a private stream of
+ * default priority, which it destroys) and instantiates the graph; the
+ * handle owns the graph.  Every buffer the plans name (plans, weights, x, y,
+ * workspaces) must stay allocated while the handle exists; their contents may
+ * change between launches (a replay reads x as it is then).
+ * wal_graph_launch enqueues one replay on `stream`, after the work already
+ * there.  wal_graph_destroy frees the graph (NULL is accepted).  The graph
+ * holds only kernel launches: no memset or copy nodes.
+ * Errors: ARG (n == 0, NULL arguments), those of wal_gemv_grouped found while
+ * capturing (nothing is created then), DEVICE. */
+typedef struct wal_graph wal_graph;
+int wal_graph_create(uint32_t n, const wal_grouped_info* ginfos, const void* const* plans_dev,
+                     wal_graph** graph);
+int wal_graph_launch(const wal_graph* graph, void* stream);
+int wal_graph_destroy(wal_graph* graph);
+
 #ifdef __cplusplus
 }
 #endif

@@ -92,6 +92,10 @@ _sig = {
                               ctypes.POINTER(wal_grouped_info)]),
     "wal_gemv_grouped": (_I, [ctypes.POINTER(wal_grouped_info), _P, _P]),
     "wal_gemv_grouped_phases": (_I, [ctypes.POINTER(wal_grouped_info), _P, _I, _P]),
+    "wal_gemv_grouped_seq": (_I, [_U32, _P, _P, _P]),
+    "wal_graph_create": (_I, [_U32, _P, _P, ctypes.POINTER(_P)]),
+    "wal_graph_launch": (_I, [_P, _P]),
+    "wal_graph_destroy": (_I, [_P]),
 }
 for _name, (_res, _args) in _sig.items():
     _fn = getattr(_lib, _name)
@@ -274,3 +278,43 @@ def wal_gemv_grouped_phases(ginfo: wal_grouped_info, plan_dev, phases: int, stre
 
 def exported_symbols() -> list:
     return list(_sig)
+
+
+def _chain_args(chain):
+    """chain: [(wal_grouped_info, plan device tensor)] -> ctypes arrays."""
+    n = len(chain)
+    infos = (wal_grouped_info * n)(*[g for g, _ in chain])
+    plans = (ctypes.c_void_p * n)(*[_ptr(p) for _, p in chain])
+    return n, infos, plans
+
+
+def wal_gemv_grouped_seq(chain, stream=None):
+    """Launch the grouped products of ``chain`` in order on the stream."""
+    n, infos, plans = _chain_args(chain)
+    _check(_lib.wal_gemv_grouped_seq(n, infos, plans, _stream(stream)), "wal_gemv_grouped_seq")
+
+
+class WalGraph:
+    """A chain of grouped products captured in a HIP graph (wal_graph_create);
+    launch() replays it on a stream; the buffers the plans name must outlive it."""
+
+    def __init__(self, chain):
+        n, infos, plans = _chain_args(chain)
+        h = ctypes.c_void_p()
+        _check(_lib.wal_graph_create(n, infos, plans, ctypes.byref(h)), "wal_graph_create")
+        self._h = h
+
+    def launch(self, stream=None):
+        _check(_lib.wal_graph_launch(self._h, _stream(stream)), "wal_graph_launch")
+
+    def close(self):
+        if self._h:
+            _check(_lib.wal_graph_destroy(self._h), "wal_graph_destroy")
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001
+            pass
+

@@ -42,6 +42,7 @@
 
 #include <atomic>
 #include <cstring>
+#include <new>
 
 #include "wal_device.h"
 #include "wal_internal.h"
@@ -962,6 +963,69 @@ int wal_gemv_grouped_phases(const wal_grouped_info* g, const void* plan_dev, int
 
 int wal_gemv_grouped(const wal_grouped_info* g, const void* plan_dev, void* stream) {
   return wal_gemv_grouped_phases(g, plan_dev, WAL_PHASE_ALL, stream);
+}
+
+int wal_gemv_grouped_seq(uint32_t n, const wal_grouped_info* ginfos, const void* const* plans_dev, void* stream) {
+  if (!n || !ginfos || !plans_dev) return WAL_ERR_ARG;
+  for (uint32_t i = 0; i < n; ++i) {
+    const int st = wal_gemv_grouped(&ginfos[i], plans_dev[i], stream);
+    if (st) return st;
+  }
+  return WAL_OK;
+}
+
+}  // extern "C"
+
+// The captured chain: the executable graph and the graph it came from.
+struct wal_graph {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
+extern "C" {
+
+int wal_graph_create(uint32_t n, const wal_grouped_info* ginfos, const void* const* plans_dev, wal_graph** out) {
+  if (!n || !ginfos || !plans_dev || !out) return WAL_ERR_ARG;
+  *out = nullptr;
+  hipStream_t s = nullptr;
+  if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return WAL_ERR_DEVICE;
+  if (hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+    (void)hipStreamDestroy(s);
+    return WAL_ERR_DEVICE;
+  }
+  const int st = wal_gemv_grouped_seq(n, ginfos, plans_dev, s);
+  hipGraph_t graph = nullptr;
+  const hipError_t ce = hipStreamEndCapture(s, &graph);
+  (void)hipStreamDestroy(s);
+  if (st || ce != hipSuccess || !graph) {
+    if (graph) (void)hipGraphDestroy(graph);
+    return st ? st : WAL_ERR_DEVICE;
+  }
+  hipGraphExec_t exec = nullptr;
+  if (hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) != hipSuccess) {
+    (void)hipGraphDestroy(graph);
+    return WAL_ERR_DEVICE;
+  }
+  wal_graph* g = new (std::nothrow) wal_graph{graph, exec};
+  if (!g) {
+    (void)hipGraphExecDestroy(exec);
+    (void)hipGraphDestroy(graph);
+    return WAL_ERR_DEVICE;
+  }
+  *out = g;
+  return WAL_OK;
+}
+
+int wal_graph_launch(const wal_graph* g, void* stream) {
+  if (!g) return WAL_ERR_ARG;
+  return hipGraphLaunch(g->exec, static_cast<hipStream_t>(stream)) == hipSuccess ? WAL_OK : WAL_ERR_DEVICE;
+}
+
+int wal_graph_destroy(wal_graph* g) {
+  if (!g) return WAL_OK;
+  const bool ok = hipGraphExecDestroy(g->exec) == hipSuccess && hipGraphDestroy(g->graph) == hipSuccess;
+  delete g;
+  return ok ? WAL_OK : WAL_ERR_DEVICE;
 }
 
 }  // extern "C"

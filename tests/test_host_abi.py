@@ -312,6 +312,12 @@ def test_product_calls_check_arguments_before_any_launch():
     assert gp(W, x, 1, 64, 256, x + 256, 64, ws, need, None) == -1           # Y overlaps X
     assert gp(W, x, 1, 16384, 1 << 17, y, 64, ws, need, None) == -2          # X beyond 2 GiB
     assert lib.wal_gemv_grouped(None, 0x1000, None) == -1
+    assert lib.wal_gemv_grouped_seq(0, None, None, None) == -1
+    assert lib.wal_graph_create(0, None, None, None) == -1
+    h = ctypes.c_void_p()
+    assert lib.wal_graph_create(0, None, None, ctypes.byref(h)) == -1
+    assert lib.wal_graph_launch(None, None) == -1
+    assert lib.wal_graph_destroy(None) == 0
 
 
 def _plan_on_host(infos, grid, x_dtype=wal.WAL_X_BF16):
