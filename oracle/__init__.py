@@ -21,9 +21,11 @@ the logical arrays, build the dense float64 matrix W, and multiply.
 Modules:
   ``oracle.format`` - independent numpy packer, unpacker, validator, sizes.
   ``oracle.dense``  - dense float64 W and products y = W x, Y = X W^T.
+  ``oracle.rotation`` - the normalised Hadamard-128 rotation of x (the
+                        WAL2-Ternary-27B card's rotation, "Архитектура").
 
 Every function is pinned by tests under ``tests/`` against facts other than
 itself (golden bytes worked from the format readings, byte totals printed on
 the pages, exact-rational brute force, library special cases, invariants).
 """
-from . import format, dense  # noqa: F401
+from . import format, dense, rotation  # noqa: F401

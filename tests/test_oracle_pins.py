@@ -438,3 +438,64 @@ def test_unpack_rows_equals_full_unpack():
         assert np.array_equal(sub.V, full.V) and np.array_equal(sub.s, full.s)
         x = np.random.default_rng(8).standard_normal(384)
         np.testing.assert_allclose(D.gemv_rows(blob, x, rows), D.gemv(blob, x)[rows], rtol=1e-13, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# The normalised Hadamard-128 rotation (oracle/rotation.py)
+
+def test_sylvester_entries_match_popcount_closed_form():
+    """Sylvester's H has entry (-1)^popcount(i & j): a closed form of its own,
+    independent of the doubling."""
+    from oracle import rotation as Rt
+    H = Rt.sylvester()
+    i = np.arange(128)[:, None]
+    j = np.arange(128)[None, :]
+    pop = np.vectorize(lambda v: bin(int(v)).count("1"))(i & j)
+    assert np.array_equal(H, np.where(pop % 2 == 0, 1, -1))
+
+
+def test_sylvester_is_orthogonal_and_symmetric():
+    from oracle import rotation as Rt
+    H = Rt.sylvester()
+    assert np.array_equal(H @ H.T, 128 * np.eye(128, dtype=np.int64))
+    assert np.array_equal(H, H.T)
+    assert H[0].sum() == 128 and all(H[r].sum() == 0 for r in range(1, 128))
+
+
+def test_rotation_special_vectors():
+    """A constant group maps to sqrt(128) c at its first entry; a basis vector
+    e_k of group g maps to column k of H / sqrt(128) inside group g only."""
+    from oracle import rotation as Rt
+    x = np.zeros(3 * 128)
+    x[128:256] = 2.5
+    y = Rt.rotate(x)
+    expect = np.zeros(3 * 128)
+    expect[128] = 2.5 * np.sqrt(128)
+    assert np.allclose(y, expect, rtol=0, atol=1e-12)
+    H = Rt.sylvester()
+    for g, k in [(0, 0), (0, 77), (2, 127)]:
+        e = np.zeros(3 * 128)
+        e[g * 128 + k] = 1.0
+        y = Rt.rotate(e)
+        assert np.allclose(y[g * 128:(g + 1) * 128], H[:, k] / np.sqrt(128), rtol=0, atol=1e-15)
+        assert not np.delete(y, np.arange(g * 128, (g + 1) * 128)).any()
+
+
+def test_rotation_is_an_orthogonal_involution():
+    """R is symmetric and orthogonal: it keeps norms, R R = I, and the rotated
+    weights give the original product (W R)(R x) = W x."""
+    from oracle import rotation as Rt
+    rng = np.random.default_rng(5)
+    X = rng.standard_normal((4, 512))
+    Y = Rt.rotate(X)
+    assert np.allclose(np.linalg.norm(Y, axis=1), np.linalg.norm(X, axis=1), rtol=1e-13)
+    assert np.allclose(Rt.rotate(Y), X, rtol=0, atol=1e-12)
+    W = rng.standard_normal((3, 512))
+    Wr = Rt.rotate(W)          # rows of W R (R symmetric)
+    assert np.allclose(Wr @ Y.T, W @ X.T, rtol=1e-12, atol=1e-12)
+
+
+def test_rotation_rejects_partial_blocks():
+    from oracle import rotation as Rt
+    with pytest.raises(ValueError):
+        Rt.rotate(np.zeros(200))
