@@ -211,13 +211,23 @@ def run_single(args):
             ws = torch.empty(max(wal.wal_workspace_size(info, 1), 4) // 4, dtype=torch.float32, device=dev)
             us = time_calls(torch, lambda i: wal.wal_gemv(info, Ws[i % len(Ws)], xt, y, ws), calls)
             gbs = info.algorithmic_bytes / (us * 1e-6) / 1e9
+            extra = {}
+            if cfg == 4:   # the 27B card's blobs are H128-rotated: x is rotated first
+                xr = torch.empty_like(xt)
+                rot_us = time_calls(torch, lambda i: wal.wal_rotate_h128(xt, xr), calls)
+
+                def rotated(i):
+                    wal.wal_rotate_h128(xt, xr)
+                    wal.wal_gemv(info, Ws[i % len(Ws)], xr, y, ws)
+                both_us = time_calls(torch, rotated, calls)
+                extra = {"rotate_h128_us": round(rot_us, 3), "rotated_product_us": round(both_us, 3)}
             t_all, t_mm = oracle_time(blob, x[:1])
             res.append({"shape": [int(info.d.out), int(info.d.in_)], "k": int(info.d.k),
                         "format": "base-3 / fp24" if info.d.trit_fmt else "2-bit / fp16",
                         "packed_bytes": int(info.algorithmic_bytes), "copies": len(Ws), "us_per_call": round(us, 3),
                         "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                         "weights_per_s": round(info.d.out * info.d.in_ / (us * 1e-6), 1),
-                        "oracle_s": round(t_all, 3), "oracle_matmul_s": round(t_mm, 4)})
+                        "oracle_s": round(t_all, 3), "oracle_matmul_s": round(t_mm, 4), **extra})
             del Ws, keep
         out = {"workload": args.workload, "entry": "wal_gemv", "x_dtype": "bf16", "data": "synthetic",
                "calls": calls, "torch_sum_2gib_gbs": read_gbs, "results": res, "host": host_info()}

@@ -293,6 +293,21 @@ enum { WAL_PHASE_LOWRANK = 1, WAL_PHASE_STREAM = 2, WAL_PHASE_ALL = 3 };
 int wal_gemv_grouped_phases(const wal_grouped_info* ginfo, const void* plan_dev, int phases,
                             void* stream);
 
+/* The normalised Hadamard-128 rotation of activations (WAL2-Ternary-27B card,
+ * "Архитектура": the packed weights are rotated by a normalised H128 with
+ * sign_mode identity, so a product of such a blob takes the rotated x):
+ *     out[r][128 g + i] = sum_j H[i][j] x[r][128 g + j] / sqrt(128)
+ * with H Sylvester's Hadamard matrix, H[i][j] = (-1)^popcount(i & j).
+ *   x_dev    [rows][ldx] bf16 or fp32 (x_dtype), 16-byte aligned rows
+ *   in       columns, a multiple of 128 (else WAL_ERR_SHAPE)
+ *   out_dev  [rows][ldo] bf16 or fp32 (out_dtype), 16-byte aligned rows;
+ *            columns past `in` untouched.  out may be x itself (same type
+ *            and pitch: in place); any other overlap is rejected
+ * Arithmetic in fp32; bf16 output rounds to nearest even.
+ * Errors: ARG, SHAPE, ALIGN, DEVICE. */
+int wal_rotate_h128(const void* x_dev, int x_dtype, uint32_t rows, uint32_t in, uint32_t ldx,
+                    void* out_dev, int out_dtype, uint32_t ldo, void* stream);
+
 /* A decode step as a chain of grouped products that depend on each other
  * (SURVEY-ranked next step after the grouped sweep; the 8B card's runtime
  * captures its decode step in a CUDA graph, "Runtime"/"Performance"): product

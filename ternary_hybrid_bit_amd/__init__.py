@@ -92,6 +92,7 @@ _sig = {
                               ctypes.POINTER(wal_grouped_info)]),
     "wal_gemv_grouped": (_I, [ctypes.POINTER(wal_grouped_info), _P, _P]),
     "wal_gemv_grouped_phases": (_I, [ctypes.POINTER(wal_grouped_info), _P, _I, _P]),
+    "wal_rotate_h128": (_I, [_P, _I, _U32, _U32, _U32, _P, _I, _U32, _P]),
     "wal_gemv_grouped_seq": (_I, [_U32, _P, _P, _P]),
     "wal_graph_create": (_I, [_U32, _P, _P, ctypes.POINTER(_P)]),
     "wal_graph_launch": (_I, [_P, _P]),
@@ -317,4 +318,19 @@ class WalGraph:
             self.close()
         except Exception:  # noqa: BLE001
             pass
+
+
+def wal_rotate_h128(X, out, stream=None):
+    """out = X rotated by the normalised Hadamard-128 along its last axis (1-D
+    or 2-D device tensors, bf16 or fp32; out may be X itself)."""
+    import torch
+
+    def dt(t):
+        return WAL_X_BF16 if t.dtype == torch.bfloat16 else WAL_X_F32
+    X2 = X if X.dim() == 2 else X.view(1, -1)
+    O2 = out if out.dim() == 2 else out.view(1, -1)
+    st = _lib.wal_rotate_h128(_ptr(X2), dt(X), X2.shape[0], X2.shape[1], X2.stride(0), _ptr(O2), dt(out),
+                              O2.stride(0), _stream(stream))
+    _check(st, "wal_rotate_h128")
+    return out
 

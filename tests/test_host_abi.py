@@ -313,6 +313,16 @@ def test_product_calls_check_arguments_before_any_launch():
     assert gp(W, x, 1, 16384, 1 << 17, y, 64, ws, need, None) == -2          # X beyond 2 GiB
     assert lib.wal_gemv_grouped(None, 0x1000, None) == -1
     assert lib.wal_gemv_grouped_seq(0, None, None, None) == -1
+    rot = lib.wal_rotate_h128
+    assert rot(None, 1, 1, 128, 128, y, 1, 128, None) == -1                     # x missing
+    assert rot(x, 1, 0, 128, 128, y, 1, 128, None) == -1                        # no rows
+    assert rot(x, 2, 1, 128, 128, y, 1, 128, None) == -1                        # dtype
+    assert rot(x, 1, 1, 200, 256, y, 1, 256, None) == -2                        # not a multiple of 128
+    assert rot(x, 1, 1, 256, 128, y, 1, 256, None) == -1                        # ldx < in
+    assert rot(x + 2, 1, 1, 128, 128, y, 1, 128, None) == -6                    # x misaligned
+    assert rot(x, 1, 2, 128, 132, y, 1, 128, None) == -6                        # row pitch
+    assert rot(x, 1, 2, 128, 128, x + 256, 1, 128, None) == -1                  # partial overlap
+    assert rot(x, 1, 2, 128, 128, x, 0, 128, None) == -1                        # same buffer, other type
     assert lib.wal_graph_create(0, None, None, None) == -1
     h = ctypes.c_void_p()
     assert lib.wal_graph_create(0, None, None, ctypes.byref(h)) == -1
