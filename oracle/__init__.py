@@ -23,9 +23,10 @@ Modules:
   ``oracle.dense``  - dense float64 W and products y = W x, Y = X W^T.
   ``oracle.rotation`` - the normalised Hadamard-128 rotation of x (the
                         WAL2-Ternary-27B card's rotation, "Архитектура").
+  ``oracle.int4``   - INT4/g128 packed matrices (the 8B cards' LM head).
 
 Every function is pinned by tests under ``tests/`` against facts other than
 itself (golden bytes worked from the format readings, byte totals printed on
 the pages, exact-rational brute force, library special cases, invariants).
 """
-from . import format, dense, rotation  # noqa: F401
+from . import format, dense, rotation, int4  # noqa: F401

@@ -499,3 +499,71 @@ def test_rotation_rejects_partial_blocks():
     from oracle import rotation as Rt
     with pytest.raises(ValueError):
         Rt.rotate(np.zeros(200))
+
+
+# ---------------------------------------------------------------------------
+# INT4/g128 packed matrices (oracle/int4.py)
+
+def test_int4_golden_bytes():
+    """Worked by hand from the layout reading: nibble codes in two's
+    complement, element 2i low; binary16 scales little-endian after them."""
+    from oracle import int4 as I
+    q = np.zeros((1, 128), dtype=np.int64)
+    q[0, :8] = [-8, -7, -1, 0, 1, 2, 3, 7]
+    b = I.pack(q, np.array([[0.5]]))
+    assert b.size == 66
+    assert list(b[:4]) == [0x98, 0x0F, 0x21, 0x73] and not b[4:64].any()
+    assert list(b[64:]) == [0x00, 0x38]                       # 0.5 = 0x3800
+
+
+def test_int4_size_matches_head_estimate():
+    """The Qwen3-8B head (151936 x 4096) packs to ~0.32 GB, the figure the
+    8B cards' INT4/g128 head implies."""
+    from oracle import int4 as I
+    n = I.size(151936, 4096)
+    assert n == 151936 * 2048 + 151936 * 32 * 2 == 320_888_832
+
+
+def test_int4_bruteforce_exact():
+    """Tiny matrices against the definition in exact rationals."""
+    from oracle import int4 as I
+    rng = np.random.default_rng(7)
+    V, inp = 3, 256
+    q = rng.integers(-8, 8, size=(V, inp))
+    s = rng.choice([0.25, 0.5, 1.5, -0.75, 2.0 ** -10, 3.0], size=(V, inp // 128))
+    x = rng.integers(-5, 6, size=inp)
+    y = I.gemv(I.pack(q, s), V, inp, x)
+    for v in range(V):
+        exact = sum(Fraction(float(s[v, j // 128])) * int(q[v, j]) * int(x[j]) for j in range(inp))
+        assert Fraction(float(y[v])) == exact
+
+
+def test_int4_columns_and_roundtrip():
+    from oracle import int4 as I
+    rng = np.random.default_rng(8)
+    V, inp = 5, 384
+    q = rng.integers(-8, 8, size=(V, inp))
+    s = rng.integers(-64, 64, size=(V, 3)) / 16.0
+    b = I.pack(q, s)
+    q2, s2 = I.unpack(b, V, inp)
+    assert np.array_equal(q2, q) and np.array_equal(s2, s)
+    for j in (0, 1, 127, 128, 383):
+        e = np.zeros(inp)
+        e[j] = 1.0
+        assert np.array_equal(I.gemv(b, V, inp, e), s[:, j // 128] * q[:, j])
+    rows = [4, 0, 2]
+    x = rng.standard_normal(inp)
+    assert np.allclose(I.gemv_rows(b, V, inp, x, rows), I.gemv(b, V, inp, x)[rows], rtol=0, atol=1e-12)
+
+
+def test_int4_rejections():
+    from oracle import int4 as I
+    ok_s = np.ones((1, 1))
+    with pytest.raises(ValueError):
+        I.pack(np.full((1, 128), 8), ok_s)
+    with pytest.raises(ValueError):
+        I.pack(np.full((1, 128), -9), ok_s)
+    with pytest.raises(ValueError):
+        I.pack(np.zeros((1, 128), dtype=np.int64), np.array([[0.1]]))   # not binary16-exact
+    with pytest.raises(ValueError):
+        I.pack(np.zeros((1, 200), dtype=np.int64), np.ones((1, 1)))
