@@ -24,7 +24,8 @@ base-3 / fp24 27B shapes through wal_gemv; ``--workload prefill`` runs the
 down shape through wal_gemm_prefill at batch 64 to 2048 beside torch's dense
 bf16 matmul of that shape; ``--workload decode-step`` runs the 36-layer step
 with its dependencies (q|k|v, o, gate|up, down per layer, one grouped product
-each, in order), eagerly and as a HIP graph replay.  Each call reads one of about
+each, in order), eagerly and as a HIP graph replay; ``--workload lmhead`` the
+151936 x 4096 INT4/g128 LM head through wal_int4_gemv.  Each call reads one of about
 1 GB of distinct packed copies in turn, so the 256 MB Infinity Cache cannot
 serve the weights; x stays fixed.  For context the line also carries the
 rate of torch's own reduction (torch.sum over 2 GiB) on the same GPU; it is
@@ -398,6 +399,33 @@ def run_decode_step(args):
     del keep
 
 
+def run_lmhead(args):
+    """The Qwen3-8B-shaped LM head, 151936 x 4096 INT4/g128 (0.32 GB), through
+    wal_int4_gemv at batch 1; calls alternate between two packed copies, so
+    the 256 MB Infinity Cache cannot serve the weights."""
+    import torch
+    import ternary_hybrid_bit_amd as wal
+    dev = torch.device("cuda:0")
+    V, inp = 151936, 4096
+    rng = np.random.default_rng(np.random.SeedSequence([0, 60, 0]))
+    q = rng.integers(-8, 8, size=(V, inp), dtype=np.int8)
+    s = (np.abs(rng.standard_normal((V, inp // 128))) / 64).astype(np.float16).astype(np.float32)
+    blob = wal.wal_int4_pack(q, s)
+    del q
+    Ws = [torch.from_numpy(blob).to(dev) for _ in range(2)]
+    _, bits = __import__("synth").make_x(60, 0, inp)
+    X = torch.from_numpy(np.ascontiguousarray(bits[0]).view(np.int16)).to(dev).view(torch.bfloat16)
+    y = torch.empty(V, dtype=torch.float32, device=dev)
+    calls = max(args.steps, 50)
+    us = time_calls(torch, lambda i: wal.wal_int4_gemv(Ws[i % 2], V, inp, X, y), calls, args.settle_s)
+    gbs = blob.size / (us * 1e-6) / 1e9
+    res = {"workload": "lmhead", "entry": "wal_int4_gemv", "shape": [V, inp], "format": "INT4/g128, fp16 scales",
+           "packed_bytes": int(blob.size), "x_dtype": "bf16", "data": "synthetic", "calls": calls,
+           "us_per_call": round(us, 2), "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+           "weights_per_s": round(V * inp / (us * 1e-6), 1)}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -409,7 +437,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after timing, run one fp32 elementwise copy of this many MiB (counter calibration)")
-    ap.add_argument("--workload", default="sweep", choices=("sweep", "config1", "config3", "config4", "prefill", "decode-step"))
+    ap.add_argument("--workload", default="sweep", choices=("sweep", "config1", "config3", "config4", "prefill", "decode-step", "lmhead"))
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -417,6 +445,9 @@ def main():
         sys.exit(2)
     if args.workload == "decode-step":
         run_decode_step(args)
+        return
+    if args.workload == "lmhead":
+        run_lmhead(args)
         return
     if args.workload != "sweep":
         run_single(args)

@@ -293,6 +293,32 @@ enum { WAL_PHASE_LOWRANK = 1, WAL_PHASE_STREAM = 2, WAL_PHASE_ALL = 3 };
 int wal_gemv_grouped_phases(const wal_grouped_info* ginfo, const void* plan_dev, int phases,
                             void* stream);
 
+/* INT4/g128 packed matrices: the LM head of the WAL-Ternary-8B cards (Kazakh
+ * card, "Модель пішімі", and the English card list it as INT4/g128; nothing
+ * more is printed).  This repository's reading: W[v][j] = s[v][j / 128] *
+ * q[v][j] with q a signed 4-bit integer in [-8, 7] and one fp16 scale per 128
+ * consecutive columns (symmetric, no zero point).  Layout of a [V][in] matrix
+ * (in a multiple of 128):
+ *   codes  [V][in / 2] bytes, element 2i in the low nibble of byte i, 2i + 1
+ *          in the high nibble, two's-complement nibbles
+ *   scales [V][in / 128] fp16, little-endian, right after the codes
+ * wal_int4_size: bytes of the layout.  Errors: ARG, SHAPE.
+ * wal_int4_pack: q int8 [V][in], s float [V][in / 128] (host) -> dst (host).
+ *   A code outside [-8, 7] (WAL_ERR_CODE) or a scale fp16 cannot hold exactly
+ *   (WAL_ERR_INEXACT) is rejected before anything is written.
+ *   Errors: ARG, SHAPE, CODE, INEXACT, BUFFER.
+ * wal_int4_unpack: the inverse (q or s may be NULL).  Errors: ARG, SHAPE, BUFFER.
+ * wal_int4_gemv: y[v] = sum_j W[v][j] x[j] on the GPU, one matrix, batch 1.
+ *   W_dev  the layout in device memory, 256-byte aligned
+ *   x_dev  [in] bf16, 16-byte aligned (fp32 x: WAL_ERR_UNSUPPORTED)
+ *   y_dev  [V] fp32, overwritten
+ *   Errors: ARG, SHAPE, ALIGN, UNSUPPORTED, DEVICE. */
+int wal_int4_size(uint32_t V, uint32_t in, size_t* bytes);
+int wal_int4_pack(uint32_t V, uint32_t in, const int8_t* q, const float* s, void* dst, size_t dst_bytes);
+int wal_int4_unpack(uint32_t V, uint32_t in, const void* src, size_t src_bytes, int8_t* q, float* s);
+int wal_int4_gemv(const void* W_dev, uint32_t V, uint32_t in, const void* x_dev, int x_dtype, float* y_dev,
+                  void* stream);
+
 /* The normalised Hadamard-128 rotation of activations (WAL2-Ternary-27B card,
  * "Архитектура": the packed weights are rotated by a normalised H128 with
  * sign_mode identity, so a product of such a blob takes the rotated x):

@@ -93,6 +93,10 @@ _sig = {
     "wal_gemv_grouped": (_I, [ctypes.POINTER(wal_grouped_info), _P, _P]),
     "wal_gemv_grouped_phases": (_I, [ctypes.POINTER(wal_grouped_info), _P, _I, _P]),
     "wal_rotate_h128": (_I, [_P, _I, _U32, _U32, _U32, _P, _I, _U32, _P]),
+    "wal_int4_size": (_I, [_U32, _U32, ctypes.POINTER(_SZ)]),
+    "wal_int4_pack": (_I, [_U32, _U32, _P, _P, _P, _SZ]),
+    "wal_int4_unpack": (_I, [_U32, _U32, _P, _SZ, _P, _P]),
+    "wal_int4_gemv": (_I, [_P, _U32, _U32, _P, _I, _P, _P]),
     "wal_gemv_grouped_seq": (_I, [_U32, _P, _P, _P]),
     "wal_graph_create": (_I, [_U32, _P, _P, ctypes.POINTER(_P)]),
     "wal_graph_launch": (_I, [_P, _P]),
@@ -333,4 +337,35 @@ def wal_rotate_h128(X, out, stream=None):
                               O2.stride(0), _stream(stream))
     _check(st, "wal_rotate_h128")
     return out
+
+
+def wal_int4_size(V: int, inp: int) -> int:
+    n = _SZ()
+    _check(_lib.wal_int4_size(V, inp, ctypes.byref(n)), "wal_int4_size")
+    return n.value
+
+
+def wal_int4_pack(q, s) -> np.ndarray:
+    """INT4/g128 codes q [V][in] in [-8, 7] and scales s [V][in/128] -> packed bytes (host)."""
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    V, inp = q.shape
+    out = np.zeros(wal_int4_size(V, inp), dtype=np.uint8)
+    _check(_lib.wal_int4_pack(V, inp, q.ctypes.data, s.ctypes.data, out.ctypes.data, out.size), "wal_int4_pack")
+    return out
+
+
+def wal_int4_unpack(blob: np.ndarray, V: int, inp: int):
+    q = np.zeros((V, inp), dtype=np.int8)
+    s = np.zeros((V, inp // 128), dtype=np.float32)
+    _check(_lib.wal_int4_unpack(V, inp, blob.ctypes.data, blob.size, q.ctypes.data, s.ctypes.data), "wal_int4_unpack")
+    return q, s
+
+
+def wal_int4_gemv(W, V: int, inp: int, x, y, stream=None):
+    """y = W x for an INT4/g128 matrix W (device bytes), x [in] bf16, y [V] fp32."""
+    import torch
+    xdt = WAL_X_BF16 if x.dtype == torch.bfloat16 else WAL_X_F32
+    _check(_lib.wal_int4_gemv(_ptr(W), V, inp, _ptr(x), xdt, _ptr(y), _stream(stream)), "wal_int4_gemv")
+    return y
 

@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libwal.so")
 ARCH = os.environ.get("WAL_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-HIP_SOURCES = ["wal_gpu.hip", "wal_base3.hip", "wal_gemm.hip", "wal_rotate.hip"]
+HIP_SOURCES = ["wal_gpu.hip", "wal_base3.hip", "wal_gemm.hip", "wal_rotate.hip", "wal_int4.hip"]
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wno-unused-command-line-argument"]

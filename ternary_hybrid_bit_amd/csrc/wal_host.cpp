@@ -441,6 +441,51 @@ int wal_workspace_size(const wal_info* info, uint32_t batch, size_t* bytes) {
   return WAL_OK;
 }
 
+int wal_int4_size(uint32_t V, uint32_t in, size_t* bytes) {
+  if (!bytes || !V || !in) return WAL_ERR_ARG;
+  if (in % 128) return WAL_ERR_SHAPE;
+  *bytes = (size_t)V * in / 2 + (size_t)V * (in / 128) * 2;
+  return WAL_OK;
+}
+
+int wal_int4_pack(uint32_t V, uint32_t in, const int8_t* q, const float* s, void* dst, size_t dst_bytes) {
+  size_t need = 0;
+  int st = wal_int4_size(V, in, &need);
+  if (st) return st;
+  if (!q || !s || !dst) return WAL_ERR_ARG;
+  if (dst_bytes < need) return WAL_ERR_BUFFER;
+  const uint64_t n = (uint64_t)V * in, G = in / 128;
+  for (uint64_t i = 0; i < n; ++i)
+    if (q[i] < -8 || q[i] > 7) return WAL_ERR_CODE;
+  uint8_t h[2];
+  for (uint64_t i = 0; i < (uint64_t)V * G; ++i)   // every scale checked before anything is written
+    if ((st = put_scale(h, s[i], WAL_SCALE_FP16))) return st;
+  uint8_t* b = static_cast<uint8_t*>(dst);
+  uint8_t* sc = b + n / 2;
+  for (uint64_t i = 0; i < (uint64_t)V * G; ++i) (void)put_scale(sc + 2 * i, s[i], WAL_SCALE_FP16);
+  for (uint64_t i = 0; i < n / 2; ++i)
+    b[i] = (uint8_t)(((uint8_t)q[2 * i] & 0xFu) | (((uint8_t)q[2 * i + 1] & 0xFu) << 4));
+  return WAL_OK;
+}
+
+int wal_int4_unpack(uint32_t V, uint32_t in, const void* src, size_t src_bytes, int8_t* q, float* s) {
+  size_t need = 0;
+  int st = wal_int4_size(V, in, &need);
+  if (st) return st;
+  if (!src) return WAL_ERR_ARG;
+  if (src_bytes < need) return WAL_ERR_BUFFER;
+  const uint64_t n = (uint64_t)V * in, G = in / 128;
+  const uint8_t* b = static_cast<const uint8_t*>(src);
+  if (q)
+    for (uint64_t i = 0; i < n; ++i) {
+      const uint32_t nib = (b[i / 2] >> (4 * (i & 1))) & 0xFu;
+      q[i] = (int8_t)(nib >= 8 ? (int)nib - 16 : (int)nib);
+    }
+  if (s)
+    for (uint64_t i = 0; i < (uint64_t)V * G; ++i) s[i] = get_scale(b + n / 2 + 2 * i, WAL_SCALE_FP16);
+  return WAL_OK;
+}
+
 int wal_prefill_workspace_size(const wal_info* info, uint32_t batch, size_t* bytes) {
   if (!info || !bytes) return WAL_ERR_ARG;
   if (batch == 0 || batch > WAL_MAX_PREFILL_BATCH) return WAL_ERR_ARG;

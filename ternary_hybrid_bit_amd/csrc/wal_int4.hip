@@ -1,0 +1,203 @@
+// INT4/g128 GEMV for gfx950 (the WAL-Ternary-8B cards' LM head, INT4/g128):
+//     y[v] = sum_g s[v][g] sum_{j in g} q[v][j] x[j]
+// with q signed 4-bit codes (two per byte, element 2i low) and one fp16 scale
+// per 128 columns (layout in include/wal.h).
+//
+// A wavefront takes kI4Rows rows at a time over one 4096-column pass: lane l covers
+// columns 64 l .. 64 l + 63 (32 code bytes, half a scale group).  Each code
+// dword (8 nibbles) is flipped to offset binary (q + 8) and split by shift
+// and mask into bf16 pairs 0x4300 | (q + 8) = 136 + q, which feed
+// v_dot2_f32_bf16 against x pairs arranged the same way (columns k and k + 4
+// of the dword); the sum of 136 x over the lane's columns, formed by the same
+// v_dot2 sequence, comes off once per row.  The x
+// pairs and that sum stay in registers when the matrix is one pass wide.  The
+// next batch's codes and scales are loaded while one batch is reduced, and
+// the rows' lane sums meet in one transposed butterfly.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "wal_device.h"
+#include "wal_internal.h"
+
+namespace {
+
+constexpr int kI4Rows = 4;        // rows per batch of a wavefront (a power of two, at most 32)
+static_assert(kI4Rows >= 2 && kI4Rows <= 32 && (kI4Rows & (kI4Rows - 1)) == 0, "rows per batch");
+constexpr uint32_t kI4Pass = 4096;
+
+struct I4Batch {
+  u32x4_t c[kI4Rows][2];   // 32 code bytes per row
+  uint32_t s[kI4Rows];     // the lane's scale bits per row
+};
+
+// x of the lane for one pass: pair registers p[d][k] = (x[64 l + 8 d + k],
+// x[64 l + 8 d + k + 4]) for code dword d and nibble pair k, and base =
+// sum of 136 x over the lane's columns, formed by the same v_dot2 sequence as
+// a row's sum, so that it cancels exactly: all-zero codes give exactly 0 and
+// a basis vector x = e_j gives s q exactly (columns past `in` read as zero).
+struct I4X {
+  uint32_t p[8][4];
+  float base;
+};
+
+constexpr uint32_t kBf16Pair136 = 0x43084308u;   // bf16 (136, 136)
+
+__device__ __forceinline__ void load_x(__amdgpu_buffer_rsrc_t rx, uint32_t col, I4X& X) {
+  uint32_t w[32];   // bf16 pairs (x[2m], x[2m + 1]) of the lane's 64 columns
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rx, 2 * col + 16 * k, 0, 0);
+    w[4 * k] = v[0]; w[4 * k + 1] = v[1]; w[4 * k + 2] = v[2]; w[4 * k + 3] = v[3];
+  }
+  float base = 0.f;
+#pragma unroll
+  for (int d = 0; d < 8; ++d) {
+    // columns 8 d .. 8 d + 7 are bf16 pairs w[4 d] .. w[4 d + 3]
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t lo = w[4 * d + (k >> 1)], hi = w[4 * d + 2 + (k >> 1)];
+      // column 8 d + k from lo (half k & 1), column 8 d + k + 4 from hi
+      X.p[d][k] = __builtin_amdgcn_perm(hi, lo, (k & 1) ? 0x07060302u : 0x05040100u);
+      base = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, kBf16Pair136),
+                                             __builtin_bit_cast(bf16x2_t, X.p[d][k]), base, false);
+    }
+  }
+  X.base = base;
+}
+
+__device__ __forceinline__ I4Batch load_rows(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs, uint32_t row0,
+                                             uint32_t V, uint32_t in, uint32_t pass, uint32_t lane) {
+  I4Batch B;
+  const uint32_t col = pass * kI4Pass + 64 * lane, G = in / 128;
+#pragma unroll
+  for (int r = 0; r < kI4Rows; ++r) {
+    const uint32_t row = min(row0 + r, V - 1);
+    // columns past `in` (a partial last pass): out of range, zeros
+    const uint32_t off = col < in ? row * (in / 2) + col / 2 : 0x7FFFFFF0u;
+    B.c[r][0] = __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, kStream);   // read once: streaming policy
+    B.c[r][1] = __builtin_amdgcn_raw_buffer_load_b128(rc, off + 16, 0, kStream);
+    B.s[r] = __builtin_amdgcn_raw_buffer_load_b16(rs, col < in ? 2 * (row * G + col / 128) : 0x7FFFFFF0u, 0, 0);
+  }
+  return B;
+}
+
+// The lane's contribution to each row: s * (sum of (136 + q) x - sum of 136 x)
+__device__ __forceinline__ void dot_rows(const I4Batch& B, const I4X& X, float (&acc)[kI4Rows]) {
+#pragma unroll
+  for (int r = 0; r < kI4Rows; ++r) {
+    float a = 0.f;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const uint32_t w = B.c[r][d >> 2][d & 3] ^ 0x88888888u;   // offset binary: q + 8
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t pr = ((w >> (4 * k)) & 0x000F000Fu) | 0x43004300u;   // (136 + q_k, 136 + q_{k+4})
+        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pr), __builtin_bit_cast(bf16x2_t, X.p[d][k]),
+                                           a, false);
+      }
+    }
+    const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)B.s[r]);
+    acc[r] += sc * (a - X.base);
+  }
+}
+
+// Sum of acc[r] over the wavefront's 64 lanes by a transposed butterfly:
+// each xor step from 32 down halves the rows a lane keeps (the lane with the
+// step's bit set keeps the upper half), until each lane holds one row, then
+// the last steps add that row over the lanes that share it.  The row of lane
+// l is reduce_row(l); the lanes with l & (64 / kI4Rows - 1) == 0 hold sums.
+__device__ __forceinline__ uint32_t reduce_row(uint32_t lane) {
+  uint32_t row = 0;
+#pragma unroll
+  for (int m = 32, half = kI4Rows / 2; half >= 1; m >>= 1, half >>= 1)
+    if (lane & m) row += half;
+  return row;
+}
+
+__device__ __forceinline__ float reduce_rows(const float (&acc)[kI4Rows], uint32_t lane) {
+  float v[kI4Rows];
+#pragma unroll
+  for (int r = 0; r < kI4Rows; ++r) v[r] = acc[r];
+  int m = 32;
+#pragma unroll
+  for (int half = kI4Rows / 2; half >= 1; half >>= 1, m >>= 1) {
+    const bool upper = lane & m;
+#pragma unroll
+    for (int i = 0; i < half; ++i) {
+      const float keep = upper ? v[i + half] : v[i], send = upper ? v[i] : v[i + half];
+      v[i] = keep + __shfl_xor(send, m);
+    }
+  }
+  float t = v[0];
+#pragma unroll
+  for (; m >= 1; m >>= 1) t += __shfl_xor(t, m);
+  return t;
+}
+
+__global__ __launch_bounds__(256) void k_int4_gemv(const uint8_t* __restrict__ W, uint32_t V, uint32_t in,
+                                                   const void* __restrict__ x, float* __restrict__ y) {
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t wave = blockIdx.x * 4 + (threadIdx.x >> 6), nwaves = gridDim.x * 4;
+  const uint32_t batches = (V + kI4Rows - 1) / kI4Rows;
+  const uint32_t npass = (in + kI4Pass - 1) / kI4Pass;
+  const uint32_t cbytes = V * (in / 2);
+  const __amdgpu_buffer_rsrc_t rc = rsrc(W, cbytes);
+  const __amdgpu_buffer_rsrc_t rs = rsrc(W + cbytes, V * (in / 128) * 2);
+  const __amdgpu_buffer_rsrc_t rx = rsrc(x, 2 * in);
+  uint32_t b = wave;
+  if (b >= batches) return;
+  I4X X;
+  load_x(rx, 64 * lane, X);
+  if (npass == 1) {
+    // one pass: x stays in registers; two batches in flight
+    I4Batch B0 = load_rows(rc, rs, b * kI4Rows, V, in, 0, lane);
+    for (;;) {
+      const uint32_t bn = b + nwaves;
+      const I4Batch B1 = load_rows(rc, rs, min(bn, batches - 1) * kI4Rows, V, in, 0, lane);
+      float acc[kI4Rows] = {};
+      dot_rows(B0, X, acc);
+      const float v = reduce_rows(acc, lane);
+      const uint32_t row = b * kI4Rows + reduce_row(lane);
+      if ((lane & (64 / kI4Rows - 1)) == 0 && row < V) y[row] = v;
+      if (bn >= batches) break;
+      b = bn;
+      B0 = B1;
+    }
+    return;
+  }
+  for (; b < batches; b += nwaves) {
+    float acc[kI4Rows] = {};
+    for (uint32_t p = 0; p < npass; ++p) {
+      if (p) load_x(rx, p * kI4Pass + 64 * lane, X);
+      dot_rows(load_rows(rc, rs, b * kI4Rows, V, in, p, lane), X, acc);
+    }
+    const float v = reduce_rows(acc, lane);
+    const uint32_t row = b * kI4Rows + reduce_row(lane);
+    if ((lane & (64 / kI4Rows - 1)) == 0 && row < V) y[row] = v;
+  }
+}
+
+}  // namespace
+
+extern "C" int wal_int4_gemv(const void* W_dev, uint32_t V, uint32_t in, const void* x_dev, int x_dtype,
+                             float* y_dev, void* stream) {
+  if (!W_dev || !x_dev || !y_dev || !V || !in) return WAL_ERR_ARG;
+  if (x_dtype != WAL_X_F32 && x_dtype != WAL_X_BF16) return WAL_ERR_ARG;
+  if (in % 128) return WAL_ERR_SHAPE;
+  if ((uint64_t)V * in / 2 + (uint64_t)V * (in / 128) * 2 >= (1ull << 32)) return WAL_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(W_dev) & 255u) || (reinterpret_cast<uintptr_t>(x_dev) & 15u) ||
+      (reinterpret_cast<uintptr_t>(y_dev) & 3u))
+    return WAL_ERR_ALIGN;
+  if (x_dtype != WAL_X_BF16) return WAL_ERR_UNSUPPORTED;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return WAL_ERR_DEVICE;
+  const uint32_t batches = (V + kI4Rows - 1) / kI4Rows;
+  // two workgroups (8 wavefronts) per CU, each wavefront looping over batches
+  // (measured on the 151936 x 4096 head: faster than 1, 1.5, 3 or 4)
+  const uint32_t blocks = std::min<uint32_t>((batches + 3) / 4, (uint32_t)cus * 2);
+  hipLaunchKernelGGL(k_int4_gemv, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint8_t*>(W_dev), V, in, x_dev, y_dev);
+  return hipGetLastError() == hipSuccess ? WAL_OK : WAL_ERR_DEVICE;
+}

@@ -430,3 +430,40 @@ def test_grouped_plan_rejects_bad_arguments():
     assert wal._lib.wal_grouped_plan(1, arr, one, (ctypes.c_void_p * 1)((1 << 40) + 2), 1, y, 1 << 42, wsb, 4,
                                      buf.ctypes.data, buf.size, ctypes.byref(ginfo)) == -6
     assert wal._lib.wal_gemv_grouped(ctypes.byref(wal.wal_grouped_info()), 1 << 40, None) == -1
+
+
+def test_int4_pack_matches_oracle_and_rejects():
+    """INT4/g128: the C++ packer writes the oracle's bytes; bad codes, inexact
+    scales, shapes and short buffers are rejected; the product entry checks
+    its arguments before any launch."""
+    import ctypes
+    from oracle import int4 as I
+    rng = np.random.default_rng(21)
+    for V, inp in [(1, 128), (5, 384), (64, 4224)]:
+        q = rng.integers(-8, 8, size=(V, inp)).astype(np.int8)
+        s = (rng.integers(-2048, 2048, size=(V, inp // 128)) / 256.0).astype(np.float32)
+        b = wal.wal_int4_pack(q, s)
+        assert np.array_equal(b, I.pack(q, s.astype(np.float64)))
+        q2, s2 = wal.wal_int4_unpack(b, V, inp)
+        assert np.array_equal(q2, q) and np.array_equal(s2, s)
+    assert wal.wal_int4_size(151936, 4096) == I.size(151936, 4096)
+    lib = wal._lib
+    buf = np.zeros(I.size(2, 256), np.uint8)
+    q = np.zeros((2, 256), np.int8)
+    s = np.ones((2, 2), np.float32)
+    assert lib.wal_int4_pack(2, 256, q.ctypes.data, s.ctypes.data, buf.ctypes.data, buf.size - 1) == -5
+    assert lib.wal_int4_pack(2, 200, q.ctypes.data, s.ctypes.data, buf.ctypes.data, buf.size) == -2
+    q[1, 3] = 8
+    assert lib.wal_int4_pack(2, 256, q.ctypes.data, s.ctypes.data, buf.ctypes.data, buf.size) == -3
+    q[1, 3] = 0
+    s[0, 1] = 0.1
+    assert lib.wal_int4_pack(2, 256, q.ctypes.data, s.ctypes.data, buf.ctypes.data, buf.size) == -4
+    assert not buf.any()                                   # nothing written on rejection
+    g = lib.wal_int4_gemv
+    W, x, y = 0x10000, 0x20000, 0x30000
+    assert g(None, 2, 256, x, 1, y, None) == -1
+    assert g(W, 2, 200, x, 1, y, None) == -2
+    assert g(W + 16, 2, 256, x, 1, y, None) == -6
+    assert g(W, 2, 256, x + 2, 1, y, None) == -6
+    assert g(W, 2, 256, x, 0, y, None) == -9                # fp32 x
+    assert g(W, 2, 256, x, 5, y, None) == -1
