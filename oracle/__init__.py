@@ -24,9 +24,11 @@ Modules:
   ``oracle.rotation`` - the normalised Hadamard-128 rotation of x (the
                         WAL2-Ternary-27B card's rotation, "Архитектура").
   ``oracle.int4``   - INT4/g128 packed matrices (the 8B cards' LM head).
+  ``oracle.int3``   - INT3/g128 packed matrices and embedding rows (the 8B
+                      cards' embedding).
 
 Every function is pinned by tests under ``tests/`` against facts other than
 itself (golden bytes worked from the format readings, byte totals printed on
 the pages, exact-rational brute force, library special cases, invariants).
 """
-from . import format, dense, rotation, int4  # noqa: F401
+from . import format, dense, rotation, int4, int3  # noqa: F401

@@ -1,0 +1,80 @@
+"""INT3/g128 packed matrices and embedding rows (the 8B cards' embedding),
+float64.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+The WAL-Ternary-8B cards list the embedding as "INT3/g128" and say nothing
+more.  Read plainly: every weight is a signed 3-bit integer q in [-4, 3]
+and every group of 128 consecutive weights of a row shares one scale s, so
+E[v][j] = s[v][j // 128] * q[v][j].  This repository stores such a matrix
+[V][in] (in a multiple of 128) as
+
+    codes  [V][in * 3 / 8] bytes: row v's codes as one bit stream, element j
+           at stream bits 3 j .. 3 j + 2 (the stream's bit b is bit b % 8 of
+           byte b // 8), each code in two's complement
+    scales [V][in / 128] IEEE binary16, little-endian, after all the codes
+
+An embedding lookup returns whole rows: rows(ids) = E[ids].
+"""
+from __future__ import annotations
+
+import numpy as np
+
+GROUP = 128
+
+
+def size(V: int, inp: int) -> int:
+    if V <= 0 or inp <= 0 or inp % GROUP:
+        raise ValueError("V > 0 and in a positive multiple of 128")
+    return V * inp * 3 // 8 + V * (inp // GROUP) * 2
+
+
+def pack(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """Codes q int [V][in] in [-4, 3] and scales s [V][in/128] -> uint8 bytes."""
+    q = np.asarray(q)
+    V, inp = q.shape
+    nbytes = size(V, inp)
+    if q.min() < -4 or q.max() > 3:
+        raise ValueError("codes must lie in [-4, 3]")
+    s = np.asarray(s, dtype=np.float64)
+    if s.shape != (V, inp // GROUP):
+        raise ValueError("scales must be [V][in / 128]")
+    s16 = s.astype(np.float16)
+    if not np.array_equal(s16.astype(np.float64), s):
+        raise ValueError("a scale is not exactly representable in binary16")
+    code = (q.astype(np.int64) & 7)                                   # two's-complement 3-bit codes
+    bits = ((code[:, :, None] >> np.arange(3)) & 1).reshape(V, inp * 3)  # element j -> stream bits 3j..3j+2
+    packed = np.packbits(bits.astype(np.uint8), axis=1, bitorder="little")
+    out = np.empty(nbytes, dtype=np.uint8)
+    out[:V * inp * 3 // 8] = packed.reshape(-1)
+    out[V * inp * 3 // 8:] = s16.astype("<f2").view(np.uint8).reshape(-1)
+    return out
+
+
+def unpack(blob: np.ndarray, V: int, inp: int):
+    """uint8 bytes -> (q int8 [V][in], s float64 [V][in/128])."""
+    blob = np.asarray(blob, dtype=np.uint8)
+    if blob.size < size(V, inp):
+        raise ValueError("buffer too small")
+    cb = V * inp * 3 // 8
+    bits = np.unpackbits(blob[:cb].reshape(V, inp * 3 // 8), axis=1, bitorder="little").reshape(V, inp, 3)
+    code = (bits.astype(np.int64) << np.arange(3)).sum(axis=2)
+    q = np.where(code >= 4, code - 8, code).astype(np.int8)
+    s = blob[cb:size(V, inp)].view("<f2").astype(np.float64).reshape(V, inp // GROUP)
+    return q, s
+
+
+def dense(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """E = s (.)_g q, float64 [V][in]."""
+    return np.repeat(np.asarray(s, dtype=np.float64), GROUP, axis=1) * np.asarray(q, dtype=np.float64)
+
+
+def rows(blob: np.ndarray, V: int, inp: int, ids) -> np.ndarray:
+    """Embedding rows E[ids] (float64); ids outside [0, V) give zero rows."""
+    q, s = unpack(blob, V, inp)
+    E = dense(q, s)
+    ids = np.asarray(ids)
+    out = np.zeros((len(ids), inp))
+    ok = (ids >= 0) & (ids < V)
+    out[ok] = E[ids[ok]]
+    return out

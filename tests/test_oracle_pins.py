@@ -567,3 +567,48 @@ def test_int4_rejections():
         I.pack(np.zeros((1, 128), dtype=np.int64), np.array([[0.1]]))   # not binary16-exact
     with pytest.raises(ValueError):
         I.pack(np.zeros((1, 200), dtype=np.int64), np.ones((1, 1)))
+
+
+# ---------------------------------------------------------------------------
+# INT3/g128 packed matrices and embedding rows (oracle/int3.py)
+
+def test_int3_golden_bytes():
+    """Worked by hand from the layout reading: one LSB-first bit stream per
+    row, element j at stream bits 3j..3j+2, two's-complement codes."""
+    from oracle import int3 as I
+    q = np.zeros((1, 128), dtype=np.int64)
+    q[0, :8] = [-4, 3, -1, 0, 1, 2, -2, -3]          # codes 100 011 111 000 001 010 110 101
+    b = I.pack(q, np.array([[2.0]]))
+    assert b.size == 48 + 2
+    assert list(b[:3]) == [0xDC, 0x11, 0xB9] and not b[3:48].any()
+    assert list(b[48:]) == [0x00, 0x40]                     # 2.0 = 0x4000
+
+
+def test_int3_size_of_8b_embedding():
+    from oracle import int3 as I
+    assert I.size(151936, 4096) == 151936 * 1536 + 151936 * 32 * 2 == 243_134_464
+
+
+def test_int3_rows_exact_roundtrip_and_rejections():
+    from oracle import int3 as I
+    rng = np.random.default_rng(9)
+    V, inp = 6, 384
+    q = rng.integers(-4, 4, size=(V, inp))
+    s = rng.integers(-64, 64, size=(V, 3)) / 8.0
+    b = I.pack(q, s)
+    q2, s2 = I.unpack(b, V, inp)
+    assert np.array_equal(q2, q) and np.array_equal(s2, s)
+    ids = np.array([5, 0, 5, 2, -1, 6])
+    R = I.rows(b, V, inp, ids)
+    for n, v in enumerate(ids):
+        if 0 <= v < V:
+            exact = [Fraction(float(s[v, j // 128])) * int(q[v, j]) for j in range(inp)]
+            assert [Fraction(float(t)) for t in R[n]] == exact
+        else:
+            assert not R[n].any()
+    with pytest.raises(ValueError):
+        I.pack(np.full((1, 128), 4), np.ones((1, 1)))
+    with pytest.raises(ValueError):
+        I.pack(np.full((1, 128), -5), np.ones((1, 1)))
+    with pytest.raises(ValueError):
+        I.pack(np.zeros((1, 128), dtype=np.int64), np.array([[0.3]]))
