@@ -586,7 +586,7 @@ def test_int3_golden_bytes():
 
 def test_int3_size_of_8b_embedding():
     from oracle import int3 as I
-    assert I.size(151936, 4096) == 151936 * 1536 + 151936 * 32 * 2 == 243_134_464
+    assert I.size(151936, 4096) == 151936 * 1536 + 151936 * 32 * 2 == 243_097_600
 
 
 def test_int3_rows_exact_roundtrip_and_rejections():
