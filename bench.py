@@ -25,7 +25,8 @@ down shape through wal_gemm_prefill at batch 64 to 2048 beside torch's dense
 bf16 matmul of that shape; ``--workload decode-step`` runs the 36-layer step
 with its dependencies (q|k|v, o, gate|up, down per layer, one grouped product
 each, in order), eagerly and as a HIP graph replay; ``--workload lmhead`` the
-151936 x 4096 INT4/g128 LM head through wal_int4_gemv.  Each call reads one of about
+151936 x 4096 INT4/g128 LM head through wal_int4_gemv, then the lookup of 1
+and 2048 tokens in INT3 and INT4 embeddings of that size (wal_embed_rows).  Each call reads one of about
 1 GB of distinct packed copies in turn, so the 256 MB Infinity Cache cannot
 serve the weights; x stays fixed.  For context the line also carries the
 rate of torch's own reduction (torch.sum over 2 GiB) on the same GPU; it is
@@ -423,6 +424,24 @@ def run_lmhead(args):
            "packed_bytes": int(blob.size), "x_dtype": "bf16", "data": "synthetic", "calls": calls,
            "us_per_call": round(us, 2), "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
            "weights_per_s": round(V * inp / (us * 1e-6), 1)}
+    # the other end of the 8B models: the embedding lookup of n tokens from
+    # a 151936 x 4096 table, INT3/g128 and INT4/g128, bf16 rows out
+    del Ws
+    emb = {}
+    for bits in (3, 4):
+        qe = rng.integers(-(1 << (bits - 1)), 1 << (bits - 1), size=(V, inp), dtype=np.int8)
+        eb = wal.wal_int3_pack(qe, s) if bits == 3 else wal.wal_int4_pack(qe, s)
+        del qe
+        E = torch.from_numpy(eb).to(dev)
+        for n in (1, 2048):
+            ids = torch.from_numpy(np.random.default_rng(n).integers(0, V, n).astype(np.int32)).to(dev)
+            out = torch.empty((n, inp), dtype=torch.bfloat16, device=dev)
+            eus = time_calls(torch, lambda i: wal.wal_embed_rows(E, bits, V, inp, ids, out), calls, 0.1)
+            moved = n * (inp * bits // 8 + inp // 128 * 2) + n * inp * 2
+            emb[f"int{bits}_n{n}"] = {"us_per_call": round(eus, 2), "bytes": moved,
+                                      "GB/s": round(moved / (eus * 1e-6) / 1e9, 1)}
+        del E
+    res["embedding_bf16_out"] = emb
     print(json.dumps(res), flush=True)
 
 

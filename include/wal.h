@@ -319,6 +319,32 @@ int wal_int4_unpack(uint32_t V, uint32_t in, const void* src, size_t src_bytes, 
 int wal_int4_gemv(const void* W_dev, uint32_t V, uint32_t in, const void* x_dev, int x_dtype, float* y_dev,
                   void* stream);
 
+/* INT3/g128 packed matrices: the embedding of the WAL-Ternary-8B cards (listed
+ * as INT3/g128; nothing more is printed).  This repository's reading:
+ * E[v][j] = s[v][j / 128] * q[v][j], q a signed 3-bit integer in [-4, 3], one
+ * fp16 scale per 128 consecutive columns.  Layout of a [V][in] matrix:
+ *   codes  [V][in * 3 / 8] bytes: row v's codes as one bit stream, element j
+ *          at stream bits 3 j .. 3 j + 2 (stream bit b = bit b % 8 of byte
+ *          b / 8), two's-complement codes
+ *   scales [V][in / 128] fp16, little-endian, right after the codes
+ * wal_int3_size / wal_int3_pack / wal_int3_unpack: as the INT4 functions,
+ * with codes in [-4, 3].
+ * wal_embed_rows: out[i][:] = row ids[i] of an INT3 (bits = 3) or INT4/g128
+ * (bits = 4) matrix, decoded on the GPU: the embedding lookup of a batch of
+ * tokens.  Each value is s * q, exact in fp32; bf16 output rounds it to
+ * nearest even.
+ *   W_dev    the matrix in device memory, 256-byte aligned
+ *   ids_dev  [n] int32 row indices (device); an index outside [0, V) gives a
+ *            row of zeros
+ *   out_dev  [n][ldo] fp32 or bf16 (out_dtype), 16-byte aligned rows, ldo >= in;
+ *            columns past `in` untouched
+ *   Errors: ARG, SHAPE, ALIGN, DEVICE. */
+int wal_int3_size(uint32_t V, uint32_t in, size_t* bytes);
+int wal_int3_pack(uint32_t V, uint32_t in, const int8_t* q, const float* s, void* dst, size_t dst_bytes);
+int wal_int3_unpack(uint32_t V, uint32_t in, const void* src, size_t src_bytes, int8_t* q, float* s);
+int wal_embed_rows(const void* W_dev, int bits, uint32_t V, uint32_t in, const int32_t* ids_dev, uint32_t n,
+                   void* out_dev, int out_dtype, uint32_t ldo, void* stream);
+
 /* The normalised Hadamard-128 rotation of activations (WAL2-Ternary-27B card,
  * "Архитектура": the packed weights are rotated by a normalised H128 with
  * sign_mode identity, so a product of such a blob takes the rotated x):

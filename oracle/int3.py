@@ -70,11 +70,21 @@ def dense(q: np.ndarray, s: np.ndarray) -> np.ndarray:
 
 
 def rows(blob: np.ndarray, V: int, inp: int, ids) -> np.ndarray:
-    """Embedding rows E[ids] (float64); ids outside [0, V) give zero rows."""
-    q, s = unpack(blob, V, inp)
-    E = dense(q, s)
-    ids = np.asarray(ids)
+    """Embedding rows E[ids] (float64); ids outside [0, V) give zero rows.
+    Only the requested rows are decoded: row v's codes are bytes
+    v * in * 3 / 8 .. (v + 1) * in * 3 / 8 of the codes plane and its scales
+    the v-th run of in / 128 binary16 values of the scales plane."""
+    blob = np.asarray(blob, dtype=np.uint8)
+    if blob.size < size(V, inp):
+        raise ValueError("buffer too small")
+    ids = np.asarray(ids, dtype=np.int64)
     out = np.zeros((len(ids), inp))
     ok = (ids >= 0) & (ids < V)
-    out[ok] = E[ids[ok]]
+    if ok.any():
+        sel = ids[ok]
+        cb = V * inp * 3 // 8
+        codes = blob[:cb].reshape(V, inp * 3 // 8)[sel]
+        sc = blob[cb:size(V, inp)].reshape(V, inp // GROUP * 2)[sel]
+        q, s = unpack(np.concatenate([codes.reshape(-1), sc.reshape(-1)]), len(sel), inp)
+        out[ok] = dense(q, s)
     return out

@@ -85,3 +85,22 @@ def gemv_rows(blob: np.ndarray, V: int, inp: int, x: np.ndarray, rows) -> np.nda
     sc = blob[V * inp // 2:size(V, inp)].view("<f2").reshape(V, inp // GROUP)[rows]
     sub = np.concatenate([codes.reshape(-1), sc.astype("<f2").view(np.uint8).reshape(-1)])
     return gemv(sub, len(rows), inp, x)
+
+
+def rows(blob: np.ndarray, V: int, inp: int, ids) -> np.ndarray:
+    """Rows W[ids] (float64), the lookup of an INT4 embedding; ids outside
+    [0, V) give zero rows.  Only the requested rows are decoded."""
+    blob = np.asarray(blob, dtype=np.uint8)
+    if blob.size < size(V, inp):
+        raise ValueError("buffer too small")
+    ids = np.asarray(ids, dtype=np.int64)
+    out = np.zeros((len(ids), inp))
+    ok = (ids >= 0) & (ids < V)
+    if ok.any():
+        sel = ids[ok]
+        codes = blob[:V * inp // 2].reshape(V, inp // 2)[sel]
+        sc = blob[V * inp // 2:size(V, inp)].reshape(V, inp // GROUP * 2)[sel]
+        q, s = unpack(np.concatenate([codes.reshape(-1), sc.reshape(-1)]), len(sel), inp)
+        out[ok] = dense_W(q, s)
+    return out
+

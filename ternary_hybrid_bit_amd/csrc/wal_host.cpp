@@ -486,6 +486,57 @@ int wal_int4_unpack(uint32_t V, uint32_t in, const void* src, size_t src_bytes, 
   return WAL_OK;
 }
 
+int wal_int3_size(uint32_t V, uint32_t in, size_t* bytes) {
+  if (!bytes || !V || !in) return WAL_ERR_ARG;
+  if (in % 128) return WAL_ERR_SHAPE;
+  *bytes = (size_t)V * in * 3 / 8 + (size_t)V * (in / 128) * 2;
+  return WAL_OK;
+}
+
+int wal_int3_pack(uint32_t V, uint32_t in, const int8_t* q, const float* s, void* dst, size_t dst_bytes) {
+  size_t need = 0;
+  int st = wal_int3_size(V, in, &need);
+  if (st) return st;
+  if (!q || !s || !dst) return WAL_ERR_ARG;
+  if (dst_bytes < need) return WAL_ERR_BUFFER;
+  const uint64_t n = (uint64_t)V * in, G = in / 128, cb = n * 3 / 8;
+  for (uint64_t i = 0; i < n; ++i)
+    if (q[i] < -4 || q[i] > 3) return WAL_ERR_CODE;
+  uint8_t h[2];
+  for (uint64_t i = 0; i < (uint64_t)V * G; ++i)   // every scale checked before anything is written
+    if ((st = put_scale(h, s[i], WAL_SCALE_FP16))) return st;
+  uint8_t* b = static_cast<uint8_t*>(dst);
+  std::memset(b, 0, cb);
+  // a row is in * 3 / 8 whole bytes (in is a multiple of 128), so the rows'
+  // bit streams simply follow each other
+  for (uint64_t i = 0; i < n; ++i) {
+    const uint32_t code = (uint32_t)q[i] & 7u;
+    for (uint32_t k = 0; k < 3; ++k)
+      if ((code >> k) & 1u) b[(3 * i + k) / 8] |= (uint8_t)(1u << ((3 * i + k) % 8));
+  }
+  for (uint64_t i = 0; i < (uint64_t)V * G; ++i) (void)put_scale(b + cb + 2 * i, s[i], WAL_SCALE_FP16);
+  return WAL_OK;
+}
+
+int wal_int3_unpack(uint32_t V, uint32_t in, const void* src, size_t src_bytes, int8_t* q, float* s) {
+  size_t need = 0;
+  int st = wal_int3_size(V, in, &need);
+  if (st) return st;
+  if (!src) return WAL_ERR_ARG;
+  if (src_bytes < need) return WAL_ERR_BUFFER;
+  const uint64_t n = (uint64_t)V * in, G = in / 128, cb = n * 3 / 8;
+  const uint8_t* b = static_cast<const uint8_t*>(src);
+  if (q)
+    for (uint64_t i = 0; i < n; ++i) {
+      uint32_t code = 0;
+      for (uint32_t k = 0; k < 3; ++k) code |= ((b[(3 * i + k) / 8] >> ((3 * i + k) % 8)) & 1u) << k;
+      q[i] = (int8_t)(code >= 4 ? (int)code - 8 : (int)code);
+    }
+  if (s)
+    for (uint64_t i = 0; i < (uint64_t)V * G; ++i) s[i] = get_scale(b + cb + 2 * i, WAL_SCALE_FP16);
+  return WAL_OK;
+}
+
 int wal_prefill_workspace_size(const wal_info* info, uint32_t batch, size_t* bytes) {
   if (!info || !bytes) return WAL_ERR_ARG;
   if (batch == 0 || batch > WAL_MAX_PREFILL_BATCH) return WAL_ERR_ARG;

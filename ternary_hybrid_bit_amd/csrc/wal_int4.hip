@@ -201,3 +201,86 @@ extern "C" int wal_int4_gemv(const void* W_dev, uint32_t V, uint32_t in, const v
                      static_cast<const uint8_t*>(W_dev), V, in, x_dev, y_dev);
   return hipGetLastError() == hipSuccess ? WAL_OK : WAL_ERR_DEVICE;
 }
+
+// ---------------------------------------------------------------------------
+// Embedding rows: out[i][:] = row ids[i] of an INT3 (3-bit stream) or INT4
+// matrix (layouts in include/wal.h).  Block (i, c) decodes columns
+// 2048 c .. 2048 c + 2047 of token i, 16 consecutive values per thread: INT3
+// takes 6 bytes at 6 (j0 / 16) of the row's stream (three 16-bit loads),
+// INT4 8 bytes; one fp16 scale per thread (16 values lie inside one group).
+namespace {
+
+template <int BITS, int OT>
+__global__ __launch_bounds__(128) void k_embed_rows(const uint8_t* __restrict__ W, uint32_t V, uint32_t in,
+                                                    const int32_t* __restrict__ ids, void* __restrict__ out,
+                                                    uint32_t ldo) {
+  const uint32_t i = blockIdx.x, j0 = blockIdx.y * 2048 + 16 * threadIdx.x;
+  if (j0 >= in) return;
+  const uint32_t row = (uint32_t)ids[i];   // a negative index wraps past V
+  const bool ok = row < V;
+  const uint32_t r = ok ? row : 0, G = in / 128;
+  const uint32_t cbytes = V * (in * BITS / 8);
+  const __amdgpu_buffer_rsrc_t rc = rsrc(W, cbytes);
+  const __amdgpu_buffer_rsrc_t rs = rsrc(W + cbytes, V * G * 2);
+  const uint32_t base = r * (in * BITS / 8) + j0 * BITS / 8;
+  uint64_t v = 0;
+  if constexpr (BITS == 3) {
+    v = (uint64_t)__builtin_amdgcn_raw_buffer_load_b16(rc, base, 0, 0) |
+        ((uint64_t)__builtin_amdgcn_raw_buffer_load_b16(rc, base + 2, 0, 0) << 16) |
+        ((uint64_t)__builtin_amdgcn_raw_buffer_load_b16(rc, base + 4, 0, 0) << 32);
+  } else {
+    const u32x2_t w = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rc, base, 0, 0));
+    v = (uint64_t)w[0] | ((uint64_t)w[1] << 32);
+  }
+  if (!ok) v = 0;   // +0 everywhere in a row past the vocabulary
+  const float sc = ok ? (float)__builtin_bit_cast(_Float16, (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(
+                            rs, 2 * (r * G + j0 / 128), 0, 0))
+                      : 0.f;
+  float e[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int code = (int)((v >> (BITS * k)) & ((1u << BITS) - 1u));
+    const int q = code >= (1 << (BITS - 1)) ? code - (1 << BITS) : code;
+    e[k] = sc * (float)q;   // exact: at most 3 or 4 bits times an fp16 scale
+  }
+  if constexpr (OT == WAL_X_F32) {
+    float4* dst = reinterpret_cast<float4*>(static_cast<float*>(out) + (size_t)i * ldo + j0);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) dst[k] = make_float4(e[4 * k], e[4 * k + 1], e[4 * k + 2], e[4 * k + 3]);
+  } else {
+    uint32_t w[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t a = __float_as_uint(e[2 * k]), b = __float_as_uint(e[2 * k + 1]);
+      w[k] = ((a + 0x7FFFu + ((a >> 16) & 1u)) >> 16) | (((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16) << 16);
+    }
+    uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + (size_t)i * ldo + j0);
+    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  }
+}
+
+}  // namespace
+
+extern "C" int wal_embed_rows(const void* W_dev, int bits, uint32_t V, uint32_t in, const int32_t* ids_dev, uint32_t n,
+                              void* out_dev, int out_dtype, uint32_t ldo, void* stream) {
+  if (!W_dev || !ids_dev || !out_dev || !V || !in || !n) return WAL_ERR_ARG;
+  if (bits != 3 && bits != 4) return WAL_ERR_ARG;
+  if (out_dtype != WAL_X_F32 && out_dtype != WAL_X_BF16) return WAL_ERR_ARG;
+  if (in % 128) return WAL_ERR_SHAPE;
+  if (ldo < in) return WAL_ERR_ARG;
+  if ((uint64_t)V * in * bits / 8 + (uint64_t)V * (in / 128) * 2 >= (1ull << 32) || n > 65535u * 256u)
+    return WAL_ERR_SHAPE;
+  const size_t oe = out_dtype == WAL_X_BF16 ? 2 : 4;
+  if ((reinterpret_cast<uintptr_t>(W_dev) & 255u) || (reinterpret_cast<uintptr_t>(ids_dev) & 3u) ||
+      (reinterpret_cast<uintptr_t>(out_dev) & 15u) || (ldo * oe) % 16)
+    return WAL_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid(n, (in + 2047) / 2048), block(128);
+  const uint8_t* W = static_cast<const uint8_t*>(W_dev);
+  if (bits == 3 && out_dtype == WAL_X_F32) hipLaunchKernelGGL((k_embed_rows<3, WAL_X_F32>), grid, block, 0, s, W, V, in, ids_dev, out_dev, ldo);
+  else if (bits == 3) hipLaunchKernelGGL((k_embed_rows<3, WAL_X_BF16>), grid, block, 0, s, W, V, in, ids_dev, out_dev, ldo);
+  else if (out_dtype == WAL_X_F32) hipLaunchKernelGGL((k_embed_rows<4, WAL_X_F32>), grid, block, 0, s, W, V, in, ids_dev, out_dev, ldo);
+  else hipLaunchKernelGGL((k_embed_rows<4, WAL_X_BF16>), grid, block, 0, s, W, V, in, ids_dev, out_dev, ldo);
+  return hipGetLastError() == hipSuccess ? WAL_OK : WAL_ERR_DEVICE;
+}

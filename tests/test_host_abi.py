@@ -467,3 +467,48 @@ def test_int4_pack_matches_oracle_and_rejects():
     assert g(W, 2, 256, x + 2, 1, y, None) == -6
     assert g(W, 2, 256, x, 0, y, None) == -9                # fp32 x
     assert g(W, 2, 256, x, 5, y, None) == -1
+
+
+def test_int3_pack_matches_oracle_and_rejects():
+    """INT3/g128: the C++ packer writes the oracle's bytes and unpacks them
+    back; bad codes, inexact scales, shapes and short buffers are rejected
+    with nothing written; the row lookup checks its arguments before any
+    launch."""
+    from oracle import int3 as I
+    rng = np.random.default_rng(22)
+    for V, inp in [(1, 128), (3, 384), (40, 4224)]:
+        q = rng.integers(-4, 4, size=(V, inp)).astype(np.int8)
+        s = (rng.integers(-2048, 2048, size=(V, inp // 128)) / 256.0).astype(np.float32)
+        b = wal.wal_int3_pack(q, s)
+        assert np.array_equal(b, I.pack(q, s.astype(np.float64)))
+        q2, s2 = wal.wal_int3_unpack(b, V, inp)
+        assert np.array_equal(q2, q) and np.array_equal(s2, s)
+    assert wal.wal_int3_size(151936, 4096) == I.size(151936, 4096)
+    lib = wal._lib
+    buf = np.zeros(I.size(2, 256), np.uint8)
+    q = np.zeros((2, 256), np.int8)
+    s = np.ones((2, 2), np.float32)
+    assert lib.wal_int3_pack(2, 256, q.ctypes.data, s.ctypes.data, buf.ctypes.data, buf.size - 1) == -5
+    assert lib.wal_int3_pack(2, 200, q.ctypes.data, s.ctypes.data, buf.ctypes.data, buf.size) == -2
+    q[1, 3] = 4
+    assert lib.wal_int3_pack(2, 256, q.ctypes.data, s.ctypes.data, buf.ctypes.data, buf.size) == -3
+    q[1, 3] = -5
+    assert lib.wal_int3_pack(2, 256, q.ctypes.data, s.ctypes.data, buf.ctypes.data, buf.size) == -3
+    q[1, 3] = 0
+    s[1, 1] = 1e-9
+    assert lib.wal_int3_pack(2, 256, q.ctypes.data, s.ctypes.data, buf.ctypes.data, buf.size) == -4
+    assert not buf.any()
+    e = lib.wal_embed_rows
+    W, ids, out = 0x10000, 0x20000, 0x30000
+    assert e(None, 3, 2, 256, ids, 1, out, 0, 256, None) == -1
+    assert e(W, 5, 2, 256, ids, 1, out, 0, 256, None) == -1          # bits
+    assert e(W, 3, 2, 200, ids, 1, out, 0, 256, None) == -2          # in % 128
+    assert e(W, 3, 2, 256, ids, 1, out, 0, 200, None) == -1          # ldo < in
+    assert e(W, 3, 2, 256, ids, 0, out, 0, 256, None) == -1          # n = 0
+    assert e(W, 3, 2, 256, ids, 1, out, 7, 256, None) == -1          # out dtype
+    assert e(W + 16, 4, 2, 256, ids, 1, out, 0, 256, None) == -6
+    assert e(W, 4, 2, 256, ids + 2, 1, out, 0, 256, None) == -6
+    assert e(W, 4, 2, 256, ids, 1, out + 4, 0, 256, None) == -6
+    assert e(W, 4, 2, 256, ids, 1, out, 1, 260, None) == -6          # bf16 rows of 520 B
+    assert e(W, 4, 1 << 20, 1 << 13, ids, 1, out, 0, 1 << 13, None) == -2   # 2^32 bytes
+

@@ -570,6 +570,25 @@ def test_int4_rejections():
 
 
 # ---------------------------------------------------------------------------
+def test_int4_rows_exact():
+    """INT4 row lookup: every selected row equals s * q worked as exact
+    rationals from the codes and scales; out-of-range ids give zero rows."""
+    from oracle import int4 as I
+    rng = np.random.default_rng(13)
+    V, inp = 5, 256
+    q = rng.integers(-8, 8, size=(V, inp))
+    s = rng.integers(-64, 64, size=(V, 2)) / 16.0
+    b = I.pack(q, s)
+    ids = np.array([4, -3, 0, 4, 5, 2])
+    R = I.rows(b, V, inp, ids)
+    for n, v in enumerate(ids):
+        if 0 <= v < V:
+            assert [Fraction(float(t)) for t in R[n]] == [Fraction(float(s[v, j // 128])) * int(q[v, j])
+                                                          for j in range(inp)]
+        else:
+            assert not R[n].any()
+
+
 # INT3/g128 packed matrices and embedding rows (oracle/int3.py)
 
 def test_int3_golden_bytes():
