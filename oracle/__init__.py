@@ -26,9 +26,10 @@ Modules:
   ``oracle.int4``   - INT4/g128 packed matrices (the 8B cards' LM head).
   ``oracle.int3``   - INT3/g128 packed matrices and embedding rows (the 8B
                       cards' embedding).
+  ``oracle.int5``   - INT5/g128 packed matrices (the RC1 card's LM head).
 
 Every function is pinned by tests under ``tests/`` against facts other than
 itself (golden bytes worked from the format readings, byte totals printed on
 the pages, exact-rational brute force, library special cases, invariants).
 """
-from . import format, dense, rotation, int4, int3  # noqa: F401
+from . import format, dense, rotation, int4, int3, int5  # noqa: F401

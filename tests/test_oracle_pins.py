@@ -569,7 +569,6 @@ def test_int4_rejections():
         I.pack(np.zeros((1, 200), dtype=np.int64), np.ones((1, 1)))
 
 
-# ---------------------------------------------------------------------------
 def test_int4_rows_exact():
     """INT4 row lookup: every selected row equals s * q worked as exact
     rationals from the codes and scales; out-of-range ids give zero rows."""
@@ -589,6 +588,7 @@ def test_int4_rows_exact():
             assert not R[n].any()
 
 
+# ---------------------------------------------------------------------------
 # INT3/g128 packed matrices and embedding rows (oracle/int3.py)
 
 def test_int3_golden_bytes():
@@ -631,3 +631,77 @@ def test_int3_rows_exact_roundtrip_and_rejections():
         I.pack(np.full((1, 128), -5), np.ones((1, 1)))
     with pytest.raises(ValueError):
         I.pack(np.zeros((1, 128), dtype=np.int64), np.array([[0.3]]))
+
+
+# ---------------------------------------------------------------------------
+# INT5/g128 packed matrices (oracle/int5.py)
+
+def test_int5_golden_bytes():
+    """Worked by hand from the layout reading: element j at stream bits
+    5j..5j+4, stream bit b in bit b % 8 of byte b // 8, two's complement.
+    Codes 1, -1, 15, -16 are 00001, 11111, 01111, 10000 (bit 0 first):
+    stream bits 0..19 = 1 0000 11111 1111 0 0000 1, i.e. bytes 0xE1, 0x3F, 0x08."""
+    from oracle import int5 as I
+    q = np.zeros((1, 128), dtype=np.int64)
+    q[0, :4] = [1, -1, 15, -16]
+    b = I.pack(q, np.array([[0.5]]))
+    assert b.size == 80 + 2
+    assert list(b[:3]) == [0xE1, 0x3F, 0x08] and not b[3:80].any()
+    assert list(b[80:]) == [0x00, 0x38]                       # 0.5 = 0x3800
+    q = np.full((2, 128), -1, dtype=np.int64)                  # all ones: every code byte 0xFF
+    b = I.pack(q, np.array([[1.0], [-2.0]]))
+    assert (b[:160] == 0xFF).all() and list(b[160:]) == [0x00, 0x3C, 0x00, 0xC0]
+
+
+def test_int5_bruteforce_exact():
+    """Tiny matrices against the definition in exact rationals."""
+    from oracle import int5 as I
+    rng = np.random.default_rng(17)
+    V, inp = 3, 256
+    q = rng.integers(-16, 16, size=(V, inp))
+    s = rng.choice([0.25, 0.5, 1.5, -0.75, 2.0 ** -10, 3.0], size=(V, inp // 128))
+    x = rng.integers(-5, 6, size=inp)
+    y = I.gemv(I.pack(q, s), V, inp, x)
+    for v in range(V):
+        exact = sum(Fraction(float(s[v, j // 128])) * int(q[v, j]) * int(x[j]) for j in range(inp))
+        assert Fraction(float(y[v])) == exact
+
+
+def test_int5_reduces_to_int4():
+    """Codes inside [-8, 7] are the INT4 head's codes: the two packed forms
+    of the same q and s give the same product (INT4 pinned above)."""
+    from oracle import int4 as I4
+    from oracle import int5 as I5
+    rng = np.random.default_rng(18)
+    V, inp = 7, 384
+    q = rng.integers(-8, 8, size=(V, inp))
+    s = rng.integers(-64, 64, size=(V, 3)) / 32.0
+    x = rng.standard_normal(inp)
+    assert np.array_equal(I5.gemv(I5.pack(q, s), V, inp, x), I4.gemv(I4.pack(q, s), V, inp, x))
+
+
+def test_int5_columns_roundtrip_and_rejections():
+    from oracle import int5 as I
+    rng = np.random.default_rng(19)
+    V, inp = 5, 384
+    q = rng.integers(-16, 16, size=(V, inp))
+    s = rng.integers(-64, 64, size=(V, 3)) / 16.0
+    b = I.pack(q, s)
+    assert b.size == I.size(V, inp) == V * 240 + V * 6
+    q2, s2 = I.unpack(b, V, inp)
+    assert np.array_equal(q2, q) and np.array_equal(s2, s)
+    for j in (0, 1, 6, 7, 8, 127, 128, 383):
+        e = np.zeros(inp)
+        e[j] = 1.0
+        assert np.array_equal(I.gemv(b, V, inp, e), s[:, j // 128] * q[:, j])
+    x = rng.standard_normal(inp)
+    assert np.allclose(I.gemv_rows(b, V, inp, x, [4, 0, 2]), I.gemv(b, V, inp, x)[[4, 0, 2]], rtol=0, atol=1e-12)
+    ok_s = np.ones((1, 1))
+    for bad in (16, -17):
+        with pytest.raises(ValueError):
+            I.pack(np.full((1, 128), bad), ok_s)
+    with pytest.raises(ValueError):
+        I.pack(np.zeros((1, 128), dtype=np.int64), np.array([[0.1]]))
+    with pytest.raises(ValueError):
+        I.pack(np.zeros((1, 200), dtype=np.int64), np.ones((1, 1)))
+
