@@ -25,7 +25,8 @@ down shape through wal_gemm_prefill at batch 64 to 2048 beside torch's dense
 bf16 matmul of that shape; ``--workload decode-step`` runs the 36-layer step
 with its dependencies (q|k|v, o, gate|up, down per layer, one grouped product
 each, in order), eagerly and as a HIP graph replay; ``--workload lmhead`` the
-151936 x 4096 INT4/g128 LM head through wal_int4_gemv, then the lookup of 1
+151936 x 4096 INT4/g128 LM head through wal_int4_gemv, the 248320 x 5120
+INT5/g128 head through wal_int5_gemv, then the lookup of 1
 and 2048 tokens in INT3 and INT4 embeddings of that size (wal_embed_rows).  Each call reads one of about
 1 GB of distinct packed copies in turn, so the 256 MB Infinity Cache cannot
 serve the weights; x stays fixed.  For context the line also carries the
@@ -424,9 +425,25 @@ def run_lmhead(args):
            "packed_bytes": int(blob.size), "x_dtype": "bf16", "data": "synthetic", "calls": calls,
            "us_per_call": round(us, 2), "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
            "weights_per_s": round(V * inp / (us * 1e-6), 1)}
+    # the RC1 card's packed INT5 head, 27B-shaped: 248320 x 5120
+    del Ws
+    V5, in5 = 248320, 5120
+    q5 = rng.integers(-16, 16, size=(V5, in5), dtype=np.int8)
+    s5 = (np.abs(rng.standard_normal((V5, in5 // 128))) / 64).astype(np.float16).astype(np.float32)
+    b5 = wal.wal_int5_pack(q5, s5)
+    del q5
+    W5 = [torch.from_numpy(b5).to(dev) for _ in range(2)]
+    _, bits5 = __import__("synth").make_x(61, 0, in5)
+    X5 = torch.from_numpy(np.ascontiguousarray(bits5[0]).view(np.int16)).to(dev).view(torch.bfloat16)
+    y5 = torch.empty(V5, dtype=torch.float32, device=dev)
+    us5 = time_calls(torch, lambda i: wal.wal_int5_gemv(W5[i % 2], V5, in5, X5, y5), calls, args.settle_s)
+    g5 = b5.size / (us5 * 1e-6) / 1e9
+    res["int5_head"] = {"entry": "wal_int5_gemv", "shape": [V5, in5], "format": "INT5/g128, fp16 scales",
+                        "packed_bytes": int(b5.size), "us_per_call": round(us5, 2), "GB/s": round(g5, 1),
+                        "hbm_frac": round(g5 / HBM_PEAK_GBS, 4)}
+    del W5
     # the other end of the 8B models: the embedding lookup of n tokens from
     # a 151936 x 4096 table, INT3/g128 and INT4/g128, bf16 rows out
-    del Ws
     emb = {}
     for bits in (3, 4):
         qe = rng.integers(-(1 << (bits - 1)), 1 << (bits - 1), size=(V, inp), dtype=np.int8)

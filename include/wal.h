@@ -312,6 +312,7 @@ int wal_gemv_grouped_phases(const wal_grouped_info* ginfo, const void* plan_dev,
  *   W_dev  the layout in device memory, 256-byte aligned
  *   x_dev  [in] bf16, 16-byte aligned (fp32 x: WAL_ERR_UNSUPPORTED)
  *   y_dev  [V] fp32, overwritten
+ *   The packed matrix must be under 2^31 bytes (else WAL_ERR_SHAPE).
  *   Errors: ARG, SHAPE, ALIGN, UNSUPPORTED, DEVICE. */
 int wal_int4_size(uint32_t V, uint32_t in, size_t* bytes);
 int wal_int4_pack(uint32_t V, uint32_t in, const int8_t* q, const float* s, void* dst, size_t dst_bytes);
@@ -338,12 +339,31 @@ int wal_int4_gemv(const void* W_dev, uint32_t V, uint32_t in, const void* x_dev,
  *            row of zeros
  *   out_dev  [n][ldo] fp32 or bf16 (out_dtype), 16-byte aligned rows, ldo >= in;
  *            columns past `in` untouched
+ *   The packed matrix must be under 2^32 bytes (else WAL_ERR_SHAPE).
  *   Errors: ARG, SHAPE, ALIGN, DEVICE. */
 int wal_int3_size(uint32_t V, uint32_t in, size_t* bytes);
 int wal_int3_pack(uint32_t V, uint32_t in, const int8_t* q, const float* s, void* dst, size_t dst_bytes);
 int wal_int3_unpack(uint32_t V, uint32_t in, const void* src, size_t src_bytes, int8_t* q, float* s);
 int wal_embed_rows(const void* W_dev, int bits, uint32_t V, uint32_t in, const int32_t* ids_dev, uint32_t n,
                    void* out_dev, int out_dtype, uint32_t ldo, void* stream);
+
+/* INT5/g128 packed matrices: the LM head of the WAL-Ternary-27B-RC1 card
+ * (section "Representation" lists it as packed INT5; nothing more is
+ * printed).  This repository's reading, in line with the other cards'
+ * symmetric INT4/g128 head: W[v][j] = s[v][j / 128] * q[v][j], q a signed
+ * 5-bit integer in [-16, 15], one fp16 scale per 128 columns, five bits per
+ * weight with no padding.  Layout of a [V][in] matrix (in a multiple of 128):
+ *   codes  [V][in * 5 / 8] bytes: row v's codes as one bit stream, element j
+ *          at stream bits 5 j .. 5 j + 4 (stream bit b = bit b % 8 of byte
+ *          b / 8), two's-complement codes
+ *   scales [V][in / 128] fp16, little-endian, right after the codes
+ * wal_int5_size / wal_int5_pack / wal_int5_unpack / wal_int5_gemv: as the
+ * INT4 functions, with codes in [-16, 15]. */
+int wal_int5_size(uint32_t V, uint32_t in, size_t* bytes);
+int wal_int5_pack(uint32_t V, uint32_t in, const int8_t* q, const float* s, void* dst, size_t dst_bytes);
+int wal_int5_unpack(uint32_t V, uint32_t in, const void* src, size_t src_bytes, int8_t* q, float* s);
+int wal_int5_gemv(const void* W_dev, uint32_t V, uint32_t in, const void* x_dev, int x_dtype, float* y_dev,
+                  void* stream);
 
 /* The normalised Hadamard-128 rotation of activations (WAL2-Ternary-27B card,
  * "Архитектура": the packed weights are rotated by a normalised H128 with

@@ -101,6 +101,10 @@ _sig = {
     "wal_int3_pack": (_I, [_U32, _U32, _P, _P, _P, _SZ]),
     "wal_int3_unpack": (_I, [_U32, _U32, _P, _SZ, _P, _P]),
     "wal_embed_rows": (_I, [_P, _I, _U32, _U32, _P, _U32, _P, _I, _U32, _P]),
+    "wal_int5_size": (_I, [_U32, _U32, ctypes.POINTER(_SZ)]),
+    "wal_int5_pack": (_I, [_U32, _U32, _P, _P, _P, _SZ]),
+    "wal_int5_unpack": (_I, [_U32, _U32, _P, _SZ, _P, _P]),
+    "wal_int5_gemv": (_I, [_P, _U32, _U32, _P, _I, _P, _P]),
     "wal_gemv_grouped_seq": (_I, [_U32, _P, _P, _P]),
     "wal_graph_create": (_I, [_U32, _P, _P, ctypes.POINTER(_P)]),
     "wal_graph_launch": (_I, [_P, _P]),
@@ -395,6 +399,37 @@ def wal_int3_unpack(blob: np.ndarray, V: int, inp: int):
     s = np.zeros((V, inp // 128), dtype=np.float32)
     _check(_lib.wal_int3_unpack(V, inp, blob.ctypes.data, blob.size, q.ctypes.data, s.ctypes.data), "wal_int3_unpack")
     return q, s
+
+
+def wal_int5_size(V: int, inp: int) -> int:
+    n = _SZ()
+    _check(_lib.wal_int5_size(V, inp, ctypes.byref(n)), "wal_int5_size")
+    return n.value
+
+
+def wal_int5_pack(q, s) -> np.ndarray:
+    """INT5/g128 codes q [V][in] in [-16, 15] and scales s [V][in/128] -> packed bytes (host)."""
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    V, inp = q.shape
+    out = np.zeros(wal_int5_size(V, inp), dtype=np.uint8)
+    _check(_lib.wal_int5_pack(V, inp, q.ctypes.data, s.ctypes.data, out.ctypes.data, out.size), "wal_int5_pack")
+    return out
+
+
+def wal_int5_unpack(blob: np.ndarray, V: int, inp: int):
+    q = np.zeros((V, inp), dtype=np.int8)
+    s = np.zeros((V, inp // 128), dtype=np.float32)
+    _check(_lib.wal_int5_unpack(V, inp, blob.ctypes.data, blob.size, q.ctypes.data, s.ctypes.data), "wal_int5_unpack")
+    return q, s
+
+
+def wal_int5_gemv(W, V: int, inp: int, x, y, stream=None):
+    """y = W x for an INT5/g128 matrix W (device bytes), x [in] bf16, y [V] fp32."""
+    import torch
+    xdt = WAL_X_BF16 if x.dtype == torch.bfloat16 else WAL_X_F32
+    _check(_lib.wal_int5_gemv(_ptr(W), V, inp, _ptr(x), xdt, _ptr(y), _stream(stream)), "wal_int5_gemv")
+    return y
 
 
 def wal_embed_rows(W, bits: int, V: int, inp: int, ids, out, stream=None):

@@ -486,55 +486,76 @@ int wal_int4_unpack(uint32_t V, uint32_t in, const void* src, size_t src_bytes, 
   return WAL_OK;
 }
 
-int wal_int3_size(uint32_t V, uint32_t in, size_t* bytes) {
+// INT3 and INT5 matrices: every row's b-bit codes as one bit stream (element j
+// at stream bits b j .. b j + b - 1, LSB first), then fp16 scales per 128.
+// A row is in * b / 8 whole bytes (in is a multiple of 128), so the rows'
+// streams simply follow each other.
+static int qstream_size(uint32_t bits, uint32_t V, uint32_t in, size_t* bytes) {
   if (!bytes || !V || !in) return WAL_ERR_ARG;
   if (in % 128) return WAL_ERR_SHAPE;
-  *bytes = (size_t)V * in * 3 / 8 + (size_t)V * (in / 128) * 2;
+  *bytes = (size_t)V * in * bits / 8 + (size_t)V * (in / 128) * 2;
   return WAL_OK;
 }
 
-int wal_int3_pack(uint32_t V, uint32_t in, const int8_t* q, const float* s, void* dst, size_t dst_bytes) {
+static int qstream_pack(uint32_t bits, uint32_t V, uint32_t in, const int8_t* q, const float* s, void* dst,
+                        size_t dst_bytes) {
   size_t need = 0;
-  int st = wal_int3_size(V, in, &need);
+  int st = qstream_size(bits, V, in, &need);
   if (st) return st;
   if (!q || !s || !dst) return WAL_ERR_ARG;
   if (dst_bytes < need) return WAL_ERR_BUFFER;
-  const uint64_t n = (uint64_t)V * in, G = in / 128, cb = n * 3 / 8;
+  const int lo = -(1 << (bits - 1)), hi = (1 << (bits - 1)) - 1;
+  const uint64_t n = (uint64_t)V * in, G = in / 128, cb = n * bits / 8;
   for (uint64_t i = 0; i < n; ++i)
-    if (q[i] < -4 || q[i] > 3) return WAL_ERR_CODE;
+    if (q[i] < lo || q[i] > hi) return WAL_ERR_CODE;
   uint8_t h[2];
   for (uint64_t i = 0; i < (uint64_t)V * G; ++i)   // every scale checked before anything is written
     if ((st = put_scale(h, s[i], WAL_SCALE_FP16))) return st;
   uint8_t* b = static_cast<uint8_t*>(dst);
   std::memset(b, 0, cb);
-  // a row is in * 3 / 8 whole bytes (in is a multiple of 128), so the rows'
-  // bit streams simply follow each other
+  const uint32_t mask = (1u << bits) - 1u;
   for (uint64_t i = 0; i < n; ++i) {
-    const uint32_t code = (uint32_t)q[i] & 7u;
-    for (uint32_t k = 0; k < 3; ++k)
-      if ((code >> k) & 1u) b[(3 * i + k) / 8] |= (uint8_t)(1u << ((3 * i + k) % 8));
+    const uint32_t code = (uint32_t)q[i] & mask;
+    for (uint32_t k = 0; k < bits; ++k)
+      if ((code >> k) & 1u) b[(bits * i + k) / 8] |= (uint8_t)(1u << ((bits * i + k) % 8));
   }
   for (uint64_t i = 0; i < (uint64_t)V * G; ++i) (void)put_scale(b + cb + 2 * i, s[i], WAL_SCALE_FP16);
   return WAL_OK;
 }
 
-int wal_int3_unpack(uint32_t V, uint32_t in, const void* src, size_t src_bytes, int8_t* q, float* s) {
+static int qstream_unpack(uint32_t bits, uint32_t V, uint32_t in, const void* src, size_t src_bytes, int8_t* q,
+                          float* s) {
   size_t need = 0;
-  int st = wal_int3_size(V, in, &need);
+  int st = qstream_size(bits, V, in, &need);
   if (st) return st;
   if (!src) return WAL_ERR_ARG;
   if (src_bytes < need) return WAL_ERR_BUFFER;
-  const uint64_t n = (uint64_t)V * in, G = in / 128, cb = n * 3 / 8;
+  const uint64_t n = (uint64_t)V * in, G = in / 128, cb = n * bits / 8;
   const uint8_t* b = static_cast<const uint8_t*>(src);
   if (q)
     for (uint64_t i = 0; i < n; ++i) {
       uint32_t code = 0;
-      for (uint32_t k = 0; k < 3; ++k) code |= ((b[(3 * i + k) / 8] >> ((3 * i + k) % 8)) & 1u) << k;
-      q[i] = (int8_t)(code >= 4 ? (int)code - 8 : (int)code);
+      for (uint32_t k = 0; k < bits; ++k) code |= ((b[(bits * i + k) / 8] >> ((bits * i + k) % 8)) & 1u) << k;
+      q[i] = (int8_t)(code >> (bits - 1) ? (int)code - (1 << bits) : (int)code);
     }
   if (s)
     for (uint64_t i = 0; i < (uint64_t)V * G; ++i) s[i] = get_scale(b + cb + 2 * i, WAL_SCALE_FP16);
   return WAL_OK;
+}
+
+int wal_int3_size(uint32_t V, uint32_t in, size_t* bytes) { return qstream_size(3, V, in, bytes); }
+int wal_int3_pack(uint32_t V, uint32_t in, const int8_t* q, const float* s, void* dst, size_t dst_bytes) {
+  return qstream_pack(3, V, in, q, s, dst, dst_bytes);
+}
+int wal_int3_unpack(uint32_t V, uint32_t in, const void* src, size_t src_bytes, int8_t* q, float* s) {
+  return qstream_unpack(3, V, in, src, src_bytes, q, s);
+}
+int wal_int5_size(uint32_t V, uint32_t in, size_t* bytes) { return qstream_size(5, V, in, bytes); }
+int wal_int5_pack(uint32_t V, uint32_t in, const int8_t* q, const float* s, void* dst, size_t dst_bytes) {
+  return qstream_pack(5, V, in, q, s, dst, dst_bytes);
+}
+int wal_int5_unpack(uint32_t V, uint32_t in, const void* src, size_t src_bytes, int8_t* q, float* s) {
+  return qstream_unpack(5, V, in, src, src_bytes, q, s);
 }
 
 int wal_prefill_workspace_size(const wal_info* info, uint32_t batch, size_t* bytes) {

@@ -1,18 +1,21 @@
-// INT4/g128 GEMV for gfx950 (the WAL-Ternary-8B cards' LM head, INT4/g128):
+// INT4/g128 and INT5/g128 GEMV for gfx950 (the WAL-Ternary-8B cards' LM
+// head, INT4/g128, and the WAL-Ternary-27B-RC1 card's packed INT5 head):
 //     y[v] = sum_g s[v][g] sum_{j in g} q[v][j] x[j]
-// with q signed 4-bit codes (two per byte, element 2i low) and one fp16 scale
-// per 128 columns (layout in include/wal.h).
+// with q signed codes (INT4: two per byte, element 2i low; INT5: an LSB-first
+// 5-bit stream per row) and one fp16 scale per 128 columns (layouts in
+// include/wal.h); and the embedding-row lookup of INT3 and INT4 tables.
 //
-// A wavefront takes kI4Rows rows at a time over one 4096-column pass: lane l covers
-// columns 64 l .. 64 l + 63 (32 code bytes, half a scale group).  Each code
-// dword (8 nibbles) is flipped to offset binary (q + 8) and split by shift
-// and mask into bf16 pairs 0x4300 | (q + 8) = 136 + q, which feed
-// v_dot2_f32_bf16 against x pairs arranged the same way (columns k and k + 4
-// of the dword); the sum of 136 x over the lane's columns, formed by the same
-// v_dot2 sequence, comes off once per row.  The x
-// pairs and that sum stay in registers when the matrix is one pass wide.  The
-// next batch's codes and scales are loaded while one batch is reduced, and
-// the rows' lane sums meet in one transposed butterfly.
+// A wavefront takes kI4Rows rows at a time over one 4096-column pass: lane l
+// covers columns 64 l .. 64 l + 63 (32 or 40 code bytes, half a scale group).
+// Codes are flipped to offset binary and spread into bf16 pairs
+// 0x4300 | (q + 2^(b-1)) = 128 + 2^(b-1) + q, which feed v_dot2_f32_bf16
+// against x pairs arranged to match (INT4: columns k and k + 4 of a dword,
+// INT5: columns 2 m and 2 m + 1); the sum of the offset times x over the
+// lane's columns, formed by the same v_dot2 sequence, comes off once per row,
+// so it cancels exactly.  x and that sum stay in registers for widths up to
+// one pass (plus a 1024-column tail spread over the wavefront); the next
+// batch's codes and scales are loaded while one batch is reduced, and the
+// rows' lane sums meet in one transposed butterfly.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -26,30 +29,48 @@ constexpr int kI4Rows = 4;        // rows per batch of a wavefront (a power of t
 static_assert(kI4Rows >= 2 && kI4Rows <= 32 && (kI4Rows & (kI4Rows - 1)) == 0, "rows per batch");
 constexpr uint32_t kI4Pass = 4096;
 
-struct I4Batch {
-  u32x4_t c[kI4Rows][2];   // 32 code bytes per row
-  uint32_t s[kI4Rows];     // the lane's scale bits per row
+template <int BITS, int NR> struct QBatch;
+template <int NR> struct QBatch<4, NR> {
+  u32x4_t c[NR][2];   // 32 code bytes per row
+  uint32_t s[NR];     // the lane's scale bits per row
+};
+template <int NR> struct QBatch<5, NR> {
+  u32x2_t c[NR][5];   // 40 code bytes per row (8-byte aligned)
+  uint32_t s[NR];
 };
 
-// x of the lane for one pass: pair registers p[d][k] = (x[64 l + 8 d + k],
-// x[64 l + 8 d + k + 4]) for code dword d and nibble pair k, and base =
-// sum of 136 x over the lane's columns, formed by the same v_dot2 sequence as
-// a row's sum, so that it cancels exactly: all-zero codes give exactly 0 and
-// a basis vector x = e_j gives s q exactly (columns past `in` read as zero).
-struct I4X {
+// x of the lane for one pass, and base = the sum of (offset) x over the
+// lane's columns formed by the same v_dot2 sequence as a row's sum, so that
+// it cancels exactly: all-zero codes give exactly 0 and a basis vector
+// x = e_j gives s q exactly (columns past `in` read as zero).
+//   INT4: p[d][k] = (x[64 l + 8 d + k], x[64 l + 8 d + k + 4]) for code dword
+//         d and nibble pair k; offset 136.
+//   INT5: p[m] = (x[64 l + 2 m], x[64 l + 2 m + 1]); offset 144.
+template <int BITS> struct QX;
+template <> struct QX<4> {
   uint32_t p[8][4];
+  float base;
+};
+template <> struct QX<5> {
+  uint32_t p[32];
   float base;
 };
 
 constexpr uint32_t kBf16Pair136 = 0x43084308u;   // bf16 (136, 136)
+constexpr uint32_t kBf16Pair144 = 0x43104310u;   // bf16 (144, 144)
 
-__device__ __forceinline__ void load_x(__amdgpu_buffer_rsrc_t rx, uint32_t col, I4X& X) {
-  uint32_t w[32];   // bf16 pairs (x[2m], x[2m + 1]) of the lane's 64 columns
+__device__ __forceinline__ void load_x_pairs(__amdgpu_buffer_rsrc_t rx, uint32_t col, uint32_t (&w)[32]) {
+  // bf16 pairs (x[2m], x[2m + 1]) of the lane's 64 columns
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rx, 2 * col + 16 * k, 0, 0);
     w[4 * k] = v[0]; w[4 * k + 1] = v[1]; w[4 * k + 2] = v[2]; w[4 * k + 3] = v[3];
   }
+}
+
+__device__ __forceinline__ void load_x(__amdgpu_buffer_rsrc_t rx, uint32_t col, QX<4>& X) {
+  uint32_t w[32];
+  load_x_pairs(rx, col, w);
   float base = 0.f;
 #pragma unroll
   for (int d = 0; d < 8; ++d) {
@@ -66,40 +87,91 @@ __device__ __forceinline__ void load_x(__amdgpu_buffer_rsrc_t rx, uint32_t col, 
   X.base = base;
 }
 
-__device__ __forceinline__ I4Batch load_rows(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs, uint32_t row0,
-                                             uint32_t V, uint32_t in, uint32_t pass, uint32_t lane) {
-  I4Batch B;
-  const uint32_t col = pass * kI4Pass + 64 * lane, G = in / 128;
+__device__ __forceinline__ void load_x(__amdgpu_buffer_rsrc_t rx, uint32_t col, QX<5>& X) {
+  load_x_pairs(rx, col, X.p);
+  float base = 0.f;
 #pragma unroll
-  for (int r = 0; r < kI4Rows; ++r) {
-    const uint32_t row = min(row0 + r, V - 1);
-    // columns past `in` (a partial last pass): out of range, zeros
-    const uint32_t off = col < in ? row * (in / 2) + col / 2 : 0x7FFFFFF0u;
+  for (int m = 0; m < 32; ++m)
+    base = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, kBf16Pair144),
+                                           __builtin_bit_cast(bf16x2_t, X.p[m]), base, false);
+  X.base = base;
+}
+
+// Row r of a batch: the lane's 64 columns from `col` of matrix row `row`;
+// col >= in (past a partial last pass, or an idle tail lane) sets bit 31 of
+// the offsets (the matrix is under 2^31 bytes), so the loads read out of
+// range, zeros, which meet x = 0 there.  (A select between two offsets
+// here becomes a branch around every load.)
+template <int BITS, int NR>
+__device__ __forceinline__ void load_row(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs, QBatch<BITS, NR>& B,
+                                         int r, uint32_t row, uint32_t col, uint32_t in) {
+  const uint32_t oob = (uint32_t)(col >= in) << 31;
+  const uint32_t off = (row * (in * BITS / 8) + col * BITS / 8) | oob;
+  if constexpr (BITS == 4) {
     B.c[r][0] = __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, kStream);   // read once: streaming policy
     B.c[r][1] = __builtin_amdgcn_raw_buffer_load_b128(rc, off + 16, 0, kStream);
-    B.s[r] = __builtin_amdgcn_raw_buffer_load_b16(rs, col < in ? 2 * (row * G + col / 128) : 0x7FFFFFF0u, 0, 0);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 5; ++k)
+      B.c[r][k] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rc, off + 8 * k, 0, kStream));
   }
+  B.s[r] = __builtin_amdgcn_raw_buffer_load_b16(rs, (2 * (row * (in / 128) + col / 128)) | oob, 0, 0);
+}
+
+// kI4Rows rows from row0 at one pass's columns, and with a tail (NR =
+// kI4Rows + 1) one more row piece: row row0 + trow at column tcol.
+template <int BITS, int NR>
+__device__ __forceinline__ QBatch<BITS, NR> load_rows(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs,
+                                                      uint32_t row0, uint32_t V, uint32_t in, uint32_t col,
+                                                      uint32_t trow, uint32_t tcol) {
+  QBatch<BITS, NR> B;
+#pragma unroll
+  for (int r = 0; r < kI4Rows; ++r) load_row(rc, rs, B, r, min(row0 + r, V - 1), col, in);
+  if constexpr (NR > kI4Rows) load_row(rc, rs, B, kI4Rows, min(row0 + trow, V - 1), tcol, in);
   return B;
 }
 
-// The lane's contribution to each row: s * (sum of (136 + q) x - sum of 136 x)
-__device__ __forceinline__ void dot_rows(const I4Batch& B, const I4X& X, float (&acc)[kI4Rows]) {
+// Row r's share of the lane: s * (sum of (136 + q) x - sum of 136 x)
+template <int NR>
+__device__ __forceinline__ float dot_row(const QBatch<4, NR>& B, int r, const QX<4>& X) {
+  float a = 0.f;
 #pragma unroll
-  for (int r = 0; r < kI4Rows; ++r) {
-    float a = 0.f;
+  for (int d = 0; d < 8; ++d) {
+    const uint32_t w = B.c[r][d >> 2][d & 3] ^ 0x88888888u;   // offset binary: q + 8
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      const uint32_t w = B.c[r][d >> 2][d & 3] ^ 0x88888888u;   // offset binary: q + 8
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t pr = ((w >> (4 * k)) & 0x000F000Fu) | 0x43004300u;   // (136 + q_k, 136 + q_{k+4})
-        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pr), __builtin_bit_cast(bf16x2_t, X.p[d][k]),
-                                           a, false);
-      }
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t pr = ((w >> (4 * k)) & 0x000F000Fu) | 0x43004300u;   // (136 + q_k, 136 + q_{k+4})
+      a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pr), __builtin_bit_cast(bf16x2_t, X.p[d][k]),
+                                         a, false);
     }
-    const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)B.s[r]);
-    acc[r] += sc * (a - X.base);
   }
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)B.s[r]) * (a - X.base);
+}
+
+// INT5: s * (sum of (144 + q) x - sum of 144 x).  Pair m is the 10-bit field
+// at window bit 10 m (codes of columns 2 m, 2 m + 1, two's complement): a
+// shift-or spreads it to bits 0..4 and 16..20, and one three-input bitwise op
+// keeps those bits, flips each code's sign bit (q + 16, offset binary) and
+// sets the exponent, giving the bf16 pair 0x4300 | (q + 16) = 144 + q.
+template <int NR>
+__device__ __forceinline__ float dot_row(const QBatch<5, NR>& B, int r, const QX<5>& X) {
+  uint32_t w[10];
+#pragma unroll
+  for (int k = 0; k < 5; ++k) {
+    w[2 * k] = B.c[r][k][0];
+    w[2 * k + 1] = B.c[r][k][1];
+  }
+  float a = 0.f;
+#pragma unroll
+  for (int m = 0; m < 32; ++m) {
+    const int d = (10 * m) >> 5, o = (10 * m) & 31;
+    const uint32_t f = (o <= 22 ? (w[d] >> o) : __builtin_amdgcn_alignbit(w[d < 9 ? d + 1 : 9], w[d], o)) & 0x3FFu;
+    // (S0 & S1) ^ S2: truth table 0x6A over (S0, S1, S2) = bit index 4 S0 + 2 S1 + S2
+    const uint32_t pr = __builtin_amdgcn_bitop3_b32((f << 11) | f, 0x001F001Fu, 0x43104310u, 0x6A);
+    a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pr), __builtin_bit_cast(bf16x2_t, X.p[m]), a,
+                                       false);
+  }
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)B.s[r]) * (a - X.base);
 }
 
 // Sum of acc[r] over the wavefront's 64 lanes by a transposed butterfly:
@@ -135,28 +207,43 @@ __device__ __forceinline__ float reduce_rows(const float (&acc)[kI4Rows], uint32
   return t;
 }
 
-__global__ __launch_bounds__(256) void k_int4_gemv(const uint8_t* __restrict__ W, uint32_t V, uint32_t in,
-                                                   const void* __restrict__ x, float* __restrict__ y) {
+// A wavefront per batch of kI4Rows rows, grid-stride over the batches.
+// Widths up to one pass keep x in registers with two batches in flight;
+// widths up to one pass + 1024 columns (the 27B models' 5120) add a tail:
+// the kI4Rows rows' remaining T = (in - 4096) / 64 lane pieces are spread
+// over the wavefront, lane l taking piece l % T of row l / T, so that one
+// extra load per lane covers all of them (every lane busy when T = 16);
+// wider matrices take one pass after another.
+enum { kPathOne = 0, kPathTail = 1, kPathMulti = 2 };
+
+__host__ __device__ constexpr int qgemv_path(uint32_t in) {
+  return in <= kI4Pass ? kPathOne : in <= kI4Pass + 1024 ? kPathTail : kPathMulti;
+}
+
+template <int BITS, int PATH>
+__device__ __forceinline__ void qgemv(const uint8_t* __restrict__ W, uint32_t V, uint32_t in,
+                                      const void* __restrict__ x, float* __restrict__ y) {
   const uint32_t lane = threadIdx.x & 63;
   const uint32_t wave = blockIdx.x * 4 + (threadIdx.x >> 6), nwaves = gridDim.x * 4;
   const uint32_t batches = (V + kI4Rows - 1) / kI4Rows;
   const uint32_t npass = (in + kI4Pass - 1) / kI4Pass;
-  const uint32_t cbytes = V * (in / 2);
+  const uint32_t cbytes = V * (in * BITS / 8);
   const __amdgpu_buffer_rsrc_t rc = rsrc(W, cbytes);
   const __amdgpu_buffer_rsrc_t rs = rsrc(W + cbytes, V * (in / 128) * 2);
   const __amdgpu_buffer_rsrc_t rx = rsrc(x, 2 * in);
   uint32_t b = wave;
   if (b >= batches) return;
-  I4X X;
+  QX<BITS> X;
   load_x(rx, 64 * lane, X);
-  if (npass == 1) {
-    // one pass: x stays in registers; two batches in flight
-    I4Batch B0 = load_rows(rc, rs, b * kI4Rows, V, in, 0, lane);
+  if constexpr (PATH == kPathOne) {
+    QBatch<BITS, kI4Rows> B0 = load_rows<BITS, kI4Rows>(rc, rs, b * kI4Rows, V, in, 64 * lane, 0, 0);
     for (;;) {
       const uint32_t bn = b + nwaves;
-      const I4Batch B1 = load_rows(rc, rs, min(bn, batches - 1) * kI4Rows, V, in, 0, lane);
-      float acc[kI4Rows] = {};
-      dot_rows(B0, X, acc);
+      const QBatch<BITS, kI4Rows> B1 =
+          load_rows<BITS, kI4Rows>(rc, rs, min(bn, batches - 1) * kI4Rows, V, in, 64 * lane, 0, 0);
+      float acc[kI4Rows];
+#pragma unroll
+      for (int r = 0; r < kI4Rows; ++r) acc[r] = dot_row(B0, r, X);
       const float v = reduce_rows(acc, lane);
       const uint32_t row = b * kI4Rows + reduce_row(lane);
       if ((lane & (64 / kI4Rows - 1)) == 0 && row < V) y[row] = v;
@@ -164,28 +251,67 @@ __global__ __launch_bounds__(256) void k_int4_gemv(const uint8_t* __restrict__ W
       b = bn;
       B0 = B1;
     }
-    return;
-  }
-  for (; b < batches; b += nwaves) {
-    float acc[kI4Rows] = {};
-    for (uint32_t p = 0; p < npass; ++p) {
-      if (p) load_x(rx, p * kI4Pass + 64 * lane, X);
-      dot_rows(load_rows(rc, rs, b * kI4Rows, V, in, p, lane), X, acc);
+  } else if constexpr (PATH == kPathTail) {
+    const uint32_t T = (in - kI4Pass) / 64, trow = lane / T;
+    const uint32_t tcol = trow < kI4Rows ? kI4Pass + 64 * (lane % T) : in;   // idle lanes read zeros
+    QX<BITS> XT;
+    load_x(rx, tcol, XT);
+    constexpr int NR = kI4Rows + 1;
+    QBatch<BITS, NR> B0 = load_rows<BITS, NR>(rc, rs, b * kI4Rows, V, in, 64 * lane, trow, tcol);
+    for (;;) {
+      const uint32_t bn = b + nwaves;
+      const QBatch<BITS, NR> B1 =
+          load_rows<BITS, NR>(rc, rs, min(bn, batches - 1) * kI4Rows, V, in, 64 * lane, trow, tcol);
+      const float t = dot_row(B0, kI4Rows, XT);
+      float acc[kI4Rows];
+#pragma unroll
+      for (int r = 0; r < kI4Rows; ++r) acc[r] = dot_row(B0, r, X) + (trow == (uint32_t)r ? t : 0.f);
+      const float v = reduce_rows(acc, lane);
+      const uint32_t row = b * kI4Rows + reduce_row(lane);
+      if ((lane & (64 / kI4Rows - 1)) == 0 && row < V) y[row] = v;
+      if (bn >= batches) break;
+      b = bn;
+      B0 = B1;
     }
-    const float v = reduce_rows(acc, lane);
-    const uint32_t row = b * kI4Rows + reduce_row(lane);
-    if ((lane & (64 / kI4Rows - 1)) == 0 && row < V) y[row] = v;
+  } else {
+    for (; b < batches; b += nwaves) {
+      float acc[kI4Rows] = {};
+      for (uint32_t p = 0; p < npass; ++p) {
+        // X holds pass 0 only before the wavefront's first batch
+        if (p || b != wave) load_x(rx, p * kI4Pass + 64 * lane, X);
+        const QBatch<BITS, kI4Rows> B =
+            load_rows<BITS, kI4Rows>(rc, rs, b * kI4Rows, V, in, p * kI4Pass + 64 * lane, 0, 0);
+#pragma unroll
+        for (int r = 0; r < kI4Rows; ++r) acc[r] += dot_row(B, r, X);
+      }
+      const float v = reduce_rows(acc, lane);
+      const uint32_t row = b * kI4Rows + reduce_row(lane);
+      if ((lane & (64 / kI4Rows - 1)) == 0 && row < V) y[row] = v;
+    }
   }
+}
+
+// one kernel per code width and path, so that each gets its own registers
+template <int PATH>
+__global__ __launch_bounds__(256) void k_int4_gemv(const uint8_t* __restrict__ W, uint32_t V, uint32_t in,
+                                                   const void* __restrict__ x, float* __restrict__ y) {
+  qgemv<4, PATH>(W, V, in, x, y);
+}
+
+template <int PATH>
+__global__ __launch_bounds__(256) void k_int5_gemv(const uint8_t* __restrict__ W, uint32_t V, uint32_t in,
+                                                   const void* __restrict__ x, float* __restrict__ y) {
+  qgemv<5, PATH>(W, V, in, x, y);
 }
 
 }  // namespace
 
-extern "C" int wal_int4_gemv(const void* W_dev, uint32_t V, uint32_t in, const void* x_dev, int x_dtype,
-                             float* y_dev, void* stream) {
+static int qgemv_launch(int bits, const void* W_dev, uint32_t V, uint32_t in, const void* x_dev, int x_dtype,
+                        float* y_dev, void* stream) {
   if (!W_dev || !x_dev || !y_dev || !V || !in) return WAL_ERR_ARG;
   if (x_dtype != WAL_X_F32 && x_dtype != WAL_X_BF16) return WAL_ERR_ARG;
   if (in % 128) return WAL_ERR_SHAPE;
-  if ((uint64_t)V * in / 2 + (uint64_t)V * (in / 128) * 2 >= (1ull << 32)) return WAL_ERR_SHAPE;
+  if ((uint64_t)V * in * bits / 8 + (uint64_t)V * (in / 128) * 2 >= (1ull << 31)) return WAL_ERR_SHAPE;
   if ((reinterpret_cast<uintptr_t>(W_dev) & 255u) || (reinterpret_cast<uintptr_t>(x_dev) & 15u) ||
       (reinterpret_cast<uintptr_t>(y_dev) & 3u))
     return WAL_ERR_ALIGN;
@@ -195,11 +321,32 @@ extern "C" int wal_int4_gemv(const void* W_dev, uint32_t V, uint32_t in, const v
     return WAL_ERR_DEVICE;
   const uint32_t batches = (V + kI4Rows - 1) / kI4Rows;
   // two workgroups (8 wavefronts) per CU, each wavefront looping over batches
-  // (measured on the 151936 x 4096 head: faster than 1, 1.5, 3 or 4)
+  // (measured on the 151936 x 4096 INT4 head: faster than 1, 1.5, 3 or 4)
   const uint32_t blocks = std::min<uint32_t>((batches + 3) / 4, (uint32_t)cus * 2);
-  hipLaunchKernelGGL(k_int4_gemv, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
-                     static_cast<const uint8_t*>(W_dev), V, in, x_dev, y_dev);
+  const uint8_t* W = static_cast<const uint8_t*>(W_dev);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 g(blocks), t(256);
+  const int path = qgemv_path(in);
+  if (bits == 4) {
+    if (path == kPathOne) hipLaunchKernelGGL(k_int4_gemv<kPathOne>, g, t, 0, s, W, V, in, x_dev, y_dev);
+    else if (path == kPathTail) hipLaunchKernelGGL(k_int4_gemv<kPathTail>, g, t, 0, s, W, V, in, x_dev, y_dev);
+    else hipLaunchKernelGGL(k_int4_gemv<kPathMulti>, g, t, 0, s, W, V, in, x_dev, y_dev);
+  } else {
+    if (path == kPathOne) hipLaunchKernelGGL(k_int5_gemv<kPathOne>, g, t, 0, s, W, V, in, x_dev, y_dev);
+    else if (path == kPathTail) hipLaunchKernelGGL(k_int5_gemv<kPathTail>, g, t, 0, s, W, V, in, x_dev, y_dev);
+    else hipLaunchKernelGGL(k_int5_gemv<kPathMulti>, g, t, 0, s, W, V, in, x_dev, y_dev);
+  }
   return hipGetLastError() == hipSuccess ? WAL_OK : WAL_ERR_DEVICE;
+}
+
+extern "C" int wal_int4_gemv(const void* W_dev, uint32_t V, uint32_t in, const void* x_dev, int x_dtype,
+                             float* y_dev, void* stream) {
+  return qgemv_launch(4, W_dev, V, in, x_dev, x_dtype, y_dev, stream);
+}
+
+extern "C" int wal_int5_gemv(const void* W_dev, uint32_t V, uint32_t in, const void* x_dev, int x_dtype,
+                             float* y_dev, void* stream) {
+  return qgemv_launch(5, W_dev, V, in, x_dev, x_dtype, y_dev, stream);
 }
 
 // ---------------------------------------------------------------------------

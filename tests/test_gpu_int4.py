@@ -47,7 +47,7 @@ def run(wal, blob, V, inp, xbits):
     return y.cpu().numpy().astype(np.float64)
 
 
-@pytest.mark.parametrize("V,inp", [(1, 128), (7, 384), (1000, 4224), (4099, 4096), (300, 12288), (65, 5120)])
+@pytest.mark.parametrize("V,inp", [(1, 128), (7, 384), (1000, 4224), (4099, 4096), (300, 12288), (65, 5120), (9000, 4224)])
 def test_shapes(wal, V, inp):
     q, s = make(V + inp, V, inp)
     blob = wal.wal_int4_pack(q, s)

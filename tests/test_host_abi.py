@@ -512,3 +512,41 @@ def test_int3_pack_matches_oracle_and_rejects():
     assert e(W, 4, 2, 256, ids, 1, out, 1, 260, None) == -6          # bf16 rows of 520 B
     assert e(W, 4, 1 << 20, 1 << 13, ids, 1, out, 0, 1 << 13, None) == -2   # 2^32 bytes
 
+
+def test_int5_pack_matches_oracle_and_rejects():
+    """INT5/g128: the C++ packer writes the oracle's bytes and unpacks them
+    back; bad codes, inexact scales, shapes and short buffers are rejected
+    with nothing written; the product entry checks its arguments first."""
+    from oracle import int5 as I
+    rng = np.random.default_rng(23)
+    for V, inp in [(1, 128), (3, 384), (40, 4224)]:
+        q = rng.integers(-16, 16, size=(V, inp)).astype(np.int8)
+        s = (rng.integers(-2048, 2048, size=(V, inp // 128)) / 256.0).astype(np.float32)
+        b = wal.wal_int5_pack(q, s)
+        assert np.array_equal(b, I.pack(q, s.astype(np.float64)))
+        q2, s2 = wal.wal_int5_unpack(b, V, inp)
+        assert np.array_equal(q2, q) and np.array_equal(s2, s)
+    assert wal.wal_int5_size(248320, 5120) == I.size(248320, 5120)
+    lib = wal._lib
+    buf = np.zeros(I.size(2, 256), np.uint8)
+    q = np.zeros((2, 256), np.int8)
+    s = np.ones((2, 2), np.float32)
+    assert lib.wal_int5_pack(2, 256, q.ctypes.data, s.ctypes.data, buf.ctypes.data, buf.size - 1) == -5
+    assert lib.wal_int5_pack(2, 200, q.ctypes.data, s.ctypes.data, buf.ctypes.data, buf.size) == -2
+    for bad in (16, -17):
+        q[1, 3] = bad
+        assert lib.wal_int5_pack(2, 256, q.ctypes.data, s.ctypes.data, buf.ctypes.data, buf.size) == -3
+    q[1, 3] = 0
+    s[0, 1] = 0.1
+    assert lib.wal_int5_pack(2, 256, q.ctypes.data, s.ctypes.data, buf.ctypes.data, buf.size) == -4
+    assert not buf.any()
+    g = lib.wal_int5_gemv
+    W, x, y = 0x10000, 0x20000, 0x30000
+    assert g(None, 2, 256, x, 1, y, None) == -1
+    assert g(W, 2, 200, x, 1, y, None) == -2
+    assert g(W, 1 << 20, 1 << 12, x, 1, y, None) == -2       # 2.6 GB: past 2^31 bytes
+    assert g(W + 16, 2, 256, x, 1, y, None) == -6
+    assert g(W, 2, 256, x + 2, 1, y, None) == -6
+    assert g(W, 2, 256, x, 0, y, None) == -9                  # fp32 x
+    assert g(W, 2, 256, x, 5, y, None) == -1
+
