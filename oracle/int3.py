@@ -88,3 +88,27 @@ def rows(blob: np.ndarray, V: int, inp: int, ids) -> np.ndarray:
         q, s = unpack(np.concatenate([codes.reshape(-1), sc.reshape(-1)]), len(sel), inp)
         out[ok] = dense(q, s)
     return out
+
+
+def rows_mixed(blob3: np.ndarray, V3: int, blob4: np.ndarray, V4: int, inp: int, row_map, ids) -> np.ndarray:
+    """Embedding rows of a table whose rows are stored either INT3/g128 or
+    INT4/g128 (the WAL-Ternary-27B-RC1 card: most rows INT3, a selected
+    quarter INT4).  Read here as two packed tables, [V3][in] INT3 and [V4][in]
+    INT4, and a row map [V]: vocabulary row v is row m = row_map[v] of the INT3
+    table when m >= 0, else row -1 - m of the INT4 table.  An id outside
+    [0, V), or a map entry outside its table, gives a row of zeros."""
+    from . import int4
+    row_map = np.asarray(row_map, dtype=np.int64)
+    ids = np.asarray(ids, dtype=np.int64)
+    V = len(row_map)
+    out = np.zeros((len(ids), inp))
+    for n, v in enumerate(ids):
+        if not 0 <= v < V:
+            continue
+        m = int(row_map[v])
+        if m >= 0:
+            if m < V3:
+                out[n] = rows(blob3, V3, inp, [m])[0]
+        elif -1 - m < V4:
+            out[n] = int4.rows(blob4, V4, inp, [-1 - m])[0]
+    return out

@@ -705,3 +705,40 @@ def test_int5_columns_roundtrip_and_rejections():
     with pytest.raises(ValueError):
         I.pack(np.zeros((1, 200), dtype=np.int64), np.ones((1, 1)))
 
+
+def test_mixed_embedding_rows():
+    """The RC1 mixed table: a map of all INT3 rows (or all INT4 rows) gives
+    the pinned single-format lookups; a mixed map gives, row by row, s * q of
+    the table the map names, in exact rationals; ids or map entries out of
+    range give zero rows."""
+    from oracle import int3 as I3
+    from oracle import int4 as I4
+    rng = np.random.default_rng(24)
+    V, inp = 12, 256
+    q3 = rng.integers(-4, 4, size=(V, inp))
+    s3 = rng.integers(-64, 64, size=(V, 2)) / 8.0
+    q4 = rng.integers(-8, 8, size=(V, inp))
+    s4 = rng.integers(-64, 64, size=(V, 2)) / 16.0
+    b3, b4 = I3.pack(q3, s3), I4.pack(q4, s4)
+    ids = np.array([0, 11, 5, 5, -1, 12, 3])
+    assert np.array_equal(I3.rows_mixed(b3, V, b4, V, inp, np.arange(V), ids), I3.rows(b3, V, inp, ids))
+    assert np.array_equal(I3.rows_mixed(b3, V, b4, V, inp, -1 - np.arange(V), ids), I4.rows(b4, V, inp, ids))
+    # 8 INT3 rows and 4 INT4 rows, interleaved; two map entries past their tables
+    row_map = np.array([0, -1, 1, 2, -2, 3, 4, -3, 5, 6, -4, 7])
+    row_map_bad = row_map.copy()
+    row_map_bad[2], row_map_bad[4] = 8, -5        # INT3 table of 8 rows, INT4 of 4
+    t3, t4 = I3.pack(q3[:8], s3[:8]), I4.pack(q4[:4], s4[:4])
+    R = I3.rows_mixed(t3, 8, t4, 4, inp, row_map, np.arange(V))
+    Rb = I3.rows_mixed(t3, 8, t4, 4, inp, row_map_bad, np.arange(V))
+    for v in range(V):
+        m = row_map[v]
+        if m >= 0:
+            exact = [Fraction(float(s3[m, j // 128])) * int(q3[m, j]) for j in range(inp)]
+        else:
+            exact = [Fraction(float(s4[-1 - m, j // 128])) * int(q4[-1 - m, j]) for j in range(inp)]
+        assert [Fraction(float(t)) for t in R[v]] == exact
+        if v in (2, 4):
+            assert not Rb[v].any()
+        else:
+            assert np.array_equal(Rb[v], R[v])
+
