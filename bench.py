@@ -27,7 +27,8 @@ with its dependencies (q|k|v, o, gate|up, down per layer, one grouped product
 each, in order), eagerly and as a HIP graph replay; ``--workload lmhead`` the
 151936 x 4096 INT4/g128 LM head through wal_int4_gemv, the 248320 x 5120
 INT5/g128 head through wal_int5_gemv, then the lookup of 1
-and 2048 tokens in INT3 and INT4 embeddings of that size (wal_embed_rows).  Each call reads one of about
+and 2048 tokens in INT3 and INT4 embeddings of that size (wal_embed_rows) and
+in a 248320 x 5120 table of INT3 and INT4 rows (wal_embed_rows_mixed).  Each call reads one of about
 1 GB of distinct packed copies in turn, so the 256 MB Infinity Cache cannot
 serve the weights; x stays fixed.  For context the line also carries the
 rate of torch's own reduction (torch.sum over 2 GiB) on the same GPU; it is
@@ -458,6 +459,30 @@ def run_lmhead(args):
             emb[f"int{bits}_n{n}"] = {"us_per_call": round(eus, 2), "bytes": moved,
                                       "GB/s": round(moved / (eus * 1e-6) / 1e9, 1)}
         del E
+    # the RC1 card's mixed table, 27B-shaped: 248320 x 5120, a quarter of
+    # the rows INT4 and the rest INT3, one row map
+    V, inp = 248320, 5120
+    is4 = np.zeros(V, bool)
+    is4[rng.choice(V, V // 4, replace=False)] = True
+    V4 = int(is4.sum())
+    V3 = V - V4
+    sm = (np.abs(rng.standard_normal((V, inp // 128))) / 64).astype(np.float16).astype(np.float32)
+    q3 = rng.integers(-4, 4, size=(V3, inp), dtype=np.int8)
+    E3 = torch.from_numpy(wal.wal_int3_pack(q3, sm[:V3])).to(dev)
+    del q3
+    q4 = rng.integers(-8, 8, size=(V4, inp), dtype=np.int8)
+    E4 = torch.from_numpy(wal.wal_int4_pack(q4, sm[V3:])).to(dev)
+    del q4
+    row_map = np.empty(V, np.int64)
+    row_map[~is4] = rng.permutation(V3)
+    row_map[is4] = -1 - rng.permutation(V4)
+    M = torch.from_numpy(row_map.astype(np.int32)).to(dev)
+    for n in (1, 2048):
+        ids = torch.from_numpy(np.random.default_rng(n).integers(0, V, n).astype(np.int32)).to(dev)
+        out = torch.empty((n, inp), dtype=torch.bfloat16, device=dev)
+        eus = time_calls(torch, lambda i: wal.wal_embed_rows_mixed(E3, V3, E4, V4, inp, M, ids, out), calls, 0.1)
+        emb[f"mixed27b_n{n}"] = {"us_per_call": round(eus, 2)}
+    del E3, E4
     res["embedding_bf16_out"] = emb
     print(json.dumps(res), flush=True)
 

@@ -347,6 +347,25 @@ int wal_int3_unpack(uint32_t V, uint32_t in, const void* src, size_t src_bytes, 
 int wal_embed_rows(const void* W_dev, int bits, uint32_t V, uint32_t in, const int32_t* ids_dev, uint32_t n,
                    void* out_dev, int out_dtype, uint32_t ldo, void* stream);
 
+/* wal_embed_rows_mixed: the embedding of the WAL-Ternary-27B-RC1 card
+ * (section "Representation": three quarters of the rows INT3, a selected
+ * quarter INT4).  This repository's reading: an INT3/g128 table [V3][in], an
+ * INT4/g128 table [V4][in] (layouts above) and a row map [V]; vocabulary row
+ * v is row m = map[v] of the INT3 table when m >= 0, else row -1 - m of the
+ * INT4 table.  out[i][:] = vocabulary row ids[i], decoded as wal_embed_rows
+ * does.
+ *   W3_dev, W4_dev  the two tables in device memory, 256-byte aligned
+ *   map_dev         [V] int32 (device); an entry outside its table gives a
+ *                   row of zeros
+ *   ids_dev         [n] int32 (device); an id outside [0, V) gives a row of
+ *                   zeros
+ *   out_dev, ldo, out_dtype  as for wal_embed_rows
+ *   Each table must be under 2^32 bytes (else WAL_ERR_SHAPE).
+ *   Errors: ARG, SHAPE, ALIGN, DEVICE. */
+int wal_embed_rows_mixed(const void* W3_dev, uint32_t V3, const void* W4_dev, uint32_t V4, uint32_t in,
+                         const int32_t* map_dev, uint32_t V, const int32_t* ids_dev, uint32_t n, void* out_dev,
+                         int out_dtype, uint32_t ldo, void* stream);
+
 /* INT5/g128 packed matrices: the LM head of the WAL-Ternary-27B-RC1 card
  * (section "Representation" lists it as packed INT5; nothing more is
  * printed).  This repository's reading, in line with the other cards'

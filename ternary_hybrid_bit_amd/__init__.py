@@ -101,6 +101,7 @@ _sig = {
     "wal_int3_pack": (_I, [_U32, _U32, _P, _P, _P, _SZ]),
     "wal_int3_unpack": (_I, [_U32, _U32, _P, _SZ, _P, _P]),
     "wal_embed_rows": (_I, [_P, _I, _U32, _U32, _P, _U32, _P, _I, _U32, _P]),
+    "wal_embed_rows_mixed": (_I, [_P, _U32, _P, _U32, _U32, _P, _U32, _P, _U32, _P, _I, _U32, _P]),
     "wal_int5_size": (_I, [_U32, _U32, ctypes.POINTER(_SZ)]),
     "wal_int5_pack": (_I, [_U32, _U32, _P, _P, _P, _SZ]),
     "wal_int5_unpack": (_I, [_U32, _U32, _P, _SZ, _P, _P]),
@@ -439,5 +440,17 @@ def wal_embed_rows(W, bits: int, V: int, inp: int, ids, out, stream=None):
     odt = WAL_X_BF16 if out.dtype == torch.bfloat16 else WAL_X_F32
     _check(_lib.wal_embed_rows(_ptr(W), bits, V, inp, _ptr(ids), ids.numel(), _ptr(out), odt, out.stride(0),
                                _stream(stream)), "wal_embed_rows")
+    return out
+
+
+def wal_embed_rows_mixed(W3, V3: int, W4, V4: int, inp: int, row_map, ids, out, stream=None):
+    """out[i] = vocabulary row ids[i] of a mixed table: row_map[v] >= 0 names
+    a row of the INT3 table W3, a negative entry m row -1 - m of the INT4
+    table W4 (device bytes); row_map and ids int32, out [n][ldo] device."""
+    import torch
+    odt = WAL_X_BF16 if out.dtype == torch.bfloat16 else WAL_X_F32
+    _check(_lib.wal_embed_rows_mixed(_ptr(W3), V3, _ptr(W4), V4, inp, _ptr(row_map), row_map.numel(), _ptr(ids),
+                                     ids.numel(), _ptr(out), odt, out.stride(0), _stream(stream)),
+           "wal_embed_rows_mixed")
     return out
 

@@ -351,26 +351,24 @@ extern "C" int wal_int5_gemv(const void* W_dev, uint32_t V, uint32_t in, const v
 
 // ---------------------------------------------------------------------------
 // Embedding rows: out[i][:] = row ids[i] of an INT3 (3-bit stream) or INT4
-// matrix (layouts in include/wal.h).  Block (i, c) decodes columns
-// 2048 c .. 2048 c + 2047 of token i, 16 consecutive values per thread: INT3
-// takes 6 bytes at 6 (j0 / 16) of the row's stream (three 16-bit loads),
-// INT4 8 bytes; one fp16 scale per thread (16 values lie inside one group).
+// matrix (layouts in include/wal.h), or of a mixed table (INT3 and INT4 rows
+// and a row map).  Block (i, c) decodes columns 2048 c .. 2048 c + 2047 of
+// token i, 16 consecutive values per thread: INT3 takes 6 bytes at
+// 6 (j0 / 16) of the row's stream (three 16-bit loads), INT4 8 bytes; one
+// fp16 scale per thread (16 values lie inside one group).
 namespace {
 
-template <int BITS, int OT>
-__global__ __launch_bounds__(128) void k_embed_rows(const uint8_t* __restrict__ W, uint32_t V, uint32_t in,
-                                                    const int32_t* __restrict__ ids, void* __restrict__ out,
-                                                    uint32_t ldo) {
-  const uint32_t i = blockIdx.x, j0 = blockIdx.y * 2048 + 16 * threadIdx.x;
-  if (j0 >= in) return;
-  const uint32_t row = (uint32_t)ids[i];   // a negative index wraps past V
-  const bool ok = row < V;
-  const uint32_t r = ok ? row : 0, G = in / 128;
+// Values j0 .. j0 + 15 of row `row` of a [V][in] table (row < V); each
+// s * q is exact in fp32.
+template <int BITS>
+__device__ __forceinline__ void decode16(const uint8_t* __restrict__ W, uint32_t V, uint32_t in, uint32_t row,
+                                         uint32_t j0, float (&e)[16]) {
+  const uint32_t G = in / 128;
   const uint32_t cbytes = V * (in * BITS / 8);
   const __amdgpu_buffer_rsrc_t rc = rsrc(W, cbytes);
   const __amdgpu_buffer_rsrc_t rs = rsrc(W + cbytes, V * G * 2);
-  const uint32_t base = r * (in * BITS / 8) + j0 * BITS / 8;
-  uint64_t v = 0;
+  const uint32_t base = row * (in * BITS / 8) + j0 * BITS / 8;
+  uint64_t v;
   if constexpr (BITS == 3) {
     v = (uint64_t)__builtin_amdgcn_raw_buffer_load_b16(rc, base, 0, 0) |
         ((uint64_t)__builtin_amdgcn_raw_buffer_load_b16(rc, base + 2, 0, 0) << 16) |
@@ -379,17 +377,19 @@ __global__ __launch_bounds__(128) void k_embed_rows(const uint8_t* __restrict__ 
     const u32x2_t w = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rc, base, 0, 0));
     v = (uint64_t)w[0] | ((uint64_t)w[1] << 32);
   }
-  if (!ok) v = 0;   // +0 everywhere in a row past the vocabulary
-  const float sc = ok ? (float)__builtin_bit_cast(_Float16, (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(
-                            rs, 2 * (r * G + j0 / 128), 0, 0))
-                      : 0.f;
-  float e[16];
+  const float sc =
+      (float)__builtin_bit_cast(_Float16, (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rs, 2 * (row * G + j0 / 128), 0, 0));
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
     const int code = (int)((v >> (BITS * k)) & ((1u << BITS) - 1u));
     const int q = code >= (1 << (BITS - 1)) ? code - (1 << BITS) : code;
     e[k] = sc * (float)q;   // exact: at most 3 or 4 bits times an fp16 scale
   }
+}
+
+template <int OT>
+__device__ __forceinline__ void store16(void* __restrict__ out, uint32_t ldo, uint32_t i, uint32_t j0,
+                                        const float (&e)[16]) {
   if constexpr (OT == WAL_X_F32) {
     float4* dst = reinterpret_cast<float4*>(static_cast<float*>(out) + (size_t)i * ldo + j0);
 #pragma unroll
@@ -407,21 +407,61 @@ __global__ __launch_bounds__(128) void k_embed_rows(const uint8_t* __restrict__ 
   }
 }
 
+template <int BITS, int OT>
+__global__ __launch_bounds__(128) void k_embed_rows(const uint8_t* __restrict__ W, uint32_t V, uint32_t in,
+                                                    const int32_t* __restrict__ ids, void* __restrict__ out,
+                                                    uint32_t ldo) {
+  const uint32_t i = blockIdx.x, j0 = blockIdx.y * 2048 + 16 * threadIdx.x;
+  if (j0 >= in) return;
+  const uint32_t row = (uint32_t)ids[i];   // a negative index wraps past V
+  float e[16] = {};                        // +0 everywhere in a row past the vocabulary
+  if (row < V) decode16<BITS>(W, V, in, row, j0, e);
+  store16<OT>(out, ldo, i, j0, e);
+}
+
+// Mixed table: vocabulary row v is row m = map[v] of the INT3 table (m >= 0)
+// or row -1 - m of the INT4 table; the choice is uniform over a block.
+template <int OT>
+__global__ __launch_bounds__(128) void k_embed_mixed(const uint8_t* __restrict__ W3, uint32_t V3,
+                                                     const uint8_t* __restrict__ W4, uint32_t V4, uint32_t in,
+                                                     const int32_t* __restrict__ map, uint32_t V,
+                                                     const int32_t* __restrict__ ids, void* __restrict__ out,
+                                                     uint32_t ldo) {
+  const uint32_t i = blockIdx.x, j0 = blockIdx.y * 2048 + 16 * threadIdx.x;
+  if (j0 >= in) return;
+  const uint32_t v = (uint32_t)ids[i];
+  float e[16] = {};
+  if (v < V) {
+    const int32_t m = map[v];
+    if (m >= 0) {
+      if ((uint32_t)m < V3) decode16<3>(W3, V3, in, (uint32_t)m, j0, e);
+    } else if ((uint32_t)(-1 - m) < V4) {
+      decode16<4>(W4, V4, in, (uint32_t)(-1 - m), j0, e);
+    }
+  }
+  store16<OT>(out, ldo, i, j0, e);
+}
+
 }  // namespace
+
+static int embed_check(uint32_t in, uint32_t n, void* out_dev, int out_dtype, uint32_t ldo) {
+  if (out_dtype != WAL_X_F32 && out_dtype != WAL_X_BF16) return WAL_ERR_ARG;
+  if (in % 128) return WAL_ERR_SHAPE;
+  if (ldo < in) return WAL_ERR_ARG;
+  if (n > 65535u * 256u) return WAL_ERR_SHAPE;
+  const size_t oe = out_dtype == WAL_X_BF16 ? 2 : 4;
+  if ((reinterpret_cast<uintptr_t>(out_dev) & 15u) || (ldo * oe) % 16) return WAL_ERR_ALIGN;
+  return WAL_OK;
+}
 
 extern "C" int wal_embed_rows(const void* W_dev, int bits, uint32_t V, uint32_t in, const int32_t* ids_dev, uint32_t n,
                               void* out_dev, int out_dtype, uint32_t ldo, void* stream) {
   if (!W_dev || !ids_dev || !out_dev || !V || !in || !n) return WAL_ERR_ARG;
   if (bits != 3 && bits != 4) return WAL_ERR_ARG;
-  if (out_dtype != WAL_X_F32 && out_dtype != WAL_X_BF16) return WAL_ERR_ARG;
-  if (in % 128) return WAL_ERR_SHAPE;
-  if (ldo < in) return WAL_ERR_ARG;
-  if ((uint64_t)V * in * bits / 8 + (uint64_t)V * (in / 128) * 2 >= (1ull << 32) || n > 65535u * 256u)
-    return WAL_ERR_SHAPE;
-  const size_t oe = out_dtype == WAL_X_BF16 ? 2 : 4;
-  if ((reinterpret_cast<uintptr_t>(W_dev) & 255u) || (reinterpret_cast<uintptr_t>(ids_dev) & 3u) ||
-      (reinterpret_cast<uintptr_t>(out_dev) & 15u) || (ldo * oe) % 16)
-    return WAL_ERR_ALIGN;
+  int st = embed_check(in, n, out_dev, out_dtype, ldo);
+  if (st) return st;
+  if ((uint64_t)V * in * bits / 8 + (uint64_t)V * (in / 128) * 2 >= (1ull << 32)) return WAL_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(W_dev) & 255u) || (reinterpret_cast<uintptr_t>(ids_dev) & 3u)) return WAL_ERR_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid(n, (in + 2047) / 2048), block(128);
   const uint8_t* W = static_cast<const uint8_t*>(W_dev);
@@ -429,5 +469,28 @@ extern "C" int wal_embed_rows(const void* W_dev, int bits, uint32_t V, uint32_t 
   else if (bits == 3) hipLaunchKernelGGL((k_embed_rows<3, WAL_X_BF16>), grid, block, 0, s, W, V, in, ids_dev, out_dev, ldo);
   else if (out_dtype == WAL_X_F32) hipLaunchKernelGGL((k_embed_rows<4, WAL_X_F32>), grid, block, 0, s, W, V, in, ids_dev, out_dev, ldo);
   else hipLaunchKernelGGL((k_embed_rows<4, WAL_X_BF16>), grid, block, 0, s, W, V, in, ids_dev, out_dev, ldo);
+  return hipGetLastError() == hipSuccess ? WAL_OK : WAL_ERR_DEVICE;
+}
+
+extern "C" int wal_embed_rows_mixed(const void* W3_dev, uint32_t V3, const void* W4_dev, uint32_t V4, uint32_t in,
+                                    const int32_t* map_dev, uint32_t V, const int32_t* ids_dev, uint32_t n,
+                                    void* out_dev, int out_dtype, uint32_t ldo, void* stream) {
+  if (!W3_dev || !W4_dev || !map_dev || !ids_dev || !out_dev || !V3 || !V4 || !V || !in || !n) return WAL_ERR_ARG;
+  int st = embed_check(in, n, out_dev, out_dtype, ldo);
+  if (st) return st;
+  if ((uint64_t)V3 * in * 3 / 8 + (uint64_t)V3 * (in / 128) * 2 >= (1ull << 32) ||
+      (uint64_t)V4 * in / 2 + (uint64_t)V4 * (in / 128) * 2 >= (1ull << 32))
+    return WAL_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(W3_dev) & 255u) || (reinterpret_cast<uintptr_t>(W4_dev) & 255u) ||
+      (reinterpret_cast<uintptr_t>(map_dev) & 3u) || (reinterpret_cast<uintptr_t>(ids_dev) & 3u))
+    return WAL_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid(n, (in + 2047) / 2048), block(128);
+  const uint8_t* W3 = static_cast<const uint8_t*>(W3_dev);
+  const uint8_t* W4 = static_cast<const uint8_t*>(W4_dev);
+  if (out_dtype == WAL_X_F32)
+    hipLaunchKernelGGL(k_embed_mixed<WAL_X_F32>, grid, block, 0, s, W3, V3, W4, V4, in, map_dev, V, ids_dev, out_dev, ldo);
+  else
+    hipLaunchKernelGGL(k_embed_mixed<WAL_X_BF16>, grid, block, 0, s, W3, V3, W4, V4, in, map_dev, V, ids_dev, out_dev, ldo);
   return hipGetLastError() == hipSuccess ? WAL_OK : WAL_ERR_DEVICE;
 }

@@ -550,3 +550,19 @@ def test_int5_pack_matches_oracle_and_rejects():
     assert g(W, 2, 256, x, 0, y, None) == -9                  # fp32 x
     assert g(W, 2, 256, x, 5, y, None) == -1
 
+
+def test_embed_rows_mixed_checks():
+    """The mixed-table lookup checks its arguments before any launch."""
+    e = wal._lib.wal_embed_rows_mixed
+    W3, W4, m, ids, out = 0x10000, 0x20000, 0x30000, 0x40000, 0x50000
+    assert e(None, 3, W4, 1, 256, m, 4, ids, 1, out, 0, 256, None) == -1
+    assert e(W3, 0, W4, 1, 256, m, 4, ids, 1, out, 0, 256, None) == -1      # empty INT3 table
+    assert e(W3, 3, W4, 1, 200, m, 4, ids, 1, out, 0, 256, None) == -2      # in % 128
+    assert e(W3, 3, W4, 1, 256, m, 4, ids, 1, out, 0, 200, None) == -1      # ldo < in
+    assert e(W3, 3, W4, 1, 256, m, 4, ids, 1, out, 2, 256, None) == -1      # out dtype
+    assert e(W3 + 16, 3, W4, 1, 256, m, 4, ids, 1, out, 0, 256, None) == -6
+    assert e(W3, 3, W4 + 16, 1, 256, m, 4, ids, 1, out, 0, 256, None) == -6
+    assert e(W3, 3, W4, 1, 256, m + 2, 4, ids, 1, out, 0, 256, None) == -6
+    assert e(W3, 3, W4, 1, 256, m, 4, ids, 1, out + 8, 0, 256, None) == -6
+    assert e(W3, 3, W4, 1 << 20, 1 << 13, m, 4, ids, 1, out, 0, 1 << 13, None) == -2   # INT4 table of 2^32 bytes
+
