@@ -343,9 +343,13 @@ __device__ __forceinline__ void a_operands(uint64_t q, uint4 (&a)[4]) {
 // once per tile.  k_mfma (small batch) gives a workgroup one kSliceCols-column
 // slice (kSweeps sweeps) and writes partial sums; k_prefill (large batch)
 // gives it every column of a 32-row batch chunk and writes Y.
+// Four tiles per workgroup (measured on the 4096 x 12288 shape, us per call
+// at batch 1 / 8 / 32): 16.2 / 17.0 / 24.4, against 17.9 / 19.1 / 25.8 with
+// eight and 17.6 / 20.0 / 32.6 with two; 512- or 2048-column slices were
+// slower with either.
 constexpr uint32_t kSlots = 4;
 constexpr uint32_t kSweeps = kSliceCols / 128 / kSlots;
-constexpr uint32_t kMfmaTiles = 8;
+constexpr uint32_t kMfmaTiles = 4;
 constexpr uint32_t kMfmaWaves = kMfmaTiles;
 
 // X rows nbase .. nbase + 16 NT - 1 of one sweep of SL groups in LDS, in

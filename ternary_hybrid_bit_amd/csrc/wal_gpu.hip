@@ -520,7 +520,7 @@ constexpr int kRB = 4;   // rows per batch of the 2-bit streaming kernels
 // Batch from which WAL_GEMM_AUTO takes the MFMA kernel (measured on MI355X
 // on the 4096 x 12288 shape); below it the batched GEMV, and at batch 1 the
 // single-product path, which is faster still.
-constexpr uint32_t kGemmCrossover = 3;
+constexpr uint32_t kGemmCrossover = 2;
 constexpr uint32_t kClasses = 16;   // kernel classes (see class_of)
 
 // Kernel class of a matrix: 8 * trit_fmt + 4 * scale_fmt + index of k in {0, 2, 4, 8}.
