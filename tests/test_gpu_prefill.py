@@ -153,6 +153,23 @@ def test_zero_case_and_determinism(wal):
         assert np.array_equal(Y1, Y2)
 
 
+def test_max_batch(wal):
+    """The largest batch the entry point takes (WAL_MAX_PREFILL_BATCH rows of
+    X) on a ragged 520 x 4224 matrix: sampled batch rows, every output,
+    against the oracle, and Y finite throughout."""
+    B = wal.WAL_MAX_PREFILL_BATCH
+    m = synth.make_matrix(324, 0, 520, 4224, k=8, n_paths=2, rank=16)
+    blob, info = wal.pack_matrix(m)
+    x, bits = synth.make_x(324, 0, 4224, B)
+    print(f"prefill 520x4224 B={B} splits={split_count(520, 4224, B)}", flush=True)
+    Y = run_prefill(wal, to_dev(blob), info, bits)
+    assert np.isfinite(Y).all()
+    rows = sorted({0, 63, 64, 8191, 8192, B - 65, B - 1})
+    ref = D.gemm(F.pack(F.from_synth(m)), x[rows])
+    for i, n in enumerate(rows):
+        assert D.rel_l2(Y[n], ref[i]) <= BF16_TOL, n
+
+
 def test_unsupported_inputs(wal):
     m = synth.make_matrix(323, 0, 64, 5120, k=4, n_paths=1, rank=16, trit_fmt=synth.TRIT_BASE3)
     blob, info = wal.pack_matrix(m)
