@@ -311,7 +311,7 @@ int wal_gemv_grouped_phases(const wal_grouped_info* ginfo, const void* plan_dev,
  * wal_int4_gemv: y[v] = sum_j W[v][j] x[j] on the GPU, one matrix, batch 1.
  *   W_dev  the layout in device memory, 256-byte aligned
  *   x_dev  [in] bf16, 16-byte aligned (fp32 x: WAL_ERR_UNSUPPORTED)
- *   y_dev  [V] fp32, overwritten
+ *   y_dev  [V] fp32, overwritten; must not overlap W or x (WAL_ERR_ARG)
  *   The packed matrix must be under 2^31 bytes (else WAL_ERR_SHAPE).
  *   Errors: ARG, SHAPE, ALIGN, UNSUPPORTED, DEVICE. */
 int wal_int4_size(uint32_t V, uint32_t in, size_t* bytes);
@@ -339,7 +339,8 @@ int wal_int4_gemv(const void* W_dev, uint32_t V, uint32_t in, const void* x_dev,
  *            row of zeros
  *   out_dev  [n][ldo] fp32 or bf16 (out_dtype), 16-byte aligned rows, ldo >= in;
  *            columns past `in` untouched
- *   The packed matrix must be under 2^32 bytes (else WAL_ERR_SHAPE).
+ *   The packed matrix must be under 2^32 bytes and n at most 2^31 - 1 (else
+ *   WAL_ERR_SHAPE); out must not overlap W or ids (WAL_ERR_ARG).
  *   Errors: ARG, SHAPE, ALIGN, DEVICE. */
 int wal_int3_size(uint32_t V, uint32_t in, size_t* bytes);
 int wal_int3_pack(uint32_t V, uint32_t in, const int8_t* q, const float* s, void* dst, size_t dst_bytes);
@@ -360,7 +361,9 @@ int wal_embed_rows(const void* W_dev, int bits, uint32_t V, uint32_t in, const i
  *   ids_dev         [n] int32 (device); an id outside [0, V) gives a row of
  *                   zeros
  *   out_dev, ldo, out_dtype  as for wal_embed_rows
- *   Each table must be under 2^32 bytes (else WAL_ERR_SHAPE).
+ *   Each table must be under 2^32 bytes and n at most 2^31 - 1 (else
+ *   WAL_ERR_SHAPE); out must not overlap the tables, the map or ids
+ *   (WAL_ERR_ARG).
  *   Errors: ARG, SHAPE, ALIGN, DEVICE. */
 int wal_embed_rows_mixed(const void* W3_dev, uint32_t V3, const void* W4_dev, uint32_t V4, uint32_t in,
                          const int32_t* map_dev, uint32_t V, const int32_t* ids_dev, uint32_t n, void* out_dev,

@@ -437,6 +437,8 @@ def wal_embed_rows(W, bits: int, V: int, inp: int, ids, out, stream=None):
     """out[i] = row ids[i] of an INT3 (bits 3) or INT4 (bits 4) matrix W (device
     bytes); ids int32 [n] and out [n][ldo] (fp32 or bf16) device tensors."""
     import torch
+    if ids.dtype != torch.int32 or out.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("ids must be int32 and out float32 or bfloat16")
     odt = WAL_X_BF16 if out.dtype == torch.bfloat16 else WAL_X_F32
     _check(_lib.wal_embed_rows(_ptr(W), bits, V, inp, _ptr(ids), ids.numel(), _ptr(out), odt, out.stride(0),
                                _stream(stream)), "wal_embed_rows")
@@ -448,6 +450,8 @@ def wal_embed_rows_mixed(W3, V3: int, W4, V4: int, inp: int, row_map, ids, out, 
     a row of the INT3 table W3, a negative entry m row -1 - m of the INT4
     table W4 (device bytes); row_map and ids int32, out [n][ldo] device."""
     import torch
+    if ids.dtype != torch.int32 or row_map.dtype != torch.int32 or out.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("ids and row_map must be int32 and out float32 or bfloat16")
     odt = WAL_X_BF16 if out.dtype == torch.bfloat16 else WAL_X_F32
     _check(_lib.wal_embed_rows_mixed(_ptr(W3), V3, _ptr(W4), V4, inp, _ptr(row_map), row_map.numel(), _ptr(ids),
                                      ids.numel(), _ptr(out), odt, out.stride(0), _stream(stream)),

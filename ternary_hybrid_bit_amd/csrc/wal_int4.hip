@@ -25,6 +25,11 @@
 
 namespace {
 
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
 constexpr int kI4Rows = 4;        // rows per batch of a wavefront (a power of two, at most 32)
 static_assert(kI4Rows >= 2 && kI4Rows <= 32 && (kI4Rows & (kI4Rows - 1)) == 0, "rows per batch");
 constexpr uint32_t kI4Pass = 4096;
@@ -316,6 +321,9 @@ static int qgemv_launch(int bits, const void* W_dev, uint32_t V, uint32_t in, co
       (reinterpret_cast<uintptr_t>(y_dev) & 3u))
     return WAL_ERR_ALIGN;
   if (x_dtype != WAL_X_BF16) return WAL_ERR_UNSUPPORTED;
+  const size_t wbytes = (size_t)V * in * bits / 8 + (size_t)V * (in / 128) * 2;
+  if (overlaps(y_dev, (size_t)V * 4, W_dev, wbytes) || overlaps(y_dev, (size_t)V * 4, x_dev, (size_t)in * 2))
+    return WAL_ERR_ARG;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return WAL_ERR_DEVICE;
@@ -448,7 +456,7 @@ static int embed_check(uint32_t in, uint32_t n, void* out_dev, int out_dtype, ui
   if (out_dtype != WAL_X_F32 && out_dtype != WAL_X_BF16) return WAL_ERR_ARG;
   if (in % 128) return WAL_ERR_SHAPE;
   if (ldo < in) return WAL_ERR_ARG;
-  if (n > 65535u * 256u) return WAL_ERR_SHAPE;
+  if (n > 0x7FFFFFFFu) return WAL_ERR_SHAPE;   // one workgroup row per token: the grid's x limit
   const size_t oe = out_dtype == WAL_X_BF16 ? 2 : 4;
   if ((reinterpret_cast<uintptr_t>(out_dev) & 15u) || (ldo * oe) % 16) return WAL_ERR_ALIGN;
   return WAL_OK;
@@ -462,6 +470,10 @@ extern "C" int wal_embed_rows(const void* W_dev, int bits, uint32_t V, uint32_t 
   if (st) return st;
   if ((uint64_t)V * in * bits / 8 + (uint64_t)V * (in / 128) * 2 >= (1ull << 32)) return WAL_ERR_SHAPE;
   if ((reinterpret_cast<uintptr_t>(W_dev) & 255u) || (reinterpret_cast<uintptr_t>(ids_dev) & 3u)) return WAL_ERR_ALIGN;
+  const size_t obytes = ((size_t)(n - 1) * ldo + in) * (out_dtype == WAL_X_BF16 ? 2 : 4);
+  if (overlaps(out_dev, obytes, W_dev, (size_t)V * in * bits / 8 + (size_t)V * (in / 128) * 2) ||
+      overlaps(out_dev, obytes, ids_dev, (size_t)n * 4))
+    return WAL_ERR_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid(n, (in + 2047) / 2048), block(128);
   const uint8_t* W = static_cast<const uint8_t*>(W_dev);
@@ -484,6 +496,11 @@ extern "C" int wal_embed_rows_mixed(const void* W3_dev, uint32_t V3, const void*
   if ((reinterpret_cast<uintptr_t>(W3_dev) & 255u) || (reinterpret_cast<uintptr_t>(W4_dev) & 255u) ||
       (reinterpret_cast<uintptr_t>(map_dev) & 3u) || (reinterpret_cast<uintptr_t>(ids_dev) & 3u))
     return WAL_ERR_ALIGN;
+  const size_t obytes = ((size_t)(n - 1) * ldo + in) * (out_dtype == WAL_X_BF16 ? 2 : 4);
+  if (overlaps(out_dev, obytes, W3_dev, (size_t)V3 * in * 3 / 8 + (size_t)V3 * (in / 128) * 2) ||
+      overlaps(out_dev, obytes, W4_dev, (size_t)V4 * in / 2 + (size_t)V4 * (in / 128) * 2) ||
+      overlaps(out_dev, obytes, map_dev, (size_t)V * 4) || overlaps(out_dev, obytes, ids_dev, (size_t)n * 4))
+    return WAL_ERR_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid(n, (in + 2047) / 2048), block(128);
   const uint8_t* W3 = static_cast<const uint8_t*>(W3_dev);

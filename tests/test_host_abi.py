@@ -566,3 +566,19 @@ def test_embed_rows_mixed_checks():
     assert e(W3, 3, W4, 1, 256, m, 4, ids, 1, out + 8, 0, 256, None) == -6
     assert e(W3, 3, W4, 1 << 20, 1 << 13, m, 4, ids, 1, out, 0, 1 << 13, None) == -2   # INT4 table of 2^32 bytes
 
+
+def test_quantised_outputs_must_not_overlap_inputs():
+    """The INT4/INT5 products and the row lookups reject an output that
+    overlaps an input, before any launch."""
+    W, x = 0x100000, 0x200000
+    for g in (wal._lib.wal_int4_gemv, wal._lib.wal_int5_gemv):
+        assert g(W, 2, 256, x, 1, W + 64, None) == -1          # y inside W
+        assert g(W, 2, 256, x, 1, x + 4, None) == -1           # y inside x
+    e = wal._lib.wal_embed_rows
+    ids = 0x300000
+    assert e(W, 4, 2, 256, ids, 4, W + 256, 0, 256, None) == -1   # out inside W
+    assert e(W, 4, 2, 256, ids, 4, ids - 16, 0, 256, None) == -1  # out over ids
+    em = wal._lib.wal_embed_rows_mixed
+    W4, m = 0x400000, 0x500000
+    assert em(W, 3, W4, 1, 256, m, 4, ids, 1, m - 256, 0, 256, None) == -1   # out over the map
+
