@@ -39,8 +39,12 @@ template <int NR> struct QBatch<4, NR> {
   u32x4_t c[NR][2];   // 32 code bytes per row
   uint32_t s[NR];     // the lane's scale bits per row
 };
+// INT5 codes travel as 16-byte chunks contiguous across the wavefront's
+// lanes (chunk j = lane + 64 k of the batch's NR row pieces of 2560 bytes)
+// and reach their lanes through LDS (stage5).
+template <int NR> constexpr int kI5Chunks = (NR * 160 + 63) / 64;
 template <int NR> struct QBatch<5, NR> {
-  u32x2_t c[NR][5];   // 40 code bytes per row (8-byte aligned)
+  u32x4_t c[kI5Chunks<NR>];
   uint32_t s[NR];
 };
 
@@ -112,13 +116,9 @@ __device__ __forceinline__ void load_row(__amdgpu_buffer_rsrc_t rc, __amdgpu_buf
                                          int r, uint32_t row, uint32_t col, uint32_t in) {
   const uint32_t oob = (uint32_t)(col >= in) << 31;
   const uint32_t off = (row * (in * BITS / 8) + col * BITS / 8) | oob;
-  if constexpr (BITS == 4) {
+  if constexpr (BITS == 4) {   // (INT5 codes: load5)
     B.c[r][0] = __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, kStream);   // read once: streaming policy
     B.c[r][1] = __builtin_amdgcn_raw_buffer_load_b128(rc, off + 16, 0, kStream);
-  } else {
-#pragma unroll
-    for (int k = 0; k < 5; ++k)
-      B.c[r][k] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rc, off + 8 * k, 0, kStream));
   }
   B.s[r] = __builtin_amdgcn_raw_buffer_load_b16(rs, (2 * (row * (in / 128) + col / 128)) | oob, 0, 0);
 }
@@ -158,14 +158,7 @@ __device__ __forceinline__ float dot_row(const QBatch<4, NR>& B, int r, const QX
 // shift-or spreads it to bits 0..4 and 16..20, and one three-input bitwise op
 // keeps those bits, flips each code's sign bit (q + 16, offset binary) and
 // sets the exponent, giving the bf16 pair 0x4300 | (q + 16) = 144 + q.
-template <int NR>
-__device__ __forceinline__ float dot_row(const QBatch<5, NR>& B, int r, const QX<5>& X) {
-  uint32_t w[10];
-#pragma unroll
-  for (int k = 0; k < 5; ++k) {
-    w[2 * k] = B.c[r][k][0];
-    w[2 * k + 1] = B.c[r][k][1];
-  }
+__device__ __forceinline__ float dot5(const uint32_t (&w)[10], uint32_t sbits, const QX<5>& X) {
   float a = 0.f;
 #pragma unroll
   for (int m = 0; m < 32; ++m) {
@@ -176,7 +169,70 @@ __device__ __forceinline__ float dot_row(const QBatch<5, NR>& B, int r, const QX
     a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pr), __builtin_bit_cast(bf16x2_t, X.p[m]), a,
                                        false);
   }
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)B.s[r]) * (a - X.base);
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)sbits) * (a - X.base);
+}
+
+// Per-lane offsets of the INT5 chunks of one pass (added to the batch's
+// first row times the row bytes).  Piece r < kI4Rows is row r's 2560 bytes
+// from pass byte cb0 (chunks at or past the pass's `pbytes` read zeros);
+// piece kI4Rows (the tail) holds the kI4Rows rows' tails of T lane pieces
+// (40 T bytes each, T even) one after another, so that lane l finds piece
+// l % T of row l / T at byte 40 l, as it finds its columns of a full row.
+// Unused chunks set only bit 31: row base + 2^31 stays below 2^32 and past
+// the codes, so they read zeros.
+template <int NR>
+struct Plan5 {
+  uint32_t off[kI5Chunks<NR>];
+};
+
+template <int NR>
+__device__ __forceinline__ Plan5<NR> plan5(uint32_t lane, uint32_t rowbytes, uint32_t cb0, uint32_t pbytes,
+                                           uint32_t T) {
+  Plan5<NR> P;
+#pragma unroll
+  for (int k = 0; k < kI5Chunks<NR>; ++k) {
+    const uint32_t j = lane + 64 * k, piece = j / 160, c = j - 160 * piece;
+    uint32_t off = 0x80000000u;
+    if (piece < kI4Rows) {
+      if (16 * c < pbytes) off = piece * rowbytes + cb0 + 16 * c;
+    } else if (piece == kI4Rows && c < 10 * T) {
+      const uint32_t per = 5 * T / 2, r = c / per;
+      off = r * rowbytes + kI4Pass * 5 / 8 + 16 * (c - r * per);
+    }
+    P.off[k] = off;
+  }
+  return P;
+}
+
+// Through the wavefront's LDS slice `sl` (NR * 160 chunks as 8-byte
+// halves): chunks in, then piece r's 40 bytes of this lane out.  The lanes
+// read what other lanes wrote, which a thread's own view of memory does not
+// show: without the wavefront-scope fences the compiler drops or sinks
+// writes that the writing thread never reads back itself, and could move the
+// next batch's writes above this batch's reads.  The fences emit no
+// instructions; the hardware performs one wavefront's LDS operations in
+// issue order.
+template <int NR>
+__device__ __forceinline__ void stage5(u32x2_t* sl, const QBatch<5, NR>& B, uint32_t lane) {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // the previous batch's reads come first
+#pragma unroll
+  for (int k = 0; k < kI5Chunks<NR>; ++k)
+    if ((NR * 160) % 64 == 0 || k + 1 < kI5Chunks<NR> || lane + 64 * k < NR * 160) {
+      const u32x4_t c = B.c[k];
+      sl[2 * (lane + 64 * k)] = u32x2_t{c[0], c[1]};
+      sl[2 * (lane + 64 * k) + 1] = u32x2_t{c[2], c[3]};
+    }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // every write lands before the reads
+}
+
+__device__ __forceinline__ void unstage5(const u32x2_t* sl, int r, uint32_t lane, uint32_t (&w)[10]) {
+  const u32x2_t* p = sl + r * 320 + 5 * lane;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const u32x2_t v = p[i];
+    w[2 * i] = v[0];
+    w[2 * i + 1] = v[1];
+  }
 }
 
 // Sum of acc[r] over the wavefront's 64 lanes by a transposed butterfly:
@@ -296,6 +352,111 @@ __device__ __forceinline__ void qgemv(const uint8_t* __restrict__ W, uint32_t V,
   }
 }
 
+// INT5: the same split as qgemv, with the codes of a batch loaded as
+// contiguous 16-byte chunks and handed to their lanes through the
+// wavefront's LDS slice `sl` (NR * 320 eight-byte halves).
+template <int NR>
+__device__ __forceinline__ QBatch<5, NR> load5(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs,
+                                               const Plan5<NR>& P, uint32_t row0, uint32_t V, uint32_t in,
+                                               uint32_t rowbytes, uint32_t col, uint32_t trow, uint32_t tcol) {
+  QBatch<5, NR> B;
+  const uint32_t base = row0 * rowbytes;   // rows past V read zeros (past the codes)
+#pragma unroll
+  for (int k = 0; k < kI5Chunks<NR>; ++k)
+    B.c[k] = __builtin_amdgcn_raw_buffer_load_b128(rc, P.off[k] + base, 0, kStream);
+#pragma unroll
+  for (int r = 0; r < kI4Rows; ++r) load_row(rc, rs, B, r, min(row0 + r, V - 1), col, in);
+  if constexpr (NR > kI4Rows) load_row(rc, rs, B, kI4Rows, min(row0 + trow, V - 1), tcol, in);
+  return B;
+}
+
+template <int PATH>
+__device__ __forceinline__ void qgemv5(const uint8_t* __restrict__ W, uint32_t V, uint32_t in,
+                                       const void* __restrict__ x, float* __restrict__ y, u32x2_t* sl) {
+  constexpr int NR = PATH == kPathTail ? kI4Rows + 1 : kI4Rows;
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t wave = blockIdx.x * 4 + (threadIdx.x >> 6), nwaves = gridDim.x * 4;
+  const uint32_t batches = (V + kI4Rows - 1) / kI4Rows;
+  const uint32_t npass = (in + kI4Pass - 1) / kI4Pass;
+  const uint32_t rowbytes = in * 5 / 8, cbytes = V * rowbytes;
+  const __amdgpu_buffer_rsrc_t rc = rsrc(W, cbytes);
+  const __amdgpu_buffer_rsrc_t rs = rsrc(W + cbytes, V * (in / 128) * 2);
+  const __amdgpu_buffer_rsrc_t rx = rsrc(x, 2 * in);
+  uint32_t b = wave;
+  if (b >= batches) return;
+  QX<5> X;
+  load_x(rx, 64 * lane, X);
+  uint32_t w[10];
+  if constexpr (PATH == kPathOne) {
+    const Plan5<NR> P = plan5<NR>(lane, rowbytes, 0, rowbytes, 0);
+    QBatch<5, NR> B0 = load5<NR>(rc, rs, P, b * kI4Rows, V, in, rowbytes, 64 * lane, 0, 0);
+    for (;;) {
+      const uint32_t bn = b + nwaves;
+      const QBatch<5, NR> B1 = load5<NR>(rc, rs, P, min(bn, batches - 1) * kI4Rows, V, in, rowbytes, 64 * lane, 0, 0);
+      stage5(sl, B0, lane);
+      float acc[kI4Rows];
+#pragma unroll
+      for (int r = 0; r < kI4Rows; ++r) {
+        unstage5(sl, r, lane, w);
+        acc[r] = dot5(w, B0.s[r], X);
+      }
+      const float v = reduce_rows(acc, lane);
+      const uint32_t row = b * kI4Rows + reduce_row(lane);
+      if ((lane & (64 / kI4Rows - 1)) == 0 && row < V) y[row] = v;
+      if (bn >= batches) break;
+      b = bn;
+      B0 = B1;
+    }
+  } else if constexpr (PATH == kPathTail) {
+    const uint32_t T = (in - kI4Pass) / 64, trow = lane / T;
+    const uint32_t tcol = trow < kI4Rows ? kI4Pass + 64 * (lane % T) : in;   // idle lanes read zeros
+    QX<5> XT;
+    load_x(rx, tcol, XT);
+    const Plan5<NR> P = plan5<NR>(lane, rowbytes, 0, kI4Pass * 5 / 8, T);
+    QBatch<5, NR> B0 = load5<NR>(rc, rs, P, b * kI4Rows, V, in, rowbytes, 64 * lane, trow, tcol);
+    for (;;) {
+      const uint32_t bn = b + nwaves;
+      const QBatch<5, NR> B1 =
+          load5<NR>(rc, rs, P, min(bn, batches - 1) * kI4Rows, V, in, rowbytes, 64 * lane, trow, tcol);
+      stage5(sl, B0, lane);
+      unstage5(sl, kI4Rows, lane, w);
+      const float t = dot5(w, B0.s[kI4Rows], XT);
+      float acc[kI4Rows];
+#pragma unroll
+      for (int r = 0; r < kI4Rows; ++r) {
+        unstage5(sl, r, lane, w);
+        acc[r] = dot5(w, B0.s[r], X) + (trow == (uint32_t)r ? t : 0.f);
+      }
+      const float v = reduce_rows(acc, lane);
+      const uint32_t row = b * kI4Rows + reduce_row(lane);
+      if ((lane & (64 / kI4Rows - 1)) == 0 && row < V) y[row] = v;
+      if (bn >= batches) break;
+      b = bn;
+      B0 = B1;
+    }
+  } else {
+    for (; b < batches; b += nwaves) {
+      float acc[kI4Rows] = {};
+      for (uint32_t p = 0; p < npass; ++p) {
+        // X holds pass 0 only before the wavefront's first batch
+        if (p || b != wave) load_x(rx, p * kI4Pass + 64 * lane, X);
+        const uint32_t cb0 = p * (kI4Pass * 5 / 8);
+        const Plan5<NR> P = plan5<NR>(lane, rowbytes, cb0, min(kI4Pass * 5 / 8, rowbytes - cb0), 0);
+        const QBatch<5, NR> B = load5<NR>(rc, rs, P, b * kI4Rows, V, in, rowbytes, p * kI4Pass + 64 * lane, 0, 0);
+        stage5(sl, B, lane);
+#pragma unroll
+        for (int r = 0; r < kI4Rows; ++r) {
+          unstage5(sl, r, lane, w);
+          acc[r] += dot5(w, B.s[r], X);
+        }
+      }
+      const float v = reduce_rows(acc, lane);
+      const uint32_t row = b * kI4Rows + reduce_row(lane);
+      if ((lane & (64 / kI4Rows - 1)) == 0 && row < V) y[row] = v;
+    }
+  }
+}
+
 // one kernel per code width and path, so that each gets its own registers
 template <int PATH>
 __global__ __launch_bounds__(256) void k_int4_gemv(const uint8_t* __restrict__ W, uint32_t V, uint32_t in,
@@ -306,7 +467,9 @@ __global__ __launch_bounds__(256) void k_int4_gemv(const uint8_t* __restrict__ W
 template <int PATH>
 __global__ __launch_bounds__(256) void k_int5_gemv(const uint8_t* __restrict__ W, uint32_t V, uint32_t in,
                                                    const void* __restrict__ x, float* __restrict__ y) {
-  qgemv<5, PATH>(W, V, in, x, y);
+  // one LDS slice of the INT5 codes per wavefront
+  __shared__ u32x2_t sm[4][(PATH == kPathTail ? kI4Rows + 1 : kI4Rows) * 320];
+  qgemv5<PATH>(W, V, in, x, y, sm[threadIdx.x >> 6]);
 }
 
 }  // namespace
