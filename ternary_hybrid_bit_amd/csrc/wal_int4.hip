@@ -5,8 +5,12 @@
 // 5-bit stream per row) and one fp16 scale per 128 columns (layouts in
 // include/wal.h); and the embedding-row lookup of INT3 and INT4 tables.
 //
-// A wavefront takes kI4Rows rows at a time over one 4096-column pass: lane l
-// covers columns 64 l .. 64 l + 63 (32 or 40 code bytes, half a scale group).
+// A wavefront takes kI4Rows rows at a time over one 4096-column pass, 64
+// columns per lane, read so that every load instruction covers contiguous
+// bytes across the lanes: INT4 lane l takes the 32-column pieces at 32 l and
+// 2048 + 32 l (16 code bytes and one scale each); INT5 lane l takes columns
+// 64 l .. 64 l + 63 (40 code bytes, half a scale group), whose codes the
+// wavefront loads as contiguous 16-byte chunks and passes through LDS.
 // Codes are flipped to offset binary and spread into bf16 pairs
 // 0x4300 | (q + 2^(b-1)) = 128 + 2^(b-1) + q, which feed v_dot2_f32_bf16
 // against x pairs arranged to match (INT4: columns k and k + 4 of a dword,
@@ -35,9 +39,12 @@ static_assert(kI4Rows >= 2 && kI4Rows <= 32 && (kI4Rows & (kI4Rows - 1)) == 0, "
 constexpr uint32_t kI4Pass = 4096;
 
 template <int BITS, int NR> struct QBatch;
+// INT4: the lane's 64 columns are two 32-column pieces (16 code bytes and
+// one scale each): columns c and c + gap, gap = 2048 in a pass, so that each
+// load instruction reads 1 KB contiguous over the wavefront.
 template <int NR> struct QBatch<4, NR> {
-  u32x4_t c[NR][2];   // 32 code bytes per row
-  uint32_t s[NR];     // the lane's scale bits per row
+  u32x4_t c[NR][2];   // 16 code bytes per piece
+  uint32_t s[NR][2];  // scale bits per piece
 };
 // INT5 codes travel as 16-byte chunks contiguous across the wavefront's
 // lanes (chunk j = lane + 64 k of the batch's NR row pieces of 2560 bytes)
@@ -52,13 +59,14 @@ template <int NR> struct QBatch<5, NR> {
 // lane's columns formed by the same v_dot2 sequence as a row's sum, so that
 // it cancels exactly: all-zero codes give exactly 0 and a basis vector
 // x = e_j gives s q exactly (columns past `in` read as zero).
-//   INT4: p[d][k] = (x[64 l + 8 d + k], x[64 l + 8 d + k + 4]) for code dword
-//         d and nibble pair k; offset 136.
+//   INT4: p[d][k] = (x[c + 8 d + k], x[c + 8 d + k + 4]) for code dword d < 4
+//         of the first piece (c its first column; d >= 4: the second piece)
+//         and nibble pair k; offset 136, one base per piece.
 //   INT5: p[m] = (x[64 l + 2 m], x[64 l + 2 m + 1]); offset 144.
 template <int BITS> struct QX;
 template <> struct QX<4> {
   uint32_t p[8][4];
-  float base;
+  float base[2];
 };
 template <> struct QX<5> {
   uint32_t p[32];
@@ -77,10 +85,15 @@ __device__ __forceinline__ void load_x_pairs(__amdgpu_buffer_rsrc_t rx, uint32_t
   }
 }
 
-__device__ __forceinline__ void load_x(__amdgpu_buffer_rsrc_t rx, uint32_t col, QX<4>& X) {
+// INT4: pieces at columns col and col + gap
+__device__ __forceinline__ void load_x(__amdgpu_buffer_rsrc_t rx, uint32_t col, uint32_t gap, QX<4>& X) {
   uint32_t w[32];
-  load_x_pairs(rx, col, w);
-  float base = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rx, 2 * (col + (k >= 4 ? gap : 0)) + 16 * (k & 3), 0, 0);
+    w[4 * k] = v[0]; w[4 * k + 1] = v[1]; w[4 * k + 2] = v[2]; w[4 * k + 3] = v[3];
+  }
+  float base[2] = {0.f, 0.f};
 #pragma unroll
   for (int d = 0; d < 8; ++d) {
     // columns 8 d .. 8 d + 7 are bf16 pairs w[4 d] .. w[4 d + 3]
@@ -89,11 +102,12 @@ __device__ __forceinline__ void load_x(__amdgpu_buffer_rsrc_t rx, uint32_t col, 
       const uint32_t lo = w[4 * d + (k >> 1)], hi = w[4 * d + 2 + (k >> 1)];
       // column 8 d + k from lo (half k & 1), column 8 d + k + 4 from hi
       X.p[d][k] = __builtin_amdgcn_perm(hi, lo, (k & 1) ? 0x07060302u : 0x05040100u);
-      base = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, kBf16Pair136),
-                                             __builtin_bit_cast(bf16x2_t, X.p[d][k]), base, false);
+      base[d >> 2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, kBf16Pair136),
+                                                     __builtin_bit_cast(bf16x2_t, X.p[d][k]), base[d >> 2], false);
     }
   }
-  X.base = base;
+  X.base[0] = base[0];
+  X.base[1] = base[1];
 }
 
 __device__ __forceinline__ void load_x(__amdgpu_buffer_rsrc_t rx, uint32_t col, QX<5>& X) {
@@ -106,51 +120,60 @@ __device__ __forceinline__ void load_x(__amdgpu_buffer_rsrc_t rx, uint32_t col, 
   X.base = base;
 }
 
-// Row r of a batch: the lane's 64 columns from `col` of matrix row `row`;
-// col >= in (past a partial last pass, or an idle tail lane) sets bit 31 of
-// the offsets (the matrix is under 2^31 bytes), so the loads read out of
-// range, zeros, which meet x = 0 there.  (A select between two offsets
-// here becomes a branch around every load.)
+// Row r of a batch at matrix row `row`: INT4 the pieces at col and
+// col + gap (codes and scales), INT5 the scale of the 64 columns from col
+// (its codes: load5).  A column >= in (past a partial last pass, or an idle
+// tail lane) sets bit 31 of the offsets (the matrix is under 2^31 bytes), so
+// the loads read out of range, zeros, which meet x = 0 there.  (A select
+// between two offsets here becomes a branch around every load.)
 template <int BITS, int NR>
 __device__ __forceinline__ void load_row(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs, QBatch<BITS, NR>& B,
-                                         int r, uint32_t row, uint32_t col, uint32_t in) {
-  const uint32_t oob = (uint32_t)(col >= in) << 31;
-  const uint32_t off = (row * (in * BITS / 8) + col * BITS / 8) | oob;
-  if constexpr (BITS == 4) {   // (INT5 codes: load5)
-    B.c[r][0] = __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, kStream);   // read once: streaming policy
-    B.c[r][1] = __builtin_amdgcn_raw_buffer_load_b128(rc, off + 16, 0, kStream);
+                                         int r, uint32_t row, uint32_t col, uint32_t in, uint32_t gap = 0) {
+  if constexpr (BITS == 4) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t c = col + (h ? gap : 0), oob = (uint32_t)(c >= in) << 31;
+      // read once: streaming policy
+      B.c[r][h] = __builtin_amdgcn_raw_buffer_load_b128(rc, (row * (in / 2) + c / 2) | oob, 0, kStream);
+      B.s[r][h] = __builtin_amdgcn_raw_buffer_load_b16(rs, (2 * (row * (in / 128) + c / 128)) | oob, 0, 0);
+    }
+  } else {
+    const uint32_t oob = (uint32_t)(col >= in) << 31;
+    B.s[r] = __builtin_amdgcn_raw_buffer_load_b16(rs, (2 * (row * (in / 128) + col / 128)) | oob, 0, 0);
   }
-  B.s[r] = __builtin_amdgcn_raw_buffer_load_b16(rs, (2 * (row * (in / 128) + col / 128)) | oob, 0, 0);
 }
 
-// kI4Rows rows from row0 at one pass's columns, and with a tail (NR =
-// kI4Rows + 1) one more row piece: row row0 + trow at column tcol.
-template <int BITS, int NR>
-__device__ __forceinline__ QBatch<BITS, NR> load_rows(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs,
-                                                      uint32_t row0, uint32_t V, uint32_t in, uint32_t col,
-                                                      uint32_t trow, uint32_t tcol) {
-  QBatch<BITS, NR> B;
+// INT4: kI4Rows rows from row0 at one pass's pieces (col, col + kI4Gap),
+// and with a tail (NR = kI4Rows + 1) one more row's 64 columns: row
+// row0 + trow at tcol (pieces tcol, tcol + 32).
+constexpr uint32_t kI4Gap = 2048;
+template <int NR>
+__device__ __forceinline__ QBatch<4, NR> load_rows(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs,
+                                                   uint32_t row0, uint32_t V, uint32_t in, uint32_t col,
+                                                   uint32_t trow, uint32_t tcol) {
+  QBatch<4, NR> B;
 #pragma unroll
-  for (int r = 0; r < kI4Rows; ++r) load_row(rc, rs, B, r, min(row0 + r, V - 1), col, in);
-  if constexpr (NR > kI4Rows) load_row(rc, rs, B, kI4Rows, min(row0 + trow, V - 1), tcol, in);
+  for (int r = 0; r < kI4Rows; ++r) load_row(rc, rs, B, r, min(row0 + r, V - 1), col, in, kI4Gap);
+  if constexpr (NR > kI4Rows) load_row(rc, rs, B, kI4Rows, min(row0 + trow, V - 1), tcol, in, 32u);
   return B;
 }
 
-// Row r's share of the lane: s * (sum of (136 + q) x - sum of 136 x)
+// Row r's share of the lane: per piece s * (sum of (136 + q) x - sum of 136 x)
 template <int NR>
 __device__ __forceinline__ float dot_row(const QBatch<4, NR>& B, int r, const QX<4>& X) {
-  float a = 0.f;
+  float a[2] = {0.f, 0.f};   // one sum per piece
 #pragma unroll
   for (int d = 0; d < 8; ++d) {
     const uint32_t w = B.c[r][d >> 2][d & 3] ^ 0x88888888u;   // offset binary: q + 8
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const uint32_t pr = ((w >> (4 * k)) & 0x000F000Fu) | 0x43004300u;   // (136 + q_k, 136 + q_{k+4})
-      a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pr), __builtin_bit_cast(bf16x2_t, X.p[d][k]),
-                                         a, false);
+      a[d >> 2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pr),
+                                                  __builtin_bit_cast(bf16x2_t, X.p[d][k]), a[d >> 2], false);
     }
   }
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)B.s[r]) * (a - X.base);
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)B.s[r][0]) * (a[0] - X.base[0]) +
+         (float)__builtin_bit_cast(_Float16, (uint16_t)B.s[r][1]) * (a[1] - X.base[1]);
 }
 
 // INT5: s * (sum of (144 + q) x - sum of 144 x).  Pair m is the 10-bit field
@@ -281,27 +304,27 @@ __host__ __device__ constexpr int qgemv_path(uint32_t in) {
   return in <= kI4Pass ? kPathOne : in <= kI4Pass + 1024 ? kPathTail : kPathMulti;
 }
 
-template <int BITS, int PATH>
-__device__ __forceinline__ void qgemv(const uint8_t* __restrict__ W, uint32_t V, uint32_t in,
+template <int PATH>
+__device__ __forceinline__ void qgemv4(const uint8_t* __restrict__ W, uint32_t V, uint32_t in,
                                       const void* __restrict__ x, float* __restrict__ y) {
   const uint32_t lane = threadIdx.x & 63;
   const uint32_t wave = blockIdx.x * 4 + (threadIdx.x >> 6), nwaves = gridDim.x * 4;
   const uint32_t batches = (V + kI4Rows - 1) / kI4Rows;
   const uint32_t npass = (in + kI4Pass - 1) / kI4Pass;
-  const uint32_t cbytes = V * (in * BITS / 8);
+  const uint32_t cbytes = V * (in / 2);
   const __amdgpu_buffer_rsrc_t rc = rsrc(W, cbytes);
   const __amdgpu_buffer_rsrc_t rs = rsrc(W + cbytes, V * (in / 128) * 2);
   const __amdgpu_buffer_rsrc_t rx = rsrc(x, 2 * in);
   uint32_t b = wave;
   if (b >= batches) return;
-  QX<BITS> X;
-  load_x(rx, 64 * lane, X);
+  QX<4> X;
+  load_x(rx, 32 * lane, kI4Gap, X);
   if constexpr (PATH == kPathOne) {
-    QBatch<BITS, kI4Rows> B0 = load_rows<BITS, kI4Rows>(rc, rs, b * kI4Rows, V, in, 64 * lane, 0, 0);
+    QBatch<4, kI4Rows> B0 = load_rows<kI4Rows>(rc, rs, b * kI4Rows, V, in, 32 * lane, 0, 0);
     for (;;) {
       const uint32_t bn = b + nwaves;
-      const QBatch<BITS, kI4Rows> B1 =
-          load_rows<BITS, kI4Rows>(rc, rs, min(bn, batches - 1) * kI4Rows, V, in, 64 * lane, 0, 0);
+      const QBatch<4, kI4Rows> B1 =
+          load_rows<kI4Rows>(rc, rs, min(bn, batches - 1) * kI4Rows, V, in, 32 * lane, 0, 0);
       float acc[kI4Rows];
 #pragma unroll
       for (int r = 0; r < kI4Rows; ++r) acc[r] = dot_row(B0, r, X);
@@ -315,14 +338,14 @@ __device__ __forceinline__ void qgemv(const uint8_t* __restrict__ W, uint32_t V,
   } else if constexpr (PATH == kPathTail) {
     const uint32_t T = (in - kI4Pass) / 64, trow = lane / T;
     const uint32_t tcol = trow < kI4Rows ? kI4Pass + 64 * (lane % T) : in;   // idle lanes read zeros
-    QX<BITS> XT;
-    load_x(rx, tcol, XT);
+    QX<4> XT;
+    load_x(rx, tcol, 32u, XT);
     constexpr int NR = kI4Rows + 1;
-    QBatch<BITS, NR> B0 = load_rows<BITS, NR>(rc, rs, b * kI4Rows, V, in, 64 * lane, trow, tcol);
+    QBatch<4, NR> B0 = load_rows<NR>(rc, rs, b * kI4Rows, V, in, 32 * lane, trow, tcol);
     for (;;) {
       const uint32_t bn = b + nwaves;
-      const QBatch<BITS, NR> B1 =
-          load_rows<BITS, NR>(rc, rs, min(bn, batches - 1) * kI4Rows, V, in, 64 * lane, trow, tcol);
+      const QBatch<4, NR> B1 =
+          load_rows<NR>(rc, rs, min(bn, batches - 1) * kI4Rows, V, in, 32 * lane, trow, tcol);
       const float t = dot_row(B0, kI4Rows, XT);
       float acc[kI4Rows];
 #pragma unroll
@@ -339,9 +362,9 @@ __device__ __forceinline__ void qgemv(const uint8_t* __restrict__ W, uint32_t V,
       float acc[kI4Rows] = {};
       for (uint32_t p = 0; p < npass; ++p) {
         // X holds pass 0 only before the wavefront's first batch
-        if (p || b != wave) load_x(rx, p * kI4Pass + 64 * lane, X);
-        const QBatch<BITS, kI4Rows> B =
-            load_rows<BITS, kI4Rows>(rc, rs, b * kI4Rows, V, in, p * kI4Pass + 64 * lane, 0, 0);
+        if (p || b != wave) load_x(rx, p * kI4Pass + 32 * lane, kI4Gap, X);
+        const QBatch<4, kI4Rows> B =
+            load_rows<kI4Rows>(rc, rs, b * kI4Rows, V, in, p * kI4Pass + 32 * lane, 0, 0);
 #pragma unroll
         for (int r = 0; r < kI4Rows; ++r) acc[r] += dot_row(B, r, X);
       }
@@ -352,7 +375,7 @@ __device__ __forceinline__ void qgemv(const uint8_t* __restrict__ W, uint32_t V,
   }
 }
 
-// INT5: the same split as qgemv, with the codes of a batch loaded as
+// INT5: the same split as qgemv4, with the codes of a batch loaded as
 // contiguous 16-byte chunks and handed to their lanes through the
 // wavefront's LDS slice `sl` (NR * 320 eight-byte halves).
 template <int NR>
@@ -461,7 +484,7 @@ __device__ __forceinline__ void qgemv5(const uint8_t* __restrict__ W, uint32_t V
 template <int PATH>
 __global__ __launch_bounds__(256) void k_int4_gemv(const uint8_t* __restrict__ W, uint32_t V, uint32_t in,
                                                    const void* __restrict__ x, float* __restrict__ y) {
-  qgemv<4, PATH>(W, V, in, x, y);
+  qgemv4<PATH>(W, V, in, x, y);
 }
 
 template <int PATH>
