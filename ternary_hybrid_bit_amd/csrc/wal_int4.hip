@@ -514,9 +514,10 @@ static int qgemv_launch(int bits, const void* W_dev, uint32_t V, uint32_t in, co
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return WAL_ERR_DEVICE;
   const uint32_t batches = (V + kI4Rows - 1) / kI4Rows;
-  // two workgroups (8 wavefronts) per CU, each wavefront looping over batches
-  // (measured on the 151936 x 4096 INT4 head: faster than 1, 1.5, 3 or 4)
-  const uint32_t blocks = std::min<uint32_t>((batches + 3) / 4, (uint32_t)cus * 2);
+  // Workgroups per CU, each wavefront looping over batches.  INT4: three
+  // (on the 151936 x 4096 head about 1 % faster than two or four, 11 %
+  // faster than one); INT5: two, all its registers allow at the 5120 width.
+  const uint32_t blocks = std::min<uint32_t>((batches + 3) / 4, (uint32_t)cus * (bits == 4 ? 3 : 2));
   const uint8_t* W = static_cast<const uint8_t*>(W_dev);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 g(blocks), t(256);
