@@ -88,28 +88,36 @@ def stored_traffic():
 
 def cpu_baseline(items, budget_s: float):
     """Time the oracle (unpack -> dense float64 W -> W @ x) on whole matrices
-    of the sweep, in order, until about ``budget_s`` seconds of CPU work."""
+    of the sweep, in order, until about ``budget_s`` seconds of CPU work; also
+    the product W @ x alone with W already built.  ``cores`` is the number of
+    host CPUs this process may run on (its affinity); the unpack runs on one
+    of them and the product on the BLAS pool (``blas_threads``)."""
     from oracle import dense as D
+    from oracle import format as F
     import synth
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:  # noqa: BLE001
-        threads = 1
-    done_bytes, t_total, n = 0, 0.0, 0
+    host = host_info()
+    done_bytes, t_total, t_mm, n = 0, 0.0, 0.0, 0
     for blob, info, xb in items:
-        x = synth.bf16_bits_to_f32(xb)
+        x = synth.bf16_bits_to_f32(xb).astype(np.float64)
         t0 = time.perf_counter()
-        D.gemv(blob, x)
-        t_total += time.perf_counter() - t0
+        W = D.dense_W(F.unpack(blob))
+        t1 = time.perf_counter()
+        W @ x
+        t2 = time.perf_counter()
+        t_total += t2 - t0
+        t_mm += t2 - t1
         done_bytes += info.algorithmic_bytes
         n += 1
+        del W
         if t_total >= budget_s:
             break
-    return {"value": round(done_bytes / t_total / 1e9, 4), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
+    return {"value": round(done_bytes / t_total / 1e9, 4), "unit": "GB/s",
+            "cores": host["affinity"] or host["cpu_count"], "kind": "oracle",
             "sample": f"first {n} of 252 sweep matrices ({done_bytes / 1e9:.3f} GB packed), "
-                      f"{t_total:.1f} s: numpy unpack + dense float64 W + W@x per matrix"}
+                      f"{t_total:.1f} s: numpy unpack + dense float64 W + W@x per matrix",
+            "matmul_only_value": round(done_bytes / t_mm / 1e9, 4), "matmul_only_s": round(t_mm, 3),
+            "cpu_count": host["cpu_count"], "affinity": host["affinity"],
+            "blas_threads": host["blas_threads"], "blas": host["blas"]}
 
 
 def torch_sum_gbs(torch, dev) -> float:
@@ -177,16 +185,21 @@ def oracle_time(blob, X):
 
 
 def host_info():
+    """Host CPUs: os.cpu_count(), the affinity of this process, and the BLAS
+    libraries numpy uses with their thread counts."""
     try:
         from threadpoolctl import threadpool_info
-        pools = [{"api": p.get("internal_api"), "threads": p.get("num_threads")} for p in threadpool_info()]
+        pools = [{"api": p.get("internal_api"), "library": os.path.basename(p.get("filepath") or ""),
+                  "threads": p.get("num_threads")} for p in threadpool_info()]
     except Exception:  # noqa: BLE001
         pools = []
     try:
         aff = len(os.sched_getaffinity(0))
     except AttributeError:
         aff = None
-    return {"cpu_count": os.cpu_count(), "affinity": aff, "blas": pools}
+    blas = [p["threads"] for p in pools if p.get("api") in ("openblas", "mkl", "blis")]
+    return {"cpu_count": os.cpu_count(), "affinity": aff, "blas": pools,
+            "blas_threads": max(blas) if blas else None}
 
 
 def run_single(args):

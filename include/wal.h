@@ -51,8 +51,11 @@
  * Conventions for every call:
  *   - The caller allocates and owns every buffer.  Host pointers are used by
  *     the packing calls; device pointers (from hipMalloc or torch) by the
- *     product calls.  The library allocates no memory, never synchronises a
- *     stream and keeps no pointer after a call returns.
+ *     product calls.  Packing and product calls allocate no memory, never
+ *     synchronise a stream and keep no pointer after they return.  The one
+ *     exception is wal_graph_create: it creates a HIP stream for the capture
+ *     (destroyed before it returns), a graph, its executable form and a small
+ *     host handle, all of which wal_graph_destroy frees.
  *   - Product calls enqueue work on `stream` (a hipStream_t; NULL = the
  *     default stream) and return.  y / Y is overwritten, never accumulated.
  *     x / X is read-only and must not overlap y / Y.
@@ -167,8 +170,11 @@ int wal_pack(const wal_desc* desc, const int8_t* T, const uint8_t* site_pos,
              const int8_t* U, const int8_t* V, const float* s,
              void* dst, size_t dst_bytes, wal_info* info);
 
-/* Parse and check a blob's header and layout (not its planes).
- * Errors: ARG, BUFFER, FORMAT. */
+/* Parse and check a blob's header and layout (not its planes).  With
+ * wal_verify and wal_unpack below, this is the fail-closed check of a packed
+ * cache before use (WAL-Ternary-8B cards, "Install" / "Орнату": the cache of
+ * packed ternary symbols, sparse positions and signs and fp16 scales is
+ * verified fail-closed).  Errors: ARG, BUFFER, FORMAT. */
 int wal_inspect(const void* blob, size_t bytes, wal_info* info);
 
 /* Full check of a host blob: header, layout, checksum and every stored code
@@ -184,7 +190,11 @@ int wal_unpack(const void* blob, size_t bytes, int8_t* T, uint8_t* site_pos,
                int8_t* V, float* s);
 
 /* Device workspace that wal_gemv and wal_gemm_small need for a blob and
- * batch: the per-path reductions z_p = diag(s_p) V_p^T X per 4096-column
+ * batch.  The WALB2 term sum_r U_r (V_r^T x) of the operator (WAL-Ternary-8B
+ * cards, "Representation") needs every V_r^T x complete before U expands it,
+ * so its partial sums live in device memory between the two steps; the
+ * small-batch kernels also keep partial products there.  Contents: the
+ * per-path reductions z_p = diag(s_p) V_p^T X per 4096-column
  * chunk [chunks][batch][n_paths * rank] and the small-batch kernels' partial
  * sums per 1024-column slice [ceil(in / 1024)][batch][out] (fp32), each part
  * padded to 256 bytes.  wal_gemv uses the first part only.
@@ -258,7 +268,9 @@ int wal_gemm_prefill(const wal_info* info, const void* W_dev, const void* X_dev,
                      void* ws_dev, size_t ws_bytes, void* stream);
 
 /* Grouped products y_i = W_i(x_i), i < n, in one pass over all matrices
- * (e.g. the 252 body matrices of a 36-layer model).  Two steps:
+ * (e.g. the 252 body matrices of a 36-layer model, all of which run straight
+ * from the packed form: WAL-Ternary-8B cards, "Модель пішімі" /
+ * "Representation", 252/252 body matrices).  Two steps:
  *   1. wal_grouped_plan writes a plan blob into plan_host (host memory of
  *      plan_bytes, see wal_grouped_plan_size) describing every matrix (device
  *      pointers of its planes, x_i, y_i, its workspace slot) and, for each
@@ -403,8 +415,8 @@ int wal_rotate_h128(const void* x_dev, int x_dtype, uint32_t rows, uint32_t in, 
                     void* out_dev, int out_dtype, uint32_t ldo, void* stream);
 
 /* A decode step as a chain of grouped products that depend on each other
- * (SURVEY-ranked next step after the grouped sweep; the 8B card's runtime
- * captures its decode step in a CUDA graph, "Runtime"/"Performance"): product
+ * (the 8B cards time their decode step with a captured graph, "Жылдамдық пен
+ * жад" / speed and memory table): product
  * i + 1 starts only after product i has finished, as when matrices that
  * share an input (q|k|v, gate|up) form one grouped product and the next
  * product reads the previous one's output.

@@ -141,6 +141,90 @@ def _stream(stream=None) -> Optional[int]:
     return torch.cuda.current_stream().cuda_stream
 
 
+# ---------------------------------------------------------------------------
+# Checks of device arguments.  The C ABI takes bare pointers and cannot see a
+# buffer's size, dtype or device, so the binding checks them before any call:
+# a wrong dtype or a short buffer would otherwise become out-of-bounds device
+# reads or writes.  Type, dtype, shape and size are checked before the device,
+# so every check can be exercised on CPU tensors.
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev(t, name: str, dtypes, min_numel: int = 0):
+    """t must be a torch tensor of one of ``dtypes`` (torch dtypes), with at
+    least ``min_numel`` elements and unit stride along its last axis."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor on the GPU, not {type(t).__name__}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}; expected one of {[str(d) for d in dtypes]}")
+    if t.numel() < min_numel:
+        raise ValueError(f"{name} holds {t.numel()} elements; at least {min_numel} are needed")
+    if t.dim() > 0 and t.numel() > 1 and t.stride(-1) != 1:
+        raise ValueError(f"{name} must have unit stride along its last axis")
+    if t.dim() > 2:
+        raise ValueError(f"{name} must be 1-D or 2-D")
+    return t
+
+
+def _dev_bytes(t, name: str, min_bytes: int):
+    """A byte buffer (any dtype) of at least min_bytes bytes, contiguous."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor on the GPU, not {type(t).__name__}")
+    nb = t.numel() * t.element_size()
+    if nb < min_bytes:
+        raise ValueError(f"{name} holds {nb} bytes; at least {min_bytes} are needed")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _gpu(**tensors):
+    """Every named tensor (None skipped) must live on a GPU; checked after
+    all other checks of a call."""
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be on the GPU (device {t.device})")
+
+
+def _xdtype(t) -> int:
+    torch = _torch()
+    return WAL_X_BF16 if t.dtype == torch.bfloat16 else WAL_X_F32
+
+
+def _act(t, name: str, n: int):
+    """An activation vector: bf16 or fp32, at least n elements."""
+    torch = _torch()
+    return _dev(t, name, (torch.bfloat16, torch.float32), n)
+
+
+def _rows(t, name: str, dtypes, cols: int, rows: Optional[int] = None):
+    """A 2-D [rows][ld] device matrix with ld >= cols (unit column stride)."""
+    _dev(t, name, dtypes)
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D [rows][ld]")
+    if t.shape[1] < cols:
+        raise ValueError(f"{name} has {t.shape[1]} columns; at least {cols} are needed")
+    if rows is not None and t.shape[0] < rows:
+        raise ValueError(f"{name} has {t.shape[0]} rows; at least {rows} are needed")
+    if t.shape[0] > 1 and t.stride(0) < t.shape[1]:
+        raise ValueError(f"{name} rows overlap (stride {t.stride(0)} < {t.shape[1]})")
+    return t
+
+
+def _ws_bytes(ws, name: str = "ws") -> int:
+    """Byte size of a workspace tensor (0 for None); the library checks it
+    against what the product needs."""
+    if ws is None:
+        return 0
+    _dev_bytes(ws, name, 0)
+    return ws.numel() * ws.element_size()
+
+
 def wal_status_str(status: int) -> str:
     return _lib.wal_status_str(status).decode()
 
@@ -224,9 +308,13 @@ def wal_prefill_workspace_size(info: wal_info, batch: int) -> int:
 def wal_gemv(info: wal_info, W, x, y, ws=None, stream=None):
     """y = W(x) on the GPU; W, x, y (and ws, see wal_workspace_size) are device
     tensors; y is fp32 [out]."""
-    import torch
-    xdt = WAL_X_BF16 if x.dtype == torch.bfloat16 else WAL_X_F32
-    wsb = ws.numel() * ws.element_size() if ws is not None else 0
+    torch = _torch()
+    _dev_bytes(W, "W", int(info.total_bytes))
+    _act(x, "x", int(info.d.in_))
+    _dev(y, "y", (torch.float32,), int(info.d.out))
+    xdt = _xdtype(x)
+    wsb = _ws_bytes(ws)
+    _gpu(W=W, x=x, y=y, ws=ws)
     st = _lib.wal_gemv(ctypes.byref(info), _ptr(W), _ptr(x), xdt, _ptr(y), _ptr(ws), wsb, _stream(stream))
     _check(st, "wal_gemv")
     return y
@@ -234,9 +322,15 @@ def wal_gemv(info: wal_info, W, x, y, ws=None, stream=None):
 
 def wal_gemm_small(info: wal_info, W, X, Y, mode=WAL_GEMM_AUTO, ws=None, stream=None):
     """Y = X W^T on the GPU; X [batch][ldx], Y [batch][ldy] device tensors."""
-    import torch
-    xdt = WAL_X_BF16 if X.dtype == torch.bfloat16 else WAL_X_F32
-    wsb = ws.numel() * ws.element_size() if ws is not None else 0
+    torch = _torch()
+    _dev_bytes(W, "W", int(info.total_bytes))
+    _rows(X, "X", (torch.bfloat16, torch.float32), int(info.d.in_))
+    _rows(Y, "Y", (torch.float32,), int(info.d.out), X.shape[0])
+    xdt = _xdtype(X)
+    if not 1 <= X.shape[0] <= WAL_MAX_BATCH:
+        raise ValueError(f"batch {X.shape[0]} outside 1..{WAL_MAX_BATCH}")
+    wsb = _ws_bytes(ws)
+    _gpu(W=W, X=X, Y=Y, ws=ws)
     st = _lib.wal_gemm_small(ctypes.byref(info), _ptr(W), _ptr(X), xdt, X.shape[0], X.stride(0), _ptr(Y),
                              Y.stride(0), mode, _ptr(ws), wsb, _stream(stream))
     _check(st, "wal_gemm_small")
@@ -246,9 +340,15 @@ def wal_gemm_small(info: wal_info, W, X, Y, mode=WAL_GEMM_AUTO, ws=None, stream=
 def wal_gemm_prefill(info: wal_info, W, X, Y, ws=None, stream=None):
     """Y = X W^T for a prefill-size batch; X [batch][ldx] bf16, Y [batch][ldy]
     fp32 device tensors, ws of wal_prefill_workspace_size bytes (or None when 0)."""
-    import torch
-    xdt = WAL_X_BF16 if X.dtype == torch.bfloat16 else WAL_X_F32
-    wsb = ws.numel() * ws.element_size() if ws is not None else 0
+    torch = _torch()
+    _dev_bytes(W, "W", int(info.total_bytes))
+    _rows(X, "X", (torch.bfloat16, torch.float32), int(info.d.in_))
+    _rows(Y, "Y", (torch.float32,), int(info.d.out), X.shape[0])
+    xdt = _xdtype(X)
+    if not 1 <= X.shape[0] <= WAL_MAX_PREFILL_BATCH:
+        raise ValueError(f"batch {X.shape[0]} outside 1..{WAL_MAX_PREFILL_BATCH}")
+    wsb = _ws_bytes(ws)
+    _gpu(W=W, X=X, Y=Y, ws=ws)
     st = _lib.wal_gemm_prefill(ctypes.byref(info), _ptr(W), _ptr(X), xdt, X.shape[0], X.stride(0), _ptr(Y),
                                Y.stride(0), _ptr(ws), wsb, _stream(stream))
     _check(st, "wal_gemm_prefill")
@@ -266,7 +366,15 @@ def wal_grouped_plan_size(infos: Sequence[wal_info], grid: int = 0, x_dtype: int
 
 def wal_grouped_plan(infos: Sequence[wal_info], Ws, xs, ys, ws, x_dtype: int, grid: int = 0):
     """Build a grouped plan; returns (plan bytes as numpy uint8, wal_grouped_info)."""
+    torch = _torch()
     n = len(infos)
+    if not (len(Ws) == len(xs) == len(ys) == n):
+        raise ValueError("infos, Ws, xs and ys must have the same length")
+    xt = torch.bfloat16 if x_dtype == WAL_X_BF16 else torch.float32
+    for i, (f, w, x, y) in enumerate(zip(infos, Ws, xs, ys)):
+        _dev_bytes(w, f"Ws[{i}]", int(f.total_bytes))
+        _dev(x, f"xs[{i}]", (xt,), int(f.d.in_))
+        _dev(y, f"ys[{i}]", (torch.float32,), int(f.d.out))
     arr = (wal_info * n)(*infos)
     pb, _ = wal_grouped_plan_size(infos, grid, x_dtype)
     plan = np.zeros(pb, dtype=np.uint8)
@@ -274,18 +382,29 @@ def wal_grouped_plan(infos: Sequence[wal_info], Ws, xs, ys, ws, x_dtype: int, gr
     xp = (ctypes.c_void_p * n)(*[_ptr(x) for x in xs])
     yp = (ctypes.c_void_p * n)(*[_ptr(y) for y in ys])
     g = wal_grouped_info()
-    wsb = ws.numel() * ws.element_size() if ws is not None else 0
+    wsb = _ws_bytes(ws)
+    for i, (w, x, y) in enumerate(zip(Ws, xs, ys)):
+        _gpu(**{f"Ws[{i}]": w, f"xs[{i}]": x, f"ys[{i}]": y})
+    _gpu(ws=ws)
     st = _lib.wal_grouped_plan(n, arr, Wp, xp, x_dtype, yp, _ptr(ws), wsb, grid, plan.ctypes.data, plan.size,
                                ctypes.byref(g))
     _check(st, "wal_grouped_plan")
     return plan, g
 
 
+def _plan(ginfo: wal_grouped_info, plan_dev, name="plan_dev"):
+    _dev_bytes(plan_dev, name, int(ginfo.plan_bytes))
+    _gpu(**{name: plan_dev})
+    return plan_dev
+
+
 def wal_gemv_grouped(ginfo: wal_grouped_info, plan_dev, stream=None):
+    _plan(ginfo, plan_dev)
     _check(_lib.wal_gemv_grouped(ctypes.byref(ginfo), _ptr(plan_dev), _stream(stream)), "wal_gemv_grouped")
 
 
 def wal_gemv_grouped_phases(ginfo: wal_grouped_info, plan_dev, phases: int, stream=None):
+    _plan(ginfo, plan_dev)
     _check(_lib.wal_gemv_grouped_phases(ctypes.byref(ginfo), _ptr(plan_dev), phases, _stream(stream)),
            "wal_gemv_grouped_phases")
 
@@ -297,6 +416,8 @@ def exported_symbols() -> list:
 def _chain_args(chain):
     """chain: [(wal_grouped_info, plan device tensor)] -> ctypes arrays."""
     n = len(chain)
+    for i, (g, p) in enumerate(chain):
+        _plan(g, p, f"chain[{i}] plan")
     infos = (wal_grouped_info * n)(*[g for g, _ in chain])
     plans = (ctypes.c_void_p * n)(*[_ptr(p) for _, p in chain])
     return n, infos, plans
@@ -336,12 +457,15 @@ class WalGraph:
 def wal_rotate_h128(X, out, stream=None):
     """out = X rotated by the normalised Hadamard-128 along its last axis (1-D
     or 2-D device tensors, bf16 or fp32; out may be X itself)."""
-    import torch
-
-    def dt(t):
-        return WAL_X_BF16 if t.dtype == torch.bfloat16 else WAL_X_F32
+    torch = _torch()
+    acts = (torch.bfloat16, torch.float32)
+    _dev(X, "X", acts)
+    _dev(out, "out", acts)
     X2 = X if X.dim() == 2 else X.view(1, -1)
     O2 = out if out.dim() == 2 else out.view(1, -1)
+    _rows(O2, "out", acts, X2.shape[1], X2.shape[0])
+    _gpu(X=X, out=out)
+    dt = _xdtype
     st = _lib.wal_rotate_h128(_ptr(X2), dt(X), X2.shape[0], X2.shape[1], X2.stride(0), _ptr(O2), dt(out),
                               O2.stride(0), _stream(stream))
     _check(st, "wal_rotate_h128")
@@ -373,8 +497,12 @@ def wal_int4_unpack(blob: np.ndarray, V: int, inp: int):
 
 def wal_int4_gemv(W, V: int, inp: int, x, y, stream=None):
     """y = W x for an INT4/g128 matrix W (device bytes), x [in] bf16, y [V] fp32."""
-    import torch
-    xdt = WAL_X_BF16 if x.dtype == torch.bfloat16 else WAL_X_F32
+    torch = _torch()
+    _dev_bytes(W, "W", wal_int4_size(V, inp))
+    _act(x, "x", inp)
+    _dev(y, "y", (torch.float32,), V)
+    xdt = _xdtype(x)
+    _gpu(W=W, x=x, y=y)
     _check(_lib.wal_int4_gemv(_ptr(W), V, inp, _ptr(x), xdt, _ptr(y), _stream(stream)), "wal_int4_gemv")
     return y
 
@@ -427,8 +555,12 @@ def wal_int5_unpack(blob: np.ndarray, V: int, inp: int):
 
 def wal_int5_gemv(W, V: int, inp: int, x, y, stream=None):
     """y = W x for an INT5/g128 matrix W (device bytes), x [in] bf16, y [V] fp32."""
-    import torch
-    xdt = WAL_X_BF16 if x.dtype == torch.bfloat16 else WAL_X_F32
+    torch = _torch()
+    _dev_bytes(W, "W", wal_int5_size(V, inp))
+    _act(x, "x", inp)
+    _dev(y, "y", (torch.float32,), V)
+    xdt = _xdtype(x)
+    _gpu(W=W, x=x, y=y)
     _check(_lib.wal_int5_gemv(_ptr(W), V, inp, _ptr(x), xdt, _ptr(y), _stream(stream)), "wal_int5_gemv")
     return y
 
@@ -436,10 +568,14 @@ def wal_int5_gemv(W, V: int, inp: int, x, y, stream=None):
 def wal_embed_rows(W, bits: int, V: int, inp: int, ids, out, stream=None):
     """out[i] = row ids[i] of an INT3 (bits 3) or INT4 (bits 4) matrix W (device
     bytes); ids int32 [n] and out [n][ldo] (fp32 or bf16) device tensors."""
-    import torch
-    if ids.dtype != torch.int32 or out.dtype not in (torch.float32, torch.bfloat16):
-        raise TypeError("ids must be int32 and out float32 or bfloat16")
-    odt = WAL_X_BF16 if out.dtype == torch.bfloat16 else WAL_X_F32
+    torch = _torch()
+    if bits not in (3, 4):
+        raise ValueError("bits must be 3 or 4")
+    _dev_bytes(W, "W", wal_int3_size(V, inp) if bits == 3 else wal_int4_size(V, inp))
+    _dev(ids, "ids", (torch.int32,))
+    _rows(out, "out", (torch.float32, torch.bfloat16), inp, ids.numel())
+    odt = _xdtype(out)
+    _gpu(W=W, ids=ids, out=out)
     _check(_lib.wal_embed_rows(_ptr(W), bits, V, inp, _ptr(ids), ids.numel(), _ptr(out), odt, out.stride(0),
                                _stream(stream)), "wal_embed_rows")
     return out
@@ -449,10 +585,14 @@ def wal_embed_rows_mixed(W3, V3: int, W4, V4: int, inp: int, row_map, ids, out, 
     """out[i] = vocabulary row ids[i] of a mixed table: row_map[v] >= 0 names
     a row of the INT3 table W3, a negative entry m row -1 - m of the INT4
     table W4 (device bytes); row_map and ids int32, out [n][ldo] device."""
-    import torch
-    if ids.dtype != torch.int32 or row_map.dtype != torch.int32 or out.dtype not in (torch.float32, torch.bfloat16):
-        raise TypeError("ids and row_map must be int32 and out float32 or bfloat16")
-    odt = WAL_X_BF16 if out.dtype == torch.bfloat16 else WAL_X_F32
+    torch = _torch()
+    _dev_bytes(W3, "W3", wal_int3_size(V3, inp) if V3 else 0)
+    _dev_bytes(W4, "W4", wal_int4_size(V4, inp) if V4 else 0)
+    _dev(row_map, "row_map", (torch.int32,))
+    _dev(ids, "ids", (torch.int32,))
+    _rows(out, "out", (torch.float32, torch.bfloat16), inp, ids.numel())
+    odt = _xdtype(out)
+    _gpu(W3=W3, W4=W4, row_map=row_map, ids=ids, out=out)
     _check(_lib.wal_embed_rows_mixed(_ptr(W3), V3, _ptr(W4), V4, inp, _ptr(row_map), row_map.numel(), _ptr(ids),
                                      ids.numel(), _ptr(out), odt, out.stride(0), _stream(stream)),
            "wal_embed_rows_mixed")

@@ -7,6 +7,7 @@ bf16 activations and 1e-5 with fp32 ones.  Rows X[n] = e_j must give column j
 of W bit-exactly (decoded values are exact in bf16 and every product and
 partial sum is exact in fp32), and the all-zero blob gives exact zeros.
 """
+import ctypes
 import numpy as np
 import pytest
 
@@ -179,9 +180,12 @@ def test_rejects_bad_leading_dimensions(wal):
     X = to_dev(bits.view(np.int16)).view(torch.bfloat16)
     Y = torch.zeros((2, 64), dtype=torch.float32, device=dev())
     ws = torch.zeros(wal.wal_workspace_size(info, 2) // 4 + 1, dtype=torch.float32, device=dev())
-    with pytest.raises(wal.WalError) as ei:   # ldx < in
+    with pytest.raises(ValueError):   # ldx < in: the binding refuses it
         wal.wal_gemm_small(info, W, X[:, :128].contiguous(), Y, wal.WAL_GEMM_VALU, ws)
-    assert ei.value.status == -1
+    Xn = X[:, :128].contiguous()      # and so does the library, called directly
+    st = wal._lib.wal_gemm_small(ctypes.byref(info), W.data_ptr(), Xn.data_ptr(), wal.WAL_X_BF16, 2, 128,
+                                 Y.data_ptr(), 64, wal.WAL_GEMM_VALU, ws.data_ptr(), ws.numel() * 4, None)
+    assert st == -1
     Xp = torch.zeros((2, 260), dtype=torch.bfloat16, device=dev())
     with pytest.raises(wal.WalError) as ei:   # row pitch not a multiple of 16 bytes
         wal.wal_gemm_small(info, W, Xp, Y, wal.WAL_GEMM_VALU, ws)

@@ -185,6 +185,75 @@ def test_sweep_counts_match_page():
     assert abs(tot / 2**30 - g["executable_cache_gb_approx"]) < 0.15
 
 
+def test_algorithmic_bytes_hand_worked():
+    """Bytes a product reads, worked by hand from the layout (codes in/4 per
+    row for 2-bit, ceil(in/5) for base-3; k site bytes and one alpha (+ beta
+    when k > 0) of 2 (fp16) or 3 (fp24) bytes per row and 128-column group;
+    per path rank*in/8 V bytes, out*ceil(rank/8) U bytes and 2*rank s bytes),
+    against the oracle's count."""
+    # 256 x 512, k = 8, fp16, no paths: 32768 codes + 256*4*8 sites
+    # + 256*4*2 alpha + 256*4*2 beta
+    assert 256 * 512 // 4 + 8192 + 2048 + 2048 == 45_056
+    assert F.algorithmic_bytes(256, 512, 8, 0, 0, F.TRIT_2BIT, F.SCALE_FP16) == 45_056
+    # 12288 x 4096, k = 8, fp16, one rank-16 path:
+    # 12,582,912 codes + 3,145,728 sites + 1,572,864 alpha/beta
+    # + 8,192 V + 24,576 U + 32 s
+    assert 12_582_912 + 3_145_728 + 1_572_864 + 8_192 + 24_576 + 32 == 17_334_304
+    assert F.algorithmic_bytes(12288, 4096, 8, 1, 16, F.TRIT_2BIT, F.SCALE_FP16) == 17_334_304
+    # 4096 x 12288 (the down shape): the same total
+    assert F.algorithmic_bytes(4096, 12288, 8, 1, 16, F.TRIT_2BIT, F.SCALE_FP16) == 17_334_304
+    # 17408 x 5120, base-3, fp24, two rank-16 paths: codes 17408 * 1024,
+    # alpha 17408*40*3, paths 2 * (10240 V + 34816 U + 32 s), then per k the
+    # sites 17408*40*k and beta 2,088,960
+    base = 17_825_792 + 2_088_960 + 90_176
+    want = {0: 20_004_928, 2: 23_486_528, 4: 24_879_168, 8: 27_664_448}
+    for k, v in want.items():
+        extra = 0 if k == 0 else 17408 * 40 * k + 2_088_960
+        assert base + extra == v
+        assert F.algorithmic_bytes(17408, 5120, k, 2, 16, F.TRIT_BASE3, F.SCALE_FP24) == v
+        # 5120 x 17408: 5120 * ceil(17408 / 5) = 5120 * 3482 code bytes, 2,048
+        # more than above; alpha 5120*136*3 is the same; row padding not counted
+        assert F.algorithmic_bytes(5120, 17408, k, 2, 16, F.TRIT_BASE3, F.SCALE_FP24) == v + 2_048
+    # 2-bit vs base-3 rows: a padded base-3 row (1024 -> stride 1024, 3482 ->
+    # 3488) still counts ceil(in / 5)
+    assert F.algorithmic_bytes(1, 640, 0, 0, 0, F.TRIT_BASE3, F.SCALE_FP16) == 128 + 10
+
+
+def test_sweep_bytes_hand_worked():
+    """The 252-matrix body: per layer q, o 4096x4096 (5,767,168 B each), k, v
+    1024x4096 (1,441,792 B each), gate, up 12288x4096 and down 4096x12288
+    (17,301,504 B each) at k = 8, fp16; a rank-16 path adds 2*(in + out) + 32
+    bytes on each of the 213 drawn matrices."""
+    per_layer = 2 * 5_767_168 + 2 * 1_441_792 + 3 * 17_301_504
+    assert per_layer * 36 == 2_387_607_552
+    shapes = synth.sweep_shapes()
+    mask = synth.sweep_lowrank_mask()
+    lowrank = sum(2 * (i + o) + 32 for (o, i), m in zip(shapes, mask) if m)
+    assert 2_387_607_552 + lowrank == 2_392_197_792
+    tot = sum(F.algorithmic_bytes(o, i, 8, int(m), 16, 0, 0) for (o, i), m in zip(shapes, mask))
+    assert tot == 2_392_197_792
+
+
+def test_rel_l2_hand_worked():
+    """rel_l2 = ||y - y_ref|| / ||y_ref||, worked by hand."""
+    # y - y_ref = (3, -1): sqrt(10) / 5
+    assert D.rel_l2([3.0, 4.0], [0.0, 5.0]) == pytest.approx(np.sqrt(10.0) / 5.0, rel=1e-15)
+    # the reference is the denominator, not y: (0, 5) vs (3, 4) gives sqrt(10)/5 too
+    # but (1, 0) vs (2, 0) is 1/2 one way and 1 the other
+    assert D.rel_l2([1.0, 0.0], [2.0, 0.0]) == pytest.approx(0.5, rel=1e-15)
+    assert D.rel_l2([2.0, 0.0], [1.0, 0.0]) == pytest.approx(1.0, rel=1e-15)
+    # (1, 2, 2) vs (1, 2, 3): 1 / sqrt(14)
+    assert D.rel_l2([1.0, 2.0, 2.0], [1.0, 2.0, 3.0]) == pytest.approx(1.0 / np.sqrt(14.0), rel=1e-15)
+    # equal vectors: exactly 0; zero vs zero: 0; anything else vs zero: inf
+    assert D.rel_l2([1.5, -2.0], [1.5, -2.0]) == 0.0
+    assert D.rel_l2([0.0, 0.0], [0.0, -0.0]) == 0.0
+    assert D.rel_l2([1e-30, 0.0], [0.0, 0.0]) == float("inf")
+    # a 2-D input is one vector (the norm over every element)
+    assert D.rel_l2([[3.0], [4.0]], [[0.0], [5.0]]) == pytest.approx(np.sqrt(10.0) / 5.0, rel=1e-15)
+    # float32 inputs are taken at their exact values
+    assert D.rel_l2(np.float32([1.0, 0.0]), np.float32([2.0, 0.0])) == 0.5
+
+
 # --------------------------------------------------------------------------
 # Exact-rational brute force.
 
