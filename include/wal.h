@@ -214,6 +214,23 @@ int wal_workspace_size(const wal_info* info, uint32_t batch, size_t* bytes);
 int wal_gemv(const wal_info* info, const void* W_dev, const void* x_dev, int x_dtype,
              float* y_dev, void* ws_dev, size_t ws_bytes, void* stream);
 
+/* y = W(x) as wal_gemv, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the workspace is a file-scope device array of
+ * WAL_NOALLOC_SCRATCH_BYTES (4 MiB) that each GPU holds from the library's
+ * first use until the process ends; the call itself allocates nothing.
+ * Arguments as for wal_gemv.  A blob whose low-rank partials exceed the
+ * scratch returns WAL_ERR_BUFFER (4 bytes per term and 4096-column chunk:
+ * only past 16 million columns at the maximum of 256 terms); a wide matrix
+ * whose per-pass partial sums do not fit
+ * runs its passes in sequence instead of splitting them.  Every call on a
+ * GPU shares that GPU's scratch: calls that overlap on one GPU (several
+ * streams or threads) race and must be ordered by the caller.
+ * Errors: those of wal_gemv, BUFFER. */
+#define WAL_NOALLOC_SCRATCH_BYTES (4u << 20)
+int wal_gemv_noalloc(const wal_info* info, const void* W_dev, const void* x_dev, int x_dtype, float* y_dev,
+                     void* stream);
+
 /* Y = X W^T for a small batch (F.linear convention): row n of Y is W(x_n)
  * with x_n row n of X (WAL-Ternary-8B cards, "Representation").
  *   X_dev  [batch][ldx] activations (bf16 or fp32), ldx >= in, ldx*elem % 16 == 0,

@@ -84,6 +84,7 @@ _sig = {
     "wal_unpack": (_I, [_P, _SZ, _P, _P, _P, _P, _P, _P, _P, _P]),
     "wal_workspace_size": (_I, [ctypes.POINTER(wal_info), _U32, ctypes.POINTER(_SZ)]),
     "wal_gemv": (_I, [ctypes.POINTER(wal_info), _P, _P, _I, _P, _P, _SZ, _P]),
+    "wal_gemv_noalloc": (_I, [ctypes.POINTER(wal_info), _P, _P, _I, _P, _P]),
     "wal_gemm_small": (_I, [ctypes.POINTER(wal_info), _P, _P, _I, _U32, _U32, _P, _U32, _I, _P, _SZ, _P]),
     "wal_prefill_workspace_size": (_I, [ctypes.POINTER(wal_info), _U32, ctypes.POINTER(_SZ)]),
     "wal_gemm_prefill": (_I, [ctypes.POINTER(wal_info), _P, _P, _I, _U32, _U32, _P, _U32, _P, _SZ, _P]),
@@ -317,6 +318,19 @@ def wal_gemv(info: wal_info, W, x, y, ws=None, stream=None):
     _gpu(W=W, x=x, y=y, ws=ws)
     st = _lib.wal_gemv(ctypes.byref(info), _ptr(W), _ptr(x), xdt, _ptr(y), _ptr(ws), wsb, _stream(stream))
     _check(st, "wal_gemv")
+    return y
+
+
+def wal_gemv_noalloc(info: wal_info, W, x, y, stream=None):
+    """y = W(x) as wal_gemv, with the library's per-device scratch as the
+    workspace (nothing is allocated; overlapping calls on one GPU race)."""
+    torch = _torch()
+    _dev_bytes(W, "W", int(info.total_bytes))
+    _act(x, "x", int(info.d.in_))
+    _dev(y, "y", (torch.float32,), int(info.d.out))
+    _gpu(W=W, x=x, y=y)
+    st = _lib.wal_gemv_noalloc(ctypes.byref(info), _ptr(W), _ptr(x), _xdtype(x), _ptr(y), _stream(stream))
+    _check(st, "wal_gemv_noalloc")
     return y
 
 

@@ -42,6 +42,7 @@
 
 #include <atomic>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "wal_device.h"
@@ -655,6 +656,37 @@ int plan_shape(uint32_t n, const wal_info* infos, uint32_t grid, int x_dtype, Pl
   return WAL_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free product (wal_gemv_noalloc): the workspace of
+// wal_gemv (low-rank partials, and per-pass partial sums of a wide matrix) in
+// a file-scope device array.  Each GPU the library runs on holds its own copy
+// until the process ends.  Host code never passes the array's name to a
+// kernel (on the host it names a stand-in, not device memory): the device
+// address comes from hipGetSymbolAddress, once per device, with that device
+// current.
+constexpr size_t kScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+static_assert(kScratchBytes == WAL_NOALLOC_SCRATCH_BYTES, "scratch size as declared in wal.h");
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array.
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return WAL_ERR_DEVICE;
+  if (dev < 0 || dev >= kMaxDevices) return WAL_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return WAL_ERR_DEVICE;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return WAL_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -706,6 +738,20 @@ int wal_gemv(const wal_info* info, const void* W_dev, const void* x_dev, int x_d
   hipLaunchKernelGGL(single_for(x_dtype, cls), dim3(nrb * (split ? npass : 1)), dim3(kThreads), 0, s, d, rpb, nrb, P);
   if ((st = launch_status()) || !split) return st;
   return launch_reduce_single(d, d.z, d.zc, P, npass, stream);
+}
+
+int wal_gemv_noalloc(const wal_info* info, const void* W_dev, const void* x_dev, int x_dtype, float* y_dev,
+                     void* stream) {
+  int st = check_info(info);
+  if (st) return st;
+  // The low-rank partials must fit; the per-pass partial sums of a wide
+  // matrix are used when they fit too (else its passes run in sequence
+  // inside each workgroup, as wal_gemv does with a short workspace).
+  const GemmShape S = gemm_shape(*info, 1);
+  if (info->d.n_paths && S.off_p > kScratchBytes) return WAL_ERR_BUFFER;
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws))) return st;
+  return wal_gemv(info, W_dev, x_dev, x_dtype, y_dev, ws, kScratchBytes, stream);
 }
 
 int wal_gemm_small(const wal_info* info, const void* W_dev, const void* X_dev, int x_dtype, uint32_t batch,
