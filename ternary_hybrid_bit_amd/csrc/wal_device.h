@@ -91,6 +91,19 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Hand-off of LDS data between the lanes of one wavefront: every lane's LDS
+// accesses before the call are ordered before every lane's accesses after
+// it.  The release and acquire fences keep the compiler from dropping or
+// moving the accesses (a lane reads what other lanes wrote, which its own
+// view of memory does not show); the wave barrier is the point every lane
+// reaches together.  One wavefront's LDS operations execute in issue order,
+// so this emits no instructions.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ uint32_t wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // ---------------------------------------------------------------------------

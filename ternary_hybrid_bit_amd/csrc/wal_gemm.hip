@@ -543,12 +543,12 @@ __device__ __forceinline__ void sweep_mfma(const uint8_t* xs, const SweepW<SL> (
           rt16[addr[r][j]] = (sb & 128u) ? 0xC000u : 0x4000u;
         }
       }
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      wave_lds_sync();
 #pragma unroll
       for (int r = 0; r < RT; ++r)
 #pragma unroll
         for (int m = 0; m < 4; ++m) ro[r][m] = reinterpret_cast<const uint4*>(rtile + 4096 * r)[m * 64 + lane];
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      wave_lds_sync();
 #pragma unroll
       for (int r = 0; r < RT; ++r) {
         uint16_t* rt16 = reinterpret_cast<uint16_t*>(rtile + 4096 * r);
@@ -644,7 +644,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void k_mfma(MatDev d, float* __res
   if constexpr (K > 0) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) reinterpret_cast<uint4*>(rtile)[m * 64 + lane] = make_uint4(0, 0, 0, 0);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    wave_lds_sync();
   }
 
   // Every load of the slice first: X of both sweeps (L2), then the weights
@@ -729,7 +729,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void k_prefill(MatDev d, Prefil
   if constexpr (K > 0) {
 #pragma unroll
     for (int m = 0; m < 4 * RT; ++m) reinterpret_cast<uint4*>(rtile)[m * 64 + lane] = make_uint4(0, 0, 0, 0);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    wave_lds_sync();
   }
 
   // Sweep s computes from xs[s & 1] while the X of sweep s + 1 (loaded during

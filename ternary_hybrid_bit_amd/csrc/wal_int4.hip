@@ -229,15 +229,13 @@ __device__ __forceinline__ Plan5<NR> plan5(uint32_t lane, uint32_t rowbytes, uin
 
 // Through the wavefront's LDS slice `sl` (NR * 160 chunks as 8-byte
 // halves): chunks in, then piece r's 40 bytes of this lane out.  The lanes
-// read what other lanes wrote, which a thread's own view of memory does not
-// show: without the wavefront-scope fences the compiler drops or sinks
-// writes that the writing thread never reads back itself, and could move the
-// next batch's writes above this batch's reads.  The fences emit no
-// instructions; the hardware performs one wavefront's LDS operations in
-// issue order.
+// read what other lanes wrote: a wave-level hand-off before the writes (the
+// previous batch's reads come first) and after them (every write lands
+// before the reads).  Without it the compiler dropped or sank writes that
+// the writing lane never reads back itself.
 template <int NR>
 __device__ __forceinline__ void stage5(u32x2_t* sl, const QBatch<5, NR>& B, uint32_t lane) {
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // the previous batch's reads come first
+  wave_lds_sync();   // the previous batch's reads come first
 #pragma unroll
   for (int k = 0; k < kI5Chunks<NR>; ++k)
     if ((NR * 160) % 64 == 0 || k + 1 < kI5Chunks<NR> || lane + 64 * k < NR * 160) {
@@ -245,7 +243,7 @@ __device__ __forceinline__ void stage5(u32x2_t* sl, const QBatch<5, NR>& B, uint
       sl[2 * (lane + 64 * k)] = u32x2_t{c[0], c[1]};
       sl[2 * (lane + 64 * k) + 1] = u32x2_t{c[2], c[3]};
     }
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // every write lands before the reads
+  wave_lds_sync();   // every write lands before the reads
 }
 
 __device__ __forceinline__ void unstage5(const u32x2_t* sl, int r, uint32_t lane, uint32_t (&w)[10]) {

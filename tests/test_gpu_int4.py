@@ -47,7 +47,8 @@ def run(wal, blob, V, inp, xbits):
     return y.cpu().numpy().astype(np.float64)
 
 
-@pytest.mark.parametrize("V,inp", [(1, 128), (7, 384), (1000, 4224), (4099, 4096), (300, 12288), (65, 5120), (9000, 4224)])
+@pytest.mark.parametrize("V,inp", [(1, 128), (7, 384), (1000, 4224), (4099, 4096), (300, 12288), (65, 5120), (9000, 4224),
+                                   (37, 3072), (29, 2176), (17, 8320), (9, 12416)])
 def test_shapes(wal, V, inp):
     q, s = make(V + inp, V, inp)
     blob = wal.wal_int4_pack(q, s)
@@ -64,7 +65,7 @@ def test_columns_exact_and_zero(wal):
     V, inp = 300, 4224
     q, s = make(1, V, inp)
     blob = wal.wal_int4_pack(q, s)
-    for j in (0, 1, 3, 4, 7, 63, 64, 127, 128, 4095, 4096, 4223):
+    for j in (0, 1, 3, 4, 7, 63, 64, 127, 128, 2047, 2048, 2049, 4095, 4096, 4223):
         e = np.zeros(inp, np.float32)
         e[j] = 1.0
         y = run(wal, blob, V, inp, synth.round_bf16_bits(e))
@@ -73,6 +74,19 @@ def test_columns_exact_and_zero(wal):
     x, bits = synth.make_x(351, 0, inp)
     assert not run(wal, z, V, inp, bits[0]).any()
 
+
+
+def test_columns_exact_partial_pass(wal):
+    """A width between 2048 and 4096 (one partial pass: lanes past the width
+    read zeros through out-of-range offsets): exact columns around 2048."""
+    V, inp = 45, 3072
+    q, s = make(4, V, inp)
+    blob = wal.wal_int4_pack(q, s)
+    for j in (0, 2047, 2048, 2049, 3071):
+        e = np.zeros(inp, np.float32)
+        e[j] = 1.0
+        y = run(wal, blob, V, inp, synth.round_bf16_bits(e))
+        assert np.array_equal(y, (s[:, j // 128].astype(np.float64) * q[:, j])), j
 
 def test_qwen3_8b_head_sampled(wal):
     """The 151936 x 4096 head at full size; sampled rows against the oracle."""

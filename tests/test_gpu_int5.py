@@ -48,7 +48,7 @@ def run(wal, blob, V, inp, xbits):
 
 
 @pytest.mark.parametrize("V,inp", [(1, 128), (7, 384), (1000, 4224), (4099, 4096), (300, 12288), (65, 5120), (9000, 4224),
-                                   (33, 8192)])
+                                   (33, 8192), (37, 3072), (29, 2176), (17, 8320), (9, 12416)])
 def test_shapes(wal, V, inp):
     q, s = make(V + inp, V, inp)
     blob = wal.wal_int5_pack(q, s)
@@ -66,7 +66,7 @@ def test_columns_exact_and_zero(wal):
     q, s = make(1, V, inp)
     q[:, :8] = np.array([-16, 15, -1, 0, 1, -8, 7, 8])   # the range's ends in the first pairs
     blob = wal.wal_int5_pack(q, s)
-    for j in (0, 1, 2, 3, 5, 6, 7, 12, 13, 63, 64, 127, 128, 4095, 4096, 4223):
+    for j in (0, 1, 2, 3, 5, 6, 7, 12, 13, 63, 64, 127, 128, 2047, 2048, 2049, 4095, 4096, 4223):
         e = np.zeros(inp, np.float32)
         e[j] = 1.0
         y = run(wal, blob, V, inp, synth.round_bf16_bits(e))
@@ -75,6 +75,19 @@ def test_columns_exact_and_zero(wal):
     x, bits = synth.make_x(356, 0, inp)
     assert not run(wal, z, V, inp, bits[0]).any()
 
+
+
+def test_columns_exact_partial_pass(wal):
+    """A width between 2048 and 4096 (one partial pass: lanes past the width
+    read zeros through out-of-range offsets): exact columns around 2048."""
+    V, inp = 45, 3072
+    q, s = make(4, V, inp)
+    blob = wal.wal_int5_pack(q, s)
+    for j in (0, 2047, 2048, 2049, 3071):
+        e = np.zeros(inp, np.float32)
+        e[j] = 1.0
+        y = run(wal, blob, V, inp, synth.round_bf16_bits(e))
+        assert np.array_equal(y, (s[:, j // 128].astype(np.float64) * q[:, j])), j
 
 def test_every_column_of_a_group(wal):
     """All 128 columns of one scale group (every bit offset of the 5-bit
