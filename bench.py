@@ -225,7 +225,7 @@ def run_single(args):
             Ws, keep = rotating_copies(torch, dev, blob)
             xt = to_x(bits[0])
             y = torch.empty(info.d.out, dtype=torch.float32, device=dev)
-            ws = torch.empty(max(wal.wal_workspace_size(info, 1), 4) // 4, dtype=torch.float32, device=dev)
+            ws = torch.zeros(max(wal.wal_workspace_size(info, 1), 4) // 4, dtype=torch.float32, device=dev)
             us = time_calls(torch, lambda i: wal.wal_gemv(info, Ws[i % len(Ws)], xt, y, ws), calls)
             gbs = info.algorithmic_bytes / (us * 1e-6) / 1e9
             extra = {}
@@ -262,7 +262,7 @@ def run_single(args):
     Ws, keep = rotating_copies(torch, dev, blob)
     X = to_x(bits)
     Y = torch.empty((32, info.d.out), dtype=torch.float32, device=dev)
-    ws = torch.empty(wal.wal_workspace_size(info, 32) // 4 + 64, dtype=torch.float32, device=dev)
+    ws = torch.zeros(wal.wal_workspace_size(info, 32) // 4 + 64, dtype=torch.float32, device=dev)
     rows = []
     for B in (1, 2, 3, 4, 5, 8, 16, 32):
         row = {"batch": B}

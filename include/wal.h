@@ -193,23 +193,47 @@ int wal_unpack(const void* blob, size_t bytes, int8_t* T, uint8_t* site_pos,
  * batch.  The WALB2 term sum_r U_r (V_r^T x) of the operator (WAL-Ternary-8B
  * cards, "Representation") needs every V_r^T x complete before U expands it,
  * so its partial sums live in device memory between the two steps; the
- * small-batch kernels also keep partial products there.  Contents: the
- * per-path reductions z_p = diag(s_p) V_p^T X per 4096-column
- * chunk [chunks][batch][n_paths * rank] and the small-batch kernels' partial
- * sums per 1024-column slice [ceil(in / 1024)][batch][out] (fp32), each part
- * padded to 256 bytes.  wal_gemv uses the first part only.
+ * small-batch kernels also keep partial products there.  Contents, each part
+ * padded to 256 bytes:
+ *   WAL_WS_ZERO_BYTES that must be zero before the workspace's first use
+ *     (hipMemset, torch.zeros) and that every call leaves zero, except the
+ *     u32 word WAL_SYNC_FALLBACK_WORD, a diagnostic count: a workgroup adds
+ *     one when its bounded wait for the low-rank terms gives up and it
+ *     computes them itself (outputs stay exact; the caller may read and
+ *     clear the word).  The region has the same size and place for every
+ *     blob, so one workspace serves products of any shape in turn.  It
+ *     holds WAL_SYNC_BYTES of synchronisation words (u32; the workgroups of
+ *     one launch coordinate through them, see wal_gemv), then one arrival
+ *     counter (u32) per row block of a split product, for up to
+ *     WAL_MAX_ROW_BLOCKS row blocks;
+ *   the per-path reductions z_p = diag(s_p) V_p^T X per 4096-column chunk
+ *     [chunks][batch][n_paths * rank] (fp32);
+ *   the small-batch kernels' partial sums per 1024-column slice
+ *     [ceil(in / 1024)][batch][out] (fp32).
+ * wal_gemv uses the last part only for matrices wider than one pass.
  * Errors: ARG, SHAPE, FORMAT. */
+#define WAL_SYNC_BYTES 4352
+#define WAL_SYNC_FALLBACK_WORD 0
+#define WAL_MAX_ROW_BLOCKS 4096
+#define WAL_WS_ZERO_BYTES (WAL_SYNC_BYTES + 4 * WAL_MAX_ROW_BLOCKS)
 int wal_workspace_size(const wal_info* info, uint32_t batch, size_t* bytes);
 
 /* y = W(x) for one matrix, batch 1 (WAL-Ternary-8B cards, "Representation":
- * the ternary-hybrid product with its binary low-rank paths): a low-rank
- * pre-pass (when the blob has paths) and one streaming launch.
+ * the ternary-hybrid product with its binary low-rank paths), one launch:
+ * its first workgroups compute the low-rank terms V^T x, the others stream
+ * the packed planes and wait for those terms (bounded, through the
+ * workspace's synchronisation words) only when they store their rows; a
+ * workgroup whose wait gives up computes the terms itself.  A matrix wider than one pass (4096 columns,
+ * 5120 for base-3 codes) has its passes in separate workgroups when the
+ * workspace is wal_workspace_size(info, 1) bytes; the workgroup that
+ * completes a row block adds its passes in pass order.
  *   info   host view of the blob (from wal_inspect / wal_pack)
  *   W_dev  the blob in device memory, 256-byte aligned
  *   x_dev  [in] activations, fp32 or bf16 (x_dtype), 16-byte aligned
  *   y_dev  [out] fp32 output, 4-byte aligned, overwritten
  *   ws_dev workspace of wal_workspace_size(info, 1) bytes, 16-byte aligned,
- *          disjoint from x and y (may be NULL for a blob without paths)
+ *          disjoint from x and y, its first WAL_WS_ZERO_BYTES zero before
+ *          its first use (may be NULL for a blob without paths)
  * Errors: ARG, SHAPE, ALIGN, BUFFER, UNSUPPORTED, DEVICE. */
 int wal_gemv(const wal_info* info, const void* W_dev, const void* x_dev, int x_dtype,
              float* y_dev, void* ws_dev, size_t ws_bytes, void* stream);
@@ -246,7 +270,8 @@ int wal_gemv_noalloc(const wal_info* info, const void* W_dev, const void* x_dev,
  *          base-3 codes run one wal_gemv per row with WAL_GEMM_VALU / AUTO,
  *          and WAL_GEMM_MFMA returns WAL_ERR_UNSUPPORTED for them.
  *   ws_dev wal_workspace_size(info, batch) bytes, 16-byte aligned, disjoint
- *          from X and Y; its contents on entry do not matter
+ *          from X and Y; its first WAL_WS_ZERO_BYTES zero before its first
+ *          use (the single-product path uses them), the rest need not be
  * Calls that share a workspace must be ordered (one stream).
  * Errors: ARG, SHAPE, ALIGN, BUFFER, UNSUPPORTED, DEVICE. */
 int wal_gemm_small(const wal_info* info, const void* W_dev, const void* X_dev, int x_dtype,
@@ -298,7 +323,15 @@ int wal_gemm_prefill(const wal_info* info, const void* W_dev, const void* X_dev,
  *      steps of planning are host-only), capped at one per 16 rows.
  *   2. The caller copies the plan blob into device memory (plan_dev, 16-byte
  *      aligned) and calls wal_gemv_grouped, as often as it likes while the
- *      pointers stay valid.
+ *      pointers stay valid.  The plan holds WAL_SYNC_BYTES of
+ *      synchronisation words at byte offset WAL_PLAN_SYNC_OFFSET, written as
+ *      zero by the planner: a call's first streaming launch computes the
+ *      low-rank terms in its first workgroups and the streaming workgroups
+ *      wait for them (bounded) only when they store their rows.  Every call
+ *      returns the words to zero, except the diagnostic count
+ *      WAL_SYNC_FALLBACK_WORD (workgroups whose wait gave up and which
+ *      computed the terms themselves; outputs stay exact).  Calls with one
+ *      plan must be ordered (one stream).
  * All matrices share x_dtype; base-3 matrices need bf16 activations
  * (WAL_ERR_UNSUPPORTED otherwise).  ws_dev must hold
  * wal_grouped_plan_size's ws_bytes.
@@ -312,13 +345,15 @@ int wal_grouped_plan(uint32_t n, const wal_info* infos, const void* const* W_dev
 int wal_gemv_grouped(const wal_grouped_info* ginfo, const void* plan_dev, void* stream);
 
 /* The two phases of wal_gemv_grouped, for callers that schedule or time them
- * apart: WAL_PHASE_LOWRANK launches the low-rank pre-pass (z_p of every
- * matrix into the workspace given to wal_grouped_plan), WAL_PHASE_STREAM the
- * streaming launches (one per class), which read those z_p; phases is a mask
- * of the two, and
- * the pre-pass of a call must precede its streaming phase on the stream.
+ * apart: WAL_PHASE_LOWRANK launches the low-rank pre-pass on its own (z_p of
+ * every matrix into the workspace given to wal_grouped_plan),
+ * WAL_PHASE_STREAM the streaming launches (one per class), which then read
+ * those z_p without waiting; the pre-pass of a call must precede its
+ * streaming phase on the stream.  WAL_PHASE_ALL is wal_gemv_grouped (the
+ * pre-pass inside the first streaming launch).
  * Errors: those of wal_gemv_grouped; ARG for an empty or unknown mask. */
 enum { WAL_PHASE_LOWRANK = 1, WAL_PHASE_STREAM = 2, WAL_PHASE_ALL = 3 };
+#define WAL_PLAN_SYNC_OFFSET 64
 int wal_gemv_grouped_phases(const wal_grouped_info* ginfo, const void* plan_dev, int phases,
                             void* stream);
 

@@ -25,6 +25,11 @@ WAL_PHASE_LOWRANK, WAL_PHASE_STREAM, WAL_PHASE_ALL = 1, 2, 3
 WAL_MAX_PATHS = 4
 WAL_MAX_BATCH = 32
 WAL_MAX_PREFILL_BATCH = 16384
+WAL_SYNC_BYTES = 4352
+WAL_MAX_ROW_BLOCKS = 4096
+WAL_WS_ZERO_BYTES = WAL_SYNC_BYTES + 4 * WAL_MAX_ROW_BLOCKS
+WAL_SYNC_FALLBACK_WORD = 0
+WAL_PLAN_SYNC_OFFSET = 64
 
 STATUS = {0: "WAL_OK", -1: "WAL_ERR_ARG", -2: "WAL_ERR_SHAPE", -3: "WAL_ERR_CODE",
           -4: "WAL_ERR_INEXACT", -5: "WAL_ERR_BUFFER", -6: "WAL_ERR_ALIGN", -7: "WAL_ERR_FORMAT",
@@ -224,6 +229,22 @@ def _ws_bytes(ws, name: str = "ws") -> int:
         return 0
     _dev_bytes(ws, name, 0)
     return ws.numel() * ws.element_size()
+
+
+def sync_fallbacks(buf, offset: int = 0) -> int:
+    """The fallback count of the synchronisation words at byte `offset` of a
+    device buffer (a workspace: 0; a device plan: WAL_PLAN_SYNC_OFFSET): the
+    workgroups of earlier calls whose bounded wait for the low-rank terms
+    gave up and which computed the terms themselves.  Synchronises the
+    device."""
+    words = buf.view(-1).view(_torch().uint8)[offset:offset + WAL_SYNC_BYTES].view(_torch().int32)
+    return int(words[WAL_SYNC_FALLBACK_WORD].item())
+
+
+def clear_sync_fallbacks(buf, offset: int = 0):
+    """Clears that count (on the current stream)."""
+    words = buf.view(-1).view(_torch().uint8)[offset:offset + WAL_SYNC_BYTES].view(_torch().int32)
+    words[WAL_SYNC_FALLBACK_WORD] = 0
 
 
 def wal_status_str(status: int) -> str:

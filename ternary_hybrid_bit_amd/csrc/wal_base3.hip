@@ -172,7 +172,6 @@ struct Raw3 {
 template <int RB>
 struct Batch3 {
   Raw3 r[RB];
-  uint32_t u;
 };
 
 // The activations of a thread's share of one pass's signed site table
@@ -226,9 +225,9 @@ __device__ __forceinline__ void build_lut(uint32_t* lut) {
 
 // ZP: low-rank partials prefetched per term; lut: the workgroup's first pass,
 // which also fills the byte table.
-template <int SF, int K, int ZP>
+template <int SF, int K>
 __device__ __forceinline__ void stream_rows_base3(const MatDev& d, uint32_t row0, uint32_t row1, uint32_t pass,
-                                                  uint32_t npass, bool lut_first, bool partial, Smem3& sm) {
+                                                  bool first, bool lut_first, Smem3& sm) {
   constexpr int RB = kRB3;
   constexpr int LOG = ilog2(RB);
   constexpr int SH = 6 - LOG;
@@ -242,9 +241,8 @@ __device__ __forceinline__ void stream_rows_base3(const MatDev& d, uint32_t row0
 
   const uint32_t pw = min(kPassBase3, d.in - pass * kPassBase3);   // trits of this pass
   const uint32_t Gp = (pw + 127) / 128, g0 = pass * kGroups3, G = d.groups;
-  // first: y starts here; last: the low-rank term is added here (a partial
-  // pass, one pass written on its own: first, without the low-rank term)
-  const bool first = partial || pass == 0, last = !partial && pass + 1 == npass;
+  // first: y starts here (the low-rank term is added after the segment's
+  // last pass, by store_segment)
   const uint32_t ncols = 80 * (uint32_t)lane < pw ? min(80u, pw - 80 * lane) : 0u;
 
   // codes
@@ -276,19 +274,6 @@ __device__ __forceinline__ void stream_rows_base3(const MatDev& d, uint32_t row0
   const float w16 = split && cls == 3 ? 1.f : 0.f, w32 = split && cls == 6 ? 1.f : 0.f;
   const float w48 = split && cls == 1 ? 1.f : 0.f, w64 = split && cls == 4 ? 1.f : 0.f;
   const float wT = split ? 0.f : 1.f;
-  // low rank
-  const uint32_t ti = lane & (LPR - 1);
-  const bool uon = last && ti < d.terms;
-  const uint32_t ub = (d.rank + 7) / 8;
-  const uint8_t* up = d.codes;
-  uint32_t ubit = 0;
-  if (uon) {
-    const uint32_t p = ti / d.rank, r = ti % d.rank;
-    up = path_plane(d.U, d, p) + r / 8;
-    ubit = r & 7;
-  }
-  const bool ulive = last && d.terms;
-  const uint32_t uoff = (uint32_t)(up - d.codes), ustride = uon ? ub : 0;
   const uint32_t* lut = sm.lut + (lane & (kLutCopies - 1));
 
   XLane3 xl;
@@ -300,7 +285,6 @@ __device__ __forceinline__ void stream_rows_base3(const MatDev& d, uint32_t row0
     Batch3<RB> B;
     const bool live = bb < nb;
     const __amdgpu_buffer_rsrc_t rw = live ? rw_ : r_none;
-    const __amdgpu_buffer_rsrc_t ru = live && ulive ? rw_ : r_none;
     const uint32_t base = row0 + (live ? bb : nb - 1) * RB;
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
@@ -329,8 +313,6 @@ __device__ __forceinline__ void stream_rows_base3(const MatDev& d, uint32_t row0
         if constexpr (K == 2) { r.s[0] = __builtin_amdgcn_raw_buffer_load_b16(rw, vs, row * G * K, kStream); r.s[1] = 0; }
       }
     }
-    const uint32_t ry = min(base + ((uint32_t)lane >> SH), row1 - 1);
-    B.u = __builtin_amdgcn_raw_buffer_load_b8(ru, uoff + ry * ustride, 0, kStream);
     __builtin_amdgcn_sched_barrier(0);
     return B;
   };
@@ -362,41 +344,22 @@ __device__ __forceinline__ void stream_rows_base3(const MatDev& d, uint32_t row0
     const uint32_t yi = bb * RB + ((uint32_t)lane >> SH);
     if (!first) v = sm.ybuf[yi] + v;
     const uint32_t row = row0 + yi;
-    if (last && d.terms) {
-      float c = 0.f;
-      if (uon) {
-        const float zt = sm.z[ti];
-        c = ((B.u >> ubit) & 1u) ? -zt : zt;
-      }
-      const uint32_t ry = min(row, row1 - 1);
-      for (uint32_t t = ti + LPR; t < d.terms; t += LPR) {
-        const uint32_t p = t / d.rank, r = t % d.rank;
-        const uint32_t byte = path_plane(d.U, d, p)[(size_t)ry * ub + r / 8];
-        const float zt = sm.z[t];
-        c += ((byte >> (r & 7)) & 1u) ? -zt : zt;
-      }
-      v += group_sum<LPR>(c);
-    }
     if ((lane & (LPR - 1)) == 0 && row < row1) sm.ybuf[yi] = v;
   };
 
-  // Set-up loads first (L2 hits: x, the table's x, the low-rank partials),
-  // then the first two batches (HBM): loads complete in order, so waiting
-  // for the set-up data does not wait for the batches.
+  // Set-up loads first (L2 hits: x, the table's x), then the first two
+  // batches (HBM): loads complete in order, so waiting for the set-up data
+  // does not wait for the batches.
   const __amdgpu_buffer_rsrc_t rx = x_rsrc<WAL_X_BF16>(d.x, d.in);
   XLane3::Raw xr;
   XLane3::load_raw(rx, pass * kPassBase3 + 80 * lane, xr);
   TableX3 tx;
   if constexpr (K > 0) tx.load(rx, pass * kPassBase3);
-  const bool zpass = !partial && pass == 0 && d.terms;
-  ZPart<ZP> zp;
-  if (zpass) z_prefetch<ZP>(d, threadIdx.x, zp);
   Batch3<RB> B0 = load_batch(b);
   Batch3<RB> B1 = load_batch(b + kWaves);
 
-  __syncthreads();   // readers of the previous table and z are done
+  __syncthreads();   // readers of the previous table are done
   if (lut_first) build_lut(sm.lut);
-  if (zpass && threadIdx.x < d.terms) sm.z[threadIdx.x] = z_total<ZP>(d, threadIdx.x, zp);
   if constexpr (K > 0) tx.store(sm.tbl);
   __syncthreads();
   if (!has_rows) return;
@@ -418,44 +381,75 @@ __device__ __forceinline__ void stream_rows_base3(const MatDev& d, uint32_t row0
   }
 }
 
-// With P, only pass `split_pass`, written to P[split_pass][row] without the
-// low-rank term (a reduce adds the passes and that term).
-template <int SF, int K, int ZP>
+// One segment, pass by pass, then its store (store_segment: the low-rank
+// term, or with P one pass's partial sums and the reduce of a completed row
+// block).
+template <int SF, int K, class ZJ>
 __device__ __forceinline__ void run_segment_base3(const MatDev& d, uint32_t row0, uint32_t row1, bool lut_first,
-                                                  Smem3& sm, float* P = nullptr, uint32_t split_pass = 0) {
+                                                  Smem3& sm, const Fuse& f, float* P = nullptr,
+                                                  uint32_t split_pass = 0, uint32_t* cnt = nullptr) {
   const uint32_t npass = (d.in + kPassBase3 - 1) / kPassBase3;
-  const bool partial = P != nullptr;
-  const uint32_t p0 = partial ? split_pass : 0, p1 = partial ? split_pass + 1 : npass;
+  const bool split = P != nullptr;
+  const uint32_t p0 = split ? split_pass : 0, p1 = split ? split_pass + 1 : npass;
   for (uint32_t pass = p0; pass < p1; ++pass)
-    stream_rows_base3<SF, K, ZP>(d, row0, row1, pass, npass, lut_first && pass == p0, partial, sm);
-  __syncthreads();
-  const uint32_t nrows = row1 - row0;
-  float* dst = partial ? P + (size_t)split_pass * d.out : d.y;
-  for (uint32_t i = threadIdx.x; i < nrows; i += kThreads) dst[row0 + i] = sm.ybuf[i];
+    stream_rows_base3<SF, K>(d, row0, row1, pass, pass == p0, lut_first && pass == p0, sm);
+  store_segment<WAL_X_BF16, ZJ>(d, row0, row1, SegEnd{sm.tbl, sm.z, sm.ybuf}, f, P, split_pass, npass, cnt);
+}
+
+// Low-rank jobs of grouped plans and single products, as in the 2-bit
+// kernels (bf16 activations).
+__device__ __forceinline__ void z_job_grouped3(const MatDev* __restrict__ descs, const uint32_t* __restrict__ jobs,
+                                               uint32_t j) {
+  const uint32_t m = jobs[2 * j], tc = jobs[2 * j + 1];
+  const MatDev& d = descs[m];
+  const uint32_t t0 = tc >> 16, cc = tc & 0xFFFFu;
+  const uint32_t c0 = cc * kZChunkCols, c1 = min(d.in, c0 + kZChunkCols);
+  z_chunk<WAL_X_BF16, (int)kZTermsGrouped>(d, d.x, t0, d.z + (size_t)cc * d.terms, c0, c1);
 }
 
 template <int SF, int K>
 __global__ __launch_bounds__(kThreads) void k_stream3_grouped(const MatDev* __restrict__ descs,
                                                               const uint32_t* __restrict__ blockseg,
-                                                              const Seg* __restrict__ segs) {
+                                                              const Seg* __restrict__ segs,
+                                                              const uint32_t* __restrict__ jobs, Fuse f) {
   __shared__ Smem3 sm;
-  const uint32_t s0 = blockseg[blockIdx.x], s1 = blockseg[blockIdx.x + 1];
-  for (uint32_t s = s0; s < s1; ++s) {
-    const Seg sg = segs[s];
-    run_segment_base3<SF, K, kZSinglePrefetch>(descs[sg.mat], sg.row0, sg.row1, s == s0, sm);
+  const uint32_t t = blockIdx.x;
+  if (t < f.nz) {
+    z_job_grouped3(descs, jobs, t);
+    publish_z(f);
+  } else {
+    const uint32_t b = t - f.nz;
+    const uint32_t s0 = blockseg[b], s1 = blockseg[b + 1];
+    for (uint32_t s = s0; s < s1; ++s) {
+      const Seg sg = segs[s];
+      run_segment_base3<SF, K, ZJobsGrouped>(descs[sg.mat], sg.row0, sg.row1, s == s0, sm, f);
+    }
   }
+  finish_launch(f);
 }
 
 template <int SF, int K>
 __global__ __launch_bounds__(kThreads) void k_stream3_single(MatDev d, uint32_t rows_per_block, uint32_t nrb,
-                                                             float* P) {
-  // without P: block b takes rows [b rpb, b rpb + rpb) over every pass; with
-  // P: block b takes pass b / nrb of row block b % nrb
+                                                             float* P, uint32_t* cnt, Fuse f) {
+  // block t < f.nz: low-rank job t; else without P block b takes rows
+  // [b rpb, b rpb + rpb) over every pass, with P pass b / nrb of row block
+  // b % nrb
   __shared__ Smem3 sm;
-  const uint32_t rb = P ? blockIdx.x % nrb : blockIdx.x;
-  const uint32_t r0 = rb * rows_per_block;
-  const uint32_t r1 = min(d.out, r0 + rows_per_block);
-  if (r0 < r1) run_segment_base3<SF, K, kZSinglePrefetch>(d, r0, r1, true, sm, P, P ? blockIdx.x / nrb : 0u);
+  const uint32_t t = blockIdx.x;
+  if (t < f.nz) {
+    const uint32_t tcs = (d.terms + kZTerms - 1) / kZTerms, tc = t % tcs, cc = t / tcs;
+    const uint32_t c0 = cc * kZSingleCols, c1 = min(d.in, c0 + kZSingleCols);
+    z_chunk<WAL_X_BF16, (int)kZTerms>(d, d.x, tc * kZTerms, d.z + (size_t)cc * d.terms, c0, c1);
+    publish_z(f);
+  } else {
+    const uint32_t b = t - f.nz;
+    const uint32_t rb = P ? b % nrb : b;
+    const uint32_t r0 = rb * rows_per_block;
+    const uint32_t r1 = min(d.out, r0 + rows_per_block);
+    if (r0 < r1)
+      run_segment_base3<SF, K, ZJobsSingle>(d, r0, r1, true, sm, f, P, P ? b / nrb : 0u, P ? cnt + rb : nullptr);
+  }
+  finish_launch(f);
 }
 
 }  // namespace

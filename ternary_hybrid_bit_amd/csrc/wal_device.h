@@ -177,12 +177,33 @@ __device__ __forceinline__ float f16_at(const uint8_t* p, uint32_t i) {
 }
 
 // ---------------------------------------------------------------------------
+// Data that workgroups of one launch hand to each other (low-rank partials,
+// per-pass partial sums) moves through device-scope (agent) atomic stores
+// and loads: on this part they go to the device's coherence point, past the
+// CU and XCD caches, so a consumer that has seen the producer's count sees
+// the data without cache maintenance.  The producer's wave waits for its own
+// stores to complete (wait_stores) before the count is raised; agent-scope
+// release and acquire fences would instead write back or invalidate the
+// whole L2 of an XCD, which costs microseconds per workgroup here.
+__device__ __forceinline__ void store_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_dev(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// s_waitcnt vmcnt(0): the wave's vector memory operations, stores included,
+// have completed.
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// ---------------------------------------------------------------------------
 // Low-rank reductions of one matrix by a whole workgroup:
 // z[t] = s_p[r] * sum_j (-1)^{V_p[r] bit j} x_j over the columns j in
 // [c0, c1) (multiples of 16) for the C terms t0 .. t0 + C - 1 (those below
-// d.terms), written to out[t] by threads t - t0.  Every thread of the
+// d.terms), written to out[t] by threads t - t0: with device-scope stores
+// (see store_dev) for device memory that other workgroups of the same
+// launch read, plain stores for LDS (LDS_OUT).  Every thread of the
 // workgroup (up to 1024) calls it (it holds a barrier).
-template <int XT, int C>
+template <int XT, int C, bool LDS_OUT = false>
 __device__ __forceinline__ void z_chunk(const MatDev& d, const void* x, uint32_t t0, float* out, uint32_t c0,
                                         uint32_t c1) {
   __shared__ float red[16][C];
@@ -254,41 +275,288 @@ __device__ __forceinline__ void z_chunk(const MatDev& d, const void* x, uint32_t
     if (t < T) {
       float sum = 0.f;
       for (uint32_t w = 0; w < (nthr >> 6); ++w) sum += red[w][tid];
-      out[t] = (float)__builtin_bit_cast(_Float16, (uint16_t)scale_bits) * sum;
+      const float v = (float)__builtin_bit_cast(_Float16, (uint16_t)scale_bits) * sum;
+      if constexpr (LDS_OUT) out[t] = v;
+      else store_dev(out + t, v);
     }
   }
 }
 
-// The low-rank reductions a streaming workgroup needs, z[t] for t < d.terms,
-// are the sums of d.zc partials (one per column chunk).  A thread first issues
-// the loads of up to ZP partials of its term (prefetch) and adds them later
-// (total), so the loads overlap other memory latency.
-template <int ZP>
-struct ZPart {
-  float v[ZP];
+// ---------------------------------------------------------------------------
+// Fused launches: the low-rank pre-pass in the first workgroups of the
+// streaming launch (see Fuse in wal_internal.h).  Producers write their jobs'
+// partials with device-scope stores and count them once the stores have
+// completed; consumers wait for all of them, only in their epilogue after
+// their streaming, with polls, and then read the partials with device-scope
+// loads.  Each word that the whole launch touches is read and written
+// through the workgroup's copy (blockIdx.x % kSyncReplicas).
+
+constexpr uint32_t kSpinLimit = 1u << 16;   // polls of a bounded wait (tens of ms)
+
+// Low-rank jobs as the producers of a launch run them: C terms of one
+// column chunk of `cols` columns each.  The fallback of a consumer whose
+// wait gave up runs the same jobs, so its terms are bit-identical.
+template <int C, uint32_t COLS>
+struct ZJobs {
+  static constexpr int kTerms = C;
+  static constexpr uint32_t kCols = COLS;
+};
+using ZJobsSingle = ZJobs<(int)kZTerms, kZSingleCols>;
+using ZJobsGrouped = ZJobs<(int)kZTermsGrouped, kZChunkCols>;
+
+__device__ __forceinline__ uint32_t* sync_copy(const Fuse& f, uint32_t word) {
+  return f.sync + word + kSyncLine * (blockIdx.x % kSyncReplicas);
+}
+
+// A finished low-rank job (device-scope stores by any thread of the
+// workgroup) becomes visible to the consumers: every wave waits for its own
+// stores before the barrier, then one lane per copy counts the job.  Every
+// thread calls it.
+__device__ __forceinline__ void publish_z(const Fuse& f) {
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x < kSyncReplicas)
+    __hip_atomic_fetch_add(f.sync + kSyncZDone + kSyncLine * threadIdx.x, 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Waits until every low-rank job of the call is published; true when they
+// are (then device-scope loads of the terms see them: the loads follow the
+// poll that saw the count).
+// Bounded: on expiry the fallback count is raised and false returned, and
+// so at once for the later waiters of a call in which a wait expired (the
+// gave-up word, which the call's last workgroup clears).  Every thread
+// calls it.
+__device__ __forceinline__ uint32_t poll_z(const Fuse& f) {
+  return __hip_atomic_load(sync_copy(f, kSyncZDone), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// `seen`: thread 0's first poll (poll_z), issued early by the caller so that
+// its latency overlaps other loads.
+__device__ __forceinline__ bool wait_z(const Fuse& f, uint32_t seen) {
+  if (!f.zwait) return true;
+  __shared__ uint32_t s_ok;
+  if (threadIdx.x == 0) {
+    uint32_t n = 0, ok = 1;
+    for (; seen != f.zwait; seen = poll_z(f)) {
+      if (__hip_atomic_load(f.sync + kSyncGaveUp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) || ++n == kSpinLimit) {
+        __hip_atomic_store(f.sync + kSyncGaveUp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(f.sync + kSyncFallback, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ok = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    s_ok = ok;
+  }
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(s_ok) != 0;
+}
+
+// The last workgroup of the launch to finish returns its slot's words (and
+// the jobs-published copies and the gave-up word, after the call's last
+// launch) to zero.  Copy r
+// counts the workgroups b % kSyncReplicas == r; the one that completes a
+// copy counts it in line 0, and the one that completes the last copy resets.
+// No data changes hands here: the counts order nothing but the reset.
+// Every thread calls it.
+__device__ __forceinline__ void finish_launch(const Fuse& f) {
+  if (!f.sync) return;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t r = blockIdx.x % kSyncReplicas;
+    const uint32_t members = (f.grid - r + kSyncReplicas - 1) / kSyncReplicas;
+    const uint32_t copies = min(f.grid, kSyncReplicas);
+    const uint32_t done = __hip_atomic_fetch_add(sync_copy(f, kSyncFinished + f.slot), 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    if (done + 1 == members &&
+        __hip_atomic_fetch_add(f.sync + kSyncSlotsDone + f.slot, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1 ==
+            copies) {
+      for (uint32_t c = 0; c < copies; ++c)
+        __hip_atomic_store(f.sync + kSyncFinished + kSyncLine * c + f.slot, 0u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(f.sync + kSyncSlotsDone + f.slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (f.reset_z) {
+        for (uint32_t c = 0; c < kSyncReplicas; ++c)
+          __hip_atomic_store(f.sync + kSyncZDone + kSyncLine * c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(f.sync + kSyncGaveUp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The end of a streaming segment: ybuf[i] holds the product of row row0 + i
+// over every pass, without the low-rank term.
+//
+// Low-rank term: U_p's byte b of a row holds the signs of terms 8 b .. 8 b
+// + 7 of path p, so the row's term is sum over (p, b) of T_pb[byte], with
+// table T_pb[u] = sum_k (bit k of u ? -z : +z)[p, 8 b + k].  The tables (one
+// per path and U byte, 256 floats each) are built in `tbl` (the site table,
+// free by then) from z, the sum of the d.zc low-rank partials in chunk order;
+// each row then adds one entry per U byte, in (p, b) order.  Every sum runs in
+// a fixed order.
+struct SegEnd {
+  float* tbl;    // >= n_paths * ceil(rank / 8) * 256 floats of LDS
+  float* z;      // >= terms floats of LDS
+  float* ybuf;   // LDS, the segment's rows
 };
 
-// Only when d.terms > 0.  Threads past the last term load the last term's
-// partials (unused) rather than branch.
-template <int ZP>
-__device__ __forceinline__ void z_prefetch(const MatDev& d, uint32_t t, ZPart<ZP>& zp) {
-  const uint32_t tt = t < d.terms ? t : d.terms - 1;
-  const __amdgpu_buffer_rsrc_t rz = rsrc(d.z, 4 * d.zc * d.terms);
-#pragma unroll
-  for (int cc = 0; cc < ZP; ++cc)
-    zp.v[cc] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rz, 4 * (cc * d.terms + tt), 0, 0));
+// z = the sum of the low-rank partials in chunk order, from the workspace, or
+// (after a wait that gave up) computed here by the producers' jobs, chunk by
+// chunk, each chunk's partials staged in tbl.  Every thread calls it
+// (barriers).
+template <int XT, class ZJ>
+__device__ __forceinline__ void lowrank_z(const MatDev& d, const SegEnd& e, const Fuse& f, uint32_t seen) {
+  const uint32_t t = threadIdx.x;
+  if (wait_z(f, seen)) {
+    if (t < d.terms) {
+      float z = 0.f;
+      for (uint32_t cc = 0; cc < d.zc; ++cc) z += load_dev(d.z + cc * d.terms + t);
+      e.z[t] = z;
+    }
+    return;
+  }
+  float z = 0.f;
+  for (uint32_t cc = 0; cc < d.zc; ++cc) {
+    const uint32_t c0 = cc * ZJ::kCols, c1 = min(d.in, c0 + ZJ::kCols);
+    for (uint32_t t0 = 0; t0 < d.terms; t0 += ZJ::kTerms) {
+      z_chunk<XT, ZJ::kTerms, true>(d, d.x, t0, e.tbl, c0, c1);
+      __syncthreads();   // z_chunk's reduction buffer is read before the next job writes it
+    }
+    if (t < d.terms) z += e.tbl[t];
+    __syncthreads();
+  }
+  if (t < d.terms) e.z[t] = z;
 }
 
-// Partials in chunk order (a fixed order: results do not depend on timing).
-// Chunks past d.zc read as zero (out of the resource's range).
-template <int ZP>
-__device__ __forceinline__ float z_total(const MatDev& d, uint32_t t, const ZPart<ZP>& zp) {
-  float z = zp.v[0];
-#pragma unroll
-  for (int cc = 1; cc < ZP; ++cc) z += zp.v[cc];
-  for (uint32_t cc = ZP; cc < d.zc; ++cc) z += d.z[cc * d.terms + t];
-  return z;
+// Builds the byte tables (after the low-rank terms are complete).  Every
+// thread calls it (barriers).
+template <int XT, class ZJ>
+__device__ __forceinline__ void lowrank_tables(const MatDev& d, const SegEnd& e, const Fuse& f, uint32_t seen) {
+  lowrank_z<XT, ZJ>(d, e, f, seen);
+  __syncthreads();
+  const uint32_t t = threadIdx.x;
+  const uint32_t ub = (d.rank + 7) / 8, ntab = d.n_paths * ub;
+  for (uint32_t i = t; i < ntab * 256; i += blockDim.x) {
+    const uint32_t tab = i >> 8, u = i & 255u, p = tab / ub, b = tab % ub;
+    float sum = 0.f;
+    for (uint32_t k = 0; k < 8 && 8 * b + k < d.rank; ++k) {
+      const float zt = e.z[p * d.rank + 8 * b + k];
+      sum += ((u >> k) & 1u) ? -zt : zt;
+    }
+    e.tbl[i] = sum;
+  }
+  __syncthreads();
 }
 
+// The U bytes of one row, loaded ahead of the tables: per path the eight
+// bytes from the dword holding the row's first U byte (a row's ub <= 4 U
+// bytes per path then lie inside them).  Reads past the blob return zero.
+struct UAhead {
+  uint64_t w[WAL_MAX_PATHS];
+  uint32_t sh;   // bit offset of the row's first byte in each window
+};
+
+__device__ __forceinline__ bool u_ahead_fits(const MatDev& d) { return d.rank <= 32; }
+
+__device__ __forceinline__ UAhead load_u_ahead(const MatDev& d, __amdgpu_buffer_rsrc_t ru, uint32_t row) {
+  const uint32_t ub = (d.rank + 7) / 8, o = (uint32_t)(d.U - d.codes) + row * ub;
+  UAhead u;
+  u.sh = 8 * (o & 3u);
+#pragma unroll
+  for (uint32_t p = 0; p < WAL_MAX_PATHS; ++p) {
+    const uint32_t a = (o & ~3u) + p * d.pstride;
+    const uint32_t lo = p < d.n_paths ? __builtin_amdgcn_raw_buffer_load_b32(ru, a, 0, 0) : 0u;
+    const uint32_t hi = p < d.n_paths ? __builtin_amdgcn_raw_buffer_load_b32(ru, a + 4, 0, 0) : 0u;
+    u.w[p] = ((uint64_t)hi << 32) | lo;
+  }
+  return u;
+}
+
+// Low-rank term of a row from the byte tables and its U bytes loaded ahead.
+__device__ __forceinline__ float lowrank_row_ahead(const MatDev& d, const SegEnd& e, const UAhead& u) {
+  const uint32_t ub = (d.rank + 7) / 8;
+  float c = 0.f;
+#pragma unroll
+  for (uint32_t p = 0; p < WAL_MAX_PATHS; ++p) {
+    if (p < d.n_paths) {
+      const uint64_t w = u.w[p] >> u.sh;
+      for (uint32_t b = 0; b < ub; ++b) c += e.tbl[(p * ub + b) * 256 + ((uint32_t)(w >> (8 * b)) & 255u)];
+    }
+  }
+  return c;
+}
+
+// Low-rank term of one row from the byte tables.
+__device__ __forceinline__ float lowrank_row(const MatDev& d, const SegEnd& e, __amdgpu_buffer_rsrc_t ru, uint32_t row) {
+  const uint32_t ub = (d.rank + 7) / 8, u0 = (uint32_t)(d.U - d.codes);
+  float c = 0.f;
+  for (uint32_t p = 0; p < d.n_paths; ++p)
+    for (uint32_t b = 0; b < ub; ++b) {
+      const uint32_t u = __builtin_amdgcn_raw_buffer_load_b8(ru, u0 + p * d.pstride + row * ub + b, 0, 0);
+      c += e.tbl[(p * ub + b) * 256 + u];
+    }
+  return c;
+}
+
+// Stores the segment: y = ybuf (+ the low-rank term when the matrix has
+// paths).  With P (a split product: this workgroup computed one pass of the
+// rows), the partial sums go to P[pass] instead; the workgroup that completes
+// a row block (cnt[rb] counts the passes stored) adds all npass planes in
+// pass order with the low-rank term and stores y, and returns cnt[rb] to
+// zero.  Every thread calls it (barriers).
+template <int XT, class ZJ>
+__device__ __forceinline__ void store_segment(const MatDev& d, uint32_t row0, uint32_t row1, const SegEnd& e,
+                                              const Fuse& f, float* P = nullptr, uint32_t pass = 0,
+                                              uint32_t npass = 1, uint32_t* cnt = nullptr) {
+  __syncthreads();   // the segment's y is complete; the site table's readers are done
+  const uint32_t nrows = row1 - row0;
+  const __amdgpu_buffer_rsrc_t ru = rsrc(d.codes, d.blob_bytes);
+  if (P) {
+    for (uint32_t i = threadIdx.x; i < nrows; i += blockDim.x) store_dev(P + (size_t)pass * d.out + row0 + i, e.ybuf[i]);
+    wait_stores();   // each wave's partial sums, before the count
+    __syncthreads();
+    __shared__ uint32_t s_last;
+    if (threadIdx.x == 0) {
+      const uint32_t arrived = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = arrived + 1 == npass;
+      if (s_last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!__builtin_amdgcn_readfirstlane(s_last)) return;   // not the row block's last pass
+    if (!d.terms) {
+      for (uint32_t i = threadIdx.x; i < nrows; i += blockDim.x) {
+        const uint32_t row = row0 + i;
+        float v = load_dev(P + row);
+        for (uint32_t q = 1; q < npass; ++q) v += load_dev(P + (size_t)q * d.out + row);
+        d.y[row] = v;
+      }
+      return;
+    }
+  } else if (!d.terms) {
+    for (uint32_t i = threadIdx.x; i < nrows; i += blockDim.x) d.y[row0 + i] = e.ybuf[i];
+    return;
+  }
+  // The low-rank term.  Thread 0's first poll of the jobs-published count
+  // and every thread's U bytes for its first row go out together, so their
+  // latencies overlap.
+  const uint32_t seen = f.zwait && threadIdx.x == 0 ? poll_z(f) : 0u;
+  const bool ahead = u_ahead_fits(d);
+  const uint32_t i0 = threadIdx.x;
+  const UAhead ua = load_u_ahead(d, ru, row0 + min(i0, nrows - 1));
+  lowrank_tables<XT, ZJ>(d, e, f, seen);
+  for (uint32_t i = i0; i < nrows; i += blockDim.x) {
+    const uint32_t row = row0 + i;
+    float v;
+    if (P) {
+      v = load_dev(P + row);
+      for (uint32_t q = 1; q < npass; ++q) v += load_dev(P + (size_t)q * d.out + row);
+    } else {
+      v = e.ybuf[i];
+    }
+    d.y[row] = v + (ahead && i == i0 ? lowrank_row_ahead(d, e, ua) : lowrank_row(d, e, ru, row));
+  }
+}
 
 }  // namespace

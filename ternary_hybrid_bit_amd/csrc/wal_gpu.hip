@@ -38,6 +38,8 @@
 //        term sum_t (-1)^{U bit} z_t (one term per lane) and one of them
 //        stores y.  Matrices wider than one pass accumulate y pass by pass.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <hip/hip_fp16.h>
 
 #include <atomic>
@@ -215,7 +217,6 @@ struct RowRaw {
 template <int RB>
 struct Batch {
   RowRaw r[RB];
-  uint32_t u;       // U byte holding this lane's low-rank sign bit
 };
 
 // Per-pass lane constants of the 2-bit stream.
@@ -224,19 +225,16 @@ struct Lane2 {
   uint32_t vc, vs, va, vb;    // lane offsets (from the codes plane) in row 0 of each plane
   uint32_t sc, ss, sa;        // row strides (bytes) of each plane
   const float* tb;            // the lane's group in the site table
-  const uint8_t* up;          // U byte of the lane's first low-rank term (row 0)
-  uint32_t ub, ubit;          // bytes per U row, bit of the term in its byte
-  bool uon;                   // the lane owns a low-rank term
 };
 
-// One pass of one segment.  The workgroup-wide set-up of the pass (site table,
-// low-rank terms, behind barriers) runs after each wave has issued the loads
-// of its first batch and of its x columns, so the set-up overlaps the
-// memory latency instead of adding to it.  Every wave reaches both barriers.
-// ZP: low-rank partials (column chunks) prefetched per term.
-template <int XT, int SF, int K, int RB, int ZP>
+// One pass of one segment.  The workgroup-wide set-up of the pass (the site
+// table, behind barriers) runs after each wave has issued the loads of its
+// first batch and of its x columns, so the set-up overlaps the memory
+// latency instead of adding to it.  Every wave reaches both barriers.  The
+// low-rank term is added after the segment's last pass (store_segment).
+template <int XT, int SF, int K, int RB>
 __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0, uint32_t row1, uint32_t pass,
-                                                 uint32_t npass, bool split, StreamSmem& sm) {
+                                                 bool first, StreamSmem& sm) {
   constexpr int LOG = ilog2(RB);
   constexpr int SH = 6 - LOG;        // lane >> SH = row of the batch after the reduction
   constexpr int LPR = 64 >> LOG;     // lanes per row after the reduction
@@ -251,11 +249,6 @@ __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0,
   const uint32_t Gp = pw / 128, g0 = pass * (kPass2bit / 128), G = d.groups;
   const bool on = (uint32_t)lane < 2 * Gp;
   const uint32_t gl = on ? (uint32_t)lane >> 1 : 0;
-  // first: y starts here (no earlier pass in LDS); last: the low-rank term is
-  // added here.  A split pass (one pass of a row range, written as a partial
-  // sum) is both first and without the low-rank term.
-  const bool first = split || pass == 0, last = !split && pass + 1 == npass;
-
   // One resource over the blob; the plane offsets go into the per-lane
   // offsets (the planes are 256-byte aligned, so alignments carry over).
   Lane2 L;
@@ -270,23 +263,6 @@ __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0,
     L.ss = G * K;
   }
   L.tb = sm.tbl + ((uint32_t)lane >> 1) * 256;
-  const uint32_t ti = lane & (LPR - 1);
-  L.uon = last && ti < d.terms;
-  L.ub = (d.rank + 7) / 8;
-  L.up = d.codes;    // any readable byte for lanes without a low-rank term
-  L.ubit = 0;
-  if (L.uon) {
-    const uint32_t p = ti / d.rank, r = ti % d.rank;
-    L.up = path_plane(d.U, d, p) + r / 8;
-    L.ubit = r & 7;
-  }
-  // The U bytes go through buffer instructions too (a generic pointer would
-  // need flat instructions, whose completion the compiler tracks more
-  // conservatively).  Passes that need no U bits (all but the last) read
-  // them through an empty resource.
-  const uint32_t uoff = (uint32_t)(L.up - d.codes);
-  const uint32_t ustride = L.uon ? L.ub : 0;
-  const bool ulive = last && d.terms;
 
   XLane<XT> xl;
 
@@ -302,7 +278,6 @@ __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0,
     Batch<RB> B;
     const bool live = bb < nb;
     const __amdgpu_buffer_rsrc_t rw = live ? L.rw : r_none;
-    const __amdgpu_buffer_rsrc_t ru = live && ulive ? L.rw : r_none;
     const uint32_t base = row0 + (live ? bb : nb - 1) * RB;
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
@@ -315,8 +290,6 @@ __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0,
       if constexpr (K == 2) r.s = __builtin_amdgcn_raw_buffer_load_b8(rw, L.vs, row * L.ss, kStream);
       if constexpr (K > 0) r.b = load_scale<SF>(rw, L.vb, row * L.sa);
     }
-    const uint32_t ry = min(base + ((uint32_t)lane >> SH), row1 - 1);
-    B.u = __builtin_amdgcn_raw_buffer_load_b8(ru, uoff + ry * ustride, 0, kStream);
     // keep the scheduler from sinking these loads into the next computation
     __builtin_amdgcn_sched_barrier(0);
     return B;
@@ -339,48 +312,27 @@ __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0,
     float v = treduce<RB>(acc, lane) * XLane<XT>::kHalf;
     const uint32_t yi = bb * RB + ((uint32_t)lane >> SH);   // row within the segment
     if (!first) v = sm.ybuf[yi] + v;   // written by this lane in the previous pass
-    const uint32_t base = row0 + bb * RB;
-    const uint32_t row = base + ((uint32_t)lane >> SH);
-    if (last && d.terms) {
-      float c = 0.f;
-      if (L.uon) {
-        const float zt = sm.z[ti];
-        c = ((B.u >> L.ubit) & 1u) ? -zt : zt;
-      }
-      // terms beyond one per lane (more than 64 / RB of them)
-      const uint32_t ry = min(row, row1 - 1);
-      for (uint32_t t = ti + LPR; t < d.terms; t += LPR) {
-        const uint32_t p = t / d.rank, r = t % d.rank;
-        const uint32_t byte = path_plane(d.U, d, p)[(size_t)ry * L.ub + r / 8];
-        const float zt = sm.z[t];
-        c += ((byte >> (r & 7)) & 1u) ? -zt : zt;
-      }
-      v += group_sum<LPR>(c);
-    }
+    const uint32_t row = row0 + yi;
     if ((lane & (LPR - 1)) == 0 && row < row1)
       sm.ybuf[yi] = v;
   };
 
-  // Set-up loads first: the lane's x, the x of its share of the site table
-  // and the low-rank partials (L2 hits).  Vector memory loads complete in
-  // order, so waiting for these after the first batch's loads (HBM) are
-  // issued does not wait for the batch.
+  // Set-up loads first: the lane's x and the x of its share of the site
+  // table (L2 hits).  Vector memory loads complete in order, so waiting for
+  // these after the first batch's loads (HBM) are issued does not wait for
+  // the batch.
   const __amdgpu_buffer_rsrc_t rx = x_rsrc<XT>(d.x, d.in);
   typename XLane<XT>::Raw xr;
   XLane<XT>::load_raw(rx, pass * kPass2bit + 64 * lane, xr);
   TableX<XT> tx;
   if constexpr (K > 0) tx.load(rx, pass * kPass2bit);
-  const bool zpass = !split && pass == 0 && d.terms;
-  ZPart<ZP> zp;
-  if (zpass) z_prefetch<ZP>(d, threadIdx.x, zp);
 
   // Two batches in registers: while one is reduced, the next is in flight
   // (three resident workgroups per CU keep three wavefronts per SIMD, six
   // batches, in flight).
   Batch<RB> B0 = load_batch(b);
 
-  __syncthreads();   // readers of the previous table and z are done
-  if (zpass && threadIdx.x < d.terms) sm.z[threadIdx.x] = z_total<ZP>(d, threadIdx.x, zp);
+  __syncthreads();   // readers of the previous table are done
   if constexpr (K > 0) tx.store(sm.tbl);
   __syncthreads();
   if (!has_rows) return;
@@ -398,26 +350,21 @@ __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0,
   }
 }
 
-// One segment (rows row0..row1-1 of one matrix) of a workgroup, pass by pass.
-// SF and K are the matrix's scale format and sites per group: every
-// (scale format, k) class has kernels of its own, so the registers of the
-// hot fp16 / k = 8 loop are not set by the heavier fp24 loads.
-// With P, only pass `split_pass`, written to P[split_pass][row] without the
-// low-rank term (a reduce adds the passes and that term).
-template <int XT, int SF, int K, int RB, int ZP>
+// One segment (rows row0..row1-1 of one matrix) of a workgroup, pass by pass,
+// then its store (store_segment: the low-rank term, or with P one pass's
+// partial sums and the reduce of a completed row block).  SF and K are the
+// matrix's scale format and sites per group: every (scale format, k) class
+// has kernels of its own, so the registers of the hot fp16 / k = 8 loop are
+// not set by the heavier fp24 loads.
+template <int XT, int SF, int K, int RB, class ZJ>
 __device__ __forceinline__ void run_segment_2bit(const MatDev& d, uint32_t row0, uint32_t row1, StreamSmem& sm,
-                                                 float* P = nullptr, uint32_t split_pass = 0) {
+                                                 const Fuse& f, float* P = nullptr, uint32_t split_pass = 0,
+                                                 uint32_t* cnt = nullptr) {
   const uint32_t npass = (d.in + kPass2bit - 1) / kPass2bit;
   const bool split = P != nullptr;
   const uint32_t p0 = split ? split_pass : 0, p1 = split ? split_pass + 1 : npass;
-  for (uint32_t pass = p0; pass < p1; ++pass)
-    stream_rows_2bit<XT, SF, K, RB, ZP>(d, row0, row1, pass, npass, split, sm);
-  // y leaves through LDS: one coalesced write of the segment's rows instead
-  // of a few scattered bytes per batch of rows.
-  __syncthreads();
-  const uint32_t nrows = row1 - row0;
-  float* dst = split ? P + (size_t)split_pass * d.out : d.y;
-  for (uint32_t i = threadIdx.x; i < nrows; i += kThreads) dst[row0 + i] = sm.ybuf[i];
+  for (uint32_t pass = p0; pass < p1; ++pass) stream_rows_2bit<XT, SF, K, RB>(d, row0, row1, pass, pass == p0, sm);
+  store_segment<XT, ZJ>(d, row0, row1, SegEnd{sm.tbl, sm.z, sm.ybuf}, f, P, split_pass, npass, cnt);
 }
 
 // Three workgroups per CU (the LDS of a workgroup allows it) when the class's
@@ -427,50 +374,73 @@ constexpr int stream_waves_per_simd(int XT, int SF, int K) {
   return XT == WAL_X_BF16 && !(SF == WAL_SCALE_FP24 && K == 8) ? 3 : 1;
 }
 
-template <int XT, int SF, int K, int RB>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(stream_waves_per_simd(XT, SF, K))))
-void k_stream_grouped(const MatDev* __restrict__ descs, const uint32_t* __restrict__ blockseg,
-                      const Seg* __restrict__ segs) {
-  __shared__ StreamSmem sm;
-  const uint32_t s0 = blockseg[blockIdx.x], s1 = blockseg[blockIdx.x + 1];
-  for (uint32_t s = s0; s < s1; ++s) {
-    const Seg sg = segs[s];
-    run_segment_2bit<XT, SF, K, RB, kZSinglePrefetch>(descs[sg.mat], sg.row0, sg.row1, sm);
-  }
-}
-
-template <int XT, int SF, int K, int RB>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(stream_waves_per_simd(XT, SF, K))))
-void k_stream_single(MatDev d, uint32_t rows_per_block, uint32_t nrb, float* P) {
-  // without P: block b takes rows [b rpb, b rpb + rpb) over every pass; with
-  // P: block b takes pass b / nrb of row block b % nrb
-  __shared__ StreamSmem sm;
-  const uint32_t rb = P ? blockIdx.x % nrb : blockIdx.x;
-  const uint32_t r0 = rb * rows_per_block;
-  const uint32_t r1 = min(d.out, r0 + rows_per_block);
-  if (r0 < r1) run_segment_2bit<XT, SF, K, RB, kZSinglePrefetch>(d, r0, r1, sm, P, P ? blockIdx.x / nrb : 0u);
-}
-
-// Low-rank partials of a single product: block (tc, cc) computes terms
-// kZTerms tc .. kZTerms tc + kZTerms - 1 over columns [8192 cc, 8192 cc + 8192)
-// into d.z[cc][t].  Few terms per block keep each thread's share short: the
-// streaming kernel waits for this launch.
+// Low-rank job of a fused launch or of the grouped pre-pass: terms t0 ..
+// t0 + kZTermsGrouped - 1 of matrix m over columns [4096 cc, 4096 cc + 4096)
+// into its partials z[cc][t] (jobs[2 j] = m, jobs[2 j + 1] = t0 << 16 | cc).
 template <int XT>
-__global__ __launch_bounds__(kThreads) void k_z_chunks(MatDev d) {
-  const uint32_t tcs = (d.terms + kZTerms - 1) / kZTerms;
-  const uint32_t tc = blockIdx.x % tcs, cc = blockIdx.x / tcs;
-  const uint32_t c0 = cc * kZSingleCols, c1 = min(d.in, c0 + kZSingleCols);
-  z_chunk<XT, (int)kZTerms>(d, d.x, tc * kZTerms, d.z + (size_t)cc * d.terms, c0, c1);
-}
-
-template <int XT>
-__global__ __launch_bounds__(kThreads) void k_z_grouped(const MatDev* __restrict__ descs,
-                                                        const uint32_t* __restrict__ jobs) {
-  const uint32_t m = jobs[2 * blockIdx.x], tc = jobs[2 * blockIdx.x + 1];
+__device__ __forceinline__ void grouped_z_job(const MatDev* __restrict__ descs, const uint32_t* __restrict__ jobs,
+                                              uint32_t j) {
+  const uint32_t m = jobs[2 * j], tc = jobs[2 * j + 1];
   const MatDev& d = descs[m];
   const uint32_t t0 = tc >> 16, cc = tc & 0xFFFFu;
   const uint32_t c0 = cc * kZChunkCols, c1 = min(d.in, c0 + kZChunkCols);
-  z_chunk<XT, (int)kZTerms>(d, d.x, t0, d.z + (size_t)cc * d.terms, c0, c1);
+  z_chunk<XT, (int)kZTermsGrouped>(d, d.x, t0, d.z + (size_t)cc * d.terms, c0, c1);
+}
+
+// Grouped products: workgroup t = blockIdx.x computes low-rank job t when
+// t < f.nz, else streams the segments of block t - f.nz.
+template <int XT, int SF, int K, int RB>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(stream_waves_per_simd(XT, SF, K))))
+void k_stream_grouped(const MatDev* __restrict__ descs, const uint32_t* __restrict__ blockseg,
+                      const Seg* __restrict__ segs, const uint32_t* __restrict__ jobs, Fuse f) {
+  __shared__ StreamSmem sm;
+  const uint32_t t = blockIdx.x;
+  if (t < f.nz) {
+    grouped_z_job<XT>(descs, jobs, t);
+    publish_z(f);
+  } else {
+    const uint32_t b = t - f.nz;
+    const uint32_t s0 = blockseg[b], s1 = blockseg[b + 1];
+    for (uint32_t s = s0; s < s1; ++s) {
+      const Seg sg = segs[s];
+      run_segment_2bit<XT, SF, K, RB, ZJobsGrouped>(descs[sg.mat], sg.row0, sg.row1, sm, f);
+    }
+  }
+  finish_launch(f);
+}
+
+// Single products: workgroup t = blockIdx.x < f.nz computes the low-rank partials of terms
+// kZTerms tc .. kZTerms tc + kZTerms - 1 over columns [8192 cc, 8192 cc +
+// 8192) into d.z[cc][t] (t = cc tcs + tc); the others stream.  Without P,
+// block b takes rows [b rpb, b rpb + rpb) over every pass; with P, block b
+// takes pass b / nrb of row block b % nrb (cnt: the row blocks' arrival
+// counters).
+template <int XT, int SF, int K, int RB>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(stream_waves_per_simd(XT, SF, K))))
+void k_stream_single(MatDev d, uint32_t rows_per_block, uint32_t nrb, float* P, uint32_t* cnt, Fuse f) {
+  __shared__ StreamSmem sm;
+  const uint32_t t = blockIdx.x;
+  if (t < f.nz) {
+    const uint32_t tcs = (d.terms + kZTerms - 1) / kZTerms, tc = t % tcs, cc = t / tcs;
+    const uint32_t c0 = cc * kZSingleCols, c1 = min(d.in, c0 + kZSingleCols);
+    z_chunk<XT, (int)kZTerms>(d, d.x, tc * kZTerms, d.z + (size_t)cc * d.terms, c0, c1);
+    publish_z(f);
+  } else {
+    const uint32_t b = t - f.nz;
+    const uint32_t rb = P ? b % nrb : b;
+    const uint32_t r0 = rb * rows_per_block;
+    const uint32_t r1 = min(d.out, r0 + rows_per_block);
+    if (r0 < r1)
+      run_segment_2bit<XT, SF, K, RB, ZJobsSingle>(d, r0, r1, sm, f, P, P ? b / nrb : 0u, P ? cnt + rb : nullptr);
+  }
+  finish_launch(f);
+}
+
+// The grouped low-rank pre-pass as a launch of its own (the phase API).
+template <int XT>
+__global__ __launch_bounds__(kThreads) void k_z_grouped(const MatDev* __restrict__ descs,
+                                                        const uint32_t* __restrict__ jobs) {
+  grouped_z_job<XT>(descs, jobs, blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -595,7 +565,7 @@ uint64_t count_zjobs(uint32_t n, const wal_info* infos) {
   uint64_t j = 0;
   for (uint32_t i = 0; i < n; ++i) {
     const uint32_t T = infos[i].d.n_paths * infos[i].d.rank;
-    j += (uint64_t)(T + kZTerms - 1) / kZTerms * (T ? grouped_zc(infos[i]) : 0);
+    j += (uint64_t)(T + kZTermsGrouped - 1) / kZTermsGrouped * (T ? grouped_zc(infos[i]) : 0);
   }
   return j;
 }
@@ -614,6 +584,15 @@ struct PlanShape {
   uint64_t off_descs, off_zjobs, off_blockseg[WAL_MAX_CLASSES], off_segs[WAL_MAX_CLASSES], bytes;
 };
 
+// The plan's synchronisation words (fused launches) follow its header; the
+// planner writes them as zero and every launch returns them to zero.
+constexpr uint64_t plan_sync_offset() { return (sizeof(PlanHeader) + 63) / 64 * 64; }
+static_assert(plan_sync_offset() == WAL_PLAN_SYNC_OFFSET, "the plan's synchronisation words as documented");
+static_assert(kSyncBytes == WAL_SYNC_BYTES && kSyncFallback == WAL_SYNC_FALLBACK_WORD,
+              "synchronisation words as documented");
+static_assert(kMaxRowBlocks == WAL_MAX_ROW_BLOCKS && kWsZeroBytes == WAL_WS_ZERO_BYTES && kWsZeroBytes % 256 == 0,
+              "workspace zero region as documented");
+
 int plan_shape(uint32_t n, const wal_info* infos, uint32_t grid, int x_dtype, PlanShape* P) {
   std::memset(P, 0, sizeof(*P));
   uint64_t rows[kClasses] = {0};
@@ -631,6 +610,10 @@ int plan_shape(uint32_t n, const wal_info* infos, uint32_t grid, int x_dtype, Pl
       uint32_t res = 0;
       int st = resident_blocks(reinterpret_cast<const void*>(grouped_for(x_dtype, c)), &res);
       if (st) return st;
+      // the first launch also runs the low-rank jobs in workgroups of its
+      // own: its streaming workgroups leave them their slots
+      const uint64_t nzj = P->n_classes == 0 ? count_zjobs(n, infos) : 0;
+      if (res > 2 * nzj) res -= (uint32_t)nzj;
       const uint64_t by_rows = (rows[c] + 15) / 16;
       g = (uint32_t)(by_rows < res ? by_rows : res);
       if (!g) g = 1;
@@ -641,7 +624,7 @@ int plan_shape(uint32_t n, const wal_info* infos, uint32_t grid, int x_dtype, Pl
     P->mats[k] = mats[c];
     P->rows[k] = rows[c];
   }
-  uint64_t off = up64(sizeof(PlanHeader), 64);
+  uint64_t off = plan_sync_offset() + kSyncBytes;
   P->off_descs = off;
   off += up64((uint64_t)n * sizeof(MatDev), 64);
   P->off_zjobs = off;
@@ -703,9 +686,15 @@ int wal_gemv(const wal_info* info, const void* W_dev, const void* x_dev, int x_d
   const uint32_t npass = cls >= 8 ? (info->d.in + kPassBase3 - 1) / kPassBase3 : (info->d.in + kPass2bit - 1) / kPass2bit;
   // Matrices wider than one pass run their passes in separate workgroups
   // when the workspace holds the per-pass partial sums (it does at
-  // wal_workspace_size(info, 1) bytes); a reduce adds them.
-  const bool split = npass > 1 && ws_dev && ws_bytes >= S.bytes;
-  const size_t need = split ? (size_t)S.bytes : info->d.n_paths ? (size_t)S.off_p : 0;   // z partials [chunks][terms]
+  // wal_workspace_size(info, 1) bytes); the workgroup that completes a row
+  // block adds them.  The workspace: synchronisation words, arrival
+  // counters, low-rank partials [chunks][terms], partial sums.
+  // A split product has at most kMaxRowBlocks row blocks (one arrival
+  // counter each) of at most seg_rows rows.
+  const uint32_t out = info->d.out;
+  const uint32_t split_min_rows = ((out + kMaxRowBlocks - 1) / kMaxRowBlocks + kRB - 1) / kRB * kRB;
+  const bool split = npass > 1 && ws_dev && ws_bytes >= S.bytes && split_min_rows <= seg_rows(cls);
+  const size_t need = split ? (size_t)S.bytes : info->d.n_paths ? (size_t)S.off_p : 0;
   if (need && (!ws_dev || ws_bytes < need)) return ws_dev ? WAL_ERR_BUFFER : WAL_ERR_ARG;
   if (need && !aligned(ws_dev, 16)) return WAL_ERR_ALIGN;
   if (overlap(x_dev, (size_t)info->d.in * xelem(x_dtype), y_dev, (size_t)info->d.out * 4)) return WAL_ERR_ARG;
@@ -715,29 +704,31 @@ int wal_gemv(const wal_info* info, const void* W_dev, const void* x_dev, int x_d
   if ((st = check_blob_size(info))) return st;
   if (!single_for(x_dtype, cls)) return WAL_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  MatDev d = make_dev(info, W_dev, x_dev, y_dev, static_cast<float*>(ws_dev), info->d.in, info->d.out, 1);
+  uint8_t* ws = static_cast<uint8_t*>(ws_dev);
+  MatDev d = make_dev(info, W_dev, x_dev, y_dev, need ? reinterpret_cast<float*>(ws + S.off_z) : nullptr,
+                      info->d.in, info->d.out, 1);
   d.zc = (info->d.in + kZSingleCols - 1) / kZSingleCols;   // at most S.zc partials
-  if (d.terms) {
-    const uint32_t g = (d.terms + kZTerms - 1) / kZTerms * d.zc;
-    if (x_dtype == WAL_X_BF16) hipLaunchKernelGGL(k_z_chunks<WAL_X_BF16>, dim3(g), dim3(kThreads), 0, s, d);
-    else hipLaunchKernelGGL(k_z_chunks<WAL_X_F32>, dim3(g), dim3(kThreads), 0, s, d);
-    if ((st = launch_status())) return st;
-  }
   uint32_t resident = 0;
   if ((st = resident_blocks(reinterpret_cast<const void*>(grouped_for(x_dtype, cls)), &resident))) return st;
+  // One launch: its first nz workgroups compute the low-rank partials, which
+  // the others read only when they store their rows.
+  const uint32_t nz = d.terms ? (d.terms + kZTerms - 1) / kZTerms * d.zc : 0;
   // rows per block: the (row, pass) work spread evenly over the blocks the
-  // GPU holds at once
-  const uint64_t units = (uint64_t)d.out * (split ? npass : 1);
-  uint32_t rpb = (uint32_t)((units + resident - 1) / resident);
-  const uint32_t min_rows = kWaves * kRB;   // one batch per wavefront
-  if (rpb < min_rows) rpb = min_rows;
-  rpb = (rpb + kRB - 1) / kRB * kRB;
-  if (rpb > seg_rows(cls)) rpb = seg_rows(cls);
-  const uint32_t nrb = (d.out + rpb - 1) / rpb;
-  float* P = split ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws_dev) + S.off_p) : nullptr;
-  hipLaunchKernelGGL(single_for(x_dtype, cls), dim3(nrb * (split ? npass : 1)), dim3(kThreads), 0, s, d, rpb, nrb, P);
-  if ((st = launch_status()) || !split) return st;
-  return launch_reduce_single(d, d.z, d.zc, P, npass, stream);
+  // GPU holds at once besides the low-rank jobs
+  const uint32_t slots = resident > 2 * nz ? resident - nz : resident;
+  const uint64_t units = (uint64_t)out * (split ? npass : 1);
+  uint32_t rpb = (uint32_t)((units + slots - 1) / slots);
+  rpb = std::max(rpb, kWaves * kRB);   // one batch per wavefront
+  if (split) rpb = std::max(rpb, split_min_rows);
+  rpb = std::min((rpb + kRB - 1) / kRB * kRB, seg_rows(cls));
+  const uint32_t nrb = (out + rpb - 1) / rpb;
+  float* P = split ? reinterpret_cast<float*>(ws + S.off_p) : nullptr;
+  uint32_t* cnt = split ? reinterpret_cast<uint32_t*>(ws + S.off_cnt) : nullptr;
+  const uint32_t grid = nz + nrb * (split ? npass : 1);
+  Fuse f{};
+  if (need) f = Fuse{reinterpret_cast<uint32_t*>(ws), 0u, nz, nz, grid, 1u};
+  hipLaunchKernelGGL(single_for(x_dtype, cls), dim3(grid), dim3(kThreads), 0, s, d, rpb, nrb, P, cnt, f);
+  return launch_status();
 }
 
 int wal_gemv_noalloc(const wal_info* info, const void* W_dev, const void* x_dev, int x_dtype, float* y_dev,
@@ -877,7 +868,7 @@ int wal_grouped_plan(uint32_t n, const wal_info* infos, const void* const* W_dev
     descs[i].zc = zc;   // z partials [zc][T]
     zoff += T ? up64(4ull * T * zc, 16) : 0;
     for (uint32_t cc = 0; T && cc < zc; ++cc)
-      for (uint32_t t0 = 0; t0 < T; t0 += kZTerms) {
+      for (uint32_t t0 = 0; t0 < T; t0 += kZTermsGrouped) {
         jobs[2 * j] = i;
         jobs[2 * j + 1] = (t0 << 16) | cc;
         ++j;
@@ -989,19 +980,30 @@ int wal_gemv_grouped_phases(const wal_grouped_info* g, const void* plan_dev, int
   const uint8_t* base = static_cast<const uint8_t*>(plan_dev);
   const MatDev* descs = reinterpret_cast<const MatDev*>(base + g->off_descs);
   const uint32_t* jobs = reinterpret_cast<const uint32_t*>(base + g->off_zjobs);
+  // Both phases: the low-rank jobs run in the first workgroups of the first
+  // streaming launch (the plan's synchronisation words order them).
+  const bool fused = phases == WAL_PHASE_ALL;
   int st;
-  if ((phases & WAL_PHASE_LOWRANK) && g->n_zjobs) {
+  if (!fused && (phases & WAL_PHASE_LOWRANK) && g->n_zjobs) {
     if (g->x_dtype == WAL_X_BF16)
       hipLaunchKernelGGL(k_z_grouped<WAL_X_BF16>, dim3(g->n_zjobs), dim3(kThreads), 0, s, descs, jobs);
     else
       hipLaunchKernelGGL(k_z_grouped<WAL_X_F32>, dim3(g->n_zjobs), dim3(kThreads), 0, s, descs, jobs);
     if ((st = launch_status())) return st;
   }
+  uint32_t* sync = reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(base) + plan_sync_offset());
   for (uint32_t k = 0; (phases & WAL_PHASE_STREAM) && k < g->n_classes; ++k) {
     const uint32_t* blockseg = reinterpret_cast<const uint32_t*>(base + g->class_blockseg[k]);
     const Seg* segs = reinterpret_cast<const Seg*>(base + g->class_segs[k]);
-    hipLaunchKernelGGL(grouped_for((int)g->x_dtype, g->class_id[k]), dim3(g->class_grid[k]), dim3(kThreads), 0, s,
-                       descs, blockseg, segs);
+    uint32_t grid = g->class_grid[k];
+    Fuse f{};
+    if (fused) {
+      const uint32_t nz = k == 0 ? g->n_zjobs : 0u;
+      grid += nz;
+      f = Fuse{sync, k, nz, g->n_zjobs, grid, k + 1 == g->n_classes ? 1u : 0u};
+    }
+    hipLaunchKernelGGL(grouped_for((int)g->x_dtype, g->class_id[k]), dim3(grid), dim3(kThreads), 0, s, descs,
+                       blockseg, segs, jobs, f);
     if ((st = launch_status())) return st;
   }
   return WAL_OK;

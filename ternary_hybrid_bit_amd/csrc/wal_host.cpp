@@ -605,8 +605,9 @@ GemmShape gemm_shape(const wal_info& f, uint32_t batch) {
   S.passes = (f.d.in + kPass2bit - 1) / kPass2bit;
   S.zc = (f.d.in + kZChunkCols - 1) / kZChunkCols;
   S.slices = (f.d.in + kSliceCols - 1) / kSliceCols;
-  S.off_z = 0;
-  S.off_p = up(4 * terms * batch * S.zc, 256);
+  S.off_cnt = kSyncBytes;
+  S.off_z = kWsZeroBytes;
+  S.off_p = S.off_z + up(4 * terms * batch * S.zc, 256);
   S.bytes = S.off_p + up(4ull * S.slices * batch * f.d.out, 256);
   return S;
 }

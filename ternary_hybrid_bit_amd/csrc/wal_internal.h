@@ -62,15 +62,65 @@ constexpr uint32_t kPassBase3 = 5120;  // base-3: 80 trits per lane
 constexpr uint32_t kSegRows = 4096;
 // Low-rank terms handled per workgroup of the V^T x pre-passes.
 constexpr uint32_t kZTerms = 4;
+// Low-rank terms of one job of a grouped plan (16: few, large jobs, so that a
+// fused launch spends few of its first workgroups on them).
+constexpr uint32_t kZTermsGrouped = 16;
 constexpr uint32_t kMaxTerms = WAL_MAX_PATHS * WAL_MAX_RANK;
 static_assert(kMaxTerms <= kThreads, "one low-rank term per thread of a streaming workgroup");
 
+// Synchronisation words of a launch that computes the low-rank pre-pass in
+// its first workgroups (see wal_device.h, fused launches), u32 words in
+// 128-byte lines.  Hundreds of workgroups that each touch one coherent word
+// queue on it, so every word the whole launch touches is kept in
+// kSyncReplicas copies, one line apart; workgroup b uses copy b % kSyncReplicas.
+//   line 0:       word 0 the fallback count, word 1 set when a wait of the
+//                 current call gave up (the later waiters then give up at
+//                 once), words 16 + s the copies of launch slot s whose
+//                 workgroups have all finished
+//   lines 1..16:  the low-rank jobs published (copy r: word 0 of line 1 + r)
+//   lines 17..32: workgroups finished (copy r: word s of line 17 + r)
+// Every call leaves them as it found them (zero), except the fallback
+// count: the workgroups whose bounded wait for the low-rank jobs gave up and
+// which computed the terms themselves (their outputs are still exact).
+constexpr uint32_t kSyncReplicas = 16;
+constexpr uint32_t kSyncLine = 32;                                  // words per line
+constexpr uint32_t kSyncFallback = 0;
+constexpr uint32_t kSyncGaveUp = 1;
+constexpr uint32_t kSyncSlotsDone = 16;                             // + slot
+constexpr uint32_t kSyncZDone = kSyncLine;                          // + kSyncLine r
+constexpr uint32_t kSyncFinished = kSyncLine * (1 + kSyncReplicas);  // + kSyncLine r + slot
+constexpr uint32_t kSyncBytes = 4352;                                // 33 lines, padded to 256 bytes
+static_assert(4 * kSyncLine * (1 + 2 * kSyncReplicas) <= kSyncBytes && kSyncBytes % 256 == 0, "sync lines");
+static_assert(WAL_MAX_CLASSES <= 16, "one finish word per launch slot in a line");
+// Arrival counters of split products follow the synchronisation words, at a
+// place and size that do not depend on the blob: a workspace that served
+// one shape still has them zero for the next.
+constexpr uint32_t kMaxRowBlocks = 4096;
+constexpr uint32_t kWsZeroBytes = kSyncBytes + 4 * kMaxRowBlocks;
+
+// What a fused launch does besides streaming.  Workgroups below nz compute
+// low-rank job blockIdx.x, the others stream (block blockIdx.x - nz).
+// Workgroups start in index order, so the jobs are under way before any
+// streaming workgroup waits for them; the wait is bounded all the same, and
+// a workgroup whose wait gives up computes the terms it needs itself.
+// Consumers wait until zdone reaches zwait before they read the low-rank
+// terms; zwait == 0 means the terms are ready (a separate pre-pass).  The
+// last workgroup to finish returns finished[slot], and with reset_z zdone,
+// to zero.
+struct Fuse {
+  uint32_t* sync;       // the synchronisation words (null: no waits, no counts)
+  uint32_t slot, nz, zwait, grid, reset_z;
+};
+
 // Streaming kernels as host-side launch targets.
 struct Seg;
-using GroupedFn = void (*)(const MatDev*, const uint32_t*, const Seg*);
+// Grouped: (descriptors, block -> segment index, segments, low-rank jobs,
+// launch context).
+using GroupedFn = void (*)(const MatDev*, const uint32_t*, const Seg*, const uint32_t*, Fuse);
 // Single-product streaming kernel: (descriptor, rows per block, row blocks,
-// per-pass partial sums or null; see k_stream_single).
-using SingleFn = void (*)(MatDev, uint32_t, uint32_t, float*);
+// per-pass partial sums or null, arrival counters per row block (with
+// partial sums), launch context; see k_stream_single).
+using SingleFn = void (*)(MatDev, uint32_t, uint32_t, float*, uint32_t*, Fuse);
 
 // Small-batch products (wal_gemm.hip).
 //  * batched GEMV (vector ALUs), two launches: the first writes per-pass
@@ -98,18 +148,17 @@ constexpr uint32_t kZTermsPerBlock = 16;
 // Columns of one partial-sum slice of the MFMA small-batch kernel.
 constexpr uint32_t kSliceCols = 1024;
 
+// Workspace of the single and small-batch products: synchronisation words
+// and arrival counters (kWsZeroBytes, zero between calls), the low-rank
+// partials, then partial sums.
 struct GemmShape {
   uint32_t nt, passes, zc;   // n-tiles, batched GEMV passes, z chunks
   uint32_t slices;           // partial-sum planes of P: ceil(in / kSliceCols) >= passes
-  uint64_t off_z, off_p, bytes;
+  uint64_t off_cnt, off_z, off_p, bytes;
 };
 GemmShape gemm_shape(const wal_info& f, uint32_t batch);
 // Launchers (stream as hipStream_t); WAL_OK or WAL_ERR_DEVICE.
 int launch_gemm_valu(const wal_info& f, const MatDev& d, uint32_t batch, void* ws, void* stream);
-// y = sum over `slices` per-pass partial planes P[slice][row] + the low-rank
-// term with z = the sum of zc partials (d.batch == 1).
-int launch_reduce_single(const MatDev& d, const float* zpart, uint32_t zc, const float* P, uint32_t slices,
-                         void* stream);
 int launch_gemm_mfma(const wal_info& f, const MatDev& d, uint32_t batch, void* ws, void* stream);
 
 // Prefill products: tiles of prefill_rows(scale format) rows x kPrefillCols

@@ -39,7 +39,7 @@ def run_gemv(wal, blob, info, x_bits):
     W = to_dev(blob)
     xt = to_dev(x_bits.view(np.int16)).view(torch.bfloat16)
     y = torch.full((info.d.out,), float("nan"), dtype=torch.float32, device=dev())
-    ws = torch.empty(max(wal.wal_workspace_size(info, 1), 4) // 4, dtype=torch.float32, device=dev())
+    ws = torch.zeros(max(wal.wal_workspace_size(info, 1), 4) // 4, dtype=torch.float32, device=dev())
     wal.wal_gemv(info, W, xt, y, ws)
     torch.cuda.synchronize()
     return y.cpu().numpy().astype(np.float64)

@@ -47,7 +47,7 @@ def run_gemv(wal, blob, info, x_f32, x_bits):
     xt = x_tensor(x_f32, x_bits)
     y = torch.full((info.d.out,), float("nan"), dtype=torch.float32, device=dev())
     nws = wal.wal_workspace_size(info, 1)
-    ws = torch.empty(max(nws, 4) // 4, dtype=torch.float32, device=dev())
+    ws = torch.zeros(max(nws, 4) // 4, dtype=torch.float32, device=dev())
     wal.wal_gemv(info, W, xt, y, ws)
     torch.cuda.synchronize()
     return y.cpu().numpy().astype(np.float64)
@@ -132,11 +132,15 @@ def test_wide_single_split_and_whole(wal, out, inp, k, P, r, sf, b3):
     ref = D.gemv(F.pack(F.from_synth(m)), x[0])
     W, xt = to_dev(blob), x_tensor(x[0], bits[0])
     full = wal.wal_workspace_size(info, 1)
-    zonly = (4 * P * r * ((inp + 4095) // 4096) + 255) // 256 * 256   # the low-rank part alone
+    # the workspace up to the end of its low-rank part (synchronisation words,
+    # one arrival counter per 16 rows, the partials): no room for the passes'
+    # partial sums
+    up = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    zonly = wal.WAL_WS_ZERO_BYTES + up(4 * P * r * ((inp + 4095) // 4096))
     for nbytes in (full, zonly):
         print(f"wide {out}x{inp} k={k} P={P} base3={b3} workspace {nbytes} B", flush=True)
         y = torch.full((out,), float("nan"), dtype=torch.float32, device=dev())
-        ws = torch.empty(nbytes // 4, dtype=torch.float32, device=dev()) if nbytes else None
+        ws = torch.zeros(nbytes // 4, dtype=torch.float32, device=dev()) if nbytes else None
         wal.wal_gemv(info, W, xt, y, ws)
         torch.cuda.synchronize()
         assert D.rel_l2(y.cpu().numpy().astype(np.float64), ref) <= BF16_TOL, nbytes

@@ -129,7 +129,7 @@ def test_rotated_blob_product(wal, out, inp, k, P, r, b3):
     Xr = torch.empty_like(X)
     wal.wal_rotate_h128(X, Xr)
     y = torch.full((out,), float("nan"), dtype=torch.float32, device=dev())
-    ws = torch.empty(max(wal.wal_workspace_size(info, 1), 4) // 4, dtype=torch.float32, device=dev())
+    ws = torch.zeros(max(wal.wal_workspace_size(info, 1), 4) // 4, dtype=torch.float32, device=dev())
     wal.wal_gemv(info, torch.from_numpy(blob).to(dev()), Xr, y, ws)
     torch.cuda.synchronize()
     xr = synth.bf16_bits_to_f32(bf16_rne(Rt.rotate(synth.bf16_bits_to_f32(synth.round_bf16_bits(x[0])).astype(np.float64))))

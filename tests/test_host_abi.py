@@ -195,9 +195,10 @@ def test_inspect_reads_header():
 
 
 def test_workspace_size():
-    """Low-rank partials z [chunk][batch][terms] (one chunk per 4096 columns)
-    | partial sums [slices][batch][out] of the small-batch kernels (one slice
-    per 1024 columns), each padded to 256 bytes."""
+    """Synchronisation words (4352 bytes: 33 lines of 128) and 4096 arrival
+    counters, the same for every shape | low-rank partials z [chunk][batch][terms] (one chunk
+    per 4096 columns) | partial sums [slices][batch][out] of the small-batch
+    kernels (one slice per 1024 columns), each padded to 256 bytes."""
     def up(v):
         return (v + 255) // 256 * 256
 
@@ -210,11 +211,12 @@ def test_workspace_size():
 
     def expect(out, inp, terms, B):
         chunks, slices = (inp + 4095) // 4096, (inp + 1023) // 1024
-        return up(4 * terms * B * chunks) + up(4 * slices * B * out)
+        return 4352 + 4 * 4096 + up(4 * terms * B * chunks) + up(4 * slices * B * out)
 
     info = wal.wal_packed_size(wal.make_desc(12288, 4096, 8, 1, 16))
-    assert wal.wal_workspace_size(info, 1) == expect(12288, 4096, 16, 1) == 256 + 4 * 49152
+    assert wal.wal_workspace_size(info, 1) == expect(12288, 4096, 16, 1) == 20736 + 256 + 4 * 49152
     assert wal.wal_workspace_size(info, 32) == expect(12288, 4096, 16, 32)
+    assert wal.WAL_WS_ZERO_BYTES == 20736
     info = wal.wal_packed_size(wal.make_desc(4096, 12288, 8, 1, 16))
     for B in (1, 4, 16, 17, 32):
         assert wal.wal_workspace_size(info, B) == expect(4096, 12288, 16, B)
@@ -379,6 +381,9 @@ def test_grouped_plan_covers_every_row_once(grid):
     infos = [wal.wal_packed_size(wal.make_desc(o, i, k, P, r, trit_fmt=tf, scale_fmt=sf))
              for o, i, k, P, r, sf, tf in shapes]
     plan, g = _plan_on_host(infos, grid)
+    # the launch's synchronisation words start out zero, ahead of the descriptors
+    sync = slice(wal.WAL_PLAN_SYNC_OFFSET, wal.WAL_PLAN_SYNC_OFFSET + wal.WAL_SYNC_BYTES)
+    assert not plan[sync].any() and g.off_descs >= sync.stop
     classes, jobs = _plan_classes(plan, g)
     assert sorted(c for c, _, _ in classes) == sorted(set(_class_of(i) for i in infos))
     assert sum(len(sg) for _, _, sg in classes) == g.n_segs
@@ -404,10 +409,10 @@ def test_grouped_plan_covers_every_row_once(grid):
         assert per_block.max() <= ideal + max(rb[m] for m in members) + 1
     for c in covered:
         assert np.all(c == 1)
-    # one low-rank job per 4 terms and 4096-column chunk of every matrix
+    # one low-rank job per 16 terms and 4096-column chunk of every matrix
     # that has paths: (matrix, t0 << 16 | chunk)
     want = [(m, (t0 << 16) | cc) for m, (o, i, k, P, r, sf, tf) in enumerate(shapes)
-            for cc in range((i + 4095) // 4096) for t0 in range(0, P * r, 4)]
+            for cc in range((i + 4095) // 4096) for t0 in range(0, P * r, 16)]
     assert sorted(map(tuple, jobs.tolist())) == sorted(want)
 
 

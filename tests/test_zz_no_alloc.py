@@ -45,7 +45,7 @@ def case(wal, seed, out, inp, k, paths, x_bf16, trit_fmt=synth.TRIT_2BIT, scale_
 def run_both(wal, blob, info, xt):
     W = torch.from_numpy(blob).to(dev())
     y_ref = torch.full((info.d.out,), float("nan"), dtype=torch.float32, device=dev())
-    ws = torch.empty(max(wal.wal_workspace_size(info, 1), 4) // 4, dtype=torch.float32, device=dev())
+    ws = torch.zeros(max(wal.wal_workspace_size(info, 1), 4) // 4, dtype=torch.float32, device=dev())
     wal.wal_gemv(info, W, xt, y_ref, ws)
     y = torch.full((info.d.out,), float("nan"), dtype=torch.float32, device=dev())
     wal.wal_gemv_noalloc(info, W, xt, y)
