@@ -367,7 +367,7 @@ def resident(torch, items, dev):
 def run_decode_step(args):
     """The 36-layer decode step with its dependencies: per layer q|k|v (one
     grouped product, shared x), o, gate|up (shared x), down, each product
-    launched after the one before (144 grouped products, 288 kernels), over
+    launched after the one before (144 grouped products, one launch each), over
     the same 252 matrices as the sweep; once as one wal_gemv_grouped_seq call
     per step and once as a replay of the chain captured in a HIP graph.  For
     context the same process times the sweep as one grouped product of
@@ -405,7 +405,7 @@ def run_decode_step(args):
     nbytes = sum(i.algorithmic_bytes for i in infos)
     res = {"workload": "decode-step", "entry": "wal_gemv_grouped_seq / wal_graph_launch",
            "layers": 36, "grouped_products": len(chain),
-           "kernels_per_step": sum(1 + g.n_classes if g.n_zjobs else g.n_classes for g, _ in chain),
+           "kernels_per_step": sum(g.n_classes for g, _ in chain),
            "packed_bytes": int(nbytes), "x_dtype": "bf16", "data": "synthetic", "steps": steps,
            "eager_ms_per_step": round(eager_ms, 4), "graph_ms_per_step": round(graph_ms, 4),
            "graph_tokens_per_s": round(1e3 / graph_ms, 1), "graph_GB/s": round(nbytes / (graph_ms * 1e-3) / 1e9, 1),

@@ -125,14 +125,16 @@ typedef struct {
 /* Launch summary of a grouped plan (filled by wal_grouped_plan).  Matrices
  * are grouped by kernel class, class id = 8 * trit_fmt + 4 * scale_fmt +
  * index of k in {0, 2, 4, 8}; each class present gets one streaming launch
- * over its own split of rows into class_grid[c] workgroups.  trit_fmt is 0
- * (classes carry the format). */
+ * over its own split of rows into class_grid[c] workgroups.  The low-rank
+ * reductions run as n_zjobs jobs of zjob_terms terms (4 when that makes at
+ * most 64 jobs, else 16) over one 4096-column chunk each. */
 typedef struct {
   uint32_t n;              /* matrices                                      */
   uint32_t n_classes;      /* classes present (streaming launches)          */
   uint32_t n_segs;         /* (matrix, row range) segments, all classes     */
   uint32_t n_zjobs;        /* workgroups of the low-rank V^T x pre-pass     */
-  uint32_t x_dtype, trit_fmt;
+  uint32_t x_dtype;
+  uint32_t zjob_terms;     /* low-rank terms per job (4 or 16)             */
   uint32_t rows_per_batch; /* rows a wavefront reduces at once              */
   uint32_t grid;           /* largest class grid                           */
   uint64_t plan_bytes;     /* bytes of the plan blob                        */
@@ -142,6 +144,9 @@ typedef struct {
   uint32_t class_grid[WAL_MAX_CLASSES];
   uint64_t class_blockseg[WAL_MAX_CLASSES];   /* plan offsets per class     */
   uint64_t class_segs[WAL_MAX_CLASSES];
+  void* sync_dev;          /* the workspace's synchronisation words (its
+                              start), or NULL when the plan has no low-rank
+                              paths and no split matrices                  */
 } wal_grouped_info;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -196,18 +201,24 @@ int wal_unpack(const void* blob, size_t bytes, int8_t* T, uint8_t* site_pos,
  * small-batch kernels also keep partial products there.  Contents, each part
  * padded to 256 bytes:
  *   WAL_WS_ZERO_BYTES that must be zero before the workspace's first use
- *     (hipMemset, torch.zeros) and that every call leaves zero, except the
- *     u32 word WAL_SYNC_FALLBACK_WORD, a diagnostic count: a workgroup adds
- *     one when its bounded wait for the low-rank terms gives up and it
- *     computes them itself (outputs stay exact; the caller may read and
- *     clear the word).  The region has the same size and place for every
- *     blob, so one workspace serves products of any shape in turn.  It
- *     holds WAL_SYNC_BYTES of synchronisation words (u32; the workgroups of
- *     one launch coordinate through them, see wal_gemv), then one arrival
- *     counter (u32) per row block of a split product, for up to
- *     WAL_MAX_ROW_BLOCKS row blocks;
- *   the per-path reductions z_p = diag(s_p) V_p^T X per 4096-column chunk
- *     [chunks][batch][n_paths * rank] (fp32);
+ *     (hipMemset, torch.zeros) and that every call leaves as it found them,
+ *     except two things: the epoch words, which count the calls made on the
+ *     workspace (a call's low-rank partials carry a tag derived from it, so
+ *     that no call takes another's partials for its own), and the u32 word
+ *     WAL_SYNC_FALLBACK_WORD, a diagnostic count: a workgroup adds one when
+ *     its bounded wait for the low-rank terms gives up and it computes them
+ *     itself (outputs stay exact; the caller may read and clear the word).
+ *     The region has the same size and place for every blob, so one
+ *     workspace serves products of any shape in turn.  It holds
+ *     WAL_SYNC_BYTES of synchronisation words (u32; the workgroups of one
+ *     launch coordinate through them, see wal_gemv), then one arrival
+ *     counter (u32) per 16 rows of a split product, for up to
+ *     WAL_MAX_ROW_BLOCKS of them (a product with more rows runs its passes
+ *     in sequence);
+ *   the per-path reductions z_p = diag(s_p) V_p^T X: the small-batch
+ *     kernels' per 4096-column chunk [chunks][batch][n_paths * rank] (fp32),
+ *     or wal_gemv's per 8192-column chunk [chunks][n_paths * rank] (fp32
+ *     value and u32 tag), whichever is larger;
  *   the small-batch kernels' partial sums per 1024-column slice
  *     [ceil(in / 1024)][batch][out] (fp32).
  * wal_gemv uses the last part only for matrices wider than one pass.
@@ -226,7 +237,7 @@ int wal_workspace_size(const wal_info* info, uint32_t batch, size_t* bytes);
  * workgroup whose wait gives up computes the terms itself.  A matrix wider than one pass (4096 columns,
  * 5120 for base-3 codes) has its passes in separate workgroups when the
  * workspace is wal_workspace_size(info, 1) bytes; the workgroup that
- * completes a row block adds its passes in pass order.
+ * completes a 16-row group adds its passes in pass order.
  *   info   host view of the blob (from wal_inspect / wal_pack)
  *   W_dev  the blob in device memory, 256-byte aligned
  *   x_dev  [in] activations, fp32 or bf16 (x_dtype), 16-byte aligned
@@ -320,21 +331,26 @@ int wal_gemm_prefill(const wal_info* info, const void* W_dev, const void* X_dev,
  *      contiguous ranges of equal packed bytes, one per workgroup of that
  *      class's streaming launch.  grid = 0 asks for the number of
  *      workgroups the current device holds at once (a HIP query; the other
- *      steps of planning are host-only), capped at one per 16 rows.
+ *      steps of planning are host-only), capped at one per 16 rows of a
+ *      pass.  A class with fewer 16-row groups than workgroups runs the
+ *      passes of its wider matrices in separate workgroups (their partial
+ *      sums in the workspace, added in pass order by the workgroup that
+ *      completes a 16-row group).
  *   2. The caller copies the plan blob into device memory (plan_dev, 16-byte
  *      aligned) and calls wal_gemv_grouped, as often as it likes while the
- *      pointers stay valid.  The plan holds WAL_SYNC_BYTES of
- *      synchronisation words at byte offset WAL_PLAN_SYNC_OFFSET, written as
- *      zero by the planner: a call's first streaming launch computes the
- *      low-rank terms in its first workgroups and the streaming workgroups
- *      wait for them (bounded) only when they store their rows.  Every call
- *      returns the words to zero, except the diagnostic count
- *      WAL_SYNC_FALLBACK_WORD (workgroups whose wait gave up and which
- *      computed the terms themselves; outputs stay exact).  Calls with one
- *      plan must be ordered (one stream).
+ *      pointers stay valid.  A call's first streaming launch computes the
+ *      low-rank terms in its first workgroups, and the streaming workgroups
+ *      wait for them (bounded) only when they store their rows; a
+ *      workgroup whose wait gives up computes them itself.
  * All matrices share x_dtype; base-3 matrices need bf16 activations
  * (WAL_ERR_UNSUPPORTED otherwise).  ws_dev must hold
- * wal_grouped_plan_size's ws_bytes.
+ * wal_grouped_plan_size's ws_bytes, 16-byte aligned (NULL when that is 0).
+ * When the plan has low-rank paths or split matrices, the workspace starts
+ * with the zero region of wal_workspace_size (WAL_WS_ZERO_BYTES, zero before
+ * its first use, left so by every call except the diagnostic count
+ * WAL_SYNC_FALLBACK_WORD and the epoch words); one workspace may serve any
+ * number of plans, products and shapes in turn.  Calls that share a
+ * workspace must be ordered (one stream).
  * Errors: ARG, SHAPE, ALIGN, BUFFER, UNSUPPORTED, DEVICE. */
 int wal_grouped_plan_size(uint32_t n, const wal_info* infos, uint32_t grid, int x_dtype,
                           size_t* plan_bytes, size_t* ws_bytes);
@@ -353,7 +369,6 @@ int wal_gemv_grouped(const wal_grouped_info* ginfo, const void* plan_dev, void* 
  * pre-pass inside the first streaming launch).
  * Errors: those of wal_gemv_grouped; ARG for an empty or unknown mask. */
 enum { WAL_PHASE_LOWRANK = 1, WAL_PHASE_STREAM = 2, WAL_PHASE_ALL = 3 };
-#define WAL_PLAN_SYNC_OFFSET 64
 int wal_gemv_grouped_phases(const wal_grouped_info* ginfo, const void* plan_dev, int phases,
                             void* stream);
 

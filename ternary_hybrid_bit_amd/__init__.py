@@ -29,7 +29,6 @@ WAL_SYNC_BYTES = 4352
 WAL_MAX_ROW_BLOCKS = 4096
 WAL_WS_ZERO_BYTES = WAL_SYNC_BYTES + 4 * WAL_MAX_ROW_BLOCKS
 WAL_SYNC_FALLBACK_WORD = 0
-WAL_PLAN_SYNC_OFFSET = 64
 
 STATUS = {0: "WAL_OK", -1: "WAL_ERR_ARG", -2: "WAL_ERR_SHAPE", -3: "WAL_ERR_CODE",
           -4: "WAL_ERR_INEXACT", -5: "WAL_ERR_BUFFER", -6: "WAL_ERR_ALIGN", -7: "WAL_ERR_FORMAT",
@@ -62,13 +61,13 @@ WAL_MAX_CLASSES = 16
 
 class wal_grouped_info(ctypes.Structure):
     _fields_ = [("n", ctypes.c_uint32), ("n_classes", ctypes.c_uint32), ("n_segs", ctypes.c_uint32),
-                ("n_zjobs", ctypes.c_uint32), ("x_dtype", ctypes.c_uint32), ("trit_fmt", ctypes.c_uint32),
+                ("n_zjobs", ctypes.c_uint32), ("x_dtype", ctypes.c_uint32), ("zjob_terms", ctypes.c_uint32),
                 ("rows_per_batch", ctypes.c_uint32), ("grid", ctypes.c_uint32),
                 ("plan_bytes", ctypes.c_uint64), ("algorithmic_bytes", ctypes.c_uint64),
                 ("off_descs", ctypes.c_uint64), ("off_zjobs", ctypes.c_uint64),
                 ("class_id", ctypes.c_uint32 * WAL_MAX_CLASSES), ("class_grid", ctypes.c_uint32 * WAL_MAX_CLASSES),
                 ("class_blockseg", ctypes.c_uint64 * WAL_MAX_CLASSES),
-                ("class_segs", ctypes.c_uint64 * WAL_MAX_CLASSES)]
+                ("class_segs", ctypes.c_uint64 * WAL_MAX_CLASSES), ("sync_dev", ctypes.c_void_p)]
 
 
 if not os.path.exists(LIB_PATH):
@@ -231,19 +230,18 @@ def _ws_bytes(ws, name: str = "ws") -> int:
     return ws.numel() * ws.element_size()
 
 
-def sync_fallbacks(buf, offset: int = 0) -> int:
-    """The fallback count of the synchronisation words at byte `offset` of a
-    device buffer (a workspace: 0; a device plan: WAL_PLAN_SYNC_OFFSET): the
+def sync_fallbacks(ws) -> int:
+    """The fallback count of a workspace's synchronisation words: the
     workgroups of earlier calls whose bounded wait for the low-rank terms
     gave up and which computed the terms themselves.  Synchronises the
     device."""
-    words = buf.view(-1).view(_torch().uint8)[offset:offset + WAL_SYNC_BYTES].view(_torch().int32)
+    words = ws.view(-1).view(_torch().uint8)[:WAL_SYNC_BYTES].view(_torch().int32)
     return int(words[WAL_SYNC_FALLBACK_WORD].item())
 
 
-def clear_sync_fallbacks(buf, offset: int = 0):
+def clear_sync_fallbacks(ws):
     """Clears that count (on the current stream)."""
-    words = buf.view(-1).view(_torch().uint8)[offset:offset + WAL_SYNC_BYTES].view(_torch().int32)
+    words = ws.view(-1).view(_torch().uint8)[:WAL_SYNC_BYTES].view(_torch().int32)
     words[WAL_SYNC_FALLBACK_WORD] = 0
 
 

@@ -399,12 +399,13 @@ __device__ __forceinline__ void run_segment_base3(const MatDev& d, uint32_t row0
 // Low-rank jobs of grouped plans and single products, as in the 2-bit
 // kernels (bf16 activations).
 __device__ __forceinline__ void z_job_grouped3(const MatDev* __restrict__ descs, const uint32_t* __restrict__ jobs,
-                                               uint32_t j) {
+                                               uint32_t j, uint32_t terms, const uint32_t* epoch) {
   const uint32_t m = jobs[2 * j], tc = jobs[2 * j + 1];
   const MatDev& d = descs[m];
   const uint32_t t0 = tc >> 16, cc = tc & 0xFFFFu;
   const uint32_t c0 = cc * kZChunkCols, c1 = min(d.in, c0 + kZChunkCols);
-  z_chunk<WAL_X_BF16, (int)kZTermsGrouped>(d, d.x, t0, d.z + (size_t)cc * d.terms, c0, c1);
+  z_job<WAL_X_BF16, ZJobsGrouped, kZOutTagged>(d, terms, t0, reinterpret_cast<uint64_t*>(d.z) + (size_t)cc * d.terms,
+                                              c0, c1, epoch);
 }
 
 template <int SF, int K>
@@ -415,14 +416,18 @@ __global__ __launch_bounds__(kThreads) void k_stream3_grouped(const MatDev* __re
   __shared__ Smem3 sm;
   const uint32_t t = blockIdx.x;
   if (t < f.nz) {
-    z_job_grouped3(descs, jobs, t);
-    publish_z(f);
+    z_job_grouped3(descs, jobs, t, zjob_terms<ZJobsGrouped>(f), epoch_of(f));
   } else {
     const uint32_t b = t - f.nz;
     const uint32_t s0 = blockseg[b], s1 = blockseg[b + 1];
     for (uint32_t s = s0; s < s1; ++s) {
       const Seg sg = segs[s];
-      run_segment_base3<SF, K, ZJobsGrouped>(descs[sg.mat], sg.row0, sg.row1, s == s0, sm, f);
+      const MatDev& d = descs[sg.mat];
+      if (sg.pass1)
+        run_segment_base3<SF, K, ZJobsGrouped>(d, sg.row0, sg.row1, s == s0, sm, f, d.P, sg.pass1 - 1,
+                                               f.sync + d.cnt_off);
+      else
+        run_segment_base3<SF, K, ZJobsGrouped>(d, sg.row0, sg.row1, s == s0, sm, f);
     }
   }
   finish_launch(f);
@@ -439,15 +444,15 @@ __global__ __launch_bounds__(kThreads) void k_stream3_single(MatDev d, uint32_t 
   if (t < f.nz) {
     const uint32_t tcs = (d.terms + kZTerms - 1) / kZTerms, tc = t % tcs, cc = t / tcs;
     const uint32_t c0 = cc * kZSingleCols, c1 = min(d.in, c0 + kZSingleCols);
-    z_chunk<WAL_X_BF16, (int)kZTerms>(d, d.x, tc * kZTerms, d.z + (size_t)cc * d.terms, c0, c1);
-    publish_z(f);
+    z_chunk<WAL_X_BF16, (int)kZTerms, kZOutTagged>(d, d.x, tc * kZTerms,
+                                                   reinterpret_cast<uint64_t*>(d.z) + (size_t)cc * d.terms, c0, c1,
+                                                   epoch_of(f));
   } else {
     const uint32_t b = t - f.nz;
     const uint32_t rb = P ? b % nrb : b;
     const uint32_t r0 = rb * rows_per_block;
     const uint32_t r1 = min(d.out, r0 + rows_per_block);
-    if (r0 < r1)
-      run_segment_base3<SF, K, ZJobsSingle>(d, r0, r1, true, sm, f, P, P ? b / nrb : 0u, P ? cnt + rb : nullptr);
+    if (r0 < r1) run_segment_base3<SF, K, ZJobsSingle>(d, r0, r1, true, sm, f, P, P ? b / nrb : 0u, cnt);
   }
   finish_launch(f);
 }

@@ -180,11 +180,12 @@ __device__ __forceinline__ float f16_at(const uint8_t* p, uint32_t i) {
 // Data that workgroups of one launch hand to each other (low-rank partials,
 // per-pass partial sums) moves through device-scope (agent) atomic stores
 // and loads: on this part they go to the device's coherence point, past the
-// CU and XCD caches, so a consumer that has seen the producer's count sees
-// the data without cache maintenance.  The producer's wave waits for its own
-// stores to complete (wait_stores) before the count is raised; agent-scope
-// release and acquire fences would instead write back or invalidate the
-// whole L2 of an XCD, which costs microseconds per workgroup here.
+// CU and XCD caches, so a consumer that has seen the producer's count (or
+// tag) sees the data without cache maintenance.  The producer's wave waits
+// for its own stores to complete (wait_stores) before a count is raised;
+// agent-scope release and acquire fences would instead write back or
+// invalidate the whole L2 of an XCD, which costs microseconds per workgroup
+// here.
 __device__ __forceinline__ void store_dev(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -195,21 +196,42 @@ __device__ __forceinline__ float load_dev(const float* p) {
 // have completed.
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Low-rank partials that a fused launch hands over carry a tag in the same
+// 64-bit word (one device-scope store and load each): a consumer that reads
+// a partial with the call's tag has its value, so one read both checks and
+// fetches it.
+__device__ __forceinline__ void store_tagged(uint64_t* p, float v, uint32_t tag) {
+  __hip_atomic_store(p, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t load_tagged(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float tagged_value(uint64_t w) { return __uint_as_float((uint32_t)w); }
+__device__ __forceinline__ uint32_t tagged_tag(uint64_t w) { return (uint32_t)(w >> 32); }
+
+// Where z_chunk writes: LDS floats, device floats (device-scope stores), or
+// tagged device words (with the tag read from *epoch: 2 epoch + 1; tag 0
+// without an epoch).
+enum ZOut { kZOutLds, kZOutDev, kZOutTagged };
+
 // ---------------------------------------------------------------------------
 // Low-rank reductions of one matrix by a whole workgroup:
 // z[t] = s_p[r] * sum_j (-1)^{V_p[r] bit j} x_j over the columns j in
 // [c0, c1) (multiples of 16) for the C terms t0 .. t0 + C - 1 (those below
-// d.terms), written to out[t] by threads t - t0: with device-scope stores
-// (see store_dev) for device memory that other workgroups of the same
-// launch read, plain stores for LDS (LDS_OUT).  Every thread of the
-// workgroup (up to 1024) calls it (it holds a barrier).
-template <int XT, int C, bool LDS_OUT = false>
-__device__ __forceinline__ void z_chunk(const MatDev& d, const void* x, uint32_t t0, float* out, uint32_t c0,
-                                        uint32_t c1) {
+// d.terms), written to out[t] by threads t - t0 as OUT says (out: float* for
+// floats, uint64_t* for tagged words).  Every thread of the workgroup (up to
+// 1024) calls it (it holds a barrier).
+template <int XT, int C, ZOut OUT>
+__device__ __forceinline__ void z_chunk(const MatDev& d, const void* x, uint32_t t0, void* out, uint32_t c0,
+                                        uint32_t c1, const uint32_t* epoch = nullptr) {
   __shared__ float red[16][C];
   const uint32_t tid = threadIdx.x, nthr = blockDim.x;
   const int lane = tid & 63;
   const uint32_t T = d.terms, vrow = d.in / 8;
+  // the writers' tag, read before the sweep (its latency overlaps it)
+  uint32_t tag = 0;
+  if constexpr (OUT == kZOutTagged)
+    if (epoch && tid < (uint32_t)C) tag = (__hip_atomic_load(epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) << 1) | 1u;
   // the per-rank scale of the thread's term, loaded before the sweep so its
   // latency is not paid after the barrier
   // (every thread loads a valid scale, without a branch, so that nothing
@@ -276,8 +298,9 @@ __device__ __forceinline__ void z_chunk(const MatDev& d, const void* x, uint32_t
       float sum = 0.f;
       for (uint32_t w = 0; w < (nthr >> 6); ++w) sum += red[w][tid];
       const float v = (float)__builtin_bit_cast(_Float16, (uint16_t)scale_bits) * sum;
-      if constexpr (LDS_OUT) out[t] = v;
-      else store_dev(out + t, v);
+      if constexpr (OUT == kZOutLds) static_cast<float*>(out)[t] = v;
+      else if constexpr (OUT == kZOutDev) store_dev(static_cast<float*>(out) + t, v);
+      else store_tagged(static_cast<uint64_t*>(out) + t, v, tag);
     }
   }
 }
@@ -285,81 +308,61 @@ __device__ __forceinline__ void z_chunk(const MatDev& d, const void* x, uint32_t
 // ---------------------------------------------------------------------------
 // Fused launches: the low-rank pre-pass in the first workgroups of the
 // streaming launch (see Fuse in wal_internal.h).  Producers write their jobs'
-// partials with device-scope stores and count them once the stores have
-// completed; consumers wait for all of them, only in their epilogue after
-// their streaming, with polls, and then read the partials with device-scope
-// loads.  Each word that the whole launch touches is read and written
-// through the workgroup's copy (blockIdx.x % kSyncReplicas).
+// partials as tagged words (store_tagged) with the call's tag; consumers, in
+// their epilogue after their streaming, read the partials they need and
+// retry (bounded) until every one carries the tag.  Each word that the whole
+// launch touches is read and written through the workgroup's copy
+// (blockIdx.x % kSyncReplicas).
 
-constexpr uint32_t kSpinLimit = 1u << 16;   // polls of a bounded wait (tens of ms)
+constexpr uint32_t kSpinLimit = 1u << 16;   // reads of a bounded wait (tens of ms)
 
-// Low-rank jobs as the producers of a launch run them: C terms of one
-// column chunk of `cols` columns each.  The fallback of a consumer whose
-// wait gave up runs the same jobs, so its terms are bit-identical.
-template <int C, uint32_t COLS>
+// Low-rank jobs as the producers of a launch run them: f.zterms terms of one
+// column chunk of kCols columns each (single products: kZTermsFew terms;
+// grouped plans: kZTermsFew or kZTermsMany, as planned).  The fallback of a
+// consumer whose wait gave up runs the same jobs, so its terms are
+// bit-identical.
+template <uint32_t COLS, bool TWO_SIZES>
 struct ZJobs {
-  static constexpr int kTerms = C;
   static constexpr uint32_t kCols = COLS;
+  static constexpr bool kTwoSizes = TWO_SIZES;
 };
-using ZJobsSingle = ZJobs<(int)kZTerms, kZSingleCols>;
-using ZJobsGrouped = ZJobs<(int)kZTermsGrouped, kZChunkCols>;
+using ZJobsSingle = ZJobs<kZSingleCols, false>;
+using ZJobsGrouped = ZJobs<kZChunkCols, true>;
+
+template <class ZJ>
+__device__ __forceinline__ uint32_t zjob_terms(const Fuse& f) {
+  return ZJ::kTwoSizes && f.zterms == kZTermsMany ? kZTermsMany : kZTermsFew;
+}
+
+// One job: terms t0 .. t0 + terms - 1 over columns [c0, c1) into out.
+template <int XT, class ZJ, ZOut OUT>
+__device__ __forceinline__ void z_job(const MatDev& d, uint32_t terms, uint32_t t0, void* out, uint32_t c0,
+                                      uint32_t c1, const uint32_t* epoch = nullptr) {
+  if constexpr (ZJ::kTwoSizes) {
+    if (terms == kZTermsMany) {
+      z_chunk<XT, (int)kZTermsMany, OUT>(d, d.x, t0, out, c0, c1, epoch);
+      return;
+    }
+  }
+  z_chunk<XT, (int)kZTermsFew, OUT>(d, d.x, t0, out, c0, c1, epoch);
+}
 
 __device__ __forceinline__ uint32_t* sync_copy(const Fuse& f, uint32_t word) {
   return f.sync + word + kSyncLine * (blockIdx.x % kSyncReplicas);
 }
 
-// A finished low-rank job (device-scope stores by any thread of the
-// workgroup) becomes visible to the consumers: every wave waits for its own
-// stores before the barrier, then one lane per copy counts the job.  Every
-// thread calls it.
-__device__ __forceinline__ void publish_z(const Fuse& f) {
-  wait_stores();
-  __syncthreads();
-  if (threadIdx.x < kSyncReplicas)
-    __hip_atomic_fetch_add(f.sync + kSyncZDone + kSyncLine * threadIdx.x, 1u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+// The epoch copy a producer's tag comes from (null: untagged, tag 0).
+__device__ __forceinline__ const uint32_t* epoch_of(const Fuse& f) {
+  return f.sync ? sync_copy(f, kSyncEpoch) : nullptr;
 }
 
-// Waits until every low-rank job of the call is published; true when they
-// are (then device-scope loads of the terms see them: the loads follow the
-// poll that saw the count).
-// Bounded: on expiry the fallback count is raised and false returned, and
-// so at once for the later waiters of a call in which a wait expired (the
-// gave-up word, which the call's last workgroup clears).  Every thread
-// calls it.
-__device__ __forceinline__ uint32_t poll_z(const Fuse& f) {
-  return __hip_atomic_load(sync_copy(f, kSyncZDone), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// `seen`: thread 0's first poll (poll_z), issued early by the caller so that
-// its latency overlaps other loads.
-__device__ __forceinline__ bool wait_z(const Fuse& f, uint32_t seen) {
-  if (!f.zwait) return true;
-  __shared__ uint32_t s_ok;
-  if (threadIdx.x == 0) {
-    uint32_t n = 0, ok = 1;
-    for (; seen != f.zwait; seen = poll_z(f)) {
-      if (__hip_atomic_load(f.sync + kSyncGaveUp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) || ++n == kSpinLimit) {
-        __hip_atomic_store(f.sync + kSyncGaveUp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_fetch_add(f.sync + kSyncFallback, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ok = 0;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
-    }
-    s_ok = ok;
-  }
-  __syncthreads();
-  return __builtin_amdgcn_readfirstlane(s_ok) != 0;
-}
-
-// The last workgroup of the launch to finish returns its slot's words (and
-// the jobs-published copies and the gave-up word, after the call's last
-// launch) to zero.  Copy r
-// counts the workgroups b % kSyncReplicas == r; the one that completes a
-// copy counts it in line 0, and the one that completes the last copy resets.
-// No data changes hands here: the counts order nothing but the reset.
-// Every thread calls it.
+// The last workgroup of the launch to finish returns its slot's words to
+// zero and, after the call's last launch, clears the gave-up word and moves
+// every epoch copy to one past its own (which also mends copies that
+// disagree).  Copy r counts the workgroups b % kSyncReplicas == r; the one
+// that completes a copy counts it in line 0, and the one that completes the
+// last copy resets.  No data changes hands here: the counts order nothing
+// but the reset.  Every thread calls it.
 __device__ __forceinline__ void finish_launch(const Fuse& f) {
   if (!f.sync) return;
   __syncthreads();
@@ -376,9 +379,10 @@ __device__ __forceinline__ void finish_launch(const Fuse& f) {
         __hip_atomic_store(f.sync + kSyncFinished + kSyncLine * c + f.slot, 0u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(f.sync + kSyncSlotsDone + f.slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (f.reset_z) {
+      if (f.last) {
+        const uint32_t next = __hip_atomic_load(sync_copy(f, kSyncEpoch), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
         for (uint32_t c = 0; c < kSyncReplicas; ++c)
-          __hip_atomic_store(f.sync + kSyncZDone + kSyncLine * c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(f.sync + kSyncEpoch + kSyncLine * c, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(f.sync + kSyncGaveUp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
@@ -402,50 +406,110 @@ struct SegEnd {
   float* ybuf;   // LDS, the segment's rows
 };
 
-// z = the sum of the low-rank partials in chunk order, from the workspace, or
-// (after a wait that gave up) computed here by the producers' jobs, chunk by
-// chunk, each chunk's partials staged in tbl.  Every thread calls it
-// (barriers).
-template <int XT, class ZJ>
-__device__ __forceinline__ void lowrank_z(const MatDev& d, const SegEnd& e, const Fuse& f, uint32_t seen) {
-  const uint32_t t = threadIdx.x;
-  if (wait_z(f, seen)) {
-    if (t < d.terms) {
-      float z = 0.f;
-      for (uint32_t cc = 0; cc < d.zc; ++cc) z += load_dev(d.z + cc * d.terms + t);
-      e.z[t] = z;
-    }
-    return;
-  }
+// One read of the partials of term t: their sum in chunk order, and whether
+// each carries `tag` (tag 0: any).  Up to kAhead chunks are loaded before
+// any is used, so they cost one round trip.
+__device__ __forceinline__ bool read_partials(const MatDev& d, uint32_t t, uint32_t tag, float* sum) {
+  constexpr uint32_t kAhead = 4;
+  const uint64_t* zt = reinterpret_cast<const uint64_t*>(d.z) + t;
+  uint64_t w[kAhead];
+#pragma unroll
+  for (uint32_t k = 0; k < kAhead; ++k) w[k] = k < d.zc ? load_tagged(zt + (size_t)k * d.terms) : 0;
   float z = 0.f;
-  for (uint32_t cc = 0; cc < d.zc; ++cc) {
-    const uint32_t c0 = cc * ZJ::kCols, c1 = min(d.in, c0 + ZJ::kCols);
-    for (uint32_t t0 = 0; t0 < d.terms; t0 += ZJ::kTerms) {
-      z_chunk<XT, ZJ::kTerms, true>(d, d.x, t0, e.tbl, c0, c1);
-      __syncthreads();   // z_chunk's reduction buffer is read before the next job writes it
+  bool ok = true;
+#pragma unroll
+  for (uint32_t k = 0; k < kAhead; ++k) {
+    if (k < d.zc) {
+      z += tagged_value(w[k]);
+      ok = ok && (tag == 0 || tagged_tag(w[k]) == tag);
     }
-    if (t < d.terms) z += e.tbl[t];
-    __syncthreads();
   }
-  if (t < d.terms) e.z[t] = z;
+  for (uint32_t k = kAhead; k < d.zc; ++k) {
+    const uint64_t v = load_tagged(zt + (size_t)k * d.terms);
+    z += tagged_value(v);
+    ok = ok && (tag == 0 || tagged_tag(v) == tag);
+  }
+  *sum = z;
+  return ok;
 }
 
-// Builds the byte tables (after the low-rank terms are complete).  Every
-// thread calls it (barriers).
-template <int XT, class ZJ>
-__device__ __forceinline__ void lowrank_tables(const MatDev& d, const SegEnd& e, const Fuse& f, uint32_t seen) {
-  lowrank_z<XT, ZJ>(d, e, f, seen);
-  __syncthreads();
-  const uint32_t t = threadIdx.x;
-  const uint32_t ub = (d.rank + 7) / 8, ntab = d.n_paths * ub;
-  for (uint32_t i = t; i < ntab * 256; i += blockDim.x) {
-    const uint32_t tab = i >> 8, u = i & 255u, p = tab / ub, b = tab % ub;
-    float sum = 0.f;
-    for (uint32_t k = 0; k < 8 && 8 * b + k < d.rank; ++k) {
-      const float zt = e.z[p * d.rank + 8 * b + k];
-      sum += ((u >> k) & 1u) ? -zt : zt;
+// The fallback of a consumer whose wait gave up: z computed here, one thread
+// per term over every column in order (few registers: it must not weigh on
+// the streaming code that shares its kernel; it runs only if a wait expires,
+// and its sums, in another order than the producers', agree with theirs to
+// rounding).  Every thread calls it.
+template <int XT>
+__device__ __forceinline__ void lowrank_z_here(const MatDev& d, const SegEnd& e) {
+  const uint32_t vrow = d.in / 8;
+  for (uint32_t t = threadIdx.x; t < d.terms; t += blockDim.x) {
+    const uint32_t p = t / d.rank, r = t % d.rank;
+    const uint16_t* bits = reinterpret_cast<const uint16_t*>(path_plane(d.V, d, p) + (size_t)r * vrow);
+    float z = 0.f;
+    for (uint32_t c = 0; c < d.in; c += 16) {
+      const uint32_t v = bits[c / 16];
+      for (uint32_t j = 0; j < 16; ++j) {
+        float xj;
+        if constexpr (XT == WAL_X_BF16)
+          xj = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(d.x)[c + j] << 16);
+        else
+          xj = reinterpret_cast<const float*>(d.x)[c + j];
+        z += ((v >> j) & 1u) ? -xj : xj;
+      }
     }
-    e.tbl[i] = sum;
+    e.z[t] = (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(path_plane(d.s, d, p))[r]) * z;
+  }
+}
+
+// z = the sum of the low-rank partials in chunk order, from the workspace:
+// with f.zwait, read until every partial carries the call's tag (the tag,
+// from the epoch, is read in the same round trip) — bounded.  False when the
+// wait gave up (then the caller computes z with lowrank_z_here).  Every
+// thread calls it (barriers).
+__device__ __forceinline__ bool lowrank_z_read(const MatDev& d, const SegEnd& e, const Fuse& f) {
+  const uint32_t t = threadIdx.x;
+  __shared__ uint32_t s_miss, s_give;
+  const uint32_t* ep = f.zwait ? sync_copy(f, kSyncEpoch) : nullptr;
+  for (uint32_t n = 1;; ++n) {
+    if (t == 0) s_miss = 0;
+    __syncthreads();
+    if (t < d.terms) {
+      const uint32_t tag = ep ? (__hip_atomic_load(ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) << 1) | 1u : 0u;
+      float z;
+      if (!read_partials(d, t, tag, &z)) s_miss = 1;
+      e.z[t] = z;
+    }
+    __syncthreads();
+    if (!__builtin_amdgcn_readfirstlane(s_miss)) return true;
+    // not all there yet: read again, bounded; on expiry, or once another
+    // workgroup of the call gave up, compute the terms here
+    if (t == 0) {
+      const bool give = n == kSpinLimit || __hip_atomic_load(f.sync + kSyncGaveUp, __ATOMIC_RELAXED,
+                                                               __HIP_MEMORY_SCOPE_AGENT);
+      if (give) {
+        __hip_atomic_store(f.sync + kSyncGaveUp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(f.sync + kSyncFallback, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      s_give = give;
+    }
+    __syncthreads();
+    if (__builtin_amdgcn_readfirstlane(s_give)) return false;
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// The byte tables from z: thread u builds entry u of every table.  Every
+// thread calls it (barrier).
+__device__ __forceinline__ void lowrank_build(const MatDev& d, const SegEnd& e) {
+  const uint32_t ub = (d.rank + 7) / 8;
+  for (uint32_t u = threadIdx.x; u < 256; u += blockDim.x) {
+    float* out = e.tbl + u;
+    const float* z = e.z;
+    for (uint32_t p = 0; p < d.n_paths; ++p, z += d.rank)
+      for (uint32_t b = 0; b < ub; ++b, out += 256) {
+        float sum = 0.f;
+        for (uint32_t k = 0; k < 8 && 8 * b + k < d.rank; ++k) sum += ((u >> k) & 1u) ? -z[8 * b + k] : z[8 * b + k];
+        *out = sum;
+      }
   }
   __syncthreads();
 }
@@ -453,19 +517,21 @@ __device__ __forceinline__ void lowrank_tables(const MatDev& d, const SegEnd& e,
 // The U bytes of one row, loaded ahead of the tables: per path the eight
 // bytes from the dword holding the row's first U byte (a row's ub <= 4 U
 // bytes per path then lie inside them).  Reads past the blob return zero.
+constexpr uint32_t kUAheadPaths = 2;
 struct UAhead {
-  uint64_t w[WAL_MAX_PATHS];
+  uint64_t w[kUAheadPaths];
   uint32_t sh;   // bit offset of the row's first byte in each window
 };
 
-__device__ __forceinline__ bool u_ahead_fits(const MatDev& d) { return d.rank <= 32; }
+// rows of at most 4 U bytes per path and at most kUAheadPaths paths
+__device__ __forceinline__ bool u_ahead_fits(const MatDev& d) { return d.rank <= 32 && d.n_paths <= kUAheadPaths; }
 
 __device__ __forceinline__ UAhead load_u_ahead(const MatDev& d, __amdgpu_buffer_rsrc_t ru, uint32_t row) {
   const uint32_t ub = (d.rank + 7) / 8, o = (uint32_t)(d.U - d.codes) + row * ub;
   UAhead u;
   u.sh = 8 * (o & 3u);
 #pragma unroll
-  for (uint32_t p = 0; p < WAL_MAX_PATHS; ++p) {
+  for (uint32_t p = 0; p < kUAheadPaths; ++p) {
     const uint32_t a = (o & ~3u) + p * d.pstride;
     const uint32_t lo = p < d.n_paths ? __builtin_amdgcn_raw_buffer_load_b32(ru, a, 0, 0) : 0u;
     const uint32_t hi = p < d.n_paths ? __builtin_amdgcn_raw_buffer_load_b32(ru, a + 4, 0, 0) : 0u;
@@ -474,15 +540,28 @@ __device__ __forceinline__ UAhead load_u_ahead(const MatDev& d, __amdgpu_buffer_
   return u;
 }
 
-// Low-rank term of a row from the byte tables and its U bytes loaded ahead.
+// Low-rank term of a row from its U bytes loaded ahead: from the byte
+// tables, or (direct) from z with the tables' own arithmetic, entry by entry
+// in the same order, so both give the same bits.
+template <bool DIRECT>
 __device__ __forceinline__ float lowrank_row_ahead(const MatDev& d, const SegEnd& e, const UAhead& u) {
   const uint32_t ub = (d.rank + 7) / 8;
   float c = 0.f;
 #pragma unroll
-  for (uint32_t p = 0; p < WAL_MAX_PATHS; ++p) {
+  for (uint32_t p = 0; p < kUAheadPaths; ++p) {
     if (p < d.n_paths) {
       const uint64_t w = u.w[p] >> u.sh;
-      for (uint32_t b = 0; b < ub; ++b) c += e.tbl[(p * ub + b) * 256 + ((uint32_t)(w >> (8 * b)) & 255u)];
+      for (uint32_t b = 0; b < ub; ++b) {
+        const uint32_t byte = (uint32_t)(w >> (8 * b)) & 255u;
+        if constexpr (DIRECT) {
+          const float* z = e.z + p * d.rank + 8 * b;
+          float sum = 0.f;
+          for (uint32_t k = 0; k < 8 && 8 * b + k < d.rank; ++k) sum += ((byte >> k) & 1u) ? -z[k] : z[k];
+          c += sum;
+        } else {
+          c += e.tbl[(p * ub + b) * 256 + byte];
+        }
+      }
     }
   }
   return c;
@@ -502,10 +581,11 @@ __device__ __forceinline__ float lowrank_row(const MatDev& d, const SegEnd& e, _
 
 // Stores the segment: y = ybuf (+ the low-rank term when the matrix has
 // paths).  With P (a split product: this workgroup computed one pass of the
-// rows), the partial sums go to P[pass] instead; the workgroup that completes
-// a row block (cnt[rb] counts the passes stored) adds all npass planes in
-// pass order with the low-rank term and stores y, and returns cnt[rb] to
-// zero.  Every thread calls it (barriers).
+// rows, row0 a multiple of 16), the partial sums go to P[pass] instead, and
+// each 16-row group of the segment counts one arrival in cnt[row / 16]; the
+// workgroup whose arrival completes a group (npass arrivals) adds its rows'
+// npass planes in pass order with the low-rank term, stores y, and returns
+// the counter to zero.  Every thread calls it (barriers).
 template <int XT, class ZJ>
 __device__ __forceinline__ void store_segment(const MatDev& d, uint32_t row0, uint32_t row1, const SegEnd& e,
                                               const Fuse& f, float* P = nullptr, uint32_t pass = 0,
@@ -513,20 +593,30 @@ __device__ __forceinline__ void store_segment(const MatDev& d, uint32_t row0, ui
   __syncthreads();   // the segment's y is complete; the site table's readers are done
   const uint32_t nrows = row1 - row0;
   const __amdgpu_buffer_rsrc_t ru = rsrc(d.codes, d.blob_bytes);
+  // groups of 16 rows whose last arrival this workgroup made (split only;
+  // ybuf is free once the partial sums are stored)
+  uint32_t* mine = reinterpret_cast<uint32_t*>(e.ybuf);
   if (P) {
     for (uint32_t i = threadIdx.x; i < nrows; i += blockDim.x) store_dev(P + (size_t)pass * d.out + row0 + i, e.ybuf[i]);
-    wait_stores();   // each wave's partial sums, before the count
+    wait_stores();   // each wave's partial sums, before the counts
+    __shared__ uint32_t s_any;
+    if (threadIdx.x == 0) s_any = 0;
     __syncthreads();
-    __shared__ uint32_t s_last;
-    if (threadIdx.x == 0) {
-      const uint32_t arrived = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_last = arrived + 1 == npass;
-      if (s_last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t g0 = row0 / 16, ng = (nrows + 15) / 16;
+    for (uint32_t t = threadIdx.x; t < ng; t += blockDim.x) {
+      const uint32_t arrived = __hip_atomic_fetch_add(cnt + g0 + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const bool last = arrived + 1 == npass;
+      if (last) {
+        __hip_atomic_store(cnt + g0 + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_any = 1;
+      }
+      mine[t] = last;
     }
     __syncthreads();
-    if (!__builtin_amdgcn_readfirstlane(s_last)) return;   // not the row block's last pass
+    if (!__builtin_amdgcn_readfirstlane(s_any)) return;   // no group completed here
     if (!d.terms) {
       for (uint32_t i = threadIdx.x; i < nrows; i += blockDim.x) {
+        if (!mine[i / 16]) continue;
         const uint32_t row = row0 + i;
         float v = load_dev(P + row);
         for (uint32_t q = 1; q < npass; ++q) v += load_dev(P + (size_t)q * d.out + row);
@@ -538,24 +628,43 @@ __device__ __forceinline__ void store_segment(const MatDev& d, uint32_t row0, ui
     for (uint32_t i = threadIdx.x; i < nrows; i += blockDim.x) d.y[row0 + i] = e.ybuf[i];
     return;
   }
-  // The low-rank term.  Thread 0's first poll of the jobs-published count
-  // and every thread's U bytes for its first row go out together, so their
-  // latencies overlap.
-  const uint32_t seen = f.zwait && threadIdx.x == 0 ? poll_z(f) : 0u;
+  // The low-rank term.  Every thread's U bytes for its first row go out
+  // before the partials are read, so their latencies overlap.  A segment of
+  // at most one row per thread needs no tables: each row's term comes
+  // straight from z.
   const bool ahead = u_ahead_fits(d);
   const uint32_t i0 = threadIdx.x;
-  const UAhead ua = load_u_ahead(d, ru, row0 + min(i0, nrows - 1));
-  lowrank_tables<XT, ZJ>(d, e, f, seen);
+  const uint32_t urow = row0 + min(i0, nrows - 1);
+  const UAhead ua = load_u_ahead(d, ru, urow);
+  if (!lowrank_z_read(d, e, f)) lowrank_z_here<XT>(d, e);   // the rare fallback
+  __syncthreads();
+  if (ahead && nrows <= blockDim.x) {
+    if (i0 < nrows) {
+      const uint32_t row = row0 + i0;
+      float v;
+      if (P) {
+        if (!mine[i0 / 16]) return;
+        v = load_dev(P + row);
+        for (uint32_t q = 1; q < npass; ++q) v += load_dev(P + (size_t)q * d.out + row);
+      } else {
+        v = e.ybuf[i0];
+      }
+      d.y[row] = v + lowrank_row_ahead<true>(d, e, ua);
+    }
+    return;
+  }
+  lowrank_build(d, e);
   for (uint32_t i = i0; i < nrows; i += blockDim.x) {
     const uint32_t row = row0 + i;
     float v;
     if (P) {
+      if (!mine[i / 16]) continue;
       v = load_dev(P + row);
       for (uint32_t q = 1; q < npass; ++q) v += load_dev(P + (size_t)q * d.out + row);
     } else {
       v = e.ybuf[i];
     }
-    d.y[row] = v + (ahead && i == i0 ? lowrank_row_ahead(d, e, ua) : lowrank_row(d, e, ru, row));
+    d.y[row] = v + (ahead && i == i0 ? lowrank_row_ahead<false>(d, e, ua) : lowrank_row(d, e, ru, row));
   }
 }
 

@@ -76,7 +76,7 @@ __device__ __forceinline__ void z_block(const MatDev& d, float* __restrict__ zpa
   const void* x = reinterpret_cast<const uint16_t*>(d.x) + (size_t)n * d.ldx;
   float* out = zpart + ((size_t)cc * d.batch + n) * d.terms;
   const uint32_t c0 = cc * kZChunkCols, c1 = min(d.in, c0 + kZChunkCols);
-  z_chunk<WAL_X_BF16, (int)kZTermsPerBlock>(d, x, tc * kZTermsPerBlock, out, c0, c1);
+  z_chunk<WAL_X_BF16, (int)kZTermsPerBlock, kZOutDev>(d, x, tc * kZTermsPerBlock, out, c0, c1);
 }
 
 uint32_t z_blocks(const MatDev& d, const GemmShape& S) {

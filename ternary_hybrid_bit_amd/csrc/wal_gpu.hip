@@ -5,16 +5,17 @@
 // computed straight from the packed planes described in include/wal.h.
 //
 // Kernels:
-//  * the binary low-rank reductions z_p[r] = s_p[r] * sum_j (-1)^{V bit} x_j,
-//    a pre-pass into the caller's workspace: kZTerms terms per workgroup for
-//    grouped products (k_z_grouped), kZTerms terms x 4096 columns per
-//    workgroup for a single product (k_z_chunks, partial sums that the
-//    streaming kernel adds), so that wide matrices get enough workgroups.
-//  * k_stream_*: one streaming pass over the packed planes.  Every workgroup
-//    owns a contiguous range of rows of one or more matrices (for grouped
-//    products the host splits the total packed bytes evenly over a grid that
-//    fits the GPU at once, so no workgroup waits for another).  Inside a
-//    range, the 4 wavefronts take batches of RB rows in turn:
+//  * k_stream_*: one launch per product (per (scale format, k) class of a
+//    grouped plan).  Its first workgroups compute the binary low-rank
+//    reductions z_p[r] = s_p[r] * sum_j (-1)^{V bit} x_j as jobs of a few
+//    terms over a column chunk (partial sums per chunk, in the workspace);
+//    the others stream the packed planes and wait for those jobs only in
+//    their epilogue (wal_device.h, fused launches).
+//    A streaming workgroup owns a contiguous range of rows of one or more
+//    matrices (for grouped products the host splits the total packed bytes
+//    evenly over a grid that fits the GPU at once), or one pass of a row
+//    block of a wide single product.  Inside a range, the 4 wavefronts take
+//    batches of RB rows in turn:
 //      - codes: each lane owns 64 consecutive columns of a 4096-column pass
 //        and reads its 16 bytes of 2-bit codes per row with one buffer load,
 //        so a wavefront reads a 1 KB row segment fully coalesced.  Row
@@ -34,9 +35,10 @@
 //        partial once per row in fp32 (fp16 scales feed v_fma_mix directly).
 //      - rows: the RB row partials of a lane are reduced across the
 //        wavefront with one transposed butterfly (permlane swaps and DPP), so
-//        each row's total lands in 64/RB lanes; those lanes add the low-rank
-//        term sum_t (-1)^{U bit} z_t (one term per lane) and one of them
-//        stores y.  Matrices wider than one pass accumulate y pass by pass.
+//        each row's total lands in 64/RB lanes, one of which keeps it in LDS.
+//        Matrices wider than one pass accumulate it pass by pass.
+//      - epilogue: tables of signed z sums, one per path and U byte, turn the
+//        low-rank term of a row into one LDS lookup per U byte; then y.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -46,6 +48,7 @@
 #include <cstring>
 #include <mutex>
 #include <new>
+#include <vector>
 
 #include "wal_device.h"
 #include "wal_internal.h"
@@ -375,16 +378,17 @@ constexpr int stream_waves_per_simd(int XT, int SF, int K) {
 }
 
 // Low-rank job of a fused launch or of the grouped pre-pass: terms t0 ..
-// t0 + kZTermsGrouped - 1 of matrix m over columns [4096 cc, 4096 cc + 4096)
-// into its partials z[cc][t] (jobs[2 j] = m, jobs[2 j + 1] = t0 << 16 | cc).
+// t0 + terms - 1 of matrix m over columns [4096 cc, 4096 cc + 4096) into its
+// partials z[cc][t] (jobs[2 j] = m, jobs[2 j + 1] = t0 << 16 | cc).
 template <int XT>
 __device__ __forceinline__ void grouped_z_job(const MatDev* __restrict__ descs, const uint32_t* __restrict__ jobs,
-                                              uint32_t j) {
+                                              uint32_t j, uint32_t terms, const uint32_t* epoch) {
   const uint32_t m = jobs[2 * j], tc = jobs[2 * j + 1];
   const MatDev& d = descs[m];
   const uint32_t t0 = tc >> 16, cc = tc & 0xFFFFu;
   const uint32_t c0 = cc * kZChunkCols, c1 = min(d.in, c0 + kZChunkCols);
-  z_chunk<XT, (int)kZTermsGrouped>(d, d.x, t0, d.z + (size_t)cc * d.terms, c0, c1);
+  z_job<XT, ZJobsGrouped, kZOutTagged>(d, terms, t0, reinterpret_cast<uint64_t*>(d.z) + (size_t)cc * d.terms, c0, c1,
+                                      epoch);
 }
 
 // Grouped products: workgroup t = blockIdx.x computes low-rank job t when
@@ -396,25 +400,29 @@ void k_stream_grouped(const MatDev* __restrict__ descs, const uint32_t* __restri
   __shared__ StreamSmem sm;
   const uint32_t t = blockIdx.x;
   if (t < f.nz) {
-    grouped_z_job<XT>(descs, jobs, t);
-    publish_z(f);
+    grouped_z_job<XT>(descs, jobs, t, zjob_terms<ZJobsGrouped>(f), epoch_of(f));
   } else {
     const uint32_t b = t - f.nz;
     const uint32_t s0 = blockseg[b], s1 = blockseg[b + 1];
     for (uint32_t s = s0; s < s1; ++s) {
       const Seg sg = segs[s];
-      run_segment_2bit<XT, SF, K, RB, ZJobsGrouped>(descs[sg.mat], sg.row0, sg.row1, sm, f);
+      const MatDev& d = descs[sg.mat];
+      if (sg.pass1)
+        run_segment_2bit<XT, SF, K, RB, ZJobsGrouped>(d, sg.row0, sg.row1, sm, f, d.P, sg.pass1 - 1,
+                                                      f.sync + d.cnt_off);
+      else
+        run_segment_2bit<XT, SF, K, RB, ZJobsGrouped>(d, sg.row0, sg.row1, sm, f);
     }
   }
   finish_launch(f);
 }
 
-// Single products: workgroup t = blockIdx.x < f.nz computes the low-rank partials of terms
-// kZTerms tc .. kZTerms tc + kZTerms - 1 over columns [8192 cc, 8192 cc +
-// 8192) into d.z[cc][t] (t = cc tcs + tc); the others stream.  Without P,
-// block b takes rows [b rpb, b rpb + rpb) over every pass; with P, block b
-// takes pass b / nrb of row block b % nrb (cnt: the row blocks' arrival
-// counters).
+// Single products: workgroup t = blockIdx.x < f.nz computes the low-rank
+// partials of terms kZTerms tc .. kZTerms tc + kZTerms - 1 over columns
+// [8192 cc, 8192 cc + 8192) into d.z[cc][t] (t = cc tcs + tc); the others
+// stream.  Without P, block b takes rows [b rpb, b rpb + rpb) over every
+// pass; with P, block b takes pass b / nrb of row block b % nrb (rpb a
+// multiple of 16; cnt: the arrival counters, one per 16 rows).
 template <int XT, int SF, int K, int RB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(stream_waves_per_simd(XT, SF, K))))
 void k_stream_single(MatDev d, uint32_t rows_per_block, uint32_t nrb, float* P, uint32_t* cnt, Fuse f) {
@@ -423,15 +431,14 @@ void k_stream_single(MatDev d, uint32_t rows_per_block, uint32_t nrb, float* P, 
   if (t < f.nz) {
     const uint32_t tcs = (d.terms + kZTerms - 1) / kZTerms, tc = t % tcs, cc = t / tcs;
     const uint32_t c0 = cc * kZSingleCols, c1 = min(d.in, c0 + kZSingleCols);
-    z_chunk<XT, (int)kZTerms>(d, d.x, tc * kZTerms, d.z + (size_t)cc * d.terms, c0, c1);
-    publish_z(f);
+    z_chunk<XT, (int)kZTerms, kZOutTagged>(d, d.x, tc * kZTerms, reinterpret_cast<uint64_t*>(d.z) + (size_t)cc * d.terms,
+                                           c0, c1, epoch_of(f));
   } else {
     const uint32_t b = t - f.nz;
     const uint32_t rb = P ? b % nrb : b;
     const uint32_t r0 = rb * rows_per_block;
     const uint32_t r1 = min(d.out, r0 + rows_per_block);
-    if (r0 < r1)
-      run_segment_2bit<XT, SF, K, RB, ZJobsSingle>(d, r0, r1, sm, f, P, P ? b / nrb : 0u, P ? cnt + rb : nullptr);
+    if (r0 < r1) run_segment_2bit<XT, SF, K, RB, ZJobsSingle>(d, r0, r1, sm, f, P, P ? b / nrb : 0u, cnt);
   }
   finish_launch(f);
 }
@@ -439,8 +446,8 @@ void k_stream_single(MatDev d, uint32_t rows_per_block, uint32_t nrb, float* P, 
 // The grouped low-rank pre-pass as a launch of its own (the phase API).
 template <int XT>
 __global__ __launch_bounds__(kThreads) void k_z_grouped(const MatDev* __restrict__ descs,
-                                                        const uint32_t* __restrict__ jobs) {
-  grouped_z_job<XT>(descs, jobs, blockIdx.x);
+                                                        const uint32_t* __restrict__ jobs, uint32_t terms) {
+  grouped_z_job<XT>(descs, jobs, blockIdx.x, terms, nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -557,17 +564,38 @@ uint64_t row_bytes(const wal_info& f) {
   return codes + G * f.d.k + G * sb * (f.d.k ? 2 : 1) + (uint64_t)f.d.n_paths * ((f.d.rank + 7) / 8);
 }
 
+// Grouped plans whose ranges hold at most this many streamed bytes snap
+// range boundaries to matrix starts (within half a range).
+constexpr uint64_t kSnapShareBytes = 256 << 10;
+
+// Passes of a matrix (4096 columns, 5120 for base-3 codes) and the bytes a
+// row contributes to pass p (its share of the row's bytes by width).
+uint32_t mat_passes(const wal_info& f) {
+  const uint32_t w = f.d.trit_fmt == WAL_TRIT_2BIT ? kPass2bit : kPassBase3;
+  return (f.d.in + w - 1) / w;
+}
+uint64_t pass_row_bytes(const wal_info& f, uint32_t p) {
+  const uint32_t w = f.d.trit_fmt == WAL_TRIT_2BIT ? kPass2bit : kPassBase3;
+  const uint64_t pw = std::min<uint64_t>(w, f.d.in - (uint64_t)p * w);
+  return std::max<uint64_t>(1, (row_bytes(f) * pw + f.d.in / 2) / f.d.in);
+}
+
 // Low-rank column chunks of a matrix in a grouped product (one partial sum of
 // z per chunk: jobs stay short however wide the matrix).
 uint32_t grouped_zc(const wal_info& f) { return (f.d.in + kZChunkCols - 1) / kZChunkCols; }
 
-uint64_t count_zjobs(uint32_t n, const wal_info* infos) {
+uint64_t count_zjobs(uint32_t n, const wal_info* infos, uint32_t terms) {
   uint64_t j = 0;
   for (uint32_t i = 0; i < n; ++i) {
     const uint32_t T = infos[i].d.n_paths * infos[i].d.rank;
-    j += (uint64_t)(T + kZTermsGrouped - 1) / kZTermsGrouped * (T ? grouped_zc(infos[i]) : 0);
+    j += (uint64_t)(T + terms - 1) / terms * (T ? grouped_zc(infos[i]) : 0);
   }
   return j;
+}
+
+// Terms per low-rank job of a grouped plan.
+uint32_t plan_zterms(uint32_t n, const wal_info* infos) {
+  return count_zjobs(n, infos, kZTermsFew) <= kZJobsFewMax ? kZTermsFew : kZTermsMany;
 }
 
 int check_blob_size(const wal_info* f) {
@@ -576,18 +604,57 @@ int check_blob_size(const wal_info* f) {
 }
 
 // Layout of a grouped plan: header | MatDev[n] | zjobs | per class:
-// blockseg[grid + 1] | segs[matrices of the class + grid].
+// blockseg[grid + 1] | segs[entries of the class + grid + ...].  Its
+// workspace: the zero region (synchronisation words, then the arrival
+// counters of split matrices, one u32 per 16 rows) when the plan has
+// low-rank paths or split matrices, the low-rank partials, the partial sums
+// of split matrices.
+//
+// A class whose 16-row groups are fewer than its workgroups splits its
+// matrices of several passes into one entry per pass (workgroups then take
+// rows of one pass, cut at multiples of 16 rows); other matrices are one
+// entry over all passes.  The class's entries, in matrix order, are split
+// into grid ranges of equal streamed bytes.
 struct PlanShape {
-  uint32_t n_classes;
-  uint32_t cls[WAL_MAX_CLASSES], grid[WAL_MAX_CLASSES], mats[WAL_MAX_CLASSES];
-  uint64_t rows[WAL_MAX_CLASSES];
+  uint32_t n_classes, zterms;
+  uint32_t cls[WAL_MAX_CLASSES], grid[WAL_MAX_CLASSES], entries[WAL_MAX_CLASSES];
+  uint32_t kof[kClasses];   // launch index of a class id
+  bool split[WAL_MAX_CLASSES];
+  uint64_t rows[WAL_MAX_CLASSES];   // rows of the class's entries
+  uint64_t counters;                // arrival counters of split matrices
   uint64_t off_descs, off_zjobs, off_blockseg[WAL_MAX_CLASSES], off_segs[WAL_MAX_CLASSES], bytes;
 };
+bool mat_split(const PlanShape& P, const wal_info& f) {
+  return P.split[P.kof[class_of(f.d)]] && mat_passes(f) > 1;
+}
 
-// The plan's synchronisation words (fused launches) follow its header; the
-// planner writes them as zero and every launch returns them to zero.
-constexpr uint64_t plan_sync_offset() { return (sizeof(PlanHeader) + 63) / 64 * 64; }
-static_assert(plan_sync_offset() == WAL_PLAN_SYNC_OFFSET, "the plan's synchronisation words as documented");
+// Whether a grouped plan's launches coordinate through the workspace's
+// synchronisation words (low-rank jobs or split matrices).
+bool plan_syncs(uint32_t n, const wal_info* infos, const PlanShape& P) {
+  for (uint32_t i = 0; i < n; ++i)
+    if (infos[i].d.n_paths || mat_split(P, infos[i])) return true;
+  return false;
+}
+
+// Workspace of a grouped plan: the zero region (when the plan syncs), each
+// matrix's tagged low-rank partials [zc][terms] (8 bytes each), then each
+// split matrix's per-pass partial sums [passes][out]; the byte offsets of
+// the partials per matrix (when zoff / poff are given) and the total.
+uint64_t grouped_ws_bytes(uint32_t n, const wal_info* infos, const PlanShape& P, uint64_t* zoff, uint64_t* poff) {
+  uint64_t off = plan_syncs(n, infos, P) ? kWsZeroBytes : 0;
+  for (uint32_t i = 0; i < n; ++i) {
+    const uint64_t T = (uint64_t)infos[i].d.n_paths * infos[i].d.rank;
+    if (zoff) zoff[i] = off;
+    off += T ? up64(8 * T * grouped_zc(infos[i]), 16) : 0;
+  }
+  off = up64(off, 256);
+  for (uint32_t i = 0; i < n; ++i) {
+    if (poff) poff[i] = off;
+    if (mat_split(P, infos[i])) off += up64(4ull * mat_passes(infos[i]) * infos[i].d.out, 256);
+  }
+  return up64(off, 256);
+}
+
 static_assert(kSyncBytes == WAL_SYNC_BYTES && kSyncFallback == WAL_SYNC_FALLBACK_WORD,
               "synchronisation words as documented");
 static_assert(kMaxRowBlocks == WAL_MAX_ROW_BLOCKS && kWsZeroBytes == WAL_WS_ZERO_BYTES && kWsZeroBytes % 256 == 0,
@@ -595,45 +662,64 @@ static_assert(kMaxRowBlocks == WAL_MAX_ROW_BLOCKS && kWsZeroBytes == WAL_WS_ZERO
 
 int plan_shape(uint32_t n, const wal_info* infos, uint32_t grid, int x_dtype, PlanShape* P) {
   std::memset(P, 0, sizeof(*P));
-  uint64_t rows[kClasses] = {0};
+  P->zterms = plan_zterms(n, infos);
+  const uint64_t nzj = count_zjobs(n, infos, P->zterms);
+  uint64_t groups[kClasses] = {0}, groups_split[kClasses] = {0};   // 16-row groups, and by pass
   uint32_t mats[kClasses] = {0};
   for (uint32_t i = 0; i < n; ++i) {
-    const uint32_t c = class_of(infos[i].d);
-    rows[c] += infos[i].d.out;
+    const uint32_t c = class_of(infos[i].d), g16 = (infos[i].d.out + 15) / 16;
+    groups[c] += g16;
+    groups_split[c] += (uint64_t)g16 * mat_passes(infos[i]);
     ++mats[c];
   }
   for (uint32_t c = 0; c < kClasses; ++c) {
     if (!mats[c]) continue;
     if (!grouped_for(x_dtype, c)) return WAL_ERR_UNSUPPORTED;
-    uint32_t g = grid;
+    uint32_t g = grid, res = 0;
     if (!g) {
-      uint32_t res = 0;
       int st = resident_blocks(reinterpret_cast<const void*>(grouped_for(x_dtype, c)), &res);
       if (st) return st;
       // the first launch also runs the low-rank jobs in workgroups of its
-      // own: its streaming workgroups leave them their slots
-      const uint64_t nzj = P->n_classes == 0 ? count_zjobs(n, infos) : 0;
-      if (res > 2 * nzj) res -= (uint32_t)nzj;
-      const uint64_t by_rows = (rows[c] + 15) / 16;
-      g = (uint32_t)(by_rows < res ? by_rows : res);
-      if (!g) g = 1;
+      // own: when they are few, its streaming workgroups leave them their
+      // slots (many jobs belong to a large plan, whose long streaming
+      // workgroups would leave those slots idle after the jobs end)
+      if (P->n_classes == 0 && nzj <= res / 8) res -= (uint32_t)nzj;
     }
+    // split when the class has fewer 16-row groups than workgroups and the
+    // arrival counters of every split class fit the workspace's
+    // kMaxRowBlocks words
+    bool split = groups[c] < (g ? g : res) && groups_split[c] > groups[c];
+    if (split) {
+      uint64_t need = 0;
+      for (uint32_t i = 0; i < n; ++i)
+        if (class_of(infos[i].d) == c && mat_passes(infos[i]) > 1) need += (infos[i].d.out + 15) / 16;
+      split = P->counters + need <= kMaxRowBlocks;
+      if (split) P->counters += need;
+    }
+    if (!g) g = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(split ? groups_split[c] : groups[c], res));
     const uint32_t k = P->n_classes++;
     P->cls[k] = c;
+    P->kof[c] = k;
     P->grid[k] = g;
-    P->mats[k] = mats[c];
-    P->rows[k] = rows[c];
+    P->split[k] = split;
   }
-  uint64_t off = plan_sync_offset() + kSyncBytes;
+  for (uint32_t i = 0; i < n; ++i) {
+    const uint32_t k = P->kof[class_of(infos[i].d)];
+    const bool sp = mat_split(*P, infos[i]);
+    const uint32_t e = sp ? mat_passes(infos[i]) : 1;
+    P->entries[k] += e;
+    P->rows[k] += (uint64_t)e * infos[i].d.out;
+  }
+  uint64_t off = up64(sizeof(PlanHeader), 64);
   P->off_descs = off;
   off += up64((uint64_t)n * sizeof(MatDev), 64);
   P->off_zjobs = off;
-  off += up64(count_zjobs(n, infos) * 8, 64);   // (matrix, t0 << 16 | chunk) pairs
+  off += up64(nzj * 8, 64);   // (matrix, t0 << 16 | chunk) pairs
   for (uint32_t k = 0; k < P->n_classes; ++k) {
     P->off_blockseg[k] = off;
     off += up64(4ull * (P->grid[k] + 1), 64);
     P->off_segs[k] = off;
-    off += up64(((uint64_t)P->mats[k] + P->grid[k] + P->rows[k] / seg_rows(P->cls[k]) + 1) * sizeof(Seg), 64);
+    off += up64(((uint64_t)P->entries[k] + P->grid[k] + P->rows[k] / seg_rows(P->cls[k]) + 1) * sizeof(Seg), 64);
   }
   P->bytes = off;
   return WAL_OK;
@@ -689,11 +775,10 @@ int wal_gemv(const wal_info* info, const void* W_dev, const void* x_dev, int x_d
   // wal_workspace_size(info, 1) bytes); the workgroup that completes a row
   // block adds them.  The workspace: synchronisation words, arrival
   // counters, low-rank partials [chunks][terms], partial sums.
-  // A split product has at most kMaxRowBlocks row blocks (one arrival
-  // counter each) of at most seg_rows rows.
+  // A split product counts arrivals per 16 rows: at most kMaxRowBlocks
+  // counters.
   const uint32_t out = info->d.out;
-  const uint32_t split_min_rows = ((out + kMaxRowBlocks - 1) / kMaxRowBlocks + kRB - 1) / kRB * kRB;
-  const bool split = npass > 1 && ws_dev && ws_bytes >= S.bytes && split_min_rows <= seg_rows(cls);
+  const bool split = npass > 1 && ws_dev && ws_bytes >= S.bytes && (out + 15) / 16 <= kMaxRowBlocks;
   const size_t need = split ? (size_t)S.bytes : info->d.n_paths ? (size_t)S.off_p : 0;
   if (need && (!ws_dev || ws_bytes < need)) return ws_dev ? WAL_ERR_BUFFER : WAL_ERR_ARG;
   if (need && !aligned(ws_dev, 16)) return WAL_ERR_ALIGN;
@@ -715,18 +800,18 @@ int wal_gemv(const wal_info* info, const void* W_dev, const void* x_dev, int x_d
   const uint32_t nz = d.terms ? (d.terms + kZTerms - 1) / kZTerms * d.zc : 0;
   // rows per block: the (row, pass) work spread evenly over the blocks the
   // GPU holds at once besides the low-rank jobs
-  const uint32_t slots = resident > 2 * nz ? resident - nz : resident;
+  const uint32_t slots = nz <= resident / 8 ? resident - nz : resident;
   const uint64_t units = (uint64_t)out * (split ? npass : 1);
   uint32_t rpb = (uint32_t)((units + slots - 1) / slots);
   rpb = std::max(rpb, kWaves * kRB);   // one batch per wavefront
-  if (split) rpb = std::max(rpb, split_min_rows);
-  rpb = std::min((rpb + kRB - 1) / kRB * kRB, seg_rows(cls));
+  const uint32_t unit = split ? 16u : (uint32_t)kRB;   // split row blocks start at multiples of 16
+  rpb = std::min((rpb + unit - 1) / unit * unit, seg_rows(cls));
   const uint32_t nrb = (out + rpb - 1) / rpb;
   float* P = split ? reinterpret_cast<float*>(ws + S.off_p) : nullptr;
   uint32_t* cnt = split ? reinterpret_cast<uint32_t*>(ws + S.off_cnt) : nullptr;
   const uint32_t grid = nz + nrb * (split ? npass : 1);
   Fuse f{};
-  if (need) f = Fuse{reinterpret_cast<uint32_t*>(ws), 0u, nz, nz, grid, 1u};
+  if (need) f = Fuse{reinterpret_cast<uint32_t*>(ws), 0u, nz, nz ? 1u : 0u, grid, 1u, kZTerms};
   hipLaunchKernelGGL(single_for(x_dtype, cls), dim3(grid), dim3(kThreads), 0, s, d, rpb, nrb, P, cnt, f);
   return launch_status();
 }
@@ -819,19 +904,16 @@ int wal_grouped_plan_size(uint32_t n, const wal_info* infos, uint32_t grid, int 
   if (!n || !infos || !plan_bytes || !ws_bytes) return WAL_ERR_ARG;
   if (x_dtype != WAL_X_F32 && x_dtype != WAL_X_BF16) return WAL_ERR_ARG;
   if (n > (1u << 24)) return WAL_ERR_ARG;
-  uint64_t ws = 0;
   for (uint32_t i = 0; i < n; ++i) {
     int st = check_info(&infos[i]);
     if (st) return st;
     if ((st = check_blob_size(&infos[i]))) return st;
-    const uint64_t T = (uint64_t)infos[i].d.n_paths * infos[i].d.rank;
-    ws += T ? up64(4 * T * grouped_zc(infos[i]), 16) : 0;
   }
   PlanShape P;
   int st = plan_shape(n, infos, grid, x_dtype, &P);
   if (st) return st;
   *plan_bytes = (size_t)P.bytes;
-  *ws_bytes = (size_t)up64(ws, 256);
+  *ws_bytes = (size_t)grouped_ws_bytes(n, infos, P, nullptr, nullptr);
   return WAL_OK;
 }
 
@@ -860,15 +942,22 @@ int wal_grouped_plan(uint32_t n, const wal_info* infos, const void* const* W_dev
   uint32_t* jobs = reinterpret_cast<uint32_t*>(base + P.off_zjobs);
 
   // descriptors and low-rank jobs
-  uint64_t zoff = 0, j = 0;
+  std::vector<uint64_t> zoff(n), poff(n);
+  grouped_ws_bytes(n, infos, P, zoff.data(), poff.data());
+  uint8_t* wsb = static_cast<uint8_t*>(ws_dev);
+  uint64_t j = 0, cnt = kSyncBytes / 4;
   for (uint32_t i = 0; i < n; ++i) {
     const uint32_t T = infos[i].d.n_paths * infos[i].d.rank, zc = grouped_zc(infos[i]);
-    float* z = T ? static_cast<float*>(ws_dev) + zoff / 4 : nullptr;
+    float* z = T ? reinterpret_cast<float*>(wsb + zoff[i]) : nullptr;
     descs[i] = make_dev(&infos[i], W_dev[i], x_dev[i], y_dev[i], z, infos[i].d.in, infos[i].d.out, 1);
     descs[i].zc = zc;   // z partials [zc][T]
-    zoff += T ? up64(4ull * T * zc, 16) : 0;
+    if (mat_split(P, infos[i])) {
+      descs[i].P = reinterpret_cast<float*>(wsb + poff[i]);
+      descs[i].cnt_off = (uint32_t)cnt;
+      cnt += (infos[i].d.out + 15) / 16;
+    }
     for (uint32_t cc = 0; T && cc < zc; ++cc)
-      for (uint32_t t0 = 0; t0 < T; t0 += kZTermsGrouped) {
+      for (uint32_t t0 = 0; t0 < T; t0 += P.zterms) {
         jobs[2 * j] = i;
         jobs[2 * j + 1] = (t0 << 16) | cc;
         ++j;
@@ -877,53 +966,82 @@ int wal_grouped_plan(uint32_t n, const wal_info* infos, const void* const* W_dev
 
   std::memset(ginfo, 0, sizeof(*ginfo));
   uint32_t nseg_total = 0, gmax = 0;
+  struct Entry {
+    uint32_t mat, pass1, out;
+    uint64_t rb;   // streamed bytes per row
+  };
+  std::vector<Entry> ent;
   for (uint32_t k = 0; k < P.n_classes; ++k) {
-    // The class's matrices in order; their rows are split into grid ranges
-    // of equal streamed bytes, one per workgroup.
+    // The class's entries in order; their rows are split into grid ranges of
+    // equal streamed bytes, one per workgroup (at multiples of 16 rows in a
+    // split entry, whose row groups count arrivals).
     const uint32_t c = P.cls[k], G = P.grid[k];
     uint32_t* blockseg = reinterpret_cast<uint32_t*>(base + P.off_blockseg[k]);
     Seg* segs = reinterpret_cast<Seg*>(base + P.off_segs[k]);
+    ent.clear();
     uint64_t total = 0;
-    for (uint32_t i = 0; i < n; ++i)
-      if (class_of(infos[i].d) == c) total += row_bytes(infos[i]) * infos[i].d.out;
-    // boundary b: (matrix, row) where the b-th range starts; mat == n past the end
-    auto boundary = [&](uint32_t b, uint32_t* mat, uint32_t* row) {
+    for (uint32_t i = 0; i < n; ++i) {
+      if (class_of(infos[i].d) != c) continue;
+      if (mat_split(P, infos[i])) {
+        for (uint32_t p = 0; p < mat_passes(infos[i]); ++p)
+          ent.push_back(Entry{i, p + 1, infos[i].d.out, pass_row_bytes(infos[i], p)});
+      } else {
+        ent.push_back(Entry{i, 0, infos[i].d.out, row_bytes(infos[i])});
+      }
+    }
+    for (const Entry& e : ent) total += e.rb * e.out;
+    const uint32_t ne = (uint32_t)ent.size();
+    // Small ranges (a few rows each): a range that would take a few rows of
+    // the next entry starts that entry instead, since a workgroup pays a
+    // segment's fixed latency per segment; large ranges stay exactly
+    // balanced.
+    const uint64_t share = total / G, snap = share <= kSnapShareBytes ? share / 2 : 0;
+    // boundary b: (entry, row) where the b-th range starts; entry == ne past the end
+    auto boundary = [&](uint32_t b, uint32_t* e_out, uint32_t* row) {
       const uint64_t pos = (uint64_t)((unsigned __int128)total * b / G);
       uint64_t acc = 0;
-      for (uint32_t i = 0; i < n; ++i) {
-        if (class_of(infos[i].d) != c) continue;
-        const uint64_t rb = row_bytes(infos[i]), mb = rb * infos[i].d.out;
+      for (uint32_t e = 0; e < ne; ++e) {
+        const uint64_t mb = ent[e].rb * ent[e].out;
         if (pos < acc + mb) {
-          const uint64_t r = (pos - acc + rb / 2) / rb;
-          *mat = i;
+          if (b > 0 && pos - acc < snap) {   // close to the entry's start
+            *e_out = e;
+            *row = 0;
+            return;
+          }
+          if (b > 0 && acc + mb - pos < snap) {   // close to the entry's end
+            *e_out = e + 1;
+            *row = 0;
+            return;
+          }
+          uint64_t r = (pos - acc + ent[e].rb / 2) / ent[e].rb;
+          if (ent[e].pass1) r = (r + 8) / 16 * 16;
+          *e_out = e;
           *row = (uint32_t)r;
-          if (r >= infos[i].d.out) {   // rounds to the next matrix of the class
-            uint32_t nx = i + 1;
-            while (nx < n && class_of(infos[nx].d) != c) ++nx;
-            *mat = nx;
+          if (r >= ent[e].out) {   // rounds to the next entry
+            *e_out = e + 1;
             *row = 0;
           }
           return;
         }
         acc += mb;
       }
-      *mat = n;
+      *e_out = ne;
       *row = 0;
     };
-    uint32_t nseg = 0, m0 = 0, r0 = 0;
-    boundary(0, &m0, &r0);
+    uint32_t nseg = 0, e0 = 0, r0 = 0;
+    boundary(0, &e0, &r0);
+    const uint32_t sr = seg_rows(c);
     for (uint32_t b = 0; b < G; ++b) {
       blockseg[b] = nseg;
-      uint32_t m1 = 0, r1 = 0;
-      boundary(b + 1, &m1, &r1);
-      for (uint32_t m = m0; m < n && m <= m1; ++m) {
-        if (class_of(infos[m].d) != c) continue;
-        const uint32_t rs = m == m0 ? r0 : 0;
-        const uint32_t re = m == m1 ? r1 : infos[m].d.out;
-        const uint32_t sr = seg_rows(c);
-        for (uint32_t r = rs; r < re; r += sr) segs[nseg++] = Seg{m, r, re - r > sr ? r + sr : re, 0};
+      uint32_t e1 = 0, r1 = 0;
+      boundary(b + 1, &e1, &r1);
+      for (uint32_t e = e0; e < ne && e <= e1; ++e) {
+        const uint32_t rs = e == e0 ? r0 : 0;
+        const uint32_t re = e == e1 ? r1 : ent[e].out;
+        for (uint32_t r = rs; r < re; r += sr)
+          segs[nseg++] = Seg{ent[e].mat, r, re - r > sr ? r + sr : re, ent[e].pass1};
       }
-      m0 = m1;
+      e0 = e1;
       r0 = r1;
     }
     blockseg[G] = nseg;
@@ -941,7 +1059,7 @@ int wal_grouped_plan(uint32_t n, const wal_info* infos, const void* const* W_dev
   h->n_segs = nseg_total;
   h->n_zjobs = (uint32_t)j;
   h->x_dtype = (uint32_t)x_dtype;
-  h->trit_fmt = 0;
+  h->zjob_terms = P.zterms;
   h->reserved = P.n_classes;
   h->off_descs = P.off_descs;
   h->off_zjobs = P.off_zjobs;
@@ -952,12 +1070,13 @@ int wal_grouped_plan(uint32_t n, const wal_info* infos, const void* const* W_dev
   ginfo->n_segs = nseg_total;
   ginfo->n_zjobs = (uint32_t)j;
   ginfo->x_dtype = (uint32_t)x_dtype;
-  ginfo->trit_fmt = 0;
+  ginfo->zjob_terms = P.zterms;
   ginfo->rows_per_batch = kRB;
   ginfo->grid = gmax;
   ginfo->plan_bytes = P.bytes;
   ginfo->off_descs = P.off_descs;
   ginfo->off_zjobs = P.off_zjobs;
+  ginfo->sync_dev = plan_syncs(n, infos, P) ? ws_dev : nullptr;
   uint64_t alg = 0;
   for (uint32_t i = 0; i < n; ++i) alg += infos[i].algorithmic_bytes;
   ginfo->algorithmic_bytes = alg;
@@ -976,6 +1095,9 @@ int wal_gemv_grouped_phases(const wal_grouped_info* g, const void* plan_dev, int
     if (g->class_blockseg[k] >= g->plan_bytes || g->class_segs[k] >= g->plan_bytes) return WAL_ERR_ARG;
   }
   if (g->off_descs >= g->plan_bytes || (g->n_zjobs && g->off_zjobs >= g->plan_bytes)) return WAL_ERR_ARG;
+  if (g->n_zjobs && g->zjob_terms != kZTermsFew && g->zjob_terms != kZTermsMany) return WAL_ERR_ARG;
+  if (g->n_zjobs && !g->sync_dev) return WAL_ERR_ARG;
+  if (g->sync_dev && !aligned(g->sync_dev, 16)) return WAL_ERR_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint8_t* base = static_cast<const uint8_t*>(plan_dev);
   const MatDev* descs = reinterpret_cast<const MatDev*>(base + g->off_descs);
@@ -986,22 +1108,21 @@ int wal_gemv_grouped_phases(const wal_grouped_info* g, const void* plan_dev, int
   int st;
   if (!fused && (phases & WAL_PHASE_LOWRANK) && g->n_zjobs) {
     if (g->x_dtype == WAL_X_BF16)
-      hipLaunchKernelGGL(k_z_grouped<WAL_X_BF16>, dim3(g->n_zjobs), dim3(kThreads), 0, s, descs, jobs);
+      hipLaunchKernelGGL(k_z_grouped<WAL_X_BF16>, dim3(g->n_zjobs), dim3(kThreads), 0, s, descs, jobs, g->zjob_terms);
     else
-      hipLaunchKernelGGL(k_z_grouped<WAL_X_F32>, dim3(g->n_zjobs), dim3(kThreads), 0, s, descs, jobs);
+      hipLaunchKernelGGL(k_z_grouped<WAL_X_F32>, dim3(g->n_zjobs), dim3(kThreads), 0, s, descs, jobs, g->zjob_terms);
     if ((st = launch_status())) return st;
   }
-  uint32_t* sync = reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(base) + plan_sync_offset());
+  uint32_t* sync = static_cast<uint32_t*>(g->sync_dev);
   for (uint32_t k = 0; (phases & WAL_PHASE_STREAM) && k < g->n_classes; ++k) {
     const uint32_t* blockseg = reinterpret_cast<const uint32_t*>(base + g->class_blockseg[k]);
     const Seg* segs = reinterpret_cast<const Seg*>(base + g->class_segs[k]);
-    uint32_t grid = g->class_grid[k];
+    // the synchronisation words also serve split matrices' arrival counts,
+    // so every streaming launch of a plan that has them takes them
+    const uint32_t nz = fused && sync && k == 0 ? g->n_zjobs : 0u;
+    const uint32_t grid = g->class_grid[k] + nz;
     Fuse f{};
-    if (fused) {
-      const uint32_t nz = k == 0 ? g->n_zjobs : 0u;
-      grid += nz;
-      f = Fuse{sync, k, nz, g->n_zjobs, grid, k + 1 == g->n_classes ? 1u : 0u};
-    }
+    if (sync) f = Fuse{sync, k, nz, nz ? 1u : 0u, grid, k + 1 == g->n_classes ? 1u : 0u, g->zjob_terms};
     hipLaunchKernelGGL(grouped_for((int)g->x_dtype, g->class_id[k]), dim3(grid), dim3(kThreads), 0, s, descs,
                        blockseg, segs, jobs, f);
     if ((st = launch_status())) return st;

@@ -607,7 +607,11 @@ GemmShape gemm_shape(const wal_info& f, uint32_t batch) {
   S.slices = (f.d.in + kSliceCols - 1) / kSliceCols;
   S.off_cnt = kSyncBytes;
   S.off_z = kWsZeroBytes;
-  S.off_p = S.off_z + up(4 * terms * batch * S.zc, 256);
+  // the small-batch kernels' fp32 partials per 4096 columns, or the single
+  // product's tagged partials (8 bytes) per kZSingleCols columns
+  const uint64_t zsmall = 4 * terms * batch * S.zc;
+  const uint64_t zsingle = 8 * terms * ((f.d.in + kZSingleCols - 1) / kZSingleCols);
+  S.off_p = S.off_z + up(zsmall > zsingle ? zsmall : zsingle, 256);
   S.bytes = S.off_p + up(4ull * S.slices * batch * f.d.out, 256);
   return S;
 }

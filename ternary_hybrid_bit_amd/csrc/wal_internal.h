@@ -32,6 +32,12 @@ struct MatDev {
   uint32_t blob_bytes;              // bytes of the blob from codes on (< 2^32)
   uint32_t trit_fmt;
   uint32_t zc;                      // chunks of z to add
+  // Grouped plans whose matrix runs its passes in separate workgroups:
+  // per-pass partial sums P[pass][out] (workspace) and the word offset of
+  // its arrival counters (one per 16 rows) from the plan's synchronisation
+  // words.
+  float* P;
+  uint32_t cnt_off;
 };
 
 // Plan blob written by wal_grouped_plan (host) and read by the kernels:
@@ -42,11 +48,13 @@ struct MatDev {
 // segs[blockseg[b] .. blockseg[b + 1]).  The header is informative only
 // (reserved = number of classes); launches take offsets from wal_grouped_info.
 struct PlanHeader {
-  uint32_t magic, n, grid, n_segs, n_zjobs, x_dtype, trit_fmt, reserved;
+  uint32_t magic, n, grid, n_segs, n_zjobs, x_dtype, zjob_terms, reserved;
   uint64_t off_descs, off_zjobs, bytes;
 };
+// Rows [row0, row1) of matrix mat; pass1 = 0: every pass, else pass pass1 - 1
+// only (row0 then a multiple of 16).
 struct Seg {
-  uint32_t mat, row0, row1, pad;
+  uint32_t mat, row0, row1, pass1;
 };
 constexpr uint32_t kPlanMagic = 0x324E4C50u;  // "PLN2"
 
@@ -62,32 +70,41 @@ constexpr uint32_t kPassBase3 = 5120;  // base-3: 80 trits per lane
 constexpr uint32_t kSegRows = 4096;
 // Low-rank terms handled per workgroup of the V^T x pre-passes.
 constexpr uint32_t kZTerms = 4;
-// Low-rank terms of one job of a grouped plan (16: few, large jobs, so that a
-// fused launch spends few of its first workgroups on them).
-constexpr uint32_t kZTermsGrouped = 16;
+// Low-rank terms of one job of a grouped plan: a plan with at most
+// kZJobsFewMax jobs of kZTermsFew terms uses those (short jobs, done before
+// the streaming workgroups need them), a larger plan jobs of kZTermsMany (few
+// jobs, so that a fused launch spends few of its first workgroups on them).
+constexpr uint32_t kZTermsFew = 4;
+constexpr uint32_t kZTermsMany = 16;
+constexpr uint32_t kZJobsFewMax = 64;
+static_assert(kZTerms == kZTermsFew, "single products run the short jobs");
 constexpr uint32_t kMaxTerms = WAL_MAX_PATHS * WAL_MAX_RANK;
 static_assert(kMaxTerms <= kThreads, "one low-rank term per thread of a streaming workgroup");
 
 // Synchronisation words of a launch that computes the low-rank pre-pass in
 // its first workgroups (see wal_device.h, fused launches), u32 words in
-// 128-byte lines.  Hundreds of workgroups that each touch one coherent word
-// queue on it, so every word the whole launch touches is kept in
-// kSyncReplicas copies, one line apart; workgroup b uses copy b % kSyncReplicas.
+// 128-byte lines at the start of the workspace.  Hundreds of workgroups that
+// each touch one coherent word queue on it, so every word the whole launch
+// touches is kept in kSyncReplicas copies, one line apart; workgroup b uses
+// copy b % kSyncReplicas.
 //   line 0:       word 0 the fallback count, word 1 set when a wait of the
 //                 current call gave up (the later waiters then give up at
 //                 once), words 16 + s the copies of launch slot s whose
 //                 workgroups have all finished
-//   lines 1..16:  the low-rank jobs published (copy r: word 0 of line 1 + r)
+//   lines 1..16:  the epoch, the number of calls made on the workspace
+//                 (copy r: word 0 of line 1 + r); the low-rank partials of a
+//                 call carry the tag 2 epoch + 1
 //   lines 17..32: workgroups finished (copy r: word s of line 17 + r)
-// Every call leaves them as it found them (zero), except the fallback
-// count: the workgroups whose bounded wait for the low-rank jobs gave up and
-// which computed the terms themselves (their outputs are still exact).
+// Every call leaves them as it found them, except the epoch, which its last
+// workgroup advances, and the fallback count: the workgroups whose bounded
+// wait for the low-rank jobs gave up and which computed the terms themselves
+// (their outputs are still exact).
 constexpr uint32_t kSyncReplicas = 16;
 constexpr uint32_t kSyncLine = 32;                                  // words per line
 constexpr uint32_t kSyncFallback = 0;
 constexpr uint32_t kSyncGaveUp = 1;
 constexpr uint32_t kSyncSlotsDone = 16;                             // + slot
-constexpr uint32_t kSyncZDone = kSyncLine;                          // + kSyncLine r
+constexpr uint32_t kSyncEpoch = kSyncLine;                          // + kSyncLine r
 constexpr uint32_t kSyncFinished = kSyncLine * (1 + kSyncReplicas);  // + kSyncLine r + slot
 constexpr uint32_t kSyncBytes = 4352;                                // 33 lines, padded to 256 bytes
 static_assert(4 * kSyncLine * (1 + 2 * kSyncReplicas) <= kSyncBytes && kSyncBytes % 256 == 0, "sync lines");
@@ -103,13 +120,14 @@ constexpr uint32_t kWsZeroBytes = kSyncBytes + 4 * kMaxRowBlocks;
 // Workgroups start in index order, so the jobs are under way before any
 // streaming workgroup waits for them; the wait is bounded all the same, and
 // a workgroup whose wait gives up computes the terms it needs itself.
-// Consumers wait until zdone reaches zwait before they read the low-rank
-// terms; zwait == 0 means the terms are ready (a separate pre-pass).  The
-// last workgroup to finish returns finished[slot], and with reset_z zdone,
-// to zero.
+// With zwait, consumers wait until every partial they read carries the
+// call's tag; without, the partials are ready (a separate pre-pass).  The
+// last workgroup to finish returns finished[slot] to zero, and after the
+// call's last launch (last) advances the epoch.
 struct Fuse {
   uint32_t* sync;       // the synchronisation words (null: no waits, no counts)
-  uint32_t slot, nz, zwait, grid, reset_z;
+  uint32_t slot, nz, zwait, grid, last;
+  uint32_t zterms;      // low-rank terms per job (kZTermsFew or kZTermsMany)
 };
 
 // Streaming kernels as host-side launch targets.
@@ -149,8 +167,8 @@ constexpr uint32_t kZTermsPerBlock = 16;
 constexpr uint32_t kSliceCols = 1024;
 
 // Workspace of the single and small-batch products: synchronisation words
-// and arrival counters (kWsZeroBytes, zero between calls), the low-rank
-// partials, then partial sums.
+// and arrival counters (kWsZeroBytes, zero before the first call), the
+// low-rank partials, then partial sums.
 struct GemmShape {
   uint32_t nt, passes, zc;   // n-tiles, batched GEMV passes, z chunks
   uint32_t slices;           // partial-sum planes of P: ceil(in / kSliceCols) >= passes

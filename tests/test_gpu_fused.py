@@ -8,12 +8,12 @@ through the C ABI:
 * repeated calls give identical outputs (every call returns the words to
   zero), for a grouped plan and for a single product, split and not split;
 * a wait that cannot end gives up, counts itself in the fallback word, and
-  the workgroup computes the low-rank terms itself with the producers' own
-  jobs: the outputs are bit-identical to a normal call's, and every kernel
-  ends.  The words are restored, so the next call waits normally.  The
-  condition is forced from the host: the copies of the "jobs published"
-  count are seeded with a value the producers never bring to the expected
-  count.
+  the workgroup computes the low-rank terms itself (in another summation
+  order than the producers: outputs agree with a normal call's to rounding,
+  FALLBACK_TOL), and every kernel ends.  The words are mended, so the next call waits normally.  The
+  condition is forced from the host: the copies of the epoch (which the
+  tags of a call's partials derive from) are seeded with values that
+  disagree, so producers and most consumers derive different tags.
 """
 import numpy as np
 import pytest
@@ -26,8 +26,9 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 BF16_TOL = 1e-3
-SYNC_LINE = 32    # u32 words per line of the synchronisation words
-ZDONE_COPIES = 16  # copies of the "low-rank jobs published" count: word 0 of lines 1..16
+FALLBACK_TOL = 1e-5   # rel-L2 between a fallback call and a normal one (fp32 sums in another order)
+SYNC_LINE = 32      # u32 words per line of the synchronisation words
+EPOCH_COPIES = 16   # copies of the epoch: word 0 of lines 1..16
 
 
 @pytest.fixture(scope="module")
@@ -50,15 +51,28 @@ def bf16(bits):
     return to_dev(bits.view(np.int16)).view(torch.bfloat16)
 
 
-def seed_zdone(buf, offset, value):
-    words = buf.view(-1).view(torch.uint8)[offset:offset + 4352].view(torch.int32)
-    for r in range(ZDONE_COPIES):
-        words[SYNC_LINE * (1 + r)] = value
+def sync_words(ws):
+    return ws.view(-1).view(torch.uint8)[:4352].view(torch.int32).cpu().numpy()
+
+
+def seed_epochs(ws):
+    """Epoch copies 1..15 one ahead of copy 0."""
+    words = ws.view(-1).view(torch.uint8)[:4352].view(torch.int32)
+    for r in range(1, EPOCH_COPIES):
+        words[SYNC_LINE * (1 + r)] = int(sync_words(ws)[SYNC_LINE]) + 1
     torch.cuda.synchronize()
 
 
-def sync_words(buf, offset):
-    return buf.view(-1).view(torch.uint8)[offset:offset + 4352].view(torch.int32).cpu().numpy()
+def check_sync_words(ws, fallbacks_cleared=True):
+    """Everything back to zero except the epoch copies, which agree."""
+    w = sync_words(ws)
+    epochs = w[SYNC_LINE:SYNC_LINE * (1 + EPOCH_COPIES):SYNC_LINE]
+    assert np.all(epochs == epochs[0]) and epochs[0] > 0
+    rest = w.copy()
+    rest[SYNC_LINE:SYNC_LINE * (1 + EPOCH_COPIES):SYNC_LINE] = 0
+    if not fallbacks_cleared:
+        rest[0] = 0
+    assert not rest.any()
 
 
 def grouped_case(wal, seed):
@@ -76,6 +90,10 @@ def grouped_case(wal, seed):
     plan_dev = to_dev(plan)
     refs = [D.gemv(b, x[0]) for (b, _), (x, _) in zip(packed, xs_host)]
     return g, plan_dev, ys, refs, (Ws, xs, ws)
+
+
+def close(a, b):
+    return D.rel_l2(np.asarray(a, np.float64), np.asarray(b, np.float64)) <= FALLBACK_TOL
 
 
 def check(ys, refs):
@@ -99,27 +117,31 @@ def test_grouped_repeated_calls_identical(wal):
     for o in outs[1:]:
         for a, b in zip(outs[0], o):
             assert np.array_equal(a, b)
-    assert wal.sync_fallbacks(plan_dev, wal.WAL_PLAN_SYNC_OFFSET) == 0
-    assert not sync_words(plan_dev, wal.WAL_PLAN_SYNC_OFFSET).any()
+    ws = keep[2]
+    assert wal.sync_fallbacks(ws) == 0
+    check_sync_words(ws)
 
 
 def test_grouped_wait_gives_up_and_falls_back(wal):
-    print("[fused] grouped plan, jobs-published copies seeded: the bounded waits give up", flush=True)
+    print("[fused] grouped plan, epoch copies seeded apart: the bounded waits give up", flush=True)
     g, plan_dev, ys, refs, keep = grouped_case(wal, 702)
+    ws = keep[2]
     assert g.n_zjobs > 0
     normal = run_grouped(wal, g, plan_dev, ys)
-    seed_zdone(plan_dev, wal.WAL_PLAN_SYNC_OFFSET, 7)
+    seed_epochs(ws)
     fell_back = run_grouped(wal, g, plan_dev, ys)   # every kernel ended
-    assert wal.sync_fallbacks(plan_dev, wal.WAL_PLAN_SYNC_OFFSET) > 0
+    n_fell = wal.sync_fallbacks(ws)
+    assert n_fell > 0
     for a, b in zip(normal, fell_back):
-        assert np.array_equal(a, b)
-    print("[fused] grouped plan, the next call (count not cleared)", flush=True)
+        assert close(a, b)
+    check_sync_words(ws, fallbacks_cleared=False)   # the epoch copies agree again
+    print("[fused] grouped plan, the next call waits normally", flush=True)
     again = run_grouped(wal, g, plan_dev, ys)
     for a, b in zip(normal, again):
         assert np.array_equal(a, b)
-    wal.clear_sync_fallbacks(plan_dev, wal.WAL_PLAN_SYNC_OFFSET)
-    run_grouped(wal, g, plan_dev, ys)
-    assert not sync_words(plan_dev, wal.WAL_PLAN_SYNC_OFFSET).any()
+    assert wal.sync_fallbacks(ws) == n_fell
+    wal.clear_sync_fallbacks(ws)
+    check_sync_words(ws)
 
 
 @pytest.mark.parametrize("out,inp,paths,base3", [(1000, 4096, 1, False), (600, 12288, 2, False),
@@ -146,15 +168,16 @@ def test_single_repeated_and_wait_gives_up(wal, out, inp, paths, base3):
     assert D.rel_l2(outs[0].astype(np.float64), ref) <= BF16_TOL
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
     assert wal.sync_fallbacks(ws) == 0
-    print("[fused] single, jobs-published copies seeded", flush=True)
-    seed_zdone(ws, 0, 7)
-    assert np.array_equal(call(), outs[0])
+    print("[fused] single, epoch copies seeded apart", flush=True)
+    seed_epochs(ws)
+    assert close(call(), outs[0])
     assert wal.sync_fallbacks(ws) > 0
     wal.clear_sync_fallbacks(ws)
     assert np.array_equal(call(), outs[0])
-    assert not sync_words(ws, 0).any()
-    zero = ws.view(-1)[:wal.WAL_WS_ZERO_BYTES // 4]
-    assert not zero.view(torch.int32).cpu().numpy().any()   # the arrival counters too
+    assert wal.sync_fallbacks(ws) == 0
+    check_sync_words(ws)
+    counters = ws.view(-1)[wal.WAL_SYNC_BYTES // 4:wal.WAL_WS_ZERO_BYTES // 4]
+    assert not counters.view(torch.int32).cpu().numpy().any()   # the arrival counters
 
 
 def test_one_workspace_serves_shapes_in_turn(wal):
@@ -183,3 +206,57 @@ def test_one_workspace_serves_shapes_in_turn(wal):
     assert np.array_equal(yb.cpu().numpy(), first)
     assert D.rel_l2(ys.cpu().numpy().astype(np.float64), D.gemv(sb, xs_f[0])) <= BF16_TOL
     assert wal.sync_fallbacks(ws) == 0
+
+
+def split_case(wal, seed, specs):
+    """A grouped plan (grid from the device) of matrices `specs` = [(out, in,
+    k, paths, trit_fmt, scale_fmt)], all on one x per matrix."""
+    ms = [synth.make_matrix(seed, i, o, n, k=k, n_paths=p, rank=16, trit_fmt=tf, scale_fmt=sf)
+          for i, (o, n, k, p, tf, sf) in enumerate(specs)]
+    packed = [wal.pack_matrix(m) for m in ms]
+    xs_host = [synth.make_x(seed, i, m.inp) for i, m in enumerate(ms)]
+    infos = [i for _, i in packed]
+    Ws = [to_dev(b) for b, _ in packed]
+    xs = [bf16(bits[0]) for _, bits in xs_host]
+    ys = [torch.full((m.out,), float("nan"), dtype=torch.float32, device=dev()) for m in ms]
+    _, wsb = wal.wal_grouped_plan_size(infos)
+    ws = torch.zeros(max(wsb, 4) // 4, dtype=torch.float32, device=dev())
+    plan, g = wal.wal_grouped_plan(infos, Ws, xs, ys, ws, wal.WAL_X_BF16)
+    return g, to_dev(plan), ys, packed, xs_host, (Ws, xs, ws)
+
+
+@pytest.mark.parametrize("base3", [False, True])
+def test_grouped_split_passes(wal, base3):
+    """Few rows, several passes: the plan runs the passes of each 16-row group
+    in separate workgroups (more workgroups than 16-row groups), and the
+    workgroup that completes a group adds its passes.  Outputs match the
+    oracle on sampled rows, repeat bit for bit, agree to rounding after a
+    forced fallback, and every arrival counter is zero after each call."""
+    if base3:
+        specs = [(2048, 17408, 4, 2, synth.TRIT_BASE3, synth.SCALE_FP24),
+                 (1000, 10240, 2, 1, synth.TRIT_BASE3, synth.SCALE_FP24)]
+    else:
+        specs = [(4096, 12288, 8, 1, synth.TRIT_2BIT, synth.SCALE_FP16),
+                 (1000, 8960, 8, 2, synth.TRIT_2BIT, synth.SCALE_FP16)]
+    print(f"[fused] grouped split passes, base3={base3}", flush=True)
+    g, plan_dev, ys, packed, xs_host, keep = split_case(wal, 711 + base3, specs)
+    groups = sum(-(-o // 16) for o, *_ in specs)
+    assert sum(g.class_grid[k] for k in range(g.n_classes)) > groups   # the passes are split
+    ws = keep[2]
+    counters = ws.view(-1)[wal.WAL_SYNC_BYTES // 4:wal.WAL_WS_ZERO_BYTES // 4].view(torch.int32)
+    normal = run_grouped(wal, g, plan_dev, ys)
+    rng = np.random.default_rng(5)
+    for (blob, info), (x, _), y in zip(packed, xs_host, normal):
+        rows = rng.choice(info.d.out, 128, replace=False)
+        assert D.rel_l2(y[rows].astype(np.float64), D.gemv_rows(blob, x[0], rows)) <= BF16_TOL
+    for _ in range(3):
+        again = run_grouped(wal, g, plan_dev, ys)
+        assert all(np.array_equal(a, b) for a, b in zip(normal, again))
+        assert not counters.cpu().numpy().any()
+    seed_epochs(ws)
+    fell_back = run_grouped(wal, g, plan_dev, ys)
+    assert wal.sync_fallbacks(ws) > 0
+    assert all(close(a, b) for a, b in zip(normal, fell_back))
+    wal.clear_sync_fallbacks(ws)
+    check_sync_words(ws)
+    assert not counters.cpu().numpy().any()

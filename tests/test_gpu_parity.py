@@ -132,11 +132,10 @@ def test_wide_single_split_and_whole(wal, out, inp, k, P, r, sf, b3):
     ref = D.gemv(F.pack(F.from_synth(m)), x[0])
     W, xt = to_dev(blob), x_tensor(x[0], bits[0])
     full = wal.wal_workspace_size(info, 1)
-    # the workspace up to the end of its low-rank part (synchronisation words,
-    # one arrival counter per 16 rows, the partials): no room for the passes'
-    # partial sums
+    # the workspace up to the end of its low-rank part (the zero region, the
+    # partials): no room for the passes' partial sums
     up = lambda v: (v + 255) // 256 * 256  # noqa: E731
-    zonly = wal.WAL_WS_ZERO_BYTES + up(4 * P * r * ((inp + 4095) // 4096))
+    zonly = wal.WAL_WS_ZERO_BYTES + up(max(4 * P * r * ((inp + 4095) // 4096), 8 * P * r * ((inp + 8191) // 8192)))
     for nbytes in (full, zonly):
         print(f"wide {out}x{inp} k={k} P={P} base3={b3} workspace {nbytes} B", flush=True)
         y = torch.full((out,), float("nan"), dtype=torch.float32, device=dev())

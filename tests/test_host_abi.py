@@ -211,7 +211,8 @@ def test_workspace_size():
 
     def expect(out, inp, terms, B):
         chunks, slices = (inp + 4095) // 4096, (inp + 1023) // 1024
-        return 4352 + 4 * 4096 + up(4 * terms * B * chunks) + up(4 * slices * B * out)
+        z = max(4 * terms * B * chunks, 8 * terms * ((inp + 8191) // 8192))   # fp32, or tagged for batch 1
+        return 4352 + 4 * 4096 + up(z) + up(4 * slices * B * out)
 
     info = wal.wal_packed_size(wal.make_desc(12288, 4096, 8, 1, 16))
     assert wal.wal_workspace_size(info, 1) == expect(12288, 4096, 16, 1) == 20736 + 256 + 4 * 49152
@@ -367,53 +368,105 @@ def _plan_classes(plan, g):
     return out, jobs
 
 
-@pytest.mark.parametrize("grid", [1, 7, 768, 1024, 3000])
+def _passes(info):
+    return -(-info.d.in_ // (4096 if info.d.trit_fmt == 0 else 5120))
+
+
+def _row_bytes(info):
+    return ((info.d.in_ // 4 if info.d.trit_fmt == 0 else (info.d.in_ + 4) // 5)
+            + (info.d.in_ // 128) * (info.d.k + (2 if info.d.scale_fmt == 0 else 3) * (2 if info.d.k else 1))
+            + info.d.n_paths * ((info.d.rank + 7) // 8))
+
+
+def _pass_row_bytes(info, p):
+    w = 4096 if info.d.trit_fmt == 0 else 5120
+    pw = min(w, info.d.in_ - p * w)
+    return max(1, (_row_bytes(info) * pw + info.d.in_ // 2) // info.d.in_)
+
+
+@pytest.mark.parametrize("grid", [1, 7, 768, 1024, 3000, 6000])
 def test_grouped_plan_covers_every_row_once(grid):
     """Per (scale format, k) class, the grouped plan splits the rows of the
     class's matrices into `grid` contiguous ranges of near-equal packed
     bytes; every row of every matrix belongs to exactly one workgroup of the
-    launch of its class."""
+    launch of its class, for every pass.  A class with more workgroups than
+    16-row groups splits its matrices of several passes by pass: segments of
+    one pass start at multiples of 16 rows."""
     shapes = [(4096, 4096, 8, 1, 16, 0, 0), (1024, 4096, 8, 0, 0, 0, 0), (1024, 4096, 8, 1, 16, 0, 0),
               (4096, 4096, 8, 1, 16, 0, 0), (12288, 4096, 8, 1, 16, 0, 0), (300, 4096, 2, 0, 0, 1, 0),
               (12288, 4096, 8, 0, 0, 0, 0), (4096, 12288, 8, 1, 16, 0, 0), (1, 128, 2, 0, 0, 0, 0),
               (7, 384, 4, 4, 64, 0, 0), (129, 512, 2, 1, 8, 1, 0), (17408, 5120, 2, 2, 16, 1, 1),
-              (5120, 17408, 4, 2, 16, 1, 1), (3000, 640, 8, 0, 0, 0, 1)]
+              (5120, 17408, 4, 2, 16, 1, 1), (3000, 640, 8, 0, 0, 0, 1), (200, 8960, 4, 1, 16, 0, 0)]
     infos = [wal.wal_packed_size(wal.make_desc(o, i, k, P, r, trit_fmt=tf, scale_fmt=sf))
              for o, i, k, P, r, sf, tf in shapes]
     plan, g = _plan_on_host(infos, grid)
-    # the launch's synchronisation words start out zero, ahead of the descriptors
-    sync = slice(wal.WAL_PLAN_SYNC_OFFSET, wal.WAL_PLAN_SYNC_OFFSET + wal.WAL_SYNC_BYTES)
-    assert not plan[sync].any() and g.off_descs >= sync.stop
+    # the synchronisation words are the workspace's (it starts with them)
+    assert g.sync_dev == (1 << 40) + (1 << 38) and g.off_descs == 64
     classes, jobs = _plan_classes(plan, g)
     assert sorted(c for c, _, _ in classes) == sorted(set(_class_of(i) for i in infos))
     assert sum(len(sg) for _, _, sg in classes) == g.n_segs
-    rb = [(i.d.in_ // 4 if i.d.trit_fmt == 0 else (i.d.in_ + 4) // 5)
-          + (i.d.in_ // 128) * (i.d.k + (2 if i.d.scale_fmt == 0 else 3) * (2 if i.d.k else 1))
-          + i.d.n_paths * ((i.d.rank + 7) // 8) for i in infos]
-    covered = [np.zeros(o, np.int32) for o, *_ in shapes]
+    covered = [np.zeros((o, _passes(infos[m])), np.int32) for m, (o, *_) in enumerate(shapes)]
+    n_split = 0
     for c, blockseg, segs in classes:
+        members = [m for m in range(len(infos)) if _class_of(infos[m]) == c]
+        groups = sum(-(-shapes[m][0] // 16) for m in members)
+        split = grid > groups and any(_passes(infos[m]) > 1 for m in members)
         assert len(blockseg) == grid + 1 and blockseg[0] == 0
         assert np.all(np.diff(blockseg.astype(np.int64)) >= 0)
         per_block = np.zeros(grid)
         for b in range(grid):
-            for m, r0, r1, _ in segs[blockseg[b]:blockseg[b + 1]]:
+            for m, r0, r1, pass1 in segs[blockseg[b]:blockseg[b + 1]]:
                 assert _class_of(infos[m]) == c
                 assert r0 < r1 <= shapes[m][0]
                 assert r1 - r0 <= (1024 if c >= 8 else 4096)   # rows whose y one workgroup stages
-                covered[m][r0:r1] += 1
-                per_block[b] += (r1 - r0) * rb[m]
+                if pass1:
+                    assert split and _passes(infos[m]) > 1 and r0 % 16 == 0
+                    covered[m][r0:r1, pass1 - 1] += 1
+                    per_block[b] += (r1 - r0) * _pass_row_bytes(infos[m], pass1 - 1)
+                    n_split += 1
+                else:
+                    assert not (split and _passes(infos[m]) > 1)
+                    covered[m][r0:r1, :] += 1
+                    per_block[b] += (r1 - r0) * _row_bytes(infos[m])
         # streamed bytes per workgroup are balanced to within a row of the
-        # class's widest matrix
-        members = [m for m in range(len(infos)) if _class_of(infos[m]) == c]
-        ideal = sum(rb[m] * infos[m].d.out for m in members) / grid
-        assert per_block.max() <= ideal + max(rb[m] for m in members) + 1
+        # class's widest matrix (16 rows of a pass in split matrices)
+        def rb(m):
+            return 16 * _pass_row_bytes(infos[m], 0) if split and _passes(infos[m]) > 1 else _row_bytes(infos[m])
+        def total(m):
+            if split and _passes(infos[m]) > 1:
+                return sum(_pass_row_bytes(infos[m], p) for p in range(_passes(infos[m]))) * shapes[m][0]
+            return _row_bytes(infos[m]) * shapes[m][0]
+        ideal = sum(total(m) for m in members) / grid
+        # small ranges (<= 256 KiB) may snap to a matrix start, within half a range
+        snap = ideal / 2 if ideal <= 256 * 1024 else 0
+        assert per_block.max() <= ideal + snap + max(rb(m) for m in members) + 1
     for c in covered:
         assert np.all(c == 1)
-    # one low-rank job per 16 terms and 4096-column chunk of every matrix
-    # that has paths: (matrix, t0 << 16 | chunk)
-    want = [(m, (t0 << 16) | cc) for m, (o, i, k, P, r, sf, tf) in enumerate(shapes)
-            for cc in range((i + 4095) // 4096) for t0 in range(0, P * r, 16)]
+    if grid == 6000:
+        assert n_split > 0   # some class has more workgroups than 16-row groups
+    # one low-rank job per zjob_terms terms and 4096-column chunk of every
+    # matrix that has paths: (matrix, t0 << 16 | chunk); 4-term jobs when
+    # that makes at most 64 jobs, else 16-term jobs
+    def jobs_of(step):
+        return [(m, (t0 << 16) | cc) for m, (o, i, k, P, r, sf, tf) in enumerate(shapes)
+                for cc in range((i + 4095) // 4096) for t0 in range(0, P * r, step)]
+    assert g.zjob_terms == (4 if len(jobs_of(4)) <= 64 else 16)
+    want = jobs_of(g.zjob_terms)
     assert sorted(map(tuple, jobs.tolist())) == sorted(want)
+
+
+def test_grouped_plan_job_size():
+    """Low-rank jobs of 4 terms when a plan has at most 64 of them, else of 16
+    terms (per 4096-column chunk of each matrix with paths)."""
+    small = [wal.wal_packed_size(wal.make_desc(4096, 4096, 8, 1, 16))] * 3
+    _, g = _plan_on_host(small, 64)
+    assert (g.zjob_terms, g.n_zjobs) == (4, 3 * 4)
+    large = [wal.wal_packed_size(wal.make_desc(4096, 12288, 8, 1, 16))] * 20
+    _, g = _plan_on_host(large, 64)
+    assert (g.zjob_terms, g.n_zjobs) == (16, 20 * 3)
+    edge = [wal.wal_packed_size(wal.make_desc(256, 4096, 8, 2, 32))] * 4   # 4 x 16 = 64 jobs of 4 terms
+    _, g = _plan_on_host(edge, 64)
+    assert (g.zjob_terms, g.n_zjobs) == (4, 64)
 
 
 def test_grouped_plan_rejects_bad_arguments():
