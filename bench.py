@@ -59,7 +59,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "packed-weight GB/s & % of HBM peak, 252-matrix Qwen3-8B-shape GEMV sweep, batch 1"
-KERNEL = "k_stream_grouped<bf16 x, fp16 scales, k=8, 4 rows/batch>"
+KERNEL = "k_stream_grouped<bf16 x, fp16 scales, k=8, 4 rows/batch> (low-rank jobs in its first workgroups)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sweep_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "ternary_hybrid_bit_amd", "csrc", f)
                   for f in ("wal_gpu.hip", "wal_device.h", "wal_internal.h")]
@@ -415,6 +415,88 @@ def run_decode_step(args):
     del keep
 
 
+def run_sweep3(args):
+    """The base-3 kernels where bandwidth decides: a 27B-shaped body of 88
+    base-3 / fp24 matrices (alternating 17408 x 5120 and 5120 x 17408, two
+    rank-16 paths, k drawn per matrix from {0, 2, 4, 8} as in configuration
+    4), about 2.1 GB packed.  One grouped plan per k class (one streaming
+    launch each, the low-rank jobs inside it); a step runs the four.  HIP
+    events around each launch, on its stream, give every class kernel's
+    average duration.  (tests/test_gpu_base3.py checks sampled rows of the
+    same matrices, planned the same way, against the oracle.)"""
+    import torch
+    import ternary_hybrid_bit_amd as wal
+    from ternary_hybrid_bit_amd import workloads
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    items = workloads.base3_body()
+    print(f"[bench] packed {len(items)} base-3 matrices in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+    infos, Ws, xs, ys, keep = resident(torch, items, dev)
+    classes = sorted(set(int(i.d.k) for i in infos))
+    plans = []
+    for k in classes:
+        ids = [j for j, i in enumerate(infos) if int(i.d.k) == k]
+        inf = [infos[j] for j in ids]
+        _, wsb = wal.wal_grouped_plan_size(inf)
+        ws = torch.zeros(max(wsb, 4) // 4, dtype=torch.float32, device=dev)
+        plan, g = wal.wal_grouped_plan(inf, [Ws[j] for j in ids], [xs[j] for j in ids], [ys[j] for j in ids], ws,
+                                       wal.WAL_X_BF16)
+        plans.append((k, ids, g, torch.from_numpy(plan).to(dev), ws))
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for _, _, g, pd, _ in plans:
+            wal.wal_gemv_grouped(g, pd)
+
+    step()
+    torch.cuda.synchronize()
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle_s:
+        for _ in range(5):
+            step()
+        torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in plans]
+           for _ in range(K)]
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(K):
+        for (_, _, g, pd, _), (a, b) in zip(plans, evs[i]):
+            a.record(stream)
+            wal.wal_gemv_grouped(g, pd)
+            b.record(stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / K
+    per_class = []
+    for c, (k, ids, g, _, _) in enumerate(plans):
+        ms = float(np.mean([evs[i][c][0].elapsed_time(evs[i][c][1]) for i in range(K)]))
+        nbytes = int(g.algorithmic_bytes)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        per_class.append({"k": k, "matrices": len(ids), "bytes_per_launch": nbytes, "ms_per_launch": round(ms, 5),
+                          "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4), "grid": int(g.class_grid[0]),
+                          "zjobs": int(g.n_zjobs)})
+    dom = max(per_class, key=lambda r: r["bytes_per_launch"])
+    nbytes = sum(int(i.algorithmic_bytes) for i in infos)
+    gbs = nbytes / (ms_step * 1e-3) / 1e9
+    out = {"workload": "sweep3", "config": {"workload": "qwen3.5-27b-shaped-base3-body-88-gemv-batch1",
+                                            "matrices": len(items), "shapes": [[17408, 5120], [5120, 17408]],
+                                            "format": "base-3 T (5 trits/byte) + sparse k in {0,2,4,8} + fp24 "
+                                                      "alpha/beta per 128 + two rank-16 WALB2 paths",
+                                            "packed_bytes": nbytes, "x_dtype": "bf16"},
+           "data": "synthetic", "steps": K, "ms_per_step": round(ms_step, 5), "GB/s": round(gbs, 2),
+           "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+           "roofline": {"bound": "hbm", "achieved": dom["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": dom["frac"], "traffic": None, "kernel": f"k_stream3_grouped<fp24 scales, k={dom['k']}>",
+                        "ms_per_launch": dom["ms_per_launch"], "bytes_per_launch": dom["bytes_per_launch"]},
+           "classes": per_class, "host": host_info()}
+    print(json.dumps(out), flush=True)
+    del keep
+
+
 def run_lmhead(args):
     """The Qwen3-8B-shaped LM head, 151936 x 4096 INT4/g128 (0.32 GB), through
     wal_int4_gemv at batch 1; calls alternate between two packed copies, so
@@ -511,7 +593,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after timing, run one fp32 elementwise copy of this many MiB (counter calibration)")
-    ap.add_argument("--workload", default="sweep", choices=("sweep", "config1", "config3", "config4", "prefill", "decode-step", "lmhead"))
+    ap.add_argument("--workload", default="sweep",
+                    choices=("sweep", "config1", "config3", "config4", "prefill", "decode-step", "lmhead", "sweep3"))
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -522,6 +605,9 @@ def main():
         return
     if args.workload == "lmhead":
         run_lmhead(args)
+        return
+    if args.workload == "sweep3":
+        run_sweep3(args)
         return
     if args.workload != "sweep":
         run_single(args)
@@ -556,9 +642,9 @@ def main():
         wal.wal_gemv_grouped(g, plan_dev)
     torch.cuda.synchronize()
 
-    # Timed region: every step is the low-rank pre-pass and the streaming
-    # launch; events around the streaming launch, on its stream, give the
-    # dominant kernel's own average duration.
+    # Timed region: every step is one launch, the streaming kernel with the
+    # low-rank jobs in its first workgroups; events around it, on its stream,
+    # give the kernel's own average duration.
     K = args.steps
     ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
@@ -566,9 +652,8 @@ def main():
     t_wall = time.perf_counter()
     ev0.record(stream)
     for i in range(K):
-        wal.wal_gemv_grouped_phases(g, plan_dev, wal.WAL_PHASE_LOWRANK)
         ev_a[i].record(stream)
-        wal.wal_gemv_grouped_phases(g, plan_dev, wal.WAL_PHASE_STREAM)
+        wal.wal_gemv_grouped(g, plan_dev)
         ev_b[i].record(stream)
     ev1.record(stream)
     torch.cuda.synchronize()
@@ -577,8 +662,19 @@ def main():
     k_ms = np.array([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)])
     ms_kernel = float(k_ms.mean())
     print(f"[bench] settle {n_settle} steps, warmup {args.warmup}; {K} steps: {ms_step:.4f} ms/step (events), "
-          f"wall {wall_s * 1e3 / K:.4f} ms; streaming kernel mean {ms_kernel:.4f} ms "
+          f"wall {wall_s * 1e3 / K:.4f} ms; kernel mean {ms_kernel:.4f} ms "
           f"(median {np.median(k_ms):.4f}, min {k_ms.min():.4f}, max {k_ms.max():.4f})", file=sys.stderr, flush=True)
+    # For reference, the streaming phase alone (its low-rank terms computed
+    # by a separate pre-pass launch beforehand): the cost of the fused jobs.
+    n_ref = max(10, K // 4)
+    ev_s = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ref)]
+    for a, b in ev_s:
+        wal.wal_gemv_grouped_phases(g, plan_dev, wal.WAL_PHASE_LOWRANK)
+        a.record(stream)
+        wal.wal_gemv_grouped_phases(g, plan_dev, wal.WAL_PHASE_STREAM)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms_stream_only = float(np.mean([a.elapsed_time(b) for a, b in ev_s]))
 
     if args.copy_mib:
         # a plain copy kernel of known size: reads and writes copy_mib MiB once
@@ -613,6 +709,7 @@ def main():
                    "packed_bytes": alg_bytes, "weights": weights, "settle_s": args.settle_s},
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "weights_per_s": round(weights / (ms_step * 1e-3), 1),
+        "stream_phase_only_ms": round(ms_stream_only, 5),
         "roofline": {"bound": "hbm", "achieved": round(k_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": stored_traffic(),
                      "kernel": KERNEL, "ms_per_launch": round(ms_kernel, 5), "bytes_per_launch": alg_bytes},

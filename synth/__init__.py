@@ -203,7 +203,23 @@ def config_matrix(config_id: int, matrix_id: int = 0) -> Matrix:
         k = config4_k(matrix_id)
         return make_matrix(4, matrix_id, shape[0], shape[1], k=k, n_paths=2, rank=16,
                            trit_fmt=TRIT_BASE3, scale_fmt=SCALE_FP24)
+    if config_id == BASE3_BODY:
+        out, inp = base3_body_shape(matrix_id)
+        return make_matrix(BASE3_BODY, matrix_id, out, inp, k=config4_k(matrix_id), n_paths=2, rank=16,
+                           trit_fmt=TRIT_BASE3, scale_fmt=SCALE_FP24)
     raise ValueError(config_id)
+
+
+# A bandwidth-scale base-3 workload: a 27B-shaped body of matrices that
+# alternate between the two shapes of configuration 4, each with configuration
+# 4's per-matrix draw of k (uniform over {0, 2, 4, 8}), fp24 scales and two
+# rank-16 paths.  BASE3_BODY_MATRICES of them hold about 2.1 GB packed.
+BASE3_BODY = 40
+BASE3_BODY_MATRICES = 88
+
+
+def base3_body_shape(matrix_id: int):
+    return [(17408, 5120), (5120, 17408)][matrix_id % 2]
 
 
 def config4_k(matrix_id: int) -> int:
@@ -225,4 +241,6 @@ def config_x(config_id: int, matrix_id: int = 0, batch: int = 1):
         return x[:batch], bits[:batch]
     if config_id == 4:
         return make_x(4, matrix_id, [5120, 17408][matrix_id], batch)
+    if config_id == BASE3_BODY:
+        return make_x(BASE3_BODY, matrix_id, base3_body_shape(matrix_id)[1], batch)
     raise ValueError(config_id)

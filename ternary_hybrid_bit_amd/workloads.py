@@ -102,6 +102,19 @@ def _load(path: str):
     return out
 
 
+def base3_body(workers: Optional[int] = None):
+    """The 27B-shaped base-3 body (synth.BASE3_BODY, about 2.1 GB packed).
+    With WAL_BASE3_CACHE set, loaded from / saved to that file."""
+    ids = list(range(synth.BASE3_BODY_MATRICES))
+    cache = os.environ.get("WAL_BASE3_CACHE")
+    if cache and os.path.exists(cache):
+        return _load(cache)
+    items = packed_config(synth.BASE3_BODY, ids, workers)
+    if cache:
+        _save(cache, items)
+    return items
+
+
 def sweep(layers: int = 36, workers: Optional[int] = None):
     """The body sweep (first ``layers`` layers, 7 matrices each), packed.
     With WAL_SWEEP_CACHE set, loaded from / saved to that file (its blobs

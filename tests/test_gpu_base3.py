@@ -139,3 +139,33 @@ def test_grouped_mixed_2bit_and_base3(wal):
     torch.cuda.synchronize()
     for y, ref in zip(ys, refs):
         assert D.rel_l2(y.cpu().numpy(), ref) <= BF16_TOL
+
+
+def test_base3_body_sampled_rows(wal):
+    """The first 8 matrices of the 27B-shaped base-3 body that bench.py's
+    sweep3 workload times (full shapes 17408 x 5120 and 5120 x 17408, fp24,
+    two rank-16 paths, k drawn per matrix), planned as it plans them: one
+    grouped plan per k class, grid from the device.  Sampled rows of every
+    matrix against the oracle."""
+    from ternary_hybrid_bit_amd import workloads
+    items = workloads.packed_config(synth.BASE3_BODY, list(range(8)), workers=1)
+    infos = [i for _, i, _ in items]
+    Ws = [to_dev(b) for b, _, _ in items]
+    xs = [to_dev(xb.view(np.int16)).view(torch.bfloat16) for _, _, xb in items]
+    ys = [torch.full((i.d.out,), float("nan"), dtype=torch.float32, device=dev()) for i in infos]
+    rng = np.random.default_rng(41)
+    for k in sorted(set(int(i.d.k) for i in infos)):
+        ids = [j for j, i in enumerate(infos) if int(i.d.k) == k]
+        print(f"base-3 body: class k={k}, matrices {ids}", flush=True)
+        inf = [infos[j] for j in ids]
+        _, wsb = wal.wal_grouped_plan_size(inf)
+        ws = torch.zeros(max(wsb, 4) // 4, dtype=torch.float32, device=dev())
+        plan, g = wal.wal_grouped_plan(inf, [Ws[j] for j in ids], [xs[j] for j in ids], [ys[j] for j in ids], ws,
+                                       wal.WAL_X_BF16)
+        wal.wal_gemv_grouped(g, to_dev(plan))
+        torch.cuda.synchronize()
+        for j in ids:
+            rows = np.sort(rng.choice(infos[j].d.out, 64, replace=False))
+            x = synth.bf16_bits_to_f32(items[j][2]).astype(np.float64)
+            ref = D.gemv_rows(items[j][0], x, rows)
+            assert D.rel_l2(ys[j].cpu().numpy()[rows].astype(np.float64), ref) <= BF16_TOL, (k, j)
