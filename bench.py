@@ -643,22 +643,26 @@ def main():
     torch.cuda.synchronize()
 
     # Timed region: every step is one launch, the streaming kernel with the
-    # low-rank jobs in its first workgroups; events around it, on its stream,
-    # give the kernel's own average duration.
+    # low-rank jobs in its first workgroups, K of them back to back between
+    # two events.  Then K more with events around each launch, on its
+    # stream, for the kernel's own average duration.
     K = args.steps
-    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_wall = time.perf_counter()
     ev0.record(stream)
     for i in range(K):
-        ev_a[i].record(stream)
         wal.wal_gemv_grouped(g, plan_dev)
-        ev_b[i].record(stream)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - t_wall
     ms_step = ev0.elapsed_time(ev1) / K
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    for i in range(K):
+        ev_a[i].record(stream)
+        wal.wal_gemv_grouped(g, plan_dev)
+        ev_b[i].record(stream)
+    torch.cuda.synchronize()
     k_ms = np.array([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)])
     ms_kernel = float(k_ms.mean())
     print(f"[bench] settle {n_settle} steps, warmup {args.warmup}; {K} steps: {ms_step:.4f} ms/step (events), "
