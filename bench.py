@@ -35,12 +35,12 @@ rate of torch's own reduction (torch.sum over 2 GiB) on the same GPU; it is
 a library kernel's rate, not a ceiling.
 
 Prints one JSON line with the contract's fields plus ``roofline`` (the
-streaming kernel's average duration from HIP events recorded around it on
-its stream in every timed step, algorithmic packed bytes per launch, against
-the 8 TB/s HBM peak; HBM traffic from the committed rocprofv3 counter runs
-when the kernel sources are unchanged since) and ``cpu_baseline`` (the
-float64 CPU oracle timed on a bounded sample of the same workload, on this
-host).
+kernel's average duration from HIP events recorded around each of K more
+launches on its stream, after the timed steps; algorithmic packed bytes per
+launch, against the 8 TB/s HBM peak; HBM traffic from the committed
+rocprofv3 counter runs when the kernel sources are unchanged since) and
+``cpu_baseline`` (the float64 CPU oracle timed on a bounded sample of the
+same workload, on this host).
 """
 from __future__ import annotations
 
