@@ -91,6 +91,7 @@ def test_config1_bf16(wal):
     (300, 8320, 0, 4, 64, 0, True),      # four paths of rank 64 (256 low-rank terms)
     (4099, 12288, 8, 1, 16, 0, True),    # down_proj width, three passes, ragged rows
     (65, 1024, 8, 3, 7, 1, False),       # fp32 activations, odd rank
+    (96, 4224, 8, 2, 8, 0, False),       # fp32 activations, two paths of rank 8, two passes
     (513, 4096, 2, 0, 0, 1, False),
 ])
 def test_shapes(wal, out, inp, k, P, r, sf, xbf16):
