@@ -91,6 +91,17 @@ typedef enum {
 enum { WAL_TRIT_2BIT = 0, WAL_TRIT_BASE3 = 1 };
 enum { WAL_SCALE_FP16 = 0, WAL_SCALE_FP24 = 1 };
 enum { WAL_X_F32 = 0, WAL_X_BF16 = 1 };
+/* Flag OR-ed into the x_dtype of wal_gemv, wal_gemv_noalloc and the grouped
+ * plans (hence chains and graphs): the blob was stored rotated (WAL2-Ternary-
+ * 27B card, "Архитектура": W' = W R, R the normalised H128 of
+ * wal_rotate_h128, one block per 128-column group), so the product takes the
+ * rotated activations, y = W'(R x).  The launch rotates x itself, with
+ * wal_rotate_h128's arithmetic and rounding (the result keeps x's type), so
+ * the output equals wal_rotate_h128 followed by the plain product bit for
+ * bit; x itself is not written.  The batched calls (wal_gemm_small,
+ * wal_gemm_prefill) return WAL_ERR_UNSUPPORTED with it: rotate X once with
+ * wal_rotate_h128 for the whole batch. */
+#define WAL_X_ROT_H128 16
 enum { WAL_GEMM_AUTO = 0, WAL_GEMM_VALU = 1, WAL_GEMM_MFMA = 2 };
 
 #define WAL_MAX_PATHS 4

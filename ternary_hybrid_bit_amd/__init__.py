@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_PKG, "libwal.so")
 WAL_TRIT_2BIT, WAL_TRIT_BASE3 = 0, 1
 WAL_SCALE_FP16, WAL_SCALE_FP24 = 0, 1
 WAL_X_F32, WAL_X_BF16 = 0, 1
+WAL_X_ROT_H128 = 16   # x_dtype flag: the product rotates x by the normalised H128 first
 WAL_GEMM_AUTO, WAL_GEMM_VALU, WAL_GEMM_MFMA = 0, 1, 2
 WAL_PHASE_LOWRANK, WAL_PHASE_STREAM, WAL_PHASE_ALL = 1, 2, 3
 WAL_MAX_PATHS = 4
@@ -325,14 +326,15 @@ def wal_prefill_workspace_size(info: wal_info, batch: int) -> int:
     return n.value
 
 
-def wal_gemv(info: wal_info, W, x, y, ws=None, stream=None):
+def wal_gemv(info: wal_info, W, x, y, ws=None, stream=None, rotate=False):
     """y = W(x) on the GPU; W, x, y (and ws, see wal_workspace_size) are device
-    tensors; y is fp32 [out]."""
+    tensors; y is fp32 [out].  rotate: the blob is stored rotated, and the
+    launch rotates x by the normalised H128 first (WAL_X_ROT_H128)."""
     torch = _torch()
     _dev_bytes(W, "W", int(info.total_bytes))
     _act(x, "x", int(info.d.in_))
     _dev(y, "y", (torch.float32,), int(info.d.out))
-    xdt = _xdtype(x)
+    xdt = _xdtype(x) | (WAL_X_ROT_H128 if rotate else 0)
     wsb = _ws_bytes(ws)
     _gpu(W=W, x=x, y=y, ws=ws)
     st = _lib.wal_gemv(ctypes.byref(info), _ptr(W), _ptr(x), xdt, _ptr(y), _ptr(ws), wsb, _stream(stream))
@@ -340,7 +342,7 @@ def wal_gemv(info: wal_info, W, x, y, ws=None, stream=None):
     return y
 
 
-def wal_gemv_noalloc(info: wal_info, W, x, y, stream=None):
+def wal_gemv_noalloc(info: wal_info, W, x, y, stream=None, rotate=False):
     """y = W(x) as wal_gemv, with the library's per-device scratch as the
     workspace (nothing is allocated; overlapping calls on one GPU race)."""
     torch = _torch()
@@ -348,7 +350,8 @@ def wal_gemv_noalloc(info: wal_info, W, x, y, stream=None):
     _act(x, "x", int(info.d.in_))
     _dev(y, "y", (torch.float32,), int(info.d.out))
     _gpu(W=W, x=x, y=y)
-    st = _lib.wal_gemv_noalloc(ctypes.byref(info), _ptr(W), _ptr(x), _xdtype(x), _ptr(y), _stream(stream))
+    xdt = _xdtype(x) | (WAL_X_ROT_H128 if rotate else 0)
+    st = _lib.wal_gemv_noalloc(ctypes.byref(info), _ptr(W), _ptr(x), xdt, _ptr(y), _stream(stream))
     _check(st, "wal_gemv_noalloc")
     return y
 
@@ -398,12 +401,13 @@ def wal_grouped_plan_size(infos: Sequence[wal_info], grid: int = 0, x_dtype: int
 
 
 def wal_grouped_plan(infos: Sequence[wal_info], Ws, xs, ys, ws, x_dtype: int, grid: int = 0):
-    """Build a grouped plan; returns (plan bytes as numpy uint8, wal_grouped_info)."""
+    """Build a grouped plan; returns (plan bytes as numpy uint8, wal_grouped_info).
+    x_dtype may carry WAL_X_ROT_H128 (every matrix of the plan rotated)."""
     torch = _torch()
     n = len(infos)
     if not (len(Ws) == len(xs) == len(ys) == n):
         raise ValueError("infos, Ws, xs and ys must have the same length")
-    xt = torch.bfloat16 if x_dtype == WAL_X_BF16 else torch.float32
+    xt = torch.bfloat16 if (x_dtype & ~WAL_X_ROT_H128) == WAL_X_BF16 else torch.float32
     for i, (f, w, x, y) in enumerate(zip(infos, Ws, xs, ys)):
         _dev_bytes(w, f"Ws[{i}]", int(f.total_bytes))
         _dev(x, f"xs[{i}]", (xt,), int(f.d.in_))

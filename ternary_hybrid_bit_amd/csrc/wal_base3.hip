@@ -82,6 +82,16 @@ struct XLane3 {
     }
   }
 
+  // The same columns from activations staged in LDS (element e on).
+  static __device__ __forceinline__ void load_lds(const void* xs, uint32_t e, Raw& r) {
+    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(xs) + e);
+#pragma unroll
+    for (int q = 0; q < 10; ++q) {
+      const uint4 v = src[q];
+      r.w[4 * q] = v.x; r.w[4 * q + 1] = v.y; r.w[4 * q + 2] = v.z; r.w[4 * q + 3] = v.w;
+    }
+  }
+
   __device__ __forceinline__ void set(const Raw& r) {
     auto xv = [&](int j) { return (r.w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu; };
 #pragma unroll
@@ -225,7 +235,7 @@ __device__ __forceinline__ void build_lut(uint32_t* lut) {
 
 // ZP: low-rank partials prefetched per term; lut: the workgroup's first pass,
 // which also fills the byte table.
-template <int SF, int K>
+template <int SF, int K, bool ROT>
 __device__ __forceinline__ void stream_rows_base3(const MatDev& d, uint32_t row0, uint32_t row1, uint32_t pass,
                                                   bool first, bool lut_first, Smem3& sm) {
   constexpr int RB = kRB3;
@@ -350,17 +360,45 @@ __device__ __forceinline__ void stream_rows_base3(const MatDev& d, uint32_t row0
   // Set-up loads first (L2 hits: x, the table's x), then the first two
   // batches (HBM): loads complete in order, so waiting for the set-up data
   // does not wait for the batches.
+  // A rotated product (ROT) instead rotates the pass's 40 groups in two rounds of
+  // 16-column pieces (the second round's pieces past the pass, and the
+  // table's zero slot, load zeros); the pass then goes through LDS twice, as
+  // compact activations that each lane reads its columns from, and as the
+  // table.
   const __amdgpu_buffer_rsrc_t rx = x_rsrc<WAL_X_BF16>(d.x, d.in);
+  const RotSlot rs0 = rot_slot(0), rs1 = rot_slot(1);
+  float rv0[16], rv1[16];
   XLane3::Raw xr;
-  XLane3::load_raw(rx, pass * kPassBase3 + 80 * lane, xr);
   TableX3 tx;
-  if constexpr (K > 0) tx.load(rx, pass * kPassBase3);
+  if constexpr (ROT) {
+    rot_load<WAL_X_BF16>(rx, pass * kPassBase3 + 128 * rs0.g + 16 * rs0.sub, rv0);
+    rot_load<WAL_X_BF16>(rs1.g < kGroups3 ? rx : r_none, pass * kPassBase3 + 128 * rs1.g + 16 * rs1.sub, rv1);
+  } else {
+    XLane3::load_raw(rx, pass * kPassBase3 + 80 * lane, xr);
+    if constexpr (K > 0) tx.load(rx, pass * kPassBase3);
+  }
   Batch3<RB> B0 = load_batch(b);
   Batch3<RB> B1 = load_batch(b + kWaves);
+  if constexpr (ROT) {
+    rot_apply<WAL_X_BF16>(rv0, rs0.sub);
+    rot_apply<WAL_X_BF16>(rv1, rs1.sub);
+  }
 
   __syncthreads();   // readers of the previous table are done
   if (lut_first) build_lut(sm.lut);
-  if constexpr (K > 0) tx.store(sm.tbl);
+  if constexpr (ROT) {
+    rot_store_x<WAL_X_BF16>(sm.tbl, 128 * rs0.g + 16 * rs0.sub, rv0);
+    if (rs1.g < kGroups3) rot_store_x<WAL_X_BF16>(sm.tbl, 128 * rs1.g + 16 * rs1.sub, rv1);
+    __syncthreads();
+    XLane3::load_lds(sm.tbl, 80 * lane, xr);
+    if constexpr (K > 0) {
+      __syncthreads();   // every lane has its columns
+      rot_store_tbl<WAL_X_BF16>(sm.tbl, rs0, rv0);
+      if (rs1.g <= kGroups3) rot_store_tbl<WAL_X_BF16>(sm.tbl, rs1, rv1);
+    }
+  } else if constexpr (K > 0) {
+    tx.store(sm.tbl);
+  }
   __syncthreads();
   if (!has_rows) return;
   xl.set(xr);
@@ -384,7 +422,7 @@ __device__ __forceinline__ void stream_rows_base3(const MatDev& d, uint32_t row0
 // One segment, pass by pass, then its store (store_segment: the low-rank
 // term, or with P one pass's partial sums and the reduce of a completed row
 // block).
-template <int SF, int K, class ZJ>
+template <int SF, int K, class ZJ, bool ROT>
 __device__ __forceinline__ void run_segment_base3(const MatDev& d, uint32_t row0, uint32_t row1, bool lut_first,
                                                   Smem3& sm, const Fuse& f, float* P = nullptr,
                                                   uint32_t split_pass = 0, uint32_t* cnt = nullptr) {
@@ -392,23 +430,24 @@ __device__ __forceinline__ void run_segment_base3(const MatDev& d, uint32_t row0
   const bool split = P != nullptr;
   const uint32_t p0 = split ? split_pass : 0, p1 = split ? split_pass + 1 : npass;
   for (uint32_t pass = p0; pass < p1; ++pass)
-    stream_rows_base3<SF, K>(d, row0, row1, pass, pass == p0, lut_first && pass == p0, sm);
-  store_segment<WAL_X_BF16, ZJ>(d, row0, row1, SegEnd{sm.tbl, sm.z, sm.ybuf}, f, P, split_pass, npass, cnt);
+    stream_rows_base3<SF, K, ROT>(d, row0, row1, pass, pass == p0, lut_first && pass == p0, sm);
+  store_segment<WAL_X_BF16, ZJ, ROT>(d, row0, row1, SegEnd{sm.tbl, sm.z, sm.ybuf}, f, P, split_pass, npass, cnt);
 }
 
 // Low-rank jobs of grouped plans and single products, as in the 2-bit
 // kernels (bf16 activations).
+template <bool ROT>
 __device__ __forceinline__ void z_job_grouped3(const MatDev* __restrict__ descs, const uint32_t* __restrict__ jobs,
-                                               uint32_t j, uint32_t terms, const uint32_t* epoch) {
+                                               uint32_t j, uint32_t terms, const uint32_t* epoch, void* xs) {
   const uint32_t m = jobs[2 * j], tc = jobs[2 * j + 1];
   const MatDev& d = descs[m];
   const uint32_t t0 = tc >> 16, cc = tc & 0xFFFFu;
   const uint32_t c0 = cc * kZChunkCols, c1 = min(d.in, c0 + kZChunkCols);
-  z_job<WAL_X_BF16, ZJobsGrouped, kZOutTagged>(d, terms, t0, reinterpret_cast<uint64_t*>(d.z) + (size_t)cc * d.terms,
-                                              c0, c1, epoch);
+  z_job<WAL_X_BF16, ZJobsGrouped, kZOutTagged, ROT>(d, terms, t0, reinterpret_cast<uint64_t*>(d.z) + (size_t)cc * d.terms,
+                                              c0, c1, epoch, xs);
 }
 
-template <int SF, int K>
+template <int SF, int K, bool ROT>
 __global__ __launch_bounds__(kThreads) void k_stream3_grouped(const MatDev* __restrict__ descs,
                                                               const uint32_t* __restrict__ blockseg,
                                                               const Seg* __restrict__ segs,
@@ -416,7 +455,7 @@ __global__ __launch_bounds__(kThreads) void k_stream3_grouped(const MatDev* __re
   __shared__ Smem3 sm;
   const uint32_t t = blockIdx.x;
   if (t < f.nz) {
-    z_job_grouped3(descs, jobs, t, zjob_terms<ZJobsGrouped>(f), epoch_of(f));
+    z_job_grouped3<ROT>(descs, jobs, t, zjob_terms<ZJobsGrouped>(f), epoch_of(f), sm.tbl);
   } else {
     const uint32_t b = t - f.nz;
     const uint32_t s0 = blockseg[b], s1 = blockseg[b + 1];
@@ -424,16 +463,16 @@ __global__ __launch_bounds__(kThreads) void k_stream3_grouped(const MatDev* __re
       const Seg sg = segs[s];
       const MatDev& d = descs[sg.mat];
       if (sg.pass1)
-        run_segment_base3<SF, K, ZJobsGrouped>(d, sg.row0, sg.row1, s == s0, sm, f, d.P, sg.pass1 - 1,
-                                               f.sync + d.cnt_off);
+        run_segment_base3<SF, K, ZJobsGrouped, ROT>(d, sg.row0, sg.row1, s == s0, sm, f, d.P, sg.pass1 - 1,
+                                                    f.sync + d.cnt_off);
       else
-        run_segment_base3<SF, K, ZJobsGrouped>(d, sg.row0, sg.row1, s == s0, sm, f);
+        run_segment_base3<SF, K, ZJobsGrouped, ROT>(d, sg.row0, sg.row1, s == s0, sm, f);
     }
   }
   finish_launch(f);
 }
 
-template <int SF, int K>
+template <int SF, int K, bool ROT>
 __global__ __launch_bounds__(kThreads) void k_stream3_single(MatDev d, uint32_t rows_per_block, uint32_t nrb,
                                                              float* P, uint32_t* cnt, Fuse f) {
   // block t < f.nz: low-rank job t; else without P block b takes rows
@@ -444,15 +483,15 @@ __global__ __launch_bounds__(kThreads) void k_stream3_single(MatDev d, uint32_t 
   if (t < f.nz) {
     const uint32_t tcs = (d.terms + kZTerms - 1) / kZTerms, tc = t % tcs, cc = t / tcs;
     const uint32_t c0 = cc * kZSingleCols, c1 = min(d.in, c0 + kZSingleCols);
-    z_chunk<WAL_X_BF16, (int)kZTerms, kZOutTagged>(d, d.x, tc * kZTerms,
-                                                   reinterpret_cast<uint64_t*>(d.z) + (size_t)cc * d.terms, c0, c1,
-                                                   epoch_of(f));
+    z_chunk_rot<WAL_X_BF16, (int)kZTerms, kZOutTagged, ROT>(d, tc * kZTerms,
+                                                       reinterpret_cast<uint64_t*>(d.z) + (size_t)cc * d.terms, c0,
+                                                       c1, epoch_of(f), sm.tbl);
   } else {
     const uint32_t b = t - f.nz;
     const uint32_t rb = P ? b % nrb : b;
     const uint32_t r0 = rb * rows_per_block;
     const uint32_t r1 = min(d.out, r0 + rows_per_block);
-    if (r0 < r1) run_segment_base3<SF, K, ZJobsSingle>(d, r0, r1, true, sm, f, P, P ? b / nrb : 0u, cnt);
+    if (r0 < r1) run_segment_base3<SF, K, ZJobsSingle, ROT>(d, r0, r1, true, sm, f, P, P ? b / nrb : 0u, cnt);
   }
   finish_launch(f);
 }
@@ -461,31 +500,36 @@ __global__ __launch_bounds__(kThreads) void k_stream3_single(MatDev d, uint32_t 
 
 namespace wal {
 
-GroupedFn base3_grouped_kernel(uint32_t cls) {
+template <bool ROT>
+GroupedFn base3_grouped(uint32_t cls) {
   switch (cls & 7) {
-    case 0: return k_stream3_grouped<WAL_SCALE_FP16, 0>;
-    case 1: return k_stream3_grouped<WAL_SCALE_FP16, 2>;
-    case 2: return k_stream3_grouped<WAL_SCALE_FP16, 4>;
-    case 3: return k_stream3_grouped<WAL_SCALE_FP16, 8>;
-    case 4: return k_stream3_grouped<WAL_SCALE_FP24, 0>;
-    case 5: return k_stream3_grouped<WAL_SCALE_FP24, 2>;
-    case 6: return k_stream3_grouped<WAL_SCALE_FP24, 4>;
-    default: return k_stream3_grouped<WAL_SCALE_FP24, 8>;
+    case 0: return k_stream3_grouped<WAL_SCALE_FP16, 0, ROT>;
+    case 1: return k_stream3_grouped<WAL_SCALE_FP16, 2, ROT>;
+    case 2: return k_stream3_grouped<WAL_SCALE_FP16, 4, ROT>;
+    case 3: return k_stream3_grouped<WAL_SCALE_FP16, 8, ROT>;
+    case 4: return k_stream3_grouped<WAL_SCALE_FP24, 0, ROT>;
+    case 5: return k_stream3_grouped<WAL_SCALE_FP24, 2, ROT>;
+    case 6: return k_stream3_grouped<WAL_SCALE_FP24, 4, ROT>;
+    default: return k_stream3_grouped<WAL_SCALE_FP24, 8, ROT>;
   }
 }
 
-SingleFn base3_single_kernel(uint32_t cls) {
+template <bool ROT>
+SingleFn base3_single(uint32_t cls) {
   switch (cls & 7) {
-    case 0: return k_stream3_single<WAL_SCALE_FP16, 0>;
-    case 1: return k_stream3_single<WAL_SCALE_FP16, 2>;
-    case 2: return k_stream3_single<WAL_SCALE_FP16, 4>;
-    case 3: return k_stream3_single<WAL_SCALE_FP16, 8>;
-    case 4: return k_stream3_single<WAL_SCALE_FP24, 0>;
-    case 5: return k_stream3_single<WAL_SCALE_FP24, 2>;
-    case 6: return k_stream3_single<WAL_SCALE_FP24, 4>;
-    default: return k_stream3_single<WAL_SCALE_FP24, 8>;
+    case 0: return k_stream3_single<WAL_SCALE_FP16, 0, ROT>;
+    case 1: return k_stream3_single<WAL_SCALE_FP16, 2, ROT>;
+    case 2: return k_stream3_single<WAL_SCALE_FP16, 4, ROT>;
+    case 3: return k_stream3_single<WAL_SCALE_FP16, 8, ROT>;
+    case 4: return k_stream3_single<WAL_SCALE_FP24, 0, ROT>;
+    case 5: return k_stream3_single<WAL_SCALE_FP24, 2, ROT>;
+    case 6: return k_stream3_single<WAL_SCALE_FP24, 4, ROT>;
+    default: return k_stream3_single<WAL_SCALE_FP24, 8, ROT>;
   }
 }
+
+GroupedFn base3_grouped_kernel(uint32_t cls, bool rot) { return rot ? base3_grouped<true>(cls) : base3_grouped<false>(cls); }
+SingleFn base3_single_kernel(uint32_t cls, bool rot) { return rot ? base3_single<true>(cls) : base3_single<false>(cls); }
 
 uint32_t base3_seg_rows() { return kSegRows3; }
 

@@ -177,6 +177,147 @@ __device__ __forceinline__ float f16_at(const uint8_t* p, uint32_t i) {
 }
 
 // ---------------------------------------------------------------------------
+// Normalised Hadamard-128 rotation of the activations (WAL2-Ternary-27B card,
+// "Архитектура": a blob stored as W' = W R, R = blockdiag(H / sqrt(128)) with
+// H Sylvester's Hadamard matrix, takes x~ = R x).
+//
+// out[128 g + i] = fp32(1/sqrt(128)) * (sum_j H[i][j] x[128 g + j]), the sum
+// as butterflies (a, b) -> (a + b, a - b) in fp32 over column bits 0..3
+// inside a thread (16 consecutive values), then bits 4, 5, 6 between the
+// eight threads of the group, in that order; bf16 activations are rounded to
+// nearest even afterwards.  wal_rotate_h128 runs the same steps, so a product
+// that rotates its own x gives the bits of the rotate-then-multiply pair.
+//
+// Inside a product the workgroup (256 threads) rotates 32 groups per round.
+// The eight threads of a group are lanes {0, 1, 2, 3, 8, 9, 10, 11} (or the
+// same + 4) of one 16-lane row, so that column bits 4, 5 and 6 sit at lane
+// bits 0, 1 and 3 and every partner is one DPP move away: xor 1 and xor 2
+// are quad permutations, xor 8 the row rotation by 8.
+constexpr float kInvSqrt128 = 0.08838834764831845f;   // 1 / sqrt(128), rounded to fp32
+
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;   // NaN stays NaN
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// The thread's piece of round r: group g of the round's columns, columns
+// 16 sub .. 16 sub + 15 of it.
+struct RotSlot {
+  uint32_t g, sub;
+};
+__device__ __forceinline__ RotSlot rot_slot(uint32_t round) {
+  static_assert(kThreads == 256, "32 groups per round of a 256-thread workgroup");
+  const uint32_t l = threadIdx.x & 63, w = threadIdx.x >> 6;
+  return RotSlot{32 * round + 2 * (4 * w + (l >> 4)) + ((l >> 2) & 1), (l & 3) | (((l >> 3) & 1) << 2)};
+}
+
+// The 16 activations of a piece starting at column col, as fp32 (columns
+// past the resource's end read as zero).
+template <int XT>
+__device__ __forceinline__ void rot_load(__amdgpu_buffer_rsrc_t rx, uint32_t col, float (&v)[16]) {
+  if constexpr (XT == WAL_X_BF16) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const u32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(rx, 2 * col + 16 * h, 0, 0);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[8 * h + 2 * k] = __uint_as_float(w[k] << 16);
+        v[8 * h + 2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const u32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(rx, 4 * col + 16 * h, 0, 0);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[4 * h + k] = __uint_as_float(w[k]);
+    }
+  }
+}
+
+// One cross-lane level: the thread whose column bit is set keeps p - v, the
+// other v + p (p the partner's value), both as one DPP add of a sign-flipped
+// own value.
+template <int CTRL>
+__device__ __forceinline__ void rot_level(float (&v)[16], bool second) {
+  const uint32_t flip = second ? 0x80000000u : 0u;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j] = dpp<CTRL>(v[j]) + __uint_as_float(__float_as_uint(v[j]) ^ flip);
+}
+
+// The rotated values of the thread's piece: the butterflies, the scale, and
+// for bf16 activations the rounding (values stay fp32 holding bf16 values).
+template <int XT>
+__device__ __forceinline__ void rot_apply(float (&v)[16], uint32_t sub) {
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1)
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (!(j & h)) {
+        const float a = v[j], b = v[j + h];
+        v[j] = a + b;
+        v[j + h] = a - b;
+      }
+  rot_level<0xB1>(v, sub & 1);    // quad_perm [1,0,3,2]: column bit 4
+  rot_level<0x4E>(v, sub & 2);    // quad_perm [2,3,0,1]: column bit 5
+  rot_level<0x128>(v, sub & 4);   // row_ror:8: column bit 6
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    v[j] *= kInvSqrt128;
+    if constexpr (XT == WAL_X_BF16) v[j] = __uint_as_float(bf16_rne(v[j]) << 16);
+  }
+}
+
+// The piece as activations of x's type at element e of xs (LDS).
+template <int XT>
+__device__ __forceinline__ void rot_store_x(void* xs, uint32_t e, const float (&v)[16]) {
+  if constexpr (XT == WAL_X_BF16) {
+    uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(xs) + e);
+    uint32_t w[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w[k] = (__float_as_uint(v[2 * k]) >> 16) | (__float_as_uint(v[2 * k + 1]) & 0xFFFF0000u);
+    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  } else {
+    float4* dst = reinterpret_cast<float4*>(static_cast<float*>(xs) + e);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) dst[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+  }
+}
+
+// The piece's entries of a signed site table tbl[group][site byte]: +-2x for
+// bf16 activations, +-x for fp32 (the streaming kernels' scaling).
+template <int XT>
+__device__ __forceinline__ void rot_store_tbl(float* tbl, const RotSlot& s, const float (&v)[16]) {
+  constexpr float m = XT == WAL_X_BF16 ? 2.0f : 1.0f;
+  float4* pos = reinterpret_cast<float4*>(tbl + s.g * 256 + 16 * s.sub);
+  float4* neg = reinterpret_cast<float4*>(tbl + s.g * 256 + 128 + 16 * s.sub);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float a = m * v[4 * k], b = m * v[4 * k + 1], c = m * v[4 * k + 2], d = m * v[4 * k + 3];
+    pos[k] = make_float4(a, b, c, d);
+    neg[k] = make_float4(-a, -b, -c, -d);
+  }
+}
+
+// Columns [c0, c0 + 128 ng) of x (n columns; ng <= 64) rotated into xs (LDS,
+// x's type, column c0 at element 0) by the whole workgroup, then a barrier.
+// Every thread calls it.
+template <int XT>
+__device__ __forceinline__ void rot_to_lds(const void* x, uint32_t n, uint32_t c0, uint32_t ng, void* xs) {
+  const __amdgpu_buffer_rsrc_t rx = rsrc(x, n * (XT == WAL_X_F32 ? 4u : 2u));
+  for (uint32_t round = 0; 32 * round < ng; ++round) {
+    const RotSlot s = rot_slot(round);
+    float v[16];
+    rot_load<XT>(rx, c0 + 128 * s.g + 16 * s.sub, v);
+    rot_apply<XT>(v, s.sub);
+    if (s.g < ng) rot_store_x<XT>(xs, 128 * s.g + 16 * s.sub, v);
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
 // Data that workgroups of one launch hand to each other (low-rank partials,
 // per-pass partial sums) moves through device-scope (agent) atomic stores
 // and loads: on this part they go to the device's coherence point, past the
@@ -219,11 +360,12 @@ enum ZOut { kZOutLds, kZOutDev, kZOutTagged };
 // z[t] = s_p[r] * sum_j (-1)^{V_p[r] bit j} x_j over the columns j in
 // [c0, c1) (multiples of 16) for the C terms t0 .. t0 + C - 1 (those below
 // d.terms), written to out[t] by threads t - t0 as OUT says (out: float* for
-// floats, uint64_t* for tagged words).  Every thread of the workgroup (up to
-// 1024) calls it (it holds a barrier).
+// floats, uint64_t* for tagged words).  Column c is element c - xoff of x
+// (a rotated chunk in LDS starts at its first column).  Every thread of the
+// workgroup (up to 1024) calls it (it holds a barrier).
 template <int XT, int C, ZOut OUT>
 __device__ __forceinline__ void z_chunk(const MatDev& d, const void* x, uint32_t t0, void* out, uint32_t c0,
-                                        uint32_t c1, const uint32_t* epoch = nullptr) {
+                                        uint32_t c1, const uint32_t* epoch = nullptr, uint32_t xoff = 0) {
   __shared__ float red[16][C];
   const uint32_t tid = threadIdx.x, nthr = blockDim.x;
   const int lane = tid & 63;
@@ -249,7 +391,7 @@ __device__ __forceinline__ void z_chunk(const MatDev& d, const void* x, uint32_t
   auto step = [&](uint32_t c) {
     uint32_t xb[16];   // fp32 bit patterns of x[c .. c + 15]
     if constexpr (XT == WAL_X_BF16) {
-      const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + c);
+      const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + (c - xoff));
       const uint4 a = src[0], b = src[1];
       const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
@@ -258,7 +400,7 @@ __device__ __forceinline__ void z_chunk(const MatDev& d, const void* x, uint32_t
         xb[2 * k + 1] = w[k] & 0xFFFF0000u;
       }
     } else {
-      const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(x) + c);
+      const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(x) + (c - xoff));
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const uint4 v = src[k];
@@ -334,17 +476,32 @@ __device__ __forceinline__ uint32_t zjob_terms(const Fuse& f) {
   return ZJ::kTwoSizes && f.zterms == kZTermsMany ? kZTermsMany : kZTermsFew;
 }
 
-// One job: terms t0 .. t0 + terms - 1 over columns [c0, c1) into out.
-template <int XT, class ZJ, ZOut OUT>
+// The terms t0 .. t0 + C - 1 of a job over columns [c0, c1): from x, or in a
+// rotated product (ROT) from the chunk rotated into xs (LDS, at least
+// c1 - c0 activations of x's type) first.  Every thread calls it.
+template <int XT, int C, ZOut OUT, bool ROT>
+__device__ __forceinline__ void z_chunk_rot(const MatDev& d, uint32_t t0, void* out, uint32_t c0, uint32_t c1,
+                                            const uint32_t* epoch, void* xs) {
+  if constexpr (ROT) {
+    rot_to_lds<XT>(d.x, d.in, c0, (c1 - c0) / 128, xs);
+    z_chunk<XT, C, OUT>(d, xs, t0, out, c0, c1, epoch, c0);
+  } else {
+    z_chunk<XT, C, OUT>(d, d.x, t0, out, c0, c1, epoch);
+  }
+}
+
+// One job: terms t0 .. t0 + terms - 1 over columns [c0, c1) into out (xs:
+// LDS for a rotated chunk).
+template <int XT, class ZJ, ZOut OUT, bool ROT>
 __device__ __forceinline__ void z_job(const MatDev& d, uint32_t terms, uint32_t t0, void* out, uint32_t c0,
-                                      uint32_t c1, const uint32_t* epoch = nullptr) {
+                                      uint32_t c1, const uint32_t* epoch, void* xs) {
   if constexpr (ZJ::kTwoSizes) {
     if (terms == kZTermsMany) {
-      z_chunk<XT, (int)kZTermsMany, OUT>(d, d.x, t0, out, c0, c1, epoch);
+      z_chunk_rot<XT, (int)kZTermsMany, OUT, ROT>(d, t0, out, c0, c1, epoch, xs);
       return;
     }
   }
-  z_chunk<XT, (int)kZTermsFew, OUT>(d, d.x, t0, out, c0, c1, epoch);
+  z_chunk_rot<XT, (int)kZTermsFew, OUT, ROT>(d, t0, out, c0, c1, epoch, xs);
 }
 
 __device__ __forceinline__ uint32_t* sync_copy(const Fuse& f, uint32_t word) {
@@ -438,9 +595,38 @@ __device__ __forceinline__ bool read_partials(const MatDev& d, uint32_t t, uint3
 // the streaming code that shares its kernel; it runs only if a wait expires,
 // and its sums, in another order than the producers', agree with theirs to
 // rounding).  Every thread calls it.
-template <int XT>
+template <int XT, bool ROT>
 __device__ __forceinline__ void lowrank_z_here(const MatDev& d, const SegEnd& e) {
   const uint32_t vrow = d.in / 8;
+  if constexpr (ROT) {
+    // Rotated activations: 4096 columns at a time rotated into the table's
+    // space (free here), one thread per term (at most kThreads terms).
+    const uint32_t t = threadIdx.x;
+    const uint32_t p = t < d.terms ? t / d.rank : 0, r = t < d.terms ? t % d.rank : 0;
+    const uint16_t* bits = reinterpret_cast<const uint16_t*>(path_plane(d.V, d, p) + (size_t)r * vrow);
+    float z = 0.f;
+    for (uint32_t c0 = 0; c0 < d.in; c0 += kPass2bit) {
+      const uint32_t nc = min(kPass2bit, d.in - c0);
+      rot_to_lds<XT>(d.x, d.in, c0, nc / 128, e.tbl);
+      if (t < d.terms) {
+        for (uint32_t c = 0; c < nc; c += 16) {
+          const uint32_t v = bits[(c0 + c) / 16];
+          for (uint32_t j = 0; j < 16; ++j) {
+            float xj;
+            if constexpr (XT == WAL_X_BF16)
+              xj = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(e.tbl)[c + j] << 16);
+            else
+              xj = e.tbl[c + j];
+            z += ((v >> j) & 1u) ? -xj : xj;
+          }
+        }
+      }
+      __syncthreads();   // the chunk's readers are done
+    }
+    if (t < d.terms)
+      e.z[t] = (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(path_plane(d.s, d, p))[r]) * z;
+    return;
+  }
   for (uint32_t t = threadIdx.x; t < d.terms; t += blockDim.x) {
     const uint32_t p = t / d.rank, r = t % d.rank;
     const uint16_t* bits = reinterpret_cast<const uint16_t*>(path_plane(d.V, d, p) + (size_t)r * vrow);
@@ -586,7 +772,7 @@ __device__ __forceinline__ float lowrank_row(const MatDev& d, const SegEnd& e, _
 // workgroup whose arrival completes a group (npass arrivals) adds its rows'
 // npass planes in pass order with the low-rank term, stores y, and returns
 // the counter to zero.  Every thread calls it (barriers).
-template <int XT, class ZJ>
+template <int XT, class ZJ, bool ROT>
 __device__ __forceinline__ void store_segment(const MatDev& d, uint32_t row0, uint32_t row1, const SegEnd& e,
                                               const Fuse& f, float* P = nullptr, uint32_t pass = 0,
                                               uint32_t npass = 1, uint32_t* cnt = nullptr) {
@@ -636,7 +822,7 @@ __device__ __forceinline__ void store_segment(const MatDev& d, uint32_t row0, ui
   const uint32_t i0 = threadIdx.x;
   const uint32_t urow = row0 + min(i0, nrows - 1);
   const UAhead ua = load_u_ahead(d, ru, urow);
-  if (!lowrank_z_read(d, e, f)) lowrank_z_here<XT>(d, e);   // the rare fallback
+  if (!lowrank_z_read(d, e, f)) lowrank_z_here<XT, ROT>(d, e);   // the rare fallback
   __syncthreads();
   if (ahead && nrows <= blockDim.x) {
     if (i0 < nrows) {

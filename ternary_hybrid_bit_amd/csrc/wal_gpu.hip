@@ -82,6 +82,16 @@ template <> struct XLane<WAL_X_BF16> {
     }
   }
 
+  // The same columns from activations staged in LDS (element e on).
+  static __device__ __forceinline__ void load_lds(const void* xs, uint32_t e, Raw& r) {
+    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(xs) + e);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint4 v = src[q];
+      r.w[4 * q] = v.x; r.w[4 * q + 1] = v.y; r.w[4 * q + 2] = v.z; r.w[4 * q + 3] = v.w;
+    }
+  }
+
   __device__ __forceinline__ void set(const Raw& r) {
 #pragma unroll
     for (int d = 0; d < 4; ++d)
@@ -131,6 +141,15 @@ template <> struct XLane<WAL_X_F32> {
       const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rx, 4 * c + 16 * q, 0, 0);
 #pragma unroll
       for (int j = 0; j < 4; ++j) r.f[4 * q + j] = __uint_as_float(v[j]);
+    }
+  }
+
+  static __device__ __forceinline__ void load_lds(const void* xs, uint32_t e, Raw& r) {
+    const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(xs) + e);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const float4 v = src[q];
+      r.f[4 * q] = v.x; r.f[4 * q + 1] = v.y; r.f[4 * q + 2] = v.z; r.f[4 * q + 3] = v.w;
     }
   }
 
@@ -235,7 +254,7 @@ struct Lane2 {
 // first batch and of its x columns, so the set-up overlaps the memory
 // latency instead of adding to it.  Every wave reaches both barriers.  The
 // low-rank term is added after the segment's last pass (store_segment).
-template <int XT, int SF, int K, int RB>
+template <int XT, int SF, int K, int RB, bool ROT>
 __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0, uint32_t row1, uint32_t pass,
                                                  bool first, StreamSmem& sm) {
   constexpr int LOG = ilog2(RB);
@@ -324,19 +343,40 @@ __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0,
   // table (L2 hits).  Vector memory loads complete in order, so waiting for
   // these after the first batch's loads (HBM) are issued does not wait for
   // the batch.
+  // A rotated product (ROT) instead loads one 16-column piece per thread of
+  // the whole pass (the workgroup's 256 pieces are the pass's 32 groups) and
+  // rotates it; the pass then goes through LDS twice, as compact
+  // activations that each lane reads its columns from, and as the table.
   const __amdgpu_buffer_rsrc_t rx = x_rsrc<XT>(d.x, d.in);
+  const RotSlot rs = rot_slot(0);
+  float rv[16];
   typename XLane<XT>::Raw xr;
-  XLane<XT>::load_raw(rx, pass * kPass2bit + 64 * lane, xr);
   TableX<XT> tx;
-  if constexpr (K > 0) tx.load(rx, pass * kPass2bit);
+  if constexpr (ROT) {
+    rot_load<XT>(rx, pass * kPass2bit + 128 * rs.g + 16 * rs.sub, rv);
+  } else {
+    XLane<XT>::load_raw(rx, pass * kPass2bit + 64 * lane, xr);
+    if constexpr (K > 0) tx.load(rx, pass * kPass2bit);
+  }
 
   // Two batches in registers: while one is reduced, the next is in flight
   // (three resident workgroups per CU keep three wavefronts per SIMD, six
   // batches, in flight).
   Batch<RB> B0 = load_batch(b);
+  if constexpr (ROT) rot_apply<XT>(rv, rs.sub);
 
   __syncthreads();   // readers of the previous table are done
-  if constexpr (K > 0) tx.store(sm.tbl);
+  if constexpr (ROT) {
+    rot_store_x<XT>(sm.tbl, 128 * rs.g + 16 * rs.sub, rv);
+    __syncthreads();
+    XLane<XT>::load_lds(sm.tbl, 64 * lane, xr);
+    if constexpr (K > 0) {
+      __syncthreads();   // every lane has its columns
+      rot_store_tbl<XT>(sm.tbl, rs, rv);
+    }
+  } else if constexpr (K > 0) {
+    tx.store(sm.tbl);
+  }
   __syncthreads();
   if (!has_rows) return;
   xl.set(xr);
@@ -359,15 +399,16 @@ __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0,
 // matrix's scale format and sites per group: every (scale format, k) class
 // has kernels of its own, so the registers of the hot fp16 / k = 8 loop are
 // not set by the heavier fp24 loads.
-template <int XT, int SF, int K, int RB, class ZJ>
+template <int XT, int SF, int K, int RB, class ZJ, bool ROT>
 __device__ __forceinline__ void run_segment_2bit(const MatDev& d, uint32_t row0, uint32_t row1, StreamSmem& sm,
                                                  const Fuse& f, float* P = nullptr, uint32_t split_pass = 0,
                                                  uint32_t* cnt = nullptr) {
   const uint32_t npass = (d.in + kPass2bit - 1) / kPass2bit;
   const bool split = P != nullptr;
   const uint32_t p0 = split ? split_pass : 0, p1 = split ? split_pass + 1 : npass;
-  for (uint32_t pass = p0; pass < p1; ++pass) stream_rows_2bit<XT, SF, K, RB>(d, row0, row1, pass, pass == p0, sm);
-  store_segment<XT, ZJ>(d, row0, row1, SegEnd{sm.tbl, sm.z, sm.ybuf}, f, P, split_pass, npass, cnt);
+  for (uint32_t pass = p0; pass < p1; ++pass)
+    stream_rows_2bit<XT, SF, K, RB, ROT>(d, row0, row1, pass, pass == p0, sm);
+  store_segment<XT, ZJ, ROT>(d, row0, row1, SegEnd{sm.tbl, sm.z, sm.ybuf}, f, P, split_pass, npass, cnt);
 }
 
 // Three workgroups per CU (the LDS of a workgroup allows it) when the class's
@@ -380,27 +421,27 @@ constexpr int stream_waves_per_simd(int XT, int SF, int K) {
 // Low-rank job of a fused launch or of the grouped pre-pass: terms t0 ..
 // t0 + terms - 1 of matrix m over columns [4096 cc, 4096 cc + 4096) into its
 // partials z[cc][t] (jobs[2 j] = m, jobs[2 j + 1] = t0 << 16 | cc).
-template <int XT>
+template <int XT, bool ROT>
 __device__ __forceinline__ void grouped_z_job(const MatDev* __restrict__ descs, const uint32_t* __restrict__ jobs,
-                                              uint32_t j, uint32_t terms, const uint32_t* epoch) {
+                                              uint32_t j, uint32_t terms, const uint32_t* epoch, void* xs) {
   const uint32_t m = jobs[2 * j], tc = jobs[2 * j + 1];
   const MatDev& d = descs[m];
   const uint32_t t0 = tc >> 16, cc = tc & 0xFFFFu;
   const uint32_t c0 = cc * kZChunkCols, c1 = min(d.in, c0 + kZChunkCols);
-  z_job<XT, ZJobsGrouped, kZOutTagged>(d, terms, t0, reinterpret_cast<uint64_t*>(d.z) + (size_t)cc * d.terms, c0, c1,
-                                      epoch);
+  z_job<XT, ZJobsGrouped, kZOutTagged, ROT>(d, terms, t0, reinterpret_cast<uint64_t*>(d.z) + (size_t)cc * d.terms, c0, c1,
+                                      epoch, xs);
 }
 
 // Grouped products: workgroup t = blockIdx.x computes low-rank job t when
 // t < f.nz, else streams the segments of block t - f.nz.
-template <int XT, int SF, int K, int RB>
+template <int XT, int SF, int K, int RB, bool ROT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(stream_waves_per_simd(XT, SF, K))))
 void k_stream_grouped(const MatDev* __restrict__ descs, const uint32_t* __restrict__ blockseg,
                       const Seg* __restrict__ segs, const uint32_t* __restrict__ jobs, Fuse f) {
   __shared__ StreamSmem sm;
   const uint32_t t = blockIdx.x;
   if (t < f.nz) {
-    grouped_z_job<XT>(descs, jobs, t, zjob_terms<ZJobsGrouped>(f), epoch_of(f));
+    grouped_z_job<XT, ROT>(descs, jobs, t, zjob_terms<ZJobsGrouped>(f), epoch_of(f), sm.tbl);
   } else {
     const uint32_t b = t - f.nz;
     const uint32_t s0 = blockseg[b], s1 = blockseg[b + 1];
@@ -408,10 +449,10 @@ void k_stream_grouped(const MatDev* __restrict__ descs, const uint32_t* __restri
       const Seg sg = segs[s];
       const MatDev& d = descs[sg.mat];
       if (sg.pass1)
-        run_segment_2bit<XT, SF, K, RB, ZJobsGrouped>(d, sg.row0, sg.row1, sm, f, d.P, sg.pass1 - 1,
-                                                      f.sync + d.cnt_off);
+        run_segment_2bit<XT, SF, K, RB, ZJobsGrouped, ROT>(d, sg.row0, sg.row1, sm, f, d.P, sg.pass1 - 1,
+                                                           f.sync + d.cnt_off);
       else
-        run_segment_2bit<XT, SF, K, RB, ZJobsGrouped>(d, sg.row0, sg.row1, sm, f);
+        run_segment_2bit<XT, SF, K, RB, ZJobsGrouped, ROT>(d, sg.row0, sg.row1, sm, f);
     }
   }
   finish_launch(f);
@@ -423,7 +464,7 @@ void k_stream_grouped(const MatDev* __restrict__ descs, const uint32_t* __restri
 // stream.  Without P, block b takes rows [b rpb, b rpb + rpb) over every
 // pass; with P, block b takes pass b / nrb of row block b % nrb (rpb a
 // multiple of 16; cnt: the arrival counters, one per 16 rows).
-template <int XT, int SF, int K, int RB>
+template <int XT, int SF, int K, int RB, bool ROT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(stream_waves_per_simd(XT, SF, K))))
 void k_stream_single(MatDev d, uint32_t rows_per_block, uint32_t nrb, float* P, uint32_t* cnt, Fuse f) {
   __shared__ StreamSmem sm;
@@ -431,23 +472,24 @@ void k_stream_single(MatDev d, uint32_t rows_per_block, uint32_t nrb, float* P, 
   if (t < f.nz) {
     const uint32_t tcs = (d.terms + kZTerms - 1) / kZTerms, tc = t % tcs, cc = t / tcs;
     const uint32_t c0 = cc * kZSingleCols, c1 = min(d.in, c0 + kZSingleCols);
-    z_chunk<XT, (int)kZTerms, kZOutTagged>(d, d.x, tc * kZTerms, reinterpret_cast<uint64_t*>(d.z) + (size_t)cc * d.terms,
-                                           c0, c1, epoch_of(f));
+    z_chunk_rot<XT, (int)kZTerms, kZOutTagged, ROT>(d, tc * kZTerms, reinterpret_cast<uint64_t*>(d.z) + (size_t)cc * d.terms,
+                                               c0, c1, epoch_of(f), sm.tbl);
   } else {
     const uint32_t b = t - f.nz;
     const uint32_t rb = P ? b % nrb : b;
     const uint32_t r0 = rb * rows_per_block;
     const uint32_t r1 = min(d.out, r0 + rows_per_block);
-    if (r0 < r1) run_segment_2bit<XT, SF, K, RB, ZJobsSingle>(d, r0, r1, sm, f, P, P ? b / nrb : 0u, cnt);
+    if (r0 < r1) run_segment_2bit<XT, SF, K, RB, ZJobsSingle, ROT>(d, r0, r1, sm, f, P, P ? b / nrb : 0u, cnt);
   }
   finish_launch(f);
 }
 
 // The grouped low-rank pre-pass as a launch of its own (the phase API).
-template <int XT>
+template <int XT, bool ROT>
 __global__ __launch_bounds__(kThreads) void k_z_grouped(const MatDev* __restrict__ descs,
                                                         const uint32_t* __restrict__ jobs, uint32_t terms) {
-  grouped_z_job<XT>(descs, jobs, blockIdx.x, terms, nullptr);
+  __shared__ float xs[ROT ? kZChunkCols : 1];   // a rotated chunk
+  grouped_z_job<XT, ROT>(descs, jobs, blockIdx.x, terms, nullptr, xs);
 }
 
 // ---------------------------------------------------------------------------
@@ -509,41 +551,48 @@ uint32_t class_of(const wal_desc& d) {
 // Longest row range one workgroup of a class takes (its y is staged in LDS).
 uint32_t seg_rows(uint32_t cls) { return cls >= 8 ? base3_seg_rows() : kSegRows; }
 
-template <int XT>
+template <int XT, bool ROT>
 GroupedFn grouped_kernel(uint32_t cls) {
   switch (cls) {
-    case 0: return k_stream_grouped<XT, WAL_SCALE_FP16, 0, kRB>;
-    case 1: return k_stream_grouped<XT, WAL_SCALE_FP16, 2, kRB>;
-    case 2: return k_stream_grouped<XT, WAL_SCALE_FP16, 4, kRB>;
-    case 3: return k_stream_grouped<XT, WAL_SCALE_FP16, 8, kRB>;
-    case 4: return k_stream_grouped<XT, WAL_SCALE_FP24, 0, kRB>;
-    case 5: return k_stream_grouped<XT, WAL_SCALE_FP24, 2, kRB>;
-    case 6: return k_stream_grouped<XT, WAL_SCALE_FP24, 4, kRB>;
-    default: return k_stream_grouped<XT, WAL_SCALE_FP24, 8, kRB>;
+    case 0: return k_stream_grouped<XT, WAL_SCALE_FP16, 0, kRB, ROT>;
+    case 1: return k_stream_grouped<XT, WAL_SCALE_FP16, 2, kRB, ROT>;
+    case 2: return k_stream_grouped<XT, WAL_SCALE_FP16, 4, kRB, ROT>;
+    case 3: return k_stream_grouped<XT, WAL_SCALE_FP16, 8, kRB, ROT>;
+    case 4: return k_stream_grouped<XT, WAL_SCALE_FP24, 0, kRB, ROT>;
+    case 5: return k_stream_grouped<XT, WAL_SCALE_FP24, 2, kRB, ROT>;
+    case 6: return k_stream_grouped<XT, WAL_SCALE_FP24, 4, kRB, ROT>;
+    default: return k_stream_grouped<XT, WAL_SCALE_FP24, 8, kRB, ROT>;
   }
 }
-template <int XT>
+template <int XT, bool ROT>
 SingleFn single_kernel(uint32_t cls) {
   switch (cls) {
-    case 0: return k_stream_single<XT, WAL_SCALE_FP16, 0, kRB>;
-    case 1: return k_stream_single<XT, WAL_SCALE_FP16, 2, kRB>;
-    case 2: return k_stream_single<XT, WAL_SCALE_FP16, 4, kRB>;
-    case 3: return k_stream_single<XT, WAL_SCALE_FP16, 8, kRB>;
-    case 4: return k_stream_single<XT, WAL_SCALE_FP24, 0, kRB>;
-    case 5: return k_stream_single<XT, WAL_SCALE_FP24, 2, kRB>;
-    case 6: return k_stream_single<XT, WAL_SCALE_FP24, 4, kRB>;
-    default: return k_stream_single<XT, WAL_SCALE_FP24, 8, kRB>;
+    case 0: return k_stream_single<XT, WAL_SCALE_FP16, 0, kRB, ROT>;
+    case 1: return k_stream_single<XT, WAL_SCALE_FP16, 2, kRB, ROT>;
+    case 2: return k_stream_single<XT, WAL_SCALE_FP16, 4, kRB, ROT>;
+    case 3: return k_stream_single<XT, WAL_SCALE_FP16, 8, kRB, ROT>;
+    case 4: return k_stream_single<XT, WAL_SCALE_FP24, 0, kRB, ROT>;
+    case 5: return k_stream_single<XT, WAL_SCALE_FP24, 2, kRB, ROT>;
+    case 6: return k_stream_single<XT, WAL_SCALE_FP24, 4, kRB, ROT>;
+    default: return k_stream_single<XT, WAL_SCALE_FP24, 8, kRB, ROT>;
   }
 }
-// Streaming kernel of a class; NULL when the combination is not built
-// (base-3 codes take bf16 activations only).
+// Streaming kernel of a class for activations of type x_dtype (with the
+// rotation flag: the kernels that rotate x); NULL when the combination is
+// not built (base-3 codes take bf16 activations only).
 GroupedFn grouped_for(int x_dtype, uint32_t cls) {
-  if (cls >= 8) return x_dtype == WAL_X_BF16 ? base3_grouped_kernel(cls) : nullptr;
-  return x_dtype == WAL_X_BF16 ? grouped_kernel<WAL_X_BF16>(cls) : grouped_kernel<WAL_X_F32>(cls);
+  const bool rot = (x_dtype & WAL_X_ROT_H128) != 0;
+  const int xt = x_dtype & ~WAL_X_ROT_H128;
+  if (cls >= 8) return xt == WAL_X_BF16 ? base3_grouped_kernel(cls, rot) : nullptr;
+  if (xt == WAL_X_BF16) return rot ? grouped_kernel<WAL_X_BF16, true>(cls) : grouped_kernel<WAL_X_BF16, false>(cls);
+  return rot ? grouped_kernel<WAL_X_F32, true>(cls) : grouped_kernel<WAL_X_F32, false>(cls);
 }
 SingleFn single_for(int x_dtype, uint32_t cls) {
-  if (cls >= 8) return x_dtype == WAL_X_BF16 ? base3_single_kernel(cls) : nullptr;
-  return x_dtype == WAL_X_BF16 ? single_kernel<WAL_X_BF16>(cls) : single_kernel<WAL_X_F32>(cls);
+  const bool rot = (x_dtype & WAL_X_ROT_H128) != 0;
+  const int xt = x_dtype & ~WAL_X_ROT_H128;
+  if (cls >= 8) return xt == WAL_X_BF16 ? base3_single_kernel(cls, rot) : nullptr;
+  if (xt == WAL_X_BF16) return rot ? single_kernel<WAL_X_BF16, true>(cls) : single_kernel<WAL_X_BF16, false>(cls);
+  return rot ? single_kernel<WAL_X_F32, true>(cls) : single_kernel<WAL_X_F32, false>(cls);
 }
 
 // Workgroups of a streaming kernel that the current device holds at once.
@@ -760,12 +809,13 @@ int scratch_address(void** out) {
 
 extern "C" {
 
-int wal_gemv(const wal_info* info, const void* W_dev, const void* x_dev, int x_dtype, float* y_dev,
+int wal_gemv(const wal_info* info, const void* W_dev, const void* x_dev, int x_dtype_flags, float* y_dev,
              void* ws_dev, size_t ws_bytes, void* stream) {
   int st = check_info(info);
   if (st) return st;
   if (!W_dev || !x_dev || !y_dev) return WAL_ERR_ARG;
-  if (x_dtype != WAL_X_F32 && x_dtype != WAL_X_BF16) return WAL_ERR_ARG;
+  if (x_dtype_flags & ~(WAL_X_BF16 | WAL_X_ROT_H128)) return WAL_ERR_ARG;
+  const int x_dtype = x_dtype_flags & ~WAL_X_ROT_H128;   // element type
   if (!aligned(W_dev, 256) || !aligned(x_dev, 16) || !aligned(y_dev, 4)) return WAL_ERR_ALIGN;
   const GemmShape S = gemm_shape(*info, 1);
   const uint32_t cls = class_of(info->d);
@@ -787,14 +837,14 @@ int wal_gemv(const wal_info* info, const void* W_dev, const void* x_dev, int x_d
                overlap(ws_dev, need, x_dev, (size_t)info->d.in * xelem(x_dtype))))
     return WAL_ERR_ARG;
   if ((st = check_blob_size(info))) return st;
-  if (!single_for(x_dtype, cls)) return WAL_ERR_UNSUPPORTED;
+  if (!single_for(x_dtype_flags, cls)) return WAL_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(ws_dev);
   MatDev d = make_dev(info, W_dev, x_dev, y_dev, need ? reinterpret_cast<float*>(ws + S.off_z) : nullptr,
                       info->d.in, info->d.out, 1);
   d.zc = (info->d.in + kZSingleCols - 1) / kZSingleCols;   // at most S.zc partials
   uint32_t resident = 0;
-  if ((st = resident_blocks(reinterpret_cast<const void*>(grouped_for(x_dtype, cls)), &resident))) return st;
+  if ((st = resident_blocks(reinterpret_cast<const void*>(single_for(x_dtype_flags, cls)), &resident))) return st;
   // One launch: its first nz workgroups compute the low-rank partials, which
   // the others read only when they store their rows.
   const uint32_t nz = d.terms ? (d.terms + kZTerms - 1) / kZTerms * d.zc : 0;
@@ -812,7 +862,7 @@ int wal_gemv(const wal_info* info, const void* W_dev, const void* x_dev, int x_d
   const uint32_t grid = nz + nrb * (split ? npass : 1);
   Fuse f{};
   if (need) f = Fuse{reinterpret_cast<uint32_t*>(ws), 0u, nz, nz ? 1u : 0u, grid, 1u, kZTerms};
-  hipLaunchKernelGGL(single_for(x_dtype, cls), dim3(grid), dim3(kThreads), 0, s, d, rpb, nrb, P, cnt, f);
+  hipLaunchKernelGGL(single_for(x_dtype_flags, cls), dim3(grid), dim3(kThreads), 0, s, d, rpb, nrb, P, cnt, f);
   return launch_status();
 }
 
@@ -838,6 +888,8 @@ int wal_gemm_small(const wal_info* info, const void* W_dev, const void* X_dev, i
   if (batch == 0 || batch > WAL_MAX_BATCH) return WAL_ERR_ARG;
   if (mode < WAL_GEMM_AUTO || mode > WAL_GEMM_MFMA) return WAL_ERR_ARG;
   if (!W_dev || !X_dev || !Y_dev) return WAL_ERR_ARG;
+  if (x_dtype == (WAL_X_F32 | WAL_X_ROT_H128) || x_dtype == (WAL_X_BF16 | WAL_X_ROT_H128))
+    return WAL_ERR_UNSUPPORTED;   // rotate X first (wal_rotate_h128)
   if (x_dtype != WAL_X_F32 && x_dtype != WAL_X_BF16) return WAL_ERR_ARG;
   if (ldx < info->d.in || ldy < info->d.out) return WAL_ERR_ARG;
   const size_t xe = xelem(x_dtype);
@@ -880,6 +932,8 @@ int wal_gemm_prefill(const wal_info* info, const void* W_dev, const void* X_dev,
   if (st) return st;
   if (batch == 0 || batch > WAL_MAX_PREFILL_BATCH) return WAL_ERR_ARG;
   if (!W_dev || !X_dev || !Y_dev) return WAL_ERR_ARG;
+  if (x_dtype == (WAL_X_F32 | WAL_X_ROT_H128) || x_dtype == (WAL_X_BF16 | WAL_X_ROT_H128))
+    return WAL_ERR_UNSUPPORTED;   // rotate X first (wal_rotate_h128)
   if (x_dtype != WAL_X_F32 && x_dtype != WAL_X_BF16) return WAL_ERR_ARG;
   if (ldx < info->d.in || ldy < info->d.out) return WAL_ERR_ARG;
   if (x_dtype != WAL_X_BF16 || info->d.trit_fmt != WAL_TRIT_2BIT) return WAL_ERR_UNSUPPORTED;
@@ -899,10 +953,10 @@ int wal_gemm_prefill(const wal_info* info, const void* W_dev, const void* X_dev,
   return launch_gemm_prefill(*info, d, batch, ws_dev, stream);
 }
 
-int wal_grouped_plan_size(uint32_t n, const wal_info* infos, uint32_t grid, int x_dtype, size_t* plan_bytes,
+int wal_grouped_plan_size(uint32_t n, const wal_info* infos, uint32_t grid, int x_dtype_flags, size_t* plan_bytes,
                           size_t* ws_bytes) {
   if (!n || !infos || !plan_bytes || !ws_bytes) return WAL_ERR_ARG;
-  if (x_dtype != WAL_X_F32 && x_dtype != WAL_X_BF16) return WAL_ERR_ARG;
+  if (x_dtype_flags & ~(WAL_X_BF16 | WAL_X_ROT_H128)) return WAL_ERR_ARG;
   if (n > (1u << 24)) return WAL_ERR_ARG;
   for (uint32_t i = 0; i < n; ++i) {
     int st = check_info(&infos[i]);
@@ -910,7 +964,7 @@ int wal_grouped_plan_size(uint32_t n, const wal_info* infos, uint32_t grid, int 
     if ((st = check_blob_size(&infos[i]))) return st;
   }
   PlanShape P;
-  int st = plan_shape(n, infos, grid, x_dtype, &P);
+  int st = plan_shape(n, infos, grid, x_dtype_flags, &P);
   if (st) return st;
   *plan_bytes = (size_t)P.bytes;
   *ws_bytes = (size_t)grouped_ws_bytes(n, infos, P, nullptr, nullptr);
@@ -918,11 +972,12 @@ int wal_grouped_plan_size(uint32_t n, const wal_info* infos, uint32_t grid, int 
 }
 
 int wal_grouped_plan(uint32_t n, const wal_info* infos, const void* const* W_dev, const void* const* x_dev,
-                     int x_dtype, float* const* y_dev, void* ws_dev, size_t ws_bytes, uint32_t grid,
+                     int x_dtype_flags, float* const* y_dev, void* ws_dev, size_t ws_bytes, uint32_t grid,
                      void* plan_host, size_t plan_bytes, wal_grouped_info* ginfo) {
   size_t need_plan = 0, need_ws = 0;
-  int st = wal_grouped_plan_size(n, infos, grid, x_dtype, &need_plan, &need_ws);
+  int st = wal_grouped_plan_size(n, infos, grid, x_dtype_flags, &need_plan, &need_ws);
   if (st) return st;
+  const int x_dtype = x_dtype_flags & ~WAL_X_ROT_H128;   // element type
   if (!W_dev || !x_dev || !y_dev || !plan_host || !ginfo) return WAL_ERR_ARG;
   if (plan_bytes < need_plan) return WAL_ERR_BUFFER;
   if (need_ws && (!ws_dev || ws_bytes < need_ws)) return ws_dev ? WAL_ERR_BUFFER : WAL_ERR_ARG;
@@ -934,7 +989,7 @@ int wal_grouped_plan(uint32_t n, const wal_info* infos, const void* const* W_dev
       return WAL_ERR_ARG;
   }
   PlanShape P;
-  if ((st = plan_shape(n, infos, grid, x_dtype, &P))) return st;
+  if ((st = plan_shape(n, infos, grid, x_dtype_flags, &P))) return st;
   uint8_t* base = static_cast<uint8_t*>(plan_host);
   std::memset(base, 0, P.bytes);
   PlanHeader* h = reinterpret_cast<PlanHeader*>(base);
@@ -1058,7 +1113,7 @@ int wal_grouped_plan(uint32_t n, const wal_info* infos, const void* const* W_dev
   h->grid = gmax;
   h->n_segs = nseg_total;
   h->n_zjobs = (uint32_t)j;
-  h->x_dtype = (uint32_t)x_dtype;
+  h->x_dtype = (uint32_t)x_dtype_flags;
   h->zjob_terms = P.zterms;
   h->reserved = P.n_classes;
   h->off_descs = P.off_descs;
@@ -1069,7 +1124,7 @@ int wal_grouped_plan(uint32_t n, const wal_info* infos, const void* const* W_dev
   ginfo->n_classes = P.n_classes;
   ginfo->n_segs = nseg_total;
   ginfo->n_zjobs = (uint32_t)j;
-  ginfo->x_dtype = (uint32_t)x_dtype;
+  ginfo->x_dtype = (uint32_t)x_dtype_flags;
   ginfo->zjob_terms = P.zterms;
   ginfo->rows_per_batch = kRB;
   ginfo->grid = gmax;
@@ -1087,7 +1142,7 @@ int wal_gemv_grouped_phases(const wal_grouped_info* g, const void* plan_dev, int
   if (!g || !plan_dev) return WAL_ERR_ARG;
   if (phases < 1 || phases > WAL_PHASE_ALL) return WAL_ERR_ARG;
   if (!aligned(plan_dev, 16)) return WAL_ERR_ALIGN;
-  if (g->x_dtype > WAL_X_BF16 || !g->n) return WAL_ERR_ARG;
+  if ((g->x_dtype & ~(uint32_t)(WAL_X_BF16 | WAL_X_ROT_H128)) || !g->n) return WAL_ERR_ARG;
   if (g->rows_per_batch != (uint32_t)kRB || !g->n_classes || g->n_classes > WAL_MAX_CLASSES) return WAL_ERR_ARG;
   for (uint32_t k = 0; k < g->n_classes; ++k) {
     if (g->class_id[k] >= kClasses || !g->class_grid[k]) return WAL_ERR_ARG;
@@ -1107,10 +1162,10 @@ int wal_gemv_grouped_phases(const wal_grouped_info* g, const void* plan_dev, int
   const bool fused = phases == WAL_PHASE_ALL;
   int st;
   if (!fused && (phases & WAL_PHASE_LOWRANK) && g->n_zjobs) {
-    if (g->x_dtype == WAL_X_BF16)
-      hipLaunchKernelGGL(k_z_grouped<WAL_X_BF16>, dim3(g->n_zjobs), dim3(kThreads), 0, s, descs, jobs, g->zjob_terms);
-    else
-      hipLaunchKernelGGL(k_z_grouped<WAL_X_F32>, dim3(g->n_zjobs), dim3(kThreads), 0, s, descs, jobs, g->zjob_terms);
+    const bool bf16 = (g->x_dtype & WAL_X_BF16) != 0, rot = (g->x_dtype & WAL_X_ROT_H128) != 0;
+    auto zk = bf16 ? (rot ? k_z_grouped<WAL_X_BF16, true> : k_z_grouped<WAL_X_BF16, false>)
+                   : (rot ? k_z_grouped<WAL_X_F32, true> : k_z_grouped<WAL_X_F32, false>);
+    hipLaunchKernelGGL(zk, dim3(g->n_zjobs), dim3(kThreads), 0, s, descs, jobs, g->zjob_terms);
     if ((st = launch_status())) return st;
   }
   uint32_t* sync = static_cast<uint32_t*>(g->sync_dev);

@@ -209,10 +209,11 @@ int launch_gemm_prefill(const wal_info& f, const MatDev& d, uint32_t batch, void
 int check_info(const wal_info* info);
 
 // Base-3 streaming kernels (wal_base3.hip), bf16 activations, by
-// (scale format, k) class (4 * scale_fmt + index of k in {0, 2, 4, 8}), and
-// the longest row range one of their workgroups takes.
-GroupedFn base3_grouped_kernel(uint32_t cls);
-SingleFn base3_single_kernel(uint32_t cls);
+// (scale format, k) class (4 * scale_fmt + index of k in {0, 2, 4, 8}) and
+// whether they rotate x (WAL_X_ROT_H128), and the longest row range one of
+// their workgroups takes.
+GroupedFn base3_grouped_kernel(uint32_t cls, bool rot);
+SingleFn base3_single_kernel(uint32_t cls, bool rot);
 uint32_t base3_seg_rows();
 
 }  // namespace wal

@@ -137,3 +137,154 @@ def test_rotated_blob_product(wal, out, inp, k, P, r, b3):
     err = D.rel_l2(y.cpu().numpy().astype(np.float64), ref)
     print(f"rotated product {out}x{inp} base3={b3}: rel_l2 {err:.2e}", flush=True)
     assert err <= 1e-3
+
+
+# ---------------------------------------------------------------------------
+# The rotation fused into the products (x_dtype | WAL_X_ROT_H128): every
+# workgroup that reads x rotates the columns it needs, with wal_rotate_h128's
+# arithmetic, so a fused product equals rotate-then-multiply bit for bit.
+
+def x_dev(x_host, xbf16):
+    if xbf16:
+        return torch.from_numpy(synth.round_bf16_bits(x_host).view(np.int16)).to(dev()).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x_host, dtype=np.float32)).to(dev())
+
+
+def oracle_rotated_x(x_host, xbf16):
+    """The oracle's rotated x in the type the product takes: float64 rotation
+    of the (bf16-rounded) activations, rounded to bf16 for bf16 x."""
+    if xbf16:
+        xr = Rt.rotate(synth.bf16_bits_to_f32(synth.round_bf16_bits(x_host)).astype(np.float64))
+        return synth.bf16_bits_to_f32(bf16_rne(xr)).astype(np.float64)
+    return Rt.rotate(np.asarray(x_host, np.float32).astype(np.float64))
+
+
+def ws_for(wal, info, mode):
+    if mode == "none":
+        return None
+    return torch.zeros(max(wal.wal_workspace_size(info, 1), 4) // 4, dtype=torch.float32, device=dev())
+
+
+FUSED_CASES = [
+    # label, out, in, k, paths, rank, trit format, scale format, bf16 x, workspace
+    ("2bit-one-pass", 257, 4096, 8, 1, 16, synth.TRIT_2BIT, synth.SCALE_FP16, True, "full"),
+    ("2bit-split-passes", 300, 12288, 4, 2, 16, synth.TRIT_2BIT, synth.SCALE_FP16, True, "full"),
+    ("2bit-passes-in-turn", 130, 12288, 8, 0, 0, synth.TRIT_2BIT, synth.SCALE_FP16, True, "none"),
+    ("2bit-fp32-ragged", 190, 8320, 2, 1, 8, synth.TRIT_2BIT, synth.SCALE_FP24, False, "full"),
+    ("2bit-fp32-in-turn", 77, 4224, 0, 0, 0, synth.TRIT_2BIT, synth.SCALE_FP16, False, "none"),
+    ("base3-one-pass", 300, 5120, 4, 2, 16, synth.TRIT_BASE3, synth.SCALE_FP24, True, "full"),
+    ("base3-split-passes", 200, 17408, 2, 2, 16, synth.TRIT_BASE3, synth.SCALE_FP24, True, "full"),
+    ("base3-passes-in-turn", 96, 10368, 8, 0, 0, synth.TRIT_BASE3, synth.SCALE_FP16, True, "none"),
+    ("base3-k0-ragged", 150, 5248, 0, 1, 16, synth.TRIT_BASE3, synth.SCALE_FP24, True, "full"),
+]
+
+
+@pytest.mark.parametrize("label,out,inp,k,P,r,tf,sf,xbf16,wsm", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_fused_rotation_equals_two_launches(wal, label, out, inp, k, P, r, tf, sf, xbf16, wsm):
+    print(f"[rot fused] {label}: {out}x{inp} k={k} paths={P} bf16={xbf16} ws={wsm}", flush=True)
+    m = synth.make_matrix(350, out + inp + k, out, inp, k=k, n_paths=P, rank=r, scale_fmt=sf, trit_fmt=tf)
+    blob, info = wal.pack_matrix(m)
+    x, _ = synth.make_x(351, out + k, inp, bf16=False)
+    W = torch.from_numpy(blob).to(dev())
+    X = x_dev(x[0], xbf16)
+    X0 = X.clone()
+    # two launches: the rotation, then the plain product
+    Xr = torch.empty_like(X)
+    wal.wal_rotate_h128(X.view(1, -1), Xr.view(1, -1))
+    y2 = torch.full((out,), float("nan"), dtype=torch.float32, device=dev())
+    wal.wal_gemv(info, W, Xr, y2, ws_for(wal, info, wsm))
+    # one launch that rotates x itself (fresh workspace, and the same one again)
+    ws = ws_for(wal, info, wsm)
+    y1 = torch.full((out,), float("nan"), dtype=torch.float32, device=dev())
+    wal.wal_gemv(info, W, X, y1, ws, rotate=True)
+    torch.cuda.synchronize()
+    a, b = y1.cpu().numpy(), y2.cpu().numpy()
+    assert np.array_equal(a, b), f"max |diff| {np.nanmax(np.abs(a - b))}"
+    assert torch.equal(X.view(torch.int16) if xbf16 else X, X0.view(torch.int16) if xbf16 else X0)   # x untouched
+    y1.fill_(float("nan"))
+    wal.wal_gemv(info, W, X, y1, ws, rotate=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(y1.cpu().numpy(), a)
+    ref = D.gemv(F.pack(F.from_synth(m)), oracle_rotated_x(x[0], xbf16))
+    err = D.rel_l2(a.astype(np.float64), ref)
+    print(f"[rot fused] {label}: rel_l2 vs oracle {err:.2e}", flush=True)
+    assert err <= (1e-3 if xbf16 else 1e-5)
+
+
+def test_fused_rotation_no_alloc_and_fallback(wal):
+    """The allocation-free entry point rotates the same way, and a consumer
+    whose bounded wait for the low-rank terms gives up rotates x itself to
+    compute them (sums in another order: agreement to rounding)."""
+    for b3 in (False, True):
+        out, inp = (700, 12288) if not b3 else (520, 17408)
+        print(f"[rot fused] no-alloc and forced fallback, base3={b3}", flush=True)
+        m = synth.make_matrix(352, out, out, inp, k=4, n_paths=2, rank=16,
+                              trit_fmt=synth.TRIT_BASE3 if b3 else synth.TRIT_2BIT,
+                              scale_fmt=synth.SCALE_FP24 if b3 else synth.SCALE_FP16)
+        blob, info = wal.pack_matrix(m)
+        x, _ = synth.make_x(353, out, inp, bf16=False)
+        W, X = torch.from_numpy(blob).to(dev()), x_dev(x[0], True)
+        ws = ws_for(wal, info, "full")
+        y = torch.full((out,), float("nan"), dtype=torch.float32, device=dev())
+        wal.wal_gemv(info, W, X, y, ws, rotate=True)
+        y_na = torch.full((out,), float("nan"), dtype=torch.float32, device=dev())
+        wal.wal_gemv_noalloc(info, W, X, y_na, rotate=True)
+        torch.cuda.synchronize()
+        want = y.cpu().numpy()
+        assert np.array_equal(y_na.cpu().numpy(), want)
+        assert wal.sync_fallbacks(ws) == 0
+        # epoch copies seeded apart: the waits give up and fall back
+        words = ws.view(-1).view(torch.uint8)[:wal.WAL_SYNC_BYTES].view(torch.int32)
+        e0 = int(words[32].item())
+        for rr in range(1, 16):
+            words[32 * (1 + rr)] = e0 + 1
+        y.fill_(float("nan"))
+        wal.wal_gemv(info, W, X, y, ws, rotate=True)
+        torch.cuda.synchronize()
+        assert wal.sync_fallbacks(ws) > 0
+        assert D.rel_l2(y.cpu().numpy().astype(np.float64), want.astype(np.float64)) <= 1e-5
+        wal.clear_sync_fallbacks(ws)
+
+
+@pytest.mark.parametrize("grid", [0, 64])
+def test_fused_rotation_grouped_plan(wal, grid):
+    """A grouped plan with WAL_X_ROT_H128 (every matrix rotated; with grid 64
+    the wide matrices run their passes in turn) against the plan without it on
+    x rotated by wal_rotate_h128: bit for bit, fused and with the low-rank
+    jobs as a launch of their own."""
+    print(f"[rot fused] grouped plan, grid={grid}", flush=True)
+    shapes = [(512, 4096, 8, 1), (1024, 4096, 8, 2), (300, 4224, 4, 1), (777, 12288, 8, 0), (96, 12288, 2, 1)]
+    ms = [synth.make_matrix(354, i, o, n, k=k, n_paths=p, rank=16 if p else 0) for i, (o, n, k, p) in enumerate(shapes)]
+    packed = [wal.pack_matrix(m) for m in ms]
+    infos = [i for _, i in packed]
+    Ws = [torch.from_numpy(b).to(dev()) for b, _ in packed]
+    xs = [x_dev(synth.make_x(355, i, m.inp, bf16=False)[0][0], True) for i, m in enumerate(ms)]
+    xr = [torch.empty_like(x) for x in xs]
+    for a, b in zip(xs, xr):
+        wal.wal_rotate_h128(a.view(1, -1), b.view(1, -1))
+
+    def plan_run(x_list, flags, phases=None):
+        ys = [torch.full((m.out,), float("nan"), dtype=torch.float32, device=dev()) for m in ms]
+        _, wsb = wal.wal_grouped_plan_size(infos, grid, flags)
+        ws = torch.zeros(max(wsb, 4) // 4, dtype=torch.float32, device=dev())
+        plan, g = wal.wal_grouped_plan(infos, Ws, x_list, ys, ws, flags, grid)
+        assert g.x_dtype == flags
+        pd = torch.from_numpy(plan).to(dev())
+        if phases is None:
+            wal.wal_gemv_grouped(g, pd)
+        else:
+            for ph in phases:
+                wal.wal_gemv_grouped_phases(g, pd, ph)
+        torch.cuda.synchronize()
+        return [y.cpu().numpy() for y in ys]
+
+    want = plan_run(xr, wal.WAL_X_BF16)
+    got = plan_run(xs, wal.WAL_X_BF16 | wal.WAL_X_ROT_H128)
+    got2 = plan_run(xs, wal.WAL_X_BF16 | wal.WAL_X_ROT_H128, phases=[wal.WAL_PHASE_LOWRANK, wal.WAL_PHASE_STREAM])
+    for i, (a, b, c) in enumerate(zip(want, got, got2)):
+        assert np.array_equal(a, b), i
+        assert np.array_equal(a, c), i
+    for i, m in enumerate(ms):
+        x = synth.make_x(355, i, m.inp, bf16=False)[0][0]
+        ref = D.gemv(F.pack(F.from_synth(m)), oracle_rotated_x(x, True))
+        assert D.rel_l2(got[i].astype(np.float64), ref) <= 1e-3

@@ -316,6 +316,17 @@ def test_product_calls_check_arguments_before_any_launch():
     assert gp(W, x, 1, 16384, 1 << 17, y, 64, ws, need, None) == -2          # X beyond 2 GiB
     assert lib.wal_gemv_grouped(None, 0x1000, None) == -1
     assert lib.wal_gemv_grouped_seq(0, None, None, None) == -1
+    # the rotation flag: accepted by the batch-1 products (their other checks
+    # still apply), refused by the batched ones, other flag bits rejected
+    R = wal.WAL_X_ROT_H128
+    assert lib.wal_gemv(ctypes.byref(info), W, x, 1 | R, y, ws, 8, None) == -5          # flag accepted
+    assert lib.wal_gemv(ctypes.byref(info), W, x, 1 | 32, y, ws, n1, None) == -1        # unknown flag
+    assert lib.wal_gemv(ctypes.byref(info), W, x, 2 | R, y, ws, n1, None) == -1         # bad type, flag
+    need = wal.wal_workspace_size(info, 2)
+    assert gs(W, x, 1 | R, 2, 256, y, 64, 0, ws, need, None) == -9
+    assert gs(W, x, 0 | R, 2, 256, y, 64, 0, ws, need, None) == -9
+    need = wal.wal_prefill_workspace_size(info, 64)
+    assert gp(W, x, 1 | R, 64, 256, y, 64, ws, need, None) == -9
     rot = lib.wal_rotate_h128
     assert rot(None, 1, 1, 128, 128, y, 1, 128, None) == -1                     # x missing
     assert rot(x, 1, 0, 128, 128, y, 1, 128, None) == -1                        # no rows
@@ -453,6 +464,24 @@ def test_grouped_plan_covers_every_row_once(grid):
     assert g.zjob_terms == (4 if len(jobs_of(4)) <= 64 else 16)
     want = jobs_of(g.zjob_terms)
     assert sorted(map(tuple, jobs.tolist())) == sorted(want)
+
+
+def test_grouped_plan_records_rotation_flag():
+    """A plan built with WAL_X_ROT_H128 keeps the flag in its info (its
+    launches take the kernels that rotate x) and is laid out like the plain
+    plan; unknown flag bits are rejected."""
+    import ctypes
+    infos = [wal.wal_packed_size(wal.make_desc(o, n, 8, p, 16 if p else 0)) for o, n, p in
+             [(512, 4096, 1), (300, 12288, 0)]]
+    plan0, g0 = _plan_on_host(infos, 64, wal.WAL_X_BF16)
+    plan1, g1 = _plan_on_host(infos, 64, wal.WAL_X_BF16 | wal.WAL_X_ROT_H128)
+    assert g0.x_dtype == wal.WAL_X_BF16 and g1.x_dtype == wal.WAL_X_BF16 | wal.WAL_X_ROT_H128
+    assert g0.plan_bytes == g1.plan_bytes and g0.n_segs == g1.n_segs and g0.n_zjobs == g1.n_zjobs
+    _, g2 = _plan_on_host(infos, 64, wal.WAL_X_F32 | wal.WAL_X_ROT_H128)
+    assert g2.x_dtype == wal.WAL_X_ROT_H128
+    arr = (wal.wal_info * 2)(*infos)
+    pb, wb = ctypes.c_size_t(), ctypes.c_size_t()
+    assert wal._lib.wal_grouped_plan_size(2, arr, 64, 1 | 64, ctypes.byref(pb), ctypes.byref(wb)) == -1
 
 
 def test_grouped_plan_job_size():
