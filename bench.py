@@ -229,7 +229,7 @@ def run_single(args):
             us = time_calls(torch, lambda i: wal.wal_gemv(info, Ws[i % len(Ws)], xt, y, ws), calls)
             gbs = info.algorithmic_bytes / (us * 1e-6) / 1e9
             extra = {}
-            if cfg == 4:   # the 27B card's blobs are H128-rotated: x is rotated first
+            if cfg == 4:   # the 27B card's blobs are H128-rotated: the product takes R x
                 xr = torch.empty_like(xt)
                 rot_us = time_calls(torch, lambda i: wal.wal_rotate_h128(xt, xr), calls)
 
@@ -237,7 +237,14 @@ def run_single(args):
                     wal.wal_rotate_h128(xt, xr)
                     wal.wal_gemv(info, Ws[i % len(Ws)], xr, y, ws)
                 both_us = time_calls(torch, rotated, calls)
-                extra = {"rotate_h128_us": round(rot_us, 3), "rotated_product_us": round(both_us, 3)}
+                # the rotation inside the product's own launch (WAL_X_ROT_H128),
+                # timed next to the plain product again
+                fused_us = time_calls(torch, lambda i: wal.wal_gemv(info, Ws[i % len(Ws)], xt, y, ws, rotate=True),
+                                      calls)
+                plain_us = time_calls(torch, lambda i: wal.wal_gemv(info, Ws[i % len(Ws)], xt, y, ws), calls)
+                extra = {"rotate_h128_us": round(rot_us, 3), "rotate_then_product_us": round(both_us, 3),
+                         "fused_rotated_product_us": round(fused_us, 3), "plain_product_again_us": round(plain_us, 3),
+                         "fused_rotation_cost_us": round(fused_us - plain_us, 3)}
             t_all, t_mm = oracle_time(blob, x[:1])
             res.append({"shape": [int(info.d.out), int(info.d.in_)], "k": int(info.d.k),
                         "format": "base-3 / fp24" if info.d.trit_fmt else "2-bit / fp16",

@@ -360,41 +360,34 @@ __device__ __forceinline__ void stream_rows_base3(const MatDev& d, uint32_t row0
   // Set-up loads first (L2 hits: x, the table's x), then the first two
   // batches (HBM): loads complete in order, so waiting for the set-up data
   // does not wait for the batches.
-  // A rotated product (ROT) instead rotates the pass's 40 groups in two rounds of
-  // 16-column pieces (the second round's pieces past the pass, and the
-  // table's zero slot, load zeros); the pass then goes through LDS twice, as
-  // compact activations that each lane reads its columns from, and as the
-  // table.
+  // A rotated product (ROT) instead has the workgroup rotate the pass's 40
+  // groups (RotPass: three 16-group tiles, the groups past the pass load
+  // zeros, so the table's zero slot receives zeros); the pass then goes
+  // through LDS twice, as compact activations that each lane reads its
+  // columns from, and as the table.
   const __amdgpu_buffer_rsrc_t rx = x_rsrc<WAL_X_BF16>(d.x, d.in);
-  const RotSlot rs0 = rot_slot(0), rs1 = rot_slot(1);
-  float rv0[16], rv1[16];
+  RotPass<WAL_X_BF16, kGroups3> rp;
   XLane3::Raw xr;
   TableX3 tx;
   if constexpr (ROT) {
-    rot_load<WAL_X_BF16>(rx, pass * kPassBase3 + 128 * rs0.g + 16 * rs0.sub, rv0);
-    rot_load<WAL_X_BF16>(rs1.g < kGroups3 ? rx : r_none, pass * kPassBase3 + 128 * rs1.g + 16 * rs1.sub, rv1);
+    rp.load(rx, pass * kPassBase3);
   } else {
     XLane3::load_raw(rx, pass * kPassBase3 + 80 * lane, xr);
     if constexpr (K > 0) tx.load(rx, pass * kPassBase3);
   }
   Batch3<RB> B0 = load_batch(b);
   Batch3<RB> B1 = load_batch(b + kWaves);
-  if constexpr (ROT) {
-    rot_apply<WAL_X_BF16>(rv0, rs0.sub);
-    rot_apply<WAL_X_BF16>(rv1, rs1.sub);
-  }
+  if constexpr (ROT) rp.compute();
 
   __syncthreads();   // readers of the previous table are done
   if (lut_first) build_lut(sm.lut);
   if constexpr (ROT) {
-    rot_store_x<WAL_X_BF16>(sm.tbl, 128 * rs0.g + 16 * rs0.sub, rv0);
-    if (rs1.g < kGroups3) rot_store_x<WAL_X_BF16>(sm.tbl, 128 * rs1.g + 16 * rs1.sub, rv1);
+    rp.store_x(sm.tbl);
     __syncthreads();
     XLane3::load_lds(sm.tbl, 80 * lane, xr);
     if constexpr (K > 0) {
       __syncthreads();   // every lane has its columns
-      rot_store_tbl<WAL_X_BF16>(sm.tbl, rs0, rv0);
-      if (rs1.g <= kGroups3) rot_store_tbl<WAL_X_BF16>(sm.tbl, rs1, rv1);
+      rp.store_tbl(sm.tbl, kGroups3 + 1);
     }
   } else if constexpr (K > 0) {
     tx.store(sm.tbl);
@@ -447,8 +440,13 @@ __device__ __forceinline__ void z_job_grouped3(const MatDev* __restrict__ descs,
                                               c0, c1, epoch, xs);
 }
 
+// Two workgroups per CU (the LDS allows no more); kernels that rotate x are
+// held to the registers of two wavefronts per SIMD.
+constexpr int stream3_waves_per_simd(bool ROT) { return ROT ? 2 : 1; }
+
 template <int SF, int K, bool ROT>
-__global__ __launch_bounds__(kThreads) void k_stream3_grouped(const MatDev* __restrict__ descs,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(stream3_waves_per_simd(ROT))))
+void k_stream3_grouped(const MatDev* __restrict__ descs,
                                                               const uint32_t* __restrict__ blockseg,
                                                               const Seg* __restrict__ segs,
                                                               const uint32_t* __restrict__ jobs, Fuse f) {
@@ -473,7 +471,8 @@ __global__ __launch_bounds__(kThreads) void k_stream3_grouped(const MatDev* __re
 }
 
 template <int SF, int K, bool ROT>
-__global__ __launch_bounds__(kThreads) void k_stream3_single(MatDev d, uint32_t rows_per_block, uint32_t nrb,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(stream3_waves_per_simd(ROT))))
+void k_stream3_single(MatDev d, uint32_t rows_per_block, uint32_t nrb,
                                                              float* P, uint32_t* cnt, Fuse f) {
   // block t < f.nz: low-rank job t; else without P block b takes rows
   // [b rpb, b rpb + rpb) over every pass, with P pass b / nrb of row block

@@ -10,6 +10,8 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x3_t __attribute__((ext_vector_type(3)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 namespace {
 
@@ -301,18 +303,217 @@ __device__ __forceinline__ void rot_store_tbl(float* tbl, const RotSlot& s, cons
   }
 }
 
+// ---------------------------------------------------------------------------
+// The same rotation of bf16 activations on the matrix cores: rotating groups
+// is a dense product X H (rows of X the groups, H the 128 x 128 +-1 matrix),
+// exact in its bf16 operands and summed in fp32, which costs each wavefront
+// a few MFMAs instead of hundreds of vector instructions per piece.
+//
+// A 16-group x 16-column tile is four v_mfma_f32_16x16x32_bf16 along the
+// input column k = 32 s + 8 kb + e (step s): x is the A operand (lane (i, kb)
+// holds x[group i][32 s + 8 kb .. + 7], 16 contiguous bytes), H the B operand
+// (lane (n, kb) holds H[32 s + 8 kb + e][16 jt + n] for e = 0..7), and lane
+// (n, q) ends with groups 4 q .. 4 q + 3 of output column 16 jt + n.  The
+// sign of H[k][j] is the parity of popcount(e & n) + kb0 n3 + kb1 jt0 +
+// s0 jt1 + s1 jt2; wavefront w takes the column tiles jt = w + 4 u (u = 0, 1),
+// so jt0 and jt1 are its own and jt2 = u is known at compile time: four B
+// registers per lane serve every tile.  The scale and the bf16 rounding
+// (v_cvt_pk_bf16_f32, to nearest even) follow, as in wal_rotate_h128, which
+// runs this same code for bf16 input, so the two agree bit for bit.
+struct RotB {
+  uint4 even, even_neg, odd, odd_neg;   // B operands of even / odd steps s
+
+  __device__ __forceinline__ void init() {
+    const uint32_t l = threadIdx.x & 63, n = l & 15, kb = l >> 4, w = wave_id();
+    uint32_t p[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t e = 2 * q + h;
+        const uint32_t neg = (__builtin_popcount(e & n) + (kb & 1) * (n >> 3) + ((kb >> 1) & w & 1)) & 1;
+        v |= (0x3F80u | (neg << 15)) << (16 * h);
+      }
+      p[q] = v;
+    }
+    const uint32_t odd_flip = (w & 2) ? 0x80008000u : 0u;   // s0 jt1, jt1 = bit 1 of w
+    even = make_uint4(p[0], p[1], p[2], p[3]);
+    even_neg = make_uint4(p[0] ^ 0x80008000u, p[1] ^ 0x80008000u, p[2] ^ 0x80008000u, p[3] ^ 0x80008000u);
+    odd = make_uint4(p[0] ^ odd_flip, p[1] ^ odd_flip, p[2] ^ odd_flip, p[3] ^ odd_flip);
+    odd_neg = make_uint4(odd.x ^ 0x80008000u, odd.y ^ 0x80008000u, odd.z ^ 0x80008000u, odd.w ^ 0x80008000u);
+  }
+  // step S of column tile w + 4 U: the s1 jt2 sign is S >> 1 & U
+  template <int S, int U>
+  __device__ __forceinline__ const uint4& op() const {
+    constexpr bool neg = ((S >> 1) & U) != 0;
+    if constexpr (S & 1) return neg ? odd_neg : odd;
+    return neg ? even_neg : even;
+  }
+};
+
+__device__ __forceinline__ f32x4_t rot_mfma(const uint4& a, const uint4& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+
+// NGT tiles of 16 groups (groups 16 gt + i) of one row of bf16 activations,
+// rotated: load the x operands, compute (rounded to bf16), then store.
+template <int NGT, bool F32OUT = false>
+struct RotTiles {
+  uint4 a[NGT][4];       // x operands [group tile][step]
+  uint32_t r[NGT][2][2];  // results as bf16 pairs: [group tile][u][pair of groups 4 q + (0, 1) / (2, 3)]
+  f32x4_t f[F32OUT ? NGT : 1][2];   // with F32OUT: the scaled fp32 results [group tile][u]
+
+  // Group g's columns start at element col0 + 128 g of the resource; groups
+  // g >= ng load zeros.
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rx, uint32_t col0, uint32_t ng) {
+    const uint32_t l = threadIdx.x & 63, i = l & 15, kb = l >> 4;
+#pragma unroll
+    for (int gt = 0; gt < NGT; ++gt) {
+      const uint32_t g = 16 * gt + i;
+      // an offset past 2 GB reads zeros without touching memory
+      const uint32_t off = g < ng ? 2 * (col0 + 128 * g + 8 * kb) : 0x80000000u;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) a[gt][s] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, off + 64 * s, 0, 0));
+    }
+  }
+  template <int GT, int U>
+  __device__ __forceinline__ f32x4_t tile(const RotB& hb) const {
+    f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+    c = rot_mfma(a[GT][0], hb.op<0, U>(), c);
+    c = rot_mfma(a[GT][1], hb.op<1, U>(), c);
+    c = rot_mfma(a[GT][2], hb.op<2, U>(), c);
+    c = rot_mfma(a[GT][3], hb.op<3, U>(), c);
+    return c;
+  }
+  template <int GT>
+  __device__ __forceinline__ void compute_from(const RotB& hb) {
+    if constexpr (GT < NGT) {
+      const f32x4_t c0 = tile<GT, 0>(hb), c1 = tile<GT, 1>(hb);
+      if constexpr (F32OUT) {
+        f[GT][0] = c0 * kInvSqrt128;
+        f[GT][1] = c1 * kInvSqrt128;
+        compute_from<GT + 1>(hb);
+        return;
+      }
+      r[GT][0][0] = pack_bf16(c0[0] * kInvSqrt128, c0[1] * kInvSqrt128);
+      r[GT][0][1] = pack_bf16(c0[2] * kInvSqrt128, c0[3] * kInvSqrt128);
+      r[GT][1][0] = pack_bf16(c1[0] * kInvSqrt128, c1[1] * kInvSqrt128);
+      r[GT][1][1] = pack_bf16(c1[2] * kInvSqrt128, c1[3] * kInvSqrt128);
+      compute_from<GT + 1>(hb);
+    }
+  }
+  __device__ __forceinline__ void compute() {
+    RotB hb;
+    hb.init();
+    compute_from<0>(hb);
+  }
+  static __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  // The rotated value of tile (gt, u), group 4 q + jj, as bf16 bits.
+  __device__ __forceinline__ uint32_t bits(int gt, int u, int jj) const {
+    return jj & 1 ? r[gt][u][jj >> 1] >> 16 : r[gt][u][jj >> 1] & 0xFFFFu;
+  }
+  // Output column of tile u for this lane, and group of (gt, jj).
+  static __device__ __forceinline__ uint32_t column(int u) { return 16 * (wave_id() + 4 * u) + (threadIdx.x & 15); }
+  static __device__ __forceinline__ uint32_t group(int gt, int jj) {
+    return 16 * gt + 4 * ((threadIdx.x & 63) >> 4) + jj;
+  }
+
+  // Compact activations xs[128 g + j] (bf16, LDS) of groups g < ng.  The
+  // lane's first element is 128 (4 q) + 16 w + n; every value sits a
+  // constant offset from it (folded into the LDS store).
+  __device__ __forceinline__ void store_x(uint16_t* xs, uint32_t ng) const {
+    const uint32_t l = threadIdx.x & 63, q = l >> 4;
+    uint16_t* base = xs + 512 * q + 16 * wave_id() + (l & 15);
+#pragma unroll
+    for (int gt = 0; gt < NGT; ++gt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        if (16 * gt + 16 <= (int)ng || 16 * gt + 4 * q + jj < ng) {
+#pragma unroll
+          for (int u = 0; u < 2; ++u) base[128 * (16 * gt + jj) + 64 * u] = (uint16_t)bits(gt, u, jj);
+        }
+      }
+  }
+  // Signed site table entries tbl[g][j] = 2 x~, tbl[g][128 + j] = -2 x~ of
+  // groups g < ng.
+  __device__ __forceinline__ void store_tbl(float* tbl, uint32_t ng) const {
+    const uint32_t l = threadIdx.x & 63, q = l >> 4;
+    float* base = tbl + 1024 * q + 16 * wave_id() + (l & 15);
+#pragma unroll
+    for (int gt = 0; gt < NGT; ++gt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        if (16 * gt + 16 <= (int)ng || 16 * gt + 4 * q + jj < ng) {
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const float v = __uint_as_float(bits(gt, u, jj) << 16);
+            base[256 * (16 * gt + jj) + 64 * u] = 2.0f * v;
+            base[256 * (16 * gt + jj) + 64 * u + 128] = -2.0f * v;
+          }
+        }
+      }
+  }
+};
+
+// The rotation of one pass of NG groups inside a streaming workgroup, in
+// three steps around its set-up barriers: load (before the first batch's
+// loads), compute (registers only), store the compact activations and the
+// signed site table (after the barrier).  bf16 activations go through the
+// matrix cores; fp32 activations (NG = 32) through the butterflies, one
+// 16-column piece per thread.
+template <int XT, int NG>
+struct RotPass;
+
+template <int NG>
+struct RotPass<WAL_X_BF16, NG> {
+  RotTiles<(NG + 15) / 16> t;
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rx, uint32_t col0) { t.load(rx, col0, NG); }
+  __device__ __forceinline__ void compute() { t.compute(); }
+  __device__ __forceinline__ void store_x(void* xs) const { t.store_x(static_cast<uint16_t*>(xs), NG); }
+  // table slots: groups < slots (slots past NG receive zeros)
+  __device__ __forceinline__ void store_tbl(float* tbl, uint32_t slots) const { t.store_tbl(tbl, slots); }
+};
+
+template <int NG>
+struct RotPass<WAL_X_F32, NG> {
+  static_assert(NG == 32, "fp32 activations: one 4096-column pass of the 2-bit kernels");
+  RotSlot s;
+  float v[16];
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rx, uint32_t col0) {
+    s = rot_slot(0);
+    rot_load<WAL_X_F32>(rx, col0 + 128 * s.g + 16 * s.sub, v);
+  }
+  __device__ __forceinline__ void compute() { rot_apply<WAL_X_F32>(v, s.sub); }
+  __device__ __forceinline__ void store_x(void* xs) const { rot_store_x<WAL_X_F32>(xs, 128 * s.g + 16 * s.sub, v); }
+  __device__ __forceinline__ void store_tbl(float* tbl, uint32_t) const { rot_store_tbl<WAL_X_F32>(tbl, s, v); }
+};
+
 // Columns [c0, c0 + 128 ng) of x (n columns; ng <= 64) rotated into xs (LDS,
 // x's type, column c0 at element 0) by the whole workgroup, then a barrier.
 // Every thread calls it.
 template <int XT>
 __device__ __forceinline__ void rot_to_lds(const void* x, uint32_t n, uint32_t c0, uint32_t ng, void* xs) {
   const __amdgpu_buffer_rsrc_t rx = rsrc(x, n * (XT == WAL_X_F32 ? 4u : 2u));
-  for (uint32_t round = 0; 32 * round < ng; ++round) {
-    const RotSlot s = rot_slot(round);
-    float v[16];
-    rot_load<XT>(rx, c0 + 128 * s.g + 16 * s.sub, v);
-    rot_apply<XT>(v, s.sub);
-    if (s.g < ng) rot_store_x<XT>(xs, 128 * s.g + 16 * s.sub, v);
+  if constexpr (XT == WAL_X_BF16) {
+    for (uint32_t g0 = 0; g0 < ng; g0 += 32) {
+      RotTiles<2> rt;
+      rt.load(rx, c0 + 128 * g0, ng - g0);
+      rt.compute();
+      rt.store_x(static_cast<uint16_t*>(xs) + 128 * g0, ng - g0);
+    }
+  } else {
+    for (uint32_t round = 0; 32 * round < ng; ++round) {
+      const RotSlot s = rot_slot(round);
+      float v[16];
+      rot_load<XT>(rx, c0 + 128 * s.g + 16 * s.sub, v);
+      rot_apply<XT>(v, s.sub);
+      if (s.g < ng) rot_store_x<XT>(xs, 128 * s.g + 16 * s.sub, v);
+    }
   }
   __syncthreads();
 }

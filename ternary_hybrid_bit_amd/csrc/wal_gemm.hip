@@ -38,8 +38,6 @@
 
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 template <int SF>
 __device__ __forceinline__ float scale_value(uint32_t raw) {

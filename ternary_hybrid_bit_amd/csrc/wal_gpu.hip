@@ -343,17 +343,16 @@ __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0,
   // table (L2 hits).  Vector memory loads complete in order, so waiting for
   // these after the first batch's loads (HBM) are issued does not wait for
   // the batch.
-  // A rotated product (ROT) instead loads one 16-column piece per thread of
-  // the whole pass (the workgroup's 256 pieces are the pass's 32 groups) and
-  // rotates it; the pass then goes through LDS twice, as compact
-  // activations that each lane reads its columns from, and as the table.
+  // A rotated product (ROT) instead has the workgroup rotate the whole
+  // pass's 32 groups (RotPass); the pass then goes through LDS twice, as
+  // compact activations that each lane reads its columns from, and as the
+  // table.
   const __amdgpu_buffer_rsrc_t rx = x_rsrc<XT>(d.x, d.in);
-  const RotSlot rs = rot_slot(0);
-  float rv[16];
+  RotPass<XT, 32> rp;
   typename XLane<XT>::Raw xr;
   TableX<XT> tx;
   if constexpr (ROT) {
-    rot_load<XT>(rx, pass * kPass2bit + 128 * rs.g + 16 * rs.sub, rv);
+    rp.load(rx, pass * kPass2bit);
   } else {
     XLane<XT>::load_raw(rx, pass * kPass2bit + 64 * lane, xr);
     if constexpr (K > 0) tx.load(rx, pass * kPass2bit);
@@ -363,16 +362,16 @@ __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0,
   // (three resident workgroups per CU keep three wavefronts per SIMD, six
   // batches, in flight).
   Batch<RB> B0 = load_batch(b);
-  if constexpr (ROT) rot_apply<XT>(rv, rs.sub);
+  if constexpr (ROT) rp.compute();
 
   __syncthreads();   // readers of the previous table are done
   if constexpr (ROT) {
-    rot_store_x<XT>(sm.tbl, 128 * rs.g + 16 * rs.sub, rv);
+    rp.store_x(sm.tbl);
     __syncthreads();
     XLane<XT>::load_lds(sm.tbl, 64 * lane, xr);
     if constexpr (K > 0) {
       __syncthreads();   // every lane has its columns
-      rot_store_tbl<XT>(sm.tbl, rs, rv);
+      rp.store_tbl(sm.tbl, 32);
     }
   } else if constexpr (K > 0) {
     tx.store(sm.tbl);
@@ -413,9 +412,11 @@ __device__ __forceinline__ void run_segment_2bit(const MatDev& d, uint32_t row0,
 
 // Three workgroups per CU (the LDS of a workgroup allows it) when the class's
 // registers fit three wavefronts per SIMD without spilling; the fp32 and the
-// fp24 / k = 8 loops need more registers and run two.
-constexpr int stream_waves_per_simd(int XT, int SF, int K) {
-  return XT == WAL_X_BF16 && !(SF == WAL_SCALE_FP24 && K == 8) ? 3 : 1;
+// fp24 / k = 8 loops need more registers and run two.  Kernels that rotate x
+// hold the rotation's operands while their first batch is in flight and run
+// two (no spills).
+constexpr int stream_waves_per_simd(int XT, int SF, int K, bool ROT) {
+  return ROT ? 2 : XT == WAL_X_BF16 && !(SF == WAL_SCALE_FP24 && K == 8) ? 3 : 1;
 }
 
 // Low-rank job of a fused launch or of the grouped pre-pass: terms t0 ..
@@ -435,7 +436,7 @@ __device__ __forceinline__ void grouped_z_job(const MatDev* __restrict__ descs, 
 // Grouped products: workgroup t = blockIdx.x computes low-rank job t when
 // t < f.nz, else streams the segments of block t - f.nz.
 template <int XT, int SF, int K, int RB, bool ROT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(stream_waves_per_simd(XT, SF, K))))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(stream_waves_per_simd(XT, SF, K, ROT))))
 void k_stream_grouped(const MatDev* __restrict__ descs, const uint32_t* __restrict__ blockseg,
                       const Seg* __restrict__ segs, const uint32_t* __restrict__ jobs, Fuse f) {
   __shared__ StreamSmem sm;
@@ -465,7 +466,7 @@ void k_stream_grouped(const MatDev* __restrict__ descs, const uint32_t* __restri
 // pass; with P, block b takes pass b / nrb of row block b % nrb (rpb a
 // multiple of 16; cnt: the arrival counters, one per 16 rows).
 template <int XT, int SF, int K, int RB, bool ROT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(stream_waves_per_simd(XT, SF, K))))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(stream_waves_per_simd(XT, SF, K, ROT))))
 void k_stream_single(MatDev d, uint32_t rows_per_block, uint32_t nrb, float* P, uint32_t* cnt, Fuse f) {
   __shared__ StreamSmem sm;
   const uint32_t t = blockIdx.x;
