@@ -144,7 +144,7 @@ typedef struct {
   uint32_t n_classes;      /* classes present (streaming launches)          */
   uint32_t n_segs;         /* (matrix, row range) segments, all classes     */
   uint32_t n_zjobs;        /* workgroups of the low-rank V^T x pre-pass     */
-  uint32_t x_dtype;
+  uint32_t x_dtype;        /* as passed to wal_grouped_plan, flags included */
   uint32_t zjob_terms;     /* low-rank terms per job (4 or 16)             */
   uint32_t rows_per_batch; /* rows a wavefront reduces at once              */
   uint32_t grid;           /* largest class grid                           */
@@ -353,7 +353,8 @@ int wal_gemm_prefill(const wal_info* info, const void* W_dev, const void* X_dev,
  *      low-rank terms in its first workgroups, and the streaming workgroups
  *      wait for them (bounded) only when they store their rows; a
  *      workgroup whose wait gives up computes them itself.
- * All matrices share x_dtype; base-3 matrices need bf16 activations
+ * All matrices share x_dtype (with WAL_X_ROT_H128 every matrix of the plan
+ * takes its own x rotated); base-3 matrices need bf16 activations
  * (WAL_ERR_UNSUPPORTED otherwise).  ws_dev must hold
  * wal_grouped_plan_size's ws_bytes, 16-byte aligned (NULL when that is 0).
  * When the plan has low-rank paths or split matrices, the workspace starts
@@ -487,7 +488,11 @@ int wal_int5_gemv(const void* W_dev, uint32_t V, uint32_t in, const void* x_dev,
  *   out_dev  [rows][ldo] bf16 or fp32 (out_dtype), 16-byte aligned rows;
  *            columns past `in` untouched.  out may be x itself (same type
  *            and pitch: in place); any other overlap is rejected
- * Arithmetic in fp32; bf16 output rounds to nearest even.
+ * Arithmetic: bf16 input as the product X H on the matrix cores (exact
+ * bf16 operands, fp32 sums), fp32 input as fp32 butterflies; then the
+ * multiply by fp32(1/sqrt(128)), and bf16 output rounds to nearest even.
+ * The products that rotate x themselves (WAL_X_ROT_H128) use the same
+ * arithmetic.
  * Errors: ARG, SHAPE, ALIGN, DEVICE. */
 int wal_rotate_h128(const void* x_dev, int x_dtype, uint32_t rows, uint32_t in, uint32_t ldx,
                     void* out_dev, int out_dtype, uint32_t ldo, void* stream);

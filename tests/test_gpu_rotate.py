@@ -11,7 +11,13 @@ the CPU oracle (oracle/rotation.py), and of products of a rotated blob.
 * in place, ragged row counts, padded pitches, fp32 and bf16 inputs;
 * a rotated product: wal_gemv of a base-3 / fp24 blob on the rotated bf16 x
   matches the oracle product on the oracle's rotated, bf16-rounded x
-  (relative L2 <= 1e-3, as for every bf16 product).
+  (relative L2 <= 1e-3, as for every bf16 product);
+* the rotation inside the products (WAL_X_ROT_H128): equal bit for bit to
+  wal_rotate_h128 followed by the plain product (both formats, bf16 and
+  fp32 x, one pass, split passes, passes in turn, ragged widths, grouped
+  plans fused and by phases, the allocation-free entry point, the forced
+  fallback of the low-rank wait), x left untouched, and within the product
+  tolerance of the oracle on the oracle's rotated x.
 """
 import numpy as np
 import pytest
