@@ -489,6 +489,27 @@ def run_sweep3(args):
     dom = max(per_class, key=lambda r: r["bytes_per_launch"])
     nbytes = sum(int(i.algorithmic_bytes) for i in infos)
     gbs = nbytes / (ms_step * 1e-3) / 1e9
+    # The 27B card's blobs are H128-rotated: the same plans with the rotation
+    # of x inside the launches (WAL_X_ROT_H128), timed the same way.
+    rplans = []
+    for k, ids, _, _, _ in plans:
+        inf = [infos[j] for j in ids]
+        flags = wal.WAL_X_BF16 | wal.WAL_X_ROT_H128
+        _, wsb = wal.wal_grouped_plan_size(inf, 0, flags)
+        ws = torch.zeros(max(wsb, 4) // 4, dtype=torch.float32, device=dev)
+        plan, g = wal.wal_grouped_plan(inf, [Ws[j] for j in ids], [xs[j] for j in ids], [ys[j] for j in ids], ws, flags)
+        rplans.append((g, torch.from_numpy(plan).to(dev), ws))
+    for _ in range(max(args.warmup, 3)):
+        for g, pd, _ in rplans:
+            wal.wal_gemv_grouped(g, pd)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(K):
+        for g, pd, _ in rplans:
+            wal.wal_gemv_grouped(g, pd)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_rot = ev0.elapsed_time(ev1) / K
     out = {"workload": "sweep3", "config": {"workload": "qwen3.5-27b-shaped-base3-body-88-gemv-batch1",
                                             "matrices": len(items), "shapes": [[17408, 5120], [5120, 17408]],
                                             "format": "base-3 T (5 trits/byte) + sparse k in {0,2,4,8} + fp24 "
@@ -499,7 +520,11 @@ def run_sweep3(args):
            "roofline": {"bound": "hbm", "achieved": dom["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": dom["frac"], "traffic": None, "kernel": f"k_stream3_grouped<fp24 scales, k={dom['k']}>",
                         "ms_per_launch": dom["ms_per_launch"], "bytes_per_launch": dom["bytes_per_launch"]},
-           "classes": per_class, "host": host_info()}
+           "classes": per_class,
+           "rotated": {"entry": "wal_gemv_grouped with WAL_X_ROT_H128 (x rotated inside the launches)",
+                       "ms_per_step": round(ms_rot, 5), "GB/s": round(nbytes / (ms_rot * 1e-3) / 1e9, 2),
+                       "hbm_frac": round(nbytes / (ms_rot * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+           "host": host_info()}
     print(json.dumps(out), flush=True)
     del keep
 
