@@ -8,7 +8,10 @@ every product reads the one before it).  Each product is checked against the
 CPU oracle on the input the GPU gave it (relative L2 <= 1e-5, fp32
 activations); graph replays must reproduce the eager chain bit for bit, with
 eager work and host synchronisations between them, and a replay after x
-changed in place must match a fresh eager run.
+changed in place must match a fresh eager run.  The same chain with every
+product rotating its own input (WAL_X_ROT_H128, the 27B card's rotated
+blobs) is checked against the oracle on the rotated inputs, and its graph
+replays against its eager run.
 """
 import numpy as np
 import pytest
@@ -16,6 +19,7 @@ import pytest
 import synth
 from oracle import dense as D
 from oracle import format as F
+from oracle import rotation as Rt
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -135,3 +139,56 @@ def test_graph_capture_error_creates_nothing(wal, chain):
     h = ctypes.c_void_p()
     assert wal._lib.wal_graph_create(2, infos, plans, ctypes.byref(h)) == -1
     assert not h.value
+
+
+@pytest.fixture(scope="module")
+def rot_chain(wal, chain):
+    """The chain's matrices and inputs with plans that rotate x (fp32) first."""
+    mats = chain["mats"]
+    ys = {k: torch.full_like(v, float("nan")) for k, v in chain["ys"].items()}
+    flags = wal.WAL_X_F32 | wal.WAL_X_ROT_H128
+    groups = []
+    for layer in range(LAYERS):
+        h = chain["h0"] if layer == 0 else ys[layer - 1, "down"]
+        groups += [(["q", "k", "v"], h), (["o"], ys[layer, "q"]), (["gate", "up"], ys[layer, "o"]),
+                   (["down"], ys[layer, "gate"])]
+    sizes = [wal.wal_grouped_plan_size([mats[0, n][2] for n in names], 0, flags)[1] for names, _ in groups]
+    ws = torch.zeros(max(max(sizes), 4) // 4, dtype=torch.float32, device=dev())
+    Ws = chain["keep"][0]
+    plans, per_layer = [], []
+    for gi, (names, x) in enumerate(groups):
+        layer = gi // 4
+        infos = [mats[layer, n][2] for n in names]
+        plan, g = wal.wal_grouped_plan(infos, [Ws[layer, n] for n in names], [x] * len(names),
+                                       [ys[layer, n] for n in names], ws, flags)
+        assert g.x_dtype == flags
+        plans.append((g, torch.from_numpy(plan).to(dev())))
+        per_layer.append((layer, names, x))
+    return dict(mats=mats, ys=ys, plans=plans, groups=per_layer, keep=ws)
+
+
+def test_rotated_chain_oracle_and_graph(wal, rot_chain):
+    c = rot_chain
+    clear(c)
+    print("rotated chain: eager, 8 grouped products", flush=True)
+    wal.wal_gemv_grouped_seq(c["plans"])
+    eager = outputs(c)
+    for layer, names, x in c["groups"]:
+        xin = Rt.rotate(x.cpu().numpy().astype(np.float64))   # the rotation of the input the GPU read
+        for n in names:
+            m, _, _ = c["mats"][layer, n]
+            ref = D.gemv(F.pack(F.from_synth(m)), xin)
+            err = D.rel_l2(eager[layer, n].astype(np.float64), ref)
+            assert err <= F32_TOL, (layer, n, err)
+    g = wal.WalGraph(c["plans"])
+    try:
+        for rep in range(3):
+            clear(c)
+            torch.cuda.synchronize()
+            print(f"rotated graph replay {rep}", flush=True)
+            g.launch()
+            got = outputs(c)
+            for k in eager:
+                assert np.array_equal(got[k], eager[k]), (rep, k)
+    finally:
+        g.close()
