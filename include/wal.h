@@ -393,7 +393,8 @@ int wal_gemv_grouped_phases(const wal_grouped_info* ginfo, const void* plan_dev,
  *   codes  [V][in / 2] bytes, element 2i in the low nibble of byte i, 2i + 1
  *          in the high nibble, two's-complement nibbles
  *   scales [V][in / 128] fp16, little-endian, right after the codes
- * wal_int4_size: bytes of the layout.  Errors: ARG, SHAPE.
+ * wal_int4_size: bytes of the layout (V * in above 2^40: WAL_ERR_SHAPE).
+ *   Errors: ARG, SHAPE.
  * wal_int4_pack: q int8 [V][in], s float [V][in / 128] (host) -> dst (host).
  *   A code outside [-8, 7] (WAL_ERR_CODE) or a scale fp16 cannot hold exactly
  *   (WAL_ERR_INEXACT) is rejected before anything is written.

@@ -21,6 +21,9 @@ constexpr uint32_t kMagic = 0x314C4157u;  // "WAL1"
 constexpr uint32_t kVersion = 1;
 constexpr uint64_t kAlign = 256;
 constexpr uint8_t kBase3Pad = 0x79;      // five zero trits (digits 1,1,1,1,1)
+// Largest V * in of an INT3/4/5 matrix: its byte count, V * in * bits / 8,
+// must not wrap in 64 bits (the ternary blobs have the same bound on out * in).
+constexpr uint64_t kMaxQElems = 1ull << 40;
 
 uint64_t up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 
@@ -443,7 +446,7 @@ int wal_workspace_size(const wal_info* info, uint32_t batch, size_t* bytes) {
 
 int wal_int4_size(uint32_t V, uint32_t in, size_t* bytes) {
   if (!bytes || !V || !in) return WAL_ERR_ARG;
-  if (in % 128) return WAL_ERR_SHAPE;
+  if (in % 128 || (uint64_t)V * in > kMaxQElems) return WAL_ERR_SHAPE;
   *bytes = (size_t)V * in / 2 + (size_t)V * (in / 128) * 2;
   return WAL_OK;
 }
@@ -492,7 +495,7 @@ int wal_int4_unpack(uint32_t V, uint32_t in, const void* src, size_t src_bytes, 
 // streams simply follow each other.
 static int qstream_size(uint32_t bits, uint32_t V, uint32_t in, size_t* bytes) {
   if (!bytes || !V || !in) return WAL_ERR_ARG;
-  if (in % 128) return WAL_ERR_SHAPE;
+  if (in % 128 || (uint64_t)V * in > kMaxQElems) return WAL_ERR_SHAPE;
   *bytes = (size_t)V * in * bits / 8 + (size_t)V * (in / 128) * 2;
   return WAL_OK;
 }

@@ -535,6 +535,12 @@ def test_int4_pack_matches_oracle_and_rejects():
         assert np.array_equal(q2, q) and np.array_equal(s2, s)
     assert wal.wal_int4_size(151936, 4096) == I.size(151936, 4096)
     lib = wal._lib
+    # V * in past 2^40 is refused: its byte count would wrap 64 bits at the largest shapes
+    n = ctypes.c_size_t(0)
+    for size in (lib.wal_int3_size, lib.wal_int4_size, lib.wal_int5_size):
+        assert size(1 << 20, 1 << 20, ctypes.byref(n)) == 0
+        assert size((1 << 20) + 1, 1 << 20, ctypes.byref(n)) == -2
+        assert size(0xFFFFFFFF, 0xFFFFFF80, ctypes.byref(n)) == -2
     buf = np.zeros(I.size(2, 256), np.uint8)
     q = np.zeros((2, 256), np.int8)
     s = np.ones((2, 2), np.float32)
