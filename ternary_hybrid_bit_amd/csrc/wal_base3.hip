@@ -414,17 +414,20 @@ __device__ __forceinline__ void stream_rows_base3(const MatDev& d, uint32_t row0
 
 // One segment, pass by pass, then its store (store_segment: the low-rank
 // term, or with P one pass's partial sums and the reduce of a completed row
-// block).
+// block).  With count (the workgroup's last segment) the store may count
+// the workgroup finished; returns whether it did.
 template <int SF, int K, class ZJ, bool ROT>
-__device__ __forceinline__ void run_segment_base3(const MatDev& d, uint32_t row0, uint32_t row1, bool lut_first,
+__device__ __forceinline__ bool run_segment_base3(const MatDev& d, uint32_t row0, uint32_t row1, bool lut_first,
                                                   Smem3& sm, const Fuse& f, float* P = nullptr,
-                                                  uint32_t split_pass = 0, uint32_t* cnt = nullptr) {
+                                                  uint32_t split_pass = 0, uint32_t* cnt = nullptr,
+                                                  bool count = false) {
   const uint32_t npass = (d.in + kPassBase3 - 1) / kPassBase3;
   const bool split = P != nullptr;
   const uint32_t p0 = split ? split_pass : 0, p1 = split ? split_pass + 1 : npass;
   for (uint32_t pass = p0; pass < p1; ++pass)
     stream_rows_base3<SF, K, ROT>(d, row0, row1, pass, pass == p0, lut_first && pass == p0, sm);
-  store_segment<WAL_X_BF16, ZJ, ROT>(d, row0, row1, SegEnd{sm.tbl, sm.z, sm.ybuf}, f, P, split_pass, npass, cnt);
+  return store_segment<WAL_X_BF16, ZJ, ROT>(d, row0, row1, SegEnd{sm.tbl, sm.z, sm.ybuf}, f, P, split_pass, npass,
+                                            cnt, count);
 }
 
 // Low-rank jobs of grouped plans and single products, as in the 2-bit
@@ -452,6 +455,7 @@ void k_stream3_grouped(const MatDev* __restrict__ descs,
                                                               const uint32_t* __restrict__ jobs, Fuse f) {
   __shared__ Smem3 sm;
   const uint32_t t = blockIdx.x;
+  bool counted = false;
   if (t < f.nz) {
     z_job_grouped3<ROT>(descs, jobs, t, zjob_terms<ZJobsGrouped>(f), epoch_of(f), sm.tbl);
   } else {
@@ -461,13 +465,14 @@ void k_stream3_grouped(const MatDev* __restrict__ descs,
       const Seg sg = segs[s];
       const MatDev& d = descs[sg.mat];
       if (sg.pass1)
-        run_segment_base3<SF, K, ZJobsGrouped, ROT>(d, sg.row0, sg.row1, s == s0, sm, f, d.P, sg.pass1 - 1,
-                                                    f.sync + d.cnt_off);
+        counted = run_segment_base3<SF, K, ZJobsGrouped, ROT>(d, sg.row0, sg.row1, s == s0, sm, f, d.P,
+                                                              sg.pass1 - 1, f.sync + d.cnt_off, s + 1 == s1);
       else
-        run_segment_base3<SF, K, ZJobsGrouped, ROT>(d, sg.row0, sg.row1, s == s0, sm, f);
+        counted = run_segment_base3<SF, K, ZJobsGrouped, ROT>(d, sg.row0, sg.row1, s == s0, sm, f, nullptr, 0,
+                                                              nullptr, s + 1 == s1);
     }
   }
-  finish_launch(f);
+  if (!counted) finish_launch(f);
 }
 
 template <int SF, int K, bool ROT>
@@ -479,6 +484,7 @@ void k_stream3_single(MatDev d, uint32_t rows_per_block, uint32_t nrb,
   // b % nrb
   __shared__ Smem3 sm;
   const uint32_t t = blockIdx.x;
+  bool counted = false;
   if (t < f.nz) {
     const uint32_t tcs = (d.terms + kZTerms - 1) / kZTerms, tc = t % tcs, cc = t / tcs;
     const uint32_t c0 = cc * kZSingleCols, c1 = min(d.in, c0 + kZSingleCols);
@@ -490,9 +496,10 @@ void k_stream3_single(MatDev d, uint32_t rows_per_block, uint32_t nrb,
     const uint32_t rb = P ? b % nrb : b;
     const uint32_t r0 = rb * rows_per_block;
     const uint32_t r1 = min(d.out, r0 + rows_per_block);
-    if (r0 < r1) run_segment_base3<SF, K, ZJobsSingle, ROT>(d, r0, r1, true, sm, f, P, P ? b / nrb : 0u, cnt);
+    if (r0 < r1)
+      counted = run_segment_base3<SF, K, ZJobsSingle, ROT>(d, r0, r1, true, sm, f, P, P ? b / nrb : 0u, cnt, true);
   }
-  finish_launch(f);
+  if (!counted) finish_launch(f);
 }
 
 }  // namespace

@@ -720,11 +720,12 @@ __device__ __forceinline__ const uint32_t* epoch_of(const Fuse& f) {
 // disagree).  Copy r counts the workgroups b % kSyncReplicas == r; the one
 // that completes a copy counts it in line 0, and the one that completes the
 // last copy resets.  No data changes hands here: the counts order nothing
-// but the reset.  Every thread calls it.
-__device__ __forceinline__ void finish_launch(const Fuse& f) {
+// but the reset.  Every thread calls it; thread `counter` does the counting
+// (its wave waits for the counts' round trips).
+__device__ __forceinline__ void finish_launch(const Fuse& f, uint32_t counter = 0) {
   if (!f.sync) return;
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (threadIdx.x == counter) {
     const uint32_t r = blockIdx.x % kSyncReplicas;
     const uint32_t members = (f.grid - r + kSyncReplicas - 1) / kSyncReplicas;
     const uint32_t copies = min(f.grid, kSyncReplicas);
@@ -973,10 +974,16 @@ __device__ __forceinline__ float lowrank_row(const MatDev& d, const SegEnd& e, _
 // workgroup whose arrival completes a group (npass arrivals) adds its rows'
 // npass planes in pass order with the low-rank term, stores y, and returns
 // the counter to zero.  Every thread calls it (barriers).
+// With `count` (the workgroup's last segment), a segment that reads the
+// low-rank terms counts the workgroup finished (finish_launch) right after
+// that read, its last use of the call's tags, so that the count's round
+// trip overlaps the rest of the epilogue; the last wave counts, as the
+// first rows of a short segment belong to the first waves.  Returns whether
+// it counted.
 template <int XT, class ZJ, bool ROT>
-__device__ __forceinline__ void store_segment(const MatDev& d, uint32_t row0, uint32_t row1, const SegEnd& e,
+__device__ __forceinline__ bool store_segment(const MatDev& d, uint32_t row0, uint32_t row1, const SegEnd& e,
                                               const Fuse& f, float* P = nullptr, uint32_t pass = 0,
-                                              uint32_t npass = 1, uint32_t* cnt = nullptr) {
+                                              uint32_t npass = 1, uint32_t* cnt = nullptr, bool count = false) {
   __syncthreads();   // the segment's y is complete; the site table's readers are done
   const uint32_t nrows = row1 - row0;
   const __amdgpu_buffer_rsrc_t ru = rsrc(d.codes, d.blob_bytes);
@@ -1000,7 +1007,7 @@ __device__ __forceinline__ void store_segment(const MatDev& d, uint32_t row0, ui
       mine[t] = last;
     }
     __syncthreads();
-    if (!__builtin_amdgcn_readfirstlane(s_any)) return;   // no group completed here
+    if (!__builtin_amdgcn_readfirstlane(s_any)) return false;   // no group completed here
     if (!d.terms) {
       for (uint32_t i = threadIdx.x; i < nrows; i += blockDim.x) {
         if (!mine[i / 16]) continue;
@@ -1009,11 +1016,11 @@ __device__ __forceinline__ void store_segment(const MatDev& d, uint32_t row0, ui
         for (uint32_t q = 1; q < npass; ++q) v += load_dev(P + (size_t)q * d.out + row);
         d.y[row] = v;
       }
-      return;
+      return false;
     }
   } else if (!d.terms) {
     for (uint32_t i = threadIdx.x; i < nrows; i += blockDim.x) d.y[row0 + i] = e.ybuf[i];
-    return;
+    return false;
   }
   // The low-rank term.  Every thread's U bytes for its first row go out
   // before the partials are read, so their latencies overlap.  A segment of
@@ -1025,12 +1032,13 @@ __device__ __forceinline__ void store_segment(const MatDev& d, uint32_t row0, ui
   const UAhead ua = load_u_ahead(d, ru, urow);
   if (!lowrank_z_read(d, e, f)) lowrank_z_here<XT, ROT>(d, e);   // the rare fallback
   __syncthreads();
+  if (count) finish_launch(f, blockDim.x - 64);
   if (ahead && nrows <= blockDim.x) {
     if (i0 < nrows) {
       const uint32_t row = row0 + i0;
       float v;
       if (P) {
-        if (!mine[i0 / 16]) return;
+        if (!mine[i0 / 16]) return count;
         v = load_dev(P + row);
         for (uint32_t q = 1; q < npass; ++q) v += load_dev(P + (size_t)q * d.out + row);
       } else {
@@ -1038,7 +1046,7 @@ __device__ __forceinline__ void store_segment(const MatDev& d, uint32_t row0, ui
       }
       d.y[row] = v + lowrank_row_ahead<true>(d, e, ua);
     }
-    return;
+    return count;
   }
   lowrank_build(d, e);
   for (uint32_t i = i0; i < nrows; i += blockDim.x) {
@@ -1053,6 +1061,7 @@ __device__ __forceinline__ void store_segment(const MatDev& d, uint32_t row0, ui
     }
     d.y[row] = v + (ahead && i == i0 ? lowrank_row_ahead<false>(d, e, ua) : lowrank_row(d, e, ru, row));
   }
+  return count;
 }
 
 }  // namespace

@@ -398,16 +398,19 @@ __device__ __forceinline__ void stream_rows_2bit(const MatDev& d, uint32_t row0,
 // matrix's scale format and sites per group: every (scale format, k) class
 // has kernels of its own, so the registers of the hot fp16 / k = 8 loop are
 // not set by the heavier fp24 loads.
+// With count (the workgroup's last segment) the store may count the
+// workgroup finished; returns whether it did.
 template <int XT, int SF, int K, int RB, class ZJ, bool ROT>
-__device__ __forceinline__ void run_segment_2bit(const MatDev& d, uint32_t row0, uint32_t row1, StreamSmem& sm,
+__device__ __forceinline__ bool run_segment_2bit(const MatDev& d, uint32_t row0, uint32_t row1, StreamSmem& sm,
                                                  const Fuse& f, float* P = nullptr, uint32_t split_pass = 0,
-                                                 uint32_t* cnt = nullptr) {
+                                                 uint32_t* cnt = nullptr, bool count = false) {
   const uint32_t npass = (d.in + kPass2bit - 1) / kPass2bit;
   const bool split = P != nullptr;
   const uint32_t p0 = split ? split_pass : 0, p1 = split ? split_pass + 1 : npass;
   for (uint32_t pass = p0; pass < p1; ++pass)
     stream_rows_2bit<XT, SF, K, RB, ROT>(d, row0, row1, pass, pass == p0, sm);
-  store_segment<XT, ZJ, ROT>(d, row0, row1, SegEnd{sm.tbl, sm.z, sm.ybuf}, f, P, split_pass, npass, cnt);
+  return store_segment<XT, ZJ, ROT>(d, row0, row1, SegEnd{sm.tbl, sm.z, sm.ybuf}, f, P, split_pass, npass, cnt,
+                                    count);
 }
 
 // Three workgroups per CU (the LDS of a workgroup allows it) when the class's
@@ -441,6 +444,7 @@ void k_stream_grouped(const MatDev* __restrict__ descs, const uint32_t* __restri
                       const Seg* __restrict__ segs, const uint32_t* __restrict__ jobs, Fuse f) {
   __shared__ StreamSmem sm;
   const uint32_t t = blockIdx.x;
+  bool counted = false;
   if (t < f.nz) {
     grouped_z_job<XT, ROT>(descs, jobs, t, zjob_terms<ZJobsGrouped>(f), epoch_of(f), sm.tbl);
   } else {
@@ -450,13 +454,14 @@ void k_stream_grouped(const MatDev* __restrict__ descs, const uint32_t* __restri
       const Seg sg = segs[s];
       const MatDev& d = descs[sg.mat];
       if (sg.pass1)
-        run_segment_2bit<XT, SF, K, RB, ZJobsGrouped, ROT>(d, sg.row0, sg.row1, sm, f, d.P, sg.pass1 - 1,
-                                                           f.sync + d.cnt_off);
+        counted = run_segment_2bit<XT, SF, K, RB, ZJobsGrouped, ROT>(d, sg.row0, sg.row1, sm, f, d.P, sg.pass1 - 1,
+                                                                     f.sync + d.cnt_off, s + 1 == s1);
       else
-        run_segment_2bit<XT, SF, K, RB, ZJobsGrouped, ROT>(d, sg.row0, sg.row1, sm, f);
+        counted = run_segment_2bit<XT, SF, K, RB, ZJobsGrouped, ROT>(d, sg.row0, sg.row1, sm, f, nullptr, 0, nullptr,
+                                                                     s + 1 == s1);
     }
   }
-  finish_launch(f);
+  if (!counted) finish_launch(f);
 }
 
 // Single products: workgroup t = blockIdx.x < f.nz computes the low-rank
@@ -470,6 +475,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(stream
 void k_stream_single(MatDev d, uint32_t rows_per_block, uint32_t nrb, float* P, uint32_t* cnt, Fuse f) {
   __shared__ StreamSmem sm;
   const uint32_t t = blockIdx.x;
+  bool counted = false;
   if (t < f.nz) {
     const uint32_t tcs = (d.terms + kZTerms - 1) / kZTerms, tc = t % tcs, cc = t / tcs;
     const uint32_t c0 = cc * kZSingleCols, c1 = min(d.in, c0 + kZSingleCols);
@@ -480,9 +486,10 @@ void k_stream_single(MatDev d, uint32_t rows_per_block, uint32_t nrb, float* P, 
     const uint32_t rb = P ? b % nrb : b;
     const uint32_t r0 = rb * rows_per_block;
     const uint32_t r1 = min(d.out, r0 + rows_per_block);
-    if (r0 < r1) run_segment_2bit<XT, SF, K, RB, ZJobsSingle, ROT>(d, r0, r1, sm, f, P, P ? b / nrb : 0u, cnt);
+    if (r0 < r1)
+      counted = run_segment_2bit<XT, SF, K, RB, ZJobsSingle, ROT>(d, r0, r1, sm, f, P, P ? b / nrb : 0u, cnt, true);
   }
-  finish_launch(f);
+  if (!counted) finish_launch(f);
 }
 
 // The grouped low-rank pre-pass as a launch of its own (the phase API).
