@@ -1030,17 +1030,36 @@ __device__ __forceinline__ bool store_segment(const MatDev& d, uint32_t row0, ui
   const uint32_t i0 = threadIdx.x;
   const uint32_t urow = row0 + min(i0, nrows - 1);
   const UAhead ua = load_u_ahead(d, ru, urow);
+  // A split product's completing workgroup also loads its thread's row's
+  // partial sums (up to kPAhead passes) before the read, for the same reason.
+  constexpr uint32_t kPAhead = 4;
+  const bool direct = ahead && nrows <= blockDim.x;
+  float pa[kPAhead];
+#pragma unroll
+  for (uint32_t q = 0; q < kPAhead; ++q) pa[q] = 0.f;
+  if (P && direct && npass <= kPAhead && i0 < nrows && mine[i0 / 16]) {
+#pragma unroll
+    for (uint32_t q = 0; q < kPAhead; ++q)
+      if (q < npass) pa[q] = load_dev(P + (size_t)q * d.out + row0 + i0);
+  }
   if (!lowrank_z_read(d, e, f)) lowrank_z_here<XT, ROT>(d, e);   // the rare fallback
   __syncthreads();
   if (count) finish_launch(f, blockDim.x - 64);
-  if (ahead && nrows <= blockDim.x) {
+  if (direct) {
     if (i0 < nrows) {
       const uint32_t row = row0 + i0;
       float v;
       if (P) {
         if (!mine[i0 / 16]) return count;
-        v = load_dev(P + row);
-        for (uint32_t q = 1; q < npass; ++q) v += load_dev(P + (size_t)q * d.out + row);
+        if (npass <= kPAhead) {
+          v = pa[0];
+#pragma unroll
+          for (uint32_t q = 1; q < kPAhead; ++q)
+            if (q < npass) v += pa[q];
+        } else {
+          v = load_dev(P + row);
+          for (uint32_t q = 1; q < npass; ++q) v += load_dev(P + (size_t)q * d.out + row);
+        }
       } else {
         v = e.ybuf[i0];
       }
