@@ -11,7 +11,9 @@ eager work and host synchronisations between them, and a replay after x
 changed in place must match a fresh eager run.  The same chain with every
 product rotating its own input (WAL_X_ROT_H128, the 27B card's rotated
 blobs) is checked against the oracle on the rotated inputs, and its graph
-replays against its eager run.
+replays against its eager run.  One layer of the 8B-shaped body at full size
+(4096-12288 rows and columns, fp32 activations) runs the same dependent
+chain, checked on sampled rows and replayed bit for bit.
 """
 import numpy as np
 import pytest
@@ -192,3 +194,58 @@ def test_rotated_chain_oracle_and_graph(wal, rot_chain):
                 assert np.array_equal(got[k], eager[k]), (rep, k)
     finally:
         g.close()
+
+
+def test_full_size_layer_chain_fp32(wal):
+    """One Qwen3-8B-shaped layer at full size with real data dependencies:
+    q|k|v read h, o reads q's output, gate|up read o's output, down reads
+    gate's output (fp32 activations, 2-bit / fp16 / k = 8 blobs of the
+    sweep, the down product's passes split over workgroups).  Sampled rows
+    of every product match the oracle on the input the GPU gave it, and two
+    graph replays reproduce the eager chain bit for bit."""
+    from ternary_hybrid_bit_amd import workloads
+    print("full-size layer: packing 7 matrices", flush=True)
+    items = workloads.sweep(layers=1)
+    names = ["q", "k", "v", "o", "gate", "up", "down"]
+    infos = {n: info for n, (_, info, _) in zip(names, items)}
+    blobs = {n: blob for n, (blob, _, _) in zip(names, items)}
+    Ws = {n: torch.from_numpy(blobs[n]).to(dev()) for n in names}
+    ys = {n: torch.full((infos[n].d.out,), float("nan"), dtype=torch.float32, device=dev()) for n in names}
+    x0, _ = synth.make_x(331, 0, 4096, bf16=False)
+    h = torch.from_numpy(x0[0].copy()).to(dev())
+    groups = [(["q", "k", "v"], h), (["o"], ys["q"]), (["gate", "up"], ys["o"]), (["down"], ys["gate"])]
+    sizes = [wal.wal_grouped_plan_size([infos[n] for n in g], 0, wal.WAL_X_F32)[1] for g, _ in groups]
+    ws = torch.zeros(max(max(sizes), 4) // 4, dtype=torch.float32, device=dev())
+    plans = []
+    for g, x in groups:
+        plan, gi = wal.wal_grouped_plan([infos[n] for n in g], [Ws[n] for n in g], [x] * len(g), [ys[n] for n in g],
+                                        ws, wal.WAL_X_F32)
+        plans.append((gi, torch.from_numpy(plan).to(dev())))
+    print("full-size layer: eager chain", flush=True)
+    wal.wal_gemv_grouped_seq(plans)
+    torch.cuda.synchronize()
+    eager = {n: ys[n].cpu().numpy().copy() for n in names}
+    rng = np.random.default_rng(12)
+    for g, x in groups:
+        xin = x.cpu().numpy().astype(np.float64)   # the input the GPU product read
+        assert np.isfinite(xin).all()
+        for n in g:
+            out = infos[n].d.out
+            rows = np.unique(np.concatenate([[0, out - 1], rng.integers(0, out, 6)]))
+            ref = D.gemv_rows(blobs[n], xin, rows)
+            err = D.rel_l2(eager[n][rows].astype(np.float64), ref)
+            assert err <= F32_TOL, (n, err)
+    gr = wal.WalGraph(plans)
+    try:
+        for rep in range(2):
+            for v in ys.values():
+                v.fill_(float("nan"))
+            torch.cuda.synchronize()
+            print(f"full-size layer: graph replay {rep}", flush=True)
+            gr.launch()
+            torch.cuda.synchronize()
+            for n in names:
+                assert np.array_equal(ys[n].cpu().numpy(), eager[n]), (rep, n)
+    finally:
+        gr.close()
+    assert wal.sync_fallbacks(ws) == 0
